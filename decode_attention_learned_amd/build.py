@@ -1,0 +1,75 @@
+"""Build libdms.so in-tree with hipcc for gfx950.
+
+    python -m decode_attention_learned_amd.build
+
+Every call recompiles.  The library lands next to this file, where
+``decode_attention_learned_amd.lib`` looks for it.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libdms.so")
+ARCH = "gfx950"
+
+SOURCES = ["api.hip", "cache_kernels.hip", "decode_kernels.hip", "decode_mfma.hip", "prefill.hip"]
+
+# Packed fp32 instructions are switched off for all device code; hipcc's host
+# pass warns that it does not know the feature, which is harmless.
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument", "-Wno-pass-failed",
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found: the HIP library cannot be built")
+    return path
+
+
+def build(verbose: bool = False) -> str:
+    objs = []
+    build_dir = os.path.join(HERE, "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+        cmd = [hipcc(), *[f for f in FLAGS if f != "-shared"], "-c", "-I", INCLUDE, "-I", CSRC,
+               os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        objs.append(obj)
+    failed = []
+    for src, p in procs:
+        out, _ = p.communicate()
+        text = out.decode(errors="replace")
+        errors = [ln for ln in text.splitlines() if "error" in ln]
+        if p.returncode != 0:
+            failed.append((src, text))
+        elif verbose and errors:
+            print(text)
+    if failed:
+        for src, text in failed:
+            sys.stderr.write(f"--- {src}\n{text}\n")
+        raise RuntimeError("hipcc failed for " + ", ".join(s for s, _ in failed))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

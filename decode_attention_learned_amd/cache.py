@@ -1,0 +1,154 @@
+"""Torch-side ownership of a DMS paged cache and thin calls into libdms.
+
+PyTorch only allocates device memory and supplies the stream; every step
+(reset, decide + append, compaction, decode, prefill) runs in the library's
+HIP kernels.  Shapes and layouts are those of include/dms.h.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import lib
+
+PAGE = lib.DMS_PAGE_SIZE
+_DTYPES = {torch.float32: lib.DMS_KV_F32, torch.bfloat16: lib.DMS_KV_BF16}
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+class DmsCache:
+    """A paged DMS cache for `batch` sequences x `kv_heads` KV heads.
+
+    Buffers (all on `device`): see the dms_cache struct in include/dms.h.
+    """
+
+    def __init__(self, batch: int, kv_heads: int, group: int, head_dim: int,
+                 dtype: torch.dtype = torch.bfloat16, num_pages: int | None = None,
+                 max_pages_per_unit: int = 64, window: int = 16, device="cuda:0"):
+        lib.load()
+        self.device = torch.device(device)
+        if dtype not in _DTYPES:
+            raise TypeError(f"unsupported KV dtype {dtype}")
+        self.dtype = dtype
+        self.batch, self.kv_heads, self.group, self.head_dim = batch, kv_heads, group, head_dim
+        self.window = window
+        self.units = batch * kv_heads
+        self.max_pages_per_unit = max_pages_per_unit
+        self.num_pages = num_pages if num_pages is not None else self.units * max_pages_per_unit
+        self.shape = lib.DmsShape(batch, kv_heads, group, head_dim, PAGE, window,
+                                  max_pages_per_unit, self.num_pages, _DTYPES[dtype])
+        rc = lib.check_shape(self.shape)
+        lib.check("dms_check_shape", rc)
+        dev = self.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.k_pages = torch.zeros((self.num_pages, PAGE, head_dim), dtype=dtype, device=dev)
+        self.v_pages = torch.zeros((self.num_pages, head_dim, PAGE), dtype=dtype, device=dev)
+        self.page_table = torch.empty((self.units, max_pages_per_unit), **i32)
+        self.slot_pos = torch.zeros((self.num_pages, PAGE), **i32)
+        self.slot_alpha = torch.zeros((self.num_pages, PAGE), dtype=torch.uint8, device=dev)
+        self.n_slots = torch.empty((self.units,), **i32)
+        self.n_clean = torch.empty((self.units,), **i32)
+        self.append_base = torch.empty((self.units,), **i32)
+        self.seq_len = torch.empty((batch,), **i32)
+        self.free_list = torch.empty((self.num_pages,), **i32)
+        self.free_top = torch.empty((1,), **i32)
+        self.status = torch.empty((1,), **i32)
+        self.cache = lib.DmsCacheStruct(*[t.data_ptr() for t in (
+            self.k_pages, self.v_pages, self.page_table, self.slot_pos, self.slot_alpha,
+            self.n_slots, self.n_clean, self.append_base, self.seq_len, self.free_list,
+            self.free_top, self.status)])
+        self.workspace_bytes = lib.decode_workspace_bytes(self.shape)
+        self.workspace = torch.empty((self.workspace_bytes,), dtype=torch.uint8, device=dev)
+        self.reset()
+
+    # -- calls -------------------------------------------------------------
+    def reset(self) -> None:
+        lib.check("dms_reset", lib.dms_reset(self.shape, self.cache, _stream()))
+
+    def append(self, k: torch.Tensor, v: torch.Tensor, logit: torch.Tensor) -> None:
+        """k, v [B, n, Hkv, D] (cache dtype), logit [B, n, Hkv] float32."""
+        n = k.shape[1]
+        kshape = (self.batch, n, self.kv_heads, self.head_dim)
+        _need(k, "k", self.dtype, kshape, self.device)
+        _need(v, "v", self.dtype, kshape, self.device)
+        _need(logit, "logit", torch.float32, kshape[:3], self.device)
+        lib.check("dms_append", lib.dms_append(self.shape, self.cache, k, v, logit, n, _stream()))
+
+    def compact(self) -> None:
+        lib.check("dms_compact", lib.dms_compact(self.shape, self.cache, _stream()))
+
+    def decode(self, q: torch.Tensor, out: torch.Tensor | None = None,
+               sm_scale: float | None = None) -> torch.Tensor:
+        """q [B, Hq, D] (cache dtype) -> out [B, Hq, D] float32."""
+        qshape = (self.batch, self.kv_heads * self.group, self.head_dim)
+        _need(q, "q", self.dtype, qshape, self.device)
+        if out is None:
+            out = torch.empty(qshape, dtype=torch.float32, device=self.device)
+        _need(out, "out", torch.float32, qshape, self.device)
+        scale = 1.0 / math.sqrt(self.head_dim) if sm_scale is None else sm_scale
+        lib.check("dms_decode_attn", lib.dms_decode_attn(
+            self.shape, self.cache, q, out, scale, self.workspace, self.workspace_bytes, _stream()))
+        return out
+
+    # -- inspection (host copies; for tests and reports) -------------------
+    def status_word(self) -> int:
+        return int(self.status.item())
+
+    def pages_in_use(self) -> int:
+        return self.num_pages - int(self.free_top.item())
+
+    def slots(self, unit: int):
+        """(pos, alpha) of every slot of `unit`, in slot order, as CPU tensors."""
+        n = int(self.n_slots[unit].item())
+        pages = self.page_table[unit, : (n + PAGE - 1) // PAGE].long()
+        pos = self.slot_pos[pages].reshape(-1)[:n].cpu()
+        alpha = self.slot_alpha[pages].reshape(-1)[:n].cpu()
+        return pos, alpha
+
+    def slot_kv(self, unit: int):
+        """(k [n, D], v [n, D]) of every slot of `unit`, in slot order, CPU tensors."""
+        n = int(self.n_slots[unit].item())
+        pages = self.page_table[unit, : (n + PAGE - 1) // PAGE].long()
+        k = self.k_pages[pages].reshape(-1, self.head_dim)[:n].cpu()
+        v = self.v_pages[pages].transpose(1, 2).reshape(-1, self.head_dim)[:n].cpu()
+        return k, v
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logit: torch.Tensor,
+            window: int = 16, sm_scale: float | None = None,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """Masked DMS prefill: q [B, S, Hq, D], k, v [B, S, Hkv, D] bf16, logit [B, S, Hkv] f32."""
+    lib.load()
+    b, s, hq, d = q.shape
+    hkv = k.shape[2]
+    if hq % hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    dev = q.device
+    _need(k, "k", q.dtype, (b, s, hkv, d), dev)
+    _need(v, "v", q.dtype, (b, s, hkv, d), dev)
+    _need(logit, "logit", torch.float32, (b, s, hkv), dev)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if out is None:
+        out = torch.empty((b, s, hq, d), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (b, s, hq, d), dev)
+    shape = lib.DmsShape(b, hkv, hq // hkv, d, PAGE, window, 1, 1, _DTYPES.get(q.dtype, -1))
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+    lib.check("dms_prefill_attn", lib.dms_prefill_attn(shape, q, k, v, logit, s, scale, out, _stream()))
+    return out

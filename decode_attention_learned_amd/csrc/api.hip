@@ -1,0 +1,115 @@
+// libdms C ABI: host-side argument checks and dispatch.  Nothing here
+// allocates, synchronises or keeps state between calls.
+#include <stdint.h>
+
+#include "dms_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_cache(const dms_shape *s, const dms_cache *c) {
+  if (!c) return DMS_EINVAL;
+  if (!c->k_pages || !c->v_pages || !c->page_table || !c->slot_pos || !c->slot_alpha ||
+      !c->n_slots || !c->n_clean || !c->append_base || !c->seq_len || !c->free_list ||
+      !c->free_top || !c->status)
+    return DMS_EINVAL;
+  if (!aligned16(c->k_pages) || !aligned16(c->v_pages)) return DMS_EINVAL;
+  (void)s;
+  return DMS_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? DMS_OK : DMS_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int dms_version(void) { return DMS_ABI_VERSION; }
+
+const char *dms_strerror(int code) {
+  switch (code) {
+    case DMS_OK: return "ok";
+    case DMS_EINVAL: return "invalid argument";
+    case DMS_EUNSUPPORTED: return "unsupported shape or dtype";
+    case DMS_EWORKSPACE: return "decode workspace too small";
+    case DMS_EHIP: return "HIP launch failed";
+    default: return "unknown error code";
+  }
+}
+
+int dms_check_shape(const dms_shape *s) {
+  if (!s) return DMS_EINVAL;
+  if (s->batch < 1 || s->kv_heads < 1 || s->group < 1 || s->window < 1) return DMS_EINVAL;
+  if (s->max_pages_per_unit < 1 || s->num_pages < 1) return DMS_EINVAL;
+  if (int64_t(s->batch) * s->kv_heads > (int64_t(1) << 24)) return DMS_EINVAL;
+  if (int64_t(s->max_pages_per_unit) * DMS_PAGE_SIZE > (int64_t(1) << 30)) return DMS_EINVAL;
+  if (s->page_size != DMS_PAGE_SIZE) return DMS_EUNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return DMS_EUNSUPPORTED;
+  if (s->group > 16) return DMS_EUNSUPPORTED;
+  if (s->kv_dtype != DMS_KV_F32 && s->kv_dtype != DMS_KV_BF16) return DMS_EUNSUPPORTED;
+  return DMS_OK;
+}
+
+int dms_reset(const dms_shape *shape, const dms_cache *cache, hipStream_t stream) {
+  int rc = dms_check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_cache(shape, cache))) return rc;
+  return from_hip(dms::launch_reset(*shape, *cache, stream));
+}
+
+int dms_append(const dms_shape *shape, const dms_cache *cache, const void *k_new,
+               const void *v_new, const float *logit, int32_t n_new, hipStream_t stream) {
+  int rc = dms_check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_cache(shape, cache))) return rc;
+  if (n_new < 0) return DMS_EINVAL;
+  if (n_new == 0) return DMS_OK;
+  if (!k_new || !v_new || !logit) return DMS_EINVAL;
+  if (!aligned16(k_new)) return DMS_EINVAL;
+  if (int64_t(n_new) > int64_t(shape->max_pages_per_unit) * DMS_PAGE_SIZE) return DMS_EINVAL;
+  if (int64_t(n_new) > int64_t(65535) * DMS_PAGE_SIZE) return DMS_EINVAL;  // grid.y limit
+  return from_hip(dms::launch_append(*shape, *cache, k_new, v_new, logit, n_new, stream));
+}
+
+int dms_compact(const dms_shape *shape, const dms_cache *cache, hipStream_t stream) {
+  int rc = dms_check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_cache(shape, cache))) return rc;
+  return from_hip(dms::launch_compact(*shape, *cache, stream));
+}
+
+size_t dms_decode_workspace_bytes(const dms_shape *shape) {
+  if (dms_check_shape(shape) != DMS_OK) return 0;
+  return dms::decode_workspace_layout(dms::units_of(*shape), shape->group, shape->head_dim).bytes;
+}
+
+int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *q, float *out,
+                    float sm_scale, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = dms_check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_cache(shape, cache))) return rc;
+  if (!q || !out || !workspace) return DMS_EINVAL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return DMS_EINVAL;
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
+  if (workspace_bytes < dms_decode_workspace_bytes(shape)) return DMS_EWORKSPACE;
+  return from_hip(dms::launch_decode(*shape, *cache, q, out, sm_scale, workspace, stream));
+}
+
+int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const void *v,
+                     const float *logit, int32_t seq_len, float sm_scale, float *out,
+                     hipStream_t stream) {
+  if (!shape) return DMS_EINVAL;
+  if (shape->batch < 1 || shape->kv_heads < 1 || shape->group < 1 || shape->window < 1)
+    return DMS_EINVAL;
+  if (seq_len < 0) return DMS_EINVAL;
+  if (shape->head_dim != 128 || shape->kv_dtype != DMS_KV_BF16 || shape->group > 16)
+    return DMS_EUNSUPPORTED;
+  if (seq_len == 0) return DMS_OK;
+  if (!q || !k || !v || !logit || !out) return DMS_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return DMS_EINVAL;
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
+  return from_hip(dms::launch_prefill(*shape, q, k, v, logit, seq_len, sm_scale, out, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,238 @@
+// Split-K decode attention for bfloat16 caches on the gfx950 matrix cores.
+//
+// Same result as the generic kernel (see decode_kernels.hip for the method
+// and its sources); this file only changes how the two contractions of a
+// chunk are carried out.  Per KV head the G query heads share every key and
+// value row, so per 32-slot group of a page the work is two small dense
+// products:
+//   S^T [32 slots x 16] = K [32 x D] . Q^T [D x 16]     (G heads, zero padded)
+//   O^T [D x 16]       += V^T [D x 32] . P^T [32 x 16]
+// each on v_mfma_f32_16x16x32_bf16 with float32 accumulation.  Every K/V byte
+// is loaded from HBM once, straight into the MFMA operand registers, and
+// serves all G heads of the group.
+//
+// Operand layouts of v_mfma_f32_16x16x32_bf16 used below (lane l, q = l / 16):
+//   A: row l % 16, eight consecutive k values chosen by q
+//   B: column l % 16, the same eight k values
+//   C: column l % 16, rows 4q .. 4q + 3
+// The two 16-slot tiles of a group take their rows from the slot permutation
+//   tile 0 row 4a + r -> slot 8a + r,   tile 1 row 4a + r -> slot 8a + 4 + r,
+// so that after the QK products lane l holds the scores of head l % 16 for the
+// eight consecutive slots 8q .. 8q + 7.  Those are exactly the eight k values
+// it must supply to the PV product, and its V^T operand is then one 16-byte
+// load from the page's value column block (v_pages keeps slots contiguous per
+// d).  No data moves between lanes except the two shuffles of the row max.
+#include "dms_internal.h"
+
+namespace dms {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaWaves = 4;
+constexpr int kGroup = 32;  // slots per group (half a page)
+
+__device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+__device__ __forceinline__ floatx4 mfma_bf16(uint4 a, uint4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)lo)) |
+         (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)hi)) << 16);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_decode_mfma(
+    int hkv, int G, int window, int maxp, float scale_log2, const uint16_t *__restrict__ q,
+    const uint16_t *__restrict__ k_pages, const uint16_t *__restrict__ v_pages,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ slot_pos,
+    const uint8_t *__restrict__ slot_alpha, const int32_t *__restrict__ n_slots,
+    const int32_t *__restrict__ n_clean_arr, const int32_t *__restrict__ seq_len,
+    const int32_t *__restrict__ hdr, const int32_t *__restrict__ first_chunk,
+    const int32_t *__restrict__ chunk_unit, float2 *__restrict__ part_ml,
+    float *__restrict__ part_o, float *__restrict__ out) {
+  constexpr int KSTEPS = D / 32;  // QK products per 16-slot tile
+  constexpr int DTILES = D / 16;  // PV products per group
+  const int c = blockIdx.x;
+  if (c >= hdr[0]) return;
+  const int C = hdr[1];
+  const int u = chunk_unit[c];
+  const int b = u / hkv, h = u % hkv;
+  const int first = first_chunk[u];
+  const int nch = first_chunk[u + 1] - first;
+  const int n = n_slots[u];
+  const int s_begin = (c - first) * C;
+  const int s_end = min(n, s_begin + C);
+  const int t = seq_len[b] - 1;
+  const int nclean = n_clean_arr[u];
+  const int lim = min(nclean, s_end);  // slots below lim need no liveness test
+  const int32_t *row = page_table + size_t(u) * maxp;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = lane_id();
+  const int col = lane & 15;  // head index in B and C operands, row index in A
+  const int quad = lane >> 4;
+
+  // Q^T operand: head `col`, dims ks*32 + quad*8 .. +8; heads >= G are zero
+  uint4 qb[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) qb[ks] = make_uint4(0, 0, 0, 0);
+  if (col < G) {
+    const uint16_t *qp = q + (size_t(b) * hkv * G + size_t(h) * G + col) * D + quad * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qb[ks] = ld16(qp + ks * 32);
+  }
+  const int krow0 = 8 * (col >> 2) + (col & 3);  // slot of A row `col` in tile 0
+  const int krow1 = krow0 + 4;                   // ... in tile 1
+
+  floatx4 o[DTILES];
+#pragma unroll
+  for (int i = 0; i < DTILES; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int ngroups = (s_end - s_begin + kGroup - 1) / kGroup;
+  for (int gi = wave; gi < ngroups; gi += kMfmaWaves) {
+    const int gs = s_begin + gi * kGroup;
+    const int page = row[gs / kPage];
+    const int poff = gs % kPage;
+    const uint16_t *kp = k_pages + (size_t(page) * kPage + poff) * D + quad * 8;
+    const uint16_t *vp = v_pages + size_t(page) * D * kPage + poff + quad * 8;
+
+    uint4 ka0[KSTEPS], ka1[KSTEPS], va[DTILES];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      ka0[ks] = ld16(kp + krow0 * D + ks * 32);
+      ka1[ks] = ld16(kp + krow1 * D + ks * 32);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt) va[dt] = ld16(vp + (dt * 16 + col) * kPage);
+
+    floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      s0 = mfma_bf16(ka0[ks], qb[ks], s0);
+      s1 = mfma_bf16(ka1[ks], qb[ks], s1);
+    }
+    // scores of head `col` for slots gs + 8*quad + e, in log2 units
+    float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[e] *= scale_log2;
+
+    if (gs + kGroup > lim) {  // wave-uniform: tail of the chunk or not yet compacted
+      const size_t mb = size_t(page) * kPage + poff + quad * 8;
+      uint32_t keep[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int slot = gs + quad * 8 + e;
+        bool live = slot < s_end;
+        if (live && slot >= nclean) live = slot_alpha[mb + e] == 0 || (t - slot_pos[mb + e]) < window;
+        if (!live) sv[e] = -INFINITY;
+        keep[e >> 1] |= live ? (0xffffu << (16 * (e & 1))) : 0u;
+      }
+      // dead or unused slots must not reach the PV product even as 0 * NaN
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) {
+        va[dt].x &= keep[0];
+        va[dt].y &= keep[1];
+        va[dt].z &= keep[2];
+        va[dt].w &= keep[3];
+      }
+    }
+
+    float mx = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx);
+    float p[8];
+    float corr = 1.f;
+    if (m_new == -INFINITY) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = 0.f;
+    } else {
+      corr = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = exp2f(sv[e] - m_new);
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ps += p[e];
+    l_run = l_run * corr + ps;
+    m_run = m_new;
+    if (__ballot(corr != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) o[dt] *= corr;
+    }
+    const uint4 pb = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
+                                pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt) o[dt] = mfma_bf16(va[dt], pb, o[dt]);
+  }
+
+  // combine the waves of this workgroup
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  __shared__ float s_m[kMfmaWaves][16], s_l[kMfmaWaves][16];
+  __shared__ __align__(16) float s_o[kMfmaWaves][16][D + 4];
+  if (quad == 0) {
+    s_m[wave][col] = m_run;
+    s_l[wave][col] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DTILES; ++dt)
+    *reinterpret_cast<floatx4 *>(&s_o[wave][col][dt * 16 + quad * 4]) = o[dt];
+  __syncthreads();
+
+  for (int x = tid; x < G * D; x += 256) {
+    const int g = x / D, d = x % D;
+    float M = s_m[0][g];
+#pragma unroll
+    for (int w = 1; w < kMfmaWaves; ++w) M = fmaxf(M, s_m[w][g]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kMfmaWaves; ++w) {
+        const float mw = s_m[w][g];
+        if (mw == -INFINITY) continue;
+        const float f = exp2f(mw - M);
+        L = fmaf(s_l[w][g], f, L);
+        O = fmaf(s_o[w][g][d], f, O);
+      }
+    }
+    if (nch == 1) {
+      out[(size_t(b) * hkv * G + size_t(h) * G) * D + x] = L > 0.f ? O / L : 0.f;
+    } else {
+      part_o[size_t(c) * G * D + x] = O;
+      if (d == 0) part_ml[size_t(c) * G + g] = make_float2(M, L);
+    }
+  }
+}
+
+bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, float *out,
+                        float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st) {
+  if (s.kv_dtype != DMS_KV_BF16 || s.group > 16) return false;
+  const char *force = getenv("DMS_DECODE_KERNEL");
+  if (force && force[0] == 'g') return false;  // "generic": the VALU kernel
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(w.max_chunks), dim3(256), 0, st, s.kv_heads, s.group, s.window,
+                       s.max_pages_per_unit, scale_log2, static_cast<const uint16_t *>(q),
+                       static_cast<const uint16_t *>(c.k_pages),
+                       static_cast<const uint16_t *>(c.v_pages), c.page_table, c.slot_pos,
+                       c.slot_alpha, c.n_slots, c.n_clean, c.seq_len,
+                       reinterpret_cast<const int32_t *>(ws + w.hdr),
+                       reinterpret_cast<const int32_t *>(ws + w.first_chunk),
+                       reinterpret_cast<const int32_t *>(ws + w.chunk_unit),
+                       reinterpret_cast<float2 *>(ws + w.part_ml),
+                       reinterpret_cast<float *>(ws + w.part_o), out);
+  };
+  if (s.head_dim == 128) args(k_decode_mfma<128>);
+  else if (s.head_dim == 64) args(k_decode_mfma<64>);
+  else return false;
+  return true;
+}
+
+}  // namespace dms

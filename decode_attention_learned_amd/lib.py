@@ -1,0 +1,157 @@
+"""ctypes binding of libdms.so: the C ABI declared in include/dms.h, name for name.
+
+Argument marshalling only: every computation happens in the HIP kernels.
+:func:`load` raises if the library has not been built; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdms.so")
+
+DMS_PAGE_SIZE = 64
+DMS_OK = 0
+DMS_EINVAL = -1
+DMS_EUNSUPPORTED = -2
+DMS_EWORKSPACE = -3
+DMS_EHIP = -4
+DMS_STATUS_POOL_EXHAUSTED = 1
+DMS_STATUS_ROW_OVERFLOW = 2
+DMS_KV_F32 = 0
+DMS_KV_BF16 = 1
+
+# every symbol include/dms.h declares
+EXPORTS = (
+    "dms_version",
+    "dms_strerror",
+    "dms_check_shape",
+    "dms_reset",
+    "dms_append",
+    "dms_compact",
+    "dms_decode_workspace_bytes",
+    "dms_decode_attn",
+    "dms_prefill_attn",
+)
+
+
+class DmsShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("kv_heads", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("max_pages_per_unit", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+    ]
+
+
+class DmsCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("k_pages", ctypes.c_void_p),
+        ("v_pages", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("slot_pos", ctypes.c_void_p),
+        ("slot_alpha", ctypes.c_void_p),
+        ("n_slots", ctypes.c_void_p),
+        ("n_clean", ctypes.c_void_p),
+        ("append_base", ctypes.c_void_p),
+        ("seq_len", ctypes.c_void_p),
+        ("free_list", ctypes.c_void_p),
+        ("free_top", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+    ]
+
+
+class DmsError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed: {code} ({strerror(code)})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libdms.so once; raise if it is missing (build it with __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() first "
+                           "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    SP = ctypes.POINTER(DmsShape)
+    CP = ctypes.POINTER(DmsCacheStruct)
+    sig = {
+        "dms_version": ([], ctypes.c_int),
+        "dms_strerror": ([ctypes.c_int], ctypes.c_char_p),
+        "dms_check_shape": ([SP], ctypes.c_int),
+        "dms_reset": ([SP, CP, P], ctypes.c_int),
+        "dms_append": ([SP, CP, P, P, P, ctypes.c_int32, P], ctypes.c_int),
+        "dms_compact": ([SP, CP, P], ctypes.c_int),
+        "dms_decode_workspace_bytes": ([SP], ctypes.c_size_t),
+        "dms_decode_attn": ([SP, CP, P, P, ctypes.c_float, P, ctypes.c_size_t, P], ctypes.c_int),
+        "dms_prefill_attn": ([SP, P, P, P, P, ctypes.c_int32, ctypes.c_float, P, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().dms_strerror(code).decode()
+
+
+def check(fn: str, code: int) -> None:
+    if code != DMS_OK:
+        raise DmsError(fn, code)
+
+
+def _p(t) -> int | None:
+    """Device pointer of a tensor (None for None)."""
+    return None if t is None else t.data_ptr()
+
+
+def version() -> int:
+    return load().dms_version()
+
+
+def check_shape(shape: DmsShape) -> int:
+    return load().dms_check_shape(ctypes.byref(shape))
+
+
+def decode_workspace_bytes(shape: DmsShape) -> int:
+    return load().dms_decode_workspace_bytes(ctypes.byref(shape))
+
+
+def dms_reset(shape, cache, stream) -> int:
+    return load().dms_reset(ctypes.byref(shape), ctypes.byref(cache), stream)
+
+
+def dms_append(shape, cache, k_new, v_new, logit, n_new, stream) -> int:
+    return load().dms_append(ctypes.byref(shape), ctypes.byref(cache), _p(k_new), _p(v_new),
+                             _p(logit), int(n_new), stream)
+
+
+def dms_compact(shape, cache, stream) -> int:
+    return load().dms_compact(ctypes.byref(shape), ctypes.byref(cache), stream)
+
+
+def dms_decode_attn(shape, cache, q, out, sm_scale, workspace, workspace_bytes, stream) -> int:
+    return load().dms_decode_attn(ctypes.byref(shape), ctypes.byref(cache), _p(q), _p(out),
+                                  float(sm_scale), _p(workspace), int(workspace_bytes), stream)
+
+
+def dms_prefill_attn(shape, q, k, v, logit, seq_len, sm_scale, out, stream) -> int:
+    return load().dms_prefill_attn(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(logit),
+                                   int(seq_len), float(sm_scale), _p(out), stream)

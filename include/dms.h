@@ -1,0 +1,195 @@
+/*
+ * dms.h - C ABI of libdms.so: Dynamic Memory Sparsification (DMS) attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (atlas.scime.ai summary of "Inference-Time Hyper-Scaling with KV
+ * Cache Compression", arXiv 2506.05345, section "Approach"): every KV head
+ * makes a binary keep/evict decision for each token; a token marked for
+ * eviction is removed only after a delay window (16 tokens: same page, table
+ * "Measured effects reported in the paper"); attention reads only what is
+ * retained.  Decode cost is the KV bytes read per step (zhaoyang97 Paper-Notes
+ * page, motivation section: decode is bandwidth bound and reads the whole
+ * cache every step).
+ *
+ * Conventions shared by every call
+ *   - All pointers are device pointers unless stated otherwise.  The library
+ *     allocates no memory, keeps no pointer after a call returns and holds no
+ *     global state: every buffer belongs to the caller.
+ *   - Calls enqueue kernels on `stream` (a hipStream_t; NULL = the default
+ *     stream) and return without synchronising.  Calls on one cache must be
+ *     ordered on one stream; calls on disjoint state may run on any streams.
+ *   - Return value: DMS_OK (0) or a negative DMS_E* code, decided on the host
+ *     before anything is enqueued (DMS_EHIP: a launch failed).
+ *   - Errors found on the device (pool exhausted, page-table row full) do not
+ *     stop the call: the affected unit's write is skipped and a bit is OR-ed
+ *     into the sticky word cache->status, which the caller reads after a
+ *     synchronisation and clears with dms_reset or by writing 0.
+ *
+ * Notation: B sequences, Hkv KV heads, G query heads per KV head (query head
+ * hq reads KV head hq / G), D head dimension, P = 64 slots per page, w the
+ * delay window.  A "unit" is one (sequence b, KV head h) pair, u = b*Hkv + h.
+ */
+#ifndef DMS_H
+#define DMS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DMS_ABI_VERSION 1
+#define DMS_PAGE_SIZE 64
+
+/* host-side return codes */
+#define DMS_OK 0
+#define DMS_EINVAL (-1)       /* null pointer, negative size, window < 1, ... */
+#define DMS_EUNSUPPORTED (-2) /* head_dim, group, dtype or page size not built */
+#define DMS_EWORKSPACE (-3)   /* decode workspace smaller than dms_decode_workspace_bytes */
+#define DMS_EHIP (-4)         /* a HIP launch returned an error */
+
+/* device-side sticky status bits (cache->status) */
+#define DMS_STATUS_POOL_EXHAUSTED 1u /* free pages ran out; that unit's tokens were dropped */
+#define DMS_STATUS_ROW_OVERFLOW 2u   /* a unit needed more than max_pages_per_unit pages */
+
+/* key/value element types */
+#define DMS_KV_F32 0
+#define DMS_KV_BF16 1
+
+typedef struct dms_shape {
+  int32_t batch;              /* B >= 1 */
+  int32_t kv_heads;           /* Hkv >= 1 */
+  int32_t group;              /* G in [1, 16] */
+  int32_t head_dim;           /* D in {64, 128} */
+  int32_t page_size;          /* must be DMS_PAGE_SIZE */
+  int32_t window;             /* w >= 1 (16 on the pages; 1 = evict at once) */
+  int32_t max_pages_per_unit; /* columns of the page table */
+  int32_t num_pages;          /* pages in the shared pool */
+  int32_t kv_dtype;           /* DMS_KV_F32 or DMS_KV_BF16 */
+} dms_shape;
+
+/*
+ * The paged cache.  Every field is a caller-owned device buffer.
+ *   k_pages     [num_pages][P][D]   key rows, one per slot
+ *   v_pages     [num_pages][D][P]   value columns: element (d, slot) of a page
+ *                                   (slots are contiguous for each d)
+ *   page_table  [units][max_pages_per_unit] int32, -1 = no page
+ *   slot_pos    [num_pages][P] int32  sequence position held by each slot
+ *   slot_alpha  [num_pages][P] uint8  1 = marked for eviction
+ *   n_slots     [units] int32  slots in use; slot s lives in page s / P
+ *   n_clean     [units] int32  slots [0, n_clean) hold unmarked tokens only
+ *   append_base [units] int32  first slot of the last append, -1 if refused
+ *   seq_len     [B] int32      tokens appended so far (next position)
+ *   free_list   [num_pages] int32, free_top [1] int32: stack of free pages
+ *   status      [1] uint32     sticky DMS_STATUS_* bits
+ * A unit's slots hold its retained tokens in ascending position order,
+ * followed by tokens appended since its last compaction; a slot is dead when
+ * its token is marked and w or more positions old, and dead slots are skipped
+ * by attention until dms_compact removes them.
+ */
+typedef struct dms_cache {
+  void *k_pages;
+  void *v_pages;
+  int32_t *page_table;
+  int32_t *slot_pos;
+  uint8_t *slot_alpha;
+  int32_t *n_slots;
+  int32_t *n_clean;
+  int32_t *append_base;
+  int32_t *seq_len;
+  int32_t *free_list;
+  int32_t *free_top;
+  uint32_t *status;
+} dms_cache;
+
+/* ABI version (DMS_ABI_VERSION).  Never fails. */
+int dms_version(void);
+
+/* Static text for a DMS_* return code.  Never fails. */
+const char *dms_strerror(int code);
+
+/* Host-only check of a shape: DMS_OK, DMS_EINVAL or DMS_EUNSUPPORTED. */
+int dms_check_shape(const dms_shape *shape);
+
+/*
+ * Empty every unit: page_table = -1, free_list = 0..num_pages-1,
+ * free_top = num_pages, n_slots = n_clean = seq_len = 0, append_base = -1,
+ * status = 0.  Must run once on fresh buffers before any other call.
+ */
+int dms_reset(const dms_shape *shape, const dms_cache *cache, hipStream_t stream);
+
+/*
+ * Decide and append n_new tokens to every unit.
+ * Decision (atlas.scime.ai summary, "Approach"; zhaoyang97 notes, key design
+ * item 2): the inference form of the Gumbel-sigmoid gate, alpha = logit > 0
+ * compared in float32 (NaN and +-0 keep).  Append (notes, motivation: the
+ * cache grows by one entry per token and head): token i of sequence b gets
+ * position seq_len[b] + i and the next free slot of its unit.
+ *   k_new, v_new  [B][n_new][Hkv][D] in kv_dtype (no conversion is done)
+ *   logit         [B][n_new][Hkv] float32
+ *   n_new         >= 0 (0 is a no-op)
+ * Pages come from the free stack; units are served in index order and a
+ * unit whose pages do not fit is refused whole: its tokens are dropped,
+ * append_base[u] = -1 and DMS_STATUS_POOL_EXHAUSTED (or _ROW_OVERFLOW) is
+ * set.  seq_len advances for every sequence either way.
+ */
+int dms_append(const dms_shape *shape, const dms_cache *cache, const void *k_new,
+               const void *v_new, const float *logit, int32_t n_new, hipStream_t stream);
+
+/*
+ * Reclaim evicted slots (atlas.scime.ai summary, "Approach": the eviction is
+ * carried out once the delay window has passed).  For each unit, with
+ * t = seq_len[b] - 1, the slots in [n_clean, n_slots) whose token is marked
+ * and t - pos >= w are removed; the survivors move down in order (stable
+ * stream compaction), whole pages left empty go back on the free stack and
+ * n_slots / n_clean are updated.  Attention results do not depend on when or
+ * whether this runs; memory use and bytes read do.
+ */
+int dms_compact(const dms_shape *shape, const dms_cache *cache, hipStream_t stream);
+
+/*
+ * Bytes of decode workspace for this shape.  0 if the shape is invalid.
+ * The workspace needs no initialisation and holds nothing between calls.
+ */
+size_t dms_decode_workspace_bytes(const dms_shape *shape);
+
+/*
+ * Decode attention over the retained entries (atlas.scime.ai summary,
+ * "Approach"; zhaoyang97 notes, motivation: one query per step reads the
+ * cache).  For query head hq = h*G + g of sequence b, with t = seq_len[b]-1:
+ *   out = sum_j softmax_j(sm_scale * <q, k_j>) v_j over the slots j of unit
+ *   (b, h) that are alive at t (unmarked, or marked and t - pos < w).
+ *   q    [B][Hq][D] in kv_dtype, Hq = Hkv*G
+ *   out  [B][Hq][D] float32
+ * The caller appends token t before this call, so each query sees its own
+ * token.  A unit with no slots gives zeros.  The work of each unit is split
+ * into chunks of whole pages, sized on the device from the live lengths,
+ * and the chunk partials are merged with the log-sum-exp rule.
+ */
+int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *q, float *out,
+                    float sm_scale, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Masked prefill attention over a whole prompt, no cache (the same rule
+ * applied to every query row; atlas.scime.ai summary, "Approach" and
+ * "Measured effects" for the 16-token window).  Row i of query head hq
+ * attends to key j of KV head hq/G iff
+ *   j <= i  and  not (alpha_j and i >= j + w),   alpha_j = logit_j > 0.
+ *   q      [B][S][Hq][D]  kv_dtype (DMS_KV_BF16 only)
+ *   k, v   [B][S][Hkv][D] kv_dtype
+ *   logit  [B][S][Hkv]    float32
+ *   out    [B][S][Hq][D]  float32
+ * Only batch, kv_heads, group, head_dim (128), window and kv_dtype of
+ * `shape` are read.  The cache is filled separately with dms_append.
+ */
+int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const void *v,
+                     const float *logit, int32_t seq_len, float sm_scale, float *out,
+                     hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMS_H */

@@ -204,22 +204,51 @@ class UnitCache:
         if window < 1:
             raise ValueError("window must be >= 1")
         self.window = int(window)
-        self.pos = np.zeros((0,), dtype=np.int64)
-        self.alpha = np.zeros((0,), dtype=bool)
-        self.k = np.zeros((0, head_dim), dtype=dtype)
-        self.v = np.zeros((0, head_dim), dtype=dtype)
-        self.length = 0  # positions consumed by the sequence
+        self._pos = np.zeros((0,), dtype=np.int64)
+        self._alpha = np.zeros((0,), dtype=bool)
+        self._k = np.zeros((0, head_dim), dtype=dtype)
+        self._v = np.zeros((0, head_dim), dtype=dtype)
+        self._pending = []   # appended (pos, alpha, k, v) blocks not yet joined
+        self.length = 0      # positions consumed by the sequence
 
     def append(self, alpha, k, v) -> None:
         """Append n tokens at positions length .. length + n - 1."""
         alpha = np.asarray(alpha, dtype=bool).reshape(-1)
         n = alpha.shape[0]
         pos = np.arange(self.length, self.length + n, dtype=np.int64)
-        self.pos = np.concatenate([self.pos, pos])
-        self.alpha = np.concatenate([self.alpha, alpha])
-        self.k = np.concatenate([self.k, np.asarray(k, dtype=self.k.dtype).reshape(n, -1)])
-        self.v = np.concatenate([self.v, np.asarray(v, dtype=self.v.dtype).reshape(n, -1)])
+        self._pending.append((pos, alpha.copy(),
+                              np.array(k, dtype=self._k.dtype).reshape(n, -1),
+                              np.array(v, dtype=self._v.dtype).reshape(n, -1)))
         self.length += n
+
+    def _join(self) -> None:
+        """Join pending appends onto the slot arrays (storage only, order kept)."""
+        if self._pending:
+            self._pos = np.concatenate([self._pos] + [p[0] for p in self._pending])
+            self._alpha = np.concatenate([self._alpha] + [p[1] for p in self._pending])
+            self._k = np.concatenate([self._k] + [p[2] for p in self._pending])
+            self._v = np.concatenate([self._v] + [p[3] for p in self._pending])
+            self._pending = []
+
+    @property
+    def pos(self) -> np.ndarray:
+        self._join()
+        return self._pos
+
+    @property
+    def alpha(self) -> np.ndarray:
+        self._join()
+        return self._alpha
+
+    @property
+    def k(self) -> np.ndarray:
+        self._join()
+        return self._k
+
+    @property
+    def v(self) -> np.ndarray:
+        self._join()
+        return self._v
 
     def skip(self, n: int) -> None:
         """Advance the position counter by n tokens that were not stored."""
@@ -234,10 +263,10 @@ class UnitCache:
     def compact(self, t: int | None = None) -> None:
         """Drop dead slots, keeping the order of the survivors."""
         keep = self.live(t)
-        self.pos = self.pos[keep]
-        self.alpha = self.alpha[keep]
-        self.k = self.k[keep]
-        self.v = self.v[keep]
+        self._pos = self._pos[keep]
+        self._alpha = self._alpha[keep]
+        self._k = self._k[keep]
+        self._v = self._v[keep]
 
     def attend(self, q, scale: float) -> np.ndarray:
         """Decode output for the G queries q [G, D] at position length - 1."""

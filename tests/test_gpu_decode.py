@@ -1,0 +1,307 @@
+"""GPU parity of the decode path (decide + append, compaction, split-K decode)
+against the float64 oracle, through the C ABI.
+
+Bit-exact: slot order, decisions, retained sets, compacted K/V bytes, page
+accounting.  Within tolerance: attention outputs (1e-5 max-abs for float32
+caches; |o - o_ref| <= 2e-2 + 2e-2 |o_ref| for bfloat16).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from decode_attention_learned_amd import DmsCache, lib
+from harness import (HostModel, check_kv_exact, check_live_sets, check_pages, check_slots_exact,
+                     compare_outputs, export_meta, say, scale_of)
+from oracle import dms_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def _dtype(w):
+    return torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+
+def run_decode(w, dev, *, steps=None, compact_every="default", check_steps=None,
+               max_pages=None, num_pages=None, gen_device="cpu", kv_units=None, window=None,
+               prompt_chunk=None):
+    """Build the prompt, then decode `steps` steps, checking against the oracle mirror.
+
+    Returns (cache, model, list of GPU outputs checked)."""
+    window = w.window if window is None else window
+    steps = w.steps if steps is None else steps
+    every = w.compact_every if compact_every == "default" else compact_every
+    chunk = w.prompt_chunk if prompt_chunk is None else prompt_chunk
+    need = (w.context + steps) // 64 + 3
+    max_pages = need if max_pages is None else max_pages
+    cache = DmsCache(w.batch, w.kv_heads, w.group, w.head_dim, _dtype(w),
+                     num_pages=num_pages or w.units * max_pages, max_pages_per_unit=max_pages,
+                     window=window, device=dev)
+    model = HostModel(w.batch, w.kv_heads, w.group, w.head_dim, window)
+    rates = wl.unit_eviction_rates(w)
+    for ci, start in enumerate(range(0, w.context, chunk)):
+        n = min(chunk, w.context - start)
+        k, v, logit = wl.prompt_chunk_inputs(w, ci, n, device=gen_device, rates=rates)
+        cache.append(k.to(dev), v.to(dev), logit.to(dev))
+        model.append(k.cpu(), v.cpu(), logit.cpu())
+        if every is not None:
+            cache.compact()
+            model.compact()
+    torch.cuda.synchronize()
+    meta = check_slots_exact(cache, model)
+    check_pages(cache, meta)
+    if kv_units:
+        check_kv_exact(cache, model, kv_units)
+    scale = scale_of(w.head_dim)
+    outs = []
+    for step in range(steps):
+        q, k, v, logit = wl.decode_step_inputs(w, step, device=gen_device, rates=rates)
+        cache.append(k.to(dev), v.to(dev), logit.to(dev))
+        model.append(k.cpu(), v.cpu(), logit.cpu())
+        out = cache.decode(q.to(dev))
+        if check_steps is None or step in check_steps:
+            ref = model.decode(q.cpu(), scale)
+            compare_outputs(out.cpu(), ref, w.kv_heads, w.group, _dtype(w), what=f"step {step}")
+            check_live_sets(cache, model)
+            outs.append(out.clone())
+        if every is not None and (step + 1) % every == 0:
+            cache.compact()
+            model.compact()
+            meta = check_slots_exact(cache, model)
+            check_pages(cache, meta)
+    assert cache.status_word() == 0
+    return cache, model, outs
+
+
+def small(name, **kw):
+    base = wl.get(name)
+    d = dict(base.__dict__)
+    d.update(kw)
+    d.pop("extra", None)
+    return wl.Workload(**d)
+
+
+# ---------------------------------------------------------------- tiny float32 workload, every step
+def test_tiny_f32_every_step(gpu):
+    w = wl.get("tiny_f32")
+    say("tiny_f32: 512-token prompt + 64 steps, fp32, G=2, D=64")
+    cache, model, _ = run_decode(w, gpu, kv_units=range(w.units))
+    check_kv_exact(cache, model, range(w.units))
+
+
+def test_tiny_f32_first_token_is_exact(gpu):
+    w = small("tiny_f32", context=0, steps=1)
+    q, k, v, logit = wl.decode_step_inputs(w, 0)
+    cache = DmsCache(1, 2, 2, 64, torch.float32, max_pages_per_unit=2, device=gpu)
+    cache.append(k.to(gpu), v.to(gpu), logit.to(gpu))
+    out = cache.decode(q.to(gpu)).cpu()
+    for h in range(2):
+        for g in range(2):
+            assert torch.equal(out[0, h * 2 + g], v[0, 0, h])
+
+
+# ---------------------------------------------------------------- bf16 shapes, both decode kernels
+@pytest.mark.parametrize("kernel", ["mfma", "generic"])
+@pytest.mark.parametrize("dims", [(3, 2, 5, 128), (2, 3, 4, 64), (1, 1, 16, 128), (2, 1, 1, 64)])
+def test_bf16_small_every_step(gpu, monkeypatch, kernel, dims):
+    b, hkv, g, d = dims
+    monkeypatch.setenv("DMS_DECODE_KERNEL", kernel)
+    w = small("qwen3_8b_cr8", batch=b, kv_heads=hkv, group=g, head_dim=d, context=301,
+              steps=40, evict_rate=0.6, compact_every=7, prompt_chunk=100, seed=77 + d + g)
+    say(f"bf16 {kernel} B={b} Hkv={hkv} G={g} D={d}")
+    cache, model, _ = run_decode(w, gpu, kv_units=range(w.units))
+    check_kv_exact(cache, model, range(w.units))
+
+
+@pytest.mark.parametrize("every", [1, 16, None])
+def test_compaction_schedule_does_not_change_results(gpu, every):
+    w = small("llama1b_cr4", batch=2, context=700, steps=40, prompt_chunk=350, seed=2101)
+    say(f"compaction every {every}")
+    run_decode(w, gpu, compact_every=every)
+
+
+@pytest.mark.parametrize("rate", [0.0, 1.0])
+def test_all_keep_and_all_evict(gpu, rate):
+    w = small("llama1b_cr4", batch=2, kv_heads=2, context=200, steps=20, evict_rate=rate,
+              prompt_chunk=200, seed=2202)
+    cache, model, _ = run_decode(w, gpu)
+    meta = export_meta(cache)
+    n = meta["n_slots"]
+    if rate == 0.0:
+        assert np.all(n == 220)          # nothing leaves
+    else:
+        assert np.all(n <= 16 + 16)      # at most the window plus uncompacted tail
+
+
+def test_all_keep_matches_dense_causal_sdpa(gpu):
+    """Nothing marked: GPU decode equals dense causal attention (torch SDPA on CPU, float64)."""
+    b, hkv, g, d, s = 2, 2, 4, 128, 150
+    w = small("llama1b_cr4", batch=b, kv_heads=hkv, group=g, head_dim=d, context=s - 1, steps=1,
+              evict_rate=0.0, prompt_chunk=200, seed=2303)
+    cache, _, outs = run_decode(w, gpu)
+    rates = wl.unit_eviction_rates(w)
+    kp, vp, _ = wl.prompt_chunk_inputs(w, 0, s - 1, rates=rates)
+    q, kd, vd, _ = wl.decode_step_inputs(w, 0, rates=rates)
+    keys = torch.cat([kp, kd], 1).double()       # [B, S, Hkv, D]
+    vals = torch.cat([vp, vd], 1).double()
+    for bi in range(b):
+        kk = keys[bi].permute(1, 0, 2).repeat_interleave(g, 0)   # [Hq, S, D]
+        vv = vals[bi].permute(1, 0, 2).repeat_interleave(g, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[bi].double()[:, None, :], kk, vv, scale=1 / math.sqrt(d))[:, 0]
+        got = outs[0][bi].cpu().double()
+        assert torch.allclose(got, ref, rtol=2e-2, atol=2e-2)
+
+
+def test_window_one_sees_only_unmarked_and_itself(gpu):
+    w = small("llama1b_cr4", batch=2, kv_heads=2, context=130, steps=10, evict_rate=0.7,
+              prompt_chunk=130, seed=2404)
+    run_decode(w, gpu, window=1)
+
+
+def test_window_larger_than_history(gpu):
+    w = small("llama1b_cr4", batch=1, kv_heads=2, context=20, steps=10, evict_rate=0.9,
+              prompt_chunk=20, seed=2505)
+    run_decode(w, gpu, window=64)
+
+
+def test_determinism_bitwise(gpu):
+    w = small("qwen3_8b_cr8", batch=4, context=1500, steps=3, prompt_chunk=500, seed=3303)
+    _, _, a = run_decode(w, gpu)
+    _, _, b = run_decode(w, gpu)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_empty_unit_gives_zeros(gpu):
+    cache = DmsCache(2, 2, 2, 64, torch.bfloat16, max_pages_per_unit=2, device=gpu)
+    q = torch.randn((2, 4, 64), device=gpu).to(torch.bfloat16)
+    out = cache.decode(q)
+    assert torch.count_nonzero(out) == 0
+
+
+# ---------------------------------------------------------------- device-detected errors
+def test_pool_exhaustion_then_recovery(gpu):
+    """A pool too small for every unit: units past the first that does not fit are refused
+    whole (status bit set, tokens dropped); after compaction frees pages, appends resume."""
+    b, hkv, g, d, win = 1, 4, 2, 64, 16
+    cache = DmsCache(b, hkv, g, d, torch.bfloat16, num_pages=6, max_pages_per_unit=4, window=win,
+                     device=gpu)
+    model = HostModel(b, hkv, g, d, win)
+    w = small("llama1b_cr4", batch=b, kv_heads=hkv, group=g, head_dim=d, evict_rate=1.0, seed=2606)
+    rates = wl.unit_eviction_rates(w)
+    # 100 tokens need 2 pages per unit: units 0..2 fit in 6 pages, unit 3 is refused
+    k, v, logit = wl.prompt_chunk_inputs(w, 0, 100, rates=rates)
+    cache.append(k.to(gpu), v.to(gpu), logit.to(gpu))
+    model.append(k, v, logit, refused={3})
+    torch.cuda.synchronize()
+    assert cache.status_word() & lib.DMS_STATUS_POOL_EXHAUSTED
+    assert int(cache.append_base[3].item()) == -1
+    meta = check_slots_exact(cache, model)
+    check_pages(cache, meta)
+    # everything is marked: compaction keeps the last 16 of each unit and frees a page each
+    cache.compact()
+    model.compact()
+    meta = check_slots_exact(cache, model)
+    check_pages(cache, meta)
+    assert meta["free_top"] == 3
+    cache.status.zero_()
+    q, k, v, logit = wl.decode_step_inputs(w, 0, rates=rates)
+    cache.append(k.to(gpu), v.to(gpu), logit.to(gpu))
+    model.append(k, v, logit)
+    out = cache.decode(q.to(gpu))
+    torch.cuda.synchronize()
+    assert cache.status_word() == 0
+    check_slots_exact(cache, model)
+    compare_outputs(out.cpu(), model.decode(q, scale_of(d)), hkv, g, torch.bfloat16)
+
+
+def test_row_overflow_sets_status(gpu):
+    cache = DmsCache(1, 2, 1, 64, torch.bfloat16, num_pages=64, max_pages_per_unit=2, device=gpu)
+    w = small("llama1b_cr4", batch=1, kv_heads=2, group=1, evict_rate=0.0, seed=2707)
+    # a single append longer than a row is refused on the host
+    k, v, logit = wl.prompt_chunk_inputs(w, 0, 129)
+    with pytest.raises(lib.DmsError):
+        cache.append(k.to(gpu), v.to(gpu), logit.to(gpu))
+    # 100 tokens fit in 2 pages; 100 more would need 4: refused on the device
+    k, v, logit = wl.prompt_chunk_inputs(w, 1, 100)
+    cache.append(k.to(gpu), v.to(gpu), logit.to(gpu))
+    torch.cuda.synchronize()
+    assert cache.status_word() == 0
+    cache.append(k.to(gpu), v.to(gpu), logit.to(gpu))
+    torch.cuda.synchronize()
+    assert cache.status_word() & lib.DMS_STATUS_ROW_OVERFLOW
+    assert cache.n_slots.cpu().tolist() == [100, 100]
+    assert cache.seq_len.cpu().tolist() == [200]
+    assert cache.append_base.cpu().tolist() == [-1, -1]
+    check_pages(cache)
+
+
+# ---------------------------------------------------------------- full-size workloads
+def test_llama1b_cr4_full(gpu):
+    """Llama-3.2-1B shape, B=16, 4096 context, 256 steps: every step checked."""
+    w = wl.get("llama1b_cr4")
+    say("llama1b_cr4 full size")
+    cache, model, _ = run_decode(w, gpu, gen_device=gpu, check_steps=set(range(0, 256, 3)) | {255},
+                                 kv_units=range(0, w.units, 17))
+
+
+def test_qwen3_8b_cr8_full_sampled(gpu):
+    """Qwen3-8B shape, B=64, 32768 context at CR 8: every unit at sampled steps."""
+    w = wl.get("qwen3_8b_cr8")
+    say("qwen3_8b_cr8 full size: building 32768-token context")
+    cache, model, _ = run_decode(w, gpu, steps=17, check_steps={0, 16}, gen_device=gpu,
+                                 max_pages=140, kv_units=range(0, w.units, 97))
+    meta = export_meta(cache)
+    cr = (w.context + 17) * w.units / meta["n_slots"].sum()
+    say(f"realised compression ratio {cr:.2f}")
+    assert 7.0 < cr < 9.0
+
+
+def test_qwen32b_width_ragged_full_sampled(gpu):
+    """Qwen2.5-32B heads (G=5), per-unit Beta(7,1) rates: ragged lengths, every unit."""
+    w = wl.get("qwen32b_width")
+    say("qwen32b_width full size (ragged)")
+    cache, _, _ = run_decode(w, gpu, steps=2, gen_device=gpu, max_pages=516,
+                             num_pages=w.units * 140)
+    n = cache.n_slots.cpu().numpy()
+    say(f"retained per unit: min {n.min()} max {n.max()} mean {n.mean():.0f}")
+    assert n.max() > 4 * n.mean() / 2
+
+
+def test_qwen3_cr1_control_subset(gpu):
+    """CR=1 control (nothing evicted), full shape: retained counts for all units, outputs
+    for 2 sequences x 8 KV heads."""
+    w = wl.get("qwen3_8b_cr1")
+    say("qwen3_8b_cr1 control full size")
+    dev = gpu
+    max_pages = 32768 // 64 + 2
+    cache = DmsCache(w.batch, w.kv_heads, w.group, w.head_dim, torch.bfloat16,
+                     num_pages=w.units * max_pages, max_pages_per_unit=max_pages, device=dev)
+    keep_units = list(range(16))  # sequences 0 and 1
+    keys = {u: [] for u in keep_units}
+    vals = {u: [] for u in keep_units}
+    for ci in range(w.context // w.prompt_chunk):
+        k, v, logit = wl.prompt_chunk_inputs(w, ci, w.prompt_chunk, device=dev)
+        cache.append(k, v, logit)
+        cache.compact()
+        for u in keep_units:
+            b, h = divmod(u, w.kv_heads)
+            keys[u].append(k[b, :, h].float().cpu().numpy())
+            vals[u].append(v[b, :, h].float().cpu().numpy())
+    q, k, v, logit = wl.decode_step_inputs(w, 0, device=dev)
+    cache.append(k, v, logit)
+    out = cache.decode(q).cpu()
+    assert np.all(cache.n_slots.cpu().numpy() == w.context + 1)
+    scale = scale_of(w.head_dim)
+    ref = {}
+    for u in keep_units:
+        b, h = divmod(u, w.kv_heads)
+        kk = np.concatenate(keys[u] + [k[b, :, h].float().cpu().numpy()])
+        vv = np.concatenate(vals[u] + [v[b, :, h].float().cpu().numpy()])
+        qq = q[b, h * w.group:(h + 1) * w.group].double().cpu().numpy()
+        ref[u] = orc.softmax_attention(qq, kk, vv, scale)
+    compare_outputs(out, ref, w.kv_heads, w.group, torch.bfloat16)

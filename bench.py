@@ -1,0 +1,305 @@
+"""DMS decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload qwen3_8b_cr8]
+
+A step is one pass of the whole decode hot path for one attention layer over
+a batch: decide + append the new token of every (sequence, KV head) unit,
+split-K decode attention over the retained entries, and (every
+`compact_every` steps of a cache) compaction.  Steps rotate over independent
+cache replicas so that the working set exceeds the 256 MB last-level cache.
+All inputs are generated on the GPU before the timed region.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+METRIC = "DMS decode-attn tokens/s and KV GB/s (% HBM peak) at CR=8, Qwen3-8B shape"
+PMC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_qwen3_8b_cr8_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "decode_attention_learned_amd", "csrc", "decode_mfma.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def retained_total(cache) -> tuple[int, int]:
+    """(sum over units of |R(t)|, sum of slots in use) from the cache metadata."""
+    import torch
+
+    n = cache.n_slots.long()
+    maxn = int(n.max().item())
+    if maxn == 0:
+        return 0, 0
+    npg = (maxn + 63) // 64
+    pages = cache.page_table[:, :npg].long().clamp(min=0)
+    pos = cache.slot_pos[pages].reshape(cache.units, -1)[:, :maxn]
+    alpha = cache.slot_alpha[pages].reshape(cache.units, -1)[:, :maxn]
+    idx = torch.arange(maxn, device=n.device)[None, :]
+    in_use = idx < n[:, None]
+    t = (cache.seq_len.long() - 1).repeat_interleave(cache.kv_heads)[:, None]
+    live = in_use & ((alpha == 0) | ((t - pos.long()) < cache.window))
+    return int(live.sum().item()), int(in_use.sum().item())
+
+
+def pool_size(w, rates, extra_tokens):
+    """(max_pages_per_unit, num_pages) with room for the expected retained set of
+    every unit (plus 6 sigma), one prompt chunk in flight and `extra_tokens`."""
+    import numpy as np
+
+    keep = 1.0 - rates.reshape(-1)
+    mean = w.context * keep + w.window
+    sd = np.sqrt(w.context * keep * (1.0 - keep))
+    per_unit = np.ceil((mean + 6 * sd + extra_tokens) / 64).astype(np.int64) + w.prompt_chunk // 64 + 2
+    per_unit = np.minimum(per_unit, (w.context + extra_tokens) // 64 + 2)
+    return int(per_unit.max()), int(per_unit.sum())
+
+
+def build_replica(w, r, dev, extra_tokens):
+    import torch
+
+    import workloads as wl
+    from decode_attention_learned_amd import DmsCache
+
+    rates = wl.unit_eviction_rates(w, r)
+    max_pages, num_pages = pool_size(w, rates, extra_tokens)
+    cache = DmsCache(w.batch, w.kv_heads, w.group, w.head_dim, torch.bfloat16,
+                     num_pages=num_pages, max_pages_per_unit=max_pages,
+                     window=w.window, device=dev)
+    for ci, start in enumerate(range(0, w.context, w.prompt_chunk)):
+        n = min(w.prompt_chunk, w.context - start)
+        k, v, logit = wl.prompt_chunk_inputs(w, ci, n, device=dev, replica=r, rates=rates)
+        cache.append(k, v, logit)
+        cache.compact()
+        del k, v, logit
+    torch.cuda.synchronize()
+    if cache.status_word() != 0:
+        raise RuntimeError(f"replica {r}: device status {cache.status_word()} while building")
+    return cache, rates
+
+
+def cpu_baseline(w, seconds: float = 12.0) -> dict:
+    """Time the float64 oracle on host cores on a bounded sample of the same workload:
+    one sequence (all its KV heads) with the full context, then decode steps
+    (append, attend, compaction every `compact_every` steps) until `seconds` pass."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import workloads as wl
+    from oracle import dms_oracle as orc
+
+    sample = wl.Workload(**{**{k: v for k, v in w.__dict__.items() if k != "extra"}, "batch": 1})
+    rates = wl.unit_eviction_rates(sample)
+    units = [orc.UnitCache(sample.window, sample.head_dim, dtype=np.float32)
+             for _ in range(sample.kv_heads)]
+    scale = 1.0 / math.sqrt(sample.head_dim)
+    with threadpool_limits(limits=1):
+        for ci, start in enumerate(range(0, sample.context, sample.prompt_chunk)):
+            n = min(sample.prompt_chunk, sample.context - start)
+            k, v, logit = wl.prompt_chunk_inputs(sample, ci, n, rates=rates)
+            alpha = orc.eviction_decisions(logit.numpy())
+            kf, vf = k.float().numpy(), v.float().numpy()
+            for h, uc in enumerate(units):
+                uc.append(alpha[0, :, h], kf[0, :, h], vf[0, :, h])
+                uc.compact()
+        steps = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            q, k, v, logit = wl.decode_step_inputs(sample, steps, rates=rates)
+            alpha = orc.eviction_decisions(logit.numpy())
+            qf = q.double().numpy()
+            kf, vf = k.float().numpy(), v.float().numpy()
+            for h, uc in enumerate(units):
+                uc.append(alpha[0, :, h], kf[0, :, h], vf[0, :, h])
+                uc.attend(qf[0, h * sample.group:(h + 1) * sample.group], scale)
+                if (steps + 1) % sample.compact_every == 0:
+                    uc.compact()
+            steps += 1
+        dt = time.perf_counter() - t0
+    return {"value": steps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"1 of {w.batch} sequences ({sample.kv_heads} KV heads x G={sample.group}, "
+                      f"context {sample.context}), {steps} decode steps in {dt:.1f} s, "
+                      "float64 NumPy with BLAS limited to 1 thread"}
+
+
+def traffic_from_profile(bytes_alg_per_launch: float):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    or None if there is none or the kernel source changed since it was taken."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    try:
+        rec = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != src_hash(DECODE_SRC):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_8b_cr8")
+    ap.add_argument("--replicas", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the DMS path here runs on a single MI355X "
+              "(no collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = wl.get(args.workload)
+    replicas = args.replicas or w.replicas
+    extra = (args.warmup + args.steps) // replicas + w.compact_every + 64
+
+    log(f"[bench] building {replicas} replica(s) of {w.name}: B={w.batch} Hkv={w.kv_heads} "
+        f"G={w.group} D={w.head_dim} context={w.context}")
+    t_build = time.perf_counter()
+    caches = [build_replica(w, r, dev, extra) for r in range(replicas)]
+    log(f"[bench] built in {time.perf_counter() - t_build:.1f} s")
+
+    total = args.warmup + args.steps
+    per_rep = (total + replicas - 1) // replicas
+    inputs = [[wl.decode_step_inputs(w, j, device=dev, replica=r, rates=caches[r][1])
+               for j in range(per_rep)] for r in range(replicas)]
+    outs = [torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+            for _ in range(replicas)]
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        r = i % replicas
+        j = i // replicas
+        cache = caches[r][0]
+        q, k, v, logit = inputs[r][j]
+        if ev is not None:
+            ev[0].record()
+        cache.append(k, v, logit)
+        if ev is not None:
+            ev[1].record()
+        cache.decode(q, out=outs[r])
+        if ev is not None:
+            ev[2].record()
+        compacted = (j + 1) % w.compact_every == 0
+        if compacted:
+            cache.compact()
+        if ev is not None:
+            ev[3].record()
+        return compacted
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    before = [retained_total(c) for c, _ in caches]
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    flags = []
+    for i in range(args.steps):
+        flags.append(step(args.warmup + i, evs[i]))
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    after = [retained_total(c) for c, _ in caches]
+    status = [c.status_word() for c, _ in caches]
+    if any(status):
+        raise RuntimeError(f"device status words {status}")
+
+    t_append = [e[0].elapsed_time(e[1]) for e in evs]
+    t_decode = [e[1].elapsed_time(e[2]) for e in evs]
+    t_compact = [e[2].elapsed_time(e[3]) for e, f in zip(evs, flags) if f]
+    ms_step = total_ms / args.steps
+    dec_ms = sum(t_decode) / len(t_decode)
+    retained = sum(a[0] + b[0] for a, b in zip(before, after)) / (2 * replicas)
+    in_use = sum(a[1] + b[1] for a, b in zip(before, after)) / (2 * replicas)
+    elem = 2  # bf16
+    bytes_alg = retained * w.head_dim * 2 * elem            # K and V of every retained entry
+    bytes_read = in_use * w.head_dim * 2 * elem             # including dead, not yet compacted slots
+    kv_gbps = bytes_alg / (dec_ms * 1e-3) / 1e9
+    tokens_s = w.batch / (ms_step * 1e-3)
+    cr = (w.context + args.warmup / replicas) * w.units / retained
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.batch, "kv_heads": w.kv_heads, "q_heads": w.q_heads,
+            "head_dim": w.head_dim, "context": w.context, "evict_rate": w.evict_rate,
+            "window": w.window, "compact_every": w.compact_every, "page_size": 64,
+            "replicas": replicas, "kv_dtype": "bf16", "accumulate": "fp32",
+        },
+        "kv_gbps": round(kv_gbps, 1),
+        "hbm_frac": round(kv_gbps / HBM_PEAK_GBPS, 4),
+        "compression_ratio": round(cr, 3),
+        "retained_per_unit": round(retained / w.units, 1),
+        "decode_attn_us": round(dec_ms * 1e3, 2),
+        "append_us": round(1e3 * sum(t_append) / len(t_append), 2),
+        "compact_us": round(1e3 * sum(t_compact) / max(1, len(t_compact)), 2),
+        "dead_slot_overhead": round(bytes_read / bytes_alg - 1.0, 5),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_decode_mfma<128>",
+            "achieved": round(kv_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(kv_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_from_profile(bytes_alg),
+            "algorithmic_bytes_per_launch": int(bytes_alg),
+        },
+    }
+    log(f"[bench] {tokens_s:.0f} tok/s, {ms_step * 1e3:.1f} us/step, decode {dec_ms * 1e3:.1f} us "
+        f"= {kv_gbps:.0f} GB/s ({100 * kv_gbps / HBM_PEAK_GBPS:.1f}% of HBM peak)")
+    del inputs, caches, outs
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the oracle on the host (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,6 +21,23 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
+def page_element_index(head_dim: int):
+    """(key_idx, value_idx), each [64, D] int64: element offset inside a page of
+    (slot, dim), for the fragment-ordered page layout described in include/dms.h.
+    Used only to read a cache back for inspection."""
+    D = head_dim
+    j = torch.arange(PAGE)[:, None]
+    d = torch.arange(D)[None, :]
+    grp, js = j >> 5, j & 31
+    t, r = (js & 7) >> 2, 4 * (js >> 3) + (js & 3)
+    ks, q, e = d >> 5, (d >> 3) & 3, d & 7
+    key = grp * 32 * D + (((t * (D >> 5) + ks) * 4 + q) * 16 + r) * 8 + e
+    qv, ev = js >> 3, js & 7
+    dt, rr = d >> 4, d & 15
+    value = grp * 32 * D + ((dt * 4 + qv) * 16 + rr) * 8 + ev
+    return key, value
+
+
 def _need(t: torch.Tensor, name: str, dtype, shape, device):
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
@@ -58,7 +75,7 @@ class DmsCache:
         dev = self.device
         i32 = dict(dtype=torch.int32, device=dev)
         self.k_pages = torch.zeros((self.num_pages, PAGE, head_dim), dtype=dtype, device=dev)
-        self.v_pages = torch.zeros((self.num_pages, head_dim, PAGE), dtype=dtype, device=dev)
+        self.v_pages = torch.zeros((self.num_pages, PAGE, head_dim), dtype=dtype, device=dev)
         self.page_table = torch.empty((self.units, max_pages_per_unit), **i32)
         self.slot_pos = torch.zeros((self.num_pages, PAGE), **i32)
         self.slot_alpha = torch.zeros((self.num_pages, PAGE), dtype=torch.uint8, device=dev)
@@ -69,10 +86,11 @@ class DmsCache:
         self.free_list = torch.empty((self.num_pages,), **i32)
         self.free_top = torch.empty((1,), **i32)
         self.status = torch.empty((1,), **i32)
+        self.plan = torch.empty((lib.plan_words(self.shape),), **i32)
         self.cache = lib.DmsCacheStruct(*[t.data_ptr() for t in (
             self.k_pages, self.v_pages, self.page_table, self.slot_pos, self.slot_alpha,
             self.n_slots, self.n_clean, self.append_base, self.seq_len, self.free_list,
-            self.free_top, self.status)])
+            self.free_top, self.status, self.plan)])
         self.workspace_bytes = lib.decode_workspace_bytes(self.shape)
         self.workspace = torch.empty((self.workspace_bytes,), dtype=torch.uint8, device=dev)
         self.reset()
@@ -125,8 +143,11 @@ class DmsCache:
         """(k [n, D], v [n, D]) of every slot of `unit`, in slot order, CPU tensors."""
         n = int(self.n_slots[unit].item())
         pages = self.page_table[unit, : (n + PAGE - 1) // PAGE].long()
-        k = self.k_pages[pages].reshape(-1, self.head_dim)[:n].cpu()
-        v = self.v_pages[pages].transpose(1, 2).reshape(-1, self.head_dim)[:n].cpu()
+        kidx, vidx = page_element_index(self.head_dim)
+        flat_k = self.k_pages.view(self.num_pages, -1)[pages]
+        flat_v = self.v_pages.view(self.num_pages, -1)[pages]
+        k = flat_k[:, kidx.reshape(-1).to(self.device)].reshape(-1, self.head_dim)[:n].cpu()
+        v = flat_v[:, vidx.reshape(-1).to(self.device)].reshape(-1, self.head_dim)[:n].cpu()
         return k, v
 
 

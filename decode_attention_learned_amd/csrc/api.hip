@@ -12,9 +12,11 @@ int check_cache(const dms_shape *s, const dms_cache *c) {
   if (!c) return DMS_EINVAL;
   if (!c->k_pages || !c->v_pages || !c->page_table || !c->slot_pos || !c->slot_alpha ||
       !c->n_slots || !c->n_clean || !c->append_base || !c->seq_len || !c->free_list ||
-      !c->free_top || !c->status)
+      !c->free_top || !c->status || !c->plan)
     return DMS_EINVAL;
-  if (!aligned16(c->k_pages) || !aligned16(c->v_pages)) return DMS_EINVAL;
+  if (!aligned16(c->k_pages) || !aligned16(c->v_pages) || !aligned16(c->slot_pos) ||
+      !aligned16(c->slot_alpha))
+    return DMS_EINVAL;
   (void)s;
   return DMS_OK;
 }
@@ -77,6 +79,11 @@ int dms_compact(const dms_shape *shape, const dms_cache *cache, hipStream_t stre
   if (rc) return rc;
   if ((rc = check_cache(shape, cache))) return rc;
   return from_hip(dms::launch_compact(*shape, *cache, stream));
+}
+
+size_t dms_plan_words(const dms_shape *shape) {
+  if (dms_check_shape(shape) != DMS_OK) return 0;
+  return dms::plan_layout(dms::units_of(*shape)).words;
 }
 
 size_t dms_decode_workspace_bytes(const dms_shape *shape) {

@@ -6,11 +6,9 @@
 // reported in the paper" (16-token window).  The decision here is the
 // inference form of the Gumbel-sigmoid gate: alpha = logit > 0.
 //
-// Layout (one page = 64 slots of one unit):
-//   k_pages [page][slot][D]   key rows
-//   v_pages [page][D][slot]   value columns, so that a page holds, for each
-//                             d, 64 consecutive slots (the decode kernels read
-//                             values slot-contiguous)
+// Layout: one page = 64 slots of one unit, 64*D key elements in k_pages and
+// 64*D value elements in v_pages, ordered by key_index / value_index
+// (dms_internal.h) so that the decode kernel reads whole operand fragments.
 #include "dms_internal.h"
 
 namespace dms {
@@ -60,6 +58,17 @@ __global__ void k_reset(int units, int maxp, int num_pages, int batch, int32_t *
   }
 }
 
+// standalone planner (after reset and compaction)
+__global__ __launch_bounds__(kPlanThreads) void k_plan(int units, const int32_t *n_slots,
+                                                       int32_t *plan) {
+  build_plan(units, n_slots, plan);
+}
+
+hipError_t launch_plan(const dms_shape &s, const dms_cache &c, hipStream_t st) {
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, st, units_of(s), c.n_slots, c.plan);
+  return hipGetLastError();
+}
+
 hipError_t launch_reset(const dms_shape &s, const dms_cache &c, hipStream_t st) {
   const int units = units_of(s);
   const long work = std::max(long(units) * s.max_pages_per_unit, long(s.num_pages));
@@ -67,7 +76,8 @@ hipError_t launch_reset(const dms_shape &s, const dms_cache &c, hipStream_t st) 
   hipLaunchKernelGGL(k_reset, dim3(std::max(blocks, 1)), dim3(256), 0, st, units,
                      s.max_pages_per_unit, s.num_pages, s.batch, c.page_table, c.free_list,
                      c.free_top, c.n_slots, c.n_clean, c.append_base, c.seq_len, c.status);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : launch_plan(s, c, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -86,7 +96,8 @@ constexpr int kAllocThreads = 1024;
 __global__ __launch_bounds__(kAllocThreads) void k_append_alloc(
     int units, int batch, int maxp, int n_new, int32_t *page_table, int32_t *n_slots,
     int32_t *append_base, int32_t *seq_len, const int32_t *free_list, int32_t *free_top,
-    uint32_t *status) {
+    uint32_t *status, int32_t *plan) {
+  static_assert(kAllocThreads == kPlanThreads, "the planner runs in this workgroup");
   __shared__ int s_tmp[kAllocThreads / kWave];
   __shared__ int s_taken;
   __shared__ uint32_t s_flags;
@@ -131,6 +142,9 @@ __global__ __launch_bounds__(kAllocThreads) void k_append_alloc(
     *free_top = F - s_taken;
     if (s_flags) atomicOr(status, s_flags);
   }
+  // n_slots changed: rebuild the decode split plan (each thread re-reads only
+  // the entries it wrote above)
+  build_plan(units, n_slots, plan);
 }
 
 // ---------------------------------------------------------------------------
@@ -170,16 +184,18 @@ __global__ __launch_bounds__(256) void k_append_write(
   }
   __syncthreads();
 
-  // key rows: straight 16-byte copies
-  const int cpr = D * int(sizeof(E)) / 16;
+  // keys: 16-byte pieces (8 or 4 consecutive dims are contiguous in a page)
+  constexpr int CE = 16 / int(sizeof(E));  // elements per 16-byte piece
+  const int cpr = D / CE;
   for (int x = tid; x < nt * cpr; x += blockDim.x) {
     const int i = x / cpr, c = x % cpr;
     const size_t tok = (size_t(b) * n_new + i0 + i) * hkv + h;
-    const uint4 *src = reinterpret_cast<const uint4 *>(k_new + tok * D) + c;
-    uint4 *dst = reinterpret_cast<uint4 *>(k_pages + (size_t(s_page[i]) * kPage + s_off[i]) * D) + c;
+    const uint4 *src = reinterpret_cast<const uint4 *>(k_new + tok * D + c * CE);
+    uint4 *dst = reinterpret_cast<uint4 *>(k_pages + size_t(s_page[i]) * kPage * D +
+                                           key_index(s_off[i], c * CE, D));
     *dst = *src;
   }
-  // value rows -> columns of the page, through LDS
+  // values: through LDS, then stored with consecutive threads on consecutive slots
   for (int x = tid; x < nt * D; x += blockDim.x) {
     const int i = x / D, d = x % D;
     const size_t tok = (size_t(b) * n_new + i0 + i) * hkv + h;
@@ -188,7 +204,7 @@ __global__ __launch_bounds__(256) void k_append_write(
   __syncthreads();
   for (int x = tid; x < nt * D; x += blockDim.x) {
     const int d = x / nt, i = x % nt;
-    v_pages[(size_t(s_page[i]) * D + d) * kPage + s_off[i]] = s_v[i * (D + 1) + d];
+    v_pages[size_t(s_page[i]) * kPage * D + value_index(s_off[i], d, D)] = s_v[i * (D + 1) + d];
   }
 }
 
@@ -197,7 +213,7 @@ hipError_t launch_append(const dms_shape &s, const dms_cache &c, const void *k_n
   const int units = units_of(s);
   hipLaunchKernelGGL(k_append_alloc, dim3(1), dim3(kAllocThreads), 0, st, units, s.batch,
                      s.max_pages_per_unit, n_new, c.page_table, c.n_slots, c.append_base,
-                     c.seq_len, c.free_list, c.free_top, c.status);
+                     c.seq_len, c.free_list, c.free_top, c.status, c.plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(units, (n_new + kPage - 1) / kPage);
@@ -239,8 +255,9 @@ __global__ __launch_bounds__(256) void k_compact(
     int32_t *__restrict__ n_clean, E *__restrict__ k_pages, E *__restrict__ v_pages,
     int32_t *__restrict__ slot_pos, uint8_t *__restrict__ slot_alpha,
     int32_t *__restrict__ free_list, int32_t *__restrict__ free_top) {
-  constexpr int CPR = D * int(sizeof(E)) / 16;      // 16-byte chunks per key row
-  constexpr int SPC = 16 / int(sizeof(E));          // slots per 16-byte value chunk
+  constexpr int CE = 16 / int(sizeof(E));           // elements per 16-byte piece
+  constexpr int CPR = D / CE;                       // key pieces per slot
+  constexpr int SPC = CE;                           // slots per 16-byte value piece
   constexpr int KCH = kPage * CPR / 256;            // key chunks per thread
   constexpr int VCH = D * (kPage / SPC) / 256;      // value chunks per thread
   static_assert(KCH >= 1 && VCH >= 1, "tile too small for 256 threads");
@@ -301,13 +318,13 @@ __global__ __launch_bounds__(256) void k_compact(
       const int j = x / CPR, c = x % CPR;
       const int d = s_dst[j];
       if (d >= 0 && d != P * kPage + j)
-        kv[r] = *(reinterpret_cast<const uint4 *>(k_pages + (size_t(page) * kPage + j) * D) + c);
+        kv[r] = *reinterpret_cast<const uint4 *>(k_pages + size_t(page) * kPage * D + key_index(j, c * CE, D));
     }
 #pragma unroll
     for (int r = 0; r < VCH; ++r) {
       const int x = tid + r * 256;
       const int d = x / (kPage / SPC), jc = x % (kPage / SPC);
-      vv[r] = *(reinterpret_cast<const uint4 *>(v_pages + (size_t(page) * D + d) * kPage) + jc);
+      vv[r] = *reinterpret_cast<const uint4 *>(v_pages + size_t(page) * kPage * D + value_index(jc * SPC, d, D));
     }
     if (tid < kPage && s_dst[tid] >= 0) {
       mpos = slot_pos[size_t(page) * kPage + tid];
@@ -323,7 +340,7 @@ __global__ __launch_bounds__(256) void k_compact(
       const int d = s_dst[j];
       if (d >= 0 && d != P * kPage + j) {
         const int dpage = row[d / kPage];
-        *(reinterpret_cast<uint4 *>(k_pages + (size_t(dpage) * kPage + d % kPage) * D) + c) = kv[r];
+        *reinterpret_cast<uint4 *>(k_pages + size_t(dpage) * kPage * D + key_index(d % kPage, c * CE, D)) = kv[r];
       }
     }
 #pragma unroll
@@ -337,7 +354,7 @@ __global__ __launch_bounds__(256) void k_compact(
         const int dst = s_dst[j];
         if (dst >= 0 && dst != P * kPage + j) {
           const int dpage = row[dst / kPage];
-          v_pages[(size_t(dpage) * D + d) * kPage + dst % kPage] = el[e];
+          v_pages[size_t(dpage) * kPage * D + value_index(dst % kPage, d, D)] = el[e];
         }
       }
     }
@@ -382,7 +399,8 @@ hipError_t launch_compact(const dms_shape &s, const dms_cache &c, hipStream_t st
   else if (bf && s.head_dim == 128) launch_compact_t<uint16_t, 128>(s, c, st);
   else if (!bf && s.head_dim == 64) launch_compact_t<uint32_t, 64>(s, c, st);
   else launch_compact_t<uint32_t, 128>(s, c, st);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : launch_plan(s, c, st);
 }
 
 }  // namespace dms

@@ -1,5 +1,5 @@
-// Decode attention over the retained entries: split plan, split-K kernels,
-// log-sum-exp merge.
+// Decode attention over the retained entries: generic split-K kernel and the
+// launch path shared with the MFMA kernel.
 //
 // Method: atlas.scime.ai summary of "Inference-Time Hyper-Scaling with KV
 // Cache Compression", section "Approach": attention reads only the entries a
@@ -12,75 +12,14 @@
 // over the slots j of unit (b, h) alive at t.  A slot below n_clean is alive
 // by construction; above it, alive iff !alpha or t - pos < w.
 //
-// Split-K: the plan kernel cuts each unit's slot list into chunks of C slots
-// (C a multiple of the page size, chosen from the total live length so that
-// about kTargetChunks chunks exist), each chunk produces (m, l, o) per head,
-// and the merge kernel combines them:
-//   M = max_c m_c,  L = sum_c l_c e^(m_c - M),  out = sum_c o_c e^(m_c - M) / L.
-#include "dms_internal.h"
+// Split-K: the plan (kept in cache state, see build_plan) cuts each unit's
+// slot list into chunks of C slots; each chunk produces (m, l, o) per head and
+// a second, small kernel merges the chunks of units that have more than one.  Scores are
+// kept in log2 units (scale * log2 e folded into the score) so that every
+// exponential is exp2.
+#include "decode_common.h"
 
 namespace dms {
-
-// ---------------------------------------------------------------------------
-// plan (one workgroup)
-// ---------------------------------------------------------------------------
-constexpr int kPlanThreads = 1024;
-
-__global__ __launch_bounds__(kPlanThreads) void k_decode_plan(int units,
-                                                              const int32_t *__restrict__ n_slots,
-                                                              int32_t *__restrict__ hdr,
-                                                              int32_t *__restrict__ first_chunk,
-                                                              int32_t *__restrict__ chunk_unit) {
-  __shared__ long long s_total;
-  __shared__ int s_tmp[kPlanThreads / kWave];
-  if (threadIdx.x == 0) s_total = 0;
-  __syncthreads();
-  long long part = 0;
-  for (int u = threadIdx.x; u < units; u += kPlanThreads) part += n_slots[u];
-  // wave reduce then one atomic per wave
-  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, kWave);
-  if (lane_id() == 0) atomicAdd(reinterpret_cast<unsigned long long *>(&s_total),
-                                (unsigned long long)part);
-  __syncthreads();
-  const long long total = s_total;
-  const long long per = (total + (long long)kPage * kTargetChunks - 1) / ((long long)kPage * kTargetChunks);
-  const int C = kPage * int(per < 1 ? 1 : per);
-
-  int carry = 0;
-  for (int base = 0; base < units; base += kPlanThreads) {
-    const int u = base + threadIdx.x;
-    int nch = 0;
-    if (u < units) {
-      const int n = n_slots[u];
-      nch = n > 0 ? (n + C - 1) / C : 1;
-    }
-    // block inclusive scan
-    const int w = threadIdx.x / kWave, l = lane_id();
-    int incl = wave_inclusive_scan(nch);
-    if (l == kWave - 1) s_tmp[w] = incl;
-    __syncthreads();
-    if (w == 0) {
-      int v = (l < kPlanThreads / kWave) ? s_tmp[l] : 0;
-      v = wave_inclusive_scan(v);
-      if (l < kPlanThreads / kWave) s_tmp[l] = v;
-    }
-    __syncthreads();
-    incl += (w > 0 ? s_tmp[w - 1] : 0) + carry;
-    const int blk_total = s_tmp[kPlanThreads / kWave - 1];
-    __syncthreads();
-    if (u < units) {
-      const int first = incl - nch;
-      first_chunk[u] = first;
-      for (int i = 0; i < nch; ++i) chunk_unit[first + i] = u;
-    }
-    carry += blk_total;
-  }
-  if (threadIdx.x == 0) {
-    first_chunk[units] = carry;
-    hdr[0] = carry;
-    hdr[1] = C;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // generic split-K decode (VALU, float32 arithmetic, either element type)
@@ -100,27 +39,20 @@ __device__ __forceinline__ float load_elem<uint32_t>(const uint32_t *p) { return
 
 template <typename E, int D, int G>
 __global__ __launch_bounds__(256) void k_decode_generic(
-    int hkv, int window, int maxp, float scale_log2, const E *__restrict__ q,
+    int units, int hkv, int window, int maxp, float scale_log2, const E *__restrict__ q,
     const E *__restrict__ k_pages, const E *__restrict__ v_pages,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ slot_pos,
     const uint8_t *__restrict__ slot_alpha, const int32_t *__restrict__ n_slots,
     const int32_t *__restrict__ n_clean_arr, const int32_t *__restrict__ seq_len,
-    const int32_t *__restrict__ hdr, const int32_t *__restrict__ first_chunk,
-    const int32_t *__restrict__ chunk_unit, float2 *__restrict__ part_ml,
-    float *__restrict__ part_o, float *__restrict__ out) {
+    int32_t *__restrict__ plan, float2 *__restrict__ part_ml, float *__restrict__ part_o,
+    float *__restrict__ out) {
   constexpr int OPT = (G * D + 255) / 256;  // outputs per thread
+  const PlanLayout L = plan_layout(units);
   const int c = blockIdx.x;
-  if (c >= hdr[0]) return;
-  const int C = hdr[1];
-  const int u = chunk_unit[c];
-  const int b = u / hkv, h = u % hkv;
-  const int first = first_chunk[u];
-  const int nch = first_chunk[u + 1] - first;
-  const int n = n_slots[u];
-  const int s_begin = (c - first) * C;
-  const int s_end = min(n, s_begin + C);
-  const int t = seq_len[b] - 1;
-  const int nclean = n_clean_arr[u];
+  ChunkInfo ci;
+  if (!locate_chunk(c, hkv, plan, n_slots, n_clean_arr, seq_len, L, ci)) return;
+  const int u = ci.unit, b = ci.b, h = ci.h;
+  const int s_begin = ci.s_begin, s_end = ci.s_end, t = ci.t, nclean = ci.nclean;
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
 
   __shared__ float s_q[G][D];
@@ -148,11 +80,11 @@ __global__ __launch_bounds__(256) void k_decode_generic(
     const int nt = min(kGenTile, s_end - s0);
     for (int x = tid; x < kGenTile * D; x += 256) {
       const int j = x / D, d = x % D;
-      s_k[j][d] = j < nt ? load_elem<E>(k_pages + (size_t(page) * kPage + off0 + j) * D + d) : 0.f;
+      s_k[j][d] = j < nt ? load_elem<E>(k_pages + size_t(page) * kPage * D + key_index(off0 + j, d, D)) : 0.f;
     }
     for (int x = tid; x < D * kGenTile; x += 256) {
       const int d = x / kGenTile, j = x % kGenTile;
-      s_v[d][j] = j < nt ? load_elem<E>(v_pages + (size_t(page) * D + d) * kPage + off0 + j) : 0.f;
+      s_v[d][j] = j < nt ? load_elem<E>(v_pages + size_t(page) * kPage * D + value_index(off0 + j, d, D)) : 0.f;
     }
     __syncthreads();
     for (int x = tid; x < G * kGenTile; x += 256) {
@@ -207,55 +139,42 @@ __global__ __launch_bounds__(256) void k_decode_generic(
     __syncthreads();
   }
 
-  if (nch == 1) {
+  if (ci.nch == 1) {
 #pragma unroll
     for (int r = 0; r < OPT; ++r) {
       const int x = tid + r * 256;
       if (x < G * D) {
-        const int g = x / D, d = x % D;
+        const int g = x / D;
         const float l = s_l[g];
-        out[(size_t(b) * hkv * G + h * G + g) * D + d] = l > 0.f ? acc[r] / l : 0.f;
+        out[size_t(u) * G * D + x] = l > 0.f ? acc[r] / l : 0.f;
       }
     }
-  } else {
-#pragma unroll
-    for (int r = 0; r < OPT; ++r) {
-      const int x = tid + r * 256;
-      if (x < G * D) part_o[size_t(c) * G * D + x] = acc[r];
-    }
-    if (tid < G) part_ml[size_t(c) * G + tid] = make_float2(s_m[tid], s_l[tid]);
+    return;
   }
+#pragma unroll
+  for (int r = 0; r < OPT; ++r) {
+    const int x = tid + r * 256;
+    if (x < G * D) part_o[size_t(c) * G * D + x] = acc[r];
+  }
+  if (tid < G) part_ml[size_t(c) * G + tid] = make_float2(s_m[tid], s_l[tid]);
 }
 
 // ---------------------------------------------------------------------------
-// merge: one workgroup per unit with more than one chunk
+// merge: one workgroup per unit; units with a single chunk were finished by
+// the decode kernel.  A separate launch, so the partials of every chunk are
+// visible without device-scope fences inside the decode kernel.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_decode_merge(int hkv, int G, int D,
-                                                      const int32_t *__restrict__ first_chunk,
+__global__ __launch_bounds__(256) void k_decode_merge(int units, int G, int D,
+                                                      const int32_t *__restrict__ plan,
                                                       const float2 *__restrict__ part_ml,
                                                       const float *__restrict__ part_o,
                                                       float *__restrict__ out) {
+  const PlanLayout L = plan_layout(units);
   const int u = blockIdx.x;
-  const int first = first_chunk[u];
-  const int nch = first_chunk[u + 1] - first;
+  const int first = plan[L.first_chunk + u];
+  const int nch = plan[L.first_chunk + u + 1] - first;
   if (nch <= 1) return;
-  const int b = u / hkv, h = u % hkv;
-  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
-    const int g = x / D;
-    float M = -INFINITY;
-    for (int i = 0; i < nch; ++i) M = fmaxf(M, part_ml[size_t(first + i) * G + g].x);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int i = 0; i < nch; ++i) {
-        const float2 ml = part_ml[size_t(first + i) * G + g];
-        if (ml.x == -INFINITY) continue;
-        const float w = exp2f(ml.x - M);
-        L = fmaf(ml.y, w, L);
-        O = fmaf(part_o[size_t(first + i) * G * D + x], w, O);
-      }
-    }
-    out[(size_t(b) * hkv * G + h * G) * D + x] = L > 0.f ? O / L : 0.f;
-  }
+  merge_chunks(u, first, nch, G, D, part_ml, part_o, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -264,12 +183,11 @@ __global__ __launch_bounds__(256) void k_decode_merge(int hkv, int G, int D,
 template <typename E, int D, int G>
 static void launch_generic_t(const dms_shape &s, const dms_cache &c, const E *q, float *out,
                              float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st) {
-  hipLaunchKernelGGL((k_decode_generic<E, D, G>), dim3(w.max_chunks), dim3(256), 0, st, s.kv_heads,
+  hipLaunchKernelGGL((k_decode_generic<E, D, G>), dim3(w.max_chunks), dim3(256), 0, st,
+                     units_of(s), s.kv_heads,
                      s.window, s.max_pages_per_unit, scale_log2, q, static_cast<const E *>(c.k_pages),
                      static_cast<const E *>(c.v_pages), c.page_table, c.slot_pos, c.slot_alpha,
-                     c.n_slots, c.n_clean, c.seq_len, reinterpret_cast<const int32_t *>(ws + w.hdr),
-                     reinterpret_cast<const int32_t *>(ws + w.first_chunk),
-                     reinterpret_cast<const int32_t *>(ws + w.chunk_unit),
+                     c.n_slots, c.n_clean, c.seq_len, c.plan,
                      reinterpret_cast<float2 *>(ws + w.part_ml), reinterpret_cast<float *>(ws + w.part_o),
                      out);
 }
@@ -289,17 +207,12 @@ static bool dispatch_group(const dms_shape &s, const dms_cache &c, const E *q, f
 bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                         float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st);
 
+// The decode grid has one workgroup per possible chunk (units +
+// kTargetChunks); workgroups past the plan's chunk count exit at once.
 hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                          float sm_scale, void *wsv, hipStream_t st) {
-  const int units = units_of(s);
-  const DecodeWorkspace w = decode_workspace_layout(units, s.group, s.head_dim);
+  const DecodeWorkspace w = decode_workspace_layout(units_of(s), s.group, s.head_dim);
   char *ws = static_cast<char *>(wsv);
-  hipLaunchKernelGGL(k_decode_plan, dim3(1), dim3(kPlanThreads), 0, st, units, c.n_slots,
-                     reinterpret_cast<int32_t *>(ws + w.hdr),
-                     reinterpret_cast<int32_t *>(ws + w.first_chunk),
-                     reinterpret_cast<int32_t *>(ws + w.chunk_unit));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const float scale_log2 = sm_scale * 1.4426950408889634f;  // exp(x) = exp2(x * log2 e)
   bool done = false;
   if (s.kv_dtype == DMS_KV_BF16) {
@@ -314,11 +227,10 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
                : dispatch_group<uint32_t, 128>(s, c, static_cast<const uint32_t *>(q), out, scale_log2, w, ws, st);
   }
   if (!done) return hipErrorInvalidValue;
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_decode_merge, dim3(units), dim3(256), 0, st, s.kv_heads, s.group, s.head_dim,
-                     reinterpret_cast<const int32_t *>(ws + w.first_chunk),
-                     reinterpret_cast<const float2 *>(ws + w.part_ml),
+  hipLaunchKernelGGL(k_decode_merge, dim3(units_of(s)), dim3(256), 0, st, units_of(s), s.group,
+                     s.head_dim, c.plan, reinterpret_cast<const float2 *>(ws + w.part_ml),
                      reinterpret_cast<const float *>(ws + w.part_o), out);
   return hipGetLastError();
 }

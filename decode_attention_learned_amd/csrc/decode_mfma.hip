@@ -19,10 +19,11 @@
 //   tile 0 row 4a + r -> slot 8a + r,   tile 1 row 4a + r -> slot 8a + 4 + r,
 // so that after the QK products lane l holds the scores of head l % 16 for the
 // eight consecutive slots 8q .. 8q + 7.  Those are exactly the eight k values
-// it must supply to the PV product, and its V^T operand is then one 16-byte
-// load from the page's value column block (v_pages keeps slots contiguous per
-// d).  No data moves between lanes except the two shuffles of the row max.
-#include "dms_internal.h"
+// it must supply to the PV product.  The page layout (key_index, value_index)
+// stores every operand fragment as one contiguous 1 KB block, so each operand
+// is one fully coalesced 16-byte-per-lane load.  No data moves between lanes
+// except the two shuffles of the row max.
+#include "decode_common.h"
 
 namespace dms {
 
@@ -31,6 +32,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaWaves = 4;
 constexpr int kGroup = 32;  // slots per group (half a page)
+constexpr int kMaxChunkPages = 1024;  // page ids staged in LDS per chunk
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
@@ -45,36 +47,39 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_decode_mfma(
-    int hkv, int G, int window, int maxp, float scale_log2, const uint16_t *__restrict__ q,
-    const uint16_t *__restrict__ k_pages, const uint16_t *__restrict__ v_pages,
-    const int32_t *__restrict__ page_table, const int32_t *__restrict__ slot_pos,
-    const uint8_t *__restrict__ slot_alpha, const int32_t *__restrict__ n_slots,
-    const int32_t *__restrict__ n_clean_arr, const int32_t *__restrict__ seq_len,
-    const int32_t *__restrict__ hdr, const int32_t *__restrict__ first_chunk,
-    const int32_t *__restrict__ chunk_unit, float2 *__restrict__ part_ml,
-    float *__restrict__ part_o, float *__restrict__ out) {
+__global__ __launch_bounds__(256, 2) void k_decode_mfma(
+    int units, int hkv, int G, int window, int maxp, float scale_log2,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pages,
+    const uint16_t *__restrict__ v_pages, const int32_t *__restrict__ page_table,
+    const int32_t *__restrict__ slot_pos, const uint8_t *__restrict__ slot_alpha,
+    const int32_t *__restrict__ n_slots, const int32_t *__restrict__ n_clean_arr,
+    const int32_t *__restrict__ seq_len, int32_t *__restrict__ plan,
+    float2 *__restrict__ part_ml, float *__restrict__ part_o, float *__restrict__ out) {
   constexpr int KSTEPS = D / 32;  // QK products per 16-slot tile
   constexpr int DTILES = D / 16;  // PV products per group
+  const PlanLayout L = plan_layout(units);
   const int c = blockIdx.x;
-  if (c >= hdr[0]) return;
-  const int C = hdr[1];
-  const int u = chunk_unit[c];
-  const int b = u / hkv, h = u % hkv;
-  const int first = first_chunk[u];
-  const int nch = first_chunk[u + 1] - first;
-  const int n = n_slots[u];
-  const int s_begin = (c - first) * C;
-  const int s_end = min(n, s_begin + C);
-  const int t = seq_len[b] - 1;
-  const int nclean = n_clean_arr[u];
+  ChunkInfo ci;
+  if (!locate_chunk(c, hkv, plan, n_slots, n_clean_arr, seq_len, L, ci)) return;
+  const int u = ci.unit, b = ci.b, h = ci.h;
+  const int s_begin = ci.s_begin, s_end = ci.s_end, t = ci.t, nclean = ci.nclean;
   const int lim = min(nclean, s_end);  // slots below lim need no liveness test
   const int32_t *row = page_table + size_t(u) * maxp;
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = lane_id();
   const int col = lane & 15;  // head index in B and C operands, row index in A
   const int quad = lane >> 4;
+
+  // page ids of this chunk, staged once in LDS (chunks start on a page boundary)
+  __shared__ int s_pages[kMaxChunkPages];
+  const int p_first = s_begin / kPage;
+  const int npages = (s_end - s_begin + kPage - 1) / kPage;
+  const bool staged = npages <= kMaxChunkPages;
+  if (staged)
+    for (int i = tid; i < npages; i += 256) s_pages[i] = row[p_first + i];
+  __syncthreads();
 
   // Q^T operand: head `col`, dims ks*32 + quad*8 .. +8; heads >= G are zero
   uint4 qb[KSTEPS];
@@ -85,8 +90,6 @@ __global__ __launch_bounds__(256) void k_decode_mfma(
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qb[ks] = ld16(qp + ks * 32);
   }
-  const int krow0 = 8 * (col >> 2) + (col & 3);  // slot of A row `col` in tile 0
-  const int krow1 = krow0 + 4;                   // ... in tile 1
 
   floatx4 o[DTILES];
 #pragma unroll
@@ -94,27 +97,38 @@ __global__ __launch_bounds__(256) void k_decode_mfma(
   float m_run = -INFINITY, l_run = 0.f;
 
   const int ngroups = (s_end - s_begin + kGroup - 1) / kGroup;
-  for (int gi = wave; gi < ngroups; gi += kMfmaWaves) {
-    const int gs = s_begin + gi * kGroup;
-    const int page = row[gs / kPage];
-    const int poff = gs % kPage;
-    const uint16_t *kp = k_pages + (size_t(page) * kPage + poff) * D + quad * 8;
-    const uint16_t *vp = v_pages + size_t(page) * D * kPage + poff + quad * 8;
 
-    uint4 ka0[KSTEPS], ka1[KSTEPS], va[DTILES];
+  // operand registers of one group; two sets alternate so that the loads of
+  // the next group are in flight while the current one is computed
+  struct Regs {
+    uint4 k0[KSTEPS], k1[KSTEPS], v[DTILES];
+    int page;
+  };
+  // Every fragment is a contiguous 1 KB block of the group: lane l reads the
+  // 16 bytes at l*8 elements (page layout: key_index / value_index).
+  auto load_group = [&](Regs &r, int gi) {
+    const int pi = (gi * kGroup) / kPage;
+    r.page = __builtin_amdgcn_readfirstlane(staged ? s_pages[pi] : row[p_first + pi]);
+    const size_t base = size_t(r.page) * kPage * D + size_t((gi * kGroup) % kPage) * D + lane * 8;
+    const uint16_t *kp = k_pages + base;
+    const uint16_t *vp = v_pages + base;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      ka0[ks] = ld16(kp + krow0 * D + ks * 32);
-      ka1[ks] = ld16(kp + krow1 * D + ks * 32);
+      r.k0[ks] = ld16(kp + ks * 512);
+      r.k1[ks] = ld16(kp + (KSTEPS + ks) * 512);
     }
 #pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) va[dt] = ld16(vp + (dt * 16 + col) * kPage);
+    for (int dt = 0; dt < DTILES; ++dt) r.v[dt] = ld16(vp + dt * 512);
+  };
 
+  auto process = [&](Regs &r, int gi) {
+    const int gs = s_begin + gi * kGroup;
+    const int poff = gs % kPage;
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      s0 = mfma_bf16(ka0[ks], qb[ks], s0);
-      s1 = mfma_bf16(ka1[ks], qb[ks], s1);
+      s0 = mfma_bf16(r.k0[ks], qb[ks], s0);
+      s1 = mfma_bf16(r.k1[ks], qb[ks], s1);
     }
     // scores of head `col` for slots gs + 8*quad + e, in log2 units
     float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
@@ -122,23 +136,29 @@ __global__ __launch_bounds__(256) void k_decode_mfma(
     for (int e = 0; e < 8; ++e) sv[e] *= scale_log2;
 
     if (gs + kGroup > lim) {  // wave-uniform: tail of the chunk or not yet compacted
-      const size_t mb = size_t(page) * kPage + poff + quad * 8;
+      // the lane's eight slots: decisions (8 bytes) and positions (2 x 16 bytes),
+      // always inside the page, then a branch-free liveness test
+      const size_t mb = size_t(r.page) * kPage + poff + quad * 8;
+      const uint2 a8 = *reinterpret_cast<const uint2 *>(slot_alpha + mb);
+      const int4 p0 = *reinterpret_cast<const int4 *>(slot_pos + mb);
+      const int4 p1 = *reinterpret_cast<const int4 *>(slot_pos + mb + 4);
+      const int pos[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
       uint32_t keep[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int slot = gs + quad * 8 + e;
-        bool live = slot < s_end;
-        if (live && slot >= nclean) live = slot_alpha[mb + e] == 0 || (t - slot_pos[mb + e]) < window;
-        if (!live) sv[e] = -INFINITY;
+        const uint32_t marked = ((e < 4 ? a8.x : a8.y) >> (8 * (e & 3))) & 0xffu;
+        const bool live = (slot < s_end) & ((slot < nclean) | (marked == 0u) | ((t - pos[e]) < window));
+        sv[e] = live ? sv[e] : -INFINITY;
         keep[e >> 1] |= live ? (0xffffu << (16 * (e & 1))) : 0u;
       }
       // dead or unused slots must not reach the PV product even as 0 * NaN
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt) {
-        va[dt].x &= keep[0];
-        va[dt].y &= keep[1];
-        va[dt].z &= keep[2];
-        va[dt].w &= keep[3];
+        r.v[dt].x &= keep[0];
+        r.v[dt].y &= keep[1];
+        r.v[dt].z &= keep[2];
+        r.v[dt].w &= keep[3];
       }
     }
 
@@ -170,7 +190,20 @@ __global__ __launch_bounds__(256) void k_decode_mfma(
     const uint4 pb = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
                                 pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
 #pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) o[dt] = mfma_bf16(va[dt], pb, o[dt]);
+    for (int dt = 0; dt < DTILES; ++dt) o[dt] = mfma_bf16(r.v[dt], pb, o[dt]);
+  };
+
+  Regs ra, rb;
+  int gi = wave;
+  if (gi < ngroups) load_group(ra, gi);
+  while (gi < ngroups) {
+    if (gi + kMfmaWaves < ngroups) load_group(rb, gi + kMfmaWaves);
+    process(ra, gi);
+    gi += kMfmaWaves;
+    if (gi >= ngroups) break;
+    if (gi + kMfmaWaves < ngroups) load_group(ra, gi + kMfmaWaves);
+    process(rb, gi);
+    gi += kMfmaWaves;
   }
 
   // combine the waves of this workgroup
@@ -192,22 +225,22 @@ __global__ __launch_bounds__(256) void k_decode_mfma(
     float M = s_m[0][g];
 #pragma unroll
     for (int w = 1; w < kMfmaWaves; ++w) M = fmaxf(M, s_m[w][g]);
-    float L = 0.f, O = 0.f;
+    float Ls = 0.f, O = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kMfmaWaves; ++w) {
         const float mw = s_m[w][g];
         if (mw == -INFINITY) continue;
         const float f = exp2f(mw - M);
-        L = fmaf(s_l[w][g], f, L);
+        Ls = fmaf(s_l[w][g], f, Ls);
         O = fmaf(s_o[w][g][d], f, O);
       }
     }
-    if (nch == 1) {
-      out[(size_t(b) * hkv * G + size_t(h) * G) * D + x] = L > 0.f ? O / L : 0.f;
+    if (ci.nch == 1) {
+      out[size_t(u) * G * D + x] = Ls > 0.f ? O / Ls : 0.f;
     } else {
       part_o[size_t(c) * G * D + x] = O;
-      if (d == 0) part_ml[size_t(c) * G + g] = make_float2(M, L);
+      if (d == 0) part_ml[size_t(c) * G + g] = make_float2(M, Ls);
     }
   }
 }
@@ -218,14 +251,12 @@ bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, f
   const char *force = getenv("DMS_DECODE_KERNEL");
   if (force && force[0] == 'g') return false;  // "generic": the VALU kernel
   auto args = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(w.max_chunks), dim3(256), 0, st, s.kv_heads, s.group, s.window,
+    hipLaunchKernelGGL(kern, dim3(w.max_chunks), dim3(256), 0, st, units_of(s), s.kv_heads,
+                       s.group, s.window,
                        s.max_pages_per_unit, scale_log2, static_cast<const uint16_t *>(q),
                        static_cast<const uint16_t *>(c.k_pages),
                        static_cast<const uint16_t *>(c.v_pages), c.page_table, c.slot_pos,
-                       c.slot_alpha, c.n_slots, c.n_clean, c.seq_len,
-                       reinterpret_cast<const int32_t *>(ws + w.hdr),
-                       reinterpret_cast<const int32_t *>(ws + w.first_chunk),
-                       reinterpret_cast<const int32_t *>(ws + w.chunk_unit),
+                       c.slot_alpha, c.n_slots, c.n_clean, c.seq_len, c.plan,
                        reinterpret_cast<float2 *>(ws + w.part_ml),
                        reinterpret_cast<float *>(ws + w.part_o), out);
   };

@@ -12,18 +12,40 @@ namespace dms {
 
 constexpr int kPage = DMS_PAGE_SIZE;   // slots per page
 constexpr int kWave = 64;              // CDNA wavefront width
-// Target number of split-K chunks per decode call: 8 per CU on a 256-CU part.
-constexpr int kTargetChunks = 2048;
+// Target number of split-K chunks per decode call: two resident workgroups
+// on each of the 256 CUs, so that equal-length units need no merge at all.
+#ifndef DMS_TARGET_CHUNKS
+#define DMS_TARGET_CHUNKS 512
+#endif
+constexpr int kTargetChunks = DMS_TARGET_CHUNKS;
 
 inline int units_of(const dms_shape &s) { return s.batch * s.kv_heads; }
 
-// Decode workspace: every region starts on a 256-byte boundary.
+// Split plan, kept in cache state (dms_cache.plan, int32 words).  Rebuilt from
+// n_slots by every call that changes n_slots (reset, append, compact), so
+// decode reads it without a planning launch of its own.
+struct PlanLayout {
+  size_t hdr;          // [16]: [0] chunk count, [1] slots per chunk
+  size_t first_chunk;  // [units + 1]: first chunk of each unit (prefix sum)
+  size_t chunk_unit;   // [max_chunks]: owning unit of each chunk
+  size_t words;
+  int max_chunks;
+};
+
+__host__ __device__ inline PlanLayout plan_layout(int units) {
+  PlanLayout p;
+  p.max_chunks = units + kTargetChunks;
+  p.hdr = 0;
+  p.first_chunk = 16;
+  p.chunk_unit = p.first_chunk + size_t(units) + 1;
+  p.words = p.chunk_unit + size_t(p.max_chunks);
+  return p;
+}
+
+// Decode workspace: partial results of the split-K chunks.
 struct DecodeWorkspace {
-  size_t hdr;          // int32[16]: [0] chunk count, [1] slots per chunk
-  size_t first_chunk;  // int32[units + 1]: first chunk of each unit (prefix sum)
-  size_t chunk_unit;   // int32[max_chunks]: owning unit of each chunk
-  size_t part_ml;      // float2[max_chunks * G]: running max and sum per chunk and head
-  size_t part_o;       // float[max_chunks * G * D]: unnormalised partial outputs
+  size_t part_ml;  // float2[max_chunks * G]: running max and sum per chunk and head
+  size_t part_o;   // float[max_chunks * G * D]: unnormalised partial outputs
   size_t bytes;
   int max_chunks;
 };
@@ -34,11 +56,8 @@ inline DecodeWorkspace decode_workspace_layout(int units, int group, int head_di
   DecodeWorkspace w;
   w.max_chunks = units + kTargetChunks;
   size_t off = 0;
-  w.hdr = off;         off = align256(off + 16 * sizeof(int32_t));
-  w.first_chunk = off; off = align256(off + size_t(units + 1) * sizeof(int32_t));
-  w.chunk_unit = off;  off = align256(off + size_t(w.max_chunks) * sizeof(int32_t));
-  w.part_ml = off;     off = align256(off + size_t(w.max_chunks) * group * 2 * sizeof(float));
-  w.part_o = off;      off = align256(off + size_t(w.max_chunks) * group * head_dim * sizeof(float));
+  w.part_ml = off; off = align256(off + size_t(w.max_chunks) * group * 2 * sizeof(float));
+  w.part_o = off;  off = align256(off + size_t(w.max_chunks) * group * head_dim * sizeof(float));
   w.bytes = off;
   return w;
 }
@@ -48,6 +67,7 @@ hipError_t launch_reset(const dms_shape &s, const dms_cache &c, hipStream_t st);
 hipError_t launch_append(const dms_shape &s, const dms_cache &c, const void *k_new,
                          const void *v_new, const float *logit, int n_new, hipStream_t st);
 hipError_t launch_compact(const dms_shape &s, const dms_cache &c, hipStream_t st);
+hipError_t launch_plan(const dms_shape &s, const dms_cache &c, hipStream_t st);
 hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                          float sm_scale, void *ws, hipStream_t st);
 hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, const void *v,
@@ -83,6 +103,93 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
     if (l >= o) x += y;
   }
   return x;
+}
+
+// Chunk plan from n_slots, run by one workgroup of kPlanThreads threads.
+// Every thread reads only the n_slots entries it is the sole writer of in a
+// caller that updated them (unit u = base + threadIdx.x), so a caller that
+// has just written n_slots needs nothing beyond a workgroup barrier.
+// Chunk size C (slots, a multiple of the page size) is the smallest that
+// keeps the chunk count at most units + kTargetChunks:
+//   C = 64 * max(1, ceil(total / (64 * kTargetChunks))),  chunks(u) = max(1, ceil(n_u / C)).
+constexpr int kPlanThreads = 1024;
+
+__device__ inline void build_plan(int units, const int32_t *n_slots, int32_t *plan) {
+  const PlanLayout L = plan_layout(units);
+  int32_t *hdr = plan + L.hdr;
+  int32_t *first_chunk = plan + L.first_chunk;
+  int32_t *chunk_unit = plan + L.chunk_unit;
+  __shared__ unsigned long long s_total;
+  __shared__ int s_tmp[kPlanThreads / kWave];
+  if (threadIdx.x == 0) s_total = 0ull;
+  __syncthreads();
+  long long part = 0;
+  for (int u = threadIdx.x; u < units; u += kPlanThreads) part += n_slots[u];
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, kWave);
+  if (lane_id() == 0) atomicAdd(&s_total, (unsigned long long)part);
+  __syncthreads();
+  const long long total = (long long)s_total;
+  const long long per = (total + (long long)kPage * kTargetChunks - 1) / ((long long)kPage * kTargetChunks);
+  const int C = kPage * int(per < 1 ? 1 : per);
+  int carry = 0;
+  for (int base = 0; base < units; base += kPlanThreads) {
+    const int u = base + threadIdx.x;
+    int nch = 0;
+    if (u < units) {
+      const int n = n_slots[u];
+      nch = n > 0 ? (n + C - 1) / C : 1;
+    }
+    const int w = threadIdx.x / kWave, l = lane_id();
+    int incl = wave_inclusive_scan(nch);
+    if (l == kWave - 1) s_tmp[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+      int v = (l < kPlanThreads / kWave) ? s_tmp[l] : 0;
+      v = wave_inclusive_scan(v);
+      if (l < kPlanThreads / kWave) s_tmp[l] = v;
+    }
+    __syncthreads();
+    incl += (w > 0 ? s_tmp[w - 1] : 0) + carry;
+    const int blk_total = s_tmp[kPlanThreads / kWave - 1];
+    __syncthreads();
+    if (u < units) {
+      const int first = incl - nch;
+      first_chunk[u] = first;
+      for (int i = 0; i < nch; ++i) chunk_unit[first + i] = u;
+    }
+    carry += blk_total;
+  }
+  if (threadIdx.x == 0) {
+    first_chunk[units] = carry;
+    hdr[0] = carry;
+    hdr[1] = C;
+  }
+}
+
+// ---- page layout ----------------------------------------------------------
+// A page holds 64 slots of one unit as two groups of 32 slots; each group
+// stores its keys in 32*D elements and its values in 32*D elements, ordered so
+// that every operand fragment of the decode kernel's matrix products is one
+// contiguous 1 KB block (64 lanes x 16 bytes for bf16):
+//   key   (slot j, dim d): fragment (t, ks) of 16 slots x 32 dims, lane q*16 + r
+//         holds dims ks*32 + q*8 .. +8 of the slot at tile row r, where slot
+//         js = j % 32 sits in tile t = (js % 8) / 4 at row r = 4*(js / 8) + js % 4
+//   value (slot j, dim d): fragment dt of 16 dims x 32 slots, lane q*16 + (d % 16)
+//         holds slots 8q .. 8q + 7 of the group for dim d
+// Within a fragment, element e of lane l is at l*8 + e.  Eight consecutive dims
+// of a key, and eight consecutive slots of a value dim, are contiguous.
+__host__ __device__ inline int key_index(int j, int d, int D) {
+  const int grp = j >> 5, js = j & 31;
+  const int t = (js & 7) >> 2, r = 4 * (js >> 3) + (js & 3);
+  const int ks = d >> 5, q = (d >> 3) & 3, e = d & 7;
+  return grp * 32 * D + (((t * (D >> 5) + ks) * 4 + q) * 16 + r) * 8 + e;
+}
+
+__host__ __device__ inline int value_index(int j, int d, int D) {
+  const int grp = j >> 5, js = j & 31;
+  const int q = js >> 3, e = js & 7;
+  const int dt = d >> 4, rr = d & 15;
+  return grp * 32 * D + ((dt * 4 + q) * 16 + rr) * 8 + e;
 }
 
 // bf16 bits -> float (exact)

@@ -28,6 +28,7 @@ EXPORTS = (
     "dms_version",
     "dms_strerror",
     "dms_check_shape",
+    "dms_plan_words",
     "dms_reset",
     "dms_append",
     "dms_compact",
@@ -65,6 +66,7 @@ class DmsCacheStruct(ctypes.Structure):
         ("free_list", ctypes.c_void_p),
         ("free_top", ctypes.c_void_p),
         ("status", ctypes.c_void_p),
+        ("plan", ctypes.c_void_p),
     ]
 
 
@@ -93,6 +95,7 @@ def load() -> ctypes.CDLL:
         "dms_version": ([], ctypes.c_int),
         "dms_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "dms_check_shape": ([SP], ctypes.c_int),
+        "dms_plan_words": ([SP], ctypes.c_size_t),
         "dms_reset": ([SP, CP, P], ctypes.c_int),
         "dms_append": ([SP, CP, P, P, P, ctypes.c_int32, P], ctypes.c_int),
         "dms_compact": ([SP, CP, P], ctypes.c_int),
@@ -128,6 +131,10 @@ def version() -> int:
 
 def check_shape(shape: DmsShape) -> int:
     return load().dms_check_shape(ctypes.byref(shape))
+
+
+def plan_words(shape: DmsShape) -> int:
+    return load().dms_plan_words(ctypes.byref(shape))
 
 
 def decode_workspace_bytes(shape: DmsShape) -> int:

@@ -84,6 +84,8 @@ typedef struct dms_shape {
  *   seq_len     [B] int32      tokens appended so far (next position)
  *   free_list   [num_pages] int32, free_top [1] int32: stack of free pages
  *   status      [1] uint32     sticky DMS_STATUS_* bits
+ *   plan        [dms_plan_words(shape)] int32: the decode split plan, rebuilt
+ *               on the device by every call that changes n_slots
  * A unit's slots hold its retained tokens in ascending position order,
  * followed by tokens appended since its last compaction; a slot is dead when
  * its token is marked and w or more positions old, and dead slots are skipped
@@ -102,6 +104,7 @@ typedef struct dms_cache {
   int32_t *free_list;
   int32_t *free_top;
   uint32_t *status;
+  int32_t *plan;
 } dms_cache;
 
 /* ABI version (DMS_ABI_VERSION).  Never fails. */
@@ -113,10 +116,14 @@ const char *dms_strerror(int code);
 /* Host-only check of a shape: DMS_OK, DMS_EINVAL or DMS_EUNSUPPORTED. */
 int dms_check_shape(const dms_shape *shape);
 
+/* int32 words of cache->plan for this shape; 0 if the shape is invalid. */
+size_t dms_plan_words(const dms_shape *shape);
+
 /*
  * Empty every unit: page_table = -1, free_list = 0..num_pages-1,
  * free_top = num_pages, n_slots = n_clean = seq_len = 0, append_base = -1,
- * status = 0.  Must run once on fresh buffers before any other call.
+ * status = 0, plan rebuilt.  Must run once on fresh buffers before any
+ * other call.
  */
 int dms_reset(const dms_shape *shape, const dms_cache *cache, hipStream_t stream);
 
@@ -144,8 +151,9 @@ int dms_append(const dms_shape *shape, const dms_cache *cache, const void *k_new
  * t = seq_len[b] - 1, the slots in [n_clean, n_slots) whose token is marked
  * and t - pos >= w are removed; the survivors move down in order (stable
  * stream compaction), whole pages left empty go back on the free stack and
- * n_slots / n_clean are updated.  Attention results do not depend on when or
- * whether this runs; memory use and bytes read do.
+ * n_slots / n_clean are updated and the decode plan is rebuilt.  Attention
+ * results do not depend on when or whether this runs; memory use and bytes
+ * read do.
  */
 int dms_compact(const dms_shape *shape, const dms_cache *cache, hipStream_t stream);
 
@@ -165,8 +173,11 @@ size_t dms_decode_workspace_bytes(const dms_shape *shape);
  *   out  [B][Hq][D] float32
  * The caller appends token t before this call, so each query sees its own
  * token.  A unit with no slots gives zeros.  The work of each unit is split
- * into chunks of whole pages, sized on the device from the live lengths,
- * and the chunk partials are merged with the log-sum-exp rule.
+ * into chunks of whole pages following cache->plan (sized on the device from
+ * the live lengths), and the last chunk of a unit to finish merges the
+ * chunk partials with the log-sum-exp rule: one kernel launch per call.
+ * The call reads cache->plan.merge counters and leaves them zero; two
+ * decode calls on one cache must not run concurrently.
  */
 int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *q, float *out,
                     float sm_scale, void *workspace, size_t workspace_bytes, hipStream_t stream);

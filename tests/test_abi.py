@@ -62,18 +62,20 @@ def test_check_shape(L, kw, code):
 
 
 def test_workspace_bytes(L):
+    assert lib.plan_words(_shape()) == 16 + (4 + 1) + (4 + 512)
+    assert lib.plan_words(_shape(window=0)) == 0
     assert lib.decode_workspace_bytes(_shape()) > 0
     assert lib.decode_workspace_bytes(_shape(window=0)) == 0
     big = lib.decode_workspace_bytes(_shape(batch=64, kv_heads=8, group=4, head_dim=128))
-    # partial outputs of (units + 2048) chunks x G x D floats dominate
-    assert big >= (512 + 2048) * 4 * 128 * 4
+    # partial outputs of (units + 512) chunks x G x D floats dominate
+    assert big >= (512 + 512) * 4 * 128 * 4
 
 
 def test_host_side_errors_need_no_gpu(L):
     s = _shape()
     null_cache = lib.DmsCacheStruct()
     fake = ctypes.c_void_p(0x1000)
-    full = lib.DmsCacheStruct(*([0x1000] * 12))
+    full = lib.DmsCacheStruct(*([0x1000] * 13))
     assert L.dms_reset(None, None, None) == lib.DMS_EINVAL
     assert L.dms_reset(ctypes.byref(s), ctypes.byref(null_cache), None) == lib.DMS_EINVAL
     assert L.dms_append(ctypes.byref(s), ctypes.byref(full), fake, fake, fake, -1, None) == lib.DMS_EINVAL
@@ -111,3 +113,16 @@ def test_product_package_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("the oracle", ""), f
+
+
+def test_page_element_index_is_a_permutation():
+    """The fragment-ordered page layout maps (slot, dim) one-to-one onto a page."""
+    import torch
+    from decode_attention_learned_amd.cache import page_element_index
+    for d in (64, 128):
+        k, v = page_element_index(d)
+        assert torch.equal(torch.sort(k.reshape(-1)).values, torch.arange(64 * d))
+        assert torch.equal(torch.sort(v.reshape(-1)).values, torch.arange(64 * d))
+        # eight consecutive dims of a key, and eight consecutive slots of a value, are contiguous
+        assert torch.all(k[:, 1:8] - k[:, 0:7] == 1)
+        assert torch.all(v[1:8, :] - v[0:7, :] == 1)

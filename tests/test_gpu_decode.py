@@ -305,3 +305,38 @@ def test_qwen3_cr1_control_subset(gpu):
         qq = q[b, h * w.group:(h + 1) * w.group].double().cpu().numpy()
         ref[u] = orc.softmax_attention(qq, kk, vv, scale)
     compare_outputs(out, ref, w.kv_heads, w.group, torch.bfloat16)
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "generic"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_dead_uncompacted_slot_with_dominant_score_is_excluded(gpu, monkeypatch, kernel, dtype):
+    """A marked token whose key dominates every query must stop counting once it is
+    `window` positions old, even while its slot is still in the cache (no compaction).
+    If it leaked in, the output would be pulled to its value vector."""
+    if dtype == torch.float32 and kernel == "mfma":
+        pytest.skip("float32 caches always use the generic kernel")
+    monkeypatch.setenv("DMS_DECODE_KERNEL", kernel)
+    b, hkv, g, d, win = 2, 2, 3, 128, 16
+    gen = torch.Generator().manual_seed(4242)
+    n = 150
+    q = torch.randn((b, hkv * g, d), generator=gen)
+    k = torch.randn((b, n, hkv, d), generator=gen) * 0.1
+    v = torch.randn((b, n, hkv, d), generator=gen)
+    logit = torch.full((b, n, hkv), -1.0)
+    for bi in range(b):
+        for h in range(hkv):
+            for j in (3, 70, 130):          # dominant, marked tokens
+                k[bi, j, h] = q[bi, h * g:(h + 1) * g].mean(0) * 4
+                v[bi, j, h] = 4.0
+                logit[bi, j, h] = 1.0
+    q, k, v = q.to(dtype), k.to(dtype), v.to(dtype)
+    cache = DmsCache(b, hkv, g, d, dtype, max_pages_per_unit=4, window=win, device=gpu)
+    model = HostModel(b, hkv, g, d, win)
+    for t in range(n):
+        cache.append(k[:, t:t + 1].contiguous().to(gpu), v[:, t:t + 1].contiguous().to(gpu),
+                     logit[:, t:t + 1].contiguous().to(gpu))
+        model.append(k[:, t:t + 1], v[:, t:t + 1], logit[:, t:t + 1])
+        if t in (10, 80, 135, 140, 149):
+            out = cache.decode(q.to(gpu)).cpu()
+            compare_outputs(out, model.decode(q, scale_of(d)), hkv, g, dtype, what=f"t={t}")
+    assert np.all(cache.n_slots.cpu().numpy() == n)   # nothing was compacted

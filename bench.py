@@ -154,6 +154,40 @@ def traffic_from_profile(bytes_alg_per_launch: float):
     return rec.get("hbm_bytes_per_launch")
 
 
+def calibrate(gib: float) -> dict:
+    """Plain device-to-device copies and a full read (sum) of a buffer of known size.
+
+    The copy is the reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE
+    counters (a copy of N bytes reads N and writes N), and both give the
+    bandwidth this machine reaches with library kernels."""
+    import torch
+
+    n = int(gib * (1 << 30)) // 2
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").normal_()
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+        a.sum(dtype=torch.float32)
+    torch.cuda.synchronize()
+    reps = 5
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    for _ in range(reps):
+        a.sum(dtype=torch.float32)
+    e2.record()
+    torch.cuda.synchronize()
+    nbytes = 2 * n
+    copy_s = e0.elapsed_time(e1) / reps * 1e-3
+    sum_s = e1.elapsed_time(e2) / reps * 1e-3
+    return {"calibration": "device copy and full read", "bytes": nbytes,
+            "copy_read_plus_write_gbps": round(2 * nbytes / copy_s / 1e9, 1),
+            "sum_read_gbps": round(nbytes / sum_s / 1e9, 1),
+            "copy_launches": reps + 2, "sum_launches": reps + 2}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +197,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate", type=float, default=None, metavar="GIB",
+                    help="only run the copy/read calibration on a buffer of GIB GiB")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -177,6 +213,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate is not None:
+        print(json.dumps(calibrate(args.calibrate)), flush=True)
+        return
     dev = torch.device("cuda:0")
     w = wl.get(args.workload)
     replicas = args.replicas or w.replicas

@@ -1,5 +1,5 @@
 // Pieces shared by the split-K decode kernels: locating a chunk in the plan,
-// and the log-sum-exp merge of a unit's chunk partials.
+// and the fused log-sum-exp merge of a unit's chunk partials.
 #pragma once
 
 #include "dms_internal.h"
@@ -32,27 +32,94 @@ __device__ __forceinline__ bool locate_chunk(int c, int hkv, const int32_t *plan
   return true;
 }
 
-// Merge rule for chunk partials in log2 units:
-//   M = max_c m_c,  L = sum_c l_c 2^(m_c - M),  out = sum_c o_c 2^(m_c - M) / L
-// over the chunks [first, first + nch) of unit u; out is [unit][G][D].
-__device__ inline void merge_chunks(int u, int first, int nch, int G, int D, const float2 *part_ml,
-                                    const float *part_o, float *out) {
-  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
-    const int g = x / D;
-    float M = -INFINITY;
-    for (int i = 0; i < nch; ++i) M = fmaxf(M, part_ml[size_t(first + i) * G + g].x);
-    float Ls = 0.f, Os = 0.f;
-    if (M != -INFINITY) {
-      for (int i = 0; i < nch; ++i) {
-        const float2 ml = part_ml[size_t(first + i) * G + g];
-        if (ml.x == -INFINITY) continue;
-        const float f = exp2f(ml.x - M);
-        Ls = fmaf(ml.y, f, Ls);
-        Os = fmaf(part_o[size_t(first + i) * G * D + x], f, Os);
+// ---------------------------------------------------------------------------
+// Cross-workgroup merge of a unit's chunk partials, inside the decode kernel.
+//
+// Partials are published with agent-scope atomic stores (written through to
+// the agent's coherence point rather than left dirty in one XCD's L2), each
+// thread waits until its stores have completed, and one relaxed atomic
+// increment per workgroup counts the chunk in.  The workgroup that brings the
+// count to the unit's chunk count reads every partial back with agent-scope
+// atomic loads and writes the output.  No device-scope fence is needed, so no
+// workgroup writes back or invalidates a whole L2.
+//
+// Merge rule in log2 units:
+//   M = max_c m_c,  w_c = 2^(m_c - M),  out = sum_c o_c w_c / sum_c l_c w_c
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void publish(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float fetch(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kMergeLds = 2048;  // (chunk, head) weights kept in LDS
+
+// Called by every thread of the workgroup after it has published its share of
+// this chunk's partials.  Returns after the unit is merged (if this workgroup
+// was the last of its unit) or at once.
+__device__ inline void count_and_merge(const ChunkInfo &ci, int G, int D, int32_t *merge_count,
+                                       const float2 *part_ml, const float *part_o, float *out) {
+  __shared__ int s_last;
+  __shared__ float s_w[kMergeLds];
+  __shared__ float s_inv[16];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&merge_count[ci.unit], 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == ci.nch - 1;
+  __syncthreads();
+  if (!s_last) return;
+
+  const float *ml = reinterpret_cast<const float *>(part_ml);
+  const size_t out_base = size_t(ci.unit) * G * D;
+  if (ci.nch * G <= kMergeLds) {
+    // w[i][g] = 2^(m_ig - M_g); 1 / L_g
+    for (int x = threadIdx.x; x < ci.nch * G; x += blockDim.x)
+      s_w[x] = fetch(ml + 2 * (size_t(ci.first) * G + x));
+    __syncthreads();
+    if (threadIdx.x < G) {
+      const int g = threadIdx.x;
+      float M = -INFINITY;
+      for (int i = 0; i < ci.nch; ++i) M = fmaxf(M, s_w[i * G + g]);
+      float Ls = 0.f;
+      for (int i = 0; i < ci.nch; ++i) {
+        const float m = s_w[i * G + g];
+        const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+        s_w[i * G + g] = w;
+        Ls = fmaf(fetch(ml + 2 * (size_t(ci.first + i) * G + g) + 1), w, Ls);
       }
+      s_inv[g] = Ls > 0.f ? 1.f / Ls : 0.f;
     }
-    out[size_t(u) * G * D + x] = Ls > 0.f ? Os / Ls : 0.f;
+    __syncthreads();
+    for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
+      const int g = x / D;
+      float acc = 0.f;
+      for (int i = 0; i < ci.nch; ++i)
+        acc = fmaf(fetch(part_o + size_t(ci.first + i) * G * D + x), s_w[i * G + g], acc);
+      out[out_base + x] = acc * s_inv[g];
+    }
+  } else {  // very many chunks: the plain two-pass loop
+    for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
+      const int g = x / D;
+      float M = -INFINITY;
+      for (int i = 0; i < ci.nch; ++i) M = fmaxf(M, fetch(ml + 2 * (size_t(ci.first + i) * G + g)));
+      float Ls = 0.f, Os = 0.f;
+      if (M != -INFINITY) {
+        for (int i = 0; i < ci.nch; ++i) {
+          const float m = fetch(ml + 2 * (size_t(ci.first + i) * G + g));
+          if (m == -INFINITY) continue;
+          const float w = exp2f(m - M);
+          Ls = fmaf(fetch(ml + 2 * (size_t(ci.first + i) * G + g) + 1), w, Ls);
+          Os = fmaf(fetch(part_o + size_t(ci.first + i) * G * D + x), w, Os);
+        }
+      }
+      out[out_base + x] = Ls > 0.f ? Os / Ls : 0.f;
+    }
   }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&merge_count[ci.unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace dms

@@ -14,7 +14,8 @@
 //
 // Split-K: the plan (kept in cache state, see build_plan) cuts each unit's
 // slot list into chunks of C slots; each chunk produces (m, l, o) per head and
-// a second, small kernel merges the chunks of units that have more than one.  Scores are
+// the last chunk of a unit to finish merges them (count_and_merge): one
+// kernel launch per call.  Scores are
 // kept in log2 units (scale * log2 e folded into the score) so that every
 // exponential is exp2.
 #include "decode_common.h"
@@ -154,27 +155,13 @@ __global__ __launch_bounds__(256) void k_decode_generic(
 #pragma unroll
   for (int r = 0; r < OPT; ++r) {
     const int x = tid + r * 256;
-    if (x < G * D) part_o[size_t(c) * G * D + x] = acc[r];
+    if (x < G * D) publish(part_o + size_t(c) * G * D + x, acc[r]);
   }
-  if (tid < G) part_ml[size_t(c) * G + tid] = make_float2(s_m[tid], s_l[tid]);
-}
-
-// ---------------------------------------------------------------------------
-// merge: one workgroup per unit; units with a single chunk were finished by
-// the decode kernel.  A separate launch, so the partials of every chunk are
-// visible without device-scope fences inside the decode kernel.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_decode_merge(int units, int G, int D,
-                                                      const int32_t *__restrict__ plan,
-                                                      const float2 *__restrict__ part_ml,
-                                                      const float *__restrict__ part_o,
-                                                      float *__restrict__ out) {
-  const PlanLayout L = plan_layout(units);
-  const int u = blockIdx.x;
-  const int first = plan[L.first_chunk + u];
-  const int nch = plan[L.first_chunk + u + 1] - first;
-  if (nch <= 1) return;
-  merge_chunks(u, first, nch, G, D, part_ml, part_o, out);
+  if (tid < G) {
+    publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + tid), s_m[tid]);
+    publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + tid) + 1, s_l[tid]);
+  }
+  count_and_merge(ci, G, D, plan + L.merge_count, part_ml, part_o, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -227,11 +214,6 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
                : dispatch_group<uint32_t, 128>(s, c, static_cast<const uint32_t *>(q), out, scale_log2, w, ws, st);
   }
   if (!done) return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_decode_merge, dim3(units_of(s)), dim3(256), 0, st, units_of(s), s.group,
-                     s.head_dim, c.plan, reinterpret_cast<const float2 *>(ws + w.part_ml),
-                     reinterpret_cast<const float *>(ws + w.part_o), out);
   return hipGetLastError();
 }
 

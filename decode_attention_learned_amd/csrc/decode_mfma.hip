@@ -30,9 +30,22 @@ namespace dms {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMfmaWaves = 4;
+#ifndef DMS_DECODE_WAVES
+#define DMS_DECODE_WAVES 4
+#endif
+constexpr int kMfmaWaves = DMS_DECODE_WAVES;  // waves per decode workgroup
+constexpr int kMfmaThreads = kMfmaWaves * 64;
 constexpr int kGroup = 32;  // slots per group (half a page)
 constexpr int kMaxChunkPages = 1024;  // page ids staged in LDS per chunk
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// K/V bytes are read exactly once per call: nontemporal loads keep them from
+// displacing reusable lines (page table, plan, partials) in the caches.
+__device__ __forceinline__ uint4 ld16_stream(const uint16_t *p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
@@ -47,7 +60,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_decode_mfma(
+__global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
     int units, int hkv, int G, int window, int maxp, float scale_log2,
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pages,
     const uint16_t *__restrict__ v_pages, const int32_t *__restrict__ page_table,
@@ -72,14 +85,11 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(
   const int col = lane & 15;  // head index in B and C operands, row index in A
   const int quad = lane >> 4;
 
-  // page ids of this chunk, staged once in LDS (chunks start on a page boundary)
+  // page ids of this chunk are staged in LDS, a segment of at most
+  // kMaxChunkPages pages at a time (chunks start on a page boundary)
   __shared__ int s_pages[kMaxChunkPages];
   const int p_first = s_begin / kPage;
   const int npages = (s_end - s_begin + kPage - 1) / kPage;
-  const bool staged = npages <= kMaxChunkPages;
-  if (staged)
-    for (int i = tid; i < npages; i += 256) s_pages[i] = row[p_first + i];
-  __syncthreads();
 
   // Q^T operand: head `col`, dims ks*32 + quad*8 .. +8; heads >= G are zero
   uint4 qb[KSTEPS];
@@ -98,27 +108,27 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(
 
   const int ngroups = (s_end - s_begin + kGroup - 1) / kGroup;
 
-  // operand registers of one group; two sets alternate so that the loads of
-  // the next group are in flight while the current one is computed
+  // operand registers of one group.  Latency is hidden by occupancy (4 waves
+  // per SIMD at this register count) rather than by a second register set.
   struct Regs {
     uint4 k0[KSTEPS], k1[KSTEPS], v[DTILES];
     int page;
   };
   // Every fragment is a contiguous 1 KB block of the group: lane l reads the
   // 16 bytes at l*8 elements (page layout: key_index / value_index).
-  auto load_group = [&](Regs &r, int gi) {
-    const int pi = (gi * kGroup) / kPage;
-    r.page = __builtin_amdgcn_readfirstlane(staged ? s_pages[pi] : row[p_first + pi]);
+  auto load_group = [&](Regs &r, int gi, int seg0) {
+    const int pi = (gi * kGroup) / kPage - seg0;
+    r.page = __builtin_amdgcn_readfirstlane(s_pages[pi]);
     const size_t base = size_t(r.page) * kPage * D + size_t((gi * kGroup) % kPage) * D + lane * 8;
     const uint16_t *kp = k_pages + base;
     const uint16_t *vp = v_pages + base;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      r.k0[ks] = ld16(kp + ks * 512);
-      r.k1[ks] = ld16(kp + (KSTEPS + ks) * 512);
+      r.k0[ks] = ld16_stream(kp + ks * 512);
+      r.k1[ks] = ld16_stream(kp + (KSTEPS + ks) * 512);
     }
 #pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) r.v[dt] = ld16(vp + dt * 512);
+    for (int dt = 0; dt < DTILES; ++dt) r.v[dt] = ld16_stream(vp + dt * 512);
   };
 
   auto process = [&](Regs &r, int gi) {
@@ -193,34 +203,37 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(
     for (int dt = 0; dt < DTILES; ++dt) o[dt] = mfma_bf16(r.v[dt], pb, o[dt]);
   };
 
-  Regs ra, rb;
-  int gi = wave;
-  if (gi < ngroups) load_group(ra, gi);
-  while (gi < ngroups) {
-    if (gi + kMfmaWaves < ngroups) load_group(rb, gi + kMfmaWaves);
-    process(ra, gi);
-    gi += kMfmaWaves;
-    if (gi >= ngroups) break;
-    if (gi + kMfmaWaves < ngroups) load_group(ra, gi + kMfmaWaves);
-    process(rb, gi);
-    gi += kMfmaWaves;
+  for (int seg0 = 0; seg0 < npages; seg0 += kMaxChunkPages) {
+    const int segp = min(kMaxChunkPages, npages - seg0);
+    __syncthreads();  // every wave is done with the previous segment
+    for (int i = tid; i < segp; i += kMfmaThreads) s_pages[i] = row[p_first + seg0 + i];
+    __syncthreads();
+    const int g_end = min(ngroups, (seg0 + segp) * (kPage / kGroup));
+    for (int gi = seg0 * (kPage / kGroup) + wave; gi < g_end; gi += kMfmaWaves) {
+      Regs r;
+      load_group(r, gi, seg0);
+      process(r, gi);
+    }
   }
 
-  // combine the waves of this workgroup
+  // combine the waves of this workgroup (s_o: [waves][G][D + 4] in dynamic LDS)
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
   __shared__ float s_m[kMfmaWaves][16], s_l[kMfmaWaves][16];
-  __shared__ __align__(16) float s_o[kMfmaWaves][16][D + 4];
+  extern __shared__ __align__(16) float s_o[];
+  const int ostride = D + 4;
   if (quad == 0) {
     s_m[wave][col] = m_run;
     s_l[wave][col] = l_run;
   }
+  if (col < G) {
 #pragma unroll
-  for (int dt = 0; dt < DTILES; ++dt)
-    *reinterpret_cast<floatx4 *>(&s_o[wave][col][dt * 16 + quad * 4]) = o[dt];
+    for (int dt = 0; dt < DTILES; ++dt)
+      *reinterpret_cast<floatx4 *>(&s_o[(wave * G + col) * ostride + dt * 16 + quad * 4]) = o[dt];
+  }
   __syncthreads();
 
-  for (int x = tid; x < G * D; x += 256) {
+  for (int x = tid; x < G * D; x += kMfmaThreads) {
     const int g = x / D, d = x % D;
     float M = s_m[0][g];
 #pragma unroll
@@ -233,16 +246,20 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(
         if (mw == -INFINITY) continue;
         const float f = exp2f(mw - M);
         Ls = fmaf(s_l[w][g], f, Ls);
-        O = fmaf(s_o[w][g][d], f, O);
+        O = fmaf(s_o[(w * G + g) * ostride + d], f, O);
       }
     }
     if (ci.nch == 1) {
       out[size_t(u) * G * D + x] = Ls > 0.f ? O / Ls : 0.f;
     } else {
-      part_o[size_t(c) * G * D + x] = O;
-      if (d == 0) part_ml[size_t(c) * G + g] = make_float2(M, Ls);
+      publish(part_o + size_t(c) * G * D + x, O);
+      if (d == 0) {
+        publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + g), M);
+        publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + g) + 1, Ls);
+      }
     }
   }
+  if (ci.nch > 1) count_and_merge(ci, G, D, plan + L.merge_count, part_ml, part_o, out);
 }
 
 bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, float *out,
@@ -251,7 +268,11 @@ bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, f
   const char *force = getenv("DMS_DECODE_KERNEL");
   if (force && force[0] == 'g') return false;  // "generic": the VALU kernel
   auto args = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(w.max_chunks), dim3(256), 0, st, units_of(s), s.kv_heads,
+    const size_t lds = size_t(kMfmaWaves) * s.group * (s.head_dim + 4) * sizeof(float);
+    if (lds > 48 * 1024)  // gfx950 workgroups may use up to 160 KB of LDS
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    hipLaunchKernelGGL(kern, dim3(w.max_chunks), dim3(kMfmaThreads), lds, st, units_of(s), s.kv_heads,
                        s.group, s.window,
                        s.max_pages_per_unit, scale_log2, static_cast<const uint16_t *>(q),
                        static_cast<const uint16_t *>(c.k_pages),

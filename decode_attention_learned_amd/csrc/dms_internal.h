@@ -12,10 +12,11 @@ namespace dms {
 
 constexpr int kPage = DMS_PAGE_SIZE;   // slots per page
 constexpr int kWave = 64;              // CDNA wavefront width
-// Target number of split-K chunks per decode call: two resident workgroups
-// on each of the 256 CUs, so that equal-length units need no merge at all.
+// Target number of split-K chunks per decode call: one round of resident
+// decode workgroups (4 per CU on the 256 CUs).  Measured on the Qwen3-8B,
+// ragged Qwen2.5-32B and Llama-1B decode workloads against 512 and 2048.
 #ifndef DMS_TARGET_CHUNKS
-#define DMS_TARGET_CHUNKS 512
+#define DMS_TARGET_CHUNKS 1024
 #endif
 constexpr int kTargetChunks = DMS_TARGET_CHUNKS;
 
@@ -28,6 +29,7 @@ struct PlanLayout {
   size_t hdr;          // [16]: [0] chunk count, [1] slots per chunk
   size_t first_chunk;  // [units + 1]: first chunk of each unit (prefix sum)
   size_t chunk_unit;   // [max_chunks]: owning unit of each chunk
+  size_t merge_count;  // [units]: chunks of the unit finished in the running decode
   size_t words;
   int max_chunks;
 };
@@ -38,7 +40,8 @@ __host__ __device__ inline PlanLayout plan_layout(int units) {
   p.hdr = 0;
   p.first_chunk = 16;
   p.chunk_unit = p.first_chunk + size_t(units) + 1;
-  p.words = p.chunk_unit + size_t(p.max_chunks);
+  p.merge_count = p.chunk_unit + size_t(p.max_chunks);
+  p.words = p.merge_count + size_t(units);
   return p;
 }
 
@@ -119,6 +122,7 @@ __device__ inline void build_plan(int units, const int32_t *n_slots, int32_t *pl
   int32_t *hdr = plan + L.hdr;
   int32_t *first_chunk = plan + L.first_chunk;
   int32_t *chunk_unit = plan + L.chunk_unit;
+  int32_t *merge_count = plan + L.merge_count;
   __shared__ unsigned long long s_total;
   __shared__ int s_tmp[kPlanThreads / kWave];
   if (threadIdx.x == 0) s_total = 0ull;
@@ -155,6 +159,7 @@ __device__ inline void build_plan(int units, const int32_t *n_slots, int32_t *pl
     if (u < units) {
       const int first = incl - nch;
       first_chunk[u] = first;
+      merge_count[u] = 0;
       for (int i = 0; i < nch; ++i) chunk_unit[first + i] = u;
     }
     carry += blk_total;

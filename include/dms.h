@@ -176,8 +176,8 @@ size_t dms_decode_workspace_bytes(const dms_shape *shape);
  * into chunks of whole pages following cache->plan (sized on the device from
  * the live lengths), and the last chunk of a unit to finish merges the
  * chunk partials with the log-sum-exp rule: one kernel launch per call.
- * The call reads cache->plan.merge counters and leaves them zero; two
- * decode calls on one cache must not run concurrently.
+ * The call uses per-unit counters inside cache->plan and leaves them zero;
+ * two decode calls on one cache must not run concurrently.
  */
 int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *q, float *out,
                     float sm_scale, void *workspace, size_t workspace_bytes, hipStream_t stream);

@@ -62,13 +62,13 @@ def test_check_shape(L, kw, code):
 
 
 def test_workspace_bytes(L):
-    assert lib.plan_words(_shape()) == 16 + (4 + 1) + (4 + 512)
+    assert lib.plan_words(_shape()) == 16 + (4 + 1) + (4 + 1024) + 4
     assert lib.plan_words(_shape(window=0)) == 0
     assert lib.decode_workspace_bytes(_shape()) > 0
     assert lib.decode_workspace_bytes(_shape(window=0)) == 0
     big = lib.decode_workspace_bytes(_shape(batch=64, kv_heads=8, group=4, head_dim=128))
-    # partial outputs of (units + 512) chunks x G x D floats dominate
-    assert big >= (512 + 512) * 4 * 128 * 4
+    # partial outputs of (units + 1024) chunks x G x D floats dominate
+    assert big >= (512 + 1024) * 4 * 128 * 4
 
 
 def test_host_side_errors_need_no_gpu(L):

@@ -87,13 +87,14 @@ def is_visible(i: int, j: int, alpha_j: bool, window: int) -> bool:
     return (j <= i) and not (bool(alpha_j) and (i - j) >= window)
 
 
-def visibility_mask(alpha, window: int) -> np.ndarray:
-    """Boolean [S, S] mask M[i, j] = is_visible(i, j, alpha[j], window)."""
+def visibility_mask(alpha, window: int, rows=None) -> np.ndarray:
+    """Boolean mask M[i, j] = is_visible(i, j, alpha[j], window): [S, S], or
+    [len(rows), S] for the query rows given."""
     if window < 1:
         raise ValueError("window must be >= 1")
     alpha = np.asarray(alpha, dtype=bool)
     s = alpha.shape[0]
-    i = np.arange(s)[:, None]
+    i = (np.arange(s) if rows is None else np.asarray(rows, dtype=np.int64))[:, None]
     j = np.arange(s)[None, :]
     return (j <= i) & ~(alpha[None, :] & ((i - j) >= window))
 
@@ -167,7 +168,7 @@ def prefill_rows(q, k, v, alpha, rows, window: int, scale: float) -> np.ndarray:
     rows = np.asarray(rows, dtype=np.int64)
     out = np.empty((rows.shape[0], hq_n, q.shape[2]), dtype=np.float64)
     for h in range(hkv_n):
-        mask = visibility_mask(alpha[:, h], window)[rows]          # [R, S]
+        mask = visibility_mask(alpha[:, h], window, rows)          # [R, S]
         kh = k[:, h, :].astype(np.float64)
         vh = v[:, h, :].astype(np.float64)
         for g in range(group):

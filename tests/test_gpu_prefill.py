@@ -1,0 +1,123 @@
+"""GPU parity of the masked prefill kernel against the float64 oracle, through the C ABI.
+
+Tolerance: |o - o_ref| <= 2e-2 + 2e-2 |o_ref| element-wise (bf16 inputs, fp32 accumulation).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from decode_attention_learned_amd import DmsCache, prefill
+from harness import BF16_TOL, HostModel, compare_outputs, say
+from oracle import dms_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(b, s, hkv, g, d=128, rate=0.5, seed=0):
+    w = wl.Workload(name="prefill_case", kind="prefill", batch=b, kv_heads=hkv, group=g,
+                    head_dim=d, dtype="bf16", context=s, evict_rate=rate, seed=seed)
+    return w, wl.prefill_inputs(w)
+
+
+def _check_rows(out, q, k, v, logit, rows, window, what=""):
+    """Compare GPU rows against oracle.prefill_rows for every sequence."""
+    b_n, s, hq, d = q.shape
+    scale = 1.0 / math.sqrt(d)
+    alpha = orc.eviction_decisions(logit.numpy())
+    worst = 0.0
+    for bi in range(b_n):
+        ref = orc.prefill_rows(q[bi].float().numpy(), k[bi].float().numpy(), v[bi].float().numpy(),
+                               alpha[bi], rows, window, scale)
+        got = out[bi, rows].double().numpy()
+        err = np.abs(got - ref)
+        worst = max(worst, float(err.max()))
+        bound = BF16_TOL["atol"] + BF16_TOL["rtol"] * np.abs(ref)
+        assert np.all(err <= bound), f"{what} seq {bi}: max err {err.max():.3g}"
+    return worst
+
+
+@pytest.mark.parametrize("b,s,hkv,g", [(2, 200, 2, 4), (1, 97, 1, 1), (1, 130, 2, 2), (1, 150, 1, 5),
+                                       (2, 64, 1, 8), (1, 1, 1, 4), (1, 33, 3, 4)])
+def test_prefill_small_all_rows(gpu, b, s, hkv, g):
+    w, (q, k, v, logit) = _inputs(b, s, hkv, g, seed=5100 + s + g)
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16).cpu()
+    worst = _check_rows(out, q, k, v, logit, np.arange(s), 16, what=f"B={b} S={s} Hkv={hkv} G={g}")
+    say(f"prefill B={b} S={s} Hkv={hkv} G={g}: max err {worst:.2e}")
+
+
+@pytest.mark.parametrize("window", [1, 3, 16, 40])
+def test_prefill_windows(gpu, window):
+    w, (q, k, v, logit) = _inputs(1, 300, 2, 4, rate=0.7, seed=5200 + window)
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=window).cpu()
+    _check_rows(out, q, k, v, logit, np.arange(300), window, what=f"window {window}")
+
+
+def test_prefill_all_keep_is_causal_sdpa(gpu):
+    """Nothing marked: the kernel is plain causal attention (torch SDPA on CPU, float64)."""
+    w, (q, k, v, logit) = _inputs(2, 257, 2, 4, rate=0.0, seed=5301)
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16).cpu()
+    for bi in range(2):
+        qq = q[bi].double().permute(1, 0, 2)
+        kk = k[bi].double().permute(1, 0, 2).repeat_interleave(4, 0)
+        vv = v[bi].double().permute(1, 0, 2).repeat_interleave(4, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, is_causal=True,
+                                                               scale=1 / math.sqrt(128))
+        assert torch.allclose(out[bi].double(), ref.permute(1, 0, 2), rtol=2e-2, atol=2e-2)
+
+
+def test_prefill_all_evict_is_sliding_window_sdpa(gpu):
+    """Everything marked: attention over the last 16 positions (SDPA with a band mask)."""
+    w, (q, k, v, logit) = _inputs(1, 200, 2, 4, rate=1.0, seed=5302)
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16).cpu()
+    i = torch.arange(200)[:, None]
+    j = torch.arange(200)[None, :]
+    band = (i - j >= 0) & (i - j < 16)
+    qq = q[0].double().permute(1, 0, 2)
+    kk = k[0].double().permute(1, 0, 2).repeat_interleave(4, 0)
+    vv = v[0].double().permute(1, 0, 2).repeat_interleave(4, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=band,
+                                                           scale=1 / math.sqrt(128))
+    assert torch.allclose(out[0].double(), ref.permute(1, 0, 2), rtol=2e-2, atol=2e-2)
+
+
+def test_prefill_matches_decode_path(gpu):
+    """Prefill row t and the decode step at t see the same set: both GPU paths agree
+    with each other and with the oracle."""
+    b, s, hkv, g = 2, 180, 2, 4
+    w, (q, k, v, logit) = _inputs(b, s, hkv, g, rate=0.6, seed=5401)
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16).cpu()
+    cache = DmsCache(b, hkv, g, 128, torch.bfloat16, max_pages_per_unit=4, device=gpu)
+    for t in range(s):
+        cache.append(k[:, t:t + 1].contiguous().to(gpu), v[:, t:t + 1].contiguous().to(gpu),
+                     logit[:, t:t + 1].contiguous().to(gpu))
+        if t in (0, 15, 16, 17, 90, 179):
+            dec = cache.decode(q[:, t].contiguous().to(gpu)).cpu()
+            assert torch.allclose(dec, out[:, t], rtol=2e-2, atol=2e-2), f"t={t}"
+        if t % 32 == 31:
+            cache.compact()
+
+
+def test_prefill_8k_sampled_rows(gpu):
+    """Masked prefill at full size (B=4, S=8192, 32/8 heads, CR 8): query rows
+    [0, 512) and [7680, 8192) of every sequence and head against the oracle."""
+    w = wl.get("prefill_8k")
+    say("prefill_8k: B=4 S=8192 Hq=32 Hkv=8 D=128")
+    q, k, v, logit = wl.prefill_inputs(w, device=gpu)
+    out = prefill(q, k, v, logit, window=16)
+    rows = np.concatenate([np.arange(0, 512), np.arange(7680, 8192)])
+    out_rows = out[:, torch.as_tensor(rows, device=gpu)].cpu()
+    qc, kc, vc, lc = q.cpu(), k.cpu(), v.cpu(), logit.cpu()
+    scale = 1.0 / math.sqrt(128)
+    alpha = orc.eviction_decisions(lc.numpy())
+    for bi in range(w.batch):
+        ref = orc.prefill_rows(qc[bi].float().numpy(), kc[bi].float().numpy(), vc[bi].float().numpy(),
+                               alpha[bi], rows, 16, scale)
+        got = out_rows[bi].double().numpy()
+        err = np.abs(got - ref)
+        bound = BF16_TOL["atol"] + BF16_TOL["rtol"] * np.abs(ref)
+        assert np.all(err <= bound), f"seq {bi}: max err {err.max():.3g}"
+        say(f"  seq {bi}: max err {err.max():.2e}")

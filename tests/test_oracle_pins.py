@@ -273,8 +273,8 @@ def test_pins_pass_unmutated(monkeypatch):
 def test_pins_catch_window_off_by_one(monkeypatch):
     real = orc.visibility_mask
 
-    def off_by_one(alpha, window):
-        return real(alpha, window + 1)
+    def off_by_one(alpha, window, rows=None):
+        return real(alpha, window + 1, rows)
 
     assert not _pins_pass(monkeypatch, mutated_mask=off_by_one)
 
@@ -282,17 +282,17 @@ def test_pins_catch_window_off_by_one(monkeypatch):
 def test_pins_catch_inverted_decision(monkeypatch):
     real = orc.visibility_mask
 
-    def inverted(alpha, window):
-        return real(~np.asarray(alpha, dtype=bool), window)
+    def inverted(alpha, window, rows=None):
+        return real(~np.asarray(alpha, dtype=bool), window, rows)
 
     assert not _pins_pass(monkeypatch, mutated_mask=inverted)
 
 
 def test_pins_catch_missing_causal_bound(monkeypatch):
-    def acausal(alpha, window):
+    def acausal(alpha, window, rows=None):
         alpha = np.asarray(alpha, dtype=bool)
         s = alpha.shape[0]
-        i = np.arange(s)[:, None]
+        i = (np.arange(s) if rows is None else np.asarray(rows))[:, None]
         j = np.arange(s)[None, :]
         return ~(alpha[None, :] & ((i - j) >= window))
 
@@ -309,3 +309,11 @@ def test_pins_catch_transposed_contraction(monkeypatch):
         return (e @ v) / e.sum(axis=0, keepdims=True).sum()
 
     assert not _pins_pass(monkeypatch, mutated_softmax=transposed)
+
+
+def test_mask_rows_match_full_mask():
+    rng = _rng(21)
+    alpha = rng.random(90) < 0.6
+    full = orc.visibility_mask(alpha, 16)
+    rows = np.array([0, 5, 15, 16, 17, 60, 89])
+    assert np.array_equal(orc.visibility_mask(alpha, 16, rows), full[rows])

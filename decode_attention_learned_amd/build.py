@@ -31,6 +31,14 @@ FLAGS = [
 ]
 
 
+# The attention kernels mask with -inf and never rely on NaN semantics; without
+# NaN honouring the compiler drops the NaN-quieting copies before every max.
+PER_FILE_FLAGS = {
+    "decode_mfma.hip": ["-fno-honor-nans"],
+    "prefill.hip": ["-fno-honor-nans"],
+}
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -45,8 +53,8 @@ def build(verbose: bool = False) -> str:
     procs = []
     for src in SOURCES:
         obj = os.path.join(build_dir, src.replace(".hip", ".o"))
-        cmd = [hipcc(), *[f for f in FLAGS if f != "-shared"], "-c", "-I", INCLUDE, "-I", CSRC,
-               os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *[f for f in FLAGS if f != "-shared"], *PER_FILE_FLAGS.get(src, []), "-c",
+               "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -153,8 +153,10 @@ class DmsCache:
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logit: torch.Tensor,
             window: int = 16, sm_scale: float | None = None,
-            out: torch.Tensor | None = None) -> torch.Tensor:
-    """Masked DMS prefill: q [B, S, Hq, D], k, v [B, S, Hkv, D] bf16, logit [B, S, Hkv] f32."""
+            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Masked DMS prefill: q [B, S, Hq, D], k, v [B, S, Hkv, D] bf16, logit [B, S, Hkv] f32.
+
+    `workspace` (uint8, at least prefill_workspace_bytes) is allocated when not given."""
     lib.load()
     b, s, hq, d = q.shape
     hkv = k.shape[2]
@@ -171,5 +173,9 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logit: torch.Tens
     _need(out, "out", torch.float32, (b, s, hq, d), dev)
     shape = lib.DmsShape(b, hkv, hq // hkv, d, PAGE, window, 1, 1, _DTYPES.get(q.dtype, -1))
     scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
-    lib.check("dms_prefill_attn", lib.dms_prefill_attn(shape, q, k, v, logit, s, scale, out, _stream()))
+    need = lib.prefill_workspace_bytes(shape, s)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    lib.check("dms_prefill_attn", lib.dms_prefill_attn(shape, q, k, v, logit, s, scale, out, workspace,
+                                                       workspace.numel(), _stream()))
     return out

@@ -103,20 +103,33 @@ int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *
   return from_hip(dms::launch_decode(*shape, *cache, q, out, sm_scale, workspace, stream));
 }
 
-int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const void *v,
-                     const float *logit, int32_t seq_len, float sm_scale, float *out,
-                     hipStream_t stream) {
+static int check_prefill_shape(const dms_shape *shape, int32_t seq_len) {
   if (!shape) return DMS_EINVAL;
   if (shape->batch < 1 || shape->kv_heads < 1 || shape->group < 1 || shape->window < 1)
     return DMS_EINVAL;
   if (seq_len < 0) return DMS_EINVAL;
   if (shape->head_dim != 128 || shape->kv_dtype != DMS_KV_BF16 || shape->group > 16)
     return DMS_EUNSUPPORTED;
+  return DMS_OK;
+}
+
+size_t dms_prefill_workspace_bytes(const dms_shape *shape, int32_t seq_len) {
+  if (check_prefill_shape(shape, seq_len) != DMS_OK) return 0;
+  return dms::prefill_workspace_bytes(shape->batch, shape->kv_heads, seq_len);
+}
+
+int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const void *v,
+                     const float *logit, int32_t seq_len, float sm_scale, float *out,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_prefill_shape(shape, seq_len);
+  if (rc) return rc;
   if (seq_len == 0) return DMS_OK;
-  if (!q || !k || !v || !logit || !out) return DMS_EINVAL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return DMS_EINVAL;
+  if (!q || !k || !v || !logit || !out || !workspace) return DMS_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
+    return DMS_EINVAL;
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
-  return from_hip(dms::launch_prefill(*shape, q, k, v, logit, seq_len, sm_scale, out, stream));
+  if (workspace_bytes < dms_prefill_workspace_bytes(shape, seq_len)) return DMS_EWORKSPACE;
+  return from_hip(dms::launch_prefill(*shape, q, k, v, logit, seq_len, sm_scale, out, workspace, stream));
 }
 
 }  // extern "C"

@@ -179,8 +179,8 @@ __global__ __launch_bounds__(256) void k_append_write(
     s_off[tid] = off;
     const size_t tok = (size_t(b) * n_new + i0 + tid) * hkv + h;
     slot_pos[size_t(page) * kPage + off] = pos0 + i0 + tid;
-    // the decision: sigmoid(logit) > 1/2  <=>  logit > 0 (NaN compares false: keep)
-    slot_alpha[size_t(page) * kPage + off] = logit[tok] > 0.0f ? 1 : 0;
+    // the decision: sigmoid(logit) > 1/2  <=>  logit > 0 (NaN keeps)
+    slot_alpha[size_t(page) * kPage + off] = evict_decision(logit[tok]) ? 1 : 0;
   }
   __syncthreads();
 

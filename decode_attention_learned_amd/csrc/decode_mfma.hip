@@ -54,9 +54,12 @@ __device__ __forceinline__ floatx4 mfma_bf16(uint4 a, uint4 b, floatx4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)lo)) |
-         (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{lo, hi}, bf16x2v));
 }
 
 template <int D>

@@ -74,8 +74,15 @@ hipError_t launch_plan(const dms_shape &s, const dms_cache &c, hipStream_t st);
 hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                          float sm_scale, void *ws, hipStream_t st);
 hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, const void *v,
-                          const float *logit, int seq_len, float sm_scale, float *out,
+                          const float *logit, int seq_len, float sm_scale, float *out, void *ws,
                           hipStream_t st);
+
+// Prefill workspace: per (b, h, 32-key tile) 8 KB of key fragments, 8 KB of
+// value fragments (head_dim 128, bf16) and one decision word.
+inline size_t prefill_workspace_bytes(int batch, int kv_heads, int seq_len) {
+  const size_t tiles = size_t(batch) * kv_heads * ((size_t(seq_len) + 31) / 32);
+  return align256(tiles * 16384) + align256(tiles * sizeof(uint32_t));
+}
 
 // ---- wave64 helpers -------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
@@ -195,6 +202,15 @@ __host__ __device__ inline int value_index(int j, int d, int D) {
   const int q = js >> 3, e = js & 7;
   const int dt = d >> 4, rr = d & 15;
   return grp * 32 * D + ((dt * 4 + q) * 16 + rr) * 8 + e;
+}
+
+// The decision: marked for eviction iff logit > 0 (+0, -0, NaN and negatives
+// keep).  Tested on the bits so that no floating-point compile flag can
+// change how NaN is treated: the positive floats, +inf included, are exactly
+// the bit patterns 0x00000001 .. 0x7f800000.
+__device__ __forceinline__ bool evict_decision(float logit) {
+  const uint32_t u = __float_as_uint(logit);
+  return u - 1u < 0x7f800000u;
 }
 
 // bf16 bits -> float (exact)

@@ -9,13 +9,20 @@
 //   j <= i  and  not (alpha_j and i - j >= w),   alpha_j = logit_j > 0.
 // out = softmax_j(scale * <q_i, k_j>) v_j over the visible keys, fp32.
 //
+// Two kernels.  k_prefill_pack re-lays keys and values out once, per (b, h,
+// 32-key tile), in the order of the matrix-core operand fragments (values
+// transposed), with one decision word per tile, into the caller's workspace.
+// k_prefill then only copies whole fragments into LDS.
+//
 // Work decomposition.  A workgroup of 8 waves takes 64 query positions of
 // one KV head: wave w serves query head g = 4*hg + (w % 4) of the group and
 // query positions i0 + 32*(w / 4) .. +32.  Keys are consumed in tiles of 32
 // from position 0 up to the causal end of the block.  Each key tile (keys
 // and values) is loaded once per workgroup into LDS, in the order of the
 // matrix-core operand fragments, and serves all four heads; the next tile's
-// global loads are in flight while the current tile is computed.
+// global loads are in flight while the current tile is computed.  Tiles that
+// lie wholly `w` or more positions behind every query of a wave need only the
+// decision bits; the tiles on the diagonal band test the full rule.
 //
 // Per tile and wave the two products are the ones of the decode kernel, with
 // query positions in place of heads:
@@ -50,24 +57,73 @@ __device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)lo)) |
-         (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{lo, hi}, bf16x2v));
 }
 
-// The tile's global pieces held by one thread between load and LDS store:
-// thread t covers the 16-byte piece t of K and of V (512 pieces per tile):
-// key t / 16, dims (t % 16) * 8 .. +8.
-struct TilePieces {
-  uint4 k, v;
-  uint32_t alpha;  // threads 0..31: decision of key j0 + t
-};
+constexpr int PTILE_U4 = (PK_FRAGS + PV_FRAGS) * PFRAG;  // uint4 per packed tile (16 KB)
+
+// One packed tile per (b, h, tile): [key fragments (8 x 1 KB) | value fragments (8 x 1 KB)].
+__device__ __forceinline__ size_t tile_index(int b, int h, int tile, int hkv, int ntiles) {
+  return (size_t(b) * hkv + h) * ntiles + tile;
+}
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// pack: one workgroup (512 threads) per (tile, h, b)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles,
+                                                      const uint16_t *__restrict__ k,
+                                                      const uint16_t *__restrict__ v,
+                                                      const float *__restrict__ logit,
+                                                      uint4 *__restrict__ packed,
+                                                      uint32_t *__restrict__ alpha_words) {
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int t = threadIdx.x;
+  const int j0 = tile * PBN;
+  const size_t T = tile_index(b, h, tile, hkv, ntiles);
+  uint4 *kdst = packed + T * PTILE_U4;
+  uint4 *vdst = kdst + PK_FRAGS * PFRAG;
+  __shared__ __align__(16) uint16_t sv[PBN][PD + 8];  // row-major values, padded rows
+
+  // thread t: key jj = t / 16, dims dc*8 .. +8
+  const int jj = t >> 4, dc = t & 15;
+  const int j = j0 + jj;
+  uint4 kp = make_uint4(0, 0, 0, 0), vp = make_uint4(0, 0, 0, 0);
+  if (j < S) {
+    const size_t off = ((size_t(b) * S + j) * hkv + h) * PD + dc * 8;
+    kp = *reinterpret_cast<const uint4 *>(k + off);
+    vp = *reinterpret_cast<const uint4 *>(v + off);
+  }
+  // key fragment (tt, ks), lane qd*16 + row (tile row from the slot permutation)
+  const int tt = (jj & 7) >> 2, row = 4 * (jj >> 3) + (jj & 3);
+  const int ks = dc >> 2, qd = dc & 3;
+  kdst[(tt * PKS + ks) * PFRAG + qd * 16 + row] = kp;
+  *reinterpret_cast<uint4 *>(&sv[jj][dc * 8]) = vp;
+  if (t < kWave) {
+    const bool marked = t < PBN && j0 + t < S && evict_decision(logit[(size_t(b) * S + j0 + t) * hkv + h]);
+    const uint64_t m = __ballot(marked);
+    if (t == 0) alpha_words[T] = uint32_t(m);
+  }
+  __syncthreads();
+  // value fragment dt = t / 64, lane l = t % 64: dim dt*16 + l % 16, keys 8*(l/16) .. +8
+  const int dt = t >> 6, l = t & 63;
+  const int d = dt * 16 + (l & 15), k0 = 8 * (l >> 4);
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = uint32_t(sv[k0 + 2 * e][d]) | (uint32_t(sv[k0 + 2 * e + 1][d]) << 16);
+  vdst[t] = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
     int batch, int S, int hkv, int G, int window, float scale_log2, const uint16_t *__restrict__ q,
-    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const float *__restrict__ logit,
+    const uint4 *__restrict__ packed, const uint32_t *__restrict__ alpha_words,
     float *__restrict__ out) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -124,111 +180,99 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
     for (int qt = 0; qt < 2; ++qt) o[dt][qt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
-  const size_t kv_row = size_t(hkv) * PD;  // elements between consecutive positions
-  const uint16_t *kb0 = k + (size_t(b) * S * hkv + h) * PD;
-  const uint16_t *vb0 = v + (size_t(b) * S * hkv + h) * PD;
-  const float *lb0 = logit + size_t(b) * S * hkv + h;
+  const int ntiles_all = (S + PBN - 1) / PBN;
+  const uint4 *pk = packed + tile_index(b, h, 0, hkv, ntiles_all) * PTILE_U4;
+  const uint32_t *pa = alpha_words + tile_index(b, h, 0, hkv, ntiles_all);
 
-  auto fetch_tile = [&](TilePieces &tp, int j0) {
-    const int jj = tid >> 4, dc = tid & 15;
-    const int j = j0 + jj;
-    tp.k = make_uint4(0, 0, 0, 0);
-    tp.v = make_uint4(0, 0, 0, 0);
-    if (j < S) {
-      tp.k = *reinterpret_cast<const uint4 *>(kb0 + size_t(j) * kv_row + dc * 8);
-      tp.v = *reinterpret_cast<const uint4 *>(vb0 + size_t(j) * kv_row + dc * 8);
-    }
-    tp.alpha = 0u;
-    if (tid < PBN && j0 + tid < S) tp.alpha = lb0[size_t(j0 + tid) * hkv] > 0.0f ? 1u : 0u;
-  };
-
-  auto store_tile = [&](const TilePieces &tp, int st) {
-    const int jj = tid >> 4, dc = tid & 15;
-    // key fragment (t, ks), lane qd*16 + row
-    const int t = (jj & 7) >> 2, row = 4 * (jj >> 3) + (jj & 3);
-    const int ks = dc >> 2, qd = dc & 3;
-    sK[st][(t * PKS + ks) * PFRAG + qd * 16 + row] = tp.k;
-    // value fragment dt = d / 16, lane (jj / 8)*16 + d % 16, element jj % 8
-    uint16_t *vb = reinterpret_cast<uint16_t *>(&sV[st][0]);
-    const uint16_t *el = reinterpret_cast<const uint16_t *>(&tp.v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = dc * 8 + e;
-      vb[(((d >> 4) * 4 + (jj >> 3)) * 16 + (d & 15)) * 8 + (jj & 7)] = el[e];
-    }
-    if (wave == 0) {
-      const uint64_t m = __ballot(lane < PBN && tp.alpha != 0u);
-      if (lane == 0) sA[st] = uint32_t(m);
-    }
-  };
-
-  const int ntiles = (i_end + PBN - 1) / PBN;
-  TilePieces tp;
-  fetch_tile(tp, 0);
-  store_tile(tp, 0);
+  // thread t copies uint4 t and t + 512 of the 16 KB packed tile (keys, then values)
+  uint4 ta = pk[tid], tb = pk[tid + PWAVES * 64];
+  uint32_t talpha = pa[0];
+  sK[0][tid] = ta;
+  sV[0][tid] = tb;
+  if (tid == 0) sA[0] = talpha;
   __syncthreads();
 
+  // Lazy rescaling: a query's reference maximum m_run (raw score units) moves
+  // only when a tile's maximum exceeds it by more than kLazy/c, so p <= 2^kLazy.
+  // The result is unchanged (numerator and denominator share the reference),
+  // and the rescale of the accumulators becomes rare after the first tiles.
+  constexpr float kLazy = 8.0f;
+  const float c = scale_log2;
+  const float lazy_raw = kLazy / c;
+  const int ntiles = (i_end + PBN - 1) / PBN;
   for (int kt = 0; kt < ntiles; ++kt) {
     const int st = kt & 1;
     const int j0 = kt * PBN;
-    if (kt + 1 < ntiles) fetch_tile(tp, j0 + PBN);  // in flight during the compute below
+    const bool more = kt + 1 < ntiles;
+    if (more) {  // next tile's loads are in flight during the compute below
+      const uint4 *src = pk + size_t(kt + 1) * PTILE_U4;
+      ta = src[tid];
+      tb = src[tid + PWAVES * 64];
+      talpha = pa[kt + 1];
+    }
 
     // this wave's queries are qi0 .. qi0 + 31; the tile is needed if j0 <= qi0 + 31
     if (active && j0 <= qi0 + 31) {
-      floatx4 s[2][2];
+      floatx4 s0[2], s1[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) s[t][qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int qt = 0; qt < 2; ++qt) {
+        s0[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        s1[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int ks = 0; ks < PKS; ++ks) {
         const uint4 a0 = sK[st][(0 * PKS + ks) * PFRAG + lane];
         const uint4 a1 = sK[st][(1 * PKS + ks) * PFRAG + lane];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-          s[0][qt] = mfma(a0, qf[qt][ks], s[0][qt]);
-          s[1][qt] = mfma(a1, qf[qt][ks], s[1][qt]);
+          s0[qt] = mfma(a0, qf[qt][ks], s0[qt]);
+          s1[qt] = mfma(a1, qf[qt][ks], s1[qt]);
         }
       }
+      // decision bits of this lane's eight keys j0 + 8*quad + e
       const uint32_t abits = sA[st] >> (8 * quad);
+      // far: every key is >= window behind every query of this wave, and inside S
+      const bool far = (qi0 - (j0 + PBN - 1) >= window) && (j0 + PBN <= S);
+      float madd[8];  // 0 for a visible key, -inf otherwise (far tiles: decision only)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) madd[e] = ((abits >> e) & 1u) ? -INFINITY : 0.f;
       uint4 pb[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        const int i = qi0 + 16 * qt + col;
-        float sv[8];
+        float sv[8] = {s0[qt][0], s0[qt][1], s0[qt][2], s0[qt][3],
+                       s1[qt][0], s1[qt][1], s1[qt][2], s1[qt][3]};
+        if (far) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = j0 + 8 * quad + e;
-          const bool marked = (abits >> e) & 1u;
-          const bool vis = (j < S) & (j <= i) & (!marked | (i - j < window));
-          const float raw = (e < 4 ? s[0][qt][e] : s[1][qt][e - 4]) * scale_log2;
-          sv[e] = vis ? raw : -INFINITY;
+          for (int e = 0; e < 8; ++e) sv[e] += madd[e];
+        } else {
+          const int i = qi0 + 16 * qt + col;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = j0 + 8 * quad + e;
+            const bool vis = (j < S) & (j <= i) & ((madd[e] == 0.f) | (i - j < window));
+            sv[e] = vis ? sv[e] : -INFINITY;
+          }
         }
-        float mx = sv[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
         mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        const float m_new = fmaxf(m_run[qt], mx);
-        float p[8];
-        float corr = 1.f;
-        if (m_new == -INFINITY) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = 0.f;
-        } else {
-          corr = m_run[qt] == -INFINITY ? 0.f : exp2f(m_run[qt] - m_new);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = exp2f(sv[e] - m_new);
-        }
-        float ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ps += p[e];
-        l_run[qt] = l_run[qt] * corr + ps;
-        m_run[qt] = m_new;
-        if (__ballot(corr != 1.f)) {
+        float m_ref = m_run[qt];
+        if (__ballot(mx > m_ref + lazy_raw)) {  // some query of the tile needs a new reference
+          const float m_new = mx > m_ref + lazy_raw ? mx : m_ref;
+          const float corr = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+          l_run[qt] *= corr;
 #pragma unroll
           for (int dt = 0; dt < PDT; ++dt) o[dt][qt] *= corr;
+          m_ref = m_new;
+          m_run[qt] = m_new;
         }
+        // arguments are <= kLazy and finite or -inf: the plain hardware exp2 needs no range reduction
+        float p[8];
+        const float mc = m_ref == -INFINITY ? 0.f : m_ref * c;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], c, -mc));
+        l_run[qt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         pb[qt] = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
       }
 #pragma unroll
@@ -239,7 +283,11 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
       }
     }
 
-    if (kt + 1 < ntiles) store_tile(tp, st ^ 1);
+    if (more) {
+      sK[st ^ 1][tid] = ta;
+      sV[st ^ 1][tid] = tb;
+      if (tid == 0) sA[st ^ 1] = talpha;
+    }
     __syncthreads();
   }
 
@@ -261,8 +309,18 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
 }
 
 hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, const void *v,
-                          const float *logit, int seq_len, float sm_scale, float *out,
+                          const float *logit, int seq_len, float sm_scale, float *out, void *ws,
                           hipStream_t st) {
+  const int ntiles = (seq_len + PBN - 1) / PBN;
+  if (s.kv_heads > 65535 || s.batch > 65535) return hipErrorInvalidValue;  // pack grid y, z
+  const size_t tiles = size_t(s.batch) * s.kv_heads * ntiles;
+  uint4 *packed = static_cast<uint4 *>(ws);
+  uint32_t *alpha_words = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + align256(tiles * 16384));
+  hipLaunchKernelGGL(k_prefill_pack, dim3(ntiles, s.kv_heads, s.batch), dim3(512), 0, st, seq_len,
+                     s.kv_heads, ntiles, static_cast<const uint16_t *>(k),
+                     static_cast<const uint16_t *>(v), logit, packed, alpha_words);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int ngh = (s.group + PHPW - 1) / PHPW;
   const int nbh = s.batch * s.kv_heads * ngh;
   const int nqb = (seq_len + PBM - 1) / PBM;
@@ -271,8 +329,7 @@ hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, cons
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_prefill, dim3(unsigned(blocks)), dim3(PWAVES * 64), 0, st, s.batch, seq_len,
                      s.kv_heads, s.group, s.window, sm_scale * 1.4426950408889634f,
-                     static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                     static_cast<const uint16_t *>(v), logit, out);
+                     static_cast<const uint16_t *>(q), packed, alpha_words, out);
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@ EXPORTS = (
     "dms_compact",
     "dms_decode_workspace_bytes",
     "dms_decode_attn",
+    "dms_prefill_workspace_bytes",
     "dms_prefill_attn",
 )
 
@@ -101,7 +102,9 @@ def load() -> ctypes.CDLL:
         "dms_compact": ([SP, CP, P], ctypes.c_int),
         "dms_decode_workspace_bytes": ([SP], ctypes.c_size_t),
         "dms_decode_attn": ([SP, CP, P, P, ctypes.c_float, P, ctypes.c_size_t, P], ctypes.c_int),
-        "dms_prefill_attn": ([SP, P, P, P, P, ctypes.c_int32, ctypes.c_float, P, P], ctypes.c_int),
+        "dms_prefill_workspace_bytes": ([SP, ctypes.c_int32], ctypes.c_size_t),
+        "dms_prefill_attn": ([SP, P, P, P, P, ctypes.c_int32, ctypes.c_float, P, P, ctypes.c_size_t, P],
+                             ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -159,6 +162,12 @@ def dms_decode_attn(shape, cache, q, out, sm_scale, workspace, workspace_bytes, 
                                   float(sm_scale), _p(workspace), int(workspace_bytes), stream)
 
 
-def dms_prefill_attn(shape, q, k, v, logit, seq_len, sm_scale, out, stream) -> int:
+def prefill_workspace_bytes(shape: DmsShape, seq_len: int) -> int:
+    return load().dms_prefill_workspace_bytes(ctypes.byref(shape), int(seq_len))
+
+
+def dms_prefill_attn(shape, q, k, v, logit, seq_len, sm_scale, out, workspace, workspace_bytes,
+                     stream) -> int:
     return load().dms_prefill_attn(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(logit),
-                                   int(seq_len), float(sm_scale), _p(out), stream)
+                                   int(seq_len), float(sm_scale), _p(out), _p(workspace),
+                                   int(workspace_bytes), stream)

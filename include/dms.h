@@ -183,6 +183,13 @@ int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *
                     float sm_scale, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Bytes of prefill workspace for `seq_len` tokens of this shape: keys and
+ * values re-laid out per 32-key tile for the matrix cores, plus one decision
+ * word per tile.  0 if the arguments are invalid.
+ */
+size_t dms_prefill_workspace_bytes(const dms_shape *shape, int32_t seq_len);
+
+/*
  * Masked prefill attention over a whole prompt, no cache (the same rule
  * applied to every query row; atlas.scime.ai summary, "Approach" and
  * "Measured effects" for the 16-token window).  Row i of query head hq
@@ -192,12 +199,14 @@ int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *
  *   k, v   [B][S][Hkv][D] kv_dtype
  *   logit  [B][S][Hkv]    float32
  *   out    [B][S][Hq][D]  float32
+ *   workspace  at least dms_prefill_workspace_bytes(shape, S) bytes, 16-byte
+ *              aligned, no initialisation needed, nothing kept after the call
  * Only batch, kv_heads, group, head_dim (128), window and kv_dtype of
  * `shape` are read.  The cache is filled separately with dms_append.
  */
 int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const void *v,
                      const float *logit, int32_t seq_len, float sm_scale, float *out,
-                     hipStream_t stream);
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

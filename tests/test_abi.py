@@ -99,11 +99,20 @@ def test_prefill_host_errors(L):
     fake = ctypes.c_void_p(0x1000)
     f32 = _shape()
     bf = _shape(kv_dtype=lib.DMS_KV_BF16, head_dim=128)
-    assert L.dms_prefill_attn(ctypes.byref(f32), fake, fake, fake, fake, 16, 0.1, fake, None) \
+    big = 1 << 40
+    assert L.dms_prefill_attn(ctypes.byref(f32), fake, fake, fake, fake, 16, 0.1, fake, fake, big, None) \
         == lib.DMS_EUNSUPPORTED
-    assert L.dms_prefill_attn(ctypes.byref(bf), fake, fake, fake, fake, -2, 0.1, fake, None) == lib.DMS_EINVAL
-    assert L.dms_prefill_attn(ctypes.byref(bf), None, None, None, None, 0, 0.1, None, None) == lib.DMS_OK
-    assert L.dms_prefill_attn(ctypes.byref(bf), None, fake, fake, fake, 16, 0.1, fake, None) == lib.DMS_EINVAL
+    assert L.dms_prefill_attn(ctypes.byref(bf), fake, fake, fake, fake, -2, 0.1, fake, fake, big, None) \
+        == lib.DMS_EINVAL
+    assert L.dms_prefill_attn(ctypes.byref(bf), None, None, None, None, 0, 0.1, None, None, 0, None) \
+        == lib.DMS_OK
+    assert L.dms_prefill_attn(ctypes.byref(bf), None, fake, fake, fake, 16, 0.1, fake, fake, big, None) \
+        == lib.DMS_EINVAL
+    assert L.dms_prefill_attn(ctypes.byref(bf), fake, fake, fake, fake, 16, 0.1, fake, fake, 10, None) \
+        == lib.DMS_EWORKSPACE
+    # 2 sequences x 2 KV heads x ceil(100/32) tiles x 16 KB, plus one word per tile
+    assert lib.prefill_workspace_bytes(bf, 100) == 2 * 2 * 4 * 16384 + 256
+    assert lib.prefill_workspace_bytes(f32, 100) == 0
 
 
 def test_product_package_does_not_import_oracle():

@@ -140,6 +140,55 @@ def cpu_baseline(w, seconds: float = 12.0) -> dict:
                       "float64 NumPy with BLAS limited to 1 thread"}
 
 
+def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
+    """Masked prefill on the 8192-token workload: causal FLOPs per second of one call
+    (pack pass + attention kernel), against the dense bf16 MFMA peak."""
+    import torch
+
+    import workloads as wl
+    from decode_attention_learned_amd import lib, prefill
+    from decode_attention_learned_amd.cache import PAGE, _DTYPES
+
+    w = wl.get(name)
+    dev = torch.device("cuda:0")
+    q, k, v, logit = wl.prefill_inputs(w, device=dev)
+    s_len, d = w.context, w.head_dim
+    out = torch.empty((w.batch, s_len, w.q_heads, d), dtype=torch.float32, device=dev)
+    shape = lib.DmsShape(w.batch, w.kv_heads, w.group, d, PAGE, w.window, 1, 1, _DTYPES[torch.bfloat16])
+    ws = torch.empty((lib.prefill_workspace_bytes(shape, s_len),), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        prefill(q, k, v, logit, window=w.window, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in evs:
+        a.record()
+        prefill(q, k, v, logit, window=w.window, out=out, workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / iters
+    causal = 4.0 * d * s_len * (s_len + 1) / 2 * w.batch * w.q_heads
+    # visible (query, key) pairs: |R(i)| = #{j <= i - w : unmarked} + min(w, i + 1), per (b, h)
+    keep = (logit <= 0).to(torch.int64)                          # [B, S, Hkv]
+    csum = torch.cumsum(keep, dim=1)
+    i = torch.arange(s_len, device=dev)
+    idx = (i - w.window).clamp(min=-1)
+    kept_before = torch.where(idx[None, :, None] >= 0,
+                              csum.gather(1, idx.clamp(min=0)[None, :, None].expand_as(csum)),
+                              torch.zeros_like(csum))
+    pairs = (kept_before + torch.clamp(i + 1, max=w.window)[None, :, None]).sum().item() * w.group
+    visible = 4.0 * d * pairs
+    tflops = causal / (ms * 1e-3) / 1e12
+    return {
+        "workload": name, "batch": w.batch, "seq_len": s_len, "q_heads": w.q_heads,
+        "kv_heads": w.kv_heads, "head_dim": d, "evict_rate": w.evict_rate, "window": w.window,
+        "ms": round(ms, 4), "causal_tflop": round(causal / 1e12, 4),
+        "visible_pair_tflop": round(visible / 1e12, 4),
+        "roofline": {"bound": "mfma", "kernel": "k_prefill_pack + k_prefill", "achieved": round(tflops, 1),
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None},
+    }
+
+
 def traffic_from_profile(bytes_alg_per_launch: float):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary,
     or None if there is none or the kernel source changed since it was taken."""
@@ -199,6 +248,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate", type=float, default=None, metavar="GIB",
                     help="only run the copy/read calibration on a buffer of GIB GiB")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the masked-prefill leg")
+    ap.add_argument("--prefill-only", action="store_true", help="only run the masked-prefill leg")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -215,6 +266,9 @@ def main():
         sys.exit(1)
     if args.calibrate is not None:
         print(json.dumps(calibrate(args.calibrate)), flush=True)
+        return
+    if args.prefill_only:
+        print(json.dumps(prefill_leg()), flush=True)
         return
     dev = torch.device("cuda:0")
     w = wl.get(args.workload)
@@ -332,6 +386,12 @@ def main():
         f"= {kv_gbps:.0f} GB/s ({100 * kv_gbps / HBM_PEAK_GBPS:.1f}% of HBM peak)")
     del inputs, caches, outs
     torch.cuda.empty_cache()
+    if not args.no_prefill:
+        log("[bench] masked prefill, 8192 tokens")
+        result["prefill"] = prefill_leg()
+        log(f"[bench] prefill {result['prefill']['ms']:.3f} ms = "
+            f"{result['prefill']['roofline']['achieved']:.0f} TFLOP/s causal")
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on the host (~{args.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -78,10 +78,10 @@ hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, cons
                           hipStream_t st);
 
 // Prefill workspace: per (b, h, 32-key tile) 8 KB of key fragments, 8 KB of
-// value fragments (head_dim 128, bf16) and one decision word.
+// value fragments (head_dim 128, bf16) and 32 floats of additive mask.
 inline size_t prefill_workspace_bytes(int batch, int kv_heads, int seq_len) {
   const size_t tiles = size_t(batch) * kv_heads * ((size_t(seq_len) + 31) / 32);
-  return align256(tiles * 16384) + align256(tiles * sizeof(uint32_t));
+  return align256(tiles * 16384) + align256(tiles * 32 * sizeof(float));
 }
 
 // ---- wave64 helpers -------------------------------------------------------

@@ -11,18 +11,16 @@
 //
 // Two kernels.  k_prefill_pack re-lays keys and values out once, per (b, h,
 // 32-key tile), in the order of the matrix-core operand fragments (values
-// transposed), with one decision word per tile, into the caller's workspace.
-// k_prefill then only copies whole fragments into LDS.
+// transposed), plus an additive mask per key (0, or -inf for a key marked
+// for eviction), into the caller's workspace.  k_prefill then only copies
+// whole fragments into LDS.
 //
 // Work decomposition.  A workgroup of 8 waves takes 64 query positions of
 // one KV head: wave w serves query head g = 4*hg + (w % 4) of the group and
 // query positions i0 + 32*(w / 4) .. +32.  Keys are consumed in tiles of 32
-// from position 0 up to the causal end of the block.  Each key tile (keys
-// and values) is loaded once per workgroup into LDS, in the order of the
-// matrix-core operand fragments, and serves all four heads; the next tile's
-// global loads are in flight while the current tile is computed.  Tiles that
-// lie wholly `w` or more positions behind every query of a wave need only the
-// decision bits; the tiles on the diagonal band test the full rule.
+// from position 0 up to the causal end of the block.  Each key tile is
+// loaded once per workgroup into LDS (three buffers, one barrier per tile)
+// and serves all four heads.
 //
 // Per tile and wave the two products are the ones of the decode kernel, with
 // query positions in place of heads:
@@ -32,6 +30,23 @@
 // softmax in exp2 form; the two 16-key tiles take their rows from the slot
 // permutation (row 4a + r -> key 8a + r, or 8a + 4 + r) so that each lane's
 // scores are exactly the eight keys it supplies to the PV product.
+//
+// Far and near tiles.  A tile whose keys all lie `w` or more positions behind
+// every query of the workgroup ("far") is masked by the decision alone, which
+// depends on the key only: the QK product starts from the additive mask as
+// its accumulator, so such a tile costs no mask arithmetic.  Far tiles are
+// software-pipelined: the QK product of tile k+1 is issued among the
+// exponentials of tile k, and the PV product of tile k among the checks of
+// tile k+1, so that matrix-core and vector work of one wave overlap.  The
+// few tiles on the diagonal band ("near") apply the full rule per element.
+//
+// Softmax reference.  Each query keeps a reference m (raw score units) that
+// moves only when a score exceeds it by more than kLazy / c (c = scale *
+// log2 e), so every exponent is at most kLazy.  The result does not depend on
+// m (numerator and denominator share it); the check is a per-lane compare
+// and a ballot, and the cross-lane maximum and the rescale of the
+// accumulators run only when some score crosses the threshold.  The row sums
+// add the same bf16-rounded p values that enter the PV product.
 #include "dms_internal.h"
 
 namespace dms {
@@ -39,7 +54,9 @@ namespace dms {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 
 constexpr int PD = 128;            // head dimension
 constexpr int PBN = 32;            // keys per tile
@@ -51,25 +68,160 @@ constexpr int PDT = PD / 16;       // PV products per tile
 constexpr int PFRAG = 64;          // uint4 per operand fragment (64 lanes x 16 bytes)
 constexpr int PK_FRAGS = 2 * PKS;  // key fragments per tile
 constexpr int PV_FRAGS = PDT;      // value fragments per tile
+constexpr int PBUF = 3;            // LDS tile buffers
+constexpr float kLazy = 8.0f;      // largest exponent (log2 units) before the reference moves
 
 __device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-typedef float float2v __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-
 // two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{lo, hi}, bf16x2v));
 }
 
+// acc + lo + hi of a packed bf16 pair, in one v_dot2c_f32_bf16
+__device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+  const bf16x2v one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pair), one, acc, false);
+}
+
 constexpr int PTILE_U4 = (PK_FRAGS + PV_FRAGS) * PFRAG;  // uint4 per packed tile (16 KB)
 
-// One packed tile per (b, h, tile): [key fragments (8 x 1 KB) | value fragments (8 x 1 KB)].
+// One packed tile per (b, h, tile): [key fragments (8 x 1 KB) | value fragments (8 x 1 KB)],
+// and separately 32 floats of additive mask.
 __device__ __forceinline__ size_t tile_index(int b, int h, int tile, int hkv, int ntiles) {
   return (size_t(b) * hkv + h) * ntiles + tile;
+}
+
+// Per-query softmax state of one wave (two query tiles; lane holds column l % 16).
+struct Softmax {
+  float m[2];    // reference, raw score units (-inf until the first visible key)
+  float nmc[2];  // -m * c (0 while m = -inf)
+  float thr[2];  // m + kLazy / c: a score above it moves the reference
+  float l[2];    // running sum of p over this lane's keys
+};
+
+// QK product of one tile for both query tiles, starting from `init`.
+__device__ __forceinline__ void qk_tile(const uint4 *__restrict__ sk, const floatx4 (&init)[2],
+                                        const uint4 (&qf)[2][PKS], int lane, floatx4 (&s)[2][2]) {
+  uint4 ka[2][PKS];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < PKS; ++ks) ka[t][ks] = sk[(t * PKS + ks) * PFRAG + lane];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      floatx4 acc = init[t];
+#pragma unroll
+      for (int ks = 0; ks < PKS; ++ks) acc = mfma(ka[t][ks], qf[qt][ks], acc);
+      s[qt][t] = acc;
+    }
+}
+
+__device__ __forceinline__ float lane_max(const floatx4 (&s)[2]) {
+  return fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+               fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+}
+
+// Does any score of this lane cross its query's threshold?
+__device__ __forceinline__ bool crosses(const floatx4 (&s)[2][2], const Softmax &sm) {
+  return (lane_max(s[0]) > sm.thr[0]) | (lane_max(s[1]) > sm.thr[1]);
+}
+
+// Rare path: move the reference of every query whose tile maximum crossed the
+// threshold, and rescale its accumulators.
+__device__ __forceinline__ void move_reference(const floatx4 (&s)[2][2], Softmax &sm,
+                                               floatx4 (&o)[PDT][2], float c) {
+  const float lazy_raw = kLazy / c;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float mx = lane_max(s[qt]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_old = sm.m[qt];
+    if (mx > sm.thr[qt]) {  // uniform over the four lanes of a query
+      const float corr = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - mx) * c);
+      sm.l[qt] *= corr;
+#pragma unroll
+      for (int dt = 0; dt < PDT; ++dt) o[dt][qt] *= corr;
+      sm.m[qt] = mx;
+      sm.nmc[qt] = -mx * c;
+      sm.thr[qt] = mx + lazy_raw;
+    }
+  }
+}
+
+// p = 2^(s c - m c) for both query tiles, packed to bf16 in PV operand order,
+// and added to the row sums.
+__device__ __forceinline__ void exponentials(const floatx4 (&s)[2][2], Softmax &sm, float c,
+                                             uint4 (&pb)[2]) {
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      p[e] = __builtin_amdgcn_exp2f(fmaf(s[qt][e >> 2][e & 3], c, sm.nmc[qt]));
+    pb[qt] = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
+    float l = sm.l[qt];
+    l = add_pair(pb[qt].x, l);
+    l = add_pair(pb[qt].y, l);
+    l = add_pair(pb[qt].z, l);
+    l = add_pair(pb[qt].w, l);
+    sm.l[qt] = l;
+  }
+}
+
+__device__ __forceinline__ void pv_tile(const uint4 *__restrict__ sv, const uint4 (&pb)[2], int lane,
+                                        floatx4 (&o)[PDT][2]) {
+#pragma unroll
+  for (int dt = 0; dt < PDT; ++dt) {
+    const uint4 va = sv[dt * PFRAG + lane];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma(va, pb[qt], o[dt][qt]);
+  }
+}
+
+// One pipelined far step: exponentials and PV product of the current tile
+// (scores in s), interleaved with the QK product of the next far tile, whose
+// scores replace s.  Returns whether any of the new scores crosses a threshold.
+__device__ __forceinline__ bool far_step(const uint4 *__restrict__ sk_next,
+                                         const floatx4 *__restrict__ sb_next,
+                                         const uint4 *__restrict__ sv_cur,
+                                         const uint4 (&qf)[2][PKS], floatx4 (&s)[2][2],
+                                         Softmax &sm, floatx4 (&o)[PDT][2], float c, int lane,
+                                         int quad) {
+  floatx4 init[2] = {sb_next[2 * quad], sb_next[2 * quad + 1]};
+  floatx4 sn[2][2];
+  qk_tile(sk_next, init, qf, lane, sn);
+  uint4 pb[2];
+  exponentials(s, sm, c, pb);
+  pv_tile(sv_cur, pb, lane, o);
+  const bool cross = crosses(sn, sm);
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) s[qt][t] = sn[qt][t];
+
+  // Issue order: operand reads first, then each matrix product followed by
+  // two vector instructions (exponentials while the QK products run, the
+  // threshold compares while the PV products run).
+  __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);  // K fragments + mask
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // V fragments
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+  }
+  return cross;
 }
 
 }  // namespace
@@ -82,7 +234,7 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
                                                       const uint16_t *__restrict__ v,
                                                       const float *__restrict__ logit,
                                                       uint4 *__restrict__ packed,
-                                                      uint32_t *__restrict__ alpha_words) {
+                                                      float *__restrict__ mask) {
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x;
   const int j0 = tile * PBN;
@@ -105,10 +257,10 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
   const int ks = dc >> 2, qd = dc & 3;
   kdst[(tt * PKS + ks) * PFRAG + qd * 16 + row] = kp;
   *reinterpret_cast<uint4 *>(&sv[jj][dc * 8]) = vp;
-  if (t < kWave) {
-    const bool marked = t < PBN && j0 + t < S && evict_decision(logit[(size_t(b) * S + j0 + t) * hkv + h]);
-    const uint64_t m = __ballot(marked);
-    if (t == 0) alpha_words[T] = uint32_t(m);
+  // additive mask of key j0 + t: -inf if marked for eviction (or past the end)
+  if (t < PBN) {
+    const bool marked = j0 + t >= S || evict_decision(logit[(size_t(b) * S + j0 + t) * hkv + h]);
+    mask[T * PBN + t] = marked ? -INFINITY : 0.f;
   }
   __syncthreads();
   // value fragment dt = t / 64, lane l = t % 64: dim dt*16 + l % 16, keys 8*(l/16) .. +8
@@ -123,8 +275,7 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
 
 __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
     int batch, int S, int hkv, int G, int window, float scale_log2, const uint16_t *__restrict__ q,
-    const uint4 *__restrict__ packed, const uint32_t *__restrict__ alpha_words,
-    float *__restrict__ out) {
+    const uint4 *__restrict__ packed, const floatx4 *__restrict__ mask, float *__restrict__ out) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
@@ -154,10 +305,14 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
   const int hq = h * G + (active ? g : 0);
   const int qi0 = qb * PBM + (wave / PHPW) * 32;  // this wave's first query position
   const int i_end = min(S, qb * PBM + PBM);       // workgroup's causal key end
+  const int ntiles = (i_end + PBN - 1) / PBN;
+  // far tiles: j0 + 31 + window <= qb * PBM, i.e. behind every query by >= window
+  const int far_x = qb * PBM - window - (PBN - 1);
+  const int nfar = far_x >= 0 ? min(ntiles, far_x / PBN + 1) : 0;
 
-  __shared__ uint4 sK[2][PK_FRAGS * PFRAG];
-  __shared__ uint4 sV[2][PV_FRAGS * PFRAG];
-  __shared__ uint32_t sA[2];
+  __shared__ uint4 sK[PBUF][PK_FRAGS * PFRAG];
+  __shared__ uint4 sV[PBUF][PV_FRAGS * PFRAG];
+  __shared__ floatx4 sB[PBUF][PBN / 4];
 
   // Q^T operand for two query tiles: query qi0 + 16*qt + col, dims ks*32 + quad*8
   uint4 qf[2][PKS];
@@ -178,123 +333,105 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
   for (int dt = 0; dt < PDT; ++dt)
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) o[dt][qt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  Softmax sm;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    sm.m[qt] = -INFINITY;
+    sm.nmc[qt] = 0.f;
+    sm.thr[qt] = -INFINITY;
+    sm.l[qt] = 0.f;
+  }
+  const float c = scale_log2;
 
   const int ntiles_all = (S + PBN - 1) / PBN;
   const uint4 *pk = packed + tile_index(b, h, 0, hkv, ntiles_all) * PTILE_U4;
-  const uint32_t *pa = alpha_words + tile_index(b, h, 0, hkv, ntiles_all);
+  const floatx4 *pm = mask + tile_index(b, h, 0, hkv, ntiles_all) * (PBN / 4);
 
-  // thread t copies uint4 t and t + 512 of the 16 KB packed tile (keys, then values)
-  uint4 ta = pk[tid], tb = pk[tid + PWAVES * 64];
-  uint32_t talpha = pa[0];
-  sK[0][tid] = ta;
-  sV[0][tid] = tb;
-  if (tid == 0) sA[0] = talpha;
+  // Tile pipeline: tile t lives in buffer t % 3.  Tile t + 2 is stored at the
+  // end of step t (its buffer held tile t - 1, read no later than step t - 1),
+  // and its global loads are issued one step earlier.  Thread t copies uint4 t
+  // and t + 512 of the 16 KB packed tile; threads 0..7 copy the mask.
+  uint4 ta, tb;
+  floatx4 tm;
+  auto gload = [&](int tile) {
+    const uint4 *src = pk + size_t(tile) * PTILE_U4;
+    ta = src[tid];
+    tb = src[tid + PWAVES * 64];
+    if (tid < PBN / 4) tm = pm[size_t(tile) * (PBN / 4) + tid];
+  };
+  auto lstore = [&](int buf) {
+    sK[buf][tid] = ta;
+    sV[buf][tid] = tb;
+    if (tid < PBN / 4) sB[buf][tid] = tm;
+  };
+  gload(0);
+  lstore(0);
+  if (ntiles > 1) {
+    gload(1);
+    lstore(1);
+  }
+  if (ntiles > 2) gload(2);
   __syncthreads();
-
-  // Lazy rescaling: a query's reference maximum m_run (raw score units) moves
-  // only when a tile's maximum exceeds it by more than kLazy/c, so p <= 2^kLazy.
-  // The result is unchanged (numerator and denominator share the reference),
-  // and the rescale of the accumulators becomes rare after the first tiles.
-  constexpr float kLazy = 8.0f;
-  const float c = scale_log2;
-  const float lazy_raw = kLazy / c;
-  const int ntiles = (i_end + PBN - 1) / PBN;
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int st = kt & 1;
-    const int j0 = kt * PBN;
-    const bool more = kt + 1 < ntiles;
-    if (more) {  // next tile's loads are in flight during the compute below
-      const uint4 *src = pk + size_t(kt + 1) * PTILE_U4;
-      ta = src[tid];
-      tb = src[tid + PWAVES * 64];
-      talpha = pa[kt + 1];
-    }
-
-    // this wave's queries are qi0 .. qi0 + 31; the tile is needed if j0 <= qi0 + 31
-    if (active && j0 <= qi0 + 31) {
-      floatx4 s0[2], s1[2];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        s0[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        s1[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int ks = 0; ks < PKS; ++ks) {
-        const uint4 a0 = sK[st][(0 * PKS + ks) * PFRAG + lane];
-        const uint4 a1 = sK[st][(1 * PKS + ks) * PFRAG + lane];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          s0[qt] = mfma(a0, qf[qt][ks], s0[qt]);
-          s1[qt] = mfma(a1, qf[qt][ks], s1[qt]);
-        }
-      }
-      // decision bits of this lane's eight keys j0 + 8*quad + e
-      const uint32_t abits = sA[st] >> (8 * quad);
-      // far: every key is >= window behind every query of this wave, and inside S
-      const bool far = (qi0 - (j0 + PBN - 1) >= window) && (j0 + PBN <= S);
-      float madd[8];  // 0 for a visible key, -inf otherwise (far tiles: decision only)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) madd[e] = ((abits >> e) & 1u) ? -INFINITY : 0.f;
-      uint4 pb[2];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        float sv[8] = {s0[qt][0], s0[qt][1], s0[qt][2], s0[qt][3],
-                       s1[qt][0], s1[qt][1], s1[qt][2], s1[qt][3]};
-        if (far) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sv[e] += madd[e];
-        } else {
-          const int i = qi0 + 16 * qt + col;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = j0 + 8 * quad + e;
-            const bool vis = (j < S) & (j <= i) & ((madd[e] == 0.f) | (i - j < window));
-            sv[e] = vis ? sv[e] : -INFINITY;
-          }
-        }
-        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        float m_ref = m_run[qt];
-        if (__ballot(mx > m_ref + lazy_raw)) {  // some query of the tile needs a new reference
-          const float m_new = mx > m_ref + lazy_raw ? mx : m_ref;
-          const float corr = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
-          l_run[qt] *= corr;
-#pragma unroll
-          for (int dt = 0; dt < PDT; ++dt) o[dt][qt] *= corr;
-          m_ref = m_new;
-          m_run[qt] = m_new;
-        }
-        // arguments are <= kLazy and finite or -inf: the plain hardware exp2 needs no range reduction
-        float p[8];
-        const float mc = m_ref == -INFINITY ? 0.f : m_ref * c;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], c, -mc));
-        l_run[qt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        pb[qt] = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
-      }
-#pragma unroll
-      for (int dt = 0; dt < PDT; ++dt) {
-        const uint4 va = sV[st][dt * PFRAG + lane];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma(va, pb[qt], o[dt][qt]);
-      }
-    }
-
-    if (more) {
-      sK[st ^ 1][tid] = ta;
-      sV[st ^ 1][tid] = tb;
-      if (tid == 0) sA[st ^ 1] = talpha;
-    }
+  auto advance = [&](int t) {  // end of step t
+    if (t + 2 < ntiles) lstore((t + 2) % PBUF);
+    if (t + 3 < ntiles) gload(t + 3);
     __syncthreads();
+  };
+
+  floatx4 s[2][2];
+  if (nfar > 0) {
+    if (active) {
+      floatx4 init[2] = {sB[0][2 * quad], sB[0][2 * quad + 1]};
+      qk_tile(sK[0], init, qf, lane, s);
+      if (__ballot(crosses(s, sm))) move_reference(s, sm, o, c);
+    }
+    for (int t = 0; t + 1 < nfar; ++t) {
+      if (active) {
+        const int nb = (t + 1) % PBUF;
+        const bool cross = far_step(sK[nb], sB[nb], sV[t % PBUF], qf, s, sm, o, c, lane, quad);
+        if (__ballot(cross)) move_reference(s, sm, o, c);
+      }
+      advance(t);
+    }
+    if (active) {  // last far tile: no next QK product
+      uint4 pb[2];
+      exponentials(s, sm, c, pb);
+      pv_tile(sV[(nfar - 1) % PBUF], pb, lane, o);
+    }
+    advance(nfar - 1);
+  }
+
+  // near tiles: the full rule per (query, key)
+  for (int t = nfar; t < ntiles; ++t) {
+    const int j0 = t * PBN;
+    const int buf = t % PBUF;
+    if (active && j0 <= qi0 + 31) {
+      const floatx4 zero[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+      qk_tile(sK[buf], zero, qf, lane, s);
+      const floatx4 mb[2] = {sB[buf][2 * quad], sB[buf][2 * quad + 1]};
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const int i = qi0 + 16 * qt + col;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + 8 * quad + e;
+          const bool keep = mb[e >> 2][e & 3] == 0.f;
+          const bool vis = (j < S) & (j <= i) & (keep | (i - j < window));
+          s[qt][e >> 2][e & 3] = vis ? s[qt][e >> 2][e & 3] : -INFINITY;
+        }
+      }
+      if (__ballot(crosses(s, sm))) move_reference(s, sm, o, c);
+      uint4 pb[2];
+      exponentials(s, sm, c, pb);
+      pv_tile(sV[buf], pb, lane, o);
+    }
+    advance(t);
   }
 
   if (!active) return;
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    float l = l_run[qt];
+    float l = sm.l[qt];
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -315,10 +452,10 @@ hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, cons
   if (s.kv_heads > 65535 || s.batch > 65535) return hipErrorInvalidValue;  // pack grid y, z
   const size_t tiles = size_t(s.batch) * s.kv_heads * ntiles;
   uint4 *packed = static_cast<uint4 *>(ws);
-  uint32_t *alpha_words = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + align256(tiles * 16384));
+  float *mask = reinterpret_cast<float *>(static_cast<char *>(ws) + align256(tiles * 16384));
   hipLaunchKernelGGL(k_prefill_pack, dim3(ntiles, s.kv_heads, s.batch), dim3(512), 0, st, seq_len,
                      s.kv_heads, ntiles, static_cast<const uint16_t *>(k),
-                     static_cast<const uint16_t *>(v), logit, packed, alpha_words);
+                     static_cast<const uint16_t *>(v), logit, packed, mask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ngh = (s.group + PHPW - 1) / PHPW;
@@ -329,7 +466,8 @@ hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, cons
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_prefill, dim3(unsigned(blocks)), dim3(PWAVES * 64), 0, st, s.batch, seq_len,
                      s.kv_heads, s.group, s.window, sm_scale * 1.4426950408889634f,
-                     static_cast<const uint16_t *>(q), packed, alpha_words, out);
+                     static_cast<const uint16_t *>(q), packed,
+                     reinterpret_cast<const floatx4 *>(mask), out);
   return hipGetLastError();
 }
 

@@ -184,8 +184,8 @@ int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *
 
 /*
  * Bytes of prefill workspace for `seq_len` tokens of this shape: keys and
- * values re-laid out per 32-key tile for the matrix cores, plus one decision
- * word per tile.  0 if the arguments are invalid.
+ * values re-laid out per 32-key tile for the matrix cores, plus one float
+ * per key (its decision as an additive mask).  0 if the arguments are invalid.
  */
 size_t dms_prefill_workspace_bytes(const dms_shape *shape, int32_t seq_len);
 

@@ -111,7 +111,7 @@ def test_prefill_host_errors(L):
     assert L.dms_prefill_attn(ctypes.byref(bf), fake, fake, fake, fake, 16, 0.1, fake, fake, 10, None) \
         == lib.DMS_EWORKSPACE
     # 2 sequences x 2 KV heads x ceil(100/32) tiles x 16 KB, plus one word per tile
-    assert lib.prefill_workspace_bytes(bf, 100) == 2 * 2 * 4 * 16384 + 256
+    assert lib.prefill_workspace_bytes(bf, 100) == 2 * 2 * 4 * 16384 + 2 * 2 * 4 * 32 * 4
     assert lib.prefill_workspace_bytes(f32, 100) == 0
 
 

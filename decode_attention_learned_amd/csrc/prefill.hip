@@ -19,8 +19,8 @@
 // one KV head: wave w serves query head g = 4*hg + (w % 4) of the group and
 // query positions i0 + 32*(w / 4) .. +32.  Keys are consumed in tiles of 32
 // from position 0 up to the causal end of the block.  Each key tile is
-// loaded once per workgroup into LDS (three buffers, one barrier per tile)
-// and serves all four heads.
+// loaded once per workgroup into LDS (four buffers) and serves all four
+// heads.
 //
 // Per tile and wave the two products are the ones of the decode kernel, with
 // query positions in place of heads:
@@ -31,14 +31,18 @@
 // permutation (row 4a + r -> key 8a + r, or 8a + 4 + r) so that each lane's
 // scores are exactly the eight keys it supplies to the PV product.
 //
+// Two phases per tile.  Phase 1 (matrix cores) computes the scores of tile k
+// and the PV product of tile k-1; phase 2 (vector unit) masks, checks and
+// exponentiates the scores of tile k.  Waves 0-3 and waves 4-7 share the four
+// SIMDs and run half a tile apart (a workgroup barrier after every phase):
+// while one wave of a SIMD is in phase 1 the other is in phase 2, so the
+// matrix products of one overlap the softmax of the other.
+//
 // Far and near tiles.  A tile whose keys all lie `w` or more positions behind
 // every query of the workgroup ("far") is masked by the decision alone, which
 // depends on the key only: the QK product starts from the additive mask as
-// its accumulator, so such a tile costs no mask arithmetic.  Far tiles are
-// software-pipelined: the QK product of tile k+1 is issued among the
-// exponentials of tile k, and the PV product of tile k among the checks of
-// tile k+1, so that matrix-core and vector work of one wave overlap.  The
-// few tiles on the diagonal band ("near") apply the full rule per element.
+// its accumulator, so such a tile costs no mask arithmetic.  The few tiles on
+// the diagonal band ("near") apply the full rule per element in phase 2.
 //
 // Softmax reference.  Each query keeps a reference m (raw score units) that
 // moves only when a score exceeds it by more than kLazy / c (c = scale *
@@ -68,7 +72,7 @@ constexpr int PDT = PD / 16;       // PV products per tile
 constexpr int PFRAG = 64;          // uint4 per operand fragment (64 lanes x 16 bytes)
 constexpr int PK_FRAGS = 2 * PKS;  // key fragments per tile
 constexpr int PV_FRAGS = PDT;      // value fragments per tile
-constexpr int PBUF = 3;            // LDS tile buffers
+constexpr int PBUF = 4;            // LDS tile buffers
 constexpr float kLazy = 8.0f;      // largest exponent (log2 units) before the reference moves
 
 __device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
@@ -142,16 +146,17 @@ __device__ __forceinline__ void move_reference(const floatx4 (&s)[2][2], Softmax
     float mx = lane_max(s[qt]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    // branch-free: queries whose maximum stays under the threshold get factor 1
+    const bool move = mx > sm.thr[qt];  // uniform over the four lanes of a query
     const float m_old = sm.m[qt];
-    if (mx > sm.thr[qt]) {  // uniform over the four lanes of a query
-      const float corr = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - mx) * c);
-      sm.l[qt] *= corr;
+    const float corr =
+        move ? (m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - mx) * c)) : 1.f;
+    sm.l[qt] *= corr;
 #pragma unroll
-      for (int dt = 0; dt < PDT; ++dt) o[dt][qt] *= corr;
-      sm.m[qt] = mx;
-      sm.nmc[qt] = -mx * c;
-      sm.thr[qt] = mx + lazy_raw;
-    }
+    for (int dt = 0; dt < PDT; ++dt) o[dt][qt] *= corr;
+    sm.m[qt] = move ? mx : m_old;
+    sm.nmc[qt] = move ? -mx * c : sm.nmc[qt];
+    sm.thr[qt] = move ? mx + lazy_raw : sm.thr[qt];
   }
 }
 
@@ -185,43 +190,56 @@ __device__ __forceinline__ void pv_tile(const uint4 *__restrict__ sv, const uint
   }
 }
 
-// One pipelined far step: exponentials and PV product of the current tile
-// (scores in s), interleaved with the QK product of the next far tile, whose
-// scores replace s.  Returns whether any of the new scores crosses a threshold.
-__device__ __forceinline__ bool far_step(const uint4 *__restrict__ sk_next,
-                                         const floatx4 *__restrict__ sb_next,
-                                         const uint4 *__restrict__ sv_cur,
-                                         const uint4 (&qf)[2][PKS], floatx4 (&s)[2][2],
-                                         Softmax &sm, floatx4 (&o)[PDT][2], float c, int lane,
-                                         int quad) {
-  floatx4 init[2] = {sb_next[2 * quad], sb_next[2 * quad + 1]};
-  floatx4 sn[2][2];
-  qk_tile(sk_next, init, qf, lane, sn);
-  uint4 pb[2];
-  exponentials(s, sm, c, pb);
-  pv_tile(sv_cur, pb, lane, o);
-  const bool cross = crosses(sn, sm);
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) s[qt][t] = sn[qt][t];
+// Phase 1 of tile k: PV product of tile k - 1 and QK product of tile k (from
+// the additive mask on far tiles, from zero on near ones).  The wave raises
+// its issue priority for the phase, so that the SIMD's other wave (in phase
+// 2) fills the gaps between matrix instructions rather than delaying them.
+__device__ __forceinline__ void phase1(int k, int ntw, int nfar, bool active,
+                                       const uint4 (*sK)[PK_FRAGS * PFRAG],
+                                       const uint4 (*sV)[PV_FRAGS * PFRAG],
+                                       const floatx4 (*sB)[PBN / 4], const uint4 (&qf)[2][PKS],
+                                       floatx4 (&s)[2][2], const uint4 (&pb)[2],
+                                       floatx4 (&o)[PDT][2], int lane, int quad) {
+  if (!active) return;
+  __builtin_amdgcn_s_setprio(2);
+  if (k >= 1 && k - 1 < ntw) pv_tile(sV[(k - 1) % PBUF], pb, lane, o);
+  if (k < ntw) {
+    const int buf = k % PBUF;
+    floatx4 init[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    if (k < nfar) {
+      init[0] = sB[buf][2 * quad];
+      init[1] = sB[buf][2 * quad + 1];
+    }
+    qk_tile(sK[buf], init, qf, lane, s);
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
 
-  // Issue order: operand reads first, then each matrix product followed by
-  // two vector instructions (exponentials while the QK products run, the
-  // threshold compares while the PV products run).
-  __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);  // K fragments + mask
+// Phase 2 of tile k: the full rule on near tiles, the reference check, and
+// the exponentials.
+__device__ __forceinline__ void phase2(int k, int ntw, int nfar, bool active, int S, int window,
+                                       int qi0, int col, int quad, const floatx4 (*sB)[PBN / 4],
+                                       floatx4 (&s)[2][2], Softmax &sm, floatx4 (&o)[PDT][2],
+                                       uint4 (&pb)[2], float c) {
+  if (!active || k < 0 || k >= ntw) return;
+  if (k >= nfar) {
+    const int j0 = k * PBN;
+    const int buf = k % PBUF;
+    const floatx4 mb[2] = {sB[buf][2 * quad], sB[buf][2 * quad + 1]};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // V fragments
-  }
+    for (int qt = 0; qt < 2; ++qt) {
+      const int i = qi0 + 16 * qt + col;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      for (int e = 0; e < 8; ++e) {
+        const int j = j0 + 8 * quad + e;
+        const bool keep = mb[e >> 2][e & 3] == 0.f;
+        const bool vis = (j < S) & (j <= i) & (keep | (i - j < window));
+        s[qt][e >> 2][e & 3] = vis ? s[qt][e >> 2][e & 3] : -INFINITY;
+      }
+    }
   }
-  return cross;
+  if (__ballot(crosses(s, sm))) move_reference(s, sm, o, c);
+  exponentials(s, sm, c, pb);
 }
 
 }  // namespace
@@ -347,86 +365,60 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
   const uint4 *pk = packed + tile_index(b, h, 0, hkv, ntiles_all) * PTILE_U4;
   const floatx4 *pm = mask + tile_index(b, h, 0, hkv, ntiles_all) * (PBN / 4);
 
-  // Tile pipeline: tile t lives in buffer t % 3.  Tile t + 2 is stored at the
-  // end of step t (its buffer held tile t - 1, read no later than step t - 1),
-  // and its global loads are issued one step earlier.  Thread t copies uint4 t
-  // and t + 512 of the 16 KB packed tile; threads 0..7 copy the mask.
+  // Tile t lives in buffer t % 4.  Every wave runs the same loop, phase 1
+  // and phase 2 of tile k with a barrier after each; waves 4-7 pass one
+  // barrier more before the loop and waves 0-3 one more after it, so that
+  // between barriers m-1 and m (window m)
+  //   waves 0-3 run phase 1 of tile k in window 2k+1 and phase 2 in 2k+2,
+  //   waves 4-7 run phase 1 of tile k in window 2k+2 and phase 2 in 2k+3.
+  // Buffer t % 4 is read in windows 2t+1 .. 2t+4 (keys and mask of tile t in
+  // its phase 1 and 2, values in phase 1 of tile t+1).  After phase 2 of tile
+  // k each thread stores its share of tile k+2 (windows 2k+2 and 2k+3, after
+  // the last read of tile k-2 in window 2k) and loads its share of tile k+3.
+  // Thread t copies uint4 t and t + 512 of the 16 KB packed tile; threads
+  // 0..7 copy the mask.
   uint4 ta, tb;
   floatx4 tm;
-  auto gload = [&](int tile) {
-    const uint4 *src = pk + size_t(tile) * PTILE_U4;
-    ta = src[tid];
-    tb = src[tid + PWAVES * 64];
-    if (tid < PBN / 4) tm = pm[size_t(tile) * (PBN / 4) + tid];
-  };
-  auto lstore = [&](int buf) {
-    sK[buf][tid] = ta;
-    sV[buf][tid] = tb;
-    if (tid < PBN / 4) sB[buf][tid] = tm;
-  };
-  gload(0);
-  lstore(0);
+#define DMS_PF_GLOAD(tile)                                         \
+  do {                                                             \
+    const uint4 *src_ = pk + size_t(tile) * PTILE_U4;              \
+    ta = src_[tid];                                                \
+    tb = src_[tid + PWAVES * 64];                                  \
+    if (tid < PBN / 4) tm = pm[size_t(tile) * (PBN / 4) + tid];    \
+  } while (0)
+#define DMS_PF_LSTORE(buf)                    \
+  do {                                        \
+    sK[buf][tid] = ta;                        \
+    sV[buf][tid] = tb;                        \
+    if (tid < PBN / 4) sB[buf][tid] = tm;     \
+  } while (0)
+  DMS_PF_GLOAD(0);
+  DMS_PF_LSTORE(0);
   if (ntiles > 1) {
-    gload(1);
-    lstore(1);
+    DMS_PF_GLOAD(1);
+    DMS_PF_LSTORE(1);
   }
-  if (ntiles > 2) gload(2);
+  if (ntiles > 2) DMS_PF_GLOAD(2);
   __syncthreads();
-  auto advance = [&](int t) {  // end of step t
-    if (t + 2 < ntiles) lstore((t + 2) % PBUF);
-    if (t + 3 < ntiles) gload(t + 3);
-    __syncthreads();
-  };
 
+  // tiles this wave needs: keys up to its last query position
+  const int ntw = min(ntiles, (qi0 + 31) / PBN + 1);
+  const bool lead = wave < PWAVES / 2;
   floatx4 s[2][2];
-  if (nfar > 0) {
-    if (active) {
-      floatx4 init[2] = {sB[0][2 * quad], sB[0][2 * quad + 1]};
-      qk_tile(sK[0], init, qf, lane, s);
-      if (__ballot(crosses(s, sm))) move_reference(s, sm, o, c);
-    }
-    for (int t = 0; t + 1 < nfar; ++t) {
-      if (active) {
-        const int nb = (t + 1) % PBUF;
-        const bool cross = far_step(sK[nb], sB[nb], sV[t % PBUF], qf, s, sm, o, c, lane, quad);
-        if (__ballot(cross)) move_reference(s, sm, o, c);
-      }
-      advance(t);
-    }
-    if (active) {  // last far tile: no next QK product
-      uint4 pb[2];
-      exponentials(s, sm, c, pb);
-      pv_tile(sV[(nfar - 1) % PBUF], pb, lane, o);
-    }
-    advance(nfar - 1);
-  }
+  uint4 pb[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
 
-  // near tiles: the full rule per (query, key)
-  for (int t = nfar; t < ntiles; ++t) {
-    const int j0 = t * PBN;
-    const int buf = t % PBUF;
-    if (active && j0 <= qi0 + 31) {
-      const floatx4 zero[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-      qk_tile(sK[buf], zero, qf, lane, s);
-      const floatx4 mb[2] = {sB[buf][2 * quad], sB[buf][2 * quad + 1]};
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const int i = qi0 + 16 * qt + col;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = j0 + 8 * quad + e;
-          const bool keep = mb[e >> 2][e & 3] == 0.f;
-          const bool vis = (j < S) & (j <= i) & (keep | (i - j < window));
-          s[qt][e >> 2][e & 3] = vis ? s[qt][e >> 2][e & 3] : -INFINITY;
-        }
-      }
-      if (__ballot(crosses(s, sm))) move_reference(s, sm, o, c);
-      uint4 pb[2];
-      exponentials(s, sm, c, pb);
-      pv_tile(sV[buf], pb, lane, o);
-    }
-    advance(t);
+  if (!lead) __syncthreads();
+  for (int k = 0; k <= ntiles; ++k) {
+    phase1(k, ntw, nfar, active, sK, sV, sB, qf, s, pb, o, lane, quad);
+    __syncthreads();
+    phase2(k, ntw, nfar, active, S, window, qi0, col, quad, sB, s, sm, o, pb, c);
+    if (k + 2 < ntiles) DMS_PF_LSTORE((k + 2) % PBUF);
+    if (k + 3 < ntiles) DMS_PF_GLOAD(k + 3);
+    __syncthreads();
   }
+  if (lead) __syncthreads();
+#undef DMS_PF_LSTORE
+#undef DMS_PF_GLOAD
 
   if (!active) return;
 #pragma unroll

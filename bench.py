@@ -140,9 +140,48 @@ def cpu_baseline(w, seconds: float = 12.0) -> dict:
                       "float64 NumPy with BLAS limited to 1 thread"}
 
 
+def _time_calls(fn, iters: int) -> float:
+    """Mean milliseconds of fn() over `iters` calls, HIP events on the current stream."""
+    import torch
+
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / iters
+
+
+def gathered_tiles(keep, s_len: int, window: int, block: int = 64, tile: int = 32) -> int:
+    """Key tiles the gathered kernel processes, summed over units and query
+    blocks: the gathered kept keys up to the block's last query - w, plus the
+    dense tiles of the band (q0 - w, last query]."""
+    import torch
+
+    csum = torch.cumsum(keep, dim=1)                               # [B, S, Hkv] kept at <= position
+    total = 0
+    for q0 in range(0, s_len, block):
+        i_max = min(s_len, q0 + block) - 1
+        x = i_max - window
+        n_any = csum[:, x, :] if x >= 0 else torch.zeros_like(csum[:, 0, :])
+        ngt = (n_any + tile - 1) // tile
+        nb = i_max // tile - max(0, q0 - window + 1) // tile + 1
+        total += int(ngt.sum().item()) + nb * keep.shape[0] * keep.shape[2]
+    return total
+
+
 def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
-    """Masked prefill on the 8192-token workload: causal FLOPs per second of one call
-    (pack pass + attention kernel), against the dense bf16 MFMA peak."""
+    """Masked prefill on the 8192-token workload, both kernels.
+
+    Dense (dms_prefill_attn): causal FLOPs per second of one call (pack pass +
+    attention kernel) against the dense bf16 MFMA peak.  Gathered
+    (dms_prefill_attn_gathered): the same result; its roofline uses the MFMA
+    work it executes (key tiles x 64 queries x heads), and the causal FLOPs
+    over its time are reported as the equivalent dense rate."""
     import torch
 
     import workloads as wl
@@ -155,17 +194,10 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
     s_len, d = w.context, w.head_dim
     out = torch.empty((w.batch, s_len, w.q_heads, d), dtype=torch.float32, device=dev)
     shape = lib.DmsShape(w.batch, w.kv_heads, w.group, d, PAGE, w.window, 1, 1, _DTYPES[torch.bfloat16])
-    ws = torch.empty((lib.prefill_workspace_bytes(shape, s_len),), dtype=torch.uint8, device=dev)
-    for _ in range(2):
-        prefill(q, k, v, logit, window=w.window, out=out, workspace=ws)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
-    for a, b in evs:
-        a.record()
-        prefill(q, k, v, logit, window=w.window, out=out, workspace=ws)
-        b.record()
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in evs) / iters
+    ws = torch.empty((lib.prefill_gathered_workspace_bytes(shape, s_len),), dtype=torch.uint8, device=dev)
+    ms = _time_calls(lambda: prefill(q, k, v, logit, window=w.window, out=out, workspace=ws), iters)
+    ms_g = _time_calls(lambda: prefill(q, k, v, logit, window=w.window, out=out, workspace=ws,
+                                       method="gathered"), iters)
     causal = 4.0 * d * s_len * (s_len + 1) / 2 * w.batch * w.q_heads
     # visible (query, key) pairs: |R(i)| = #{j <= i - w : unmarked} + min(w, i + 1), per (b, h)
     keep = (logit <= 0).to(torch.int64)                          # [B, S, Hkv]
@@ -178,6 +210,10 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
     pairs = (kept_before + torch.clamp(i + 1, max=w.window)[None, :, None]).sum().item() * w.group
     visible = 4.0 * d * pairs
     tflops = causal / (ms * 1e-3) / 1e12
+    # executed MFMA work of the gathered kernel: per key tile and workgroup,
+    # QK and PV products over 32 keys x 64 queries x G heads x D
+    executed = 4.0 * 32 * 64 * d * w.group * gathered_tiles(keep, s_len, w.window)
+    g_tflops = executed / (ms_g * 1e-3) / 1e12
     return {
         "workload": name, "batch": w.batch, "seq_len": s_len, "q_heads": w.q_heads,
         "kv_heads": w.kv_heads, "head_dim": d, "evict_rate": w.evict_rate, "window": w.window,
@@ -186,6 +222,15 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
         "roofline": {"bound": "mfma", "kernel": "k_prefill_pack + k_prefill", "achieved": round(tflops, 1),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None},
+        "gathered": {
+            "ms": round(ms_g, 4), "speedup_vs_dense": round(ms / ms_g, 2),
+            "causal_equivalent_tflops": round(causal / (ms_g * 1e-3) / 1e12, 1),
+            "executed_tflop": round(executed / 1e12, 4),
+            "roofline": {"bound": "mfma",
+                         "kernel": "k_prefill_pack + k_sparse_scan + k_sparse_pack + k_prefill_gathered",
+                         "achieved": round(g_tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(g_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None},
+        },
     }
 
 
@@ -390,7 +435,8 @@ def main():
         log("[bench] masked prefill, 8192 tokens")
         result["prefill"] = prefill_leg()
         log(f"[bench] prefill {result['prefill']['ms']:.3f} ms = "
-            f"{result['prefill']['roofline']['achieved']:.0f} TFLOP/s causal")
+            f"{result['prefill']['roofline']['achieved']:.0f} TFLOP/s causal; gathered "
+            f"{result['prefill']['gathered']['ms']:.3f} ms")
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on the host (~{args.cpu_seconds:.0f} s)")

@@ -153,10 +153,16 @@ class DmsCache:
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logit: torch.Tensor,
             window: int = 16, sm_scale: float | None = None,
-            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+            method: str = "dense") -> torch.Tensor:
     """Masked DMS prefill: q [B, S, Hq, D], k, v [B, S, Hkv, D] bf16, logit [B, S, Hkv] f32.
 
-    `workspace` (uint8, at least prefill_workspace_bytes) is allocated when not given."""
+    method "dense" runs dms_prefill_attn (every causal tile, masked), "gathered"
+    runs dms_prefill_attn_gathered (gathered kept keys plus the window band).
+    `workspace` (uint8, at least the method's workspace size) is allocated when
+    not given."""
+    if method not in ("dense", "gathered"):
+        raise ValueError(f"unknown prefill method {method!r}")
     lib.load()
     b, s, hq, d = q.shape
     hkv = k.shape[2]
@@ -173,9 +179,11 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logit: torch.Tens
     _need(out, "out", torch.float32, (b, s, hq, d), dev)
     shape = lib.DmsShape(b, hkv, hq // hkv, d, PAGE, window, 1, 1, _DTYPES.get(q.dtype, -1))
     scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
-    need = lib.prefill_workspace_bytes(shape, s)
+    gathered = method == "gathered"
+    need = (lib.prefill_gathered_workspace_bytes if gathered else lib.prefill_workspace_bytes)(shape, s)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    lib.check("dms_prefill_attn", lib.dms_prefill_attn(shape, q, k, v, logit, s, scale, out, workspace,
-                                                       workspace.numel(), _stream()))
+    call = lib.dms_prefill_attn_gathered if gathered else lib.dms_prefill_attn
+    name = "dms_prefill_attn_gathered" if gathered else "dms_prefill_attn"
+    lib.check(name, call(shape, q, k, v, logit, s, scale, out, workspace, workspace.numel(), _stream()))
     return out

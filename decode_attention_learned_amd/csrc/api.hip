@@ -132,4 +132,24 @@ int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const
   return from_hip(dms::launch_prefill(*shape, q, k, v, logit, seq_len, sm_scale, out, workspace, stream));
 }
 
+size_t dms_prefill_gathered_workspace_bytes(const dms_shape *shape, int32_t seq_len) {
+  if (check_prefill_shape(shape, seq_len) != DMS_OK) return 0;
+  return dms::prefill_gathered_layout(shape->batch, shape->kv_heads, seq_len).total;
+}
+
+int dms_prefill_attn_gathered(const dms_shape *shape, const void *q, const void *k, const void *v,
+                              const float *logit, int32_t seq_len, float sm_scale, float *out,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_prefill_shape(shape, seq_len);
+  if (rc) return rc;
+  if (seq_len == 0) return DMS_OK;
+  if (!q || !k || !v || !logit || !out || !workspace) return DMS_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
+    return DMS_EINVAL;
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
+  if (workspace_bytes < dms_prefill_gathered_workspace_bytes(shape, seq_len)) return DMS_EWORKSPACE;
+  return from_hip(
+      dms::launch_prefill_gathered(*shape, q, k, v, logit, seq_len, sm_scale, out, workspace, stream));
+}
+
 }  // extern "C"

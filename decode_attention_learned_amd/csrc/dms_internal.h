@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <climits>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -76,12 +78,37 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
 hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, const void *v,
                           const float *logit, int seq_len, float sm_scale, float *out, void *ws,
                           hipStream_t st);
+hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void *k, const void *v,
+                                   const float *logit, int seq_len, float sm_scale, float *out,
+                                   void *ws, hipStream_t st);
 
 // Prefill workspace: per (b, h, 32-key tile) 8 KB of key fragments, 8 KB of
 // value fragments (head_dim 128, bf16) and 32 floats of additive mask.
 inline size_t prefill_workspace_bytes(int batch, int kv_heads, int seq_len) {
   const size_t tiles = size_t(batch) * kv_heads * ((size_t(seq_len) + 31) / 32);
   return align256(tiles * 16384) + align256(tiles * 32 * sizeof(float));
+}
+
+// Gathered-key prefill workspace: the dense prefill workspace (for the band
+// tiles), the same layout for the gathered kept keys plus their positions,
+// and per unit the kept positions in order, kept counts before each tile and
+// each tile's kept-key bits.  Byte offsets of each region.
+struct PrefillGatheredLayout {
+  size_t dense_mask, gathered, gathered_pos, gpos, tile_cnt, keptw, total;
+};
+inline PrefillGatheredLayout prefill_gathered_layout(int batch, int kv_heads, int seq_len) {
+  const size_t units = size_t(batch) * kv_heads;
+  const size_t nt = (size_t(seq_len) + 31) / 32;
+  const size_t tiles = units * nt;
+  PrefillGatheredLayout L;
+  L.dense_mask = align256(tiles * 16384);
+  L.gathered = L.dense_mask + align256(tiles * 32 * sizeof(float));
+  L.gathered_pos = L.gathered + align256(tiles * 16384);
+  L.gpos = L.gathered_pos + align256(tiles * 32 * sizeof(int32_t));
+  L.tile_cnt = L.gpos + align256(units * size_t(seq_len) * sizeof(int32_t));
+  L.keptw = L.tile_cnt + align256(units * (nt + 1) * sizeof(int32_t));
+  L.total = L.keptw + align256(tiles * sizeof(uint32_t));
+  return L;
 }
 
 // ---- wave64 helpers -------------------------------------------------------

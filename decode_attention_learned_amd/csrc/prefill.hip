@@ -242,6 +242,61 @@ __device__ __forceinline__ void phase2(int k, int ntw, int nfar, bool active, in
   exponentials(s, sm, c, pb);
 }
 
+// ---- gathered-key prefill --------------------------------------------------
+// Tile kinds of the gathered kernel's tile list: gathered tiles whose keys
+// every query of the workgroup sees, gathered tiles on the edge (a key is seen
+// by query i iff its position <= i - w), and dense band tiles (key j is seen
+// iff i - w < j <= i).
+__device__ __forceinline__ void g_phase1(int k, int nT, bool active,
+                                         const uint4 (*sK)[PK_FRAGS * PFRAG],
+                                         const uint4 (*sV)[PV_FRAGS * PFRAG],
+                                         const uint4 (&qf)[2][PKS], floatx4 (&s)[2][2],
+                                         const uint4 (&pb)[2], floatx4 (&o)[PDT][2], int lane) {
+  if (!active) return;
+  __builtin_amdgcn_s_setprio(2);
+  if (k >= 1 && k - 1 < nT) pv_tile(sV[(k - 1) % PBUF], pb, lane, o);
+  if (k < nT) {
+    const floatx4 zero[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    qk_tile(sK[k % PBUF], zero, qf, lane, s);
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
+__device__ __forceinline__ void g_phase2(int k, int nT, int nclean, int ngt, int band_j0,
+                                         bool active, int S, int window, int qi0, int col,
+                                         int quad, const int4 (*sP)[PBN / 4], floatx4 (&s)[2][2],
+                                         Softmax &sm, floatx4 (&o)[PDT][2], uint4 (&pb)[2],
+                                         float c) {
+  if (!active || k < 0 || k >= nT) return;
+  if (k >= nclean) {
+    if (k < ngt) {  // gathered edge tile: position <= i - w
+      const int4 p0 = sP[k % PBUF][2 * quad], p1 = sP[k % PBUF][2 * quad + 1];
+      const int pos[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const int lim = qi0 + 16 * qt + col - window;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          s[qt][e >> 2][e & 3] = pos[e] <= lim ? s[qt][e >> 2][e & 3] : -INFINITY;
+      }
+    } else {  // band tile: i - w < j <= i
+      const int j0 = band_j0 + (k - ngt) * PBN + 8 * quad;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const int i = qi0 + 16 * qt + col;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + e;
+          const bool vis = (j < S) & (j <= i) & (i - j < window);
+          s[qt][e >> 2][e & 3] = vis ? s[qt][e >> 2][e & 3] : -INFINITY;
+        }
+      }
+    }
+  }
+  if (__ballot(crosses(s, sm))) move_reference(s, sm, o, c);
+  exponentials(s, sm, c, pb);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -437,6 +492,252 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// gathered-key prefill, step 1: per unit, the positions of the kept keys in
+// order (gpos), the number kept before each 32-key tile (tile_cnt, ntiles + 1
+// entries) and each tile's kept-key bits (keptw).  One workgroup per unit.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_sparse_scan(int S, int hkv, int ntiles,
+                                                      const float *__restrict__ logit,
+                                                      int32_t *__restrict__ gpos,
+                                                      int32_t *__restrict__ tile_cnt,
+                                                      uint32_t *__restrict__ keptw) {
+  const int u = blockIdx.x;
+  const int b = u / hkv, h = u % hkv;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  __shared__ int s_wcnt[16];
+  __shared__ int s_total;
+  int running = 0;
+  for (int base = 0; base < S; base += 1024) {
+    const int j = base + tid;
+    const bool kept = j < S && !evict_decision(logit[(size_t(b) * S + j) * hkv + h]);
+    const uint64_t m = __ballot(kept);
+    if (lane == 0) s_wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int before = running;
+    for (int w = 0; w < wave; ++w) before += s_wcnt[w];
+    if (kept) gpos[size_t(u) * S + before + lanes_below(m)] = j;
+    if ((lane & 31) == 0 && j < S) {
+      const int t = j >> 5;
+      const uint32_t half = uint32_t(m >> (lane & 32));
+      keptw[size_t(u) * ntiles + t] = half;
+      tile_cnt[size_t(u) * (ntiles + 1) + t] = before + (lane ? __popc(uint32_t(m)) : 0);
+    }
+    if (tid == 0) {
+      int tot = 0;
+      for (int w = 0; w < 16; ++w) tot += s_wcnt[w];
+      s_total = tot;
+    }
+    __syncthreads();
+    running += s_total;
+    __syncthreads();
+  }
+  if (tid == 0) tile_cnt[size_t(u) * (ntiles + 1) + ntiles] = running;
+}
+
+// ---------------------------------------------------------------------------
+// gathered-key prefill, step 2: gathered tile gt of a unit holds kept keys
+// 32 gt .. 32 gt + 31 (in position order) in the packed fragment layout, and
+// their positions (INT_MAX past the last kept key).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) void k_sparse_pack(int S, int hkv, int ntiles,
+                                                     const uint16_t *__restrict__ k,
+                                                     const uint16_t *__restrict__ v,
+                                                     const int32_t *__restrict__ gpos,
+                                                     const int32_t *__restrict__ tile_cnt,
+                                                     uint4 *__restrict__ packed,
+                                                     int32_t *__restrict__ gposp) {
+  const int gt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int u = b * hkv + h;
+  const int n = tile_cnt[size_t(u) * (ntiles + 1) + ntiles];
+  if (gt * PBN >= n) return;
+  const int t = threadIdx.x;
+  const size_t T = tile_index(b, h, gt, hkv, ntiles);
+  uint4 *kdst = packed + T * PTILE_U4;
+  uint4 *vdst = kdst + PK_FRAGS * PFRAG;
+  __shared__ __align__(16) uint16_t sv[PBN][PD + 8];
+
+  const int jj = t >> 4, dc = t & 15;
+  const int g = gt * PBN + jj;
+  uint4 kp = make_uint4(0, 0, 0, 0), vp = make_uint4(0, 0, 0, 0);
+  if (g < n) {
+    const int j = gpos[size_t(u) * S + g];
+    const size_t off = ((size_t(b) * S + j) * hkv + h) * PD + dc * 8;
+    kp = *reinterpret_cast<const uint4 *>(k + off);
+    vp = *reinterpret_cast<const uint4 *>(v + off);
+  }
+  const int tt = (jj & 7) >> 2, row = 4 * (jj >> 3) + (jj & 3);
+  const int ks = dc >> 2, qd = dc & 3;
+  kdst[(tt * PKS + ks) * PFRAG + qd * 16 + row] = kp;
+  *reinterpret_cast<uint4 *>(&sv[jj][dc * 8]) = vp;
+  if (t < PBN) {
+    const int gg = gt * PBN + t;
+    gposp[T * PBN + t] = gg < n ? gpos[size_t(u) * S + gg] : INT_MAX;
+  }
+  __syncthreads();
+  const int dt = t >> 6, l = t & 63;
+  const int d = dt * 16 + (l & 15), k0 = 8 * (l >> 4);
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = uint32_t(sv[k0 + 2 * e][d]) | (uint32_t(sv[k0 + 2 * e + 1][d]) << 16);
+  vdst[t] = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// kept keys of unit u at positions <= x
+__device__ __forceinline__ int kept_upto(int x, int S, int ntiles, const int32_t *tc,
+                                         const uint32_t *kw) {
+  if (x < 0) return 0;
+  if (x >= S - 1) return tc[ntiles];
+  const int t = x >> 5, r = x & 31;
+  const uint32_t below = r == 31 ? 0xffffffffu : ((2u << r) - 1u);
+  return tc[t] + __popc(kw[t] & below);
+}
+
+// ---------------------------------------------------------------------------
+// gathered-key prefill, step 3: attention over [gathered tiles | band tiles]
+// with the two-phase schedule of k_prefill.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill_gathered(
+    int batch, int S, int hkv, int G, int window, float scale_log2, const uint16_t *__restrict__ q,
+    const uint4 *__restrict__ dense, const uint4 *__restrict__ gathered,
+    const int4 *__restrict__ gposp, const int32_t *__restrict__ tile_cnt,
+    const uint32_t *__restrict__ keptw, float *__restrict__ out) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = lane_id();
+  const int col = lane & 15, quad = lane >> 4;
+  const int Hq = hkv * G;
+  const int ngh = (G + PHPW - 1) / PHPW;
+  const int nqb = (S + PBM - 1) / PBM;
+
+  const int nbh = batch * hkv * ngh;
+  const int id = blockIdx.x;
+  const int xcd = id & 7, slot = id >> 3;
+  const int per_xcd_pairs = (nbh + 7) / 8;
+  const int pair_in_xcd = slot / nqb;
+  const int qb = nqb - 1 - slot % nqb;
+  const int pair = pair_in_xcd * 8 + xcd;
+  if (pair_in_xcd >= per_xcd_pairs || pair >= nbh) return;
+  const int b = pair / (hkv * ngh);
+  const int h = (pair / ngh) % hkv;
+  const int hg = pair % ngh;
+  const int u = b * hkv + h;
+
+  const int g = hg * PHPW + (wave % PHPW);
+  const bool active = g < G;
+  const int hq = h * G + (active ? g : 0);
+  const int qi0 = qb * PBM + (wave / PHPW) * 32;
+  const int q0 = qb * PBM;
+  const int i_max = min(S, q0 + PBM) - 1;  // last query position of the workgroup
+
+  // tile list: gathered tiles [0, ngt) (the first nclean seen by every query),
+  // then dense tiles covering the band (q0 - w, i_max]
+  const int ntiles_all = (S + PBN - 1) / PBN;
+  const int32_t *tc = tile_cnt + size_t(u) * (ntiles_all + 1);
+  const uint32_t *kw = keptw + size_t(u) * ntiles_all;
+  const int n_any = kept_upto(i_max - window, S, ntiles_all, tc, kw);
+  const int n_all = kept_upto(q0 - window, S, ntiles_all, tc, kw);
+  const int ngt = (n_any + PBN - 1) / PBN;
+  const int nclean = n_all / PBN;
+  const int tb0 = max(0, q0 - window + 1) / PBN;
+  const int nT = ngt + i_max / PBN - tb0 + 1;
+  const int band_j0 = tb0 * PBN;
+
+  __shared__ uint4 sK[PBUF][PK_FRAGS * PFRAG];
+  __shared__ uint4 sV[PBUF][PV_FRAGS * PFRAG];
+  __shared__ int4 sP[PBUF][PBN / 4];
+
+  uint4 qf[2][PKS];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int i = qi0 + 16 * qt + col;
+#pragma unroll
+    for (int ks = 0; ks < PKS; ++ks) {
+      qf[qt][ks] = make_uint4(0, 0, 0, 0);
+      if (active && i < S)
+        qf[qt][ks] = *reinterpret_cast<const uint4 *>(
+            q + ((size_t(b) * S + i) * Hq + hq) * PD + ks * 32 + quad * 8);
+    }
+  }
+  floatx4 o[PDT][2];
+#pragma unroll
+  for (int dt = 0; dt < PDT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  Softmax sm;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    sm.m[qt] = -INFINITY;
+    sm.nmc[qt] = 0.f;
+    sm.thr[qt] = -INFINITY;
+    sm.l[qt] = 0.f;
+  }
+  const float c = scale_log2;
+
+  // Same four-buffer pipeline as k_prefill; tile t comes from the gathered
+  // layout (t < ngt, with its key positions) or the dense one.
+  const size_t ubase = size_t(u) * ntiles_all;
+  uint4 ta, tb;
+  int4 tp;
+#define DMS_PG_GLOAD(t)                                                                   \
+  do {                                                                                    \
+    const bool gath_ = (t) < ngt;                                                         \
+    const uint4 *src_ = gath_ ? gathered + (ubase + (t)) * PTILE_U4                       \
+                              : dense + (ubase + tb0 + (t) - ngt) * PTILE_U4;             \
+    ta = src_[tid];                                                                       \
+    tb = src_[tid + PWAVES * 64];                                                         \
+    if (tid < PBN / 4 && gath_) tp = gposp[(ubase + (t)) * (PBN / 4) + tid];              \
+  } while (0)
+#define DMS_PG_LSTORE(t)                                    \
+  do {                                                      \
+    sK[(t) % PBUF][tid] = ta;                               \
+    sV[(t) % PBUF][tid] = tb;                               \
+    if (tid < PBN / 4 && (t) < ngt) sP[(t) % PBUF][tid] = tp; \
+  } while (0)
+  DMS_PG_GLOAD(0);
+  DMS_PG_LSTORE(0);
+  if (nT > 1) {
+    DMS_PG_GLOAD(1);
+    DMS_PG_LSTORE(1);
+  }
+  if (nT > 2) DMS_PG_GLOAD(2);
+  __syncthreads();
+
+  const bool lead = wave < PWAVES / 2;
+  floatx4 s[2][2];
+  uint4 pb[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  if (!lead) __syncthreads();
+  for (int k = 0; k <= nT; ++k) {
+    g_phase1(k, nT, active, sK, sV, qf, s, pb, o, lane);
+    __syncthreads();
+    g_phase2(k, nT, nclean, ngt, band_j0, active, S, window, qi0, col, quad, sP, s, sm, o, pb, c);
+    if (k + 2 < nT) DMS_PG_LSTORE(k + 2);
+    if (k + 3 < nT) DMS_PG_GLOAD(k + 3);
+    __syncthreads();
+  }
+  if (lead) __syncthreads();
+#undef DMS_PG_LSTORE
+#undef DMS_PG_GLOAD
+
+  if (!active) return;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float l = sm.l[qt];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int i = qi0 + 16 * qt + col;
+    if (i < S) {
+      float *op = out + ((size_t(b) * S + i) * Hq + hq) * PD + quad * 4;
+#pragma unroll
+      for (int dt = 0; dt < PDT; ++dt)
+        *reinterpret_cast<floatx4 *>(op + dt * 16) = o[dt][qt] * inv;
+    }
+  }
+}
+
 hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, const void *v,
                           const float *logit, int seq_len, float sm_scale, float *out, void *ws,
                           hipStream_t st) {
@@ -460,6 +761,44 @@ hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, cons
                      s.kv_heads, s.group, s.window, sm_scale * 1.4426950408889634f,
                      static_cast<const uint16_t *>(q), packed,
                      reinterpret_cast<const floatx4 *>(mask), out);
+  return hipGetLastError();
+}
+
+
+hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void *k, const void *v,
+                                   const float *logit, int seq_len, float sm_scale, float *out,
+                                   void *ws, hipStream_t st) {
+  const int ntiles = (seq_len + PBN - 1) / PBN;
+  if (s.kv_heads > 65535 || s.batch > 65535) return hipErrorInvalidValue;
+  const PrefillGatheredLayout L = prefill_gathered_layout(s.batch, s.kv_heads, seq_len);
+  char *base = static_cast<char *>(ws);
+  uint4 *dense = reinterpret_cast<uint4 *>(base);
+  float *mask = reinterpret_cast<float *>(base + L.dense_mask);
+  uint4 *gathered = reinterpret_cast<uint4 *>(base + L.gathered);
+  int32_t *gposp = reinterpret_cast<int32_t *>(base + L.gathered_pos);
+  int32_t *gpos = reinterpret_cast<int32_t *>(base + L.gpos);
+  int32_t *tile_cnt = reinterpret_cast<int32_t *>(base + L.tile_cnt);
+  uint32_t *keptw = reinterpret_cast<uint32_t *>(base + L.keptw);
+  const uint16_t *k16 = static_cast<const uint16_t *>(k), *v16 = static_cast<const uint16_t *>(v);
+  hipLaunchKernelGGL(k_prefill_pack, dim3(ntiles, s.kv_heads, s.batch), dim3(512), 0, st, seq_len,
+                     s.kv_heads, ntiles, k16, v16, logit, dense, mask);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sparse_scan, dim3(s.batch * s.kv_heads), dim3(1024), 0, st, seq_len,
+                     s.kv_heads, ntiles, logit, gpos, tile_cnt, keptw);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sparse_pack, dim3(ntiles, s.kv_heads, s.batch), dim3(512), 0, st, seq_len,
+                     s.kv_heads, ntiles, k16, v16, gpos, tile_cnt, gathered, gposp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int ngh = (s.group + PHPW - 1) / PHPW;
+  const int nbh = s.batch * s.kv_heads * ngh;
+  const int nqb = (seq_len + PBM - 1) / PBM;
+  const long blocks = long((nbh + 7) / 8) * nqb * 8;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_prefill_gathered, dim3(unsigned(blocks)), dim3(PWAVES * 64), 0, st, s.batch,
+                     seq_len, s.kv_heads, s.group, s.window, sm_scale * 1.4426950408889634f,
+                     static_cast<const uint16_t *>(q), dense, gathered,
+                     reinterpret_cast<const int4 *>(gposp), tile_cnt, keptw, out);
   return hipGetLastError();
 }
 

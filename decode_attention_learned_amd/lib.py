@@ -36,6 +36,8 @@ EXPORTS = (
     "dms_decode_attn",
     "dms_prefill_workspace_bytes",
     "dms_prefill_attn",
+    "dms_prefill_gathered_workspace_bytes",
+    "dms_prefill_attn_gathered",
 )
 
 
@@ -105,6 +107,9 @@ def load() -> ctypes.CDLL:
         "dms_prefill_workspace_bytes": ([SP, ctypes.c_int32], ctypes.c_size_t),
         "dms_prefill_attn": ([SP, P, P, P, P, ctypes.c_int32, ctypes.c_float, P, P, ctypes.c_size_t, P],
                              ctypes.c_int),
+        "dms_prefill_gathered_workspace_bytes": ([SP, ctypes.c_int32], ctypes.c_size_t),
+        "dms_prefill_attn_gathered": ([SP, P, P, P, P, ctypes.c_int32, ctypes.c_float, P, P,
+                                       ctypes.c_size_t, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -171,3 +176,14 @@ def dms_prefill_attn(shape, q, k, v, logit, seq_len, sm_scale, out, workspace, w
     return load().dms_prefill_attn(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(logit),
                                    int(seq_len), float(sm_scale), _p(out), _p(workspace),
                                    int(workspace_bytes), stream)
+
+
+def prefill_gathered_workspace_bytes(shape: DmsShape, seq_len: int) -> int:
+    return load().dms_prefill_gathered_workspace_bytes(ctypes.byref(shape), int(seq_len))
+
+
+def dms_prefill_attn_gathered(shape, q, k, v, logit, seq_len, sm_scale, out, workspace,
+                              workspace_bytes, stream) -> int:
+    return load().dms_prefill_attn_gathered(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(logit),
+                                            int(seq_len), float(sm_scale), _p(out), _p(workspace),
+                                            int(workspace_bytes), stream)

@@ -208,6 +208,33 @@ int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const
                      const float *logit, int32_t seq_len, float sm_scale, float *out,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Bytes of workspace for dms_prefill_attn_gathered: the dense prefill
+ * workspace, the same layout again for the gathered kept keys, and per
+ * (sequence, KV head) the kept positions and per-tile counts.  0 if the
+ * arguments are invalid.
+ */
+size_t dms_prefill_gathered_workspace_bytes(const dms_shape *shape, int32_t seq_len);
+
+/*
+ * Masked prefill attention, same result as dms_prefill_attn, computed over
+ * the keys each query can see rather than over the whole causal triangle.
+ * With the rule of atlas.scime.ai's summary ("Approach"; 16-token window in
+ * "Measured effects"), the keys visible to query i are exactly
+ *   the kept keys (alpha_j = 0) with j <= i - w,   and
+ *   every key with i - w < j <= i,
+ * two disjoint sets.  The kept keys of each (sequence, KV head) are gathered
+ * once in position order; each block of queries then attends to a prefix of
+ * the gathered keys plus the dense band of its last w positions, in one
+ * softmax.  At an eviction rate p the work is about (1 - p) of the dense
+ * kernel's plus the band.  Arguments, layouts and errors as for
+ * dms_prefill_attn; the workspace must hold
+ * dms_prefill_gathered_workspace_bytes(shape, S) bytes.
+ */
+int dms_prefill_attn_gathered(const dms_shape *shape, const void *q, const void *k, const void *v,
+                              const float *logit, int32_t seq_len, float sm_scale, float *out,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

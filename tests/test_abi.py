@@ -110,9 +110,21 @@ def test_prefill_host_errors(L):
         == lib.DMS_EINVAL
     assert L.dms_prefill_attn(ctypes.byref(bf), fake, fake, fake, fake, 16, 0.1, fake, fake, 10, None) \
         == lib.DMS_EWORKSPACE
-    # 2 sequences x 2 KV heads x ceil(100/32) tiles x 16 KB, plus one word per tile
+    # 2 sequences x 2 KV heads x ceil(100/32) tiles x 16 KB, plus 32 floats per tile
     assert lib.prefill_workspace_bytes(bf, 100) == 2 * 2 * 4 * 16384 + 2 * 2 * 4 * 32 * 4
     assert lib.prefill_workspace_bytes(f32, 100) == 0
+    # gathered: dense part, gathered copy of it, kept positions (S per unit),
+    # counts (ntiles + 1 per unit) and kept bits (ntiles per unit), each 256-aligned
+    dense = 2 * 2 * 4 * 16384 + 2 * 2 * 4 * 32 * 4
+    assert lib.prefill_gathered_workspace_bytes(bf, 100) == 2 * dense + 1792 + 256 + 256
+    G = L.dms_prefill_attn_gathered
+    assert G(ctypes.byref(f32), fake, fake, fake, fake, 16, 0.1, fake, fake, big, None) == lib.DMS_EUNSUPPORTED
+    assert G(ctypes.byref(bf), fake, fake, fake, fake, -2, 0.1, fake, fake, big, None) == lib.DMS_EINVAL
+    assert G(ctypes.byref(bf), None, None, None, None, 0, 0.1, None, None, 0, None) == lib.DMS_OK
+    assert G(ctypes.byref(bf), None, fake, fake, fake, 16, 0.1, fake, fake, big, None) == lib.DMS_EINVAL
+    assert G(ctypes.byref(bf), fake, fake, fake, fake, 16, -1.0, fake, fake, big, None) == lib.DMS_EINVAL
+    assert G(ctypes.byref(bf), fake, fake, fake, fake, 16, 0.1, fake, fake, 10, None) == lib.DMS_EWORKSPACE
+    assert lib.prefill_gathered_workspace_bytes(f32, 100) == 0
 
 
 def test_product_package_does_not_import_oracle():

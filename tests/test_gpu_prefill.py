@@ -1,6 +1,9 @@
-"""GPU parity of the masked prefill kernel against the float64 oracle, through the C ABI.
+"""GPU parity of the masked prefill kernels against the float64 oracle, through the C ABI.
 
-Tolerance: |o - o_ref| <= 2e-2 + 2e-2 |o_ref| element-wise (bf16 inputs, fp32 accumulation).
+Both entry points are covered: dms_prefill_attn ("dense": every causal tile,
+masked) and dms_prefill_attn_gathered ("gathered": kept keys gathered per head
+plus the window band).  Tolerance: |o - o_ref| <= 2e-2 + 2e-2 |o_ref|
+element-wise (bf16 inputs, fp32 accumulation).
 """
 
 import math
@@ -40,26 +43,55 @@ def _check_rows(out, q, k, v, logit, rows, window, what=""):
     return worst
 
 
+METHODS = ["dense", "gathered"]
+
+
+@pytest.mark.parametrize("method", METHODS)
 @pytest.mark.parametrize("b,s,hkv,g", [(2, 200, 2, 4), (1, 97, 1, 1), (1, 130, 2, 2), (1, 150, 1, 5),
                                        (2, 64, 1, 8), (1, 1, 1, 4), (1, 33, 3, 4)])
-def test_prefill_small_all_rows(gpu, b, s, hkv, g):
+def test_prefill_small_all_rows(gpu, b, s, hkv, g, method):
     w, (q, k, v, logit) = _inputs(b, s, hkv, g, seed=5100 + s + g)
-    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16).cpu()
-    worst = _check_rows(out, q, k, v, logit, np.arange(s), 16, what=f"B={b} S={s} Hkv={hkv} G={g}")
-    say(f"prefill B={b} S={s} Hkv={hkv} G={g}: max err {worst:.2e}")
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16, method=method).cpu()
+    worst = _check_rows(out, q, k, v, logit, np.arange(s), 16,
+                        what=f"{method} B={b} S={s} Hkv={hkv} G={g}")
+    say(f"prefill {method} B={b} S={s} Hkv={hkv} G={g}: max err {worst:.2e}")
 
 
-@pytest.mark.parametrize("window", [1, 3, 16, 40])
-def test_prefill_windows(gpu, window):
+@pytest.mark.parametrize("method", METHODS)
+@pytest.mark.parametrize("window", [1, 3, 16, 40, 100])
+def test_prefill_windows(gpu, window, method):
     w, (q, k, v, logit) = _inputs(1, 300, 2, 4, rate=0.7, seed=5200 + window)
-    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=window).cpu()
-    _check_rows(out, q, k, v, logit, np.arange(300), window, what=f"window {window}")
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=window, method=method).cpu()
+    _check_rows(out, q, k, v, logit, np.arange(300), window, what=f"{method} window {window}")
 
 
-def test_prefill_all_keep_is_causal_sdpa(gpu):
+@pytest.mark.parametrize("rate", [0.0, 0.3, 0.875, 0.97, 1.0])
+def test_prefill_gathered_rates(gpu, rate):
+    """Gathered kernel over the range of eviction rates: from no key gathered
+    away (everything kept) to nothing gathered (only the band), on 3 query
+    blocks and 12 key tiles with a ragged end."""
+    w, (q, k, v, logit) = _inputs(2, 371, 2, 4, rate=rate, seed=5500 + int(rate * 100))
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16, method="gathered").cpu()
+    worst = _check_rows(out, q, k, v, logit, np.arange(371), 16, what=f"gathered rate {rate}")
+    say(f"prefill gathered rate {rate}: max err {worst:.2e}")
+
+
+def test_prefill_methods_agree(gpu):
+    """Dense and gathered kernels on the same inputs: both within tolerance of
+    the oracle on every row, and within tolerance of each other."""
+    w, (q, k, v, logit) = _inputs(2, 700, 2, 4, rate=0.875, seed=5601)
+    qd, kd, vd, ld = q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu)
+    dense = prefill(qd, kd, vd, ld, window=16, method="dense").cpu()
+    gath = prefill(qd, kd, vd, ld, window=16, method="gathered").cpu()
+    _check_rows(gath, q, k, v, logit, np.arange(700), 16, what="gathered")
+    assert torch.allclose(dense, gath, rtol=2e-2, atol=2e-2)
+
+
+@pytest.mark.parametrize("method", METHODS)
+def test_prefill_all_keep_is_causal_sdpa(gpu, method):
     """Nothing marked: the kernel is plain causal attention (torch SDPA on CPU, float64)."""
     w, (q, k, v, logit) = _inputs(2, 257, 2, 4, rate=0.0, seed=5301)
-    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16).cpu()
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16, method=method).cpu()
     for bi in range(2):
         qq = q[bi].double().permute(1, 0, 2)
         kk = k[bi].double().permute(1, 0, 2).repeat_interleave(4, 0)
@@ -69,10 +101,11 @@ def test_prefill_all_keep_is_causal_sdpa(gpu):
         assert torch.allclose(out[bi].double(), ref.permute(1, 0, 2), rtol=2e-2, atol=2e-2)
 
 
-def test_prefill_all_evict_is_sliding_window_sdpa(gpu):
+@pytest.mark.parametrize("method", METHODS)
+def test_prefill_all_evict_is_sliding_window_sdpa(gpu, method):
     """Everything marked: attention over the last 16 positions (SDPA with a band mask)."""
     w, (q, k, v, logit) = _inputs(1, 200, 2, 4, rate=1.0, seed=5302)
-    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16).cpu()
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16, method=method).cpu()
     i = torch.arange(200)[:, None]
     j = torch.arange(200)[None, :]
     band = (i - j >= 0) & (i - j < 16)
@@ -101,13 +134,14 @@ def test_prefill_matches_decode_path(gpu):
             cache.compact()
 
 
-def test_prefill_8k_sampled_rows(gpu):
+@pytest.mark.parametrize("method", METHODS)
+def test_prefill_8k_sampled_rows(gpu, method):
     """Masked prefill at full size (B=4, S=8192, 32/8 heads, CR 8): query rows
     [0, 512) and [7680, 8192) of every sequence and head against the oracle."""
     w = wl.get("prefill_8k")
-    say("prefill_8k: B=4 S=8192 Hq=32 Hkv=8 D=128")
+    say(f"prefill_8k {method}: B=4 S=8192 Hq=32 Hkv=8 D=128")
     q, k, v, logit = wl.prefill_inputs(w, device=gpu)
-    out = prefill(q, k, v, logit, window=16)
+    out = prefill(q, k, v, logit, window=16, method=method)
     rows = np.concatenate([np.arange(0, 512), np.arange(7680, 8192)])
     out_rows = out[:, torch.as_tensor(rows, device=gpu)].cpu()
     qc, kc, vc, lc = q.cpu(), k.cpu(), v.cpu(), logit.cpu()

@@ -74,6 +74,9 @@ constexpr int PK_FRAGS = 2 * PKS;  // key fragments per tile
 constexpr int PV_FRAGS = PDT;      // value fragments per tile
 constexpr int PBUF = 4;            // LDS tile buffers
 constexpr float kLazy = 8.0f;      // largest exponent (log2 units) before the reference moves
+#ifndef DMS_GATHERED_WAVES
+#define DMS_GATHERED_WAVES 4       // waves per workgroup of the gathered kernel (4 or 8)
+#endif
 
 __device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -599,7 +602,8 @@ __device__ __forceinline__ int kept_upto(int x, int S, int ntiles, const int32_t
 // gathered-key prefill, step 3: attention over [gathered tiles | band tiles]
 // with the two-phase schedule of k_prefill.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill_gathered(
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 2) void k_prefill_gathered(
     int batch, int S, int hkv, int G, int window, float scale_log2, const uint16_t *__restrict__ q,
     const uint4 *__restrict__ dense, const uint4 *__restrict__ gathered,
     const int4 *__restrict__ gposp, const int32_t *__restrict__ tile_cnt,
@@ -610,7 +614,9 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill_gathered(
   const int col = lane & 15, quad = lane >> 4;
   const int Hq = hkv * G;
   const int ngh = (G + PHPW - 1) / PHPW;
-  const int nqb = (S + PBM - 1) / PBM;
+  constexpr int GBM = 32 * (NW / PHPW);  // query positions per workgroup
+  constexpr int NT = NW * 64;
+  const int nqb = (S + GBM - 1) / GBM;
 
   const int nbh = batch * hkv * ngh;
   const int id = blockIdx.x;
@@ -628,9 +634,9 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill_gathered(
   const int g = hg * PHPW + (wave % PHPW);
   const bool active = g < G;
   const int hq = h * G + (active ? g : 0);
-  const int qi0 = qb * PBM + (wave / PHPW) * 32;
-  const int q0 = qb * PBM;
-  const int i_max = min(S, q0 + PBM) - 1;  // last query position of the workgroup
+  const int qi0 = qb * GBM + (wave / PHPW) * 32;
+  const int q0 = qb * GBM;
+  const int i_max = min(S, q0 + GBM) - 1;  // last query position of the workgroup
 
   // tile list: gathered tiles [0, ngt) (the first nclean seen by every query),
   // then dense tiles covering the band (q0 - w, i_max]
@@ -679,21 +685,35 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill_gathered(
   // Same four-buffer pipeline as k_prefill; tile t comes from the gathered
   // layout (t < ngt, with its key positions) or the dense one.
   const size_t ubase = size_t(u) * ntiles_all;
-  uint4 ta, tb;
+  // thread t copies uint4 t + NT r of the 16 KB packed tile (r < 1024 / NT);
+  // threads 0..7 copy the key positions of a gathered tile
+  static_assert(NT == 256 || NT == 512, "four or eight waves");
+  uint4 tr0, tr1, tr2, tr3;
   int4 tp;
 #define DMS_PG_GLOAD(t)                                                                   \
   do {                                                                                    \
     const bool gath_ = (t) < ngt;                                                         \
     const uint4 *src_ = gath_ ? gathered + (ubase + (t)) * PTILE_U4                       \
                               : dense + (ubase + tb0 + (t) - ngt) * PTILE_U4;             \
-    ta = src_[tid];                                                                       \
-    tb = src_[tid + PWAVES * 64];                                                         \
+    tr0 = src_[tid];                                                                      \
+    tr1 = src_[tid + NT];                                                                 \
+    if constexpr (NT == 256) {                                                            \
+      tr2 = src_[tid + 2 * NT];                                                           \
+      tr3 = src_[tid + 3 * NT];                                                           \
+    }                                                                                     \
     if (tid < PBN / 4 && gath_) tp = gposp[(ubase + (t)) * (PBN / 4) + tid];              \
   } while (0)
-#define DMS_PG_LSTORE(t)                                    \
-  do {                                                      \
-    sK[(t) % PBUF][tid] = ta;                               \
-    sV[(t) % PBUF][tid] = tb;                               \
+#define DMS_PG_LSTORE(t)                                      \
+  do {                                                        \
+    if constexpr (NT == 256) {                                \
+      sK[(t) % PBUF][tid] = tr0;                              \
+      sK[(t) % PBUF][tid + NT] = tr1;                         \
+      sV[(t) % PBUF][tid] = tr2;                              \
+      sV[(t) % PBUF][tid + NT] = tr3;                         \
+    } else {                                                  \
+      sK[(t) % PBUF][tid] = tr0;                              \
+      sV[(t) % PBUF][tid] = tr1;                              \
+    }                                                         \
     if (tid < PBN / 4 && (t) < ngt) sP[(t) % PBUF][tid] = tp; \
   } while (0)
   DMS_PG_GLOAD(0);
@@ -705,19 +725,23 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill_gathered(
   if (nT > 2) DMS_PG_GLOAD(2);
   __syncthreads();
 
-  const bool lead = wave < PWAVES / 2;
+  // With 8 waves, the two-phase schedule of k_prefill (waves 4-7 half a tile
+  // behind).  With 4 waves, two workgroups share a CU and one barrier per
+  // tile suffices (phase 1 of tile k+1 reads buffers that the stores of step
+  // k do not touch).
+  const bool lead = NW == 4 || wave < NW / 2;
   floatx4 s[2][2];
   uint4 pb[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
   if (!lead) __syncthreads();
   for (int k = 0; k <= nT; ++k) {
     g_phase1(k, nT, active, sK, sV, qf, s, pb, o, lane);
-    __syncthreads();
+    if (NW == 8) __syncthreads();
     g_phase2(k, nT, nclean, ngt, band_j0, active, S, window, qi0, col, quad, sP, s, sm, o, pb, c);
     if (k + 2 < nT) DMS_PG_LSTORE(k + 2);
     if (k + 3 < nT) DMS_PG_GLOAD(k + 3);
     __syncthreads();
   }
-  if (lead) __syncthreads();
+  if (NW == 8 && lead) __syncthreads();
 #undef DMS_PG_LSTORE
 #undef DMS_PG_GLOAD
 
@@ -790,12 +814,13 @@ hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void
   hipLaunchKernelGGL(k_sparse_pack, dim3(ntiles, s.kv_heads, s.batch), dim3(512), 0, st, seq_len,
                      s.kv_heads, ntiles, k16, v16, gpos, tile_cnt, gathered, gposp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  constexpr int NW = DMS_GATHERED_WAVES;
   const int ngh = (s.group + PHPW - 1) / PHPW;
   const int nbh = s.batch * s.kv_heads * ngh;
-  const int nqb = (seq_len + PBM - 1) / PBM;
+  const int nqb = (seq_len + 32 * (NW / PHPW) - 1) / (32 * (NW / PHPW));
   const long blocks = long((nbh + 7) / 8) * nqb * 8;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_prefill_gathered, dim3(unsigned(blocks)), dim3(PWAVES * 64), 0, st, s.batch,
+  hipLaunchKernelGGL(k_prefill_gathered<NW>, dim3(unsigned(blocks)), dim3(NW * 64), 0, st, s.batch,
                      seq_len, s.kv_heads, s.group, s.window, sm_scale * 1.4426950408889634f,
                      static_cast<const uint16_t *>(q), dense, gathered,
                      reinterpret_cast<const int4 *>(gposp), tile_cnt, keptw, out);

@@ -4,4 +4,4 @@ TEST INFRASTRUCTURE ONLY: importable from ``tests/``, ``__graft_entry__.smoke()`
 and ``bench.py``'s ``cpu_baseline`` leg, never from the product package.
 """
 
-from . import bruteforce, dms_oracle  # noqa: F401
+from . import bruteforce, dms_oracle, soft_mask  # noqa: F401

@@ -198,6 +198,9 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
     ms = _time_calls(lambda: prefill(q, k, v, logit, window=w.window, out=out, workspace=ws), iters)
     ms_g = _time_calls(lambda: prefill(q, k, v, logit, window=w.window, out=out, workspace=ws,
                                        method="gathered"), iters)
+    noise = wl.logistic_noise(w, device=dev)
+    ms_r = _time_calls(lambda: prefill(q, k, v, logit, window=w.window, out=out, workspace=ws,
+                                       method="relaxed", noise=noise, temperature=1.0), iters)
     causal = 4.0 * d * s_len * (s_len + 1) / 2 * w.batch * w.q_heads
     # visible (query, key) pairs: |R(i)| = #{j <= i - w : unmarked} + min(w, i + 1), per (b, h)
     keep = (logit <= 0).to(torch.int64)                          # [B, S, Hkv]
@@ -222,6 +225,9 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
         "roofline": {"bound": "mfma", "kernel": "k_prefill_pack + k_prefill", "achieved": round(tflops, 1),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None},
+        "relaxed": {"ms": round(ms_r, 4), "temperature": 1.0, "noise": "logistic",
+                    "causal_tflops": round(causal / (ms_r * 1e-3) / 1e12, 1),
+                    "frac": round(causal / (ms_r * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
         "gathered": {
             "ms": round(ms_g, 4), "speedup_vs_dense": round(ms / ms_g, 2),
             "causal_equivalent_tflops": round(causal / (ms_g * 1e-3) / 1e12, 1),

@@ -154,14 +154,17 @@ class DmsCache:
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logit: torch.Tensor,
             window: int = 16, sm_scale: float | None = None,
             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-            method: str = "dense") -> torch.Tensor:
+            method: str = "dense", noise: torch.Tensor | None = None,
+            temperature: float = 1.0) -> torch.Tensor:
     """Masked DMS prefill: q [B, S, Hq, D], k, v [B, S, Hkv, D] bf16, logit [B, S, Hkv] f32.
 
     method "dense" runs dms_prefill_attn (every causal tile, masked), "gathered"
-    runs dms_prefill_attn_gathered (gathered kept keys plus the window band).
+    runs dms_prefill_attn_gathered (gathered kept keys plus the window band),
+    "relaxed" runs dms_prefill_attn_relaxed (keep factor 1 - sigmoid((logit +
+    noise) / temperature) outside the window; noise [B, S, Hkv] f32 or None).
     `workspace` (uint8, at least the method's workspace size) is allocated when
     not given."""
-    if method not in ("dense", "gathered"):
+    if method not in ("dense", "gathered", "relaxed"):
         raise ValueError(f"unknown prefill method {method!r}")
     lib.load()
     b, s, hq, d = q.shape
@@ -183,6 +186,13 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logit: torch.Tens
     need = (lib.prefill_gathered_workspace_bytes if gathered else lib.prefill_workspace_bytes)(shape, s)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    if method == "relaxed":
+        if noise is not None:
+            _need(noise, "noise", torch.float32, (b, s, hkv), dev)
+        lib.check("dms_prefill_attn_relaxed", lib.dms_prefill_attn_relaxed(
+            shape, q, k, v, logit, noise, temperature, s, scale, out, workspace, workspace.numel(),
+            _stream()))
+        return out
     call = lib.dms_prefill_attn_gathered if gathered else lib.dms_prefill_attn
     name = "dms_prefill_attn_gathered" if gathered else "dms_prefill_attn"
     lib.check(name, call(shape, q, k, v, logit, s, scale, out, workspace, workspace.numel(), _stream()))

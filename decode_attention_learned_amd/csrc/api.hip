@@ -129,7 +129,25 @@ int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const
     return DMS_EINVAL;
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
   if (workspace_bytes < dms_prefill_workspace_bytes(shape, seq_len)) return DMS_EWORKSPACE;
-  return from_hip(dms::launch_prefill(*shape, q, k, v, logit, seq_len, sm_scale, out, workspace, stream));
+  return from_hip(dms::launch_prefill(*shape, q, k, v, logit, nullptr, 0.f, seq_len, sm_scale, out,
+                                      workspace, stream));
+}
+
+int dms_prefill_attn_relaxed(const dms_shape *shape, const void *q, const void *k, const void *v,
+                             const float *logit, const float *noise, float temperature,
+                             int32_t seq_len, float sm_scale, float *out, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_prefill_shape(shape, seq_len);
+  if (rc) return rc;
+  if (!(temperature > 0.0f) || temperature == INFINITY) return DMS_EINVAL;
+  if (seq_len == 0) return DMS_OK;
+  if (!q || !k || !v || !logit || !out || !workspace) return DMS_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
+    return DMS_EINVAL;
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
+  if (workspace_bytes < dms_prefill_workspace_bytes(shape, seq_len)) return DMS_EWORKSPACE;
+  return from_hip(dms::launch_prefill(*shape, q, k, v, logit, noise, temperature, seq_len, sm_scale,
+                                      out, workspace, stream));
 }
 
 size_t dms_prefill_gathered_workspace_bytes(const dms_shape *shape, int32_t seq_len) {

@@ -226,6 +226,8 @@ __device__ __forceinline__ void phase2(int k, int ntw, int nfar, bool active, in
                                        uint4 (&pb)[2], float c) {
   if (!active || k < 0 || k >= ntw) return;
   if (k >= nfar) {
+    // near tile: causal bound, and the key's additive mask once it is w or
+    // more behind the query (0 / -inf for the hard rule)
     const int j0 = k * PBN;
     const int buf = k % PBUF;
     const floatx4 mb[2] = {sB[buf][2 * quad], sB[buf][2 * quad + 1]};
@@ -235,9 +237,9 @@ __device__ __forceinline__ void phase2(int k, int ntw, int nfar, bool active, in
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = j0 + 8 * quad + e;
-        const bool keep = mb[e >> 2][e & 3] == 0.f;
-        const bool vis = (j < S) & (j <= i) & (keep | (i - j < window));
-        s[qt][e >> 2][e & 3] = vis ? s[qt][e >> 2][e & 3] : -INFINITY;
+        const float add = i - j >= window ? mb[e >> 2][e & 3] : 0.f;
+        const bool causal = (j < S) & (j <= i);
+        s[qt][e >> 2][e & 3] = causal ? s[qt][e >> 2][e & 3] + add : -INFINITY;
       }
     }
   }
@@ -309,6 +311,8 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
                                                       const uint16_t *__restrict__ k,
                                                       const uint16_t *__restrict__ v,
                                                       const float *__restrict__ logit,
+                                                      const float *__restrict__ noise, float inv_tau,
+                                                      float inv_scale, int relaxed,
                                                       uint4 *__restrict__ packed,
                                                       float *__restrict__ mask) {
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -333,10 +337,23 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
   const int ks = dc >> 2, qd = dc & 3;
   kdst[(tt * PKS + ks) * PFRAG + qd * 16 + row] = kp;
   *reinterpret_cast<uint4 *>(&sv[jj][dc * 8]) = vp;
-  // additive mask of key j0 + t: -inf if marked for eviction (or past the end)
+  // additive mask of key j0 + t, applied once the key is w or more behind
+  // the query: hard rule -inf if marked for eviction, 0 if kept; relaxed
+  // rule log(1 - sigmoid((logit + noise) / tau)) = -softplus(x); -inf past
+  // the end of the sequence.  Stored in raw score units (divided by the
+  // softmax scale), the units the attention kernel adds it in.
   if (t < PBN) {
-    const bool marked = j0 + t >= S || evict_decision(logit[(size_t(b) * S + j0 + t) * hkv + h]);
-    mask[T * PBN + t] = marked ? -INFINITY : 0.f;
+    float bias = -INFINITY;
+    if (j0 + t < S) {
+      const size_t at = (size_t(b) * S + j0 + t) * hkv + h;
+      if (relaxed) {
+        const float x = (logit[at] + (noise ? noise[at] : 0.f)) * inv_tau;
+        bias = -(fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))) * inv_scale;
+      } else {
+        bias = evict_decision(logit[at]) ? -INFINITY : 0.f;
+      }
+    }
+    mask[T * PBN + t] = bias;
   }
   __syncthreads();
   // value fragment dt = t / 64, lane l = t % 64: dim dt*16 + l % 16, keys 8*(l/16) .. +8
@@ -763,16 +780,18 @@ __global__ __launch_bounds__(NW * 64, 2) void k_prefill_gathered(
 }
 
 hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, const void *v,
-                          const float *logit, int seq_len, float sm_scale, float *out, void *ws,
-                          hipStream_t st) {
+                          const float *logit, const float *noise, float temperature, int seq_len,
+                          float sm_scale, float *out, void *ws, hipStream_t st) {
   const int ntiles = (seq_len + PBN - 1) / PBN;
   if (s.kv_heads > 65535 || s.batch > 65535) return hipErrorInvalidValue;  // pack grid y, z
   const size_t tiles = size_t(s.batch) * s.kv_heads * ntiles;
   uint4 *packed = static_cast<uint4 *>(ws);
   float *mask = reinterpret_cast<float *>(static_cast<char *>(ws) + align256(tiles * 16384));
+  const int relaxed = temperature > 0.f;
   hipLaunchKernelGGL(k_prefill_pack, dim3(ntiles, s.kv_heads, s.batch), dim3(512), 0, st, seq_len,
                      s.kv_heads, ntiles, static_cast<const uint16_t *>(k),
-                     static_cast<const uint16_t *>(v), logit, packed, mask);
+                     static_cast<const uint16_t *>(v), logit, noise,
+                     relaxed ? 1.f / temperature : 0.f, 1.f / sm_scale, relaxed, packed, mask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ngh = (s.group + PHPW - 1) / PHPW;
@@ -805,7 +824,7 @@ hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void
   uint32_t *keptw = reinterpret_cast<uint32_t *>(base + L.keptw);
   const uint16_t *k16 = static_cast<const uint16_t *>(k), *v16 = static_cast<const uint16_t *>(v);
   hipLaunchKernelGGL(k_prefill_pack, dim3(ntiles, s.kv_heads, s.batch), dim3(512), 0, st, seq_len,
-                     s.kv_heads, ntiles, k16, v16, logit, dense, mask);
+                     s.kv_heads, ntiles, k16, v16, logit, nullptr, 0.f, 1.f, 0, dense, mask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_sparse_scan, dim3(s.batch * s.kv_heads), dim3(1024), 0, st, seq_len,

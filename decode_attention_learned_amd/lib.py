@@ -36,6 +36,7 @@ EXPORTS = (
     "dms_decode_attn",
     "dms_prefill_workspace_bytes",
     "dms_prefill_attn",
+    "dms_prefill_attn_relaxed",
     "dms_prefill_gathered_workspace_bytes",
     "dms_prefill_attn_gathered",
 )
@@ -107,6 +108,8 @@ def load() -> ctypes.CDLL:
         "dms_prefill_workspace_bytes": ([SP, ctypes.c_int32], ctypes.c_size_t),
         "dms_prefill_attn": ([SP, P, P, P, P, ctypes.c_int32, ctypes.c_float, P, P, ctypes.c_size_t, P],
                              ctypes.c_int),
+        "dms_prefill_attn_relaxed": ([SP, P, P, P, P, P, ctypes.c_float, ctypes.c_int32, ctypes.c_float, P,
+                                      P, ctypes.c_size_t, P], ctypes.c_int),
         "dms_prefill_gathered_workspace_bytes": ([SP, ctypes.c_int32], ctypes.c_size_t),
         "dms_prefill_attn_gathered": ([SP, P, P, P, P, ctypes.c_int32, ctypes.c_float, P, P,
                                        ctypes.c_size_t, P], ctypes.c_int),
@@ -187,3 +190,11 @@ def dms_prefill_attn_gathered(shape, q, k, v, logit, seq_len, sm_scale, out, wor
     return load().dms_prefill_attn_gathered(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(logit),
                                             int(seq_len), float(sm_scale), _p(out), _p(workspace),
                                             int(workspace_bytes), stream)
+
+
+def dms_prefill_attn_relaxed(shape, q, k, v, logit, noise, temperature, seq_len, sm_scale, out,
+                             workspace, workspace_bytes, stream) -> int:
+    return load().dms_prefill_attn_relaxed(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(logit),
+                                           _p(noise), float(temperature),
+                                           int(seq_len), float(sm_scale), _p(out), _p(workspace),
+                                           int(workspace_bytes), stream)

@@ -209,6 +209,26 @@ int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Prefill attention with the relaxed (training-form) decision: the binary
+ * decision of atlas.scime.ai's summary ("Approach": learned per head, relaxed
+ * with a Gumbel-sigmoid while retrofitting) replaced by
+ *   a~_j = sigmoid((logit_j + noise_j) / temperature),
+ * key j keeping the weight factor (1 - a~_j) for queries at least w positions
+ * after it and its full weight inside the window, i.e. scores
+ *   sm_scale <q_i, k_j> + (i - j >= w ? log(1 - a~_j) : 0),   j <= i.
+ * The pages give neither the noise law nor the temperature; both are inputs.
+ * noise: [B][S][Hkv] float32 (e.g. logistic draws for a Gumbel-sigmoid), or
+ * NULL for none.  temperature > 0 and finite, else DMS_EINVAL.  logit and
+ * noise must be finite.  Other arguments, the workspace
+ * (dms_prefill_workspace_bytes) and errors as for dms_prefill_attn.  As the
+ * temperature goes to 0 without noise the result tends to dms_prefill_attn's.
+ */
+int dms_prefill_attn_relaxed(const dms_shape *shape, const void *q, const void *k, const void *v,
+                             const float *logit, const float *noise, float temperature,
+                             int32_t seq_len, float sm_scale, float *out, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Bytes of workspace for dms_prefill_attn_gathered: the dense prefill
  * workspace, the same layout again for the gathered kept keys, and per
  * (sequence, KV head) the kept positions and per-tile counts.  0 if the

@@ -117,6 +117,14 @@ def test_prefill_host_errors(L):
     # counts (ntiles + 1 per unit) and kept bits (ntiles per unit), each 256-aligned
     dense = 2 * 2 * 4 * 16384 + 2 * 2 * 4 * 32 * 4
     assert lib.prefill_gathered_workspace_bytes(bf, 100) == 2 * dense + 1792 + 256 + 256
+    R = L.dms_prefill_attn_relaxed
+    assert R(ctypes.byref(bf), fake, fake, fake, fake, None, 0.0, 16, 0.1, fake, fake, big, None) == lib.DMS_EINVAL
+    assert R(ctypes.byref(bf), fake, fake, fake, fake, None, float("inf"), 16, 0.1, fake, fake, big, None) \
+        == lib.DMS_EINVAL
+    assert R(ctypes.byref(bf), fake, fake, fake, fake, None, 1.0, 16, 0.1, fake, fake, 10, None) \
+        == lib.DMS_EWORKSPACE
+    assert R(ctypes.byref(f32), fake, fake, fake, fake, None, 1.0, 16, 0.1, fake, fake, big, None) \
+        == lib.DMS_EUNSUPPORTED
     G = L.dms_prefill_attn_gathered
     assert G(ctypes.byref(f32), fake, fake, fake, fake, 16, 0.1, fake, fake, big, None) == lib.DMS_EUNSUPPORTED
     assert G(ctypes.byref(bf), fake, fake, fake, fake, -2, 0.1, fake, fake, big, None) == lib.DMS_EINVAL

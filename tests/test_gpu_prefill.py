@@ -155,3 +155,70 @@ def test_prefill_8k_sampled_rows(gpu, method):
         bound = BF16_TOL["atol"] + BF16_TOL["rtol"] * np.abs(ref)
         assert np.all(err <= bound), f"seq {bi}: max err {err.max():.3g}"
         say(f"  seq {bi}: max err {err.max():.2e}")
+
+
+# ---------------------------------------------------------------- relaxed mask
+def _check_relaxed(out, q, k, v, logit, noise, tau, rows, window, what=""):
+    from oracle import soft_mask as smo
+
+    b_n, s, hq, d = q.shape
+    worst = 0.0
+    for bi in range(b_n):
+        ref = smo.soft_prefill_rows(q[bi].float().numpy(), k[bi].float().numpy(), v[bi].float().numpy(),
+                                    logit[bi].numpy(), noise[bi].numpy() if noise is not None else 0.0,
+                                    tau, rows, window, 1.0 / math.sqrt(d))
+        got = out[bi, rows].double().numpy()
+        err = np.abs(got - ref)
+        worst = max(worst, float(err.max()))
+        assert np.all(err <= BF16_TOL["atol"] + BF16_TOL["rtol"] * np.abs(ref)), \
+            f"{what} seq {bi}: max err {err.max():.3g}"
+    return worst
+
+
+@pytest.mark.parametrize("tau", [0.25, 1.0, 4.0])
+@pytest.mark.parametrize("with_noise", [False, True])
+def test_prefill_relaxed_all_rows(gpu, tau, with_noise):
+    """Relaxed-mask prefill against the float64 relaxed oracle, every row,
+    logits with mean 0 so that keep factors spread over (0, 1)."""
+    w, (q, k, v, logit) = _inputs(2, 230, 2, 4, rate=0.5, seed=5700 + int(tau * 10))
+    noise = wl.logistic_noise(w) if with_noise else None
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16, method="relaxed",
+                  noise=noise.to(gpu) if noise is not None else None, temperature=tau).cpu()
+    worst = _check_relaxed(out, q, k, v, logit, noise, tau, np.arange(230), 16,
+                           what=f"relaxed tau {tau} noise {with_noise}")
+    say(f"prefill relaxed tau={tau} noise={with_noise}: max err {worst:.2e}")
+
+
+@pytest.mark.parametrize("window", [1, 40])
+def test_prefill_relaxed_windows(gpu, window):
+    w, (q, k, v, logit) = _inputs(1, 300, 2, 4, rate=0.7, seed=5800 + window)
+    noise = wl.logistic_noise(w)
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=window, method="relaxed",
+                  noise=noise.to(gpu), temperature=0.5).cpu()
+    _check_relaxed(out, q, k, v, logit, noise, 0.5, np.arange(300), window, what=f"relaxed window {window}")
+
+
+def test_prefill_relaxed_cold_limit_is_hard_rule(gpu):
+    """Temperature 1e-4 without noise: the relaxed kernel gives the hard-rule
+    result (logits kept at |logit| >= 0.05 so every factor saturates)."""
+    w, (q, k, v, logit) = _inputs(2, 200, 2, 4, rate=0.6, seed=5901)
+    logit = torch.where(logit.abs() < 0.05, torch.full_like(logit, 0.5), logit)
+    qd, kd, vd, ld = q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu)
+    relaxed = prefill(qd, kd, vd, ld, window=16, method="relaxed", temperature=1e-4).cpu()
+    _check_rows(relaxed, q, k, v, logit, np.arange(200), 16, what="relaxed, cold")
+
+
+def test_prefill_relaxed_8k_sampled_rows(gpu):
+    """Relaxed mask at full size (B=4, S=8192, 32/8 heads), temperature 1 with
+    logistic noise: rows [0, 256) and [7936, 8192) against the oracle."""
+    w = wl.get("prefill_8k")
+    q, k, v, logit = wl.prefill_inputs(w, device=gpu)
+    noise = wl.logistic_noise(w, device=gpu)
+    out = prefill(q, k, v, logit, window=16, method="relaxed", noise=noise, temperature=1.0)
+    rows = np.concatenate([np.arange(0, 256), np.arange(7936, 8192)])
+    out_rows = out[:, torch.as_tensor(rows, device=gpu)].cpu()
+    full = torch.zeros((w.batch, w.context, w.q_heads, 128), dtype=torch.float32)
+    full[:, torch.as_tensor(rows)] = out_rows
+    worst = _check_relaxed(full, q.cpu(), k.cpu(), v.cpu(), logit.cpu(), noise.cpu(), 1.0, rows, 16,
+                           what="relaxed 8k")
+    say(f"prefill relaxed 8k: max err {worst:.2e}")

@@ -61,3 +61,20 @@ def test_beta_rates_are_per_unit_and_aggregate_cr_near_8():
     kept = (1 - rates) * (32768 - 16) + 16
     cr = 32768 * rates.size / kept.sum()
     assert 6.0 < cr < 11.0
+
+
+def test_logistic_noise_law():
+    """The noise generator draws the standard logistic law: mean 0, variance
+    pi^2 / 3, CDF 1 / (1 + e^-x) at x = 1 (0.7311), within sampling error."""
+    import math
+
+    w = wl.Workload(name="noise_case", kind="prefill", batch=4, kv_heads=8, group=4, head_dim=128,
+                    dtype="bf16", context=4096, evict_rate=0.5, seed=77)
+    n = wl.logistic_noise(w).double()
+    assert n.shape == (4, 4096, 8)
+    cnt = n.numel()
+    assert abs(n.mean().item()) < 5 * math.sqrt(math.pi ** 2 / 3 / cnt)
+    assert abs(n.var().item() - math.pi ** 2 / 3) < 0.05
+    p1 = (n <= 1.0).double().mean().item()
+    assert abs(p1 - 1 / (1 + math.exp(-1))) < 5 * math.sqrt(0.2 / cnt)
+    assert torch.equal(wl.logistic_noise(w), n.float())

@@ -8,6 +8,7 @@ and the float64 oracle receive the tensors it returns.
 from .configs import WORKLOADS, Workload, get  # noqa: F401
 from .synth import (  # noqa: F401
     logit_mean_for_rate,
+    logistic_noise,
     decode_step_inputs,
     prompt_chunk_inputs,
     prefill_inputs,

@@ -24,7 +24,7 @@ import torch
 
 from .configs import Workload
 
-_TAGS = {"prompt": 1, "decode": 2, "prefill": 3, "rates": 4}
+_TAGS = {"prompt": 1, "decode": 2, "prefill": 3, "rates": 4, "noise": 5}
 
 
 def logit_mean_for_rate(rate: float) -> float | None:
@@ -118,3 +118,13 @@ def prefill_inputs(w: Workload, device="cpu", replica: int = 0, seq_len: int | N
     v = torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(_kv_dtype(w))
     logit = _logits(w, rates, s, g, device)
     return q, k, v, logit
+
+
+def logistic_noise(w: Workload, device="cpu", replica: int = 0, seq_len: int | None = None) -> torch.Tensor:
+    """[B, S, Hkv] float32 draws of the standard logistic law (the difference of
+    two standard Gumbel draws), by inversion of uniforms: log(u) - log(1 - u)."""
+    s = w.context if seq_len is None else int(seq_len)
+    g = _gen(device, _seed(w, replica, "noise", 0))
+    u = torch.rand((w.batch, s, w.kv_heads), generator=g, device=device, dtype=torch.float64)
+    u = u.clamp(1e-12, 1.0 - 1e-12)
+    return (torch.log(u) - torch.log1p(-u)).to(torch.float32)

@@ -124,6 +124,26 @@ class DmsCache:
             self.shape, self.cache, q, out, scale, self.workspace, self.workspace_bytes, _stream()))
         return out
 
+    def decode_chunk(self, q: torch.Tensor, out: torch.Tensor | None = None,
+                     sm_scale: float | None = None) -> torch.Tensor:
+        """q [B, C, Hq, D] (bf16): queries of the last C appended tokens of every
+        sequence -> out [B, C, Hq, D] float32.  Call before compacting."""
+        if q.dim() != 4 or q.shape[0] != self.batch:
+            raise ValueError("q must be [B, C, Hq, D]")
+        n_query = q.shape[1]
+        qshape = (self.batch, n_query, self.kv_heads * self.group, self.head_dim)
+        _need(q, "q", self.dtype, qshape, self.device)
+        if out is None:
+            out = torch.empty(qshape, dtype=torch.float32, device=self.device)
+        _need(out, "out", torch.float32, qshape, self.device)
+        need = lib.decode_multi_workspace_bytes(self.shape)
+        if getattr(self, "_multi_ws", None) is None or self._multi_ws.numel() < need:
+            self._multi_ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=self.device)
+        scale = 1.0 / math.sqrt(self.head_dim) if sm_scale is None else sm_scale
+        lib.check("dms_decode_attn_multi", lib.dms_decode_attn_multi(
+            self.shape, self.cache, q, n_query, out, scale, self._multi_ws, self._multi_ws.numel(), _stream()))
+        return out
+
     # -- inspection (host copies; for tests and reports) -------------------
     def status_word(self) -> int:
         return int(self.status.item())

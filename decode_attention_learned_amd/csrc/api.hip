@@ -103,6 +103,26 @@ int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *
   return from_hip(dms::launch_decode(*shape, *cache, q, out, sm_scale, workspace, stream));
 }
 
+size_t dms_decode_multi_workspace_bytes(const dms_shape *shape) {
+  if (dms_check_shape(shape) != DMS_OK) return 0;
+  return dms::decode_workspace_layout(dms::units_of(*shape), 16, shape->head_dim).bytes;
+}
+
+int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const void *q,
+                          int32_t n_query, float *out, float sm_scale, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  int rc = dms_check_shape(shape);
+  if (rc) return rc;
+  if (shape->kv_dtype != DMS_KV_BF16) return DMS_EUNSUPPORTED;
+  if ((rc = check_cache(shape, cache))) return rc;
+  if (n_query < 1) return DMS_EINVAL;
+  if (!q || !out || !workspace) return DMS_EINVAL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return DMS_EINVAL;
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
+  if (workspace_bytes < dms_decode_multi_workspace_bytes(shape)) return DMS_EWORKSPACE;
+  return from_hip(dms::launch_decode_multi(*shape, *cache, q, n_query, out, sm_scale, workspace, stream));
+}
+
 static int check_prefill_shape(const dms_shape *shape, int32_t seq_len) {
   if (!shape) return DMS_EINVAL;
   if (shape->batch < 1 || shape->kv_heads < 1 || shape->group < 1 || shape->window < 1)

@@ -56,11 +56,26 @@ __device__ __forceinline__ float fetch(const float *p) {
 
 constexpr int kMergeLds = 2048;  // (chunk, head) weights kept in LDS
 
+// Where column x / D (query head col % G of query col / G) of a unit's output
+// goes: base + (col / G) * query_stride + (col % G) * D + d.  For one query
+// per sequence this is the [B][Hq][D] layout (base = unit * G * D).
+struct OutMap {
+  size_t base, query_stride;
+  int G, D;
+  __device__ __forceinline__ size_t at(int x) const {
+    const int col = x / D, d = x - col * D;
+    return base + size_t(col / G) * query_stride + size_t(col % G) * D + d;
+  }
+};
+
 // Called by every thread of the workgroup after it has published its share of
 // this chunk's partials.  Returns after the unit is merged (if this workgroup
 // was the last of its unit) or at once.
+// G here is the number of output columns of the unit (query heads times
+// queries); `om` places them.
 __device__ inline void count_and_merge(const ChunkInfo &ci, int G, int D, int32_t *merge_count,
-                                       const float2 *part_ml, const float *part_o, float *out) {
+                                       const float2 *part_ml, const float *part_o, float *out,
+                                       const OutMap &om) {
   __shared__ int s_last;
   __shared__ float s_w[kMergeLds];
   __shared__ float s_inv[16];
@@ -73,7 +88,6 @@ __device__ inline void count_and_merge(const ChunkInfo &ci, int G, int D, int32_
   if (!s_last) return;
 
   const float *ml = reinterpret_cast<const float *>(part_ml);
-  const size_t out_base = size_t(ci.unit) * G * D;
   if (ci.nch * G <= kMergeLds) {
     // w[i][g] = 2^(m_ig - M_g); 1 / L_g
     for (int x = threadIdx.x; x < ci.nch * G; x += blockDim.x)
@@ -98,7 +112,7 @@ __device__ inline void count_and_merge(const ChunkInfo &ci, int G, int D, int32_
       float acc = 0.f;
       for (int i = 0; i < ci.nch; ++i)
         acc = fmaf(fetch(part_o + size_t(ci.first + i) * G * D + x), s_w[i * G + g], acc);
-      out[out_base + x] = acc * s_inv[g];
+      out[om.at(x)] = acc * s_inv[g];
     }
   } else {  // very many chunks: the plain two-pass loop
     for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
@@ -115,7 +129,7 @@ __device__ inline void count_and_merge(const ChunkInfo &ci, int G, int D, int32_
           Os = fmaf(fetch(part_o + size_t(ci.first + i) * G * D + x), w, Os);
         }
       }
-      out[out_base + x] = Ls > 0.f ? Os / Ls : 0.f;
+      out[om.at(x)] = Ls > 0.f ? Os / Ls : 0.f;
     }
   }
   if (threadIdx.x == 0)

@@ -161,7 +161,8 @@ __global__ __launch_bounds__(256) void k_decode_generic(
     publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + tid), s_m[tid]);
     publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + tid) + 1, s_l[tid]);
   }
-  count_and_merge(ci, G, D, plan + L.merge_count, part_ml, part_o, out);
+  const OutMap om{size_t(u) * G * D, size_t(G) * D, G, D};
+  count_and_merge(ci, G, D, plan + L.merge_count, part_ml, part_o, out, om);
 }
 
 // ---------------------------------------------------------------------------
@@ -192,7 +193,8 @@ static bool dispatch_group(const dms_shape &s, const dms_cache &c, const E *q, f
 }
 
 bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, float *out,
-                        float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st);
+                        float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
+                        int n_query);
 
 // The decode grid has one workgroup per possible chunk (units +
 // kTargetChunks); workgroups past the plan's chunk count exit at once.
@@ -203,7 +205,7 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
   const float scale_log2 = sm_scale * 1.4426950408889634f;  // exp(x) = exp2(x * log2 e)
   bool done = false;
   if (s.kv_dtype == DMS_KV_BF16) {
-    done = launch_decode_mfma(s, c, q, out, scale_log2, w, ws, st);
+    done = launch_decode_mfma(s, c, q, out, scale_log2, w, ws, st, 1);
     if (!done)
       done = s.head_dim == 64
                  ? dispatch_group<uint16_t, 64>(s, c, static_cast<const uint16_t *>(q), out, scale_log2, w, ws, st)
@@ -214,6 +216,18 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
                : dispatch_group<uint32_t, 128>(s, c, static_cast<const uint32_t *>(q), out, scale_log2, w, ws, st);
   }
   if (!done) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// Queries of a chunk of n_query tokens just appended (bf16 caches, matrix-core
+// kernel): successive launches of at most 16 / G queries, each over the
+// whole split-K plan.  The workspace holds partials for 16 columns.
+hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
+                               float *out, float sm_scale, void *wsv, hipStream_t st) {
+  const DecodeWorkspace w = decode_workspace_layout(units_of(s), 16, s.head_dim);
+  const float scale_log2 = sm_scale * 1.4426950408889634f;
+  if (!launch_decode_mfma(s, c, q, out, scale_log2, w, static_cast<char *>(wsv), st, n_query))
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

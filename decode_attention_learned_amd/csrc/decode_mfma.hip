@@ -62,9 +62,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{lo, hi}, bf16x2v));
 }
 
+// Several queries per sequence (a chunk of C tokens just appended, at
+// positions seq_len - C .. seq_len - 1): one launch serves queries c0 ..
+// c0 + nq - 1 of the chunk, and the 16 B-operand columns hold (query, head)
+// pairs col = (c - c0) * G + g, nq * G <= 16.  Decode is nq = C = 1.
 template <int D>
 __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
-    int units, int hkv, int G, int window, int maxp, float scale_log2,
+    int units, int hkv, int G, int window, int maxp, float scale_log2, int nq, int c0, int C,
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pages,
     const uint16_t *__restrict__ v_pages, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ slot_pos, const uint8_t *__restrict__ slot_alpha,
@@ -85,8 +89,14 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
-  const int col = lane & 15;  // head index in B and C operands, row index in A
+  const int col = lane & 15;  // (query, head) column in B and C operands, row index in A
   const int quad = lane >> 4;
+  const int ncol = nq * G;
+  const int cq = col < ncol ? col / G : 0;
+  // query positions: this column's, and the first and last of the launch
+  const int t_first = t - (C - 1) + c0;
+  const int t_last = t_first + nq - 1;
+  const int t_col = t_first + cq;
 
   // page ids of this chunk are staged in LDS, a segment of at most
   // kMaxChunkPages pages at a time (chunks start on a page boundary)
@@ -94,12 +104,14 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
   const int p_first = s_begin / kPage;
   const int npages = (s_end - s_begin + kPage - 1) / kPage;
 
-  // Q^T operand: head `col`, dims ks*32 + quad*8 .. +8; heads >= G are zero
+  // Q^T operand: column `col`, dims ks*32 + quad*8 .. +8; columns >= nq * G are zero
   uint4 qb[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) qb[ks] = make_uint4(0, 0, 0, 0);
-  if (col < G) {
-    const uint16_t *qp = q + (size_t(b) * hkv * G + size_t(h) * G + col) * D + quad * 8;
+  if (col < ncol) {
+    const int g = col - cq * G;
+    const uint16_t *qp =
+        q + ((size_t(b) * C + c0 + cq) * hkv * G + size_t(h) * G + g) * D + quad * 8;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qb[ks] = ld16(qp + ks * 32);
   }
@@ -161,11 +173,17 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
       for (int e = 0; e < 8; ++e) {
         const int slot = gs + quad * 8 + e;
         const uint32_t marked = ((e < 4 ? a8.x : a8.y) >> (8 * (e & 3))) & 0xffu;
-        const bool live = (slot < s_end) & ((slot < nclean) | (marked == 0u) | ((t - pos[e]) < window));
+        // live for this column's query; live for at least one query of the launch
+        const bool live = (slot < s_end) & ((slot < nclean) | ((pos[e] <= t_col) &
+                                            ((marked == 0u) | ((t_col - pos[e]) < window))));
+        const bool any = (slot < s_end) & ((slot < nclean) | ((pos[e] <= t_last) &
+                                           ((marked == 0u) | ((t_first - pos[e]) < window))));
         sv[e] = live ? sv[e] : -INFINITY;
-        keep[e >> 1] |= live ? (0xffffu << (16 * (e & 1))) : 0u;
+        keep[e >> 1] |= any ? (0xffffu << (16 * (e & 1))) : 0u;
       }
-      // dead or unused slots must not reach the PV product even as 0 * NaN
+      // slots dead for every query of the launch, or unused, must not reach
+      // the PV product even as 0 * NaN (the mask depends on the slot only,
+      // as the value operand row does)
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt) {
         r.v[dt].x &= keep[0];
@@ -219,7 +237,7 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
     }
   }
 
-  // combine the waves of this workgroup (s_o: [waves][G][D + 4] in dynamic LDS)
+  // combine the waves of this workgroup (s_o: [waves][ncol][D + 4] in dynamic LDS)
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
   __shared__ float s_m[kMfmaWaves][16], s_l[kMfmaWaves][16];
@@ -229,14 +247,16 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
     s_m[wave][col] = m_run;
     s_l[wave][col] = l_run;
   }
-  if (col < G) {
+  if (col < ncol) {
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt)
-      *reinterpret_cast<floatx4 *>(&s_o[(wave * G + col) * ostride + dt * 16 + quad * 4]) = o[dt];
+      *reinterpret_cast<floatx4 *>(&s_o[(wave * ncol + col) * ostride + dt * 16 + quad * 4]) = o[dt];
   }
   __syncthreads();
 
-  for (int x = tid; x < G * D; x += kMfmaThreads) {
+  // output of column x / D: query c0 + col / G, head h * G + col % G
+  const OutMap om{((size_t(b) * C + c0) * hkv * G + size_t(h) * G) * D, size_t(hkv) * G * D, G, D};
+  for (int x = tid; x < ncol * D; x += kMfmaThreads) {
     const int g = x / D, d = x % D;
     float M = s_m[0][g];
 #pragma unroll
@@ -249,35 +269,33 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
         if (mw == -INFINITY) continue;
         const float f = exp2f(mw - M);
         Ls = fmaf(s_l[w][g], f, Ls);
-        O = fmaf(s_o[(w * G + g) * ostride + d], f, O);
+        O = fmaf(s_o[(w * ncol + g) * ostride + d], f, O);
       }
     }
     if (ci.nch == 1) {
-      out[size_t(u) * G * D + x] = Ls > 0.f ? O / Ls : 0.f;
+      out[om.at(x)] = Ls > 0.f ? O / Ls : 0.f;
     } else {
-      publish(part_o + size_t(c) * G * D + x, O);
+      publish(part_o + size_t(c) * ncol * D + x, O);
       if (d == 0) {
-        publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + g), M);
-        publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + g) + 1, Ls);
+        publish(reinterpret_cast<float *>(part_ml + size_t(c) * ncol + g), M);
+        publish(reinterpret_cast<float *>(part_ml + size_t(c) * ncol + g) + 1, Ls);
       }
     }
   }
-  if (ci.nch > 1) count_and_merge(ci, G, D, plan + L.merge_count, part_ml, part_o, out);
+  if (ci.nch > 1) count_and_merge(ci, ncol, D, plan + L.merge_count, part_ml, part_o, out, om);
 }
 
-bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, float *out,
-                        float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st) {
-  if (s.kv_dtype != DMS_KV_BF16 || s.group > 16) return false;
-  const char *force = getenv("DMS_DECODE_KERNEL");
-  if (force && force[0] == 'g') return false;  // "generic": the VALU kernel
+bool launch_decode_mfma_part(const dms_shape &s, const dms_cache &c, const void *q, float *out,
+                             float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
+                             int nq, int c0, int C) {
   auto args = [&](auto kern) {
-    const size_t lds = size_t(kMfmaWaves) * s.group * (s.head_dim + 4) * sizeof(float);
+    const size_t lds = size_t(kMfmaWaves) * nq * s.group * (s.head_dim + 4) * sizeof(float);
     if (lds > 48 * 1024)  // gfx950 workgroups may use up to 160 KB of LDS
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     hipLaunchKernelGGL(kern, dim3(w.max_chunks), dim3(kMfmaThreads), lds, st, units_of(s), s.kv_heads,
                        s.group, s.window,
-                       s.max_pages_per_unit, scale_log2, static_cast<const uint16_t *>(q),
+                       s.max_pages_per_unit, scale_log2, nq, c0, C, static_cast<const uint16_t *>(q),
                        static_cast<const uint16_t *>(c.k_pages),
                        static_cast<const uint16_t *>(c.v_pages), c.page_table, c.slot_pos,
                        c.slot_alpha, c.n_slots, c.n_clean, c.seq_len, c.plan,
@@ -287,6 +305,22 @@ bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, f
   if (s.head_dim == 128) args(k_decode_mfma<128>);
   else if (s.head_dim == 64) args(k_decode_mfma<64>);
   else return false;
+  return true;
+}
+
+
+bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, float *out,
+                        float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
+                        int n_query) {
+  if (s.kv_dtype != DMS_KV_BF16 || s.group > 16) return false;
+  const char *force = getenv("DMS_DECODE_KERNEL");
+  if (n_query == 1 && force && force[0] == 'g') return false;  // "generic": the VALU kernel
+  // queries per launch: as many as fit the 16 operand columns
+  const int per = 16 / s.group;
+  for (int c0 = 0; c0 < n_query; c0 += per) {
+    const int nq = n_query - c0 < per ? n_query - c0 : per;
+    if (!launch_decode_mfma_part(s, c, q, out, scale_log2, w, ws, st, nq, c0, n_query)) return false;
+  }
   return true;
 }
 

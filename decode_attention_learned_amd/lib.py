@@ -34,6 +34,8 @@ EXPORTS = (
     "dms_compact",
     "dms_decode_workspace_bytes",
     "dms_decode_attn",
+    "dms_decode_multi_workspace_bytes",
+    "dms_decode_attn_multi",
     "dms_prefill_workspace_bytes",
     "dms_prefill_attn",
     "dms_prefill_attn_relaxed",
@@ -105,6 +107,9 @@ def load() -> ctypes.CDLL:
         "dms_compact": ([SP, CP, P], ctypes.c_int),
         "dms_decode_workspace_bytes": ([SP], ctypes.c_size_t),
         "dms_decode_attn": ([SP, CP, P, P, ctypes.c_float, P, ctypes.c_size_t, P], ctypes.c_int),
+        "dms_decode_multi_workspace_bytes": ([SP], ctypes.c_size_t),
+        "dms_decode_attn_multi": ([SP, CP, P, ctypes.c_int32, P, ctypes.c_float, P, ctypes.c_size_t, P],
+                                  ctypes.c_int),
         "dms_prefill_workspace_bytes": ([SP, ctypes.c_int32], ctypes.c_size_t),
         "dms_prefill_attn": ([SP, P, P, P, P, ctypes.c_int32, ctypes.c_float, P, P, ctypes.c_size_t, P],
                              ctypes.c_int),
@@ -198,3 +203,14 @@ def dms_prefill_attn_relaxed(shape, q, k, v, logit, noise, temperature, seq_len,
                                            _p(noise), float(temperature),
                                            int(seq_len), float(sm_scale), _p(out), _p(workspace),
                                            int(workspace_bytes), stream)
+
+
+def decode_multi_workspace_bytes(shape: DmsShape) -> int:
+    return load().dms_decode_multi_workspace_bytes(ctypes.byref(shape))
+
+
+def dms_decode_attn_multi(shape, cache, q, n_query, out, sm_scale, workspace, workspace_bytes,
+                          stream) -> int:
+    return load().dms_decode_attn_multi(ctypes.byref(shape), ctypes.byref(cache), _p(q), int(n_query),
+                                        _p(out), float(sm_scale), _p(workspace), int(workspace_bytes),
+                                        stream)

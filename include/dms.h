@@ -182,6 +182,30 @@ size_t dms_decode_workspace_bytes(const dms_shape *shape);
 int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *q, float *out,
                     float sm_scale, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of workspace for dms_decode_attn_multi (partials for 16 columns). */
+size_t dms_decode_multi_workspace_bytes(const dms_shape *shape);
+
+/*
+ * Attention of the last n_query tokens of every sequence (a chunk appended
+ * with dms_append(n_new = n_query)) over the cache: query c of sequence b
+ * sits at position t_c = seq_len[b] - n_query + c and attends over the slots
+ * j with pos_j <= t_c and (alpha_j == 0 or t_c - pos_j < w), the same rule as
+ * dms_decode_attn at each t_c (atlas.scime.ai summary, "Approach": eviction
+ * carried out after the delay window; the earlier queries of the chunk do
+ * not see its later tokens).  Call it after appending the chunk and before
+ * any dms_compact: a compaction at the chunk's last position would drop
+ * slots that earlier queries of the chunk still see.
+ *   q    [B][n_query][Hq][D] bf16,   out [B][n_query][Hq][D] float32
+ * bf16 caches only (DMS_EUNSUPPORTED otherwise).  n_query >= 1.  Every
+ * sequence must hold at least n_query tokens (not checked: a query before
+ * position 0 sees nothing and its output is 0).  The chunk is served in
+ * launches of 16 / G queries.  Workspace: dms_decode_multi_workspace_bytes.
+ * Errors as for dms_decode_attn.
+ */
+int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const void *q,
+                          int32_t n_query, float *out, float sm_scale, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Bytes of prefill workspace for `seq_len` tokens of this shape: keys and
  * values re-laid out per 32-key tile for the matrix cores, plus one float

@@ -91,6 +91,15 @@ def test_host_side_errors_need_no_gpu(L):
     misaligned = ctypes.c_void_p(0x1008)
     assert L.dms_decode_attn(ctypes.byref(s), ctypes.byref(full), misaligned, fake, 0.125, fake,
                              1 << 30, None) == lib.DMS_EINVAL
+    M = L.dms_decode_attn_multi
+    sb = _shape(kv_dtype=lib.DMS_KV_BF16)
+    assert M(ctypes.byref(sb), ctypes.byref(full), fake, 0, fake, 0.125, fake, 1 << 30, None) == lib.DMS_EINVAL
+    assert M(ctypes.byref(sb), ctypes.byref(full), fake, 4, fake, 0.125, fake, 10, None) == lib.DMS_EWORKSPACE
+    assert M(ctypes.byref(sb), ctypes.byref(full), fake, 4, fake, 0.0, fake, 1 << 30, None) == lib.DMS_EINVAL
+    assert M(ctypes.byref(_shape(kv_dtype=lib.DMS_KV_F32)), ctypes.byref(full), fake, 4, fake, 0.125, fake,
+             1 << 30, None) == lib.DMS_EUNSUPPORTED
+    # partials for 16 columns, whatever the group
+    assert lib.decode_multi_workspace_bytes(sb) >= lib.decode_workspace_bytes(sb)
     bad = _shape(head_dim=80)
     assert L.dms_compact(ctypes.byref(bad), ctypes.byref(full), None) == lib.DMS_EUNSUPPORTED
 

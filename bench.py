@@ -240,6 +240,57 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
     }
 
 
+def chunk_leg(caches, w, dev, n_query: int = 4, rounds: int = 32) -> dict:
+    """Chunk queries on the decode workload's caches: every round appends
+    n_query tokens to one replica and attends all of them at once
+    (dms_decode_attn_multi), compacting each replica every 16 tokens.  The
+    K/V of every retained entry is read once per launch of 16 / G queries."""
+    import torch
+
+    import workloads as wl
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(977)
+    per_launch = max(1, 16 // w.group)
+    launches = (n_query + per_launch - 1) // per_launch
+    t_app, t_att, t_cmp, retained = [], [], [], []
+    for i in range(rounds):
+        r = i % len(caches)
+        cache, rates = caches[r]
+        k, v, logit = wl.prompt_chunk_inputs(w, 100000 + i, n_query, device=dev, replica=r, rates=rates)
+        q = torch.randn((w.batch, n_query, w.q_heads, w.head_dim), generator=gen, device=dev,
+                        dtype=torch.float32).to(torch.bfloat16)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        cache.append(k, v, logit)
+        ev[1].record()
+        cache.decode_chunk(q)
+        ev[2].record()
+        compacted = ((i // len(caches) + 1) * n_query) % 16 == 0
+        if compacted:
+            cache.compact()
+        ev[3].record()
+        torch.cuda.synchronize()
+        if i >= len(caches):  # first round per replica is warm-up
+            t_app.append(ev[0].elapsed_time(ev[1]))
+            t_att.append(ev[1].elapsed_time(ev[2]))
+            if compacted:
+                t_cmp.append(ev[2].elapsed_time(ev[3]))
+            retained.append(retained_total(cache)[0])
+    att = sum(t_att) / len(t_att)
+    app = sum(t_app) / len(t_app)
+    cmp_per_round = (sum(t_cmp) / max(1, len(t_cmp))) * n_query / 16
+    step = app + att + cmp_per_round
+    bytes_alg = (sum(retained) / len(retained)) * w.head_dim * 2 * 2 * launches
+    return {
+        "n_query": n_query, "launches_per_call": launches,
+        "attn_us": round(att * 1e3, 2), "append_us": round(app * 1e3, 2),
+        "tokens_per_s": round(w.batch * n_query / (step * 1e-3), 1),
+        "kv_gbps": round(bytes_alg / (att * 1e-3) / 1e9, 1),
+        "hbm_frac": round(bytes_alg / (att * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+    }
+
+
 def traffic_from_profile(bytes_alg_per_launch: float):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary,
     or None if there is none or the kernel source changed since it was taken."""
@@ -301,6 +352,7 @@ def main():
                     help="only run the copy/read calibration on a buffer of GIB GiB")
     ap.add_argument("--no-prefill", action="store_true", help="skip the masked-prefill leg")
     ap.add_argument("--prefill-only", action="store_true", help="only run the masked-prefill leg")
+    ap.add_argument("--no-chunk", action="store_true", help="skip the chunk-query leg")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -435,6 +487,10 @@ def main():
     }
     log(f"[bench] {tokens_s:.0f} tok/s, {ms_step * 1e3:.1f} us/step, decode {dec_ms * 1e3:.1f} us "
         f"= {kv_gbps:.0f} GB/s ({100 * kv_gbps / HBM_PEAK_GBPS:.1f}% of HBM peak)")
+    if not args.no_chunk:
+        result["chunk"] = chunk_leg(caches, w, dev)
+        log(f"[bench] chunk of {result['chunk']['n_query']} queries: {result['chunk']['attn_us']:.1f} us, "
+            f"{result['chunk']['tokens_per_s']:.0f} tok/s")
     del inputs, caches, outs
     torch.cuda.empty_cache()
     if not args.no_prefill:

@@ -119,7 +119,10 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
   floatx4 o[DTILES];
 #pragma unroll
   for (int i = 0; i < DTILES; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  // m_run: the column's reference (-inf until a live slot is seen); m_thr =
+  // m_run + kLazy; m_sub: what the exponent subtracts (0 while m_run = -inf)
+  float m_run = -INFINITY, l_run = 0.f, m_thr = -INFINITY, m_sub = 0.f;
+  constexpr float kLazy = 8.0f;
 
   const int ngroups = (s_end - s_begin + kGroup - 1) / kGroup;
 
@@ -193,31 +196,33 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
       }
     }
 
+    // Lazy reference: a column's reference m_run moves only when one of its
+    // scores exceeds it by more than kLazy (log2 units), so every p <= 2^kLazy;
+    // the result is independent of the reference.  The common path is a
+    // per-lane compare; the cross-lane maximum and the rescale run only when
+    // some score crosses the threshold.
     float mx = sv[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    float p[8];
-    float corr = 1.f;
-    if (m_new == -INFINITY) {
+    if (__ballot(mx > m_thr)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const bool move = mx > m_thr;  // uniform over the four lanes of a column
+      const float corr = move ? (m_run == -INFINITY ? 0.f : exp2f(m_run - mx)) : 1.f;
+      l_run *= corr;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = 0.f;
-    } else {
-      corr = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = exp2f(sv[e] - m_new);
+      for (int dt = 0; dt < DTILES; ++dt) o[dt] *= corr;
+      m_run = move ? mx : m_run;
+      m_thr = move ? mx + kLazy : m_thr;
+      m_sub = m_run == -INFINITY ? 0.f : m_run;
     }
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = exp2f(sv[e] - m_sub);
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ps += p[e];
-    l_run = l_run * corr + ps;
-    m_run = m_new;
-    if (__ballot(corr != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt) o[dt] *= corr;
-    }
+    l_run += ps;
     const uint4 pb = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
                                 pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
 #pragma unroll

@@ -87,10 +87,11 @@ class DmsCache:
         self.free_top = torch.empty((1,), **i32)
         self.status = torch.empty((1,), **i32)
         self.plan = torch.empty((lib.plan_words(self.shape),), **i32)
+        self.page_ref = torch.empty((self.num_pages,), **i32)
         self.cache = lib.DmsCacheStruct(*[t.data_ptr() for t in (
             self.k_pages, self.v_pages, self.page_table, self.slot_pos, self.slot_alpha,
             self.n_slots, self.n_clean, self.append_base, self.seq_len, self.free_list,
-            self.free_top, self.status, self.plan)])
+            self.free_top, self.status, self.plan, self.page_ref)])
         self.workspace_bytes = lib.decode_workspace_bytes(self.shape)
         self.workspace = torch.empty((self.workspace_bytes,), dtype=torch.uint8, device=dev)
         self.reset()
@@ -123,6 +124,16 @@ class DmsCache:
         lib.check("dms_decode_attn", lib.dms_decode_attn(
             self.shape, self.cache, q, out, scale, self.workspace, self.workspace_bytes, _stream()))
         return out
+
+    def share_prefix(self, src_seq: int, dst_first: int, n_dst: int) -> None:
+        """Sequences dst_first .. dst_first + n_dst - 1 (empty) take over the state
+        of sequence src_seq, sharing its clean full pages (dms_share_prefix)."""
+        lib.check("dms_share_prefix", lib.dms_share_prefix(self.shape, self.cache, src_seq, dst_first,
+                                                           n_dst, _stream()))
+
+    def release(self, first: int, n: int = 1) -> None:
+        """Empty sequences first .. first + n - 1 and return their pages (dms_release)."""
+        lib.check("dms_release", lib.dms_release(self.shape, self.cache, first, n, _stream()))
 
     def decode_chunk(self, q: torch.Tensor, out: torch.Tensor | None = None,
                      sm_scale: float | None = None) -> torch.Tensor:

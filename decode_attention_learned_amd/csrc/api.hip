@@ -103,6 +103,31 @@ int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *
   return from_hip(dms::launch_decode(*shape, *cache, q, out, sm_scale, workspace, stream));
 }
 
+int dms_share_prefix(const dms_shape *shape, const dms_cache *cache, int32_t src_seq,
+                     int32_t dst_first, int32_t n_dst, hipStream_t stream) {
+  int rc = dms_check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_cache(shape, cache))) return rc;
+  if (!cache->page_ref) return DMS_EINVAL;
+  const int64_t B = shape->batch;
+  if (src_seq < 0 || src_seq >= B || dst_first < 0 || n_dst < 1 || int64_t(dst_first) + n_dst > B)
+    return DMS_EINVAL;
+  if (src_seq >= dst_first && src_seq < dst_first + n_dst) return DMS_EINVAL;
+  if (int64_t(n_dst) * shape->kv_heads > 65535) return DMS_EINVAL;  // copy grid y
+  return from_hip(dms::launch_share(*shape, *cache, src_seq, dst_first, n_dst, stream));
+}
+
+int dms_release(const dms_shape *shape, const dms_cache *cache, int32_t first, int32_t n,
+                hipStream_t stream) {
+  int rc = dms_check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_cache(shape, cache))) return rc;
+  if (!cache->page_ref) return DMS_EINVAL;
+  if (first < 0 || n < 0 || int64_t(first) + n > shape->batch) return DMS_EINVAL;
+  if (n == 0) return DMS_OK;
+  return from_hip(dms::launch_release(*shape, *cache, first, n, stream));
+}
+
 size_t dms_decode_multi_workspace_bytes(const dms_shape *shape) {
   if (dms_check_shape(shape) != DMS_OK) return 0;
   return dms::decode_workspace_layout(dms::units_of(*shape), 16, shape->head_dim).bytes;

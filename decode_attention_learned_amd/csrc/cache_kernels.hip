@@ -41,11 +41,13 @@ __device__ int block_inclusive_scan(int x, int *s_tmp, int &total) {
 __global__ void k_reset(int units, int maxp, int num_pages, int batch, int32_t *page_table,
                         int32_t *free_list, int32_t *free_top, int32_t *n_slots,
                         int32_t *n_clean, int32_t *append_base, int32_t *seq_len,
-                        uint32_t *status) {
+                        uint32_t *status, int32_t *page_ref) {
   const long i0 = long(blockIdx.x) * blockDim.x + threadIdx.x;
   const long stride = long(gridDim.x) * blockDim.x;
   for (long x = i0; x < long(units) * maxp; x += stride) page_table[x] = -1;
   for (long x = i0; x < num_pages; x += stride) free_list[x] = int32_t(x);
+  if (page_ref)
+    for (long x = i0; x < num_pages; x += stride) page_ref[x] = 0;
   for (long x = i0; x < units; x += stride) {
     n_slots[x] = 0;
     n_clean[x] = 0;
@@ -75,7 +77,8 @@ hipError_t launch_reset(const dms_shape &s, const dms_cache &c, hipStream_t st) 
   const int blocks = int(std::min<long>((work + 255) / 256, 4096));
   hipLaunchKernelGGL(k_reset, dim3(std::max(blocks, 1)), dim3(256), 0, st, units,
                      s.max_pages_per_unit, s.num_pages, s.batch, c.page_table, c.free_list,
-                     c.free_top, c.n_slots, c.n_clean, c.append_base, c.seq_len, c.status);
+                     c.free_top, c.n_slots, c.n_clean, c.append_base, c.seq_len, c.status,
+                     c.page_ref);
   const hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : launch_plan(s, c, st);
 }
@@ -401,6 +404,177 @@ hipError_t launch_compact(const dms_shape &s, const dms_cache &c, hipStream_t st
   else launch_compact_t<uint32_t, 128>(s, c, st);
   const hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : launch_plan(s, c, st);
+}
+
+// ---------------------------------------------------------------------------
+// prefix sharing, part 1 (one workgroup): for receiver unit du = d * hkv + h
+// and source unit su = src * hkv + h, the source's full clean pages
+// [0, P), P = n_clean / 64, are entered in the receiver's row and their
+// page_ref counts raised; the T = ceil(n_slots / 64) - P remaining pages are
+// taken from the free stack in unit order (prefix sums, as in append).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kAllocThreads) void k_share_alloc(
+    int hkv, int maxp, int src, int dst_first, int n_dst, int units, int32_t *page_table,
+    int32_t *n_slots, int32_t *n_clean, int32_t *append_base, int32_t *seq_len,
+    const int32_t *free_list, int32_t *free_top, int32_t *page_ref, uint32_t *status,
+    int32_t *plan) {
+  __shared__ int s_tmp[kAllocThreads / kWave];
+  __shared__ int s_taken;
+  __shared__ uint32_t s_flags;
+  if (threadIdx.x == 0) {
+    s_taken = 0;
+    s_flags = 0u;
+  }
+  const int F = *free_top;
+  const int n = n_dst * hkv;
+  __syncthreads();
+  int carry = 0;
+  for (int base = 0; base < n; base += kAllocThreads) {
+    const int x = base + threadIdx.x;
+    int need = 0, du = 0, su = 0, P = 0;
+    bool empty = true;
+    if (x < n) {
+      const int d = dst_first + x / hkv, h = x % hkv;
+      du = d * hkv + h;
+      su = src * hkv + h;
+      empty = n_slots[du] == 0;
+      P = n_clean[su] / kPage;
+      need = empty ? (n_slots[su] + kPage - 1) / kPage - P : 0;
+    }
+    int total = 0;
+    const int incl = block_inclusive_scan<kAllocThreads>(need, s_tmp, total) + carry;
+    if (x < n) {
+      const bool ok = empty && (need == 0 || incl <= F);
+      if (ok) {
+        const int32_t *srow = page_table + size_t(su) * maxp;
+        int32_t *drow = page_table + size_t(du) * maxp;
+        for (int i = 0; i < P; ++i) {
+          drow[i] = srow[i];
+          atomicAdd(&page_ref[srow[i]], 1);
+        }
+        for (int i = 0; i < need; ++i) drow[P + i] = free_list[F - incl + i];
+        n_slots[du] = n_slots[su];
+        n_clean[du] = n_clean[su];
+        append_base[du] = -1;
+        if (x % hkv == 0) seq_len[dst_first + x / hkv] = seq_len[src];
+        if (need > 0) atomicMax(&s_taken, incl);
+      } else {
+        atomicOr(&s_flags, empty ? DMS_STATUS_POOL_EXHAUSTED : DMS_STATUS_NOT_EMPTY);
+      }
+    }
+    carry += total;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    *free_top = F - s_taken;
+    if (s_flags) atomicOr(status, s_flags);
+  }
+  __syncthreads();
+  // every unit's n_slots is read back by the planner: make this workgroup's
+  // writes visible to all of its threads first
+  __threadfence_block();
+  build_plan(units, n_slots, plan);
+}
+
+// prefix sharing, part 2: copy the source's page P + i into the receiver's
+// page P + i (keys, values, positions, decisions), one workgroup per
+// (page, receiver unit); pages the receiver did not get are skipped.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_share_copy(int hkv, int maxp, int src, int dst_first,
+                                                    const int32_t *__restrict__ page_table,
+                                                    const int32_t *__restrict__ n_slots,
+                                                    const int32_t *__restrict__ n_clean,
+                                                    E *__restrict__ k_pages, E *__restrict__ v_pages,
+                                                    int32_t *__restrict__ slot_pos,
+                                                    uint8_t *__restrict__ slot_alpha) {
+  const int i = blockIdx.x, x = blockIdx.y;
+  const int du = (dst_first + x / hkv) * hkv + x % hkv;
+  const int su = src * hkv + x % hkv;
+  const int P = n_clean[su] / kPage;
+  const int T = (n_slots[su] + kPage - 1) / kPage - P;
+  if (i >= T || P + i >= maxp) return;
+  const int dp = page_table[size_t(du) * maxp + P + i];
+  const int sp = page_table[size_t(su) * maxp + P + i];
+  if (dp < 0 || dp == sp) return;
+  constexpr int U4 = kPage * D * int(sizeof(E)) / 16;  // uint4 per page of keys (or values)
+  const uint4 *ks = reinterpret_cast<const uint4 *>(k_pages + size_t(sp) * kPage * D);
+  const uint4 *vs = reinterpret_cast<const uint4 *>(v_pages + size_t(sp) * kPage * D);
+  uint4 *kd = reinterpret_cast<uint4 *>(k_pages + size_t(dp) * kPage * D);
+  uint4 *vd = reinterpret_cast<uint4 *>(v_pages + size_t(dp) * kPage * D);
+  for (int e = threadIdx.x; e < U4; e += blockDim.x) {
+    kd[e] = ks[e];
+    vd[e] = vs[e];
+  }
+  if (threadIdx.x < kPage) {
+    slot_pos[size_t(dp) * kPage + threadIdx.x] = slot_pos[size_t(sp) * kPage + threadIdx.x];
+    slot_alpha[size_t(dp) * kPage + threadIdx.x] = slot_alpha[size_t(sp) * kPage + threadIdx.x];
+  }
+}
+
+hipError_t launch_share(const dms_shape &s, const dms_cache &c, int src, int dst_first, int n_dst,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(k_share_alloc, dim3(1), dim3(kAllocThreads), 0, st, s.kv_heads,
+                     s.max_pages_per_unit, src, dst_first, n_dst, units_of(s), c.page_table,
+                     c.n_slots, c.n_clean, c.append_base, c.seq_len, c.free_list, c.free_top,
+                     c.page_ref, c.status, c.plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(s.max_pages_per_unit, n_dst * s.kv_heads);
+  auto copy = [&](auto kern, auto *kp, auto *vp) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, s.kv_heads, s.max_pages_per_unit, src,
+                       dst_first, c.page_table, c.n_slots, c.n_clean, kp, vp, c.slot_pos,
+                       c.slot_alpha);
+  };
+  const bool bf = s.kv_dtype == DMS_KV_BF16;
+  if (s.head_dim == 128) {
+    if (bf) copy(k_share_copy<uint16_t, 128>, static_cast<uint16_t *>(c.k_pages), static_cast<uint16_t *>(c.v_pages));
+    else copy(k_share_copy<uint32_t, 128>, static_cast<uint32_t *>(c.k_pages), static_cast<uint32_t *>(c.v_pages));
+  } else {
+    if (bf) copy(k_share_copy<uint16_t, 64>, static_cast<uint16_t *>(c.k_pages), static_cast<uint16_t *>(c.v_pages));
+    else copy(k_share_copy<uint32_t, 64>, static_cast<uint32_t *>(c.k_pages), static_cast<uint32_t *>(c.v_pages));
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// release (one workgroup): every page of the released units goes back on the
+// free stack unless another holder remains.  With r = page_ref before the
+// decrement, the holder that sees r <= 0 is the last one and frees the page.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kAllocThreads) void k_release(int hkv, int maxp, int first, int nseq,
+                                                         int units, int32_t *page_table,
+                                                         int32_t *n_slots, int32_t *n_clean,
+                                                         int32_t *append_base, int32_t *seq_len,
+                                                         int32_t *free_list, int32_t *free_top,
+                                                         int32_t *page_ref, int32_t *plan) {
+  const int n = nseq * hkv;
+  for (int x = threadIdx.x; x < n; x += kAllocThreads) {
+    const int u = first * hkv + x;
+    int32_t *row = page_table + size_t(u) * maxp;
+    const int np = (n_slots[u] + kPage - 1) / kPage;
+    for (int i = 0; i < np; ++i) {
+      const int pg = row[i];
+      if (atomicAdd(&page_ref[pg], -1) <= 0) {
+        page_ref[pg] = 0;
+        free_list[atomicAdd(free_top, 1)] = pg;
+      }
+    }
+    for (int i = 0; i < maxp; ++i) row[i] = -1;
+    n_slots[u] = 0;
+    n_clean[u] = 0;
+    append_base[u] = -1;
+  }
+  for (int b = threadIdx.x; b < nseq; b += kAllocThreads) seq_len[first + b] = 0;
+  __syncthreads();
+  build_plan(units, n_slots, plan);
+}
+
+hipError_t launch_release(const dms_shape &s, const dms_cache &c, int first, int n, hipStream_t st) {
+  hipLaunchKernelGGL(k_release, dim3(1), dim3(kAllocThreads), 0, st, s.kv_heads,
+                     s.max_pages_per_unit, first, n, units_of(s), c.page_table, c.n_slots,
+                     c.n_clean, c.append_base, c.seq_len, c.free_list, c.free_top, c.page_ref,
+                     c.plan);
+  return hipGetLastError();
 }
 
 }  // namespace dms

@@ -20,6 +20,7 @@ DMS_EWORKSPACE = -3
 DMS_EHIP = -4
 DMS_STATUS_POOL_EXHAUSTED = 1
 DMS_STATUS_ROW_OVERFLOW = 2
+DMS_STATUS_NOT_EMPTY = 4
 DMS_KV_F32 = 0
 DMS_KV_BF16 = 1
 
@@ -32,6 +33,8 @@ EXPORTS = (
     "dms_reset",
     "dms_append",
     "dms_compact",
+    "dms_share_prefix",
+    "dms_release",
     "dms_decode_workspace_bytes",
     "dms_decode_attn",
     "dms_decode_multi_workspace_bytes",
@@ -73,6 +76,7 @@ class DmsCacheStruct(ctypes.Structure):
         ("free_top", ctypes.c_void_p),
         ("status", ctypes.c_void_p),
         ("plan", ctypes.c_void_p),
+        ("page_ref", ctypes.c_void_p),
     ]
 
 
@@ -105,6 +109,8 @@ def load() -> ctypes.CDLL:
         "dms_reset": ([SP, CP, P], ctypes.c_int),
         "dms_append": ([SP, CP, P, P, P, ctypes.c_int32, P], ctypes.c_int),
         "dms_compact": ([SP, CP, P], ctypes.c_int),
+        "dms_share_prefix": ([SP, CP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P], ctypes.c_int),
+        "dms_release": ([SP, CP, ctypes.c_int32, ctypes.c_int32, P], ctypes.c_int),
         "dms_decode_workspace_bytes": ([SP], ctypes.c_size_t),
         "dms_decode_attn": ([SP, CP, P, P, ctypes.c_float, P, ctypes.c_size_t, P], ctypes.c_int),
         "dms_decode_multi_workspace_bytes": ([SP], ctypes.c_size_t),
@@ -214,3 +220,12 @@ def dms_decode_attn_multi(shape, cache, q, n_query, out, sm_scale, workspace, wo
     return load().dms_decode_attn_multi(ctypes.byref(shape), ctypes.byref(cache), _p(q), int(n_query),
                                         _p(out), float(sm_scale), _p(workspace), int(workspace_bytes),
                                         stream)
+
+
+def dms_share_prefix(shape, cache, src_seq, dst_first, n_dst, stream) -> int:
+    return load().dms_share_prefix(ctypes.byref(shape), ctypes.byref(cache), int(src_seq), int(dst_first),
+                                   int(n_dst), stream)
+
+
+def dms_release(shape, cache, first, n, stream) -> int:
+    return load().dms_release(ctypes.byref(shape), ctypes.byref(cache), int(first), int(n), stream)

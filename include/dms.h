@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DMS_ABI_VERSION 1
+#define DMS_ABI_VERSION 2
 #define DMS_PAGE_SIZE 64
 
 /* host-side return codes */
@@ -53,6 +53,7 @@ extern "C" {
 /* device-side sticky status bits (cache->status) */
 #define DMS_STATUS_POOL_EXHAUSTED 1u /* free pages ran out; that unit's tokens were dropped */
 #define DMS_STATUS_ROW_OVERFLOW 2u   /* a unit needed more than max_pages_per_unit pages */
+#define DMS_STATUS_NOT_EMPTY 4u      /* dms_share_prefix target unit held tokens; left as it was */
 
 /* key/value element types */
 #define DMS_KV_F32 0
@@ -86,6 +87,9 @@ typedef struct dms_shape {
  *   status      [1] uint32     sticky DMS_STATUS_* bits
  *   plan        [dms_plan_words(shape)] int32: the decode split plan, rebuilt
  *               on the device by every call that changes n_slots
+ *   page_ref    [num_pages] int32: holders of a page beyond the first (pages
+ *               shared by dms_share_prefix); may be NULL when no prefix is
+ *               ever shared
  * A unit's slots hold its retained tokens in ascending position order,
  * followed by tokens appended since its last compaction; a slot is dead when
  * its token is marked and w or more positions old, and dead slots are skipped
@@ -105,6 +109,7 @@ typedef struct dms_cache {
   int32_t *free_top;
   uint32_t *status;
   int32_t *plan;
+  int32_t *page_ref;
 } dms_cache;
 
 /* ABI version (DMS_ABI_VERSION).  Never fails. */
@@ -122,7 +127,7 @@ size_t dms_plan_words(const dms_shape *shape);
 /*
  * Empty every unit: page_table = -1, free_list = 0..num_pages-1,
  * free_top = num_pages, n_slots = n_clean = seq_len = 0, append_base = -1,
- * status = 0, plan rebuilt.  Must run once on fresh buffers before any
+ * status = 0, page_ref = 0 (if given), plan rebuilt.  Must run once on fresh buffers before any
  * other call.
  */
 int dms_reset(const dms_shape *shape, const dms_cache *cache, hipStream_t stream);
@@ -181,6 +186,34 @@ size_t dms_decode_workspace_bytes(const dms_shape *shape);
  */
 int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *q, float *out,
                     float sm_scale, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Share a sequence's prompt with other sequences (several reasoning threads
+ * from one prompt; zhaoyang97 Paper-Notes, framework section: many parallel
+ * generations, and the same cache budget spent on more of them).  For every
+ * KV head, sequences dst_first .. dst_first + n_dst - 1 receive the state of
+ * sequence src_seq: its full pages below n_clean (tokens that stay retained
+ * for good, which no later call writes) are shared, not copied, and their
+ * page_ref counts go up by one per receiver; the rest of its slots are
+ * copied into pages taken from the free stack.  n_slots, n_clean and seq_len
+ * are copied; the receivers then append and compact independently.
+ * Receivers must be empty (n_slots == 0); a non-empty one is left unchanged
+ * with DMS_STATUS_NOT_EMPTY set, one that cannot get its pages with
+ * DMS_STATUS_POOL_EXHAUSTED (deterministic order as for dms_append).
+ * cache->page_ref is required.  Host errors: DMS_EINVAL for a null
+ * page_ref, a source inside the receiver range or indices out of range.
+ */
+int dms_share_prefix(const dms_shape *shape, const dms_cache *cache, int32_t src_seq,
+                     int32_t dst_first, int32_t n_dst, hipStream_t stream);
+
+/*
+ * Empty sequences first .. first + n - 1: each page of their units goes back
+ * on the free stack unless another holder remains (page_ref > 0, then
+ * decremented).  n_slots = n_clean = seq_len = 0, append_base = -1,
+ * page_table rows = -1, plan rebuilt.  cache->page_ref is required.
+ */
+int dms_release(const dms_shape *shape, const dms_cache *cache, int32_t first, int32_t n,
+                hipStream_t stream);
 
 /* Bytes of workspace for dms_decode_attn_multi (partials for 16 columns). */
 size_t dms_decode_multi_workspace_bytes(const dms_shape *shape);

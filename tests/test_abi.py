@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strerror(L):
-    assert lib.version() == 1
+    assert lib.version() == 2
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(lib.strerror(code), str)
 
@@ -75,7 +75,7 @@ def test_host_side_errors_need_no_gpu(L):
     s = _shape()
     null_cache = lib.DmsCacheStruct()
     fake = ctypes.c_void_p(0x1000)
-    full = lib.DmsCacheStruct(*([0x1000] * 13))
+    full = lib.DmsCacheStruct(*([0x1000] * 14))
     assert L.dms_reset(None, None, None) == lib.DMS_EINVAL
     assert L.dms_reset(ctypes.byref(s), ctypes.byref(null_cache), None) == lib.DMS_EINVAL
     assert L.dms_append(ctypes.byref(s), ctypes.byref(full), fake, fake, fake, -1, None) == lib.DMS_EINVAL
@@ -91,6 +91,15 @@ def test_host_side_errors_need_no_gpu(L):
     misaligned = ctypes.c_void_p(0x1008)
     assert L.dms_decode_attn(ctypes.byref(s), ctypes.byref(full), misaligned, fake, 0.125, fake,
                              1 << 30, None) == lib.DMS_EINVAL
+    no_ref = lib.DmsCacheStruct(*([0x1000] * 13), None)
+    assert L.dms_share_prefix(ctypes.byref(s), ctypes.byref(no_ref), 0, 1, 1, None) == lib.DMS_EINVAL
+    assert L.dms_release(ctypes.byref(s), ctypes.byref(no_ref), 0, 1, None) == lib.DMS_EINVAL
+    assert L.dms_share_prefix(ctypes.byref(s), ctypes.byref(full), 0, 0, 2, None) == lib.DMS_EINVAL  # src in range
+    assert L.dms_share_prefix(ctypes.byref(s), ctypes.byref(full), 0, 1, 2, None) == lib.DMS_EINVAL  # past B
+    assert L.dms_share_prefix(ctypes.byref(s), ctypes.byref(full), 2, 0, 1, None) == lib.DMS_EINVAL  # src past B
+    assert L.dms_share_prefix(ctypes.byref(s), ctypes.byref(full), 1, 0, 0, None) == lib.DMS_EINVAL  # no receiver
+    assert L.dms_release(ctypes.byref(s), ctypes.byref(full), 1, 2, None) == lib.DMS_EINVAL
+    assert L.dms_release(ctypes.byref(s), ctypes.byref(full), 0, 0, None) == lib.DMS_OK
     M = L.dms_decode_attn_multi
     sb = _shape(kv_dtype=lib.DMS_KV_BF16)
     assert M(ctypes.byref(sb), ctypes.byref(full), fake, 0, fake, 0.125, fake, 1 << 30, None) == lib.DMS_EINVAL

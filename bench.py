@@ -291,6 +291,80 @@ def chunk_leg(caches, w, dev, n_query: int = 4, rounds: int = 32) -> dict:
     }
 
 
+def shared_prefix_leg(w, dev, threads: int = 8, steps: int = 24) -> dict:
+    """Width scaling from shared prompts: the decode workload's B sequences as
+    B / threads prompts with `threads` threads each.  One cache holds every
+    prompt once per thread (each thread appended it); the other holds it once
+    per prompt and shares it (dms_share_prefix).  Same tokens, same outputs;
+    reported: pages held and decode-attention time of both."""
+    import dataclasses
+
+    import torch
+
+    import workloads as wl
+    from decode_attention_learned_amd import DmsCache
+
+    n_prompts = w.batch // threads
+    wp = dataclasses.replace(w, batch=n_prompts)
+    rates = wl.unit_eviction_rates(wp)
+    max_pages, _ = pool_size(w, wl.unit_eviction_rates(w), steps + 64)
+    num_pages = w.units * max_pages
+    caches = {m: DmsCache(w.batch, w.kv_heads, w.group, w.head_dim, torch.bfloat16, num_pages=num_pages,
+                          max_pages_per_unit=max_pages, window=w.window, device=dev)
+              for m in ("copied", "shared")}
+    lead = torch.arange(0, w.batch, threads, device=dev)
+    for ci, start in enumerate(range(0, w.context, w.prompt_chunk)):
+        n = min(w.prompt_chunk, w.context - start)
+        k, v, logit = wl.prompt_chunk_inputs(wp, ci, n, device=dev, rates=rates)
+        caches["copied"].append(k.repeat_interleave(threads, 0), v.repeat_interleave(threads, 0),
+                                logit.repeat_interleave(threads, 0))
+        caches["copied"].compact()
+        # followers of the shared cache receive marked zero tokens, dropped below
+        kz = torch.zeros((w.batch, *k.shape[1:]), dtype=k.dtype, device=dev)
+        vz = torch.zeros_like(kz)
+        lz = torch.ones((w.batch, *logit.shape[1:]), dtype=logit.dtype, device=dev)
+        kz[lead], vz[lead], lz[lead] = k, v, logit
+        caches["shared"].append(kz, vz, lz)
+        caches["shared"].compact()
+        del k, v, logit, kz, vz, lz
+    sh = caches["shared"]
+    for p_ in range(n_prompts):
+        sh.release(p_ * threads + 1, threads - 1)
+        sh.share_prefix(p_ * threads, p_ * threads + 1, threads - 1)
+    torch.cuda.synchronize()
+    held = {m: c.num_pages - int(c.free_top.item()) for m, c in caches.items()}
+    if any(c.status_word() for c in caches.values()):
+        raise RuntimeError("device status set while building the shared-prefix caches")
+    ws = dataclasses.replace(w, context=steps)
+    q, k, v, logit = wl.prefill_inputs(ws, device=dev)
+    times = {m: [] for m in caches}
+    outs = {}
+    for t in range(steps):
+        for m, c in caches.items():
+            c.append(k[:, t:t + 1].contiguous(), v[:, t:t + 1].contiguous(), logit[:, t:t + 1].contiguous())
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            outs[m] = c.decode(q[:, t].contiguous())
+            b.record()
+            torch.cuda.synchronize()
+            if t >= 4:
+                times[m].append(a.elapsed_time(b))
+            if t % w.compact_every == w.compact_every - 1:
+                c.compact()
+    same = bool(torch.equal(outs["copied"], outs["shared"]))
+    retained, _ = retained_total(caches["copied"])
+    bytes_alg = retained * w.head_dim * 2 * 2
+    us = {m: 1e3 * sum(x) / len(x) for m, x in times.items()}
+    return {
+        "prompts": n_prompts, "threads_per_prompt": threads, "context": w.context,
+        "pages_copied": held["copied"], "pages_shared": held["shared"],
+        "memory_ratio": round(held["copied"] / held["shared"], 2),
+        "decode_us_copied": round(us["copied"], 2), "decode_us_shared": round(us["shared"], 2),
+        "kv_gbps_algorithmic_shared": round(bytes_alg / (us["shared"] * 1e-6) / 1e9, 1),
+        "outputs_identical": same,
+    }
+
+
 def traffic_from_profile(bytes_alg_per_launch: float):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary,
     or None if there is none or the kernel source changed since it was taken."""
@@ -353,6 +427,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the masked-prefill leg")
     ap.add_argument("--prefill-only", action="store_true", help="only run the masked-prefill leg")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunk-query leg")
+    ap.add_argument("--no-share", action="store_true", help="skip the shared-prefix leg")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -493,6 +568,12 @@ def main():
             f"{result['chunk']['tokens_per_s']:.0f} tok/s")
     del inputs, caches, outs
     torch.cuda.empty_cache()
+    if not args.no_share:
+        result["shared_prefix"] = shared_prefix_leg(w, dev)
+        sp = result["shared_prefix"]
+        log(f"[bench] shared prompts: {sp['pages_shared']} pages vs {sp['pages_copied']}, decode "
+            f"{sp['decode_us_shared']:.1f} us vs {sp['decode_us_copied']:.1f} us")
+        torch.cuda.empty_cache()
     if not args.no_prefill:
         log("[bench] masked prefill, 8192 tokens")
         result["prefill"] = prefill_leg()

@@ -156,7 +156,7 @@ def _time_calls(fn, iters: int) -> float:
     return sum(a.elapsed_time(b) for a, b in evs) / iters
 
 
-def gathered_tiles(keep, s_len: int, window: int, block: int = 64, tile: int = 32) -> int:
+def gathered_tiles(keep, s_len: int, window: int, block: int = 32, tile: int = 32) -> int:
     """Key tiles the gathered kernel processes, summed over units and query
     blocks: the gathered kept keys up to the block's last query - w, plus the
     dense tiles of the band (q0 - w, last query]."""
@@ -180,7 +180,7 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
     Dense (dms_prefill_attn): causal FLOPs per second of one call (pack pass +
     attention kernel) against the dense bf16 MFMA peak.  Gathered
     (dms_prefill_attn_gathered): the same result; its roofline uses the MFMA
-    work it executes (key tiles x 64 queries x heads), and the causal FLOPs
+    work it executes (key tiles x 32 queries x heads), and the causal FLOPs
     over its time are reported as the equivalent dense rate."""
     import torch
 
@@ -213,9 +213,9 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
     pairs = (kept_before + torch.clamp(i + 1, max=w.window)[None, :, None]).sum().item() * w.group
     visible = 4.0 * d * pairs
     tflops = causal / (ms * 1e-3) / 1e12
-    # executed MFMA work of the gathered kernel: per key tile and workgroup,
-    # QK and PV products over 32 keys x 64 queries x G heads x D
-    executed = 4.0 * 32 * 64 * d * w.group * gathered_tiles(keep, s_len, w.window)
+    # executed MFMA work of the gathered kernel: per key tile and workgroup
+    # (32 query positions), QK and PV products over 32 keys x 32 queries x G heads x D
+    executed = 4.0 * 32 * 32 * d * w.group * gathered_tiles(keep, s_len, w.window)
     g_tflops = executed / (ms_g * 1e-3) / 1e12
     return {
         "workload": name, "batch": w.batch, "seq_len": s_len, "q_heads": w.q_heads,

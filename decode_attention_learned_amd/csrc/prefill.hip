@@ -15,12 +15,13 @@
 // for eviction), into the caller's workspace.  k_prefill then only copies
 // whole fragments into LDS.
 //
-// Work decomposition.  A workgroup of 8 waves takes 64 query positions of
-// one KV head: wave w serves query head g = 4*hg + (w % 4) of the group and
-// query positions i0 + 32*(w / 4) .. +32.  Keys are consumed in tiles of 32
-// from position 0 up to the causal end of the block.  Each key tile is
-// loaded once per workgroup into LDS (four buffers) and serves all four
-// heads.
+// Work decomposition.  A workgroup of NW = 4 or 8 waves takes 32 (NW / 4)
+// query positions of one KV head: wave w serves query head g = 4*hg + (w % 4)
+// of the group and query positions i0 + 32*(w / 4) .. +32.  Keys are consumed
+// in tiles of 32 from position 0 up to the causal end of the block.  Each key
+// tile is loaded once per workgroup into LDS (four buffers) and serves all
+// four heads.  The build uses NW = 4 with two workgroups per CU (measured
+// faster than NW = 8 with the two-phase offset below).
 //
 // Per tile and wave the two products are the ones of the decode kernel, with
 // query positions in place of heads:
@@ -33,10 +34,10 @@
 //
 // Two phases per tile.  Phase 1 (matrix cores) computes the scores of tile k
 // and the PV product of tile k-1; phase 2 (vector unit) masks, checks and
-// exponentiates the scores of tile k.  Waves 0-3 and waves 4-7 share the four
-// SIMDs and run half a tile apart (a workgroup barrier after every phase):
-// while one wave of a SIMD is in phase 1 the other is in phase 2, so the
-// matrix products of one overlap the softmax of the other.
+// exponentiates the scores of tile k.  With 8 waves, waves 0-3 and waves 4-7
+// share the four SIMDs and run half a tile apart (a workgroup barrier after
+// every phase): while one wave of a SIMD is in phase 1 the other is in phase
+// 2.  With 4 waves the two workgroups of a CU interleave freely.
 //
 // Far and near tiles.  A tile whose keys all lie `w` or more positions behind
 // every query of the workgroup ("far") is masked by the decision alone, which
@@ -64,7 +65,6 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 
 constexpr int PD = 128;            // head dimension
 constexpr int PBN = 32;            // keys per tile
-constexpr int PBM = 64;            // query positions per workgroup
 constexpr int PWAVES = 8;          // waves per workgroup
 constexpr int PHPW = 4;            // query heads per workgroup
 constexpr int PKS = PD / 32;       // QK products per 16-key tile
@@ -74,6 +74,9 @@ constexpr int PK_FRAGS = 2 * PKS;  // key fragments per tile
 constexpr int PV_FRAGS = PDT;      // value fragments per tile
 constexpr int PBUF = 4;            // LDS tile buffers
 constexpr float kLazy = 8.0f;      // largest exponent (log2 units) before the reference moves
+#ifndef DMS_PREFILL_WAVES
+#define DMS_PREFILL_WAVES 4        // waves per workgroup of the dense kernel (4 or 8)
+#endif
 #ifndef DMS_GATHERED_WAVES
 #define DMS_GATHERED_WAVES 4       // waves per workgroup of the gathered kernel (4 or 8)
 #endif
@@ -183,14 +186,20 @@ __device__ __forceinline__ void exponentials(const floatx4 (&s)[2][2], Softmax &
   }
 }
 
+// PV product of one tile: every value fragment is read before the products,
+// so the LDS latency is paid once per tile.
 __device__ __forceinline__ void pv_tile(const uint4 *__restrict__ sv, const uint4 (&pb)[2], int lane,
                                         floatx4 (&o)[PDT][2]) {
+  uint4 va[PDT];
+#pragma unroll
+  for (int dt = 0; dt < PDT; ++dt) va[dt] = sv[dt * PFRAG + lane];
 #pragma unroll
   for (int dt = 0; dt < PDT; ++dt) {
-    const uint4 va = sv[dt * PFRAG + lane];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma(va, pb[qt], o[dt][qt]);
+    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma(va[dt], pb[qt], o[dt][qt]);
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, PDT, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * PDT, 0);
 }
 
 // Phase 1 of tile k: PV product of tile k - 1 and QK product of tile k (from
@@ -366,7 +375,8 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
   vdst[t] = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-__global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 2) void k_prefill(
     int batch, int S, int hkv, int G, int window, float scale_log2, const uint16_t *__restrict__ q,
     const uint4 *__restrict__ packed, const floatx4 *__restrict__ mask, float *__restrict__ out) {
   const int tid = threadIdx.x;
@@ -375,7 +385,9 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
   const int col = lane & 15, quad = lane >> 4;
   const int Hq = hkv * G;
   const int ngh = (G + PHPW - 1) / PHPW;
-  const int nqb = (S + PBM - 1) / PBM;
+  constexpr int GBM = 32 * (NW / PHPW);  // query positions per workgroup
+  constexpr int NT = NW * 64;
+  const int nqb = (S + GBM - 1) / GBM;
 
   // Workgroup -> (b, h, hg, query block).  Consecutive ids go to different
   // XCDs (round-robin), so all query blocks of one (b, h, hg) are given ids of
@@ -396,11 +408,11 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
   const int g = hg * PHPW + (wave % PHPW);
   const bool active = g < G;
   const int hq = h * G + (active ? g : 0);
-  const int qi0 = qb * PBM + (wave / PHPW) * 32;  // this wave's first query position
-  const int i_end = min(S, qb * PBM + PBM);       // workgroup's causal key end
+  const int qi0 = qb * GBM + (wave / PHPW) * 32;  // this wave's first query position
+  const int i_end = min(S, qb * GBM + GBM);       // workgroup's causal key end
   const int ntiles = (i_end + PBN - 1) / PBN;
-  // far tiles: j0 + 31 + window <= qb * PBM, i.e. behind every query by >= window
-  const int far_x = qb * PBM - window - (PBN - 1);
+  // far tiles: j0 + 31 + window <= qb * GBM, i.e. behind every query by >= window
+  const int far_x = qb * GBM - window - (PBN - 1);
   const int nfar = far_x >= 0 ? min(ntiles, far_x / PBN + 1) : 0;
 
   __shared__ uint4 sK[PBUF][PK_FRAGS * PFRAG];
@@ -452,19 +464,31 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
   // the last read of tile k-2 in window 2k) and loads its share of tile k+3.
   // Thread t copies uint4 t and t + 512 of the 16 KB packed tile; threads
   // 0..7 copy the mask.
-  uint4 ta, tb;
+  static_assert(NT == 256 || NT == 512, "four or eight waves");
+  uint4 tr0, tr1, tr2, tr3;
   floatx4 tm;
 #define DMS_PF_GLOAD(tile)                                         \
   do {                                                             \
     const uint4 *src_ = pk + size_t(tile) * PTILE_U4;              \
-    ta = src_[tid];                                                \
-    tb = src_[tid + PWAVES * 64];                                  \
+    tr0 = src_[tid];                                               \
+    tr1 = src_[tid + NT];                                          \
+    if constexpr (NT == 256) {                                     \
+      tr2 = src_[tid + 2 * NT];                                    \
+      tr3 = src_[tid + 3 * NT];                                    \
+    }                                                              \
     if (tid < PBN / 4) tm = pm[size_t(tile) * (PBN / 4) + tid];    \
   } while (0)
 #define DMS_PF_LSTORE(buf)                    \
   do {                                        \
-    sK[buf][tid] = ta;                        \
-    sV[buf][tid] = tb;                        \
+    if constexpr (NT == 256) {                \
+      sK[buf][tid] = tr0;                     \
+      sK[buf][tid + NT] = tr1;                \
+      sV[buf][tid] = tr2;                     \
+      sV[buf][tid + NT] = tr3;                \
+    } else {                                  \
+      sK[buf][tid] = tr0;                     \
+      sV[buf][tid] = tr1;                     \
+    }                                         \
     if (tid < PBN / 4) sB[buf][tid] = tm;     \
   } while (0)
   DMS_PF_GLOAD(0);
@@ -478,20 +502,20 @@ __global__ __launch_bounds__(PWAVES * 64, 2) void k_prefill(
 
   // tiles this wave needs: keys up to its last query position
   const int ntw = min(ntiles, (qi0 + 31) / PBN + 1);
-  const bool lead = wave < PWAVES / 2;
+  const bool lead = NW == 4 || wave < NW / 2;
   floatx4 s[2][2];
   uint4 pb[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
 
   if (!lead) __syncthreads();
   for (int k = 0; k <= ntiles; ++k) {
     phase1(k, ntw, nfar, active, sK, sV, sB, qf, s, pb, o, lane, quad);
-    __syncthreads();
+    if (NW == 8) __syncthreads();
     phase2(k, ntw, nfar, active, S, window, qi0, col, quad, sB, s, sm, o, pb, c);
     if (k + 2 < ntiles) DMS_PF_LSTORE((k + 2) % PBUF);
     if (k + 3 < ntiles) DMS_PF_GLOAD(k + 3);
     __syncthreads();
   }
-  if (lead) __syncthreads();
+  if (NW == 8 && lead) __syncthreads();
 #undef DMS_PF_LSTORE
 #undef DMS_PF_GLOAD
 
@@ -794,13 +818,14 @@ hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, cons
                      relaxed ? 1.f / temperature : 0.f, 1.f / sm_scale, relaxed, packed, mask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  constexpr int NW = DMS_PREFILL_WAVES;
   const int ngh = (s.group + PHPW - 1) / PHPW;
   const int nbh = s.batch * s.kv_heads * ngh;
-  const int nqb = (seq_len + PBM - 1) / PBM;
+  const int nqb = (seq_len + 32 * (NW / PHPW) - 1) / (32 * (NW / PHPW));
   const int per_xcd_pairs = (nbh + 7) / 8;
   const long blocks = long(per_xcd_pairs) * nqb * 8;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_prefill, dim3(unsigned(blocks)), dim3(PWAVES * 64), 0, st, s.batch, seq_len,
+  hipLaunchKernelGGL(k_prefill<NW>, dim3(unsigned(blocks)), dim3(NW * 64), 0, st, s.batch, seq_len,
                      s.kv_heads, s.group, s.window, sm_scale * 1.4426950408889634f,
                      static_cast<const uint16_t *>(q), packed,
                      reinterpret_cast<const floatx4 *>(mask), out);

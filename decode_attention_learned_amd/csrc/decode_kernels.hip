@@ -219,11 +219,17 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
   return hipGetLastError();
 }
 
-// Queries of a chunk of n_query tokens just appended (bf16 caches, matrix-core
-// kernel): successive launches of at most 16 / G queries, each over the
-// whole split-K plan.  The workspace holds partials for 16 columns.
+// Queries of a chunk of n_query tokens just appended (bf16 caches).  Long
+// chunks (32 queries or more, head_dim 128) run the tiled chunk kernel, one
+// pass over the cache per 32 queries; shorter ones run the split-K decode
+// kernel in launches of at most 16 / G queries.  The workspace holds partials
+// for 16 columns.
+constexpr int kChunkKernelMin = 32;
+
 hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
                                float *out, float sm_scale, void *wsv, hipStream_t st) {
+  if (n_query >= kChunkKernelMin && s.head_dim == 128 && s.group <= 16)
+    return launch_chunk_attn(s, c, q, n_query, out, sm_scale, st);
   const DecodeWorkspace w = decode_workspace_layout(units_of(s), 16, s.head_dim);
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   if (!launch_decode_mfma(s, c, q, out, scale_log2, w, static_cast<char *>(wsv), st, n_query))

@@ -78,6 +78,8 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
 hipError_t launch_share(const dms_shape &s, const dms_cache &c, int src, int dst_first, int n_dst,
                         hipStream_t st);
 hipError_t launch_release(const dms_shape &s, const dms_cache &c, int first, int n, hipStream_t st);
+hipError_t launch_chunk_attn(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
+                             float *out, float sm_scale, hipStream_t st);
 hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
                                float *out, float sm_scale, void *ws, hipStream_t st);
 // temperature <= 0: the hard rule; > 0: the relaxed mask (noise may be null)

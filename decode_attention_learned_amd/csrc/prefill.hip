@@ -311,6 +311,38 @@ __device__ __forceinline__ void g_phase2(int k, int nT, int nclean, int ngt, int
   exponentials(s, sm, c, pb);
 }
 
+// ---- chunk attention over the paged cache -----------------------------------
+// Phase 2 of cache tile k for chunk queries: slots below n_clean are seen by
+// every query; above it, slot j is seen by query position t iff it is in use,
+// pos_j <= t, and it is unmarked or t - pos_j < w.
+__device__ __forceinline__ void c_phase2(int k, int nt, int nclean_t, bool active, int ns, int nc,
+                                         int window, int t_first, int col, int quad,
+                                         const int4 (*sPos)[PBN / 4], const uint2 (*sAl)[PBN / 8],
+                                         floatx4 (&s)[2][2], Softmax &sm, floatx4 (&o)[PDT][2],
+                                         uint4 (&pb)[2], float c) {
+  if (!active || k >= nt) return;
+  if (k >= nclean_t) {
+    const int buf = k % PBUF;
+    const int4 p0 = sPos[buf][2 * quad], p1 = sPos[buf][2 * quad + 1];
+    const int pos[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    const uint2 a8 = sAl[buf][quad];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int t = t_first + 16 * qt + col;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int slot = k * PBN + 8 * quad + e;
+        const uint32_t marked = ((e < 4 ? a8.x : a8.y) >> (8 * (e & 3))) & 0xffu;
+        const bool vis = (slot < ns) &
+                         ((slot < nc) | ((pos[e] <= t) & ((marked == 0u) | (t - pos[e] < window))));
+        s[qt][e >> 2][e & 3] = vis ? s[qt][e >> 2][e & 3] : -INFINITY;
+      }
+    }
+  }
+  if (__ballot(crosses(s, sm))) move_reference(s, sm, o, c);
+  exponentials(s, sm, c, pb);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -868,6 +900,159 @@ hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void
                      seq_len, s.kv_heads, s.group, s.window, sm_scale * 1.4426950408889634f,
                      static_cast<const uint16_t *>(q), dense, gathered,
                      reinterpret_cast<const int4 *>(gposp), tile_cnt, keptw, out);
+  return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// Chunk attention: the last C appended tokens of every sequence attend over
+// the unit's cache, each at its own position (same rule as decode).  A 32-slot
+// group of a cache page has exactly the layout of a packed prefill tile
+// (key_index / value_index), so tiles are copied from the pages into LDS with
+// no pack pass.  Workgroup: one unit, 32 chunk queries, four query heads (one
+// per wave); grid (ceil(C / 32), units * ceil(G / 4)).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void k_chunk_attn(
+    int hkv, int G, int window, int maxp, int C, float scale_log2, const uint16_t *__restrict__ q,
+    const uint4 *__restrict__ k_pages, const uint4 *__restrict__ v_pages,
+    const int32_t *__restrict__ page_table, const int4 *__restrict__ slot_pos,
+    const uint4 *__restrict__ slot_alpha, const int32_t *__restrict__ n_slots,
+    const int32_t *__restrict__ n_clean, const int32_t *__restrict__ seq_len, float *__restrict__ out) {
+  constexpr int NT = 256;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = lane_id();
+  const int col = lane & 15, quad = lane >> 4;
+  const int ngh = (G + PHPW - 1) / PHPW;
+  const int u = blockIdx.y / ngh, hg = blockIdx.y % ngh;
+  const int b = u / hkv, h = u % hkv;
+  const int Hq = hkv * G;
+  const int g = hg * PHPW + wave;
+  const bool active = g < G;
+  const int hq = h * G + (active ? g : 0);
+  const int c0 = blockIdx.x * 32;                 // first chunk query of the workgroup
+  const int t_first = seq_len[b] - C + c0;        // its position
+  const int ns = n_slots[u], nc = n_clean[u];
+  const int nt = (ns + PBN - 1) / PBN;
+  const int nclean_t = nc / PBN;                  // tiles wholly below n_clean
+  const int32_t *row = page_table + size_t(u) * maxp;
+
+  __shared__ uint4 sK[PBUF][PK_FRAGS * PFRAG];
+  __shared__ uint4 sV[PBUF][PV_FRAGS * PFRAG];
+  __shared__ int4 sPos[PBUF][PBN / 4];
+  __shared__ uint2 sAl[PBUF][PBN / 8];
+
+  uint4 qf[2][PKS];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int cq = c0 + 16 * qt + col;
+#pragma unroll
+    for (int ks = 0; ks < PKS; ++ks) {
+      qf[qt][ks] = make_uint4(0, 0, 0, 0);
+      if (active && cq < C)
+        qf[qt][ks] = *reinterpret_cast<const uint4 *>(
+            q + ((size_t(b) * C + cq) * Hq + hq) * PD + ks * 32 + quad * 8);
+    }
+  }
+  floatx4 o[PDT][2];
+#pragma unroll
+  for (int dt = 0; dt < PDT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  Softmax sm;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    sm.m[qt] = -INFINITY;
+    sm.nmc[qt] = 0.f;
+    sm.thr[qt] = -INFINITY;
+    sm.l[qt] = 0.f;
+  }
+  const float c = scale_log2;
+
+  // tile t = slots 32 t .. 32 t + 31: page row[t / 2], group t % 2 of the
+  // page; thread t copies uint4 tid and tid + 256 of its keys and of its
+  // values, threads 0..7 the positions, threads 8..9 the decisions
+  uint4 tk0, tk1, tv0, tv1, tx;
+#define DMS_PC_GLOAD(t)                                                                   \
+  do {                                                                                    \
+    const size_t grp_ = size_t(row[(t) >> 1]) * 2 + ((t) & 1);                            \
+    const uint4 *ks_ = k_pages + grp_ * (PK_FRAGS * PFRAG);                               \
+    const uint4 *vs_ = v_pages + grp_ * (PV_FRAGS * PFRAG);                               \
+    tk0 = ks_[tid];                                                                       \
+    tk1 = ks_[tid + NT];                                                                  \
+    tv0 = vs_[tid];                                                                       \
+    tv1 = vs_[tid + NT];                                                                  \
+    if (tid < 8) tx = __builtin_bit_cast(uint4, slot_pos[grp_ * 8 + tid]);                \
+    else if (tid < 10) tx = slot_alpha[grp_ * 2 + tid - 8];                               \
+  } while (0)
+#define DMS_PC_LSTORE(t)                                                                  \
+  do {                                                                                    \
+    const int b_ = (t) % PBUF;                                                            \
+    sK[b_][tid] = tk0;                                                                    \
+    sK[b_][tid + NT] = tk1;                                                               \
+    sV[b_][tid] = tv0;                                                                    \
+    sV[b_][tid + NT] = tv1;                                                               \
+    if (tid < 8) sPos[b_][tid] = __builtin_bit_cast(int4, tx);                            \
+    else if (tid < 10) {                                                                  \
+      sAl[b_][2 * (tid - 8)] = make_uint2(tx.x, tx.y);                                    \
+      sAl[b_][2 * (tid - 8) + 1] = make_uint2(tx.z, tx.w);                                \
+    }                                                                                     \
+  } while (0)
+  if (nt > 0) {
+    DMS_PC_GLOAD(0);
+    DMS_PC_LSTORE(0);
+  }
+  if (nt > 1) {
+    DMS_PC_GLOAD(1);
+    DMS_PC_LSTORE(1);
+  }
+  if (nt > 2) DMS_PC_GLOAD(2);
+  __syncthreads();
+
+  floatx4 s[2][2];
+  uint4 pb[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  const floatx4 zero[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+  for (int k = 0; k <= nt; ++k) {
+    if (active) {
+      if (k >= 1) pv_tile(sV[(k - 1) % PBUF], pb, lane, o);
+      if (k < nt) qk_tile(sK[k % PBUF], zero, qf, lane, s);
+    }
+    c_phase2(k, nt, nclean_t, active, ns, nc, window, t_first, col, quad, sPos, sAl, s, sm, o, pb, c);
+    if (k + 2 < nt) DMS_PC_LSTORE(k + 2);
+    if (k + 3 < nt) DMS_PC_GLOAD(k + 3);
+    __syncthreads();
+  }
+#undef DMS_PC_LSTORE
+#undef DMS_PC_GLOAD
+
+  if (!active) return;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float l = sm.l[qt];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int cq = c0 + 16 * qt + col;
+    if (cq < C) {
+      float *op = out + ((size_t(b) * C + cq) * Hq + hq) * PD + quad * 4;
+#pragma unroll
+      for (int dt = 0; dt < PDT; ++dt)
+        *reinterpret_cast<floatx4 *>(op + dt * 16) = o[dt][qt] * inv;
+    }
+  }
+}
+
+hipError_t launch_chunk_attn(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
+                             float *out, float sm_scale, hipStream_t st) {
+  const int ngh = (s.group + PHPW - 1) / PHPW;
+  const long gy = long(s.batch) * s.kv_heads * ngh;
+  if (gy > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_chunk_attn, dim3((n_query + 31) / 32, unsigned(gy)), dim3(256), 0, st,
+                     s.kv_heads, s.group, s.window, s.max_pages_per_unit, n_query,
+                     sm_scale * 1.4426950408889634f, static_cast<const uint16_t *>(q),
+                     static_cast<const uint4 *>(c.k_pages), static_cast<const uint4 *>(c.v_pages),
+                     c.page_table, reinterpret_cast<const int4 *>(c.slot_pos),
+                     reinterpret_cast<const uint4 *>(c.slot_alpha), c.n_slots, c.n_clean, c.seq_len, out);
   return hipGetLastError();
 }
 

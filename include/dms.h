@@ -230,10 +230,11 @@ size_t dms_decode_multi_workspace_bytes(const dms_shape *shape);
  * slots that earlier queries of the chunk still see.
  *   q    [B][n_query][Hq][D] bf16,   out [B][n_query][Hq][D] float32
  * bf16 caches only (DMS_EUNSUPPORTED otherwise).  n_query >= 1.  Every
- * sequence must hold at least n_query tokens (not checked: a query before
- * position 0 sees nothing and its output is 0).  The chunk is served in
- * launches of 16 / G queries.  Workspace: dms_decode_multi_workspace_bytes.
- * Errors as for dms_decode_attn.
+ * sequence must hold at least n_query tokens (not checked; outputs are
+ * unspecified otherwise).  Chunks of 32 queries or more with head_dim 128
+ * run a tiled kernel that reads the cache once per 32 queries; shorter ones
+ * run the split-K decode kernel in launches of 16 / G queries.  Workspace:
+ * dms_decode_multi_workspace_bytes.  Errors as for dms_decode_attn.
  */
 int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const void *q,
                           int32_t n_query, float *out, float sm_scale, void *workspace,

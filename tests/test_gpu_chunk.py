@@ -115,3 +115,28 @@ def test_single_query_chunk_equals_decode(gpu):
     a = cache.decode(q[:, 300].contiguous().to(gpu))
     m = cache.decode_chunk(q[:, 300:].contiguous().to(gpu))
     assert torch.equal(a, m[:, 0])
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 129])
+def test_long_chunks_tiled_kernel(gpu, chunk):
+    """Chunks of 32 queries or more run the tiled chunk kernel (32 queries per
+    workgroup, cache tiles straight from the pages): ragged query blocks."""
+    worst = _run(gpu, 2, 2, 4, 128, 1000, [chunk], 0.75, 6800 + chunk)
+    say(f"tiled chunk {chunk}: max err {worst:.2e}")
+
+
+def test_long_chunk_after_steps_with_dead_tail(gpu):
+    """A chunk on a cache whose tail holds dead, not yet compacted slots and a
+    clean prefix that is not a whole number of tiles."""
+    _run(gpu, 2, 2, 4, 128, 517, [7, 9, 48], 0.9, 6901)
+
+
+def test_long_chunk_group_five(gpu):
+    """G = 5: the second head group of a workgroup has one active wave."""
+    _run(gpu, 1, 2, 5, 128, 300, [40], 0.7, 7001)
+
+
+def test_prefill_sized_chunk(gpu):
+    """A 512-token chunk into a 2048-token cache (chunked prefill)."""
+    worst = _run(gpu, 1, 2, 4, 128, 2048, [512], 0.875, 7101)
+    say(f"512-token chunk: max err {worst:.2e}")

@@ -365,6 +365,43 @@ def shared_prefix_leg(w, dev, threads: int = 8, steps: int = 24) -> dict:
     }
 
 
+def chunked_prefill_leg(name: str = "prefill_8k", chunk: int = 512, iters: int = 5) -> dict:
+    """Chunked prefill into a cache: the prefill workload's first S - chunk
+    tokens are appended and compacted, then the last `chunk` tokens are
+    appended and attend at once (dms_decode_attn_multi, tiled kernel).  The
+    same rows as the prefill's last `chunk` query rows.  Reported: time of the
+    chunk attention and its rate on the visible (query, key) pairs."""
+    import torch
+
+    import workloads as wl
+    from decode_attention_learned_amd import DmsCache
+
+    w = wl.get(name)
+    dev = torch.device("cuda:0")
+    q, k, v, logit = wl.prefill_inputs(w, device=dev)
+    s_len, d = w.context, w.head_dim
+    head = s_len - chunk
+    cache = DmsCache(w.batch, w.kv_heads, w.group, d, torch.bfloat16,
+                     max_pages_per_unit=(s_len + 63) // 64 + 2, window=w.window, device=dev)
+    cache.append(k[:, :head].contiguous(), v[:, :head].contiguous(), logit[:, :head].contiguous())
+    cache.compact()
+    cache.append(k[:, head:].contiguous(), v[:, head:].contiguous(), logit[:, head:].contiguous())
+    qc = q[:, head:].contiguous()
+    out = torch.empty((w.batch, chunk, w.q_heads, d), dtype=torch.float32, device=dev)
+    ms = _time_calls(lambda: cache.decode_chunk(qc, out=out), iters)
+    if cache.status_word():
+        raise RuntimeError("device status set in the chunked-prefill leg")
+    keep = (logit <= 0).to(torch.int64)
+    csum = torch.cumsum(keep, dim=1)
+    i = torch.arange(head, s_len, device=dev)
+    kept_before = csum[:, i - w.window, :]
+    pairs = (kept_before + w.window).sum().item() * w.group
+    flops = 4.0 * d * pairs
+    return {"chunk": chunk, "context_before": head, "ms": round(ms, 4),
+            "visible_pair_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "tokens_per_s": round(w.batch * chunk / (ms * 1e-3), 1)}
+
+
 def traffic_from_profile(bytes_alg_per_launch: float):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary,
     or None if there is none or the kernel source changed since it was taken."""
@@ -428,6 +465,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="only run the masked-prefill leg")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunk-query leg")
     ap.add_argument("--no-share", action="store_true", help="skip the shared-prefix leg")
+    ap.add_argument("--chunked-prefill-only", action="store_true",
+                    help="only run the chunked-prefill leg")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -447,6 +486,9 @@ def main():
         return
     if args.prefill_only:
         print(json.dumps(prefill_leg()), flush=True)
+        return
+    if args.chunked_prefill_only:
+        print(json.dumps(chunked_prefill_leg()), flush=True)
         return
     dev = torch.device("cuda:0")
     w = wl.get(args.workload)
@@ -580,6 +622,10 @@ def main():
         log(f"[bench] prefill {result['prefill']['ms']:.3f} ms = "
             f"{result['prefill']['roofline']['achieved']:.0f} TFLOP/s causal; gathered "
             f"{result['prefill']['gathered']['ms']:.3f} ms")
+        torch.cuda.empty_cache()
+        result["chunked_prefill"] = chunked_prefill_leg()
+        log(f"[bench] chunked prefill: last {result['chunked_prefill']['chunk']} tokens in "
+            f"{result['chunked_prefill']['ms']:.3f} ms")
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on the host (~{args.cpu_seconds:.0f} s)")

@@ -340,3 +340,22 @@ def test_dead_uncompacted_slot_with_dominant_score_is_excluded(gpu, monkeypatch,
             out = cache.decode(q.to(gpu)).cpu()
             compare_outputs(out, model.decode(q, scale_of(d)), hkv, g, dtype, what=f"t={t}")
     assert np.all(cache.n_slots.cpu().numpy() == n)   # nothing was compacted
+
+
+# ---------------------------------------------------------------- constant values (pin P8)
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, 1e-5), (torch.bfloat16, 2e-2)])
+def test_constant_values_give_the_constant(gpu, dtype, tol):
+    """Every value row of a unit equal to one vector c: whatever the scores and
+    the retained set, the output is c (weights sum to one)."""
+    b, hkv, g, d = 2, 2, 4, 64
+    w = small("llama1b_cr4", batch=b, kv_heads=hkv, group=g, head_dim=d, evict_rate=0.6, seed=2901)
+    rates = wl.unit_eviction_rates(w)
+    k, _, logit = wl.prompt_chunk_inputs(w, 0, 700, rates=rates)
+    c = torch.linspace(-2.0, 2.0, d).to(dtype)
+    v = c.expand(b, 700, hkv, d).contiguous()
+    cache = DmsCache(b, hkv, g, d, dtype, max_pages_per_unit=14, device=gpu)
+    cache.append(k.to(dtype).to(gpu), v.to(gpu), logit.to(gpu))
+    cache.compact()
+    q = torch.randn((b, hkv * g, d), generator=torch.Generator().manual_seed(5)).to(dtype)
+    out = cache.decode(q.to(gpu)).cpu().double()
+    assert torch.max(torch.abs(out - c.double())).item() <= tol

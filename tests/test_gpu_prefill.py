@@ -222,3 +222,17 @@ def test_prefill_relaxed_8k_sampled_rows(gpu):
     worst = _check_relaxed(full, q.cpu(), k.cpu(), v.cpu(), logit.cpu(), noise.cpu(), 1.0, rows, 16,
                            what="relaxed 8k")
     say(f"prefill relaxed 8k: max err {worst:.2e}")
+
+
+@pytest.mark.parametrize("method", METHODS + ["relaxed"])
+def test_prefill_constant_values(gpu, method):
+    """Constant value rows: the output is the constant.  The prefill kernels
+    add the same bf16-rounded weights into the row sums as into the PV
+    product, so the ratio is exact up to float32 rounding (1e-5 relative)."""
+    w, (q, k, v, logit) = _inputs(2, 333, 2, 4, rate=0.8, seed=5951)
+    c = torch.linspace(-3.0, 3.0, 128).to(torch.bfloat16)
+    v = c.expand_as(v).contiguous()
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16, method=method,
+                  temperature=0.5).cpu().double()
+    ref = c.double().expand_as(out)
+    assert torch.max(torch.abs(out - ref) / (1e-3 + ref.abs())).item() <= 1e-5

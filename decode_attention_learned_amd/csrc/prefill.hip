@@ -15,13 +15,20 @@
 // for eviction), into the caller's workspace.  k_prefill then only copies
 // whole fragments into LDS.
 //
-// Work decomposition.  A workgroup of NW = 4 or 8 waves takes 32 (NW / 4)
-// query positions of one KV head: wave w serves query head g = 4*hg + (w % 4)
-// of the group and query positions i0 + 32*(w / 4) .. +32.  Keys are consumed
-// in tiles of 32 from position 0 up to the causal end of the block.  Each key
-// tile is loaded once per workgroup into LDS (four buffers) and serves all
-// four heads.  The build uses NW = 4 with two workgroups per CU (measured
-// faster than NW = 8 with the two-phase offset below).
+// Work decomposition.  A workgroup of four waves takes 32 query positions of
+// one KV head: wave w serves query head g = 4*hg + w of the group.  Keys are
+// consumed in tiles of 32 from position 0 up to the causal end of the block.
+// Each key tile is copied once per workgroup into LDS and serves all four
+// heads.  Three workgroups share a CU (at most 168 VGPRs and 49.5 KB of LDS
+// each), so every SIMD interleaves three waves.
+//
+// Tile ring.  Three LDS buffers, each its own array; tile t lives in buffer
+// t % 3.  The load unit copies a packed tile from global memory straight
+// into LDS (global_load_lds, 16 bytes per lane, no registers involved): the
+// copy of tile k + 1 is issued at the start of iteration k into the buffer
+// of tile k - 2, whose last reader (the PV product of iteration k - 1) every
+// wave has passed at the barrier ending iteration k - 1.  Each wave waits
+// for its own copies before the barrier that ends iteration k.
 //
 // Per tile and wave the two products are the ones of the decode kernel, with
 // query positions in place of heads:
@@ -34,10 +41,9 @@
 //
 // Two phases per tile.  Phase 1 (matrix cores) computes the scores of tile k
 // and the PV product of tile k-1; phase 2 (vector unit) masks, checks and
-// exponentiates the scores of tile k.  With 8 waves, waves 0-3 and waves 4-7
-// share the four SIMDs and run half a tile apart (a workgroup barrier after
-// every phase): while one wave of a SIMD is in phase 1 the other is in phase
-// 2.  With 4 waves the two workgroups of a CU interleave freely.
+// exponentiates the scores of tile k.  The waves of a SIMD come from
+// different workgroups and interleave freely; a wave raises its issue
+// priority during phase 1.
 //
 // Far and near tiles.  A tile whose keys all lie `w` or more positions behind
 // every query of the workgroup ("far") is masked by the decision alone, which
@@ -65,21 +71,15 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 
 constexpr int PD = 128;            // head dimension
 constexpr int PBN = 32;            // keys per tile
-constexpr int PWAVES = 8;          // waves per workgroup
 constexpr int PHPW = 4;            // query heads per workgroup
 constexpr int PKS = PD / 32;       // QK products per 16-key tile
 constexpr int PDT = PD / 16;       // PV products per tile
 constexpr int PFRAG = 64;          // uint4 per operand fragment (64 lanes x 16 bytes)
 constexpr int PK_FRAGS = 2 * PKS;  // key fragments per tile
 constexpr int PV_FRAGS = PDT;      // value fragments per tile
-constexpr int PBUF = 4;            // LDS tile buffers
+constexpr int PBUF = 4;            // LDS tile buffers of the chunk kernel
+constexpr int PNT = 256;           // threads per workgroup of the prefill kernels
 constexpr float kLazy = 8.0f;      // largest exponent (log2 units) before the reference moves
-#ifndef DMS_PREFILL_WAVES
-#define DMS_PREFILL_WAVES 4        // waves per workgroup of the dense kernel (4 or 8)
-#endif
-#ifndef DMS_GATHERED_WAVES
-#define DMS_GATHERED_WAVES 4       // waves per workgroup of the gathered kernel (4 or 8)
-#endif
 
 __device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -114,22 +114,22 @@ struct Softmax {
 };
 
 // QK product of one tile for both query tiles, starting from `init`.
+// The key fragments are read one 16-key half at a time (16 VGPRs).
 __device__ __forceinline__ void qk_tile(const uint4 *__restrict__ sk, const floatx4 (&init)[2],
                                         const uint4 (&qf)[2][PKS], int lane, floatx4 (&s)[2][2]) {
-  uint4 ka[2][PKS];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 2; ++t) {
+    uint4 ka[PKS];
 #pragma unroll
-    for (int ks = 0; ks < PKS; ++ks) ka[t][ks] = sk[(t * PKS + ks) * PFRAG + lane];
+    for (int ks = 0; ks < PKS; ++ks) ka[ks] = sk[(t * PKS + ks) * PFRAG + lane];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int qt = 0; qt < 2; ++qt) {
       floatx4 acc = init[t];
 #pragma unroll
-      for (int ks = 0; ks < PKS; ++ks) acc = mfma(ka[t][ks], qf[qt][ks], acc);
+      for (int ks = 0; ks < PKS; ++ks) acc = mfma(ka[ks], qf[qt][ks], acc);
       s[qt][t] = acc;
     }
+  }
 }
 
 __device__ __forceinline__ float lane_max(const floatx4 (&s)[2]) {
@@ -186,60 +186,85 @@ __device__ __forceinline__ void exponentials(const floatx4 (&s)[2][2], Softmax &
   }
 }
 
-// PV product of one tile: every value fragment is read before the products,
-// so the LDS latency is paid once per tile.
+// PV product of one tile; the value fragments are read four at a time.
 __device__ __forceinline__ void pv_tile(const uint4 *__restrict__ sv, const uint4 (&pb)[2], int lane,
                                         floatx4 (&o)[PDT][2]) {
-  uint4 va[PDT];
 #pragma unroll
-  for (int dt = 0; dt < PDT; ++dt) va[dt] = sv[dt * PFRAG + lane];
+  for (int hh = 0; hh < 2; ++hh) {
+    uint4 va[PDT / 2];
 #pragma unroll
-  for (int dt = 0; dt < PDT; ++dt) {
+    for (int d = 0; d < PDT / 2; ++d) va[d] = sv[(hh * PDT / 2 + d) * PFRAG + lane];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma(va[dt], pb[qt], o[dt][qt]);
+    for (int d = 0; d < PDT / 2; ++d) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        o[hh * PDT / 2 + d][qt] = mfma(va[d], pb[qt], o[hh * PDT / 2 + d][qt]);
+    }
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, PDT, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 2 * PDT, 0);
 }
 
-// Phase 1 of tile k: PV product of tile k - 1 and QK product of tile k (from
-// the additive mask on far tiles, from zero on near ones).  The wave raises
-// its issue priority for the phase, so that the SIMD's other wave (in phase
-// 2) fills the gaps between matrix instructions rather than delaying them.
-__device__ __forceinline__ void phase1(int k, int ntw, int nfar, bool active,
-                                       const uint4 (*sK)[PK_FRAGS * PFRAG],
-                                       const uint4 (*sV)[PV_FRAGS * PFRAG],
-                                       const floatx4 (*sB)[PBN / 4], const uint4 (&qf)[2][PKS],
-                                       floatx4 (&s)[2][2], const uint4 (&pb)[2],
-                                       floatx4 (&o)[PDT][2], int lane, int quad) {
-  if (!active) return;
+// ---- tile ring -----------------------------------------------------------
+// Copy one 16 KB packed tile into LDS with the load unit: wave w copies
+// uint4 256 r + 64 w + lane (r = 0..3), one contiguous 1 KB run per copy.
+__device__ __forceinline__ void ring_copy(const uint4 *__restrict__ src, uint4 *dst, int tid,
+                                          int wave) {
+#pragma unroll
+  for (int r = 0; r < PTILE_U4 / PNT; ++r)
+    __builtin_amdgcn_global_load_lds(src + r * PNT + tid, dst + r * PNT + wave * kWave, 16, 0, 0);
+}
+
+// Copy 128 bytes of per-key data (a mask or positions) with lanes 0..7 of wave 0.
+template <typename T>
+__device__ __forceinline__ void ring_copy_keys(const T *__restrict__ src, T *dst, int tid) {
+  static_assert(sizeof(T) == 16, "16-byte elements");
+  if (tid < PBN / 4) __builtin_amdgcn_global_load_lds(src + tid, dst, 16, 0, 0);
+}
+
+// End of an iteration: this wave's copies have landed, then the workgroup
+// barrier.  The signal fences keep the compiler from moving LDS accesses
+// across the barrier without making the hardware drain the LDS queue.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), no wait on the other counters
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Phase 1 of tile k: PV product of tile k - 1 (values `sv`) and QK product of
+// tile k (keys `sk`; from the additive mask `sb` on far tiles, from zero on
+// near ones).  The wave raises its issue priority for the phase, so that the
+// SIMD's other waves (in phase 2) fill the gaps between matrix instructions
+// rather than delaying them.
+__device__ __forceinline__ void phase1(int k, int ntw, int nfar, const uint4 *__restrict__ sk,
+                                       const uint4 *__restrict__ sv, const floatx4 *__restrict__ sb,
+                                       const uint4 (&qf)[2][PKS], floatx4 (&s)[2][2],
+                                       const uint4 (&pb)[2], floatx4 (&o)[PDT][2], int lane,
+                                       int quad) {
   __builtin_amdgcn_s_setprio(2);
-  if (k >= 1 && k - 1 < ntw) pv_tile(sV[(k - 1) % PBUF], pb, lane, o);
+  if (k >= 1 && k - 1 < ntw) pv_tile(sv, pb, lane, o);
   if (k < ntw) {
-    const int buf = k % PBUF;
     floatx4 init[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
     if (k < nfar) {
-      init[0] = sB[buf][2 * quad];
-      init[1] = sB[buf][2 * quad + 1];
+      init[0] = sb[2 * quad];
+      init[1] = sb[2 * quad + 1];
     }
-    qk_tile(sK[buf], init, qf, lane, s);
+    qk_tile(sk, init, qf, lane, s);
   }
   __builtin_amdgcn_s_setprio(0);
 }
 
 // Phase 2 of tile k: the full rule on near tiles, the reference check, and
 // the exponentials.
-__device__ __forceinline__ void phase2(int k, int ntw, int nfar, bool active, int S, int window,
-                                       int qi0, int col, int quad, const floatx4 (*sB)[PBN / 4],
+__device__ __forceinline__ void phase2(int k, int ntw, int nfar, int S, int window, int qi0,
+                                       int col, int quad, const floatx4 *__restrict__ sb,
                                        floatx4 (&s)[2][2], Softmax &sm, floatx4 (&o)[PDT][2],
                                        uint4 (&pb)[2], float c) {
-  if (!active || k < 0 || k >= ntw) return;
+  if (k >= ntw) return;
   if (k >= nfar) {
     // near tile: causal bound, and the key's additive mask once it is w or
     // more behind the query (0 / -inf for the hard rule)
     const int j0 = k * PBN;
-    const int buf = k % PBUF;
-    const floatx4 mb[2] = {sB[buf][2 * quad], sB[buf][2 * quad + 1]};
+    const floatx4 mb[2] = {sb[2 * quad], sb[2 * quad + 1]};
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const int i = qi0 + 16 * qt + col;
@@ -261,30 +286,28 @@ __device__ __forceinline__ void phase2(int k, int ntw, int nfar, bool active, in
 // every query of the workgroup sees, gathered tiles on the edge (a key is seen
 // by query i iff its position <= i - w), and dense band tiles (key j is seen
 // iff i - w < j <= i).
-__device__ __forceinline__ void g_phase1(int k, int nT, bool active,
-                                         const uint4 (*sK)[PK_FRAGS * PFRAG],
-                                         const uint4 (*sV)[PV_FRAGS * PFRAG],
-                                         const uint4 (&qf)[2][PKS], floatx4 (&s)[2][2],
-                                         const uint4 (&pb)[2], floatx4 (&o)[PDT][2], int lane) {
-  if (!active) return;
+__device__ __forceinline__ void g_phase1(int k, int nT, const uint4 *__restrict__ sk,
+                                         const uint4 *__restrict__ sv, const uint4 (&qf)[2][PKS],
+                                         floatx4 (&s)[2][2], const uint4 (&pb)[2],
+                                         floatx4 (&o)[PDT][2], int lane) {
   __builtin_amdgcn_s_setprio(2);
-  if (k >= 1 && k - 1 < nT) pv_tile(sV[(k - 1) % PBUF], pb, lane, o);
+  if (k >= 1 && k - 1 < nT) pv_tile(sv, pb, lane, o);
   if (k < nT) {
     const floatx4 zero[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-    qk_tile(sK[k % PBUF], zero, qf, lane, s);
+    qk_tile(sk, zero, qf, lane, s);
   }
   __builtin_amdgcn_s_setprio(0);
 }
 
-__device__ __forceinline__ void g_phase2(int k, int nT, int nclean, int ngt, int band_j0,
-                                         bool active, int S, int window, int qi0, int col,
-                                         int quad, const int4 (*sP)[PBN / 4], floatx4 (&s)[2][2],
+__device__ __forceinline__ void g_phase2(int k, int nT, int nclean, int ngt, int band_j0, int S,
+                                         int window, int qi0, int col, int quad,
+                                         const int4 *__restrict__ sp, floatx4 (&s)[2][2],
                                          Softmax &sm, floatx4 (&o)[PDT][2], uint4 (&pb)[2],
                                          float c) {
-  if (!active || k < 0 || k >= nT) return;
+  if (k >= nT) return;
   if (k >= nclean) {
     if (k < ngt) {  // gathered edge tile: position <= i - w
-      const int4 p0 = sP[k % PBUF][2 * quad], p1 = sP[k % PBUF][2 * quad + 1];
+      const int4 p0 = sp[2 * quad], p1 = sp[2 * quad + 1];
       const int pos[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
@@ -407,8 +430,7 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
   vdst[t] = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64, 2) void k_prefill(
+__global__ __launch_bounds__(PNT, 3) void k_prefill(
     int batch, int S, int hkv, int G, int window, float scale_log2, const uint16_t *__restrict__ q,
     const uint4 *__restrict__ packed, const floatx4 *__restrict__ mask, float *__restrict__ out) {
   const int tid = threadIdx.x;
@@ -417,9 +439,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_prefill(
   const int col = lane & 15, quad = lane >> 4;
   const int Hq = hkv * G;
   const int ngh = (G + PHPW - 1) / PHPW;
-  constexpr int GBM = 32 * (NW / PHPW);  // query positions per workgroup
-  constexpr int NT = NW * 64;
-  const int nqb = (S + GBM - 1) / GBM;
+  const int nqb = (S + PBN - 1) / PBN;  // 32 query positions per workgroup
 
   // Workgroup -> (b, h, hg, query block).  Consecutive ids go to different
   // XCDs (round-robin), so all query blocks of one (b, h, hg) are given ids of
@@ -437,19 +457,15 @@ __global__ __launch_bounds__(NW * 64, 2) void k_prefill(
   const int h = (pair / ngh) % hkv;
   const int hg = pair % ngh;
 
-  const int g = hg * PHPW + (wave % PHPW);
+  const int g = hg * PHPW + wave;
   const bool active = g < G;
   const int hq = h * G + (active ? g : 0);
-  const int qi0 = qb * GBM + (wave / PHPW) * 32;  // this wave's first query position
-  const int i_end = min(S, qb * GBM + GBM);       // workgroup's causal key end
+  const int qi0 = qb * PBN;                 // first query position of the workgroup
+  const int i_end = min(S, qi0 + PBN);      // causal key end
   const int ntiles = (i_end + PBN - 1) / PBN;
-  // far tiles: j0 + 31 + window <= qb * GBM, i.e. behind every query by >= window
-  const int far_x = qb * GBM - window - (PBN - 1);
+  // far tiles: j0 + 31 + window <= qi0, i.e. behind every query by >= window
+  const int far_x = qi0 - window - (PBN - 1);
   const int nfar = far_x >= 0 ? min(ntiles, far_x / PBN + 1) : 0;
-
-  __shared__ uint4 sK[PBUF][PK_FRAGS * PFRAG];
-  __shared__ uint4 sV[PBUF][PV_FRAGS * PFRAG];
-  __shared__ floatx4 sB[PBUF][PBN / 4];
 
   // Q^T operand for two query tiles: query qi0 + 16*qt + col, dims ks*32 + quad*8
   uint4 qf[2][PKS];
@@ -484,72 +500,37 @@ __global__ __launch_bounds__(NW * 64, 2) void k_prefill(
   const uint4 *pk = packed + tile_index(b, h, 0, hkv, ntiles_all) * PTILE_U4;
   const floatx4 *pm = mask + tile_index(b, h, 0, hkv, ntiles_all) * (PBN / 4);
 
-  // Tile t lives in buffer t % 4.  Every wave runs the same loop, phase 1
-  // and phase 2 of tile k with a barrier after each; waves 4-7 pass one
-  // barrier more before the loop and waves 0-3 one more after it, so that
-  // between barriers m-1 and m (window m)
-  //   waves 0-3 run phase 1 of tile k in window 2k+1 and phase 2 in 2k+2,
-  //   waves 4-7 run phase 1 of tile k in window 2k+2 and phase 2 in 2k+3.
-  // Buffer t % 4 is read in windows 2t+1 .. 2t+4 (keys and mask of tile t in
-  // its phase 1 and 2, values in phase 1 of tile t+1).  After phase 2 of tile
-  // k each thread stores its share of tile k+2 (windows 2k+2 and 2k+3, after
-  // the last read of tile k-2 in window 2k) and loads its share of tile k+3.
-  // Thread t copies uint4 t and t + 512 of the 16 KB packed tile; threads
-  // 0..7 copy the mask.
-  static_assert(NT == 256 || NT == 512, "four or eight waves");
-  uint4 tr0, tr1, tr2, tr3;
-  floatx4 tm;
-#define DMS_PF_GLOAD(tile)                                         \
-  do {                                                             \
-    const uint4 *src_ = pk + size_t(tile) * PTILE_U4;              \
-    tr0 = src_[tid];                                               \
-    tr1 = src_[tid + NT];                                          \
-    if constexpr (NT == 256) {                                     \
-      tr2 = src_[tid + 2 * NT];                                    \
-      tr3 = src_[tid + 3 * NT];                                    \
-    }                                                              \
-    if (tid < PBN / 4) tm = pm[size_t(tile) * (PBN / 4) + tid];    \
-  } while (0)
-#define DMS_PF_LSTORE(buf)                    \
-  do {                                        \
-    if constexpr (NT == 256) {                \
-      sK[buf][tid] = tr0;                     \
-      sK[buf][tid + NT] = tr1;                \
-      sV[buf][tid] = tr2;                     \
-      sV[buf][tid + NT] = tr3;                \
-    } else {                                  \
-      sK[buf][tid] = tr0;                     \
-      sV[buf][tid] = tr1;                     \
-    }                                         \
-    if (tid < PBN / 4) sB[buf][tid] = tm;     \
-  } while (0)
-  DMS_PF_GLOAD(0);
-  DMS_PF_LSTORE(0);
-  if (ntiles > 1) {
-    DMS_PF_GLOAD(1);
-    DMS_PF_LSTORE(1);
-  }
-  if (ntiles > 2) DMS_PF_GLOAD(2);
-  __syncthreads();
+  // the tile ring: packed tile and mask of tile t in buffer t % 3
+  __shared__ uint4 sT0[PTILE_U4], sT1[PTILE_U4], sT2[PTILE_U4];
+  __shared__ floatx4 sM0[PBN / 4], sM1[PBN / 4], sM2[PBN / 4];
+  auto copy = [&](int tile, uint4 *dt, floatx4 *dm) {
+    ring_copy(pk + size_t(tile) * PTILE_U4, dt, tid, wave);
+    ring_copy_keys(pm + size_t(tile) * (PBN / 4), dm, tid);
+  };
+  copy(0, sT0, sM0);
+  ring_barrier();
 
-  // tiles this wave needs: keys up to its last query position
-  const int ntw = min(ntiles, (qi0 + 31) / PBN + 1);
-  const bool lead = NW == 4 || wave < NW / 2;
+  const int ntw = ntiles;  // every wave needs every tile of the block
   floatx4 s[2][2];
   uint4 pb[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-
-  if (!lead) __syncthreads();
-  for (int k = 0; k <= ntiles; ++k) {
-    phase1(k, ntw, nfar, active, sK, sV, sB, qf, s, pb, o, lane, quad);
-    if (NW == 8) __syncthreads();
-    phase2(k, ntw, nfar, active, S, window, qi0, col, quad, sB, s, sm, o, pb, c);
-    if (k + 2 < ntiles) DMS_PF_LSTORE((k + 2) % PBUF);
-    if (k + 3 < ntiles) DMS_PF_GLOAD(k + 3);
-    __syncthreads();
+  // iteration k: keys and mask of tile k in (t, m), values of tile k - 1 in
+  // tp; the copy of tile k + 1 goes to (tn, mn)
+  auto iteration = [&](int k, const uint4 *t, const floatx4 *m, const uint4 *tp, uint4 *tn,
+                       floatx4 *mn) {
+    if (k + 1 < ntiles) copy(k + 1, tn, mn);
+    if (active) {
+      phase1(k, ntw, nfar, t, tp + PK_FRAGS * PFRAG, m, qf, s, pb, o, lane, quad);
+      phase2(k, ntw, nfar, S, window, qi0, col, quad, m, s, sm, o, pb, c);
+    }
+    ring_barrier();
+  };
+  for (int k = 0; k <= ntiles; k += 3) {
+    iteration(k, sT0, sM0, sT2, sT1, sM1);
+    if (k + 1 > ntiles) break;
+    iteration(k + 1, sT1, sM1, sT0, sT2, sM2);
+    if (k + 2 > ntiles) break;
+    iteration(k + 2, sT2, sM2, sT1, sT0, sM0);
   }
-  if (NW == 8 && lead) __syncthreads();
-#undef DMS_PF_LSTORE
-#undef DMS_PF_GLOAD
 
   if (!active) return;
 #pragma unroll
@@ -675,8 +656,7 @@ __device__ __forceinline__ int kept_upto(int x, int S, int ntiles, const int32_t
 // gathered-key prefill, step 3: attention over [gathered tiles | band tiles]
 // with the two-phase schedule of k_prefill.
 // ---------------------------------------------------------------------------
-template <int NW>
-__global__ __launch_bounds__(NW * 64, 2) void k_prefill_gathered(
+__global__ __launch_bounds__(PNT, 3) void k_prefill_gathered(
     int batch, int S, int hkv, int G, int window, float scale_log2, const uint16_t *__restrict__ q,
     const uint4 *__restrict__ dense, const uint4 *__restrict__ gathered,
     const int4 *__restrict__ gposp, const int32_t *__restrict__ tile_cnt,
@@ -687,9 +667,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_prefill_gathered(
   const int col = lane & 15, quad = lane >> 4;
   const int Hq = hkv * G;
   const int ngh = (G + PHPW - 1) / PHPW;
-  constexpr int GBM = 32 * (NW / PHPW);  // query positions per workgroup
-  constexpr int NT = NW * 64;
-  const int nqb = (S + GBM - 1) / GBM;
+  const int nqb = (S + PBN - 1) / PBN;  // 32 query positions per workgroup
 
   const int nbh = batch * hkv * ngh;
   const int id = blockIdx.x;
@@ -704,12 +682,12 @@ __global__ __launch_bounds__(NW * 64, 2) void k_prefill_gathered(
   const int hg = pair % ngh;
   const int u = b * hkv + h;
 
-  const int g = hg * PHPW + (wave % PHPW);
+  const int g = hg * PHPW + wave;
   const bool active = g < G;
   const int hq = h * G + (active ? g : 0);
-  const int qi0 = qb * GBM + (wave / PHPW) * 32;
-  const int q0 = qb * GBM;
-  const int i_max = min(S, q0 + GBM) - 1;  // last query position of the workgroup
+  const int qi0 = qb * PBN;
+  const int q0 = qi0;
+  const int i_max = min(S, q0 + PBN) - 1;  // last query position of the workgroup
 
   // tile list: gathered tiles [0, ngt) (the first nclean seen by every query),
   // then dense tiles covering the band (q0 - w, i_max]
@@ -723,10 +701,6 @@ __global__ __launch_bounds__(NW * 64, 2) void k_prefill_gathered(
   const int tb0 = max(0, q0 - window + 1) / PBN;
   const int nT = ngt + i_max / PBN - tb0 + 1;
   const int band_j0 = tb0 * PBN;
-
-  __shared__ uint4 sK[PBUF][PK_FRAGS * PFRAG];
-  __shared__ uint4 sV[PBUF][PV_FRAGS * PFRAG];
-  __shared__ int4 sP[PBUF][PBN / 4];
 
   uint4 qf[2][PKS];
 #pragma unroll
@@ -755,68 +729,40 @@ __global__ __launch_bounds__(NW * 64, 2) void k_prefill_gathered(
   }
   const float c = scale_log2;
 
-  // Same four-buffer pipeline as k_prefill; tile t comes from the gathered
-  // layout (t < ngt, with its key positions) or the dense one.
+  // The tile ring of k_prefill; tile t comes from the gathered layout (t <
+  // ngt, with its key positions) or the dense one.
   const size_t ubase = size_t(u) * ntiles_all;
-  // thread t copies uint4 t + NT r of the 16 KB packed tile (r < 1024 / NT);
-  // threads 0..7 copy the key positions of a gathered tile
-  static_assert(NT == 256 || NT == 512, "four or eight waves");
-  uint4 tr0, tr1, tr2, tr3;
-  int4 tp;
-#define DMS_PG_GLOAD(t)                                                                   \
-  do {                                                                                    \
-    const bool gath_ = (t) < ngt;                                                         \
-    const uint4 *src_ = gath_ ? gathered + (ubase + (t)) * PTILE_U4                       \
-                              : dense + (ubase + tb0 + (t) - ngt) * PTILE_U4;             \
-    tr0 = src_[tid];                                                                      \
-    tr1 = src_[tid + NT];                                                                 \
-    if constexpr (NT == 256) {                                                            \
-      tr2 = src_[tid + 2 * NT];                                                           \
-      tr3 = src_[tid + 3 * NT];                                                           \
-    }                                                                                     \
-    if (tid < PBN / 4 && gath_) tp = gposp[(ubase + (t)) * (PBN / 4) + tid];              \
-  } while (0)
-#define DMS_PG_LSTORE(t)                                      \
-  do {                                                        \
-    if constexpr (NT == 256) {                                \
-      sK[(t) % PBUF][tid] = tr0;                              \
-      sK[(t) % PBUF][tid + NT] = tr1;                         \
-      sV[(t) % PBUF][tid] = tr2;                              \
-      sV[(t) % PBUF][tid + NT] = tr3;                         \
-    } else {                                                  \
-      sK[(t) % PBUF][tid] = tr0;                              \
-      sV[(t) % PBUF][tid] = tr1;                              \
-    }                                                         \
-    if (tid < PBN / 4 && (t) < ngt) sP[(t) % PBUF][tid] = tp; \
-  } while (0)
-  DMS_PG_GLOAD(0);
-  DMS_PG_LSTORE(0);
-  if (nT > 1) {
-    DMS_PG_GLOAD(1);
-    DMS_PG_LSTORE(1);
-  }
-  if (nT > 2) DMS_PG_GLOAD(2);
-  __syncthreads();
+  __shared__ uint4 sT0[PTILE_U4], sT1[PTILE_U4], sT2[PTILE_U4];
+  __shared__ int4 sP0[PBN / 4], sP1[PBN / 4], sP2[PBN / 4];
+  auto copy = [&](int t, uint4 *dt, int4 *dp) {
+    if (t < ngt) {
+      ring_copy(gathered + (ubase + t) * PTILE_U4, dt, tid, wave);
+      ring_copy_keys(gposp + (ubase + t) * (PBN / 4), dp, tid);
+    } else {
+      ring_copy(dense + (ubase + tb0 + t - ngt) * PTILE_U4, dt, tid, wave);
+    }
+  };
+  copy(0, sT0, sP0);
+  ring_barrier();
 
-  // With 8 waves, the two-phase schedule of k_prefill (waves 4-7 half a tile
-  // behind).  With 4 waves, two workgroups share a CU and one barrier per
-  // tile suffices (phase 1 of tile k+1 reads buffers that the stores of step
-  // k do not touch).
-  const bool lead = NW == 4 || wave < NW / 2;
   floatx4 s[2][2];
   uint4 pb[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-  if (!lead) __syncthreads();
-  for (int k = 0; k <= nT; ++k) {
-    g_phase1(k, nT, active, sK, sV, qf, s, pb, o, lane);
-    if (NW == 8) __syncthreads();
-    g_phase2(k, nT, nclean, ngt, band_j0, active, S, window, qi0, col, quad, sP, s, sm, o, pb, c);
-    if (k + 2 < nT) DMS_PG_LSTORE(k + 2);
-    if (k + 3 < nT) DMS_PG_GLOAD(k + 3);
-    __syncthreads();
+  auto iteration = [&](int k, const uint4 *t, const int4 *p, const uint4 *tp, uint4 *tn,
+                       int4 *pn) {
+    if (k + 1 < nT) copy(k + 1, tn, pn);
+    if (active) {
+      g_phase1(k, nT, t, tp + PK_FRAGS * PFRAG, qf, s, pb, o, lane);
+      g_phase2(k, nT, nclean, ngt, band_j0, S, window, qi0, col, quad, p, s, sm, o, pb, c);
+    }
+    ring_barrier();
+  };
+  for (int k = 0; k <= nT; k += 3) {
+    iteration(k, sT0, sP0, sT2, sT1, sP1);
+    if (k + 1 > nT) break;
+    iteration(k + 1, sT1, sP1, sT0, sT2, sP2);
+    if (k + 2 > nT) break;
+    iteration(k + 2, sT2, sP2, sT1, sT0, sP0);
   }
-  if (NW == 8 && lead) __syncthreads();
-#undef DMS_PG_LSTORE
-#undef DMS_PG_GLOAD
 
   if (!active) return;
 #pragma unroll
@@ -850,14 +796,13 @@ hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, cons
                      relaxed ? 1.f / temperature : 0.f, 1.f / sm_scale, relaxed, packed, mask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int NW = DMS_PREFILL_WAVES;
   const int ngh = (s.group + PHPW - 1) / PHPW;
   const int nbh = s.batch * s.kv_heads * ngh;
-  const int nqb = (seq_len + 32 * (NW / PHPW) - 1) / (32 * (NW / PHPW));
+  const int nqb = (seq_len + PBN - 1) / PBN;
   const int per_xcd_pairs = (nbh + 7) / 8;
   const long blocks = long(per_xcd_pairs) * nqb * 8;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_prefill<NW>, dim3(unsigned(blocks)), dim3(NW * 64), 0, st, s.batch, seq_len,
+  hipLaunchKernelGGL(k_prefill, dim3(unsigned(blocks)), dim3(PNT), 0, st, s.batch, seq_len,
                      s.kv_heads, s.group, s.window, sm_scale * 1.4426950408889634f,
                      static_cast<const uint16_t *>(q), packed,
                      reinterpret_cast<const floatx4 *>(mask), out);
@@ -890,13 +835,12 @@ hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void
   hipLaunchKernelGGL(k_sparse_pack, dim3(ntiles, s.kv_heads, s.batch), dim3(512), 0, st, seq_len,
                      s.kv_heads, ntiles, k16, v16, gpos, tile_cnt, gathered, gposp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  constexpr int NW = DMS_GATHERED_WAVES;
   const int ngh = (s.group + PHPW - 1) / PHPW;
   const int nbh = s.batch * s.kv_heads * ngh;
-  const int nqb = (seq_len + 32 * (NW / PHPW) - 1) / (32 * (NW / PHPW));
+  const int nqb = (seq_len + PBN - 1) / PBN;
   const long blocks = long((nbh + 7) / 8) * nqb * 8;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_prefill_gathered<NW>, dim3(unsigned(blocks)), dim3(NW * 64), 0, st, s.batch,
+  hipLaunchKernelGGL(k_prefill_gathered, dim3(unsigned(blocks)), dim3(PNT), 0, st, s.batch,
                      seq_len, s.kv_heads, s.group, s.window, sm_scale * 1.4426950408889634f,
                      static_cast<const uint16_t *>(q), dense, gathered,
                      reinterpret_cast<const int4 *>(gposp), tile_cnt, keptw, out);

@@ -77,7 +77,6 @@ constexpr int PDT = PD / 16;       // PV products per tile
 constexpr int PFRAG = 64;          // uint4 per operand fragment (64 lanes x 16 bytes)
 constexpr int PK_FRAGS = 2 * PKS;  // key fragments per tile
 constexpr int PV_FRAGS = PDT;      // value fragments per tile
-constexpr int PBUF = 4;            // LDS tile buffers of the chunk kernel
 constexpr int PNT = 256;           // threads per workgroup of the prefill kernels
 constexpr float kLazy = 8.0f;      // largest exponent (log2 units) before the reference moves
 
@@ -204,12 +203,15 @@ __device__ __forceinline__ void pv_tile(const uint4 *__restrict__ sv, const uint
 }
 
 // ---- tile ring -----------------------------------------------------------
-// Copy one 16 KB packed tile into LDS with the load unit: wave w copies
-// uint4 256 r + 64 w + lane (r = 0..3), one contiguous 1 KB run per copy.
+// Copy N uint4 (a 16 KB packed tile, or half of one) into LDS with the load
+// unit: wave w copies uint4 256 r + 64 w + lane, one contiguous 1 KB run per
+// copy instruction.
+template <int N = PTILE_U4>
 __device__ __forceinline__ void ring_copy(const uint4 *__restrict__ src, uint4 *dst, int tid,
                                           int wave) {
+  static_assert(N % PNT == 0, "whole runs");
 #pragma unroll
-  for (int r = 0; r < PTILE_U4 / PNT; ++r)
+  for (int r = 0; r < N / PNT; ++r)
     __builtin_amdgcn_global_load_lds(src + r * PNT + tid, dst + r * PNT + wave * kWave, 16, 0, 0);
 }
 
@@ -338,17 +340,17 @@ __device__ __forceinline__ void g_phase2(int k, int nT, int nclean, int ngt, int
 // Phase 2 of cache tile k for chunk queries: slots below n_clean are seen by
 // every query; above it, slot j is seen by query position t iff it is in use,
 // pos_j <= t, and it is unmarked or t - pos_j < w.
-__device__ __forceinline__ void c_phase2(int k, int nt, int nclean_t, bool active, int ns, int nc,
-                                         int window, int t_first, int col, int quad,
-                                         const int4 (*sPos)[PBN / 4], const uint2 (*sAl)[PBN / 8],
-                                         floatx4 (&s)[2][2], Softmax &sm, floatx4 (&o)[PDT][2],
-                                         uint4 (&pb)[2], float c) {
-  if (!active || k >= nt) return;
+__device__ __forceinline__ void c_phase2(int k, int nt, int nclean_t, int ns, int nc, int window,
+                                         int t_first, int col, int quad,
+                                         const int4 *__restrict__ sp,
+                                         const uint2 *__restrict__ sa, floatx4 (&s)[2][2],
+                                         Softmax &sm, floatx4 (&o)[PDT][2], uint4 (&pb)[2],
+                                         float c) {
+  if (k >= nt) return;
   if (k >= nclean_t) {
-    const int buf = k % PBUF;
-    const int4 p0 = sPos[buf][2 * quad], p1 = sPos[buf][2 * quad + 1];
+    const int4 p0 = sp[2 * quad], p1 = sp[2 * quad + 1];
     const int pos[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    const uint2 a8 = sAl[buf][quad];
+    const uint2 a8 = sa[quad];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const int t = t_first + 16 * qt + col;
@@ -856,13 +858,12 @@ hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void
 // no pack pass.  Workgroup: one unit, 32 chunk queries, four query heads (one
 // per wave); grid (ceil(C / 32), units * ceil(G / 4)).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void k_chunk_attn(
+__global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
     int hkv, int G, int window, int maxp, int C, float scale_log2, const uint16_t *__restrict__ q,
     const uint4 *__restrict__ k_pages, const uint4 *__restrict__ v_pages,
     const int32_t *__restrict__ page_table, const int4 *__restrict__ slot_pos,
     const uint4 *__restrict__ slot_alpha, const int32_t *__restrict__ n_slots,
     const int32_t *__restrict__ n_clean, const int32_t *__restrict__ seq_len, float *__restrict__ out) {
-  constexpr int NT = 256;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
@@ -880,11 +881,6 @@ __global__ __launch_bounds__(256, 2) void k_chunk_attn(
   const int nt = (ns + PBN - 1) / PBN;
   const int nclean_t = nc / PBN;                  // tiles wholly below n_clean
   const int32_t *row = page_table + size_t(u) * maxp;
-
-  __shared__ uint4 sK[PBUF][PK_FRAGS * PFRAG];
-  __shared__ uint4 sV[PBUF][PV_FRAGS * PFRAG];
-  __shared__ int4 sPos[PBUF][PBN / 4];
-  __shared__ uint2 sAl[PBUF][PBN / 8];
 
   uint4 qf[2][PKS];
 #pragma unroll
@@ -913,61 +909,46 @@ __global__ __launch_bounds__(256, 2) void k_chunk_attn(
   }
   const float c = scale_log2;
 
-  // tile t = slots 32 t .. 32 t + 31: page row[t / 2], group t % 2 of the
-  // page; thread t copies uint4 tid and tid + 256 of its keys and of its
-  // values, threads 0..7 the positions, threads 8..9 the decisions
-  uint4 tk0, tk1, tv0, tv1, tx;
-#define DMS_PC_GLOAD(t)                                                                   \
-  do {                                                                                    \
-    const size_t grp_ = size_t(row[(t) >> 1]) * 2 + ((t) & 1);                            \
-    const uint4 *ks_ = k_pages + grp_ * (PK_FRAGS * PFRAG);                               \
-    const uint4 *vs_ = v_pages + grp_ * (PV_FRAGS * PFRAG);                               \
-    tk0 = ks_[tid];                                                                       \
-    tk1 = ks_[tid + NT];                                                                  \
-    tv0 = vs_[tid];                                                                       \
-    tv1 = vs_[tid + NT];                                                                  \
-    if (tid < 8) tx = __builtin_bit_cast(uint4, slot_pos[grp_ * 8 + tid]);                \
-    else if (tid < 10) tx = slot_alpha[grp_ * 2 + tid - 8];                               \
-  } while (0)
-#define DMS_PC_LSTORE(t)                                                                  \
-  do {                                                                                    \
-    const int b_ = (t) % PBUF;                                                            \
-    sK[b_][tid] = tk0;                                                                    \
-    sK[b_][tid + NT] = tk1;                                                               \
-    sV[b_][tid] = tv0;                                                                    \
-    sV[b_][tid + NT] = tv1;                                                               \
-    if (tid < 8) sPos[b_][tid] = __builtin_bit_cast(int4, tx);                            \
-    else if (tid < 10) {                                                                  \
-      sAl[b_][2 * (tid - 8)] = make_uint2(tx.x, tx.y);                                    \
-      sAl[b_][2 * (tid - 8) + 1] = make_uint2(tx.z, tx.w);                                \
-    }                                                                                     \
-  } while (0)
-  if (nt > 0) {
-    DMS_PC_GLOAD(0);
-    DMS_PC_LSTORE(0);
-  }
-  if (nt > 1) {
-    DMS_PC_GLOAD(1);
-    DMS_PC_LSTORE(1);
-  }
-  if (nt > 2) DMS_PC_GLOAD(2);
-  __syncthreads();
+  // The tile ring of k_prefill.  Tile t = slots 32 t .. 32 t + 31: page
+  // row[t / 2], group t % 2 of the page; its keys and values (8 KB each) go
+  // to the first and second half of a buffer, its positions (128 bytes, lanes
+  // 0..7 of wave 0) and decisions (32 bytes, lanes 0..1 of wave 1) beside.
+  __shared__ uint4 sT0[PTILE_U4], sT1[PTILE_U4], sT2[PTILE_U4];
+  __shared__ int4 sP0[PBN / 4], sP1[PBN / 4], sP2[PBN / 4];
+  __shared__ uint4 sA0[PBN / 16], sA1[PBN / 16], sA2[PBN / 16];
+  auto copy = [&](int t, uint4 *dt, int4 *dp, uint4 *da) {
+    const size_t grp = size_t(row[t >> 1]) * 2 + (t & 1);
+    ring_copy<PK_FRAGS * PFRAG>(k_pages + grp * (PK_FRAGS * PFRAG), dt, tid, wave);
+    ring_copy<PV_FRAGS * PFRAG>(v_pages + grp * (PV_FRAGS * PFRAG), dt + PK_FRAGS * PFRAG, tid,
+                                wave);
+    ring_copy_keys(slot_pos + grp * (PBN / 4), dp, tid);
+    if (wave == 1 && lane < PBN / 16)
+      __builtin_amdgcn_global_load_lds(slot_alpha + grp * (PBN / 16) + lane, da, 16, 0, 0);
+  };
+  if (nt > 0) copy(0, sT0, sP0, sA0);
+  ring_barrier();
 
   floatx4 s[2][2];
   uint4 pb[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
   const floatx4 zero[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-  for (int k = 0; k <= nt; ++k) {
+  auto iteration = [&](int k, const uint4 *t, const int4 *p, const uint4 *a, const uint4 *tp,
+                       uint4 *tn, int4 *pn, uint4 *an) {
+    if (k + 1 < nt) copy(k + 1, tn, pn, an);
     if (active) {
-      if (k >= 1) pv_tile(sV[(k - 1) % PBUF], pb, lane, o);
-      if (k < nt) qk_tile(sK[k % PBUF], zero, qf, lane, s);
+      if (k >= 1) pv_tile(tp + PK_FRAGS * PFRAG, pb, lane, o);
+      if (k < nt) qk_tile(t, zero, qf, lane, s);
+      c_phase2(k, nt, nclean_t, ns, nc, window, t_first, col, quad, p,
+               reinterpret_cast<const uint2 *>(a), s, sm, o, pb, c);
     }
-    c_phase2(k, nt, nclean_t, active, ns, nc, window, t_first, col, quad, sPos, sAl, s, sm, o, pb, c);
-    if (k + 2 < nt) DMS_PC_LSTORE(k + 2);
-    if (k + 3 < nt) DMS_PC_GLOAD(k + 3);
-    __syncthreads();
+    ring_barrier();
+  };
+  for (int k = 0; k <= nt; k += 3) {
+    iteration(k, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
+    if (k + 1 > nt) break;
+    iteration(k + 1, sT1, sP1, sA1, sT0, sT2, sP2, sA2);
+    if (k + 2 > nt) break;
+    iteration(k + 2, sT2, sP2, sA2, sT1, sT0, sP0, sA0);
   }
-#undef DMS_PC_LSTORE
-#undef DMS_PC_GLOAD
 
   if (!active) return;
 #pragma unroll

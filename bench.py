@@ -427,9 +427,12 @@ def calibrate(gib: float) -> dict:
     n = int(gib * (1 << 30)) // 2
     a = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").normal_()
     b = torch.empty_like(a)
+    # the read: a sum over the same bytes viewed as fp32 (every value finite:
+    # its high half is a finite bf16), which torch reduces with wide loads
+    a32 = a.view(torch.float32)
     for _ in range(2):
         b.copy_(a)
-        a.sum(dtype=torch.float32)
+        a32.sum()
     torch.cuda.synchronize()
     reps = 5
     e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
@@ -438,7 +441,7 @@ def calibrate(gib: float) -> dict:
         b.copy_(a)
     e1.record()
     for _ in range(reps):
-        a.sum(dtype=torch.float32)
+        a32.sum()
     e2.record()
     torch.cuda.synchronize()
     nbytes = 2 * n

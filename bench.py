@@ -607,13 +607,12 @@ def main():
     }
     log(f"[bench] {tokens_s:.0f} tok/s, {ms_step * 1e3:.1f} us/step, decode {dec_ms * 1e3:.1f} us "
         f"= {kv_gbps:.0f} GB/s ({100 * kv_gbps / HBM_PEAK_GBPS:.1f}% of HBM peak)")
-    # the decode rate against what library kernels reach on this GPU over 4 GiB (beyond the
-    # MALL): a full read (torch sum), the like-for-like reference for a read-only kernel,
-    # and a device copy (read + write)
+    # context, not a ceiling: what two torch kernels reach on this GPU over 4 GiB (beyond
+    # the MALL), a full read (sum) and a device copy (read + write); torch's reduction does
+    # not stream at the HBM rate, so the decode kernel can exceed it
     cal = calibrate(4.0)
-    result["measured_read_gbps"] = cal["sum_read_gbps"]
-    result["measured_copy_gbps"] = cal["copy_read_plus_write_gbps"]
-    result["kv_frac_of_measured_read"] = round(kv_gbps / cal["sum_read_gbps"], 4)
+    result["torch_sum_read_gbps"] = cal["sum_read_gbps"]
+    result["torch_copy_gbps"] = cal["copy_read_plus_write_gbps"]
     if not args.no_chunk:
         result["chunk"] = chunk_leg(caches, w, dev)
         log(f"[bench] chunk of {result['chunk']['n_query']} queries: {result['chunk']['attn_us']:.1f} us, "

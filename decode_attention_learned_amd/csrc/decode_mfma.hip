@@ -37,6 +37,7 @@ constexpr int kMfmaWaves = DMS_DECODE_WAVES;  // waves per decode workgroup
 constexpr int kMfmaThreads = kMfmaWaves * 64;
 constexpr int kGroup = 32;  // slots per group (half a page)
 constexpr int kMaxChunkPages = 1024;  // page ids staged in LDS per chunk
+constexpr int kCombineCols = 8;       // output columns combined across waves per round
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -242,7 +243,9 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
     }
   }
 
-  // combine the waves of this workgroup (s_o: [waves][ncol][D + 4] in dynamic LDS)
+  // combine the waves of this workgroup, kCombineCols columns at a time
+  // (s_o: [waves][kCombineCols][D + 4] in dynamic LDS, so that a launch with
+  // 16 columns needs no more LDS than four resident workgroups per CU allow)
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
   __shared__ float s_m[kMfmaWaves][16], s_l[kMfmaWaves][16];
@@ -252,38 +255,42 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
     s_m[wave][col] = m_run;
     s_l[wave][col] = l_run;
   }
-  if (col < ncol) {
-#pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt)
-      *reinterpret_cast<floatx4 *>(&s_o[(wave * ncol + col) * ostride + dt * 16 + quad * 4]) = o[dt];
-  }
-  __syncthreads();
-
   // output of column x / D: query c0 + col / G, head h * G + col % G
   const OutMap om{((size_t(b) * C + c0) * hkv * G + size_t(h) * G) * D, size_t(hkv) * G * D, G, D};
-  for (int x = tid; x < ncol * D; x += kMfmaThreads) {
-    const int g = x / D, d = x % D;
-    float M = s_m[0][g];
+  const int rcols = min(ncol, kCombineCols);
+  for (int r0 = 0; r0 < ncol; r0 += rcols) {
+    if (r0 > 0) __syncthreads();  // every thread is done reading the previous columns
+    if (col >= r0 && col < min(ncol, r0 + rcols)) {
 #pragma unroll
-    for (int w = 1; w < kMfmaWaves; ++w) M = fmaxf(M, s_m[w][g]);
-    float Ls = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kMfmaWaves; ++w) {
-        const float mw = s_m[w][g];
-        if (mw == -INFINITY) continue;
-        const float f = exp2f(mw - M);
-        Ls = fmaf(s_l[w][g], f, Ls);
-        O = fmaf(s_o[(w * ncol + g) * ostride + d], f, O);
-      }
+      for (int dt = 0; dt < DTILES; ++dt)
+        *reinterpret_cast<floatx4 *>(&s_o[(wave * rcols + col - r0) * ostride + dt * 16 + quad * 4]) = o[dt];
     }
-    if (ci.nch == 1) {
-      out[om.at(x)] = Ls > 0.f ? O / Ls : 0.f;
-    } else {
-      publish(part_o + size_t(c) * ncol * D + x, O);
-      if (d == 0) {
-        publish(reinterpret_cast<float *>(part_ml + size_t(c) * ncol + g), M);
-        publish(reinterpret_cast<float *>(part_ml + size_t(c) * ncol + g) + 1, Ls);
+    __syncthreads();
+    const int xend = min(ncol, r0 + rcols) * D;
+    for (int x = r0 * D + tid; x < xend; x += kMfmaThreads) {
+      const int g = x / D, d = x % D;
+      float M = s_m[0][g];
+#pragma unroll
+      for (int w = 1; w < kMfmaWaves; ++w) M = fmaxf(M, s_m[w][g]);
+      float Ls = 0.f, O = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kMfmaWaves; ++w) {
+          const float mw = s_m[w][g];
+          if (mw == -INFINITY) continue;
+          const float f = exp2f(mw - M);
+          Ls = fmaf(s_l[w][g], f, Ls);
+          O = fmaf(s_o[(w * rcols + g - r0) * ostride + d], f, O);
+        }
+      }
+      if (ci.nch == 1) {
+        out[om.at(x)] = Ls > 0.f ? O / Ls : 0.f;
+      } else {
+        publish(part_o + size_t(c) * ncol * D + x, O);
+        if (d == 0) {
+          publish(reinterpret_cast<float *>(part_ml + size_t(c) * ncol + g), M);
+          publish(reinterpret_cast<float *>(part_ml + size_t(c) * ncol + g) + 1, Ls);
+        }
       }
     }
   }
@@ -294,7 +301,8 @@ bool launch_decode_mfma_part(const dms_shape &s, const dms_cache &c, const void 
                              float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
                              int nq, int c0, int C) {
   auto args = [&](auto kern) {
-    const size_t lds = size_t(kMfmaWaves) * nq * s.group * (s.head_dim + 4) * sizeof(float);
+    const int rcols = nq * s.group < kCombineCols ? nq * s.group : kCombineCols;
+    const size_t lds = size_t(kMfmaWaves) * rcols * (s.head_dim + 4) * sizeof(float);
     if (lds > 48 * 1024)  // gfx950 workgroups may use up to 160 KB of LDS
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));

@@ -205,14 +205,20 @@ __device__ __forceinline__ void pv_tile(const uint4 *__restrict__ sv, const uint
 // ---- tile ring -----------------------------------------------------------
 // Copy N uint4 (a 16 KB packed tile, or half of one) into LDS with the load
 // unit: wave w copies uint4 256 r + 64 w + lane, one contiguous 1 KB run per
-// copy instruction.
+// copy instruction.  The copies are buffer loads: the source is a buffer
+// resource (scalar registers) and the lane's byte offset 16 * tid is the same
+// for every tile, so a copy costs no vector instruction.
+constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer resource word 3 (32-bit data)
 template <int N = PTILE_U4>
 __device__ __forceinline__ void ring_copy(const uint4 *__restrict__ src, uint4 *dst, int tid,
                                           int wave) {
   static_assert(N % PNT == 0, "whole runs");
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4 *>(src), 0, N * 16, kBufferFlags);
 #pragma unroll
   for (int r = 0; r < N / PNT; ++r)
-    __builtin_amdgcn_global_load_lds(src + r * PNT + tid, dst + r * PNT + wave * kWave, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + r * PNT + wave * kWave, 16, tid * 16,
+                                             r * PNT * 16, 0, 0);
 }
 
 // Copy 128 bytes of per-key data (a mask or positions) with lanes 0..7 of wave 0.
@@ -233,23 +239,20 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 // Phase 1 of tile k: PV product of tile k - 1 (values `sv`) and QK product of
-// tile k (keys `sk`; from the additive mask `sb` on far tiles, from zero on
-// near ones).  The wave raises its issue priority for the phase, so that the
-// SIMD's other waves (in phase 2) fill the gaps between matrix instructions
-// rather than delaying them.
+// tile k (keys `sk`; from the additive mask `sb` on far tiles, from the zeros
+// `sz` on near ones, both read from LDS).  The wave raises its issue priority
+// for the phase, so that the SIMD's other waves (in phase 2) fill the gaps
+// between matrix instructions rather than delaying them.
 __device__ __forceinline__ void phase1(int k, int ntw, int nfar, const uint4 *__restrict__ sk,
                                        const uint4 *__restrict__ sv, const floatx4 *__restrict__ sb,
-                                       const uint4 (&qf)[2][PKS], floatx4 (&s)[2][2],
-                                       const uint4 (&pb)[2], floatx4 (&o)[PDT][2], int lane,
-                                       int quad) {
+                                       const floatx4 *__restrict__ sz, const uint4 (&qf)[2][PKS],
+                                       floatx4 (&s)[2][2], const uint4 (&pb)[2],
+                                       floatx4 (&o)[PDT][2], int lane, int quad) {
   __builtin_amdgcn_s_setprio(2);
   if (k >= 1 && k - 1 < ntw) pv_tile(sv, pb, lane, o);
   if (k < ntw) {
-    floatx4 init[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-    if (k < nfar) {
-      init[0] = sb[2 * quad];
-      init[1] = sb[2 * quad + 1];
-    }
+    const floatx4 *ip = k < nfar ? sb : sz;
+    const floatx4 init[2] = {ip[2 * quad], ip[2 * quad + 1]};
     qk_tile(sk, init, qf, lane, s);
   }
   __builtin_amdgcn_s_setprio(0);
@@ -505,11 +508,13 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill(
   // the tile ring: packed tile and mask of tile t in buffer t % 3
   __shared__ uint4 sT0[PTILE_U4], sT1[PTILE_U4], sT2[PTILE_U4];
   __shared__ floatx4 sM0[PBN / 4], sM1[PBN / 4], sM2[PBN / 4];
+  __shared__ floatx4 sZ[PBN / 4];  // zeros: the initial scores of a near tile
   auto copy = [&](int tile, uint4 *dt, floatx4 *dm) {
     ring_copy(pk + size_t(tile) * PTILE_U4, dt, tid, wave);
     ring_copy_keys(pm + size_t(tile) * (PBN / 4), dm, tid);
   };
   copy(0, sT0, sM0);
+  if (tid < PBN / 4) sZ[tid] = floatx4{0.f, 0.f, 0.f, 0.f};
   ring_barrier();
 
   const int ntw = ntiles;  // every wave needs every tile of the block
@@ -521,7 +526,7 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill(
                        floatx4 *mn) {
     if (k + 1 < ntiles) copy(k + 1, tn, mn);
     if (active) {
-      phase1(k, ntw, nfar, t, tp + PK_FRAGS * PFRAG, m, qf, s, pb, o, lane, quad);
+      phase1(k, ntw, nfar, t, tp + PK_FRAGS * PFRAG, m, sZ, qf, s, pb, o, lane, quad);
       phase2(k, ntw, nfar, S, window, qi0, col, quad, m, s, sm, o, pb, c);
     }
     ring_barrier();

@@ -96,10 +96,21 @@ def build_replica(w, r, dev, extra_tokens):
     return cache, rates
 
 
-def cpu_baseline(w, seconds: float = 12.0) -> dict:
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, seconds: float = 12.0, threads: int = 1) -> dict:
     """Time the float64 oracle on host cores on a bounded sample of the same workload:
     one sequence (all its KV heads) with the full context, then decode steps
-    (append, attend, compaction every `compact_every` steps) until `seconds` pass."""
+    (append, attend, compaction every `compact_every` steps) until `seconds` pass.
+    BLAS may use `threads` threads."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -111,7 +122,7 @@ def cpu_baseline(w, seconds: float = 12.0) -> dict:
     units = [orc.UnitCache(sample.window, sample.head_dim, dtype=np.float32)
              for _ in range(sample.kv_heads)]
     scale = 1.0 / math.sqrt(sample.head_dim)
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         for ci, start in enumerate(range(0, sample.context, sample.prompt_chunk)):
             n = min(sample.prompt_chunk, sample.context - start)
             k, v, logit = wl.prompt_chunk_inputs(sample, ci, n, rates=rates)
@@ -121,6 +132,7 @@ def cpu_baseline(w, seconds: float = 12.0) -> dict:
                 uc.append(alpha[0, :, h], kf[0, :, h], vf[0, :, h])
                 uc.compact()
         steps = 0
+        kv_bytes = 0
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < seconds:
             q, k, v, logit = wl.decode_step_inputs(sample, steps, rates=rates)
@@ -130,14 +142,18 @@ def cpu_baseline(w, seconds: float = 12.0) -> dict:
             for h, uc in enumerate(units):
                 uc.append(alpha[0, :, h], kf[0, :, h], vf[0, :, h])
                 uc.attend(qf[0, h * sample.group:(h + 1) * sample.group], scale)
+                kv_bytes += int(uc.live().sum()) * sample.head_dim * 2 * 2  # K and V, bf16
                 if (steps + 1) % sample.compact_every == 0:
                     uc.compact()
             steps += 1
         dt = time.perf_counter() - t0
-    return {"value": steps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": steps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(), "seconds_per_step": round(dt / steps, 6),
+            "kv_gbps": round(kv_bytes / dt / 1e9, 4),
             "sample": f"1 of {w.batch} sequences ({sample.kv_heads} KV heads x G={sample.group}, "
                       f"context {sample.context}), {steps} decode steps in {dt:.1f} s, "
-                      "float64 NumPy with BLAS limited to 1 thread"}
+                      f"float64 NumPy with BLAS limited to {threads} thread(s); tokens/s is the "
+                      "same for the full batch (each of its steps is 64 such sequences)"}
 
 
 def _time_calls(fn, iters: int) -> float:
@@ -637,8 +653,11 @@ def main():
             f"{result['chunked_prefill']['ms']:.3f} ms")
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        log(f"[bench] timing the oracle on the host (~{args.cpu_seconds:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        # the oracle as it stands: BLAS on every core this process may use, then on one
+        cores = len(os.sched_getaffinity(0))
+        log(f"[bench] timing the oracle on the host (~{2 * args.cpu_seconds:.0f} s: {cores} cores, then 1)")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, threads=cores)
+        result["cpu_baseline_1core"] = cpu_baseline(w, args.cpu_seconds, threads=1)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

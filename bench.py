@@ -629,6 +629,7 @@ def main():
     cal = calibrate(4.0)
     result["torch_sum_read_gbps"] = cal["sum_read_gbps"]
     result["torch_copy_gbps"] = cal["copy_read_plus_write_gbps"]
+    result["kv_frac_of_torch_copy"] = round(kv_gbps / cal["copy_read_plus_write_gbps"], 4)
     if not args.no_chunk:
         result["chunk"] = chunk_leg(caches, w, dev)
         log(f"[bench] chunk of {result['chunk']['n_query']} queries: {result['chunk']['attn_us']:.1f} us, "

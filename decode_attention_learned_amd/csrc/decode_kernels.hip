@@ -196,8 +196,8 @@ bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, f
                         float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
                         int n_query);
 
-// The decode grid has one workgroup per possible chunk (units +
-// kTargetChunks); workgroups past the plan's chunk count exit at once.
+// The decode grid has one workgroup per possible chunk (max_chunks_of(units));
+// workgroups past the plan's chunk count exit at once.
 hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                          float sm_scale, void *wsv, hipStream_t st) {
   const DecodeWorkspace w = decode_workspace_layout(units_of(s), s.group, s.head_dim);

@@ -31,7 +31,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 #ifndef DMS_DECODE_WAVES
-#define DMS_DECODE_WAVES 4
+#define DMS_DECODE_WAVES 8
 #endif
 constexpr int kMfmaWaves = DMS_DECODE_WAVES;  // waves per decode workgroup
 constexpr int kMfmaThreads = kMfmaWaves * 64;

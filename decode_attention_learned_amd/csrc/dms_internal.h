@@ -14,13 +14,23 @@ namespace dms {
 
 constexpr int kPage = DMS_PAGE_SIZE;   // slots per page
 constexpr int kWave = 64;              // CDNA wavefront width
-// Target number of split-K chunks per decode call: one round of resident
-// decode workgroups (4 per CU on the 256 CUs).  Measured on the Qwen3-8B,
-// ragged Qwen2.5-32B and Llama-1B decode workloads against 512 and 2048.
+// Split-K chunks per decode call.  kTargetChunks is one round of resident
+// decode workgroups (8 waves each, 2 per CU on the 256 CUs).  Units of even
+// length fill one round: with at least that many units every unit is one
+// chunk (no merge), with fewer they are split.  Units of ragged length
+// (longest > twice the mean) are split into up to three rounds' worth, so that
+// workgroups that finish early take more chunks.  Measured on the Qwen3-8B (CR 8 and 1), ragged Qwen2.5-32B and
+// Llama-1B decode workloads.
 #ifndef DMS_TARGET_CHUNKS
-#define DMS_TARGET_CHUNKS 1024
+#define DMS_TARGET_CHUNKS 512
 #endif
 constexpr int kTargetChunks = DMS_TARGET_CHUNKS;
+constexpr int kRaggedRounds = 3;
+
+// the largest chunk count of a plan for `units` units
+__host__ __device__ inline int max_chunks_of(int units) {
+  return units > kTargetChunks ? units : kRaggedRounds * kTargetChunks;
+}
 
 inline int units_of(const dms_shape &s) { return s.batch * s.kv_heads; }
 
@@ -38,7 +48,7 @@ struct PlanLayout {
 
 __host__ __device__ inline PlanLayout plan_layout(int units) {
   PlanLayout p;
-  p.max_chunks = units + kTargetChunks;
+  p.max_chunks = max_chunks_of(units);
   p.hdr = 0;
   p.first_chunk = 16;
   p.chunk_unit = p.first_chunk + size_t(units) + 1;
@@ -59,7 +69,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline DecodeWorkspace decode_workspace_layout(int units, int group, int head_dim) {
   DecodeWorkspace w;
-  w.max_chunks = units + kTargetChunks;
+  w.max_chunks = max_chunks_of(units);
   size_t off = 0;
   w.part_ml = off; off = align256(off + size_t(w.max_chunks) * group * 2 * sizeof(float));
   w.part_o = off;  off = align256(off + size_t(w.max_chunks) * group * head_dim * sizeof(float));
@@ -154,9 +164,12 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 // Every thread reads only the n_slots entries it is the sole writer of in a
 // caller that updated them (unit u = base + threadIdx.x), so a caller that
 // has just written n_slots needs nothing beyond a workgroup barrier.
-// Chunk size C (slots, a multiple of the page size) is the smallest that
-// keeps the chunk count at most units + kTargetChunks:
-//   C = 64 * max(1, ceil(total / (64 * kTargetChunks))),  chunks(u) = max(1, ceil(n_u / C)).
+// Chunk size C (slots, a multiple of the page size), chunks(u) = max(1, ceil(n_u / C)),
+// with a budget of R * kTargetChunks chunks, R = kRaggedRounds if the longest
+// unit holds more than twice the mean (max_u n_u > 2 * total / units), else 1:
+//   units >= budget:  C = 64 * ceil(max_u n_u / 64)   (one chunk per unit)
+//   otherwise:        C = 64 * max(1, ceil(total / (64 * (budget - units))))
+// so that sum_u chunks(u) <= total / C + units <= budget.
 constexpr int kPlanThreads = 1024;
 
 __device__ inline void build_plan(int units, const int32_t *n_slots, int32_t *plan) {
@@ -166,16 +179,39 @@ __device__ inline void build_plan(int units, const int32_t *n_slots, int32_t *pl
   int32_t *chunk_unit = plan + L.chunk_unit;
   int32_t *merge_count = plan + L.merge_count;
   __shared__ unsigned long long s_total;
+  __shared__ int s_max;
   __shared__ int s_tmp[kPlanThreads / kWave];
-  if (threadIdx.x == 0) s_total = 0ull;
+  if (threadIdx.x == 0) {
+    s_total = 0ull;
+    s_max = 0;
+  }
   __syncthreads();
   long long part = 0;
-  for (int u = threadIdx.x; u < units; u += kPlanThreads) part += n_slots[u];
-  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, kWave);
-  if (lane_id() == 0) atomicAdd(&s_total, (unsigned long long)part);
+  int mx = 0;
+  for (int u = threadIdx.x; u < units; u += kPlanThreads) {
+    const int n = n_slots[u];
+    part += n;
+    mx = max(mx, n);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    part += __shfl_xor(part, o, kWave);
+    mx = max(mx, __shfl_xor(mx, o, kWave));
+  }
+  if (lane_id() == 0) {
+    atomicAdd(&s_total, (unsigned long long)part);
+    atomicMax(&s_max, mx);
+  }
   __syncthreads();
   const long long total = (long long)s_total;
-  const long long per = (total + (long long)kPage * kTargetChunks - 1) / ((long long)kPage * kTargetChunks);
+  const bool ragged = (long long)s_max * units > 2 * total;
+  const int budget = (ragged ? kRaggedRounds : 1) * kTargetChunks;
+  long long per;
+  if (units >= budget) {
+    per = (s_max + kPage - 1) / kPage;
+  } else {
+    const long long room = (long long)kPage * (budget - units);
+    per = (total + room - 1) / room;
+  }
   const int C = kPage * int(per < 1 ? 1 : per);
   int carry = 0;
   for (int base = 0; base < units; base += kPlanThreads) {

@@ -553,7 +553,13 @@ def main():
     torch.cuda.synchronize()
     before = [retained_total(c) for c, _ in caches]
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Per-call HIP events are recorded on one step in eight of each replica (every
+    # compaction step among them): an event record costs a few microseconds of
+    # queue time, so events on every call would inflate the step it measures.
+    def sampled(i):  # short runs (profiling) sample every step
+        return args.steps < 64 or (i // replicas) % 8 == 7
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] if sampled(args.warmup + i) else None
+           for i in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -569,9 +575,9 @@ def main():
     if any(status):
         raise RuntimeError(f"device status words {status}")
 
-    t_append = [e[0].elapsed_time(e[1]) for e in evs]
-    t_decode = [e[1].elapsed_time(e[2]) for e in evs]
-    t_compact = [e[2].elapsed_time(e[3]) for e, f in zip(evs, flags) if f]
+    t_append = [e[0].elapsed_time(e[1]) for e in evs if e is not None]
+    t_decode = [e[1].elapsed_time(e[2]) for e in evs if e is not None]
+    t_compact = [e[2].elapsed_time(e[3]) for e, f in zip(evs, flags) if e is not None and f]
     ms_step = total_ms / args.steps
     dec_ms = sum(t_decode) / len(t_decode)
     retained = sum(a[0] + b[0] for a, b in zip(before, after)) / (2 * replicas)

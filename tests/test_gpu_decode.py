@@ -359,3 +359,86 @@ def test_constant_values_give_the_constant(gpu, dtype, tol):
     q = torch.randn((b, hkv * g, d), generator=torch.Generator().manual_seed(5)).to(dtype)
     out = cache.decode(q.to(gpu)).cpu().double()
     assert torch.max(torch.abs(out - c.double())).item() <= tol
+
+
+# ---------------------------------------------------------------- split plan
+def _plan(cache):
+    """(chunk count, chunk size C, first_chunk [units + 1], chunk_unit [count]) from the
+    device plan (layout: 16 header words, first chunk per unit + 1, owning unit per chunk)."""
+    p = cache.plan.cpu().numpy()
+    units = cache.units
+    count, C = int(p[0]), int(p[1])
+    first = p[16:16 + units + 1]
+    owner = p[16 + units + 1:16 + units + 1 + count]
+    return count, C, first, owner
+
+
+def _check_plan(cache, budget):
+    """The plan covers every unit with max(1, ceil(n / C)) chunks, in unit order, within
+    `budget` chunks.  Returns (chunk count, C, n_slots)."""
+    n = cache.n_slots.cpu().numpy().astype(np.int64)
+    count, C, first, owner = _plan(cache)
+    assert C % 64 == 0 and C >= 64
+    nch = np.where(n > 0, (n + C - 1) // C, 1)
+    assert first[0] == 0 and np.array_equal(np.diff(first), nch), "first_chunk is the prefix sum"
+    assert first[-1] == count
+    assert np.array_equal(owner, np.repeat(np.arange(cache.units), nch)), "chunk -> unit map"
+    assert count <= budget, f"{count} chunks over the budget {budget}"
+    return count, C, n
+
+
+def _plan_case(b, hkv, tokens, logit_of_unit, dev, seed):
+    """A bf16 cache of b x hkv units (G = 4, D = 128): `tokens` appended tokens (unit u's
+    logits all logit_of_unit(u)), a compaction, then one more token, kept.  Returns
+    (cache, q, k, v, logits) with the full token history on the host."""
+    g = torch.Generator().manual_seed(seed)
+    T = tokens + 1
+    cache = DmsCache(b, hkv, 4, 128, torch.bfloat16, max_pages_per_unit=T // 64 + 3, device=dev)
+    k = torch.randn(b, T, hkv, 128, generator=g).to(torch.bfloat16)
+    v = torch.randn(b, T, hkv, 128, generator=g).to(torch.bfloat16)
+    q = torch.randn(b, 4 * hkv, 128, generator=g).to(torch.bfloat16)
+    lg = torch.tensor([[logit_of_unit(bi * hkv + h) for h in range(hkv)] for bi in range(b)],
+                      dtype=torch.float32)[:, None, :].repeat(1, T, 1)
+    lg[:, -1] = -1.0
+    cache.append(k[:, :tokens].contiguous().to(dev), v[:, :tokens].contiguous().to(dev),
+                 lg[:, :tokens].contiguous().to(dev))
+    cache.compact()
+    cache.append(k[:, tokens:].contiguous().to(dev), v[:, tokens:].contiguous().to(dev),
+                 lg[:, tokens:].contiguous().to(dev))
+    torch.cuda.synchronize()
+    return cache, q, k, v, lg
+
+
+def _check_units(out, q, k, v, lg, units, hkv):
+    alpha = orc.eviction_decisions(lg.numpy())
+    t = k.shape[1] - 1
+    for u in units:
+        bi, h = divmod(u, hkv)
+        ref = orc.decode_output(q[bi, 4 * h:4 * h + 4].float().numpy(), k[bi, :, h].float().numpy(),
+                                v[bi, :, h].float().numpy(), alpha[bi, :, h], t, 16, scale_of(128))
+        got = out[bi, 4 * h:4 * h + 4].double().numpy()
+        assert np.all(np.abs(got - ref) <= 2e-2 + 2e-2 * np.abs(ref)), f"unit {u}"
+
+
+def test_split_plan_even_units_fill_one_round(gpu):
+    """512 units of equal length: one chunk per unit (no merge); 128 units of equal
+    length: split to at most one round of 512 workgroups.  Outputs against the oracle
+    on sampled units."""
+    cache, q, k, v, lg = _plan_case(64, 8, 300, lambda u: -1.0, gpu, 91)
+    count, _, _ = _check_plan(cache, 512)
+    assert count == 512
+    _check_units(cache.decode(q.to(gpu)).cpu(), q, k, v, lg, range(0, 512, 37), 8)
+    cache, q, k, v, lg = _plan_case(16, 8, 2000, lambda u: -1.0, gpu, 92)
+    count, _, _ = _check_plan(cache, 512)
+    assert 128 < count <= 512
+    _check_units(cache.decode(q.to(gpu)).cpu(), q, k, v, lg, range(0, 128, 11), 8)
+
+
+def test_split_plan_ragged_units_take_up_to_three_rounds(gpu):
+    """Ragged lengths (a quarter of the units keep everything, the rest only the window):
+    more than one round's worth of chunks, at most three; outputs against the oracle."""
+    cache, q, k, v, lg = _plan_case(32, 8, 3000, lambda u: -1.0 if u % 4 == 0 else 1.0, gpu, 93)
+    count, _, n = _check_plan(cache, 3 * 512)
+    assert n.max() > 2 * n.mean()
+    assert count > 512
+    _check_units(cache.decode(q.to(gpu)).cpu(), q, k, v, lg, list(range(0, 256, 9)) + [1, 4], 8)

@@ -179,8 +179,9 @@ size_t dms_decode_workspace_bytes(const dms_shape *shape);
  * The caller appends token t before this call, so each query sees its own
  * token.  A unit with no slots gives zeros.  The work of each unit is split
  * into chunks of whole pages following cache->plan (sized on the device from
- * the live lengths), and the last chunk of a unit to finish merges the
- * chunk partials with the log-sum-exp rule: one kernel launch per call.
+ * the live lengths: one chunk per unit when the units are many and of even
+ * length), and the last chunk of a unit to finish merges the chunk partials
+ * with the log-sum-exp rule: one kernel launch per call.
  * The call uses per-unit counters inside cache->plan and leaves them zero;
  * two decode calls on one cache must not run concurrently.
  */

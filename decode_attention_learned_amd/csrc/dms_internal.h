@@ -104,7 +104,8 @@ hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void
 // value fragments (head_dim 128, bf16) and 32 floats of additive mask.
 inline size_t prefill_workspace_bytes(int batch, int kv_heads, int seq_len) {
   const size_t tiles = size_t(batch) * kv_heads * ((size_t(seq_len) + 31) / 32);
-  return align256(tiles * 16384) + align256(tiles * 32 * sizeof(float));
+  // packed tiles, their masks, packed tiles with masked keys zero (far use)
+  return align256(tiles * 16384) + align256(tiles * 32 * sizeof(float)) + align256(tiles * 16384);
 }
 
 // Gathered-key prefill workspace: the dense prefill workspace (for the band

@@ -383,7 +383,8 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
                                                       const float *__restrict__ noise, float inv_tau,
                                                       float inv_scale, int relaxed,
                                                       uint4 *__restrict__ packed,
-                                                      float *__restrict__ mask) {
+                                                      float *__restrict__ mask,
+                                                      uint4 *__restrict__ packed_far) {
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x;
   const int j0 = tile * PBN;
@@ -391,6 +392,7 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
   uint4 *kdst = packed + T * PTILE_U4;
   uint4 *vdst = kdst + PK_FRAGS * PFRAG;
   __shared__ __align__(16) uint16_t sv[PBN][PD + 8];  // row-major values, padded rows
+  __shared__ uint32_t s_gone[PBN];                    // key masked (-inf) for far use
 
   // thread t: key jj = t / 16, dims dc*8 .. +8
   const int jj = t >> 4, dc = t & 15;
@@ -406,6 +408,14 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
   const int ks = dc >> 2, qd = dc & 3;
   kdst[(tt * PKS + ks) * PFRAG + qd * 16 + row] = kp;
   *reinterpret_cast<uint4 *>(&sv[jj][dc * 8]) = vp;
+  // The far-tile copy: a key whose additive mask is -inf (marked, or past the
+  // end) is invisible wherever a tile is far, so its key and value rows are
+  // zero there.  Same scores and output; the matrix cores draw less power on
+  // zero operands, which keeps the clock up.
+  const bool gone = j >= S || (!relaxed && evict_decision(logit[(size_t(b) * S + j) * hkv + h]));
+  uint4 *kfar = packed_far ? packed_far + T * PTILE_U4 : nullptr;
+  if (kfar) kfar[(tt * PKS + ks) * PFRAG + qd * 16 + row] = gone ? make_uint4(0, 0, 0, 0) : kp;
+  if (dc == 0) s_gone[jj] = gone ? 0u : 0xffffffffu;
   // additive mask of key j0 + t, applied once the key is w or more behind
   // the query: hard rule -inf if marked for eviction, 0 if kept; relaxed
   // rule log(1 - sigmoid((logit + noise) / tau)) = -softplus(x); -inf past
@@ -433,11 +443,18 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
   for (int e = 0; e < 4; ++e)
     w[e] = uint32_t(sv[k0 + 2 * e][d]) | (uint32_t(sv[k0 + 2 * e + 1][d]) << 16);
   vdst[t] = make_uint4(w[0], w[1], w[2], w[3]);
+  if (kfar) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] &= (s_gone[k0 + 2 * e] & 0xffffu) | (s_gone[k0 + 2 * e + 1] & 0xffff0000u);
+    kfar[PK_FRAGS * PFRAG + t] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
 __global__ __launch_bounds__(PNT, 3) void k_prefill(
     int batch, int S, int hkv, int G, int window, float scale_log2, const uint16_t *__restrict__ q,
-    const uint4 *__restrict__ packed, const floatx4 *__restrict__ mask, float *__restrict__ out) {
+    const uint4 *__restrict__ packed, const floatx4 *__restrict__ mask,
+    const uint4 *__restrict__ packed_far, float *__restrict__ out) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
@@ -503,14 +520,16 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill(
 
   const int ntiles_all = (S + PBN - 1) / PBN;
   const uint4 *pk = packed + tile_index(b, h, 0, hkv, ntiles_all) * PTILE_U4;
+  const uint4 *pkf = packed_far + tile_index(b, h, 0, hkv, ntiles_all) * PTILE_U4;
   const floatx4 *pm = mask + tile_index(b, h, 0, hkv, ntiles_all) * (PBN / 4);
 
-  // the tile ring: packed tile and mask of tile t in buffer t % 3
+  // the tile ring: packed tile and mask of tile t in buffer t % 3 (a far tile
+  // from the copy whose masked keys are zero)
   __shared__ uint4 sT0[PTILE_U4], sT1[PTILE_U4], sT2[PTILE_U4];
   __shared__ floatx4 sM0[PBN / 4], sM1[PBN / 4], sM2[PBN / 4];
   __shared__ floatx4 sZ[PBN / 4];  // zeros: the initial scores of a near tile
   auto copy = [&](int tile, uint4 *dt, floatx4 *dm) {
-    ring_copy(pk + size_t(tile) * PTILE_U4, dt, tid, wave);
+    ring_copy((tile < nfar ? pkf : pk) + size_t(tile) * PTILE_U4, dt, tid, wave);
     ring_copy_keys(pm + size_t(tile) * (PBN / 4), dm, tid);
   };
   copy(0, sT0, sM0);
@@ -796,11 +815,17 @@ hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, cons
   const size_t tiles = size_t(s.batch) * s.kv_heads * ntiles;
   uint4 *packed = static_cast<uint4 *>(ws);
   float *mask = reinterpret_cast<float *>(static_cast<char *>(ws) + align256(tiles * 16384));
+  // far-tile copy (masked keys zero); the relaxed mask hides no key, so its
+  // far tiles read the plain copy
   const int relaxed = temperature > 0.f;
+  uint4 *packed_far = relaxed ? nullptr
+                              : reinterpret_cast<uint4 *>(static_cast<char *>(ws) + align256(tiles * 16384) +
+                                                          align256(tiles * PBN * sizeof(float)));
   hipLaunchKernelGGL(k_prefill_pack, dim3(ntiles, s.kv_heads, s.batch), dim3(512), 0, st, seq_len,
                      s.kv_heads, ntiles, static_cast<const uint16_t *>(k),
                      static_cast<const uint16_t *>(v), logit, noise,
-                     relaxed ? 1.f / temperature : 0.f, 1.f / sm_scale, relaxed, packed, mask);
+                     relaxed ? 1.f / temperature : 0.f, 1.f / sm_scale, relaxed, packed, mask,
+                     packed_far);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ngh = (s.group + PHPW - 1) / PHPW;
@@ -812,7 +837,7 @@ hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, cons
   hipLaunchKernelGGL(k_prefill, dim3(unsigned(blocks)), dim3(PNT), 0, st, s.batch, seq_len,
                      s.kv_heads, s.group, s.window, sm_scale * 1.4426950408889634f,
                      static_cast<const uint16_t *>(q), packed,
-                     reinterpret_cast<const floatx4 *>(mask), out);
+                     reinterpret_cast<const floatx4 *>(mask), packed_far ? packed_far : packed, out);
   return hipGetLastError();
 }
 
@@ -833,7 +858,7 @@ hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void
   uint32_t *keptw = reinterpret_cast<uint32_t *>(base + L.keptw);
   const uint16_t *k16 = static_cast<const uint16_t *>(k), *v16 = static_cast<const uint16_t *>(v);
   hipLaunchKernelGGL(k_prefill_pack, dim3(ntiles, s.kv_heads, s.batch), dim3(512), 0, st, seq_len,
-                     s.kv_heads, ntiles, k16, v16, logit, nullptr, 0.f, 1.f, 0, dense, mask);
+                     s.kv_heads, ntiles, k16, v16, logit, nullptr, 0.f, 1.f, 0, dense, mask, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_sparse_scan, dim3(s.batch * s.kv_heads), dim3(1024), 0, st, seq_len,

@@ -243,8 +243,11 @@ int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const 
 
 /*
  * Bytes of prefill workspace for `seq_len` tokens of this shape: keys and
- * values re-laid out per 32-key tile for the matrix cores, plus one float
- * per key (its decision as an additive mask).  0 if the arguments are invalid.
+ * values re-laid out per 32-key tile for the matrix cores, one float per key
+ * (its decision as an additive mask), and the re-laid keys and values again
+ * with every key masked out under the hard rule zeroed (read where all of a
+ * tile's keys are at least w behind every query).  0 if the arguments are
+ * invalid.
  */
 size_t dms_prefill_workspace_bytes(const dms_shape *shape, int32_t seq_len);
 

@@ -132,8 +132,9 @@ def test_prefill_host_errors(L):
         == lib.DMS_EINVAL
     assert L.dms_prefill_attn(ctypes.byref(bf), fake, fake, fake, fake, 16, 0.1, fake, fake, 10, None) \
         == lib.DMS_EWORKSPACE
-    # 2 sequences x 2 KV heads x ceil(100/32) tiles x 16 KB, plus 32 floats per tile
-    assert lib.prefill_workspace_bytes(bf, 100) == 2 * 2 * 4 * 16384 + 2 * 2 * 4 * 32 * 4
+    # 2 sequences x 2 KV heads x ceil(100/32) tiles x 16 KB, plus 32 floats per tile,
+    # plus the far-tile copy (16 KB per tile)
+    assert lib.prefill_workspace_bytes(bf, 100) == 2 * (2 * 2 * 4 * 16384) + 2 * 2 * 4 * 32 * 4
     assert lib.prefill_workspace_bytes(f32, 100) == 0
     # gathered: dense part, gathered copy of it, kept positions (S per unit),
     # counts (ntiles + 1 per unit) and kept bits (ntiles per unit), each 256-aligned

@@ -48,8 +48,11 @@
 // Far and near tiles.  A tile whose keys all lie `w` or more positions behind
 // every query of the workgroup ("far") is masked by the decision alone, which
 // depends on the key only: the QK product starts from the additive mask as
-// its accumulator, so such a tile costs no mask arithmetic.  The few tiles on
-// the diagonal band ("near") apply the full rule per element in phase 2.
+// its accumulator, so such a tile costs no mask arithmetic.  Far tiles are
+// read from a second packed copy in which the keys the hard rule masks out
+// have zero rows (they are invisible there; zero operands cost the matrix
+// cores less power).  The few tiles on the diagonal band ("near") come from
+// the plain copy and apply the full rule per element in phase 2.
 //
 // Softmax reference.  Each query keeps a reference m (raw score units) that
 // moves only when a score exceeds it by more than kLazy / c (c = scale *

@@ -589,35 +589,53 @@ __global__ __launch_bounds__(1024) void k_sparse_scan(int S, int hkv, int ntiles
                                                       int32_t *__restrict__ gpos,
                                                       int32_t *__restrict__ tile_cnt,
                                                       uint32_t *__restrict__ keptw) {
+  // Thread t takes keys base + 8t .. + 7 of each 8192-key stretch: its eight
+  // decisions are loaded together, one workgroup scan of the per-thread kept
+  // counts orders the whole stretch, and a 32-key tile is the keys of four
+  // consecutive threads.
+  constexpr int KPT = 8, NT = 1024, STRETCH = KPT * NT;
   const int u = blockIdx.x;
   const int b = u / hkv, h = u % hkv;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  __shared__ int s_wcnt[16];
-  __shared__ int s_total;
+  __shared__ int s_wsum[NT / kWave];
   int running = 0;
-  for (int base = 0; base < S; base += 1024) {
-    const int j = base + tid;
-    const bool kept = j < S && !evict_decision(logit[(size_t(b) * S + j) * hkv + h]);
-    const uint64_t m = __ballot(kept);
-    if (lane == 0) s_wcnt[wave] = __popcll(m);
-    __syncthreads();
-    int before = running;
-    for (int w = 0; w < wave; ++w) before += s_wcnt[w];
-    if (kept) gpos[size_t(u) * S + before + lanes_below(m)] = j;
-    if ((lane & 31) == 0 && j < S) {
-      const int t = j >> 5;
-      const uint32_t half = uint32_t(m >> (lane & 32));
-      keptw[size_t(u) * ntiles + t] = half;
-      tile_cnt[size_t(u) * (ntiles + 1) + t] = before + (lane ? __popc(uint32_t(m)) : 0);
+  for (int base = 0; base < S; base += STRETCH) {
+    const int j0 = base + KPT * tid;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int j = j0 + r;
+      const bool kept = j < S && !evict_decision(logit[(size_t(b) * S + j) * hkv + h]);
+      bits |= uint32_t(kept) << r;
     }
-    if (tid == 0) {
-      int tot = 0;
-      for (int w = 0; w < 16; ++w) tot += s_wcnt[w];
-      s_total = tot;
+    const int cnt = __popc(bits);
+    // exclusive prefix of the kept counts over the workgroup
+    const int incl = wave_inclusive_scan(cnt);
+    if (lane == kWave - 1) s_wsum[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+      int v = lane < NT / kWave ? s_wsum[lane] : 0;
+      v = wave_inclusive_scan(v);
+      if (lane < NT / kWave) s_wsum[lane] = v;
     }
     __syncthreads();
-    running += s_total;
-    __syncthreads();
+    const int before = running + (wave > 0 ? s_wsum[wave - 1] : 0) + incl - cnt;
+    const int total = s_wsum[NT / kWave - 1];
+    int g = before;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r)
+      if (bits & (1u << r)) gpos[size_t(u) * S + g++] = j0 + r;
+    // tile (j0 / 32): the bits of threads 4T .. 4T+3, and the count before it
+    uint32_t tile_bits = bits << (KPT * (tid & 3));
+    tile_bits |= __shfl_xor(tile_bits, 1, kWave);
+    tile_bits |= __shfl_xor(tile_bits, 2, kWave);
+    if ((tid & 3) == 0 && j0 < S) {
+      const int t = j0 >> 5;
+      keptw[size_t(u) * ntiles + t] = tile_bits;
+      tile_cnt[size_t(u) * (ntiles + 1) + t] = before;
+    }
+    running += total;
+    __syncthreads();  // s_wsum is rewritten by the next stretch
   }
   if (tid == 0) tile_cnt[size_t(u) * (ntiles + 1) + ntiles] = running;
 }

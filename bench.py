@@ -260,7 +260,9 @@ def chunk_leg(caches, w, dev, n_query: int = 4, rounds: int = 32) -> dict:
     """Chunk queries on the decode workload's caches: every round appends
     n_query tokens to one replica and attends all of them at once
     (dms_decode_attn_multi), compacting each replica every 16 tokens.  The
-    K/V of every retained entry is read once per launch of 16 / G queries."""
+    K/V of every retained entry is read once per launch of 16 / G queries.
+    The rounds are queued back to back (one synchronisation at the end), as a
+    serving loop would issue them."""
     import torch
 
     import workloads as wl
@@ -269,13 +271,20 @@ def chunk_leg(caches, w, dev, n_query: int = 4, rounds: int = 32) -> dict:
     gen.manual_seed(977)
     per_launch = max(1, 16 // w.group)
     launches = (n_query + per_launch - 1) // per_launch
-    t_app, t_att, t_cmp, retained = [], [], [], []
+    inputs = []
     for i in range(rounds):
         r = i % len(caches)
-        cache, rates = caches[r]
-        k, v, logit = wl.prompt_chunk_inputs(w, 100000 + i, n_query, device=dev, replica=r, rates=rates)
+        k, v, logit = wl.prompt_chunk_inputs(w, 100000 + i, n_query, device=dev, replica=r,
+                                             rates=caches[r][1])
         q = torch.randn((w.batch, n_query, w.q_heads, w.head_dim), generator=gen, device=dev,
                         dtype=torch.float32).to(torch.bfloat16)
+        inputs.append((q, k, v, logit))
+    torch.cuda.synchronize()
+    before = [retained_total(c)[0] for c, _ in caches]
+    evs, flags = [], []
+    for i in range(rounds):
+        cache = caches[i % len(caches)][0]
+        q, k, v, logit = inputs[i]
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         ev[0].record()
         cache.append(k, v, logit)
@@ -286,18 +295,22 @@ def chunk_leg(caches, w, dev, n_query: int = 4, rounds: int = 32) -> dict:
         if compacted:
             cache.compact()
         ev[3].record()
-        torch.cuda.synchronize()
-        if i >= len(caches):  # first round per replica is warm-up
-            t_app.append(ev[0].elapsed_time(ev[1]))
-            t_att.append(ev[1].elapsed_time(ev[2]))
-            if compacted:
-                t_cmp.append(ev[2].elapsed_time(ev[3]))
-            retained.append(retained_total(cache)[0])
+        evs.append(ev)
+        flags.append(compacted)
+    torch.cuda.synchronize()
+    after = [retained_total(c)[0] for c, _ in caches]
+    if any(c.status_word() for c, _ in caches):
+        raise RuntimeError("device status set during the chunk leg")
+    warm = len(caches)  # first round per replica is warm-up
+    t_app = [e[0].elapsed_time(e[1]) for e in evs[warm:]]
+    t_att = [e[1].elapsed_time(e[2]) for e in evs[warm:]]
+    t_cmp = [e[2].elapsed_time(e[3]) for e, f in zip(evs[warm:], flags[warm:]) if f]
     att = sum(t_att) / len(t_att)
     app = sum(t_app) / len(t_app)
     cmp_per_round = (sum(t_cmp) / max(1, len(t_cmp))) * n_query / 16
     step = app + att + cmp_per_round
-    bytes_alg = (sum(retained) / len(retained)) * w.head_dim * 2 * 2 * launches
+    retained = (sum(before) + sum(after)) / (2 * len(caches))
+    bytes_alg = retained * w.head_dim * 2 * 2 * launches
     return {
         "n_query": n_query, "launches_per_call": launches,
         "attn_us": round(att * 1e3, 2), "append_us": round(app * 1e3, 2),

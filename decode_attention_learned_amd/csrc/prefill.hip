@@ -52,7 +52,9 @@
 // read from a second packed copy in which the keys the hard rule masks out
 // have zero rows (they are invisible there; zero operands cost the matrix
 // cores less power).  The few tiles on the diagonal band ("near") come from
-// the plain copy and apply the full rule per element in phase 2.
+// the plain copy and apply the full rule per element in phase 2.  The far
+// tiles after the first run in a loop of their own, whose body has no test
+// on the tile index.
 //
 // Softmax reference.  Each query keeps a reference m (raw score units) that
 // moves only when a score exceeds it by more than kLazy / c (c = scale *
@@ -259,6 +261,23 @@ __device__ __forceinline__ void phase1(int k, int ntw, int nfar, const uint4 *__
     qk_tile(sk, init, qf, lane, s);
   }
   __builtin_amdgcn_s_setprio(0);
+}
+
+// Steady state, tile k >= 1 that needs no per-element mask (a far tile of
+// the dense kernel, a tile whose keys every query sees in the others): phase
+// 1 and phase 2 with every test on k resolved, for the loops that run only
+// such tiles.  The QK product starts from `init`.
+__device__ __forceinline__ void steady_step(const uint4 *__restrict__ sk,
+                                            const uint4 *__restrict__ sv, const floatx4 (&init)[2],
+                                            const uint4 (&qf)[2][PKS], floatx4 (&s)[2][2],
+                                            uint4 (&pb)[2], floatx4 (&o)[PDT][2], Softmax &sm,
+                                            float c, int lane) {
+  __builtin_amdgcn_s_setprio(2);
+  pv_tile(sv, pb, lane, o);
+  qk_tile(sk, init, qf, lane, s);
+  __builtin_amdgcn_s_setprio(0);
+  if (__ballot(crosses(s, sm))) move_reference(s, sm, o, c);
+  exponentials(s, sm, c, pb);
 }
 
 // Phase 2 of tile k: the full rule on near tiles, the reference check, and
@@ -553,12 +572,31 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill(
     }
     ring_barrier();
   };
-  for (int k = 0; k <= ntiles; k += 3) {
-    iteration(k, sT0, sM0, sT2, sT1, sM1);
+  auto far_iteration = [&](int k, const uint4 *t, const floatx4 *m, const uint4 *tp, uint4 *tn,
+                           floatx4 *mn) {
+    if (k + 1 < ntiles) copy(k + 1, tn, mn);
+    if (active) {
+      const floatx4 init[2] = {m[2 * quad], m[2 * quad + 1]};
+      steady_step(t, tp + PK_FRAGS * PFRAG, init, qf, s, pb, o, sm, c, lane);
+    }
+    ring_barrier();
+  };
+  // tile 0; then the far tiles 1 .. nfar - 1 in whole rounds of three; then
+  // the rest (the last far tiles, the near tiles, the PV product of the last
+  // tile) on the general path.  Tile k is in buffer k % 3.
+  iteration(0, sT0, sM0, sT2, sT1, sM1);
+  int k = 1;
+  for (; k + 2 < nfar; k += 3) {
+    far_iteration(k, sT1, sM1, sT0, sT2, sM2);
+    far_iteration(k + 1, sT2, sM2, sT1, sT0, sM0);
+    far_iteration(k + 2, sT0, sM0, sT2, sT1, sM1);
+  }
+  for (; k <= ntiles; k += 3) {
+    iteration(k, sT1, sM1, sT0, sT2, sM2);
     if (k + 1 > ntiles) break;
-    iteration(k + 1, sT1, sM1, sT0, sT2, sM2);
+    iteration(k + 1, sT2, sM2, sT1, sT0, sM0);
     if (k + 2 > ntiles) break;
-    iteration(k + 2, sT2, sM2, sT1, sT0, sM0);
+    iteration(k + 2, sT0, sM0, sT2, sT1, sM1);
   }
 
   if (!active) return;
@@ -803,12 +841,29 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill_gathered(
     }
     ring_barrier();
   };
-  for (int k = 0; k <= nT; k += 3) {
-    iteration(k, sT0, sP0, sT2, sT1, sP1);
+  auto clean_iteration = [&](int k, const uint4 *t, const uint4 *tp, uint4 *tn, int4 *pn) {
+    if (k + 1 < nT) copy(k + 1, tn, pn);
+    if (active) {
+      const floatx4 zero[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+      steady_step(t, tp + PK_FRAGS * PFRAG, zero, qf, s, pb, o, sm, c, lane);
+    }
+    ring_barrier();
+  };
+  // tile 0; the clean tiles 1 .. nclean - 1 in whole rounds of three; the rest
+  // on the general path.  Tile k is in buffer k % 3.
+  iteration(0, sT0, sP0, sT2, sT1, sP1);
+  int k = 1;
+  for (; k + 2 < nclean; k += 3) {
+    clean_iteration(k, sT1, sT0, sT2, sP2);
+    clean_iteration(k + 1, sT2, sT1, sT0, sP0);
+    clean_iteration(k + 2, sT0, sT2, sT1, sP1);
+  }
+  for (; k <= nT; k += 3) {
+    iteration(k, sT1, sP1, sT0, sT2, sP2);
     if (k + 1 > nT) break;
-    iteration(k + 1, sT1, sP1, sT0, sT2, sP2);
+    iteration(k + 1, sT2, sP2, sT1, sT0, sP0);
     if (k + 2 > nT) break;
-    iteration(k + 2, sT2, sP2, sT1, sT0, sP0);
+    iteration(k + 2, sT0, sP0, sT2, sT1, sP1);
   }
 
   if (!active) return;
@@ -993,12 +1048,27 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
     }
     ring_barrier();
   };
-  for (int k = 0; k <= nt; k += 3) {
-    iteration(k, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
+  auto clean_iteration = [&](int k, const uint4 *t, const uint4 *tp, uint4 *tn, int4 *pn,
+                             uint4 *an) {
+    if (k + 1 < nt) copy(k + 1, tn, pn, an);
+    if (active) steady_step(t, tp + PK_FRAGS * PFRAG, zero, qf, s, pb, o, sm, c, lane);
+    ring_barrier();
+  };
+  // tile 0; the tiles 1 .. nclean_t - 1 wholly below n_clean in whole rounds
+  // of three; the rest on the general path.  Tile k is in buffer k % 3.
+  iteration(0, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
+  int k = 1;
+  for (; k + 2 < nclean_t; k += 3) {
+    clean_iteration(k, sT1, sT0, sT2, sP2, sA2);
+    clean_iteration(k + 1, sT2, sT1, sT0, sP0, sA0);
+    clean_iteration(k + 2, sT0, sT2, sT1, sP1, sA1);
+  }
+  for (; k <= nt; k += 3) {
+    iteration(k, sT1, sP1, sA1, sT0, sT2, sP2, sA2);
     if (k + 1 > nt) break;
-    iteration(k + 1, sT1, sP1, sA1, sT0, sT2, sP2, sA2);
+    iteration(k + 1, sT2, sP2, sA2, sT1, sT0, sP0, sA0);
     if (k + 2 > nt) break;
-    iteration(k + 2, sT2, sP2, sA2, sT1, sT0, sP0, sA0);
+    iteration(k + 2, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
   }
 
   if (!active) return;

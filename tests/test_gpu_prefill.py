@@ -48,7 +48,7 @@ METHODS = ["dense", "gathered"]
 
 @pytest.mark.parametrize("method", METHODS)
 @pytest.mark.parametrize("b,s,hkv,g", [(2, 200, 2, 4), (1, 97, 1, 1), (1, 130, 2, 2), (1, 150, 1, 5),
-                                       (2, 64, 1, 8), (1, 1, 1, 4), (1, 33, 3, 4)])
+                                       (2, 64, 1, 8), (1, 1, 1, 4), (1, 33, 3, 4), (1, 385, 1, 4)])
 def test_prefill_small_all_rows(gpu, b, s, hkv, g, method):
     w, (q, k, v, logit) = _inputs(b, s, hkv, g, seed=5100 + s + g)
     out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16, method=method).cpu()

@@ -31,6 +31,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 METRIC = "DMS decode-attn tokens/s and KV GB/s (% HBM peak) at CR=8, Qwen3-8B shape"
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_qwen3_8b_cr8_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "decode_attention_learned_amd", "csrc", "decode_mfma.hip")
+PREFILL_PMC_FILE = os.path.join(ROOT, "profiles", "prefill_8k_traffic.json")
+PREFILL_SRC = os.path.join(ROOT, "decode_attention_learned_amd", "csrc", "prefill.hip")
 
 
 def log(*a):
@@ -240,7 +242,10 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
         "visible_pair_tflop": round(visible / 1e12, 4),
         "roofline": {"bound": "mfma", "kernel": "k_prefill_pack + k_prefill", "achieved": round(tflops, 1),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": prefill_traffic_from_profile(),
+                     "algorithmic_bytes_per_call": prefill_algorithmic_bytes(
+                         w.batch, s_len, w.q_heads, w.kv_heads, d)},
         "relaxed": {"ms": round(ms_r, 4), "temperature": 1.0, "noise": "logistic",
                     "causal_tflops": round(causal / (ms_r * 1e-3) / 1e12, 1),
                     "frac": round(causal / (ms_r * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
@@ -431,18 +436,43 @@ def chunked_prefill_leg(name: str = "prefill_8k", chunk: int = 512, iters: int =
             "tokens_per_s": round(w.batch * chunk / (ms * 1e-3), 1)}
 
 
-def traffic_from_profile(bytes_alg_per_launch: float):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    or None if there is none or the kernel source changed since it was taken."""
-    if not os.path.exists(PMC_FILE):
+def _profile_record(path: str, src: str):
+    """A committed rocprofv3 counter summary, or None if there is none or the
+    kernel source changed since it was taken."""
+    if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(PMC_FILE))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != src_hash(DECODE_SRC):
+    if rec.get("kernel_source_sha256_16") != src_hash(src):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def traffic_from_profile(bytes_alg_per_launch: float):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary."""
+    rec = _profile_record(PMC_FILE, DECODE_SRC)
+    return rec.get("hbm_bytes_per_launch") if rec else None
+
+
+def prefill_traffic_from_profile():
+    """HBM bytes per dense prefill call (pack pass + attention kernel) from the
+    committed rocprofv3 counter summary."""
+    rec = _profile_record(PREFILL_PMC_FILE, PREFILL_SRC)
+    return rec.get("hbm_bytes_per_call") if rec else None
+
+
+def prefill_algorithmic_bytes(batch: int, seq_len: int, q_heads: int, kv_heads: int, d: int) -> int:
+    """Bytes a dense prefill call cannot avoid moving through HBM (bf16 inputs,
+    fp32 output): the pack pass reads K, V and the logits and writes the two
+    packed copies and the masks; the attention kernel reads Q, each packed
+    copy once, and writes the output."""
+    kv = batch * seq_len * kv_heads * d * 2 * 2          # K and V, bf16
+    small = batch * seq_len * kv_heads * 4 * 2          # logits in, masks out
+    q = batch * seq_len * q_heads * d * 2
+    o = batch * seq_len * q_heads * d * 4
+    return kv + 2 * kv + small + q + 2 * kv + o
 
 
 def calibrate(gib: float) -> dict:

@@ -52,9 +52,10 @@
 // read from a second packed copy in which the keys the hard rule masks out
 // have zero rows (they are invisible there; zero operands cost the matrix
 // cores less power).  The few tiles on the diagonal band ("near") come from
-// the plain copy and apply the full rule per element in phase 2.  The far
-// tiles after the first run in a loop of their own, whose body has no test
-// on the tile index.
+// the plain copy and apply the full rule per element in phase 2.  Far
+// tiles from tile 1 on run, in whole rounds of three (one per buffer), in a
+// loop of their own whose body has no test on the tile index; tile 0 and
+// the tiles after the last whole round take the general path.
 //
 // Softmax reference.  Each query keeps a reference m (raw score units) that
 // moves only when a score exceeds it by more than kLazy / c (c = scale *

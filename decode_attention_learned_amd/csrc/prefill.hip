@@ -208,6 +208,41 @@ __device__ __forceinline__ void pv_tile(const uint4 *__restrict__ sv, const uint
   }
 }
 
+// Write a wave's output (32 query rows of one head, o / l) through LDS so that
+// each store instruction covers two whole 512-byte rows.  `stage` holds 16
+// rows of 128 floats (8 KB) for this wave; row r is rotated by 4 r floats so
+// that the sixteen rows of a write land in different banks.
+__device__ __forceinline__ void store_rows(const floatx4 (&o)[PDT][2], const Softmax &sm,
+                                           float *stage, float *out, size_t row0, size_t rstride,
+                                           int i0, int S, int lane) {
+  const int col = lane & 15, quad = lane >> 4;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float l = sm.l[qt];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < PDT; ++dt)
+      *reinterpret_cast<floatx4 *>(stage + col * 128 + ((dt * 16 + quad * 4 + 4 * col) & 127)) =
+          o[dt][qt] * inv;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int half = lane >> 5, c4 = (lane & 31) * 4;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const int row = r + half;
+      const int i = i0 + 16 * qt + row;
+      const floatx4 v = *reinterpret_cast<const floatx4 *>(stage + row * 128 + ((c4 + 4 * row) & 127));
+      if (i < S) *reinterpret_cast<floatx4 *>(out + row0 + size_t(i) * rstride + c4) = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 // ---- tile ring -----------------------------------------------------------
 // Copy N uint4 (a 16 KB packed tile, or half of one) into LDS with the load
 // unit: wave w copies uint4 256 r + 64 w + lane, one contiguous 1 KB run per
@@ -601,20 +636,9 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill(
   }
 
   if (!active) return;
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    float l = sm.l[qt];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int i = qi0 + 16 * qt + col;
-    if (i < S) {
-      float *op = out + ((size_t(b) * S + i) * Hq + hq) * PD + quad * 4;
-#pragma unroll
-      for (int dt = 0; dt < PDT; ++dt)
-        *reinterpret_cast<floatx4 *>(op + dt * 16) = o[dt][qt] * inv;
-    }
-  }
+  // the ring buffers are free: every wave has passed the last barrier
+  float *stage = reinterpret_cast<float *>(wave < 2 ? sT0 : sT1) + (wave & 1) * (16 * 128);
+  store_rows(o, sm, stage, out, (size_t(b) * S * Hq + hq) * PD, size_t(Hq) * PD, qi0, S, lane);
 }
 
 
@@ -868,20 +892,9 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill_gathered(
   }
 
   if (!active) return;
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    float l = sm.l[qt];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int i = qi0 + 16 * qt + col;
-    if (i < S) {
-      float *op = out + ((size_t(b) * S + i) * Hq + hq) * PD + quad * 4;
-#pragma unroll
-      for (int dt = 0; dt < PDT; ++dt)
-        *reinterpret_cast<floatx4 *>(op + dt * 16) = o[dt][qt] * inv;
-    }
-  }
+  // the ring buffers are free: every wave has passed the last barrier
+  float *stage = reinterpret_cast<float *>(wave < 2 ? sT0 : sT1) + (wave & 1) * (16 * 128);
+  store_rows(o, sm, stage, out, (size_t(b) * S * Hq + hq) * PD, size_t(Hq) * PD, qi0, S, lane);
 }
 
 hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, const void *v,
@@ -1073,20 +1086,9 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
   }
 
   if (!active) return;
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    float l = sm.l[qt];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int cq = c0 + 16 * qt + col;
-    if (cq < C) {
-      float *op = out + ((size_t(b) * C + cq) * Hq + hq) * PD + quad * 4;
-#pragma unroll
-      for (int dt = 0; dt < PDT; ++dt)
-        *reinterpret_cast<floatx4 *>(op + dt * 16) = o[dt][qt] * inv;
-    }
-  }
+  // the ring buffers are free: every wave has passed the last barrier
+  float *stage = reinterpret_cast<float *>(wave < 2 ? sT0 : sT1) + (wave & 1) * (16 * 128);
+  store_rows(o, sm, stage, out, (size_t(b) * C * Hq + hq) * PD, size_t(Hq) * PD, c0, C, lane);
 }
 
 hipError_t launch_chunk_attn(const dms_shape &s, const dms_cache &c, const void *q, int n_query,

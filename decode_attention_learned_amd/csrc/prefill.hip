@@ -57,6 +57,10 @@
 // loop of their own whose body has no test on the tile index; tile 0 and
 // the tiles after the last whole round take the general path.
 //
+// Output.  After the last tile each wave stages its 32 fp32 output rows in
+// the (then idle) ring buffers, so that one store instruction writes two
+// whole 512-byte rows.
+//
 // Softmax reference.  Each query keeps a reference m (raw score units) that
 // moves only when a score exceeds it by more than kLazy / c (c = scale *
 // log2 e), so every exponent is at most kLazy.  The result does not depend on

@@ -166,13 +166,19 @@ def cpu_baseline(w, seconds: float = 12.0, threads: int = 1) -> dict:
 
 
 def _time_calls(fn, iters: int) -> float:
-    """Mean milliseconds of fn() over `iters` calls, HIP events on the current stream."""
+    """Mean milliseconds of fn() over `iters` calls, HIP events on the current stream.
+
+    One untimed call is queued right before the timed ones, so that the stream
+    is busy when the first start event is recorded: otherwise the first
+    interval would also hold the time the idle GPU waits for the host to
+    queue that call's kernels."""
     import torch
 
     for _ in range(2):
         fn()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    fn()
     for a, b in evs:
         a.record()
         fn()

@@ -162,7 +162,7 @@ def cpu_baseline(w, seconds: float = 12.0, threads: int = 1) -> dict:
             "sample": f"1 of {w.batch} sequences ({sample.kv_heads} KV heads x G={sample.group}, "
                       f"context {sample.context}), {steps} decode steps in {dt:.1f} s, "
                       f"float64 NumPy with BLAS limited to {threads} thread(s); tokens/s is the "
-                      "same for the full batch (each of its steps is 64 such sequences)"}
+                      f"same for the full batch (each of its steps is {w.batch} such sequences)"}
 
 
 def _time_calls(fn, iters: int) -> float:

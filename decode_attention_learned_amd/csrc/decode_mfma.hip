@@ -70,12 +70,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 template <int D>
 __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
     int units, int hkv, int G, int window, int maxp, float scale_log2, int nq, int c0, int C,
-    const uint16_t *__restrict__ q, uint16_t *k_pages, uint16_t *v_pages,
-    const int32_t *__restrict__ page_table, int32_t *slot_pos, uint8_t *slot_alpha,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pages,
+    const uint16_t *__restrict__ v_pages, const int32_t *__restrict__ page_table,
+    const int32_t *__restrict__ slot_pos, const uint8_t *__restrict__ slot_alpha,
     const int32_t *__restrict__ n_slots, const int32_t *__restrict__ n_clean_arr,
     const int32_t *__restrict__ seq_len, int32_t *__restrict__ plan,
-    const int32_t *__restrict__ append_base, const uint16_t *__restrict__ k_new,
-    const uint16_t *__restrict__ v_new, const float *__restrict__ logit_new,
     float2 *__restrict__ part_ml, float *__restrict__ part_o, float *__restrict__ out) {
   constexpr int KSTEPS = D / 32;  // QK products per 16-slot tile
   constexpr int DTILES = D / 16;  // PV products per group
@@ -89,28 +88,6 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
   const int32_t *row = page_table + size_t(u) * maxp;
 
   const int tid = threadIdx.x;
-  // The step's token, reserved by the allocation launch (n_new = 1), written
-  // here by the unit's last chunk, which holds the newest slot: the decision
-  // and position beside the slot, the key as 16-byte pieces and the value
-  // element by element, as the append's write kernel lays them out.  Each
-  // wave waits for its stores; the barrier ahead of the first page-id read
-  // orders them before any load of the slot.
-  if (k_new != nullptr && c == ci.first + ci.nch - 1) {
-    const int base = append_base[u];
-    if (base >= 0) {  // a refused unit keeps no token
-      const int page = row[base / kPage], off = base % kPage;
-      const size_t tok = size_t(b) * hkv + h;
-      if (tid < D / 8)
-        *reinterpret_cast<uint4 *>(k_pages + size_t(page) * kPage * D + key_index(off, tid * 8, D)) =
-            *reinterpret_cast<const uint4 *>(k_new + tok * D + tid * 8);
-      if (tid < D) v_pages[size_t(page) * kPage * D + value_index(off, tid, D)] = v_new[tok * D + tid];
-      if (tid == 0) {
-        slot_pos[size_t(page) * kPage + off] = t;
-        slot_alpha[size_t(page) * kPage + off] = evict_decision(logit_new[tok]) ? 1 : 0;
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have completed
-    }
-  }
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
   const int col = lane & 15;  // (query, head) column in B and C operands, row index in A
@@ -322,7 +299,7 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
 
 bool launch_decode_mfma_part(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                              float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
-                             int nq, int c0, int C, const DecodeFill *fill) {
+                             int nq, int c0, int C) {
   auto args = [&](auto kern) {
     const int rcols = nq * s.group < kCombineCols ? nq * s.group : kCombineCols;
     const size_t lds = size_t(kMfmaWaves) * rcols * (s.head_dim + 4) * sizeof(float);
@@ -332,12 +309,9 @@ bool launch_decode_mfma_part(const dms_shape &s, const dms_cache &c, const void 
     hipLaunchKernelGGL(kern, dim3(w.max_chunks), dim3(kMfmaThreads), lds, st, units_of(s), s.kv_heads,
                        s.group, s.window,
                        s.max_pages_per_unit, scale_log2, nq, c0, C, static_cast<const uint16_t *>(q),
-                       static_cast<uint16_t *>(c.k_pages), static_cast<uint16_t *>(c.v_pages),
-                       c.page_table, c.slot_pos, c.slot_alpha, c.n_slots, c.n_clean, c.seq_len,
-                       c.plan, c.append_base,
-                       fill ? static_cast<const uint16_t *>(fill->k_new) : nullptr,
-                       fill ? static_cast<const uint16_t *>(fill->v_new) : nullptr,
-                       fill ? fill->logit : nullptr,
+                       static_cast<const uint16_t *>(c.k_pages),
+                       static_cast<const uint16_t *>(c.v_pages), c.page_table, c.slot_pos,
+                       c.slot_alpha, c.n_slots, c.n_clean, c.seq_len, c.plan,
                        reinterpret_cast<float2 *>(ws + w.part_ml),
                        reinterpret_cast<float *>(ws + w.part_o), out);
   };
@@ -350,7 +324,7 @@ bool launch_decode_mfma_part(const dms_shape &s, const dms_cache &c, const void 
 
 bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                         float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
-                        int n_query, const DecodeFill *fill) {
+                        int n_query) {
   if (s.kv_dtype != DMS_KV_BF16 || s.group > 16) return false;
   const char *force = getenv("DMS_DECODE_KERNEL");
   if (n_query == 1 && force && force[0] == 'g') return false;  // "generic": the VALU kernel
@@ -358,9 +332,7 @@ bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, f
   const int per = 16 / s.group;
   for (int c0 = 0; c0 < n_query; c0 += per) {
     const int nq = n_query - c0 < per ? n_query - c0 : per;
-    if (!launch_decode_mfma_part(s, c, q, out, scale_log2, w, ws, st, nq, c0, n_query,
-                                 n_query == 1 ? fill : nullptr))
-      return false;
+    if (!launch_decode_mfma_part(s, c, q, out, scale_log2, w, ws, st, nq, c0, n_query)) return false;
   }
   return true;
 }

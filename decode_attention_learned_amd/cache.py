@@ -125,6 +125,40 @@ class DmsCache:
             self.shape, self.cache, q, out, scale, self.workspace, self.workspace_bytes, _stream()))
         return out
 
+    def step(self, k: torch.Tensor, v: torch.Tensor, logit: torch.Tensor, q: torch.Tensor,
+             out: torch.Tensor | None = None, sm_scale: float | None = None) -> torch.Tensor:
+        """One decode step: append one token per sequence (k, v [B, 1, Hkv, D],
+        logit [B, 1, Hkv]) and attend its query q [B, Hq, D] -> out [B, Hq, D]
+        float32.  Equivalent to append() then decode(), with one launch less
+        (dms_append_reserve + dms_decode_attn_fill): the same cache state, and
+        outputs equal to rounding (the new token's weight stays float32)."""
+        kshape = (self.batch, 1, self.kv_heads, self.head_dim)
+        _need(k, "k", self.dtype, kshape, self.device)
+        _need(v, "v", self.dtype, kshape, self.device)
+        _need(logit, "logit", torch.float32, kshape[:3], self.device)
+        qshape = (self.batch, self.kv_heads * self.group, self.head_dim)
+        _need(q, "q", self.dtype, qshape, self.device)
+        if out is None:
+            out = torch.empty(qshape, dtype=torch.float32, device=self.device)
+        _need(out, "out", torch.float32, qshape, self.device)
+        scale = 1.0 / math.sqrt(self.head_dim) if sm_scale is None else sm_scale
+        self.reserve()
+        self.fill_and_decode(k, v, logit, q, out, scale)
+        return out
+
+    def reserve(self) -> None:
+        """First half of step(): slots, pages and counts for one token per sequence."""
+        lib.check("dms_append_reserve", lib.dms_append_reserve(self.shape, self.cache, _stream()))
+
+    def fill_and_decode(self, k: torch.Tensor, v: torch.Tensor, logit: torch.Tensor,
+                        q: torch.Tensor, out: torch.Tensor, sm_scale: float) -> torch.Tensor:
+        """Second half of step() (argument checks are step()'s): attend with the
+        reserved token included, and write it to its slot."""
+        lib.check("dms_decode_attn_fill", lib.dms_decode_attn_fill(
+            self.shape, self.cache, k, v, logit, q, out, sm_scale, self.workspace,
+            self.workspace_bytes, _stream()))
+        return out
+
     def share_prefix(self, src_seq: int, dst_first: int, n_dst: int) -> None:
         """Sequences dst_first .. dst_first + n_dst - 1 (empty) take over the state
         of sequence src_seq, sharing its clean full pages (dms_share_prefix)."""

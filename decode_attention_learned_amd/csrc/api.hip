@@ -103,6 +103,30 @@ int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *
   return from_hip(dms::launch_decode(*shape, *cache, q, out, sm_scale, workspace, stream));
 }
 
+int dms_append_reserve(const dms_shape *shape, const dms_cache *cache, hipStream_t stream) {
+  int rc = dms_check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_cache(shape, cache))) return rc;
+  return from_hip(dms::launch_append_alloc(*shape, *cache, 1, stream));
+}
+
+int dms_decode_attn_fill(const dms_shape *shape, const dms_cache *cache, const void *k_new,
+                         const void *v_new, const float *logit, const void *q, float *out,
+                         float sm_scale, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  int rc = dms_check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_cache(shape, cache))) return rc;
+  if (!k_new || !v_new || !logit || !q || !out || !workspace) return DMS_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(out) ||
+      !aligned16(workspace))
+    return DMS_EINVAL;
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
+  if (workspace_bytes < dms_decode_workspace_bytes(shape)) return DMS_EWORKSPACE;
+  const dms::DecodeFill fill{k_new, v_new, logit};
+  return from_hip(dms::launch_decode(*shape, *cache, q, out, sm_scale, workspace, stream, &fill));
+}
+
 int dms_share_prefix(const dms_shape *shape, const dms_cache *cache, int32_t src_seq,
                      int32_t dst_first, int32_t n_dst, hipStream_t stream) {
   int rc = dms_check_shape(shape);

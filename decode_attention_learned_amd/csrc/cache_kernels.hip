@@ -211,14 +211,22 @@ __global__ __launch_bounds__(256) void k_append_write(
   }
 }
 
-hipError_t launch_append(const dms_shape &s, const dms_cache &c, const void *k_new,
-                         const void *v_new, const float *logit, int n_new, hipStream_t st) {
-  const int units = units_of(s);
-  hipLaunchKernelGGL(k_append_alloc, dim3(1), dim3(kAllocThreads), 0, st, units, s.batch,
+hipError_t launch_append_alloc(const dms_shape &s, const dms_cache &c, int n_new, hipStream_t st) {
+  hipLaunchKernelGGL(k_append_alloc, dim3(1), dim3(kAllocThreads), 0, st, units_of(s), s.batch,
                      s.max_pages_per_unit, n_new, c.page_table, c.n_slots, c.append_base,
                      c.seq_len, c.free_list, c.free_top, c.status, c.plan);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const dms_shape &s, const dms_cache &c, const void *k_new,
+                         const void *v_new, const float *logit, int n_new, hipStream_t st) {
+  const hipError_t e = launch_append_alloc(s, c, n_new, st);
+  return e != hipSuccess ? e : launch_append_write(s, c, k_new, v_new, logit, n_new, st);
+}
+
+hipError_t launch_append_write(const dms_shape &s, const dms_cache &c, const void *k_new,
+                               const void *v_new, const float *logit, int n_new, hipStream_t st) {
+  const int units = units_of(s);
   const dim3 grid(units, (n_new + kPage - 1) / kPage);
   const int D = s.head_dim;
   if (s.kv_dtype == DMS_KV_BF16) {

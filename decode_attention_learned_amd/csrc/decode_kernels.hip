@@ -194,18 +194,24 @@ static bool dispatch_group(const dms_shape &s, const dms_cache &c, const E *q, f
 
 bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                         float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
-                        int n_query);
+                        int n_query, const DecodeFill *fill = nullptr);
 
 // The decode grid has one workgroup per possible chunk (max_chunks_of(units));
-// workgroups past the plan's chunk count exit at once.
+// workgroups past the plan's chunk count exit at once.  With `fill`, the
+// matrix-core kernel writes the reserved token itself; the vector kernels
+// take it from a write launch ahead of them.
 hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, float *out,
-                         float sm_scale, void *wsv, hipStream_t st) {
+                         float sm_scale, void *wsv, hipStream_t st, const DecodeFill *fill) {
   const DecodeWorkspace w = decode_workspace_layout(units_of(s), s.group, s.head_dim);
   char *ws = static_cast<char *>(wsv);
   const float scale_log2 = sm_scale * 1.4426950408889634f;  // exp(x) = exp2(x * log2 e)
   bool done = false;
+  if (s.kv_dtype == DMS_KV_BF16) done = launch_decode_mfma(s, c, q, out, scale_log2, w, ws, st, 1, fill);
+  if (!done && fill) {
+    const hipError_t e = launch_append_write(s, c, fill->k_new, fill->v_new, fill->logit, 1, st);
+    if (e != hipSuccess) return e;
+  }
   if (s.kv_dtype == DMS_KV_BF16) {
-    done = launch_decode_mfma(s, c, q, out, scale_log2, w, ws, st, 1);
     if (!done)
       done = s.head_dim == 64
                  ? dispatch_group<uint16_t, 64>(s, c, static_cast<const uint16_t *>(q), out, scale_log2, w, ws, st)

@@ -70,11 +70,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 template <int D>
 __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
     int units, int hkv, int G, int window, int maxp, float scale_log2, int nq, int c0, int C,
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pages,
-    const uint16_t *__restrict__ v_pages, const int32_t *__restrict__ page_table,
-    const int32_t *__restrict__ slot_pos, const uint8_t *__restrict__ slot_alpha,
+    const uint16_t *__restrict__ q, uint16_t *k_pages, uint16_t *v_pages,
+    const int32_t *__restrict__ page_table, int32_t *slot_pos, uint8_t *slot_alpha,
     const int32_t *__restrict__ n_slots, const int32_t *__restrict__ n_clean_arr,
     const int32_t *__restrict__ seq_len, int32_t *__restrict__ plan,
+    const int32_t *__restrict__ append_base, const uint16_t *__restrict__ k_new,
+    const uint16_t *__restrict__ v_new, const float *__restrict__ logit_new,
     float2 *__restrict__ part_ml, float *__restrict__ part_o, float *__restrict__ out) {
   constexpr int KSTEPS = D / 32;  // QK products per 16-slot tile
   constexpr int DTILES = D / 16;  // PV products per group
@@ -83,11 +84,32 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
   ChunkInfo ci;
   if (!locate_chunk(c, hkv, plan, n_slots, n_clean_arr, seq_len, L, ci)) return;
   const int u = ci.unit, b = ci.b, h = ci.h;
-  const int s_begin = ci.s_begin, s_end = ci.s_end, t = ci.t, nclean = ci.nclean;
-  const int lim = min(nclean, s_end);  // slots below lim need no liveness test
+  const int s_begin = ci.s_begin, t = ci.t, nclean = ci.nclean;
   const int32_t *row = page_table + size_t(u) * maxp;
-
   const int tid = threadIdx.x;
+
+  // The step's token (decode with fill): its slot, reserved by the
+  // allocation launch (n_new = 1), is the unit's newest and lies in the
+  // unit's last chunk.  That chunk streams the slots before it; the token's
+  // key and value are staged in LDS here by the load unit (no registers, no
+  // wait), enter the combine below as one more softmax term, and are written
+  // to the token's slot after the stream.
+  __shared__ __align__(16) uint16_t s_tok[2 * D];  // key, then value
+  __shared__ float s_tm[16];                       // the token's score per column (log2 units)
+  const int tok_slot = k_new != nullptr && c == ci.first + ci.nch - 1 ? append_base[u] : -1;
+  const bool own_tok = tok_slot >= 0;  // a refused unit has no token
+  const size_t tok = size_t(b) * hkv + h;  // [B][1][Hkv]
+  if (own_tok) {
+    if (tid < D / 8)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(k_new + tok * D) + tid,
+                                       reinterpret_cast<uint4 *>(s_tok), 16, 0, 0);
+    else if (tid >= kWave && tid < kWave + D / 8)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(v_new + tok * D) + (tid - kWave),
+                                       reinterpret_cast<uint4 *>(s_tok + D), 16, 0, 0);
+  }
+  const int s_end = own_tok ? tok_slot : ci.s_end;  // the token's slot is not streamed
+  const int lim = min(nclean, s_end);  // slots below lim need no liveness test
+
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
   const int col = lane & 15;  // (query, head) column in B and C operands, row index in A
@@ -242,10 +264,53 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
       process(r, gi);
     }
   }
+  // The token to its slot, by waves 0 (key, position, decision) and 1
+  // (value), after the stream: the staging copies issued before it have long
+  // landed.  (Ahead of the stream, the wait for them delays the start of two
+  // waves and costs more than the launch it saves; inside the group loop the
+  // compiler spills.)
+  if (own_tok && wave < 2) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's staging copy has landed
+    const int page = row[tok_slot / kPage], off = tok_slot % kPage;
+    if (wave == 0) {
+      if (lane < D / 8)
+        *reinterpret_cast<uint4 *>(k_pages + size_t(page) * kPage * D + key_index(off, lane * 8, D)) =
+            *reinterpret_cast<const uint4 *>(s_tok + lane * 8);
+      if (lane == 0) {
+        slot_pos[size_t(page) * kPage + off] = t;
+        // the decision: sigmoid(logit) > 1/2  <=>  logit > 0 (NaN keeps)
+        slot_alpha[size_t(page) * kPage + off] = evict_decision(logit_new[tok]) ? 1 : 0;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < D / kWave; ++e)
+        v_pages[size_t(page) * kPage * D + value_index(off, lane + kWave * e, D)] =
+            s_tok[D + lane + kWave * e];
+    }
+  }
 
   // combine the waves of this workgroup, kCombineCols columns at a time
   // (s_o: [waves][kCombineCols][D + 4] in dynamic LDS, so that a launch with
   // 16 columns needs no more LDS than four resident workgroups per CU allow)
+  if (own_tok && wave == 0) {
+    // the token's score q . k_new for column `col` (log2 units): this lane's
+    // 32 dims, then the four quads
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const uint4 kf = *reinterpret_cast<const uint4 *>(s_tok + ks * 32 + quad * 8);
+      const uint32_t qa[4] = {qb[ks].x, qb[ks].y, qb[ks].z, qb[ks].w};
+      const uint32_t ka[4] = {kf.x, kf.y, kf.z, kf.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(__uint_as_float(qa[e] << 16), __uint_as_float(ka[e] << 16), acc);
+        acc = fmaf(__uint_as_float(qa[e] & 0xffff0000u), __uint_as_float(ka[e] & 0xffff0000u), acc);
+      }
+    }
+    acc += __shfl_xor(acc, 16, kWave);
+    acc += __shfl_xor(acc, 32, kWave);
+    if (quad == 0) s_tm[col] = acc * scale_log2;
+  }
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
   __shared__ float s_m[kMfmaWaves][16], s_l[kMfmaWaves][16];
@@ -272,6 +337,7 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
       float M = s_m[0][g];
 #pragma unroll
       for (int w = 1; w < kMfmaWaves; ++w) M = fmaxf(M, s_m[w][g]);
+      if (own_tok) M = fmaxf(M, s_tm[g]);
       float Ls = 0.f, O = 0.f;
       if (M != -INFINITY) {
 #pragma unroll
@@ -281,6 +347,11 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
           const float f = exp2f(mw - M);
           Ls = fmaf(s_l[w][g], f, Ls);
           O = fmaf(s_o[(w * rcols + g - r0) * ostride + d], f, O);
+        }
+        if (own_tok) {  // the token: weight 2^(score - M), value v_new
+          const float f = exp2f(s_tm[g] - M);
+          Ls += f;
+          O = fmaf(__uint_as_float(uint32_t(s_tok[D + d]) << 16), f, O);
         }
       }
       if (ci.nch == 1) {
@@ -299,7 +370,7 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
 
 bool launch_decode_mfma_part(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                              float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
-                             int nq, int c0, int C) {
+                             int nq, int c0, int C, const DecodeFill *fill) {
   auto args = [&](auto kern) {
     const int rcols = nq * s.group < kCombineCols ? nq * s.group : kCombineCols;
     const size_t lds = size_t(kMfmaWaves) * rcols * (s.head_dim + 4) * sizeof(float);
@@ -309,9 +380,12 @@ bool launch_decode_mfma_part(const dms_shape &s, const dms_cache &c, const void 
     hipLaunchKernelGGL(kern, dim3(w.max_chunks), dim3(kMfmaThreads), lds, st, units_of(s), s.kv_heads,
                        s.group, s.window,
                        s.max_pages_per_unit, scale_log2, nq, c0, C, static_cast<const uint16_t *>(q),
-                       static_cast<const uint16_t *>(c.k_pages),
-                       static_cast<const uint16_t *>(c.v_pages), c.page_table, c.slot_pos,
-                       c.slot_alpha, c.n_slots, c.n_clean, c.seq_len, c.plan,
+                       static_cast<uint16_t *>(c.k_pages), static_cast<uint16_t *>(c.v_pages),
+                       c.page_table, c.slot_pos, c.slot_alpha, c.n_slots, c.n_clean, c.seq_len,
+                       c.plan, c.append_base,
+                       fill ? static_cast<const uint16_t *>(fill->k_new) : nullptr,
+                       fill ? static_cast<const uint16_t *>(fill->v_new) : nullptr,
+                       fill ? fill->logit : nullptr,
                        reinterpret_cast<float2 *>(ws + w.part_ml),
                        reinterpret_cast<float *>(ws + w.part_o), out);
   };
@@ -324,7 +398,7 @@ bool launch_decode_mfma_part(const dms_shape &s, const dms_cache &c, const void 
 
 bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                         float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
-                        int n_query) {
+                        int n_query, const DecodeFill *fill) {
   if (s.kv_dtype != DMS_KV_BF16 || s.group > 16) return false;
   const char *force = getenv("DMS_DECODE_KERNEL");
   if (n_query == 1 && force && force[0] == 'g') return false;  // "generic": the VALU kernel
@@ -332,7 +406,9 @@ bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, f
   const int per = 16 / s.group;
   for (int c0 = 0; c0 < n_query; c0 += per) {
     const int nq = n_query - c0 < per ? n_query - c0 : per;
-    if (!launch_decode_mfma_part(s, c, q, out, scale_log2, w, ws, st, nq, c0, n_query)) return false;
+    if (!launch_decode_mfma_part(s, c, q, out, scale_log2, w, ws, st, nq, c0, n_query,
+                                 n_query == 1 ? fill : nullptr))
+      return false;
   }
   return true;
 }

@@ -81,10 +81,20 @@ inline DecodeWorkspace decode_workspace_layout(int units, int group, int head_di
 hipError_t launch_reset(const dms_shape &s, const dms_cache &c, hipStream_t st);
 hipError_t launch_append(const dms_shape &s, const dms_cache &c, const void *k_new,
                          const void *v_new, const float *logit, int n_new, hipStream_t st);
+// the two parts of launch_append: slots, pages and counts; then decisions and K/V
+hipError_t launch_append_alloc(const dms_shape &s, const dms_cache &c, int n_new, hipStream_t st);
+hipError_t launch_append_write(const dms_shape &s, const dms_cache &c, const void *k_new,
+                               const void *v_new, const float *logit, int n_new, hipStream_t st);
+// The token that launch_append_alloc(n_new = 1) reserved in every unit, for a
+// decode launch to write (decision, K, V) before it attends.
+struct DecodeFill {
+  const void *k_new, *v_new;  // [B][1][Hkv][D]
+  const float *logit;         // [B][1][Hkv]
+};
 hipError_t launch_compact(const dms_shape &s, const dms_cache &c, hipStream_t st);
 hipError_t launch_plan(const dms_shape &s, const dms_cache &c, hipStream_t st);
 hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, float *out,
-                         float sm_scale, void *ws, hipStream_t st);
+                         float sm_scale, void *ws, hipStream_t st, const DecodeFill *fill = nullptr);
 hipError_t launch_share(const dms_shape &s, const dms_cache &c, int src, int dst_first, int n_dst,
                         hipStream_t st);
 hipError_t launch_release(const dms_shape &s, const dms_cache &c, int first, int n, hipStream_t st);

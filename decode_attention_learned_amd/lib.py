@@ -37,6 +37,8 @@ EXPORTS = (
     "dms_release",
     "dms_decode_workspace_bytes",
     "dms_decode_attn",
+    "dms_append_reserve",
+    "dms_decode_attn_fill",
     "dms_decode_multi_workspace_bytes",
     "dms_decode_attn_multi",
     "dms_prefill_workspace_bytes",
@@ -113,6 +115,9 @@ def load() -> ctypes.CDLL:
         "dms_release": ([SP, CP, ctypes.c_int32, ctypes.c_int32, P], ctypes.c_int),
         "dms_decode_workspace_bytes": ([SP], ctypes.c_size_t),
         "dms_decode_attn": ([SP, CP, P, P, ctypes.c_float, P, ctypes.c_size_t, P], ctypes.c_int),
+        "dms_append_reserve": ([SP, CP, P], ctypes.c_int),
+        "dms_decode_attn_fill": ([SP, CP, P, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t, P],
+                                 ctypes.c_int),
         "dms_decode_multi_workspace_bytes": ([SP], ctypes.c_size_t),
         "dms_decode_attn_multi": ([SP, CP, P, ctypes.c_int32, P, ctypes.c_float, P, ctypes.c_size_t, P],
                                   ctypes.c_int),
@@ -179,6 +184,17 @@ def dms_compact(shape, cache, stream) -> int:
 def dms_decode_attn(shape, cache, q, out, sm_scale, workspace, workspace_bytes, stream) -> int:
     return load().dms_decode_attn(ctypes.byref(shape), ctypes.byref(cache), _p(q), _p(out),
                                   float(sm_scale), _p(workspace), int(workspace_bytes), stream)
+
+
+def dms_append_reserve(shape, cache, stream) -> int:
+    return load().dms_append_reserve(ctypes.byref(shape), ctypes.byref(cache), stream)
+
+
+def dms_decode_attn_fill(shape, cache, k_new, v_new, logit, q, out, sm_scale, workspace,
+                         workspace_bytes, stream) -> int:
+    return load().dms_decode_attn_fill(ctypes.byref(shape), ctypes.byref(cache), _p(k_new),
+                                       _p(v_new), _p(logit), _p(q), _p(out), float(sm_scale),
+                                       _p(workspace), int(workspace_bytes), stream)
 
 
 def prefill_workspace_bytes(shape: DmsShape, seq_len: int) -> int:

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DMS_ABI_VERSION 2
+#define DMS_ABI_VERSION 3
 #define DMS_PAGE_SIZE 64
 
 /* host-side return codes */
@@ -187,6 +187,37 @@ size_t dms_decode_workspace_bytes(const dms_shape *shape);
  */
 int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *q, float *out,
                     float sm_scale, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One decode step in two calls, for callers that attend right after
+ * appending one token per sequence: together equivalent to
+ * dms_append(n_new = 1) followed by dms_decode_attn, with one launch less.
+ * The cache state afterwards is the same, byte for byte (page ids aside,
+ * which depend on the free stack's order).  The outputs agree to rounding:
+ * on bf16 caches the decode launch takes the new token as one more softmax
+ * term, its weight kept in float32 where the cached tokens' weights are
+ * rounded to bf16 for the matrix cores; other caches give identical outputs.
+ *
+ * dms_append_reserve: the slot, page and count part of dms_append(n_new = 1)
+ * (positions seq_len[b], pages from the free stack in unit order, refusal
+ * and status flags as there; decode plan rebuilt).  The reserved slots hold
+ * no token yet: the next call on the cache (same stream) must be
+ * dms_decode_attn_fill, and no other call may come in between.
+ *
+ * dms_decode_attn_fill: attends as dms_decode_attn, the new token included
+ * (atlas.scime.ai summary, "Approach": a query always sees its own token),
+ * and writes the token reserved in every unit that was not refused into its
+ * slot, with the decision alpha = logit > 0 as dms_append.
+ *   k_new, v_new  [B][1][Hkv][D] in kv_dtype;  logit [B][1][Hkv] float32
+ *   q, out, sm_scale, workspace as for dms_decode_attn
+ * Host errors as for dms_decode_attn, plus DMS_EINVAL for a null k_new,
+ * v_new or logit, or a k_new or v_new that is not 16-byte aligned.
+ */
+int dms_append_reserve(const dms_shape *shape, const dms_cache *cache, hipStream_t stream);
+int dms_decode_attn_fill(const dms_shape *shape, const dms_cache *cache, const void *k_new,
+                         const void *v_new, const float *logit, const void *q, float *out,
+                         float sm_scale, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /*
  * Share a sequence's prompt with other sequences (several reasoning threads

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strerror(L):
-    assert lib.version() == 2
+    assert lib.version() == 3
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(lib.strerror(code), str)
 

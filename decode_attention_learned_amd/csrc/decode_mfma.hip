@@ -99,13 +99,16 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
   const int tok_slot = k_new != nullptr && c == ci.first + ci.nch - 1 ? append_base[u] : -1;
   const bool own_tok = tok_slot >= 0;  // a refused unit has no token
   const size_t tok = size_t(b) * hkv + h;  // [B][1][Hkv]
-  if (own_tok) {
-    if (tid < D / 8)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(k_new + tok * D) + tid,
-                                       reinterpret_cast<uint4 *>(s_tok), 16, 0, 0);
-    else if (tid >= kWave && tid < kWave + D / 8)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(v_new + tok * D) + (tid - kWave),
-                                       reinterpret_cast<uint4 *>(s_tok + D), 16, 0, 0);
+  // The last wave handles the token: with a group count that is not a
+  // multiple of the wave count it has one group less than the first waves,
+  // so its token work after the stream overlaps their last group.
+  constexpr int kTokWave = kMfmaWaves - 1;
+  if (own_tok && tid >= kTokWave * kWave && tid < kTokWave * kWave + D / 8) {
+    const int piece = tid - kTokWave * kWave;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(k_new + tok * D) + piece,
+                                     reinterpret_cast<uint4 *>(s_tok), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(v_new + tok * D) + piece,
+                                     reinterpret_cast<uint4 *>(s_tok + D), 16, 0, 0);
   }
   const int s_end = own_tok ? tok_slot : ci.s_end;  // the token's slot is not streamed
   const int lim = min(nclean, s_end);  // slots below lim need no liveness test
@@ -264,37 +267,14 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
       process(r, gi);
     }
   }
-  // The token to its slot, by waves 0 (key, position, decision) and 1
-  // (value), after the stream: the staging copies issued before it have long
-  // landed.  (Ahead of the stream, the wait for them delays the start of two
-  // waves and costs more than the launch it saves; inside the group loop the
-  // compiler spills.)
-  if (own_tok && wave < 2) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's staging copy has landed
-    const int page = row[tok_slot / kPage], off = tok_slot % kPage;
-    if (wave == 0) {
-      if (lane < D / 8)
-        *reinterpret_cast<uint4 *>(k_pages + size_t(page) * kPage * D + key_index(off, lane * 8, D)) =
-            *reinterpret_cast<const uint4 *>(s_tok + lane * 8);
-      if (lane == 0) {
-        slot_pos[size_t(page) * kPage + off] = t;
-        // the decision: sigmoid(logit) > 1/2  <=>  logit > 0 (NaN keeps)
-        slot_alpha[size_t(page) * kPage + off] = evict_decision(logit_new[tok]) ? 1 : 0;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < D / kWave; ++e)
-        v_pages[size_t(page) * kPage * D + value_index(off, lane + kWave * e, D)] =
-            s_tok[D + lane + kWave * e];
-    }
-  }
-
-  // combine the waves of this workgroup, kCombineCols columns at a time
-  // (s_o: [waves][kCombineCols][D + 4] in dynamic LDS, so that a launch with
-  // 16 columns needs no more LDS than four resident workgroups per CU allow)
-  if (own_tok && wave == 0) {
-    // the token's score q . k_new for column `col` (log2 units): this lane's
-    // 32 dims, then the four quads
+  // The token, by the last wave after its stream (the staging copies issued
+  // before it have long landed): its score q . k_new per column (this lane's
+  // 32 dims, then the four quads; log2 units) for the combine, and its key,
+  // value, position and decision to its slot.  (Ahead of the stream, the wait
+  // for the staging copies delays the start of a wave and costs more than
+  // the launch it saves; inside the group loop the compiler spills.)
+  if (own_tok && wave == kTokWave) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the staging copies have landed
     float acc = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -310,6 +290,19 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
     acc += __shfl_xor(acc, 16, kWave);
     acc += __shfl_xor(acc, 32, kWave);
     if (quad == 0) s_tm[col] = acc * scale_log2;
+    const int page = row[tok_slot / kPage], off = tok_slot % kPage;
+    if (lane < D / 8)
+      *reinterpret_cast<uint4 *>(k_pages + size_t(page) * kPage * D + key_index(off, lane * 8, D)) =
+          *reinterpret_cast<const uint4 *>(s_tok + lane * 8);
+#pragma unroll
+    for (int e = 0; e < D / kWave; ++e)
+      v_pages[size_t(page) * kPage * D + value_index(off, lane + kWave * e, D)] =
+          s_tok[D + lane + kWave * e];
+    if (lane == 0) {
+      slot_pos[size_t(page) * kPage + off] = t;
+      // the decision: sigmoid(logit) > 1/2  <=>  logit > 0 (NaN keeps)
+      slot_alpha[size_t(page) * kPage + off] = evict_decision(logit_new[tok]) ? 1 : 0;
+    }
   }
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);

@@ -104,6 +104,21 @@ def test_host_side_errors_need_no_gpu(L):
     assert L.dms_share_prefix(ctypes.byref(s), ctypes.byref(full), 1, 0, 0, None) == lib.DMS_EINVAL  # no receiver
     assert L.dms_release(ctypes.byref(s), ctypes.byref(full), 1, 2, None) == lib.DMS_EINVAL
     assert L.dms_release(ctypes.byref(s), ctypes.byref(full), 0, 0, None) == lib.DMS_OK
+    # the decode step with the token in the decode launch
+    assert L.dms_append_reserve(None, ctypes.byref(full), None) == lib.DMS_EINVAL
+    assert L.dms_append_reserve(ctypes.byref(s), ctypes.byref(null_cache), None) == lib.DMS_EINVAL
+    F = L.dms_decode_attn_fill
+    args = [fake, fake, fake, fake, fake, 0.125, fake, 1 << 30, None]
+    for i in (0, 1, 2, 3, 4, 6):  # k_new, v_new, logit, q, out, workspace
+        bad_args = list(args)
+        bad_args[i] = None
+        assert F(ctypes.byref(s), ctypes.byref(full), *bad_args) == lib.DMS_EINVAL, i
+    for i in (0, 1, 3, 4, 6):  # 16-byte alignment of k_new, v_new, q, out, workspace
+        bad_args = list(args)
+        bad_args[i] = misaligned
+        assert F(ctypes.byref(s), ctypes.byref(full), *bad_args) == lib.DMS_EINVAL, i
+    assert F(ctypes.byref(s), ctypes.byref(full), *args[:5], 0.0, *args[6:]) == lib.DMS_EINVAL
+    assert F(ctypes.byref(s), ctypes.byref(full), *args[:7], 10, None) == lib.DMS_EWORKSPACE
     M = L.dms_decode_attn_multi
     sb = _shape(kv_dtype=lib.DMS_KV_BF16)
     assert M(ctypes.byref(sb), ctypes.byref(full), fake, 0, fake, 0.125, fake, 1 << 30, None) == lib.DMS_EINVAL

@@ -539,6 +539,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the masked-prefill leg")
     ap.add_argument("--prefill-only", action="store_true", help="only run the masked-prefill leg")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunk-query leg")
+    ap.add_argument("--append-launch", action="store_true",
+                    help="time the step as dms_append + dms_decode_attn (the token written by its "
+                         "own launch) instead of dms_append_reserve + dms_decode_attn_fill")
     ap.add_argument("--no-share", action="store_true", help="skip the shared-prefix leg")
     ap.add_argument("--chunked-prefill-only", action="store_true",
                     help="only run the chunked-prefill leg")
@@ -596,10 +599,16 @@ def main():
         q, k, v, logit = inputs[r][j]
         if ev is not None:
             ev[0].record()
-        cache.reserve()
+        if args.append_launch:
+            cache.append(k, v, logit)
+        else:
+            cache.reserve()
         if ev is not None:
             ev[1].record()
-        cache.fill_and_decode(k, v, logit, q, outs[r], scale)
+        if args.append_launch:
+            cache.decode(q, out=outs[r], sm_scale=scale)
+        else:
+            cache.fill_and_decode(k, v, logit, q, outs[r], scale)
         if ev is not None:
             ev[2].record()
         compacted = (j + 1) % w.compact_every == 0
@@ -674,7 +683,8 @@ def main():
         "compression_ratio": round(cr, 3),
         "retained_per_unit": round(retained / w.units, 1),
         "decode_attn_us": round(dec_ms * 1e3, 2),
-        "step_calls": "dms_append_reserve + dms_decode_attn_fill",
+        "step_calls": ("dms_append + dms_decode_attn" if args.append_launch
+                       else "dms_append_reserve + dms_decode_attn_fill"),
         "reserve_us": round(1e3 * sum(t_reserve) / len(t_reserve), 2),
         "compact_us": round(1e3 * sum(t_compact) / max(1, len(t_compact)), 2),
         "dead_slot_overhead": round(bytes_read / bytes_alg - 1.0, 5),

@@ -42,8 +42,8 @@
 // Two phases per tile.  Phase 1 (matrix cores) computes the scores of tile k
 // and the PV product of tile k-1; phase 2 (vector unit) masks, checks and
 // exponentiates the scores of tile k.  The waves of a SIMD come from
-// different workgroups and interleave freely; a wave raises its issue
-// priority during phase 1.
+// different workgroups and interleave freely; on the general path a wave
+// raises its issue priority during phase 1 (not in the steady loops).
 //
 // Far and near tiles.  A tile whose keys all lie `w` or more positions behind
 // every query of the workgroup ("far") is masked by the decision alone, which
@@ -306,16 +306,16 @@ __device__ __forceinline__ void phase1(int k, int ntw, int nfar, const uint4 *__
 // Steady state, tile k >= 1 that needs no per-element mask (a far tile of
 // the dense kernel, a tile whose keys every query sees in the others): phase
 // 1 and phase 2 with every test on k resolved, for the loops that run only
-// such tiles.  The QK product starts from `init`.
+// such tiles.  The QK product starts from `init`.  Unlike phase 1, the
+// products run at the default issue priority: in this loop a raised priority
+// made the dense kernel 2 % slower.
 __device__ __forceinline__ void steady_step(const uint4 *__restrict__ sk,
                                             const uint4 *__restrict__ sv, const floatx4 (&init)[2],
                                             const uint4 (&qf)[2][PKS], floatx4 (&s)[2][2],
                                             uint4 (&pb)[2], floatx4 (&o)[PDT][2], Softmax &sm,
                                             float c, int lane) {
-  __builtin_amdgcn_s_setprio(2);
   pv_tile(sv, pb, lane, o);
   qk_tile(sk, init, qf, lane, s);
-  __builtin_amdgcn_s_setprio(0);
   if (__ballot(crosses(s, sm))) move_reference(s, sm, o, c);
   exponentials(s, sm, c, pb);
 }

@@ -23,6 +23,11 @@
 // stores every operand fragment as one contiguous 1 KB block, so each operand
 // is one fully coalesced 16-byte-per-lane load.  No data moves between lanes
 // except the two shuffles of the row max.
+//
+// Called through dms_decode_attn_fill, the kernel also takes the step's new
+// token (reserved, not yet written): the unit's last chunk stages its key and
+// value in LDS, adds it to the final combine as one more softmax term, and
+// writes it to its slot.
 #include "decode_common.h"
 
 namespace dms {

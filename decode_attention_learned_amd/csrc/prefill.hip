@@ -42,8 +42,7 @@
 // Two phases per tile.  Phase 1 (matrix cores) computes the scores of tile k
 // and the PV product of tile k-1; phase 2 (vector unit) masks, checks and
 // exponentiates the scores of tile k.  The waves of a SIMD come from
-// different workgroups and interleave freely; on the general path a wave
-// raises its issue priority during phase 1 (not in the steady loops).
+// different workgroups and interleave freely.
 //
 // Far and near tiles.  A tile whose keys all lie `w` or more positions behind
 // every query of the workgroup ("far") is masked by the decision alone, which
@@ -285,30 +284,26 @@ __device__ __forceinline__ void ring_barrier() {
 
 // Phase 1 of tile k: PV product of tile k - 1 (values `sv`) and QK product of
 // tile k (keys `sk`; from the additive mask `sb` on far tiles, from the zeros
-// `sz` on near ones, both read from LDS).  The wave raises its issue priority
-// for the phase, so that the SIMD's other waves (in phase 2) fill the gaps
-// between matrix instructions rather than delaying them.
+// `sz` on near ones, both read from LDS), at the default issue priority (a
+// raised priority for the phase made the kernel 1-2 % slower).
 __device__ __forceinline__ void phase1(int k, int ntw, int nfar, const uint4 *__restrict__ sk,
                                        const uint4 *__restrict__ sv, const floatx4 *__restrict__ sb,
                                        const floatx4 *__restrict__ sz, const uint4 (&qf)[2][PKS],
                                        floatx4 (&s)[2][2], const uint4 (&pb)[2],
                                        floatx4 (&o)[PDT][2], int lane, int quad) {
-  __builtin_amdgcn_s_setprio(2);
   if (k >= 1 && k - 1 < ntw) pv_tile(sv, pb, lane, o);
   if (k < ntw) {
     const floatx4 *ip = k < nfar ? sb : sz;
     const floatx4 init[2] = {ip[2 * quad], ip[2 * quad + 1]};
     qk_tile(sk, init, qf, lane, s);
   }
-  __builtin_amdgcn_s_setprio(0);
 }
 
 // Steady state, tile k >= 1 that needs no per-element mask (a far tile of
 // the dense kernel, a tile whose keys every query sees in the others): phase
 // 1 and phase 2 with every test on k resolved, for the loops that run only
-// such tiles.  The QK product starts from `init`.  Unlike phase 1, the
-// products run at the default issue priority: in this loop a raised priority
-// made the dense kernel 2 % slower.
+// such tiles.  The QK product starts from `init`.  The products run at the
+// default issue priority: a raised one made the dense kernel 2 % slower here.
 __device__ __forceinline__ void steady_step(const uint4 *__restrict__ sk,
                                             const uint4 *__restrict__ sv, const floatx4 (&init)[2],
                                             const uint4 (&qf)[2][PKS], floatx4 (&s)[2][2],

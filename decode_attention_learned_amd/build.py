@@ -2,8 +2,12 @@
 
     python -m decode_attention_learned_amd.build
 
-Every call recompiles.  The library lands next to this file, where
-``decode_attention_learned_amd.lib`` looks for it.
+Every call recompiles.  The libraries land next to this file, where
+``decode_attention_learned_amd.lib`` looks for them: ``libdms.so`` (the
+product) and ``libdms_generic.so``, a test build of the same sources whose
+one-query decode of bf16 caches runs the vector kernel (decode_mfma.hip
+compiled with DMS_DECODE_BF16_GENERIC), against which tests check the
+matrix-core kernel.
 """
 
 from __future__ import annotations
@@ -18,6 +22,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdms.so")
+LIB_GENERIC = os.path.join(HERE, "libdms_generic.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "cache_kernels.hip", "decode_kernels.hip", "decode_mfma.hip", "prefill.hip"]
@@ -46,19 +51,27 @@ def hipcc() -> str:
     return path
 
 
+# the test build differs in one object
+GENERIC_VARIANT = ("decode_mfma.hip", ["-DDMS_DECODE_BF16_GENERIC"])
+
+
 def build(verbose: bool = False) -> str:
     objs = []
     build_dir = os.path.join(HERE, "_build")
     os.makedirs(build_dir, exist_ok=True)
     procs = []
-    for src in SOURCES:
-        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
-        cmd = [hipcc(), *[f for f in FLAGS if f != "-shared"], *PER_FILE_FLAGS.get(src, []), "-c",
-               "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, src), "-o", obj]
+    jobs = [(src, os.path.join(build_dir, src.replace(".hip", ".o")), []) for src in SOURCES]
+    gsrc, gflags = GENERIC_VARIANT
+    gobj = os.path.join(build_dir, gsrc.replace(".hip", "_generic.o"))
+    jobs.append((gsrc, gobj, gflags))
+    for src, obj, extra in jobs:
+        cmd = [hipcc(), *[f for f in FLAGS if f != "-shared"], *PER_FILE_FLAGS.get(src, []), *extra,
+               "-c", "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
-        objs.append(obj)
+        if not extra:
+            objs.append(obj)
     failed = []
     for src, p in procs:
         out, _ = p.communicate()
@@ -72,10 +85,12 @@ def build(verbose: bool = False) -> str:
         for src, text in failed:
             sys.stderr.write(f"--- {src}\n{text}\n")
         raise RuntimeError("hipcc failed for " + ", ".join(s for s, _ in failed))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    gobjs = [gobj if o.endswith(gsrc.replace(".hip", ".o")) else o for o in objs]
+    for lib, members in ((LIB, objs), (LIB_GENERIC, gobjs)):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *members, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -21,23 +21,6 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-def page_element_index(head_dim: int):
-    """(key_idx, value_idx), each [64, D] int64: element offset inside a page of
-    (slot, dim), for the fragment-ordered page layout described in include/dms.h.
-    Used only to read a cache back for inspection."""
-    D = head_dim
-    j = torch.arange(PAGE)[:, None]
-    d = torch.arange(D)[None, :]
-    grp, js = j >> 5, j & 31
-    t, r = (js & 7) >> 2, 4 * (js >> 3) + (js & 3)
-    ks, q, e = d >> 5, (d >> 3) & 3, d & 7
-    key = grp * 32 * D + (((t * (D >> 5) + ks) * 4 + q) * 16 + r) * 8 + e
-    qv, ev = js >> 3, js & 7
-    dt, rr = d >> 4, d & 15
-    value = grp * 32 * D + ((dt * 4 + qv) * 16 + rr) * 8 + ev
-    return key, value
-
-
 def _need(t: torch.Tensor, name: str, dtype, shape, device):
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
@@ -196,6 +179,27 @@ class DmsCache:
     def pages_in_use(self) -> int:
         return self.num_pages - int(self.free_top.item())
 
+    def export(self, all_slots: bool = False, max_per_unit: int | None = None, kv: bool = True):
+        """dms_export_retained: (count [units], pos [units, m], alpha [units, m],
+        k [units, m, D], v [units, m, D]) as device tensors, m = max_per_unit (default:
+        the longest unit).  The retained set R(t) of every unit at its last position,
+        or with `all_slots` every slot in use; rows past a unit's count are zero.
+        k and v are None when `kv` is false."""
+        if max_per_unit is None:
+            max_per_unit = int(self.n_slots.max().item()) if self.units else 0
+        dev = self.device
+        m = max(int(max_per_unit), 0)
+        count = torch.empty((self.units,), dtype=torch.int32, device=dev)
+        pos = torch.zeros((self.units, m), dtype=torch.int32, device=dev)
+        alpha = torch.zeros((self.units, m), dtype=torch.uint8, device=dev)
+        k = v = None
+        if kv:
+            k = torch.zeros((self.units, m, self.head_dim), dtype=self.dtype, device=dev)
+            v = torch.zeros_like(k)
+        lib.check("dms_export_retained", lib.dms_export_retained(
+            self.shape, self.cache, 1 if all_slots else 0, m, count, pos, alpha, k, v, _stream()))
+        return count, pos, alpha, k, v
+
     def slots(self, unit: int):
         """(pos, alpha) of every slot of `unit`, in slot order, as CPU tensors."""
         n = int(self.n_slots[unit].item())
@@ -204,16 +208,13 @@ class DmsCache:
         alpha = self.slot_alpha[pages].reshape(-1)[:n].cpu()
         return pos, alpha
 
-    def slot_kv(self, unit: int):
-        """(k [n, D], v [n, D]) of every slot of `unit`, in slot order, CPU tensors."""
-        n = int(self.n_slots[unit].item())
-        pages = self.page_table[unit, : (n + PAGE - 1) // PAGE].long()
-        kidx, vidx = page_element_index(self.head_dim)
-        flat_k = self.k_pages.view(self.num_pages, -1)[pages]
-        flat_v = self.v_pages.view(self.num_pages, -1)[pages]
-        k = flat_k[:, kidx.reshape(-1).to(self.device)].reshape(-1, self.head_dim)[:n].cpu()
-        v = flat_v[:, vidx.reshape(-1).to(self.device)].reshape(-1, self.head_dim)[:n].cpu()
-        return k, v
+    def slot_kv(self, units=None):
+        """{unit: (k [n, D], v [n, D])} of every slot of each unit in `units` (default:
+        all), in slot order, as CPU tensors, read back through dms_export_retained."""
+        count, _, _, k, v = self.export(all_slots=True)
+        count = count.cpu()
+        units = range(self.units) if units is None else units
+        return {u: (k[u, :int(count[u])].cpu(), v[u, :int(count[u])].cpu()) for u in units}
 
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logit: torch.Tensor,

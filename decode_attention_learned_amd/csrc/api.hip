@@ -81,6 +81,17 @@ int dms_compact(const dms_shape *shape, const dms_cache *cache, hipStream_t stre
   return from_hip(dms::launch_compact(*shape, *cache, stream));
 }
 
+int dms_export_retained(const dms_shape *shape, const dms_cache *cache, int32_t all_slots,
+                        int32_t max_per_unit, int32_t *count_out, int32_t *pos_out,
+                        uint8_t *alpha_out, void *k_out, void *v_out, hipStream_t stream) {
+  int rc = dms_check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_cache(shape, cache))) return rc;
+  if (!count_out || max_per_unit < 0 || (all_slots != 0 && all_slots != 1)) return DMS_EINVAL;
+  return from_hip(dms::launch_export(*shape, *cache, all_slots, max_per_unit, count_out, pos_out,
+                                     alpha_out, k_out, v_out, stream));
+}
+
 size_t dms_plan_words(const dms_shape *shape) {
   if (dms_check_shape(shape) != DMS_OK) return 0;
   return dms::plan_layout(dms::units_of(*shape)).words;

@@ -9,6 +9,8 @@
 // Layout: one page = 64 slots of one unit, 64*D key elements in k_pages and
 // 64*D value elements in v_pages, ordered by key_index / value_index
 // (dms_internal.h) so that the decode kernel reads whole operand fragments.
+#include <type_traits>
+
 #include "dms_internal.h"
 
 namespace dms {
@@ -41,7 +43,8 @@ __device__ int block_inclusive_scan(int x, int *s_tmp, int &total) {
 __global__ void k_reset(int units, int maxp, int num_pages, int batch, int32_t *page_table,
                         int32_t *free_list, int32_t *free_top, int32_t *n_slots,
                         int32_t *n_clean, int32_t *append_base, int32_t *seq_len,
-                        uint32_t *status, int32_t *page_ref) {
+                        uint32_t *status, int32_t *page_ref, int32_t *plan) {
+  int32_t *compact_pos = plan + plan_layout(units).compact_pos;
   const long i0 = long(blockIdx.x) * blockDim.x + threadIdx.x;
   const long stride = long(gridDim.x) * blockDim.x;
   for (long x = i0; x < long(units) * maxp; x += stride) page_table[x] = -1;
@@ -52,6 +55,7 @@ __global__ void k_reset(int units, int maxp, int num_pages, int batch, int32_t *
     n_slots[x] = 0;
     n_clean[x] = 0;
     append_base[x] = -1;
+    compact_pos[x] = -1;
   }
   for (long x = i0; x < batch; x += stride) seq_len[x] = 0;
   if (i0 == 0) {
@@ -78,7 +82,7 @@ hipError_t launch_reset(const dms_shape &s, const dms_cache &c, hipStream_t st) 
   hipLaunchKernelGGL(k_reset, dim3(std::max(blocks, 1)), dim3(256), 0, st, units,
                      s.max_pages_per_unit, s.num_pages, s.batch, c.page_table, c.free_list,
                      c.free_top, c.n_slots, c.n_clean, c.append_base, c.seq_len, c.status,
-                     c.page_ref);
+                     c.page_ref, c.plan);
   const hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : launch_plan(s, c, st);
 }
@@ -265,7 +269,8 @@ __global__ __launch_bounds__(256) void k_compact(
     const int32_t *__restrict__ seq_len, int32_t *__restrict__ n_slots,
     int32_t *__restrict__ n_clean, E *__restrict__ k_pages, E *__restrict__ v_pages,
     int32_t *__restrict__ slot_pos, uint8_t *__restrict__ slot_alpha,
-    int32_t *__restrict__ free_list, int32_t *__restrict__ free_top) {
+    int32_t *__restrict__ free_list, int32_t *__restrict__ free_top,
+    int32_t *__restrict__ compact_pos) {
   constexpr int CE = 16 / int(sizeof(E));           // elements per 16-byte piece
   constexpr int CPR = D / CE;                       // key pieces per slot
   constexpr int SPC = CE;                           // slots per 16-byte value piece
@@ -277,8 +282,9 @@ __global__ __launch_bounds__(256) void k_compact(
   const int b = u / hkv;
   const int lo = n_clean[u];
   const int hi = n_slots[u];
-  if (lo >= hi) return;
   const int t = seq_len[b] - 1;
+  if (threadIdx.x == 0) compact_pos[u] = t;
+  if (lo >= hi) return;
   const int thr = t - window;  // a marked slot with pos <= thr is dead
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = lane_id();
@@ -401,7 +407,8 @@ static void launch_compact_t(const dms_shape &s, const dms_cache &c, hipStream_t
   hipLaunchKernelGGL((k_compact<E, D>), dim3(units_of(s)), dim3(256), 0, st, s.kv_heads,
                      s.window, s.max_pages_per_unit, c.page_table, c.seq_len, c.n_slots,
                      c.n_clean, static_cast<E *>(c.k_pages), static_cast<E *>(c.v_pages),
-                     c.slot_pos, c.slot_alpha, c.free_list, c.free_top);
+                     c.slot_pos, c.slot_alpha, c.free_list, c.free_top,
+                     c.plan + plan_layout(units_of(s)).compact_pos);
 }
 
 hipError_t launch_compact(const dms_shape &s, const dms_cache &c, hipStream_t st) {
@@ -412,6 +419,88 @@ hipError_t launch_compact(const dms_shape &s, const dms_cache &c, hipStream_t st
   else launch_compact_t<uint32_t, 128>(s, c, st);
   const hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : launch_plan(s, c, st);
+}
+
+// ---------------------------------------------------------------------------
+// export: one workgroup (4 waves) per unit copies the retained set R(t),
+// t = seq_len[b] - 1 (or, with all_slots, every slot in use), in slot order,
+// which is position order: positions, decisions, and keys and values as
+// plain [D] rows, undoing the fragment order of the pages.  For each page,
+// wave 0 ranks the selected slots with a ballot and mbcnt; then every thread
+// copies its share of their elements.  Only the first max_out are written;
+// count_out gets the full count.
+// ---------------------------------------------------------------------------
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_export(
+    int hkv, int window, int maxp, int all_slots, int max_out,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_len,
+    const int32_t *__restrict__ n_slots, const int32_t *__restrict__ n_clean,
+    const E *__restrict__ k_pages, const E *__restrict__ v_pages,
+    const int32_t *__restrict__ slot_pos, const uint8_t *__restrict__ slot_alpha,
+    int32_t *__restrict__ count_out, int32_t *__restrict__ pos_out,
+    uint8_t *__restrict__ alpha_out, E *__restrict__ k_out, E *__restrict__ v_out) {
+  const int u = blockIdx.x;
+  const int b = u / hkv;
+  const int hi = n_slots[u], nc = n_clean[u];
+  const int t = seq_len[b] - 1;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  const int32_t *row = page_table + size_t(u) * maxp;
+  __shared__ int s_dst[kPage];
+  int cnt = 0;  // selected slots so far (wave 0)
+  for (int P = 0; P * kPage < hi; ++P) {
+    const int page = row[P];
+    if (wave == 0) {
+      const int slot = P * kPage + lane;
+      bool sel = slot < hi;
+      if (sel && !all_slots && slot >= nc) {
+        const size_t m = size_t(page) * kPage + lane;
+        sel = slot_alpha[m] == 0 || (t - slot_pos[m]) < window;
+      }
+      const uint64_t mask = __ballot(sel);
+      s_dst[lane] = sel ? cnt + lanes_below(mask) : -1;
+      cnt += __popcll(mask);
+    }
+    __syncthreads();
+    if (tid < kPage) {
+      const int dst = s_dst[tid];
+      if (dst >= 0 && dst < max_out) {
+        const size_t o = size_t(u) * max_out + dst;
+        if (pos_out) pos_out[o] = slot_pos[size_t(page) * kPage + tid];
+        if (alpha_out) alpha_out[o] = slot_alpha[size_t(page) * kPage + tid];
+      }
+    }
+    for (int x = tid; x < kPage * D; x += 256) {
+      const int j = x / D, d = x % D;
+      const int dst = s_dst[j];
+      if (dst >= 0 && dst < max_out) {
+        const size_t o = (size_t(u) * max_out + dst) * D + d;
+        if (k_out) k_out[o] = k_pages[size_t(page) * kPage * D + key_index(j, d, D)];
+        if (v_out) v_out[o] = v_pages[size_t(page) * kPage * D + value_index(j, d, D)];
+      }
+    }
+    __syncthreads();  // s_dst is rewritten for the next page
+  }
+  if (tid == 0) count_out[u] = cnt;
+}
+
+hipError_t launch_export(const dms_shape &s, const dms_cache &c, int all_slots, int max_out,
+                         int32_t *count_out, int32_t *pos_out, uint8_t *alpha_out, void *k_out,
+                         void *v_out, hipStream_t st) {
+  auto go = [&](auto kern, auto *kp, auto *vp) {
+    using E = std::remove_const_t<std::remove_pointer_t<decltype(kp)>>;
+    hipLaunchKernelGGL(kern, dim3(units_of(s)), dim3(256), 0, st, s.kv_heads, s.window,
+                       s.max_pages_per_unit, all_slots, max_out, c.page_table, c.seq_len,
+                       c.n_slots, c.n_clean, kp, vp, c.slot_pos, c.slot_alpha, count_out, pos_out,
+                       alpha_out, static_cast<E *>(k_out), static_cast<E *>(v_out));
+  };
+  const bool bf = s.kv_dtype == DMS_KV_BF16;
+  const uint16_t *k16 = static_cast<const uint16_t *>(c.k_pages), *v16 = static_cast<const uint16_t *>(c.v_pages);
+  const uint32_t *k32 = static_cast<const uint32_t *>(c.k_pages), *v32 = static_cast<const uint32_t *>(c.v_pages);
+  if (bf && s.head_dim == 64) go(k_export<uint16_t, 64>, k16, v16);
+  else if (bf) go(k_export<uint16_t, 128>, k16, v16);
+  else if (s.head_dim == 64) go(k_export<uint32_t, 64>, k32, v32);
+  else go(k_export<uint32_t, 128>, k32, v32);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -464,6 +553,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_share_alloc(
         n_slots[du] = n_slots[su];
         n_clean[du] = n_clean[su];
         append_base[du] = -1;
+        plan[plan_layout(units).compact_pos + du] = plan[plan_layout(units).compact_pos + su];
         if (x % hkv == 0) seq_len[dst_first + x / hkv] = seq_len[src];
         if (need > 0) atomicMax(&s_taken, incl);
       } else {
@@ -571,6 +661,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_release(int hkv, int maxp, in
     n_slots[u] = 0;
     n_clean[u] = 0;
     append_base[u] = -1;
+    plan[plan_layout(units).compact_pos + u] = -1;
   }
   for (int b = threadIdx.x; b < nseq; b += kAllocThreads) seq_len[first + b] = 0;
   __syncthreads();

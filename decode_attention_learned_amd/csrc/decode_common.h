@@ -36,12 +36,14 @@ __device__ __forceinline__ bool locate_chunk(int c, int hkv, const int32_t *plan
 // Cross-workgroup merge of a unit's chunk partials, inside the decode kernel.
 //
 // Partials are published with agent-scope atomic stores (written through to
-// the agent's coherence point rather than left dirty in one XCD's L2), each
-// thread waits until its stores have completed, and one relaxed atomic
-// increment per workgroup counts the chunk in.  The workgroup that brings the
-// count to the unit's chunk count reads every partial back with agent-scope
-// atomic loads and writes the output.  No device-scope fence is needed, so no
-// workgroup writes back or invalidates a whole L2.
+// the agent's coherence point rather than left dirty in one XCD's L2).  After
+// a workgroup barrier (every thread's stores happen before it), one thread
+// counts the chunk in with an agent-scope release increment.  The workgroup
+// whose increment brings the count to the unit's chunk count takes an
+// agent-scope acquire fence: every other chunk's release increment heads a
+// release sequence its increment read from, so all partials happen before
+// its reads.  It reads them back with agent-scope atomic loads and writes the
+// output.  Only that workgroup acquires.
 //
 // Merge rule in log2 units:
 //   M = max_c m_c,  w_c = 2^(m_c - M),  out = sum_c o_c w_c / sum_c l_c w_c
@@ -79,11 +81,13 @@ __device__ inline void count_and_merge(const ChunkInfo &ci, int G, int D, int32_
   __shared__ int s_last;
   __shared__ float s_w[kMergeLds];
   __shared__ float s_inv[16];
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's stores are complete
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(&merge_count[ci.unit], 1, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT) == ci.nch - 1;
+  __syncthreads();  // every thread's partial stores happen before the increment
+  if (threadIdx.x == 0) {
+    const bool last = __hip_atomic_fetch_add(&merge_count[ci.unit], 1, __ATOMIC_RELEASE,
+                                             __HIP_MEMORY_SCOPE_AGENT) == ci.nch - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_last = last;
+  }
   __syncthreads();
   if (!s_last) return;
 

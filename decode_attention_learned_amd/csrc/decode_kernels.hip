@@ -194,7 +194,7 @@ static bool dispatch_group(const dms_shape &s, const dms_cache &c, const E *q, f
 
 bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                         float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
-                        int n_query, const DecodeFill *fill = nullptr);
+                        int n_query, const DecodeFill *fill, bool chunk);
 
 // The decode grid has one workgroup per possible chunk (max_chunks_of(units));
 // workgroups past the plan's chunk count exit at once.  With `fill`, the
@@ -206,7 +206,8 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
   char *ws = static_cast<char *>(wsv);
   const float scale_log2 = sm_scale * 1.4426950408889634f;  // exp(x) = exp2(x * log2 e)
   bool done = false;
-  if (s.kv_dtype == DMS_KV_BF16) done = launch_decode_mfma(s, c, q, out, scale_log2, w, ws, st, 1, fill);
+  if (s.kv_dtype == DMS_KV_BF16)
+    done = launch_decode_mfma(s, c, q, out, scale_log2, w, ws, st, 1, fill, false);
   if (!done && fill) {
     const hipError_t e = launch_append_write(s, c, fill->k_new, fill->v_new, fill->logit, 1, st);
     if (e != hipSuccess) return e;
@@ -238,7 +239,8 @@ hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const voi
     return launch_chunk_attn(s, c, q, n_query, out, sm_scale, st);
   const DecodeWorkspace w = decode_workspace_layout(units_of(s), 16, s.head_dim);
   const float scale_log2 = sm_scale * 1.4426950408889634f;
-  if (!launch_decode_mfma(s, c, q, out, scale_log2, w, static_cast<char *>(wsv), st, n_query))
+  if (!launch_decode_mfma(s, c, q, out, scale_log2, w, static_cast<char *>(wsv), st, n_query,
+                          nullptr, true))
     return hipErrorInvalidValue;
   return hipGetLastError();
 }

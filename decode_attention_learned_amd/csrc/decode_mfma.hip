@@ -68,10 +68,19 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{lo, hi}, bf16x2v));
 }
 
+// acc + lo + hi of a packed bf16 pair, in one v_dot2c_f32_bf16
+__device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+  const bf16x2v one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pair), one, acc, false);
+}
+
 // Several queries per sequence (a chunk of C tokens just appended, at
 // positions seq_len - C .. seq_len - 1): one launch serves queries c0 ..
 // c0 + nq - 1 of the chunk, and the 16 B-operand columns hold (query, head)
 // pairs col = (c - c0) * G + g, nq * G <= 16.  Decode is nq = C = 1.
+// `chunk_status` (chunk queries only, else null): the first launch of a chunk
+// flags DMS_STATUS_CHUNK_INVALID for a sequence shorter than the chunk or
+// compacted after the chunk's first position.
 template <int D>
 __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
     int units, int hkv, int G, int window, int maxp, float scale_log2, int nq, int c0, int C,
@@ -81,7 +90,8 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
     const int32_t *__restrict__ seq_len, int32_t *__restrict__ plan,
     const int32_t *__restrict__ append_base, const uint16_t *__restrict__ k_new,
     const uint16_t *__restrict__ v_new, const float *__restrict__ logit_new,
-    float2 *__restrict__ part_ml, float *__restrict__ part_o, float *__restrict__ out) {
+    uint32_t *__restrict__ chunk_status, float2 *__restrict__ part_ml, float *__restrict__ part_o,
+    float *__restrict__ out) {
   constexpr int KSTEPS = D / 32;  // QK products per 16-slot tile
   constexpr int DTILES = D / 16;  // PV products per group
   const PlanLayout L = plan_layout(units);
@@ -92,6 +102,10 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
   const int s_begin = ci.s_begin, t = ci.t, nclean = ci.nclean;
   const int32_t *row = page_table + size_t(u) * maxp;
   const int tid = threadIdx.x;
+  if (chunk_status != nullptr && c0 == 0 && c == ci.first && tid == 0) {
+    const int p0 = t - (C - 1);  // the chunk's first position
+    if (p0 < 0 || plan[L.compact_pos + u] > p0) atomicOr(chunk_status, DMS_STATUS_CHUNK_INVALID);
+  }
 
   // The step's token (decode with fill): its slot, reserved by the
   // allocation launch (n_new = 1), is the unit's newest and lies in the
@@ -250,12 +264,14 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
     float p[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) p[e] = exp2f(sv[e] - m_sub);
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ps += p[e];
-    l_run += ps;
     const uint4 pb = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
                                 pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
+    // the row sum adds the bf16-rounded weights that enter the PV product, so
+    // numerator and denominator use the same weights
+    l_run = add_pair(pb.x, l_run);
+    l_run = add_pair(pb.y, l_run);
+    l_run = add_pair(pb.z, l_run);
+    l_run = add_pair(pb.w, l_run);
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) o[dt] = mfma_bf16(r.v[dt], pb, o[dt]);
   };
@@ -368,7 +384,7 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
 
 bool launch_decode_mfma_part(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                              float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
-                             int nq, int c0, int C, const DecodeFill *fill) {
+                             int nq, int c0, int C, const DecodeFill *fill, bool chunk) {
   auto args = [&](auto kern) {
     const int rcols = nq * s.group < kCombineCols ? nq * s.group : kCombineCols;
     const size_t lds = size_t(kMfmaWaves) * rcols * (s.head_dim + 4) * sizeof(float);
@@ -383,7 +399,7 @@ bool launch_decode_mfma_part(const dms_shape &s, const dms_cache &c, const void 
                        c.plan, c.append_base,
                        fill ? static_cast<const uint16_t *>(fill->k_new) : nullptr,
                        fill ? static_cast<const uint16_t *>(fill->v_new) : nullptr,
-                       fill ? fill->logit : nullptr,
+                       fill ? fill->logit : nullptr, chunk ? c.status : nullptr,
                        reinterpret_cast<float2 *>(ws + w.part_ml),
                        reinterpret_cast<float *>(ws + w.part_o), out);
   };
@@ -394,18 +410,21 @@ bool launch_decode_mfma_part(const dms_shape &s, const dms_cache &c, const void 
 }
 
 
+// A library built with DMS_DECODE_BF16_GENERIC (a test build, checked against
+// this one) serves one-query decode of bf16 caches with the vector kernel.
 bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                         float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
-                        int n_query, const DecodeFill *fill) {
+                        int n_query, const DecodeFill *fill, bool chunk) {
   if (s.kv_dtype != DMS_KV_BF16 || s.group > 16) return false;
-  const char *force = getenv("DMS_DECODE_KERNEL");
-  if (n_query == 1 && force && force[0] == 'g') return false;  // "generic": the VALU kernel
+#ifdef DMS_DECODE_BF16_GENERIC
+  if (!chunk) return false;
+#endif
   // queries per launch: as many as fit the 16 operand columns
   const int per = 16 / s.group;
   for (int c0 = 0; c0 < n_query; c0 += per) {
     const int nq = n_query - c0 < per ? n_query - c0 : per;
     if (!launch_decode_mfma_part(s, c, q, out, scale_log2, w, ws, st, nq, c0, n_query,
-                                 n_query == 1 ? fill : nullptr))
+                                 chunk ? nullptr : fill, chunk))
       return false;
   }
   return true;

@@ -27,9 +27,12 @@ constexpr int kWave = 64;              // CDNA wavefront width
 constexpr int kTargetChunks = DMS_TARGET_CHUNKS;
 constexpr int kRaggedRounds = 3;
 
-// the largest chunk count of a plan for `units` units
+// The largest chunk count of a plan for `units` units.  build_plan gives one
+// chunk per unit when units >= its budget (kTargetChunks, or kRaggedRounds *
+// kTargetChunks for ragged lengths), and at most the budget otherwise, so the
+// count never exceeds max(units, kRaggedRounds * kTargetChunks).
 __host__ __device__ inline int max_chunks_of(int units) {
-  return units > kTargetChunks ? units : kRaggedRounds * kTargetChunks;
+  return units > kRaggedRounds * kTargetChunks ? units : kRaggedRounds * kTargetChunks;
 }
 
 inline int units_of(const dms_shape &s) { return s.batch * s.kv_heads; }
@@ -37,11 +40,17 @@ inline int units_of(const dms_shape &s) { return s.batch * s.kv_heads; }
 // Split plan, kept in cache state (dms_cache.plan, int32 words).  Rebuilt from
 // n_slots by every call that changes n_slots (reset, append, compact), so
 // decode reads it without a planning launch of its own.
+// Besides the plan, the same buffer holds per unit the position of the last
+// token at its last compaction (compact_pos, -1 before any): a chunk of
+// queries appended at positions >= p0 can be answered only if no compaction
+// ran after position p0 (a later one may have dropped keys the chunk's
+// earlier queries still see, or moved chunk tokens into the clean prefix).
 struct PlanLayout {
   size_t hdr;          // [16]: [0] chunk count, [1] slots per chunk
   size_t first_chunk;  // [units + 1]: first chunk of each unit (prefix sum)
   size_t chunk_unit;   // [max_chunks]: owning unit of each chunk
   size_t merge_count;  // [units]: chunks of the unit finished in the running decode
+  size_t compact_pos;  // [units]: position t of the unit's last compaction, -1 if none
   size_t words;
   int max_chunks;
 };
@@ -53,7 +62,8 @@ __host__ __device__ inline PlanLayout plan_layout(int units) {
   p.first_chunk = 16;
   p.chunk_unit = p.first_chunk + size_t(units) + 1;
   p.merge_count = p.chunk_unit + size_t(p.max_chunks);
-  p.words = p.merge_count + size_t(units);
+  p.compact_pos = p.merge_count + size_t(units);
+  p.words = p.compact_pos + size_t(units);
   return p;
 }
 
@@ -92,6 +102,9 @@ struct DecodeFill {
   const float *logit;         // [B][1][Hkv]
 };
 hipError_t launch_compact(const dms_shape &s, const dms_cache &c, hipStream_t st);
+hipError_t launch_export(const dms_shape &s, const dms_cache &c, int all_slots, int max_out,
+                         int32_t *count_out, int32_t *pos_out, uint8_t *alpha_out, void *k_out,
+                         void *v_out, hipStream_t st);
 hipError_t launch_plan(const dms_shape &s, const dms_cache &c, hipStream_t st);
 hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                          float sm_scale, void *ws, hipStream_t st, const DecodeFill *fill = nullptr);

@@ -211,6 +211,30 @@ __device__ __forceinline__ void pv_tile(const uint4 *__restrict__ sv, const uint
   }
 }
 
+// PV product of a cache tile whose slots from `valid` on (0..31) are unused:
+// their value rows may hold anything a recycled page held (even NaN), so they
+// are cleared in the operand (their weights are already zero).
+__device__ __forceinline__ void pv_tile_tail(const uint4 *__restrict__ sv, const uint4 (&pb)[2],
+                                             int lane, int valid, floatx4 (&o)[PDT][2]) {
+  const int quad = lane >> 4;
+  uint32_t keep[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = 8 * quad + 2 * e;  // this lane's slots j, j + 1 of the tile
+    keep[e] = (j < valid ? 0xffffu : 0u) | (j + 1 < valid ? 0xffff0000u : 0u);
+  }
+#pragma unroll
+  for (int dt = 0; dt < PDT; ++dt) {
+    uint4 va = sv[dt * PFRAG + lane];
+    va.x &= keep[0];
+    va.y &= keep[1];
+    va.z &= keep[2];
+    va.w &= keep[3];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma(va, pb[qt], o[dt][qt]);
+  }
+}
+
 // Write a wave's output (32 query rows of one head, o / l) through LDS so that
 // each store instruction covers two whole 512-byte rows.  `stage` holds 16
 // rows of 128 floats (8 KB) for this wave; row r is rotated by 4 r floats so
@@ -975,14 +999,18 @@ hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void
 // group of a cache page has exactly the layout of a packed prefill tile
 // (key_index / value_index), so tiles are copied from the pages into LDS with
 // no pack pass.  Workgroup: one unit, 32 chunk queries, four query heads (one
-// per wave); grid (ceil(C / 32), units * ceil(G / 4)).
+// per wave); grid (ceil(C / 32), units * ceil(G / 4)).  A sequence shorter
+// than the chunk, or compacted after the chunk's first position (compact_pos,
+// kept with the plan), is flagged DMS_STATUS_CHUNK_INVALID in `status`.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
     int hkv, int G, int window, int maxp, int C, float scale_log2, const uint16_t *__restrict__ q,
     const uint4 *__restrict__ k_pages, const uint4 *__restrict__ v_pages,
     const int32_t *__restrict__ page_table, const int4 *__restrict__ slot_pos,
     const uint4 *__restrict__ slot_alpha, const int32_t *__restrict__ n_slots,
-    const int32_t *__restrict__ n_clean, const int32_t *__restrict__ seq_len, float *__restrict__ out) {
+    const int32_t *__restrict__ n_clean, const int32_t *__restrict__ seq_len,
+    const int32_t *__restrict__ compact_pos, uint32_t *__restrict__ status,
+    float *__restrict__ out) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
@@ -1000,6 +1028,11 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
   const int nt = (ns + PBN - 1) / PBN;
   const int nclean_t = nc / PBN;                  // tiles wholly below n_clean
   const int32_t *row = page_table + size_t(u) * maxp;
+  if (blockIdx.x == 0 && hg == 0 && tid == 0) {
+    const int p0 = seq_len[b] - C;  // the chunk's first position
+    if (p0 < 0 || compact_pos[u] > p0) atomicOr(status, DMS_STATUS_CHUNK_INVALID);
+  }
+  const int tail_valid = ns - (nt - 1) * PBN;     // slots in use in the last tile
 
   uint4 qf[2][PKS];
 #pragma unroll
@@ -1054,7 +1087,10 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
                        uint4 *tn, int4 *pn, uint4 *an) {
     if (k + 1 < nt) copy(k + 1, tn, pn, an);
     if (active) {
-      if (k >= 1) pv_tile(tp + PK_FRAGS * PFRAG, pb, lane, o);
+      if (k >= 1) {
+        if (k == nt && tail_valid < PBN) pv_tile_tail(tp + PK_FRAGS * PFRAG, pb, lane, tail_valid, o);
+        else pv_tile(tp + PK_FRAGS * PFRAG, pb, lane, o);
+      }
       if (k < nt) qk_tile(t, zero, qf, lane, s);
       c_phase2(k, nt, nclean_t, ns, nc, window, t_first, col, quad, p,
                reinterpret_cast<const uint2 *>(a), s, sm, o, pb, c);
@@ -1100,7 +1136,8 @@ hipError_t launch_chunk_attn(const dms_shape &s, const dms_cache &c, const void 
                      sm_scale * 1.4426950408889634f, static_cast<const uint16_t *>(q),
                      static_cast<const uint4 *>(c.k_pages), static_cast<const uint4 *>(c.v_pages),
                      c.page_table, reinterpret_cast<const int4 *>(c.slot_pos),
-                     reinterpret_cast<const uint4 *>(c.slot_alpha), c.n_slots, c.n_clean, c.seq_len, out);
+                     reinterpret_cast<const uint4 *>(c.slot_alpha), c.n_slots, c.n_clean, c.seq_len,
+                     c.plan + plan_layout(units_of(s)).compact_pos, c.status, out);
   return hipGetLastError();
 }
 

@@ -2,15 +2,23 @@
 
 Argument marshalling only: every computation happens in the HIP kernels.
 :func:`load` raises if the library has not been built; there is no fallback.
+
+Two builds of the same sources exist: ``libdms.so`` (the product) and
+``libdms_generic.so``, a test build whose one-query decode of bf16 caches runs
+the vector kernel instead of the matrix-core one, so tests can check the two
+against each other.  :func:`variant` switches the calls of this module to it
+for the duration of a ``with`` block.
 """
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdms.so")
+VARIANT_PATHS = {"": LIB_PATH, "generic": os.path.join(_HERE, "libdms_generic.so")}
 
 DMS_PAGE_SIZE = 64
 DMS_OK = 0
@@ -21,6 +29,7 @@ DMS_EHIP = -4
 DMS_STATUS_POOL_EXHAUSTED = 1
 DMS_STATUS_ROW_OVERFLOW = 2
 DMS_STATUS_NOT_EMPTY = 4
+DMS_STATUS_CHUNK_INVALID = 8
 DMS_KV_F32 = 0
 DMS_KV_BF16 = 1
 
@@ -30,6 +39,7 @@ EXPORTS = (
     "dms_strerror",
     "dms_check_shape",
     "dms_plan_words",
+    "dms_export_retained",
     "dms_reset",
     "dms_append",
     "dms_compact",
@@ -88,18 +98,33 @@ class DmsError(RuntimeError):
         super().__init__(f"{fn} failed: {code} ({strerror(code)})")
 
 
-_lib = None
+_libs: dict = {}
+_active = ""
+
+
+@contextlib.contextmanager
+def variant(name: str):
+    """Route this module's calls to the build `name` ("" = the product library)."""
+    global _active
+    if name not in VARIANT_PATHS:
+        raise ValueError(f"unknown library build {name!r}")
+    prev, _active = _active, name
+    try:
+        load()
+        yield
+    finally:
+        _active = prev
 
 
 def load() -> ctypes.CDLL:
-    """Load libdms.so once; raise if it is missing (build it with __graft_entry__.build())."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() first "
+    """Load the active build once; raise if it is missing (build it with __graft_entry__.build())."""
+    if _active in _libs:
+        return _libs[_active]
+    path = VARIANT_PATHS[_active]
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first "
                            "(there is no non-HIP fallback)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     SP = ctypes.POINTER(DmsShape)
     CP = ctypes.POINTER(DmsCacheStruct)
@@ -108,6 +133,8 @@ def load() -> ctypes.CDLL:
         "dms_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "dms_check_shape": ([SP], ctypes.c_int),
         "dms_plan_words": ([SP], ctypes.c_size_t),
+        "dms_export_retained": ([SP, CP, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P],
+                                ctypes.c_int),
         "dms_reset": ([SP, CP, P], ctypes.c_int),
         "dms_append": ([SP, CP, P, P, P, ctypes.c_int32, P], ctypes.c_int),
         "dms_compact": ([SP, CP, P], ctypes.c_int),
@@ -134,7 +161,7 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
-    _lib = lib
+    _libs[_active] = lib
     return lib
 
 
@@ -175,6 +202,13 @@ def dms_reset(shape, cache, stream) -> int:
 def dms_append(shape, cache, k_new, v_new, logit, n_new, stream) -> int:
     return load().dms_append(ctypes.byref(shape), ctypes.byref(cache), _p(k_new), _p(v_new),
                              _p(logit), int(n_new), stream)
+
+
+def dms_export_retained(shape, cache, all_slots, max_per_unit, count_out, pos_out, alpha_out,
+                        k_out, v_out, stream) -> int:
+    return load().dms_export_retained(ctypes.byref(shape), ctypes.byref(cache), int(all_slots),
+                                      int(max_per_unit), _p(count_out), _p(pos_out), _p(alpha_out),
+                                      _p(k_out), _p(v_out), stream)
 
 
 def dms_compact(shape, cache, stream) -> int:

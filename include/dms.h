@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DMS_ABI_VERSION 3
+#define DMS_ABI_VERSION 4
 #define DMS_PAGE_SIZE 64
 
 /* host-side return codes */
@@ -54,6 +54,9 @@ extern "C" {
 #define DMS_STATUS_POOL_EXHAUSTED 1u /* free pages ran out; that unit's tokens were dropped */
 #define DMS_STATUS_ROW_OVERFLOW 2u   /* a unit needed more than max_pages_per_unit pages */
 #define DMS_STATUS_NOT_EMPTY 4u      /* dms_share_prefix target unit held tokens; left as it was */
+#define DMS_STATUS_CHUNK_INVALID 8u  /* dms_decode_attn_multi: a sequence held fewer tokens than the
+                                        chunk, or was compacted after the chunk's first position;
+                                        that sequence's outputs are unspecified */
 
 /* key/value element types */
 #define DMS_KV_F32 0
@@ -73,9 +76,8 @@ typedef struct dms_shape {
 
 /*
  * The paged cache.  Every field is a caller-owned device buffer.
- *   k_pages     [num_pages][P][D]   key rows, one per slot
- *   v_pages     [num_pages][D][P]   value columns: element (d, slot) of a page
- *                                   (slots are contiguous for each d)
+ *   k_pages     [num_pages][P*D]  keys, in the order of the decode kernel's
+ *   v_pages     [num_pages][P*D]  matrix-core operand fragments (below)
  *   page_table  [units][max_pages_per_unit] int32, -1 = no page
  *   slot_pos    [num_pages][P] int32  sequence position held by each slot
  *   slot_alpha  [num_pages][P] uint8  1 = marked for eviction
@@ -85,8 +87,9 @@ typedef struct dms_shape {
  *   seq_len     [B] int32      tokens appended so far (next position)
  *   free_list   [num_pages] int32, free_top [1] int32: stack of free pages
  *   status      [1] uint32     sticky DMS_STATUS_* bits
- *   plan        [dms_plan_words(shape)] int32: the decode split plan, rebuilt
- *               on the device by every call that changes n_slots
+ *   plan        [dms_plan_words(shape)] int32, opaque: the decode split plan,
+ *               rebuilt on the device by every call that changes n_slots,
+ *               and per unit the position of its last compaction
  *   page_ref    [num_pages] int32: holders of a page beyond the first (pages
  *               shared by dms_share_prefix); may be NULL when no prefix is
  *               ever shared
@@ -94,6 +97,17 @@ typedef struct dms_shape {
  * followed by tokens appended since its last compaction; a slot is dead when
  * its token is marked and w or more positions old, and dead slots are skipped
  * by attention until dms_compact removes them.
+ *
+ * Element order inside a page (E = kv_dtype element; slot j in 0..63, dim d
+ * in 0..D-1).  A page is two groups of 32 slots, g = j / 32, js = j % 32, each
+ * holding 32*D keys then (in v_pages) 32*D values:
+ *   key (j, d)   at g*32*D + (((t*(D/32) + d/32)*4 + (d/8)%4)*16 + r)*8 + d%8,
+ *                t = (js%8)/4, r = 4*(js/8) + js%4
+ *   value (j, d) at g*32*D + (((d/16)*4 + js/8)*16 + d%16)*8 + js%8
+ * so that each 16-slot x 32-dim key fragment and each 16-dim x 32-slot value
+ * fragment of a bf16 matrix product is one contiguous 1 KB block, and eight
+ * consecutive dims of a key, or eight consecutive slots of a value dim, are
+ * contiguous.  dms_export_retained reads a cache back in plain row order.
  */
 typedef struct dms_cache {
   void *k_pages;
@@ -123,6 +137,28 @@ int dms_check_shape(const dms_shape *shape);
 
 /* int32 words of cache->plan for this shape; 0 if the shape is invalid. */
 size_t dms_plan_words(const dms_shape *shape);
+
+/*
+ * Read a cache back: for every unit, its retained set R(t) at t = seq_len[b] - 1
+ * (the slots alive at t: below n_clean, unmarked, or marked and t - pos < w;
+ * atlas.scime.ai summary, "Approach": eviction carried out after the delay
+ * window), or with all_slots = 1 every slot in use, dead ones included.  In
+ * slot order, which is ascending position order.
+ *   all_slots     0 or 1
+ *   max_per_unit  >= 0: rows per unit in the outputs below
+ *   count_out     [units] int32: the number of entries (all of them, also
+ *                 beyond max_per_unit); required
+ *   pos_out       [units][max_per_unit] int32 positions, or NULL
+ *   alpha_out     [units][max_per_unit] uint8 decisions (1 = marked), or NULL
+ *   k_out, v_out  [units][max_per_unit][D] in kv_dtype, plain rows, or NULL
+ * Only the first min(count, max_per_unit) rows of a unit are written; the
+ * rest of the outputs is left as it was.  Must not run between
+ * dms_append_reserve and dms_decode_attn_fill.  Host errors: DMS_EINVAL for
+ * a null count_out, a negative max_per_unit or all_slots not 0 or 1.
+ */
+int dms_export_retained(const dms_shape *shape, const dms_cache *cache, int32_t all_slots,
+                        int32_t max_per_unit, int32_t *count_out, int32_t *pos_out,
+                        uint8_t *alpha_out, void *k_out, void *v_out, hipStream_t stream);
 
 /*
  * Empty every unit: page_table = -1, free_list = 0..num_pages-1,
@@ -158,7 +194,7 @@ int dms_append(const dms_shape *shape, const dms_cache *cache, const void *k_new
  * stream compaction), whole pages left empty go back on the free stack and
  * n_slots / n_clean are updated and the decode plan is rebuilt.  Attention
  * results do not depend on when or whether this runs; memory use and bytes
- * read do.
+ * read do.  The position t is recorded per unit (see dms_decode_attn_multi).
  */
 int dms_compact(const dms_shape *shape, const dms_cache *cache, hipStream_t stream);
 
@@ -259,11 +295,13 @@ size_t dms_decode_multi_workspace_bytes(const dms_shape *shape);
  * carried out after the delay window; the earlier queries of the chunk do
  * not see its later tokens).  Call it after appending the chunk and before
  * any dms_compact: a compaction at the chunk's last position would drop
- * slots that earlier queries of the chunk still see.
+ * slots that earlier queries of the chunk still see.  The kernels check this
+ * per sequence: one that holds fewer than n_query tokens, or whose units were
+ * compacted after the chunk's first position, gets unspecified outputs and
+ * sets DMS_STATUS_CHUNK_INVALID in cache->status.
  *   q    [B][n_query][Hq][D] bf16,   out [B][n_query][Hq][D] float32
- * bf16 caches only (DMS_EUNSUPPORTED otherwise).  n_query >= 1.  Every
- * sequence must hold at least n_query tokens (not checked; outputs are
- * unspecified otherwise).  Chunks of 32 queries or more with head_dim 128
+ * bf16 caches only (DMS_EUNSUPPORTED otherwise).  n_query >= 1.  Chunks of
+ * 32 queries or more with head_dim 128
  * run a tiled kernel that reads the cache once per 32 queries; shorter ones
  * run the split-K decode kernel in launches of 16 / G queries.  Workspace:
  * dms_decode_multi_workspace_bytes.  Errors as for dms_decode_attn.

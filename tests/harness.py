@@ -129,15 +129,18 @@ def check_pages(cache, meta=None):
     return meta
 
 
-def gpu_unit_kv(cache, u):
-    """(k [n, D], v [n, D]) float32 CPU arrays of unit u's slots, gathered on the GPU."""
-    k, v = cache.slot_kv(u)
-    return k.float().numpy(), v.float().numpy()
+def gpu_kv(cache, units=None):
+    """{unit: (k [n, D], v [n, D])} float32 CPU arrays of the units' slots in slot
+    order, read back through dms_export_retained (all slots)."""
+    return {u: (k.float().numpy(), v.float().numpy())
+            for u, (k, v) in cache.slot_kv(units).items()}
 
 
 def check_kv_exact(cache, model, units):
+    units = list(units)
+    kv = gpu_kv(cache, units)
     for u in units:
-        k, v = gpu_unit_kv(cache, u)
+        k, v = kv[u]
         uc = model.units[u]
         assert np.array_equal(k, uc.k), f"unit {u}: key bytes differ"
         assert np.array_equal(v, uc.v), f"unit {u}: value bytes differ"
@@ -162,3 +165,11 @@ def compare_outputs(out_gpu, ref, kv_heads, group, dtype, what=""):
 
 def scale_of(d):
     return 1.0 / math.sqrt(d)
+
+
+def decode_build(kernel):
+    """Context that routes library calls to the build running `kernel` for one-query
+    bf16 decode: "mfma" (the product library) or "generic" (the test build)."""
+    from decode_attention_learned_amd import lib
+
+    return lib.variant("" if kernel == "mfma" else "generic")

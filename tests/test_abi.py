@@ -33,8 +33,18 @@ def test_every_declared_symbol_is_exported(L):
         assert hasattr(L, name), name
 
 
+def test_test_build_exports_the_same_symbols(L):
+    """libdms_generic.so (the test build) is the same ABI."""
+    with lib.variant("generic"):
+        G = lib.load()
+        assert G is not L
+        for name in _declared():
+            assert hasattr(G, name), name
+        assert lib.version() == 4
+
+
 def test_version_and_strerror(L):
-    assert lib.version() == 3
+    assert lib.version() == 4
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(lib.strerror(code), str)
 
@@ -62,9 +72,12 @@ def test_check_shape(L, kw, code):
 
 
 def test_workspace_bytes(L):
-    # header, first chunk per unit (+1), owning unit per chunk (at most
-    # 3 * 512 chunks for fewer than 512 units, else one per unit), merge count per unit
-    assert lib.plan_words(_shape()) == 16 + (4 + 1) + 1536 + 4
+    # header, first chunk per unit (+1), owning unit per chunk (at most 3 * 512
+    # chunks up to 1536 units, else one per unit), merge count and last
+    # compaction position per unit
+    assert lib.plan_words(_shape()) == 16 + (4 + 1) + 1536 + 4 + 4
+    assert lib.plan_words(_shape(batch=100, kv_heads=8)) == 16 + 801 + 1536 + 800 + 800
+    assert lib.plan_words(_shape(batch=256, kv_heads=8)) == 16 + 2049 + 2048 + 2048 + 2048
     assert lib.plan_words(_shape(window=0)) == 0
     assert lib.decode_workspace_bytes(_shape()) > 0
     assert lib.decode_workspace_bytes(_shape(window=0)) == 0
@@ -130,6 +143,15 @@ def test_host_side_errors_need_no_gpu(L):
     assert lib.decode_multi_workspace_bytes(sb) >= lib.decode_workspace_bytes(sb)
     bad = _shape(head_dim=80)
     assert L.dms_compact(ctypes.byref(bad), ctypes.byref(full), None) == lib.DMS_EUNSUPPORTED
+    # export: count_out required, max_per_unit >= 0, all_slots 0 or 1
+    E = L.dms_export_retained
+    assert E(ctypes.byref(s), ctypes.byref(full), 0, 4, None, fake, None, None, None, None) == lib.DMS_EINVAL
+    assert E(ctypes.byref(s), ctypes.byref(full), 0, -1, fake, fake, None, None, None, None) == lib.DMS_EINVAL
+    assert E(ctypes.byref(s), ctypes.byref(full), 2, 4, fake, fake, None, None, None, None) == lib.DMS_EINVAL
+    assert E(ctypes.byref(s), ctypes.byref(null_cache), 0, 4, fake, fake, None, None, None, None) \
+        == lib.DMS_EINVAL
+    assert E(ctypes.byref(bad), ctypes.byref(full), 0, 4, fake, fake, None, None, None, None) \
+        == lib.DMS_EUNSUPPORTED
 
 
 def test_prefill_host_errors(L):
@@ -180,16 +202,3 @@ def test_product_package_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("the oracle", ""), f
-
-
-def test_page_element_index_is_a_permutation():
-    """The fragment-ordered page layout maps (slot, dim) one-to-one onto a page."""
-    import torch
-    from decode_attention_learned_amd.cache import page_element_index
-    for d in (64, 128):
-        k, v = page_element_index(d)
-        assert torch.equal(torch.sort(k.reshape(-1)).values, torch.arange(64 * d))
-        assert torch.equal(torch.sort(v.reshape(-1)).values, torch.arange(64 * d))
-        # eight consecutive dims of a key, and eight consecutive slots of a value, are contiguous
-        assert torch.all(k[:, 1:8] - k[:, 0:7] == 1)
-        assert torch.all(v[1:8, :] - v[0:7, :] == 1)

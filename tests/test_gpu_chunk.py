@@ -140,3 +140,49 @@ def test_prefill_sized_chunk(gpu):
     """A 512-token chunk into a 2048-token cache (chunked prefill)."""
     worst = _run(gpu, 1, 2, 4, 128, 2048, [512], 0.875, 7101)
     say(f"512-token chunk: max err {worst:.2e}")
+
+
+@pytest.mark.parametrize("chunk", [4, 40])
+def test_compaction_between_append_and_chunk_queries_is_flagged(gpu, chunk):
+    """A compaction after the chunk was appended may have dropped keys that its
+    earlier queries still see (and moves chunk tokens into the clean prefix):
+    both chunk kernels (split-K for 4 queries, tiled for 40) flag
+    DMS_STATUS_CHUNK_INVALID; the same chunk queried before compacting is not
+    flagged, and neither is the next chunk after the compaction."""
+    from decode_attention_learned_amd import lib
+    b, hkv, g, d = 2, 2, 4, 128
+    q, k, v, logit = _tokens(b, hkv, g, d, 200 + 2 * chunk, 0.8, 7201 + chunk)
+    cache = DmsCache(b, hkv, g, d, torch.bfloat16, max_pages_per_unit=8, device=gpu)
+    cache.append(k[:, :200].contiguous().to(gpu), v[:, :200].contiguous().to(gpu),
+                 logit[:, :200].contiguous().to(gpu))
+    cache.compact()
+    sl = slice(200, 200 + chunk)
+    cache.append(k[:, sl].contiguous().to(gpu), v[:, sl].contiguous().to(gpu),
+                 logit[:, sl].contiguous().to(gpu))
+    cache.decode_chunk(q[:, sl].contiguous().to(gpu))
+    torch.cuda.synchronize()
+    assert cache.status_word() == 0
+    cache.compact()
+    cache.decode_chunk(q[:, sl].contiguous().to(gpu))
+    torch.cuda.synchronize()
+    assert cache.status_word() == lib.DMS_STATUS_CHUNK_INVALID
+    cache.status.zero_()
+    sl = slice(200 + chunk, 200 + 2 * chunk)
+    cache.append(k[:, sl].contiguous().to(gpu), v[:, sl].contiguous().to(gpu),
+                 logit[:, sl].contiguous().to(gpu))
+    cache.decode_chunk(q[:, sl].contiguous().to(gpu))
+    torch.cuda.synchronize()
+    assert cache.status_word() == 0
+
+
+@pytest.mark.parametrize("chunk", [5, 33])
+def test_chunk_longer_than_the_sequence_is_flagged(gpu, chunk):
+    from decode_attention_learned_amd import lib
+    b, hkv, g, d = 1, 2, 4, 128
+    q, k, v, logit = _tokens(b, hkv, g, d, chunk, 0.5, 7301 + chunk)
+    cache = DmsCache(b, hkv, g, d, torch.bfloat16, max_pages_per_unit=4, device=gpu)
+    cache.append(k[:, :3].contiguous().to(gpu), v[:, :3].contiguous().to(gpu),
+                 logit[:, :3].contiguous().to(gpu))
+    cache.decode_chunk(q.contiguous().to(gpu))
+    torch.cuda.synchronize()
+    assert cache.status_word() == lib.DMS_STATUS_CHUNK_INVALID

@@ -15,8 +15,9 @@ import torch
 
 import workloads as wl
 from decode_attention_learned_amd import DmsCache, lib
-from harness import (HostModel, check_pages, compare_outputs, export_meta, gpu_unit_kv, say, scale_of,
-                     unit_slots)
+from harness import (HostModel, check_pages, compare_outputs, decode_build, export_meta, gpu_kv, say,
+                     scale_of, unit_slots)
+from oracle import dms_oracle as orc
 
 pytestmark = pytest.mark.gpu
 
@@ -48,12 +49,13 @@ def _same_state(a, b, units):
     for key in ("n_slots", "n_clean", "seq_len"):
         assert np.array_equal(ma[key], mb[key]), key
     assert ma["free_top"] == mb["free_top"] and ma["status"] == mb["status"]
+    units = list(units)
+    kva, kvb = gpu_kv(a, units), gpu_kv(b, units)
     for u in units:
         pa, aa = unit_slots(ma, u)
         pb, ab = unit_slots(mb, u)
         assert np.array_equal(pa, pb) and np.array_equal(aa, ab), f"unit {u}: slots differ"
-        ka, va = gpu_unit_kv(a, u)
-        kb, vb = gpu_unit_kv(b, u)
+        (ka, va), (kb, vb) = kva[u], kvb[u]
         assert np.array_equal(ka, kb) and np.array_equal(va, vb), f"unit {u}: K/V differ"
     check_pages(b, mb)
 
@@ -92,8 +94,12 @@ def _run(w, dev, steps, every, rates, a, b, check_every=5, exact=False, model=No
 
 @pytest.mark.parametrize("kernel", ["mfma", "generic"])
 @pytest.mark.parametrize("dims", [(3, 2, 5, 128), (2, 3, 4, 64), (1, 1, 16, 128)])
-def test_step_matches_append_then_decode_bf16(gpu, monkeypatch, kernel, dims):
-    monkeypatch.setenv("DMS_DECODE_KERNEL", kernel)
+def test_step_matches_append_then_decode_bf16(gpu, kernel, dims):
+    with decode_build(kernel):
+        _step_bf16(gpu, kernel, dims)
+
+
+def _step_bf16(gpu, kernel, dims):
     b, hkv, g, d = dims
     w = _workload(b, hkv, g, d, "bf16", 123, 0.6, 8100 + d + g)
     say(f"step vs append+decode, bf16 {kernel} B={b} Hkv={hkv} G={g} D={d}")
@@ -113,12 +119,17 @@ def test_step_matches_append_then_decode_f32(gpu):
 
 
 def test_step_one_chunk_per_unit(gpu):
-    """512 units of even length: the plan gives each unit one chunk."""
+    """512 units of even length: the plan gives each unit one chunk (the headline
+    plan).  Every step's fill-path output is checked against the oracle."""
     w = _workload(64, 8, 4, 128, "bf16", 300, 0.875, 8301)
     a, b, rates = _twins(w, gpu)
     plan = b.plan.cpu()
     assert int(plan[0]) == w.units, "expected one chunk per unit"
-    _run(w, gpu, 40, 16, rates, a, b, check_every=20)
+    model = HostModel(w.batch, w.kv_heads, w.group, w.head_dim, w.window)
+    k, v, logit = wl.prompt_chunk_inputs(w, 0, w.context, rates=rates)
+    model.append(k, v, logit)
+    model.compact()
+    _run(w, gpu, 40, 16, rates, a, b, check_every=20, model=model)
 
 
 def test_step_with_refused_units(gpu):
@@ -140,13 +151,26 @@ def test_step_with_refused_units(gpu):
 
 
 def test_step_full_size_qwen3_8b_cr8(gpu):
-    """The headline shape, as bench.py runs it: a few steps, twin caches."""
+    """The headline shape, as bench.py runs it (dms_append_reserve +
+    dms_decode_attn_fill, compaction every 16 steps): twin caches, and sampled
+    units against the oracle at steps 0, 7, 15, 16 (right after a compaction)
+    and 19."""
     w = wl.get("qwen3_8b_cr8")
     say("step vs append+decode at full size (building two 32768-token caches)")
     tdt = torch.bfloat16
     caches = []
     rates = wl.unit_eviction_rates(w)
-    for _ in range(2):
+    sample = list(range(0, w.units, 37)) + [w.units - 1]
+    mirror = {u: orc.UnitCache(w.window, w.head_dim, dtype=np.float32) for u in sample}
+
+    def feed(k, v, logit):
+        alpha = orc.eviction_decisions(logit.cpu().numpy())
+        for u, uc in mirror.items():
+            bi, h = divmod(u, w.kv_heads)
+            uc.append(alpha[bi, :, h], k[bi, :, h].float().cpu().numpy(),
+                      v[bi, :, h].float().cpu().numpy())
+
+    for ci_ in range(2):
         c = DmsCache(w.batch, w.kv_heads, w.group, w.head_dim, tdt, num_pages=w.units * 140,
                      max_pages_per_unit=140, window=w.window, device=gpu)
         for ci, start in enumerate(range(0, w.context, w.prompt_chunk)):
@@ -154,16 +178,33 @@ def test_step_full_size_qwen3_8b_cr8(gpu):
             k, v, logit = wl.prompt_chunk_inputs(w, ci, n, device=gpu, rates=rates)
             c.append(k, v, logit)
             c.compact()
+            if ci_ == 0:
+                feed(k, v, logit)
+                for uc in mirror.values():
+                    uc.compact()
         caches.append(c)
     a, b = caches
+    scale = scale_of(w.head_dim)
+    worst = 0.0
     for step in range(20):
         q, k, v, logit = wl.decode_step_inputs(w, step, device=gpu, rates=rates)
+        feed(k, v, logit)
         a.append(k, v, logit)
         oa = a.decode(q)
         ob = b.step(k, v, logit, q)
         _agree(oa, ob, False, f"step {step}")
+        if step in (0, 7, 15, 16, 19):
+            ref = {u: uc.attend(q[u // w.kv_heads, (u % w.kv_heads) * w.group:
+                                  (u % w.kv_heads + 1) * w.group].double().cpu().numpy(), scale)
+                   for u, uc in mirror.items()}
+            worst = max(worst, compare_outputs(ob.cpu(), ref, w.kv_heads, w.group, tdt,
+                                               what=f"step {step} (fill path vs oracle)"))
         if (step + 1) % 16 == 0:
             a.compact()
             b.compact()
+            for uc in mirror.values():
+                uc.compact()
     torch.cuda.synchronize()
+    say(f"full-size fill path vs oracle: max abs err {worst:.2e} over {len(sample)} units")
+    assert b.status_word() == 0
     _same_state(a, b, range(0, w.units, 61))

@@ -317,3 +317,58 @@ def test_mask_rows_match_full_mask():
     full = orc.visibility_mask(alpha, 16)
     rows = np.array([0, 5, 15, 16, 17, 60, 89])
     assert np.array_equal(orc.visibility_mask(alpha, 16, rows), full[rows])
+
+
+# ---------------------------------------------------------------- is_visible, the rule itself
+def _is_visible_pins(fn):
+    """Check a visibility predicate fn(i, j, alpha_j, w) against (a) the brute-force
+    process simulation (a token enters when produced; a marked token is removed
+    once `w` more tokens have been produced) over every decision vector of small
+    lengths, and (b) the hand-worked retained sets of the golden fixture."""
+    for window, n in ((1, 8), (2, 8), (3, 7), (4, 7)):
+        for bits in bf.all_decision_vectors(n):
+            seen = bf.run_process(bits, window)
+            for i in range(n):
+                got = [j for j in range(n) if fn(i, j, bits[j], window)]
+                assert got == seen[i], (bits, window, i)
+    g = json.load(open(GOLDEN))["retained_sets"]
+    alpha = [j not in g["kept_positions"] for j in range(g["n_tokens"])]
+    for case in g["cases"]:
+        t = case["t"]
+        got = [j for j in range(g["n_tokens"]) if fn(t, j, alpha[j], g["window"])]
+        assert got == case["retained"], t
+
+
+def test_is_visible_matches_process_and_hand_worked_sets():
+    _is_visible_pins(orc.is_visible)
+
+
+def test_is_visible_agrees_with_visibility_mask():
+    """The scalar rule and the mask builder state the same set (element by element)."""
+    rng = _rng(31)
+    for window in (1, 2, 16):
+        alpha = rng.random(70) < 0.7
+        mask = orc.visibility_mask(alpha, window)
+        for i in range(70):
+            for j in range(70):
+                assert mask[i, j] == orc.is_visible(i, j, alpha[j], window)
+
+
+def test_is_visible_rejects_a_zero_window():
+    with pytest.raises(ValueError):
+        orc.is_visible(3, 1, True, 0)
+
+
+@pytest.mark.parametrize("mutation", ["late_by_one", "early_by_one", "acausal", "decision_ignored"])
+def test_is_visible_pins_catch_planted_mistakes(mutation):
+    """Plausible mistakes in the predicate fail the pins above."""
+    def planted(i, j, alpha_j, window):
+        if mutation == "late_by_one":
+            return (j <= i) and not (bool(alpha_j) and (i - j) > window)
+        if mutation == "early_by_one":
+            return (j <= i) and not (bool(alpha_j) and (i - j) >= window - 1)
+        if mutation == "acausal":
+            return not (bool(alpha_j) and (i - j) >= window)
+        return j <= i
+    with pytest.raises(AssertionError):
+        _is_visible_pins(planted)

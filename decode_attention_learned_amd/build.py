@@ -25,7 +25,8 @@ LIB = os.path.join(HERE, "libdms.so")
 LIB_GENERIC = os.path.join(HERE, "libdms_generic.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "cache_kernels.hip", "decode_kernels.hip", "decode_mfma.hip", "prefill.hip"]
+SOURCES = ["api.hip", "cache_kernels.hip", "decode_kernels.hip", "decode_mfma.hip", "decode_scratch.hip",
+           "prefill.hip"]
 
 # Packed fp32 instructions are switched off for all device code; hipcc's host
 # pass warns that it does not know the feature, which is harmless.

@@ -36,6 +36,7 @@ const char *dms_strerror(int code) {
     case DMS_EUNSUPPORTED: return "unsupported shape or dtype";
     case DMS_EWORKSPACE: return "decode workspace too small";
     case DMS_EHIP: return "HIP launch failed";
+    case DMS_ESCRATCH: return "shape needs more decode scratch than the library's static buffer holds";
     default: return "unknown error code";
   }
 }
@@ -112,6 +113,20 @@ int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
   if (workspace_bytes < dms_decode_workspace_bytes(shape)) return DMS_EWORKSPACE;
   return from_hip(dms::launch_decode(*shape, *cache, q, out, sm_scale, workspace, stream));
+}
+
+int dms_decode_attn_noalloc(const dms_shape *shape, const dms_cache *cache, const void *q,
+                            float *out, float sm_scale, hipStream_t stream) {
+  int rc = dms_check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_cache(shape, cache))) return rc;
+  if (!q || !out) return DMS_EINVAL;
+  if (!aligned16(q) || !aligned16(out)) return DMS_EINVAL;
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
+  if (dms_decode_workspace_bytes(shape) > DMS_NOALLOC_SCRATCH_BYTES) return DMS_ESCRATCH;
+  void *ws = nullptr;
+  if (dms::scratch_address(&ws) != hipSuccess) return DMS_EHIP;
+  return from_hip(dms::launch_decode(*shape, *cache, q, out, sm_scale, ws, stream));
 }
 
 int dms_append_reserve(const dms_shape *shape, const dms_cache *cache, hipStream_t stream) {

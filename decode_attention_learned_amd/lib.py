@@ -26,6 +26,8 @@ DMS_EINVAL = -1
 DMS_EUNSUPPORTED = -2
 DMS_EWORKSPACE = -3
 DMS_EHIP = -4
+DMS_ESCRATCH = -5
+DMS_NOALLOC_SCRATCH_BYTES = 16 << 20
 DMS_STATUS_POOL_EXHAUSTED = 1
 DMS_STATUS_ROW_OVERFLOW = 2
 DMS_STATUS_NOT_EMPTY = 4
@@ -47,6 +49,7 @@ EXPORTS = (
     "dms_release",
     "dms_decode_workspace_bytes",
     "dms_decode_attn",
+    "dms_decode_attn_noalloc",
     "dms_append_reserve",
     "dms_decode_attn_fill",
     "dms_decode_multi_workspace_bytes",
@@ -142,6 +145,7 @@ def load() -> ctypes.CDLL:
         "dms_release": ([SP, CP, ctypes.c_int32, ctypes.c_int32, P], ctypes.c_int),
         "dms_decode_workspace_bytes": ([SP], ctypes.c_size_t),
         "dms_decode_attn": ([SP, CP, P, P, ctypes.c_float, P, ctypes.c_size_t, P], ctypes.c_int),
+        "dms_decode_attn_noalloc": ([SP, CP, P, P, ctypes.c_float, P], ctypes.c_int),
         "dms_append_reserve": ([SP, CP, P], ctypes.c_int),
         "dms_decode_attn_fill": ([SP, CP, P, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t, P],
                                  ctypes.c_int),
@@ -218,6 +222,11 @@ def dms_compact(shape, cache, stream) -> int:
 def dms_decode_attn(shape, cache, q, out, sm_scale, workspace, workspace_bytes, stream) -> int:
     return load().dms_decode_attn(ctypes.byref(shape), ctypes.byref(cache), _p(q), _p(out),
                                   float(sm_scale), _p(workspace), int(workspace_bytes), stream)
+
+
+def dms_decode_attn_noalloc(shape, cache, q, out, sm_scale, stream) -> int:
+    return load().dms_decode_attn_noalloc(ctypes.byref(shape), ctypes.byref(cache), _p(q), _p(out),
+                                          float(sm_scale), stream)
 
 
 def dms_append_reserve(shape, cache, stream) -> int:

@@ -49,6 +49,10 @@ extern "C" {
 #define DMS_EUNSUPPORTED (-2) /* head_dim, group, dtype or page size not built */
 #define DMS_EWORKSPACE (-3)   /* decode workspace smaller than dms_decode_workspace_bytes */
 #define DMS_EHIP (-4)         /* a HIP launch returned an error */
+#define DMS_ESCRATCH (-5)     /* the shape needs more than DMS_NOALLOC_SCRATCH_BYTES of scratch */
+
+/* size of the static per-GPU scratch array of dms_decode_attn_noalloc */
+#define DMS_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /* device-side sticky status bits (cache->status) */
 #define DMS_STATUS_POOL_EXHAUSTED 1u /* free pages ran out; that unit's tokens were dropped */
@@ -223,6 +227,25 @@ size_t dms_decode_workspace_bytes(const dms_shape *shape);
  */
 int dms_decode_attn(const dms_shape *shape, const dms_cache *cache, const void *q, float *out,
                     float sm_scale, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dms_decode_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc.  Same
+ * result and same kernels as dms_decode_attn (identical outputs), but the
+ * split-K partials live in the library's own static device array of
+ * DMS_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held from the first use until
+ * the process ends, instead of a caller's workspace.  The call allocates
+ * nothing.  Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents (nothing in it needs to start at zero): two calls that
+ * overlap in time on one GPU (on different streams) race and give undefined
+ * outputs.  Arguments and host errors as for dms_decode_attn without the
+ * workspace, plus DMS_ESCRATCH when dms_decode_workspace_bytes(shape) exceeds
+ * DMS_NOALLOC_SCRATCH_BYTES (with D = 128: more than 2016 units at G = 16,
+ * more than 8066 at G = 4),
+ * and DMS_EHIP if the array's device address cannot be obtained.
+ */
+int dms_decode_attn_noalloc(const dms_shape *shape, const dms_cache *cache, const void *q,
+                            float *out, float sm_scale, hipStream_t stream);
 
 /*
  * One decode step in two calls, for callers that attend right after

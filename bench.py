@@ -4,10 +4,13 @@
 
 A step is one pass of the whole decode hot path for one attention layer over
 a batch: decide + append the new token of every (sequence, KV head) unit,
-split-K decode attention over the retained entries, and (every
-`compact_every` steps of a cache) compaction.  Steps rotate over independent
-cache replicas so that the working set exceeds the 256 MB last-level cache.
-All inputs are generated on the GPU before the timed region.
+split-K decode attention over the retained entries, and compaction, one
+every `compact_every` steps (rotating over the cache replicas, so that each
+replica is compacted once every `compact_every` of its own steps).  Steps
+rotate over independent cache replicas so that the working set exceeds the
+256 MB last-level cache.  All inputs are generated on the GPU before the
+timed region, which holds only the steps between two HIP events; per-call
+times come from a separate pass over further steps.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -205,6 +208,39 @@ def gathered_tiles(keep, s_len: int, window: int, block: int = 32, tile: int = 3
     return total
 
 
+def prefill_cpu_baseline(name: str = "prefill_8k", threads: int = 1) -> dict:
+    """Time the float64 oracle's masked prefill (prefill_rows) on the host on a
+    bounded sample of the prefill workload: one sequence of the same shape and
+    distributions, query rows [0, 512) and [S - 512, S), every query head.  The
+    oracle computes each row over all S keys (masked), so its cost per row is
+    the same everywhere; the rate is query positions (all heads) per second."""
+    import dataclasses
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import workloads as wl
+    from oracle import dms_oracle as orc
+
+    w = wl.get(name)
+    ws = dataclasses.replace(w, batch=1)
+    q, k, v, logit = wl.prefill_inputs(ws)
+    alpha = orc.eviction_decisions(logit.numpy())
+    s_len = w.context
+    rows = np.r_[0:512, s_len - 512:s_len]
+    qf, kf, vf = q[0].float().numpy(), k[0].float().numpy(), v[0].float().numpy()
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
+        orc.prefill_rows(qf, kf, vf, alpha[0], rows, w.window, 1.0 / math.sqrt(w.head_dim))
+        dt = time.perf_counter() - t0
+    return {"value": round(len(rows) / dt, 2), "unit": "query positions/s", "cores": threads,
+            "kind": "oracle", "cpu": cpu_model(), "seconds": round(dt, 3),
+            "seconds_per_call_extrapolated": round(dt * s_len / len(rows) * w.batch, 1),
+            "sample": f"1 sequence of the {name} shape ({w.q_heads}/{w.kv_heads} heads, D={w.head_dim}, "
+                      f"S={s_len}), query rows [0, 512) and [{s_len - 512}, {s_len}) with all heads, "
+                      f"float64 NumPy, BLAS limited to {threads} thread(s)"}
+
+
 def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
     """Masked prefill on the 8192-token workload, both kernels.
 
@@ -253,12 +289,15 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
         "kv_heads": w.kv_heads, "head_dim": d, "evict_rate": w.evict_rate, "window": w.window,
         "ms": round(ms, 4), "causal_tflop": round(causal / 1e12, 4),
         "visible_pair_tflop": round(visible / 1e12, 4),
+        "query_positions_per_s": round(w.batch * s_len / (ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "kernel": "k_prefill_pack + k_prefill", "achieved": round(tflops, 1),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": prefill_traffic_from_profile(),
                      "algorithmic_bytes_per_call": prefill_algorithmic_bytes(
-                         w.batch, s_len, w.q_heads, w.kv_heads, d)},
+                         w.batch, s_len, w.q_heads, w.kv_heads, d),
+                     "workspace_bytes_per_call": prefill_workspace_traffic(
+                         w.batch, s_len, w.kv_heads, d)},
         "relaxed": {"ms": round(ms_r, 4), "temperature": 1.0, "noise": "logistic",
                     "causal_tflops": round(causal / (ms_r * 1e-3) / 1e12, 1),
                     "frac": round(causal / (ms_r * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
@@ -477,15 +516,22 @@ def prefill_traffic_from_profile():
 
 
 def prefill_algorithmic_bytes(batch: int, seq_len: int, q_heads: int, kv_heads: int, d: int) -> int:
-    """Bytes a dense prefill call cannot avoid moving through HBM (bf16 inputs,
-    fp32 output): the pack pass reads K, V and the logits and writes the two
-    packed copies and the masks; the attention kernel reads Q, each packed
-    copy once, and writes the output."""
+    """Bytes a masked prefill call must move through HBM whatever its design
+    (bf16 inputs, fp32 output): Q, K, V and the logits in once, O out once."""
     kv = batch * seq_len * kv_heads * d * 2 * 2          # K and V, bf16
-    small = batch * seq_len * kv_heads * 4 * 2          # logits in, masks out
+    logits = batch * seq_len * kv_heads * 4
     q = batch * seq_len * q_heads * d * 2
     o = batch * seq_len * q_heads * d * 4
-    return kv + 2 * kv + small + q + 2 * kv + o
+    return kv + logits + q + o
+
+
+def prefill_workspace_traffic(batch: int, seq_len: int, kv_heads: int, d: int) -> int:
+    """Bytes the dense call's own design adds on top (overhead, not algorithmic):
+    the pack pass writes the packed tiles, their zeroed far copy and the masks,
+    and the attention kernel reads them back."""
+    kv = batch * seq_len * kv_heads * d * 2 * 2
+    masks = batch * seq_len * kv_heads * 4
+    return 2 * (2 * kv + masks)
 
 
 def calibrate(gib: float) -> dict:
@@ -571,7 +617,13 @@ def main():
     dev = torch.device("cuda:0")
     w = wl.get(args.workload)
     replicas = args.replicas or w.replicas
-    extra = (args.warmup + args.steps) // replicas + w.compact_every + 64
+    every = w.compact_every
+    # the breakdown pass: per-call events on every step, at least one compaction
+    # of every replica, after the timed window
+    n_break = max(64, every * replicas)
+    total = args.warmup + args.steps + n_break
+    per_rep = (total + replicas - 1) // replicas
+    extra = per_rep + every + 64
 
     log(f"[bench] building {replicas} replica(s) of {w.name}: B={w.batch} Hkv={w.kv_heads} "
         f"G={w.group} D={w.head_dim} context={w.context}")
@@ -579,8 +631,6 @@ def main():
     caches = [build_replica(w, r, dev, extra) for r in range(replicas)]
     log(f"[bench] built in {time.perf_counter() - t_build:.1f} s")
 
-    total = args.warmup + args.steps
-    per_rep = (total + replicas - 1) // replicas
     inputs = [[wl.decode_step_inputs(w, j, device=dev, replica=r, rates=caches[r][1])
                for j in range(per_rep)] for r in range(replicas)]
     outs = [torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
@@ -589,10 +639,15 @@ def main():
 
     scale = 1.0 / math.sqrt(w.head_dim)
 
-    # One step: reserve the token's slot (dms_append_reserve), then the decode
-    # launch takes the token into the attention and writes it to its page
-    # (dms_decode_attn_fill); the same as dms_append + dms_decode_attn.
-    def step(i, ev=None):
+    # Global step i runs on replica i % replicas.  Step i: reserve the token's slot
+    # (dms_append_reserve), then the decode launch takes the token into the
+    # attention and writes it to its page (dms_decode_attn_fill); the same as
+    # dms_append + dms_decode_attn.  Every `every`-th global step also compacts
+    # one replica, in turn, so each replica is compacted once every `every` of
+    # its own steps and any window of steps holds its share of compactions.
+    # With `ev`, per-call events are recorded (the breakdown pass only), and
+    # `peak` collects pages and slots in use of the replica about to be compacted.
+    def step(i, ev=None, peak=None):
         r = i % replicas
         j = i // replicas
         cache = caches[r][0]
@@ -611,11 +666,16 @@ def main():
             cache.fill_and_decode(k, v, logit, q, outs[r], scale)
         if ev is not None:
             ev[2].record()
-        compacted = (j + 1) % w.compact_every == 0
+        compacted = (i + 1) % every == 0
         if compacted:
-            cache.compact()
+            rc = caches[((i + 1) // every - 1) % replicas][0]
+            if peak is not None:
+                peak.append((rc.num_pages - rc.free_top[0], rc.n_slots.sum()))
+            if ev is not None:
+                ev[3].record()
+            rc.compact()
         if ev is not None:
-            ev[3].record()
+            ev[4].record()
         return compacted
 
     for i in range(args.warmup):
@@ -623,20 +683,14 @@ def main():
     torch.cuda.synchronize()
     before = [retained_total(c) for c, _ in caches]
 
-    # Per-call HIP events are recorded on one step in eight of each replica (every
-    # compaction step among them): an event record costs a few microseconds of
-    # queue time, so events on every call would inflate the step it measures.
-    def sampled(i):  # short runs (profiling) sample every step
-        return args.steps < 64 or (i // replicas) % 8 == 7
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] if sampled(args.warmup + i) else None
-           for i in range(args.steps)]
+    # the timed window: the steps alone between two events on the library's stream
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    flags = []
-    for i in range(args.steps):
-        flags.append(step(args.warmup + i, evs[i]))
+    n_compact = 0
+    for i in range(args.warmup, args.warmup + args.steps):
+        n_compact += step(i)
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
@@ -645,11 +699,24 @@ def main():
     if any(status):
         raise RuntimeError(f"device status words {status}")
 
-    t_reserve = [e[0].elapsed_time(e[1]) for e in evs if e is not None]
-    t_decode = [e[1].elapsed_time(e[2]) for e in evs if e is not None]
-    t_compact = [e[2].elapsed_time(e[3]) for e, f in zip(evs, flags) if e is not None and f]
+    # breakdown pass: per-call events on further steps of the same caches
+    i0 = args.warmup + args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_break)]
+    peaks = []
+    flags = [step(i0 + i, evs[i], peaks) for i in range(n_break)]
+    torch.cuda.synchronize()
+    if any(c.status_word() for c, _ in caches):
+        raise RuntimeError("device status set in the breakdown pass")
+    t_reserve = [e[0].elapsed_time(e[1]) for e in evs]
+    t_decode = [e[1].elapsed_time(e[2]) for e in evs]
+    t_compact = [e[3].elapsed_time(e[4]) for e, f in zip(evs, flags) if f]
+    peak_pages = max(int(p) for p, _ in peaks)
+    peak_slots = max(int(n) for _, n in peaks)
+
     ms_step = total_ms / args.steps
     dec_ms = sum(t_decode) / len(t_decode)
+    res_ms = sum(t_reserve) / len(t_reserve)
+    cmp_ms = sum(t_compact) / len(t_compact)
     retained = sum(a[0] + b[0] for a, b in zip(before, after)) / (2 * replicas)
     in_use = sum(a[1] + b[1] for a, b in zip(before, after)) / (2 * replicas)
     elem = 2  # bf16
@@ -657,7 +724,8 @@ def main():
     bytes_read = in_use * w.head_dim * 2 * elem             # including dead, not yet compacted slots
     kv_gbps = bytes_alg / (dec_ms * 1e-3) / 1e9
     tokens_s = w.batch / (ms_step * 1e-3)
-    cr = (w.context + args.warmup / replicas) * w.units / retained
+    cr = (w.context + (args.warmup + args.steps / 2) / replicas) * w.units / retained
+    dense_tokens = w.units * (w.context + per_rep)
 
     result = {
         "metric": METRIC,
@@ -675,18 +743,30 @@ def main():
         "config": {
             "workload": w.name, "batch": w.batch, "kv_heads": w.kv_heads, "q_heads": w.q_heads,
             "head_dim": w.head_dim, "context": w.context, "evict_rate": w.evict_rate,
-            "window": w.window, "compact_every": w.compact_every, "page_size": 64,
+            "window": w.window, "compact_every": every, "page_size": 64,
             "replicas": replicas, "kv_dtype": "bf16", "accumulate": "fp32",
         },
+        "step_calls": ("dms_append + dms_decode_attn" if args.append_launch
+                       else "dms_append_reserve + dms_decode_attn_fill") + " + dms_compact every "
+                      f"{every} steps",
+        "compactions_in_window": n_compact,
         "kv_gbps": round(kv_gbps, 1),
         "hbm_frac": round(kv_gbps / HBM_PEAK_GBPS, 4),
         "compression_ratio": round(cr, 3),
         "retained_per_unit": round(retained / w.units, 1),
-        "decode_attn_us": round(dec_ms * 1e3, 2),
-        "step_calls": ("dms_append + dms_decode_attn" if args.append_launch
-                       else "dms_append_reserve + dms_decode_attn_fill"),
-        "reserve_us": round(1e3 * sum(t_reserve) / len(t_reserve), 2),
-        "compact_us": round(1e3 * sum(t_compact) / max(1, len(t_compact)), 2),
+        "breakdown": {
+            "steps": n_break, "reserve_us": round(res_ms * 1e3, 2),
+            "decode_attn_us": round(dec_ms * 1e3, 2), "compact_us": round(cmp_ms * 1e3, 2),
+            "compactions": len(t_compact),
+            "step_us": round((res_ms + dec_ms + cmp_ms / every) * 1e3, 2),
+        },
+        "memory": {
+            "peak_pages_in_use": peak_pages, "page_bytes": 64 * w.head_dim * 2 * elem,
+            "peak_tokens_in_memory": peak_slots, "dense_tokens": dense_tokens,
+            "dense_over_peak": round(dense_tokens / peak_slots, 3),
+            "per": "one replica (one attention layer, all sequences and KV heads), just before "
+                   "its compaction",
+        },
         "dead_slot_overhead": round(bytes_read / bytes_alg - 1.0, 5),
         "roofline": {
             "bound": "hbm",
@@ -697,9 +777,11 @@ def main():
             "frac": round(kv_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic_from_profile(bytes_alg),
             "algorithmic_bytes_per_launch": int(bytes_alg),
+            "launch_time_from": "HIP events around each dms_decode_attn_fill call of the breakdown pass",
         },
     }
-    log(f"[bench] {tokens_s:.0f} tok/s, {ms_step * 1e3:.1f} us/step, decode {dec_ms * 1e3:.1f} us "
+    log(f"[bench] {tokens_s:.0f} tok/s, {ms_step * 1e3:.1f} us/step ({n_compact} compactions in the "
+        f"window), decode {dec_ms * 1e3:.1f} us "
         f"= {kv_gbps:.0f} GB/s ({100 * kv_gbps / HBM_PEAK_GBPS:.1f}% of HBM peak)")
     # context, not a ceiling: what two torch kernels reach on this GPU over 4 GiB (beyond
     # the MALL), a full read (sum) and a device copy (read + write); torch's reduction does
@@ -726,6 +808,9 @@ def main():
         log(f"[bench] prefill {result['prefill']['ms']:.3f} ms = "
             f"{result['prefill']['roofline']['achieved']:.0f} TFLOP/s causal; gathered "
             f"{result['prefill']['gathered']['ms']:.3f} ms")
+        if not args.no_cpu_baseline:
+            log("[bench] timing the oracle's masked prefill on a 1024-row sample")
+            result["prefill"]["cpu_baseline"] = prefill_cpu_baseline(threads=1)
         torch.cuda.empty_cache()
         result["chunked_prefill"] = chunked_prefill_leg()
         log(f"[bench] chunked prefill: last {result['chunked_prefill']['chunk']} tokens in "

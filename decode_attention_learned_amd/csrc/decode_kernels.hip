@@ -13,9 +13,11 @@
 // by construction; above it, alive iff !alpha or t - pos < w.
 //
 // Split-K: the plan (kept in cache state, see build_plan) cuts each unit's
-// slot list into chunks of C slots; each chunk produces (m, l, o) per head and
-// the last chunk of a unit to finish merges them (count_and_merge): one
-// kernel launch per call.  Scores are
+// slot list into chunks of C slots; each chunk produces (m, l, o) per head,
+// and a unit split into several chunks is merged with the log-sum-exp rule:
+// by a merge launch right after the decode launch for plans of fewer than
+// kTargetChunks units, else by the unit's last chunk to finish inside the
+// decode launch (decode_common.h).  Scores are
 // kept in log2 units (scale * log2 e folded into the score) so that every
 // exponential is exp2.
 #include "decode_common.h"
@@ -161,8 +163,41 @@ __global__ __launch_bounds__(256) void k_decode_generic(
     publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + tid), s_m[tid]);
     publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + tid) + 1, s_l[tid]);
   }
+  if (!fused_merge(units)) return;  // merged by k_merge_partials
   const OutMap om{size_t(u) * G * D, size_t(G) * D, G, D};
   count_and_merge(ci, G, D, plan + L.merge_count, part_ml, part_o, out, om);
+}
+
+// ---------------------------------------------------------------------------
+// Deferred merge (plans of fewer than kTargetChunks units): one workgroup per
+// unit combines the partials its chunks wrote in the decode launch before it
+// on the stream.  Units of one chunk were written by the decode launch itself.
+// Output columns ncol = queries x G of the launch; c0 and C place them as in
+// the decode launch (one query: c0 = 0, C = 1).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_merge_partials(int units, int hkv, int ncol, int G, int D,
+                                                        int c0, int C, const int32_t *__restrict__ plan,
+                                                        const float2 *__restrict__ part_ml,
+                                                        const float *__restrict__ part_o,
+                                                        float *__restrict__ out) {
+  const PlanLayout L = plan_layout(units);
+  const int u = blockIdx.x;
+  const int first = plan[L.first_chunk + u];
+  const int nch = plan[L.first_chunk + u + 1] - first;
+  if (nch <= 1) return;
+  const int b = u / hkv, h = u % hkv;
+  const OutMap om{((size_t(b) * C + c0) * hkv * G + size_t(h) * G) * D, size_t(hkv) * G * D, G, D};
+  merge_unit(first, nch, ncol, D, part_ml, part_o, out, om);
+}
+
+hipError_t launch_merge(const dms_shape &s, const dms_cache &c, const DecodeWorkspace &w, char *ws,
+                        float *out, int ncol, int c0, int C, hipStream_t st) {
+  if (fused_merge(units_of(s))) return hipSuccess;
+  hipLaunchKernelGGL(k_merge_partials, dim3(units_of(s)), dim3(256), 0, st, units_of(s), s.kv_heads,
+                     ncol, s.group, s.head_dim, c0, C, c.plan,
+                     reinterpret_cast<const float2 *>(ws + w.part_ml),
+                     reinterpret_cast<const float *>(ws + w.part_o), out);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -197,7 +232,8 @@ bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, f
                         int n_query, const DecodeFill *fill, bool chunk);
 
 // The decode grid has one workgroup per possible chunk (max_chunks_of(units));
-// workgroups past the plan's chunk count exit at once.  With `fill`, the
+// workgroups past the plan's chunk count exit at once.  Plans of fewer than
+// kTargetChunks units are merged by a second launch (launch_merge).  With `fill`, the
 // matrix-core kernel writes the reserved token itself; the vector kernels
 // take it from a write launch ahead of them.
 hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, float *out,
@@ -208,6 +244,7 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
   bool done = false;
   if (s.kv_dtype == DMS_KV_BF16)
     done = launch_decode_mfma(s, c, q, out, scale_log2, w, ws, st, 1, fill, false);
+  const bool mfma = done;
   if (!done && fill) {
     const hipError_t e = launch_append_write(s, c, fill->k_new, fill->v_new, fill->logit, 1, st);
     if (e != hipSuccess) return e;
@@ -223,7 +260,11 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
                : dispatch_group<uint32_t, 128>(s, c, static_cast<const uint32_t *>(q), out, scale_log2, w, ws, st);
   }
   if (!done) return hipErrorInvalidValue;
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the matrix-core launcher merges after each of its launches itself
+  if (s.kv_dtype == DMS_KV_BF16 && mfma) return hipSuccess;
+  return launch_merge(s, c, w, ws, out, s.group, 0, 1, st);
 }
 
 // Queries of a chunk of n_query tokens just appended (bf16 caches).  Long

@@ -379,7 +379,8 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
       }
     }
   }
-  if (ci.nch > 1) count_and_merge(ci, ncol, D, plan + L.merge_count, part_ml, part_o, out, om);
+  if (ci.nch > 1 && fused_merge(units))  // else merged by k_merge_partials
+    count_and_merge(ci, ncol, D, plan + L.merge_count, part_ml, part_o, out, om);
 }
 
 bool launch_decode_mfma_part(const dms_shape &s, const dms_cache &c, const void *q, float *out,
@@ -406,7 +407,7 @@ bool launch_decode_mfma_part(const dms_shape &s, const dms_cache &c, const void 
   if (s.head_dim == 128) args(k_decode_mfma<128>);
   else if (s.head_dim == 64) args(k_decode_mfma<64>);
   else return false;
-  return true;
+  return launch_merge(s, c, w, ws, out, nq * s.group, c0, C, st) == hipSuccess;
 }
 
 

@@ -117,6 +117,9 @@ hipError_t launch_chunk_attn(const dms_shape &s, const dms_cache &c, const void 
                              float *out, float sm_scale, hipStream_t st);
 hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
                                float *out, float sm_scale, void *ws, hipStream_t st);
+// the deferred split-K merge after a decode launch (nothing for plans that merge in the launch)
+hipError_t launch_merge(const dms_shape &s, const dms_cache &c, const DecodeWorkspace &w, char *ws,
+                        float *out, int ncol, int c0, int C, hipStream_t st);
 // temperature <= 0: the hard rule; > 0: the relaxed mask (noise may be null)
 hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, const void *v,
                           const float *logit, const float *noise, float temperature, int seq_len,

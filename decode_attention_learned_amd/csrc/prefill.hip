@@ -1087,11 +1087,8 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
                        uint4 *tn, int4 *pn, uint4 *an) {
     if (k + 1 < nt) copy(k + 1, tn, pn, an);
     if (active) {
-      if (k >= 1) {
-        if (k == nt && tail_valid < PBN) pv_tile_tail(tp + PK_FRAGS * PFRAG, pb, lane, tail_valid, o);
-        else pv_tile(tp + PK_FRAGS * PFRAG, pb, lane, o);
-      }
-      if (k < nt) qk_tile(t, zero, qf, lane, s);
+      if (k >= 1) pv_tile(tp + PK_FRAGS * PFRAG, pb, lane, o);
+      qk_tile(t, zero, qf, lane, s);
       c_phase2(k, nt, nclean_t, ns, nc, window, t_first, col, quad, p,
                reinterpret_cast<const uint2 *>(a), s, sm, o, pb, c);
     }
@@ -1104,21 +1101,29 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
     ring_barrier();
   };
   // tile 0; the tiles 1 .. nclean_t - 1 wholly below n_clean in whole rounds
-  // of three; the rest on the general path.  Tile k is in buffer k % 3.
-  iteration(0, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
+  // of three; the rest on the general path.  Tile k is in buffer k % 3.  The
+  // PV product of the last tile comes after the loop: its unused tail slots
+  // are cleared there, away from the loop body's registers.
+  if (nt > 0) iteration(0, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
   int k = 1;
   for (; k + 2 < nclean_t; k += 3) {
     clean_iteration(k, sT1, sT0, sT2, sP2, sA2);
     clean_iteration(k + 1, sT2, sT1, sT0, sP0, sA0);
     clean_iteration(k + 2, sT0, sT2, sT1, sP1, sA1);
   }
-  for (; k <= nt; k += 3) {
+  for (; k < nt; k += 3) {
     iteration(k, sT1, sP1, sA1, sT0, sT2, sP2, sA2);
-    if (k + 1 > nt) break;
+    if (k + 1 >= nt) break;
     iteration(k + 1, sT2, sP2, sA2, sT1, sT0, sP0, sA0);
-    if (k + 2 > nt) break;
+    if (k + 2 >= nt) break;
     iteration(k + 2, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
   }
+  if (nt > 0 && active) {
+    const int lt = (nt - 1) % 3;  // the last tile's buffer
+    const uint4 *tl = lt == 0 ? sT0 : (lt == 1 ? sT1 : sT2);
+    pv_tile_tail(tl + PK_FRAGS * PFRAG, pb, lane, tail_valid, o);
+  }
+  ring_barrier();  // every wave is done with the ring before it stages its output there
 
   if (!active) return;
   // the ring buffers are free: every wave has passed the last barrier

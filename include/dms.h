@@ -220,8 +220,9 @@ size_t dms_decode_workspace_bytes(const dms_shape *shape);
  * token.  A unit with no slots gives zeros.  The work of each unit is split
  * into chunks of whole pages following cache->plan (sized on the device from
  * the live lengths: one chunk per unit when the units are many and of even
- * length), and the last chunk of a unit to finish merges the chunk partials
- * with the log-sum-exp rule: one kernel launch per call.
+ * length), and the chunk partials of a split unit are merged with the
+ * log-sum-exp rule: with fewer than 512 units by a second kernel launch on
+ * the stream, else by the unit's last chunk inside the decode launch.
  * The call uses per-unit counters inside cache->plan and leaves them zero;
  * two decode calls on one cache must not run concurrently.
  */

@@ -22,13 +22,24 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_prefill_algorithmic_bytes_by_hand():
-    # B=4, S=8192, 32 query / 8 KV heads, D=128: K and V in (2 x 67.1 MB),
-    # two packed copies out and back in (4 x 134.2 MB), logits in and masks
-    # out (2 x 1.05 MB), Q in (268.4 MB), fp32 output out (536.9 MB)
+    # B=4, S=8192, 32 query / 8 KV heads, D=128: Q in (268.4 MB), K and V in
+    # (2 x 67.1 MB), logits in (1.05 MB), fp32 output out (536.9 MB)
     b, s, hq, hkv, d = 4, 8192, 32, 8, 128
     kv_one = b * s * hkv * d * 2
-    expect = 2 * kv_one + 4 * 2 * kv_one + 2 * b * s * hkv * 4 + b * s * hq * d * 2 + b * s * hq * d * 4
-    assert bench.prefill_algorithmic_bytes(b, s, hq, hkv, d) == expect == 1478492160
+    expect = b * s * hq * d * 2 + 2 * kv_one + b * s * hkv * 4 + b * s * hq * d * 4
+    assert bench.prefill_algorithmic_bytes(b, s, hq, hkv, d) == expect == 940572672
+    # the design's own workspace round trip: packed tiles, zeroed far copy and masks, out and in
+    assert bench.prefill_workspace_traffic(b, s, hkv, d) == 2 * (2 * 2 * kv_one + b * s * hkv * 4)
+
+
+def test_prefill_oracle_baseline_record(monkeypatch):
+    """The prefill baseline record on a small stand-in workload (same code path)."""
+    import dataclasses
+    small = dataclasses.replace(wl.get("prefill_8k"), batch=1, context=1024, kv_heads=2)
+    monkeypatch.setattr(wl, "get", lambda name: small)
+    rec = bench.prefill_cpu_baseline("prefill_8k", threads=1)
+    assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["unit"] == "query positions/s"
+    assert rec["value"] > 0 and "sample" in rec and rec["seconds_per_call_extrapolated"] > 0
 
 
 def _tiles_brute(keep, s_len, window, block=32, tile=32):

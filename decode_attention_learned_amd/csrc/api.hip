@@ -203,14 +203,15 @@ static int check_prefill_shape(const dms_shape *shape, int32_t seq_len) {
   if (shape->batch < 1 || shape->kv_heads < 1 || shape->group < 1 || shape->window < 1)
     return DMS_EINVAL;
   if (seq_len < 0) return DMS_EINVAL;
-  if (shape->head_dim != 128 || shape->kv_dtype != DMS_KV_BF16 || shape->group > 16)
+  if ((shape->head_dim != 128 && shape->head_dim != 64) || shape->kv_dtype != DMS_KV_BF16 ||
+      shape->group > 16)
     return DMS_EUNSUPPORTED;
   return DMS_OK;
 }
 
 size_t dms_prefill_workspace_bytes(const dms_shape *shape, int32_t seq_len) {
   if (check_prefill_shape(shape, seq_len) != DMS_OK) return 0;
-  return dms::prefill_workspace_bytes(shape->batch, shape->kv_heads, seq_len);
+  return dms::prefill_workspace_bytes(shape->batch, shape->kv_heads, seq_len, shape->head_dim);
 }
 
 int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const void *v,
@@ -247,7 +248,7 @@ int dms_prefill_attn_relaxed(const dms_shape *shape, const void *q, const void *
 
 size_t dms_prefill_gathered_workspace_bytes(const dms_shape *shape, int32_t seq_len) {
   if (check_prefill_shape(shape, seq_len) != DMS_OK) return 0;
-  return dms::prefill_gathered_layout(shape->batch, shape->kv_heads, seq_len).total;
+  return dms::prefill_gathered_layout(shape->batch, shape->kv_heads, seq_len, shape->head_dim).total;
 }
 
 int dms_prefill_attn_gathered(const dms_shape *shape, const void *q, const void *k, const void *v,

@@ -128,12 +128,14 @@ hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void
                                    const float *logit, int seq_len, float sm_scale, float *out,
                                    void *ws, hipStream_t st);
 
-// Prefill workspace: per (b, h, 32-key tile) 8 KB of key fragments, 8 KB of
-// value fragments (head_dim 128, bf16) and 32 floats of additive mask.
-inline size_t prefill_workspace_bytes(int batch, int kv_heads, int seq_len) {
+// Prefill workspace: per (b, h, 32-key tile) the key and value fragments
+// (64 D bytes each, bf16: 8 KB each at D = 128) and 32 floats of additive mask.
+inline size_t prefill_workspace_bytes(int batch, int kv_heads, int seq_len, int head_dim) {
   const size_t tiles = size_t(batch) * kv_heads * ((size_t(seq_len) + 31) / 32);
+  const size_t tile_bytes = size_t(128) * head_dim;
   // packed tiles, their masks, packed tiles with masked keys zero (far use)
-  return align256(tiles * 16384) + align256(tiles * 32 * sizeof(float)) + align256(tiles * 16384);
+  return align256(tiles * tile_bytes) + align256(tiles * 32 * sizeof(float)) +
+         align256(tiles * tile_bytes);
 }
 
 // Gathered-key prefill workspace: the dense prefill workspace (for the band
@@ -143,14 +145,16 @@ inline size_t prefill_workspace_bytes(int batch, int kv_heads, int seq_len) {
 struct PrefillGatheredLayout {
   size_t dense_mask, gathered, gathered_pos, gpos, tile_cnt, keptw, total;
 };
-inline PrefillGatheredLayout prefill_gathered_layout(int batch, int kv_heads, int seq_len) {
+inline PrefillGatheredLayout prefill_gathered_layout(int batch, int kv_heads, int seq_len,
+                                                     int head_dim) {
   const size_t units = size_t(batch) * kv_heads;
   const size_t nt = (size_t(seq_len) + 31) / 32;
   const size_t tiles = units * nt;
+  const size_t tile_bytes = size_t(128) * head_dim;
   PrefillGatheredLayout L;
-  L.dense_mask = align256(tiles * 16384);
+  L.dense_mask = align256(tiles * tile_bytes);
   L.gathered = L.dense_mask + align256(tiles * 32 * sizeof(float));
-  L.gathered_pos = L.gathered + align256(tiles * 16384);
+  L.gathered_pos = L.gathered + align256(tiles * tile_bytes);
   L.gpos = L.gathered_pos + align256(tiles * 32 * sizeof(int32_t));
   L.tile_cnt = L.gpos + align256(units * size_t(seq_len) * sizeof(int32_t));
   L.keptw = L.tile_cnt + align256(units * (nt + 1) * sizeof(int32_t));

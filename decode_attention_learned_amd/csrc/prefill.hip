@@ -78,15 +78,22 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 
-constexpr int PD = 128;            // head dimension
 constexpr int PBN = 32;            // keys per tile
 constexpr int PHPW = 4;            // query heads per workgroup
-constexpr int PKS = PD / 32;       // QK products per 16-key tile
-constexpr int PDT = PD / 16;       // PV products per tile
 constexpr int PFRAG = 64;          // uint4 per operand fragment (64 lanes x 16 bytes)
-constexpr int PK_FRAGS = 2 * PKS;  // key fragments per tile
-constexpr int PV_FRAGS = PDT;      // value fragments per tile
 constexpr int PNT = 256;           // threads per workgroup of the prefill kernels
+// Sizes that follow from the head dimension D (64 or 128): QK products per
+// 16-key tile, PV products per tile, key fragments per tile, uint4 per packed
+// tile (D*8: 16 KB at D = 128).  Every kernel and helper below is a template
+// on D and names them by these short local constants.
+#define PDIMS(D)                          \
+  constexpr int PD = (D);                 \
+  constexpr int PKS = PD / 32;            \
+  constexpr int PDT = PD / 16;            \
+  constexpr int PK_FRAGS = 2 * PKS;       \
+  constexpr int PV_FRAGS = PDT;           \
+  constexpr int PTILE_U4 = (PK_FRAGS + PV_FRAGS) * PFRAG;  \
+  (void)PKS; (void)PDT; (void)PK_FRAGS; (void)PV_FRAGS; (void)PTILE_U4
 constexpr float kLazy = 8.0f;      // largest exponent (log2 units) before the reference moves
 
 __device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
@@ -105,8 +112,6 @@ __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pair), one, acc, false);
 }
 
-constexpr int PTILE_U4 = (PK_FRAGS + PV_FRAGS) * PFRAG;  // uint4 per packed tile (16 KB)
-
 // One packed tile per (b, h, tile): [key fragments (8 x 1 KB) | value fragments (8 x 1 KB)],
 // and separately 32 floats of additive mask.
 __device__ __forceinline__ size_t tile_index(int b, int h, int tile, int hkv, int ntiles) {
@@ -123,8 +128,10 @@ struct Softmax {
 
 // QK product of one tile for both query tiles, starting from `init`.
 // The key fragments are read one 16-key half at a time (16 VGPRs).
+template <int D>
 __device__ __forceinline__ void qk_tile(const uint4 *__restrict__ sk, const floatx4 (&init)[2],
-                                        const uint4 (&qf)[2][PKS], int lane, floatx4 (&s)[2][2]) {
+                                        const uint4 (&qf)[2][D / 32], int lane, floatx4 (&s)[2][2]) {
+  PDIMS(D);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     uint4 ka[PKS];
@@ -152,8 +159,10 @@ __device__ __forceinline__ bool crosses(const floatx4 (&s)[2][2], const Softmax 
 
 // Rare path: move the reference of every query whose tile maximum crossed the
 // threshold, and rescale its accumulators.
+template <int D>
 __device__ __forceinline__ void move_reference(const floatx4 (&s)[2][2], Softmax &sm,
-                                               floatx4 (&o)[PDT][2], float c) {
+                                               floatx4 (&o)[D / 16][2], float c) {
+  PDIMS(D);
   const float lazy_raw = kLazy / c;
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
@@ -195,8 +204,10 @@ __device__ __forceinline__ void exponentials(const floatx4 (&s)[2][2], Softmax &
 }
 
 // PV product of one tile; the value fragments are read four at a time.
+template <int D>
 __device__ __forceinline__ void pv_tile(const uint4 *__restrict__ sv, const uint4 (&pb)[2], int lane,
-                                        floatx4 (&o)[PDT][2]) {
+                                        floatx4 (&o)[D / 16][2]) {
+  PDIMS(D);
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     uint4 va[PDT / 2];
@@ -214,8 +225,10 @@ __device__ __forceinline__ void pv_tile(const uint4 *__restrict__ sv, const uint
 // PV product of a cache tile whose slots from `valid` on (0..31) are unused:
 // their value rows may hold anything a recycled page held (even NaN), so they
 // are cleared in the operand (their weights are already zero).
+template <int D>
 __device__ __forceinline__ void pv_tile_tail(const uint4 *__restrict__ sv, const uint4 (&pb)[2],
-                                             int lane, int valid, floatx4 (&o)[PDT][2]) {
+                                             int lane, int valid, floatx4 (&o)[D / 16][2]) {
+  PDIMS(D);
   const int quad = lane >> 4;
   uint32_t keep[4];
 #pragma unroll
@@ -236,12 +249,17 @@ __device__ __forceinline__ void pv_tile_tail(const uint4 *__restrict__ sv, const
 }
 
 // Write a wave's output (32 query rows of one head, o / l) through LDS so that
-// each store instruction covers two whole 512-byte rows.  `stage` holds 16
-// rows of 128 floats (8 KB) for this wave; row r is rotated by 4 r floats so
-// that the sixteen rows of a write land in different banks.
-__device__ __forceinline__ void store_rows(const floatx4 (&o)[PDT][2], const Softmax &sm,
+// each store instruction covers whole rows (two 512-byte rows at D = 128, four
+// 256-byte rows at D = 64).  `stage` holds 16 rows of D floats for this wave;
+// row r is rotated by 4 r floats so that the sixteen rows of a write land in
+// different banks.
+template <int D>
+__device__ __forceinline__ void store_rows(const floatx4 (&o)[D / 16][2], const Softmax &sm,
                                            float *stage, float *out, size_t row0, size_t rstride,
                                            int i0, int S, int lane) {
+  PDIMS(D);
+  constexpr int LPR = D / 4;      // lanes per row (four floats each)
+  constexpr int RPI = 64 / LPR;   // rows per store instruction
   const int col = lane & 15, quad = lane >> 4;
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
@@ -251,17 +269,17 @@ __device__ __forceinline__ void store_rows(const floatx4 (&o)[PDT][2], const Sof
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int dt = 0; dt < PDT; ++dt)
-      *reinterpret_cast<floatx4 *>(stage + col * 128 + ((dt * 16 + quad * 4 + 4 * col) & 127)) =
+      *reinterpret_cast<floatx4 *>(stage + col * D + ((dt * 16 + quad * 4 + 4 * col) & (D - 1))) =
           o[dt][qt] * inv;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int half = lane >> 5, c4 = (lane & 31) * 4;
+    const int sub = lane / LPR, c4 = (lane % LPR) * 4;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const int row = r + half;
+    for (int r = 0; r < 16; r += RPI) {
+      const int row = r + sub;
       const int i = i0 + 16 * qt + row;
-      const floatx4 v = *reinterpret_cast<const floatx4 *>(stage + row * 128 + ((c4 + 4 * row) & 127));
+      const floatx4 v = *reinterpret_cast<const floatx4 *>(stage + row * D + ((c4 + 4 * row) & (D - 1)));
       if (i < S) *reinterpret_cast<floatx4 *>(out + row0 + size_t(i) * rstride + c4) = v;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -277,7 +295,7 @@ __device__ __forceinline__ void store_rows(const floatx4 (&o)[PDT][2], const Sof
 // resource (scalar registers) and the lane's byte offset 16 * tid is the same
 // for every tile, so a copy costs no vector instruction.
 constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer resource word 3 (32-bit data)
-template <int N = PTILE_U4>
+template <int N>
 __device__ __forceinline__ void ring_copy(const uint4 *__restrict__ src, uint4 *dst, int tid,
                                           int wave) {
   static_assert(N % PNT == 0, "whole runs");
@@ -310,16 +328,17 @@ __device__ __forceinline__ void ring_barrier() {
 // tile k (keys `sk`; from the additive mask `sb` on far tiles, from the zeros
 // `sz` on near ones, both read from LDS), at the default issue priority (a
 // raised priority for the phase made the kernel 1-2 % slower).
+template <int D>
 __device__ __forceinline__ void phase1(int k, int ntw, int nfar, const uint4 *__restrict__ sk,
                                        const uint4 *__restrict__ sv, const floatx4 *__restrict__ sb,
-                                       const floatx4 *__restrict__ sz, const uint4 (&qf)[2][PKS],
+                                       const floatx4 *__restrict__ sz, const uint4 (&qf)[2][D / 32],
                                        floatx4 (&s)[2][2], const uint4 (&pb)[2],
-                                       floatx4 (&o)[PDT][2], int lane, int quad) {
-  if (k >= 1 && k - 1 < ntw) pv_tile(sv, pb, lane, o);
+                                       floatx4 (&o)[D / 16][2], int lane, int quad) {
+  if (k >= 1 && k - 1 < ntw) pv_tile<D>(sv, pb, lane, o);
   if (k < ntw) {
     const floatx4 *ip = k < nfar ? sb : sz;
     const floatx4 init[2] = {ip[2 * quad], ip[2 * quad + 1]};
-    qk_tile(sk, init, qf, lane, s);
+    qk_tile<D>(sk, init, qf, lane, s);
   }
 }
 
@@ -328,22 +347,24 @@ __device__ __forceinline__ void phase1(int k, int ntw, int nfar, const uint4 *__
 // 1 and phase 2 with every test on k resolved, for the loops that run only
 // such tiles.  The QK product starts from `init`.  The products run at the
 // default issue priority: a raised one made the dense kernel 2 % slower here.
+template <int D>
 __device__ __forceinline__ void steady_step(const uint4 *__restrict__ sk,
                                             const uint4 *__restrict__ sv, const floatx4 (&init)[2],
-                                            const uint4 (&qf)[2][PKS], floatx4 (&s)[2][2],
-                                            uint4 (&pb)[2], floatx4 (&o)[PDT][2], Softmax &sm,
+                                            const uint4 (&qf)[2][D / 32], floatx4 (&s)[2][2],
+                                            uint4 (&pb)[2], floatx4 (&o)[D / 16][2], Softmax &sm,
                                             float c, int lane) {
-  pv_tile(sv, pb, lane, o);
-  qk_tile(sk, init, qf, lane, s);
-  if (__ballot(crosses(s, sm))) move_reference(s, sm, o, c);
+  pv_tile<D>(sv, pb, lane, o);
+  qk_tile<D>(sk, init, qf, lane, s);
+  if (__ballot(crosses(s, sm))) move_reference<D>(s, sm, o, c);
   exponentials(s, sm, c, pb);
 }
 
 // Phase 2 of tile k: the full rule on near tiles, the reference check, and
 // the exponentials.
+template <int D>
 __device__ __forceinline__ void phase2(int k, int ntw, int nfar, int S, int window, int qi0,
                                        int col, int quad, const floatx4 *__restrict__ sb,
-                                       floatx4 (&s)[2][2], Softmax &sm, floatx4 (&o)[PDT][2],
+                                       floatx4 (&s)[2][2], Softmax &sm, floatx4 (&o)[D / 16][2],
                                        uint4 (&pb)[2], float c) {
   if (k >= ntw) return;
   if (k >= nfar) {
@@ -363,7 +384,7 @@ __device__ __forceinline__ void phase2(int k, int ntw, int nfar, int S, int wind
       }
     }
   }
-  if (__ballot(crosses(s, sm))) move_reference(s, sm, o, c);
+  if (__ballot(crosses(s, sm))) move_reference<D>(s, sm, o, c);
   exponentials(s, sm, c, pb);
 }
 
@@ -372,23 +393,25 @@ __device__ __forceinline__ void phase2(int k, int ntw, int nfar, int S, int wind
 // every query of the workgroup sees, gathered tiles on the edge (a key is seen
 // by query i iff its position <= i - w), and dense band tiles (key j is seen
 // iff i - w < j <= i).
+template <int D>
 __device__ __forceinline__ void g_phase1(int k, int nT, const uint4 *__restrict__ sk,
-                                         const uint4 *__restrict__ sv, const uint4 (&qf)[2][PKS],
+                                         const uint4 *__restrict__ sv, const uint4 (&qf)[2][D / 32],
                                          floatx4 (&s)[2][2], const uint4 (&pb)[2],
-                                         floatx4 (&o)[PDT][2], int lane) {
+                                         floatx4 (&o)[D / 16][2], int lane) {
   __builtin_amdgcn_s_setprio(2);
-  if (k >= 1 && k - 1 < nT) pv_tile(sv, pb, lane, o);
+  if (k >= 1 && k - 1 < nT) pv_tile<D>(sv, pb, lane, o);
   if (k < nT) {
     const floatx4 zero[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-    qk_tile(sk, zero, qf, lane, s);
+    qk_tile<D>(sk, zero, qf, lane, s);
   }
   __builtin_amdgcn_s_setprio(0);
 }
 
+template <int D>
 __device__ __forceinline__ void g_phase2(int k, int nT, int nclean, int ngt, int band_j0, int S,
                                          int window, int qi0, int col, int quad,
                                          const int4 *__restrict__ sp, floatx4 (&s)[2][2],
-                                         Softmax &sm, floatx4 (&o)[PDT][2], uint4 (&pb)[2],
+                                         Softmax &sm, floatx4 (&o)[D / 16][2], uint4 (&pb)[2],
                                          float c) {
   if (k >= nT) return;
   if (k >= nclean) {
@@ -416,7 +439,7 @@ __device__ __forceinline__ void g_phase2(int k, int nT, int nclean, int ngt, int
       }
     }
   }
-  if (__ballot(crosses(s, sm))) move_reference(s, sm, o, c);
+  if (__ballot(crosses(s, sm))) move_reference<D>(s, sm, o, c);
   exponentials(s, sm, c, pb);
 }
 
@@ -424,11 +447,12 @@ __device__ __forceinline__ void g_phase2(int k, int nT, int nclean, int ngt, int
 // Phase 2 of cache tile k for chunk queries: slots below n_clean are seen by
 // every query; above it, slot j is seen by query position t iff it is in use,
 // pos_j <= t, and it is unmarked or t - pos_j < w.
+template <int D>
 __device__ __forceinline__ void c_phase2(int k, int nt, int nclean_t, int ns, int nc, int window,
                                          int t_first, int col, int quad,
                                          const int4 *__restrict__ sp,
                                          const uint2 *__restrict__ sa, floatx4 (&s)[2][2],
-                                         Softmax &sm, floatx4 (&o)[PDT][2], uint4 (&pb)[2],
+                                         Softmax &sm, floatx4 (&o)[D / 16][2], uint4 (&pb)[2],
                                          float c) {
   if (k >= nt) return;
   if (k >= nclean_t) {
@@ -448,15 +472,16 @@ __device__ __forceinline__ void c_phase2(int k, int nt, int nclean_t, int ns, in
       }
     }
   }
-  if (__ballot(crosses(s, sm))) move_reference(s, sm, o, c);
+  if (__ballot(crosses(s, sm))) move_reference<D>(s, sm, o, c);
   exponentials(s, sm, c, pb);
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// pack: one workgroup (512 threads) per (tile, h, b)
+// pack: one workgroup (4 D threads) per (tile, h, b)
 // ---------------------------------------------------------------------------
+template <int D>
 __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles,
                                                       const uint16_t *__restrict__ k,
                                                       const uint16_t *__restrict__ v,
@@ -466,6 +491,7 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
                                                       uint4 *__restrict__ packed,
                                                       float *__restrict__ mask,
                                                       uint4 *__restrict__ packed_far) {
+  PDIMS(D);
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x;
   const int j0 = tile * PBN;
@@ -475,8 +501,8 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
   __shared__ __align__(16) uint16_t sv[PBN][PD + 8];  // row-major values, padded rows
   __shared__ uint32_t s_gone[PBN];                    // key masked (-inf) for far use
 
-  // thread t: key jj = t / 16, dims dc*8 .. +8
-  const int jj = t >> 4, dc = t & 15;
+  // thread t: key jj = t / (D / 8), dims dc*8 .. +8
+  const int jj = t / (PD / 8), dc = t % (PD / 8);
   const int j = j0 + jj;
   uint4 kp = make_uint4(0, 0, 0, 0), vp = make_uint4(0, 0, 0, 0);
   if (j < S) {
@@ -532,10 +558,12 @@ __global__ __launch_bounds__(512) void k_prefill_pack(int S, int hkv, int ntiles
   }
 }
 
+template <int D>
 __global__ __launch_bounds__(PNT, 3) void k_prefill(
     int batch, int S, int hkv, int G, int window, float scale_log2, const uint16_t *__restrict__ q,
     const uint4 *__restrict__ packed, const floatx4 *__restrict__ mask,
     const uint4 *__restrict__ packed_far, float *__restrict__ out) {
+  PDIMS(D);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
@@ -610,7 +638,7 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill(
   __shared__ floatx4 sM0[PBN / 4], sM1[PBN / 4], sM2[PBN / 4];
   __shared__ floatx4 sZ[PBN / 4];  // zeros: the initial scores of a near tile
   auto copy = [&](int tile, uint4 *dt, floatx4 *dm) {
-    ring_copy((tile < nfar ? pkf : pk) + size_t(tile) * PTILE_U4, dt, tid, wave);
+    ring_copy<PTILE_U4>((tile < nfar ? pkf : pk) + size_t(tile) * PTILE_U4, dt, tid, wave);
     ring_copy_keys(pm + size_t(tile) * (PBN / 4), dm, tid);
   };
   copy(0, sT0, sM0);
@@ -626,8 +654,8 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill(
                        floatx4 *mn) {
     if (k + 1 < ntiles) copy(k + 1, tn, mn);
     if (active) {
-      phase1(k, ntw, nfar, t, tp + PK_FRAGS * PFRAG, m, sZ, qf, s, pb, o, lane, quad);
-      phase2(k, ntw, nfar, S, window, qi0, col, quad, m, s, sm, o, pb, c);
+      phase1<D>(k, ntw, nfar, t, tp + PK_FRAGS * PFRAG, m, sZ, qf, s, pb, o, lane, quad);
+      phase2<D>(k, ntw, nfar, S, window, qi0, col, quad, m, s, sm, o, pb, c);
     }
     ring_barrier();
   };
@@ -636,7 +664,7 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill(
     if (k + 1 < ntiles) copy(k + 1, tn, mn);
     if (active) {
       const floatx4 init[2] = {m[2 * quad], m[2 * quad + 1]};
-      steady_step(t, tp + PK_FRAGS * PFRAG, init, qf, s, pb, o, sm, c, lane);
+      steady_step<D>(t, tp + PK_FRAGS * PFRAG, init, qf, s, pb, o, sm, c, lane);
     }
     ring_barrier();
   };
@@ -660,8 +688,8 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill(
 
   if (!active) return;
   // the ring buffers are free: every wave has passed the last barrier
-  float *stage = reinterpret_cast<float *>(wave < 2 ? sT0 : sT1) + (wave & 1) * (16 * 128);
-  store_rows(o, sm, stage, out, (size_t(b) * S * Hq + hq) * PD, size_t(Hq) * PD, qi0, S, lane);
+  float *stage = reinterpret_cast<float *>(wave < 2 ? sT0 : sT1) + (wave & 1) * (16 * PD);
+  store_rows<D>(o, sm, stage, out, (size_t(b) * S * Hq + hq) * PD, size_t(Hq) * PD, qi0, S, lane);
 }
 
 
@@ -731,6 +759,7 @@ __global__ __launch_bounds__(1024) void k_sparse_scan(int S, int hkv, int ntiles
 // 32 gt .. 32 gt + 31 (in position order) in the packed fragment layout, and
 // their positions (INT_MAX past the last kept key).
 // ---------------------------------------------------------------------------
+template <int D>
 __global__ __launch_bounds__(512) void k_sparse_pack(int S, int hkv, int ntiles,
                                                      const uint16_t *__restrict__ k,
                                                      const uint16_t *__restrict__ v,
@@ -738,6 +767,7 @@ __global__ __launch_bounds__(512) void k_sparse_pack(int S, int hkv, int ntiles,
                                                      const int32_t *__restrict__ tile_cnt,
                                                      uint4 *__restrict__ packed,
                                                      int32_t *__restrict__ gposp) {
+  PDIMS(D);
   const int gt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int u = b * hkv + h;
   const int n = tile_cnt[size_t(u) * (ntiles + 1) + ntiles];
@@ -748,7 +778,7 @@ __global__ __launch_bounds__(512) void k_sparse_pack(int S, int hkv, int ntiles,
   uint4 *vdst = kdst + PK_FRAGS * PFRAG;
   __shared__ __align__(16) uint16_t sv[PBN][PD + 8];
 
-  const int jj = t >> 4, dc = t & 15;
+  const int jj = t / (PD / 8), dc = t % (PD / 8);
   const int g = gt * PBN + jj;
   uint4 kp = make_uint4(0, 0, 0, 0), vp = make_uint4(0, 0, 0, 0);
   if (g < n) {
@@ -789,11 +819,13 @@ __device__ __forceinline__ int kept_upto(int x, int S, int ntiles, const int32_t
 // gathered-key prefill, step 3: attention over [gathered tiles | band tiles]
 // with the two-phase schedule of k_prefill.
 // ---------------------------------------------------------------------------
+template <int D>
 __global__ __launch_bounds__(PNT, 3) void k_prefill_gathered(
     int batch, int S, int hkv, int G, int window, float scale_log2, const uint16_t *__restrict__ q,
     const uint4 *__restrict__ dense, const uint4 *__restrict__ gathered,
     const int4 *__restrict__ gposp, const int32_t *__restrict__ tile_cnt,
     const uint32_t *__restrict__ keptw, float *__restrict__ out) {
+  PDIMS(D);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
@@ -869,10 +901,10 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill_gathered(
   __shared__ int4 sP0[PBN / 4], sP1[PBN / 4], sP2[PBN / 4];
   auto copy = [&](int t, uint4 *dt, int4 *dp) {
     if (t < ngt) {
-      ring_copy(gathered + (ubase + t) * PTILE_U4, dt, tid, wave);
+      ring_copy<PTILE_U4>(gathered + (ubase + t) * PTILE_U4, dt, tid, wave);
       ring_copy_keys(gposp + (ubase + t) * (PBN / 4), dp, tid);
     } else {
-      ring_copy(dense + (ubase + tb0 + t - ngt) * PTILE_U4, dt, tid, wave);
+      ring_copy<PTILE_U4>(dense + (ubase + tb0 + t - ngt) * PTILE_U4, dt, tid, wave);
     }
   };
   copy(0, sT0, sP0);
@@ -884,8 +916,8 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill_gathered(
                        int4 *pn) {
     if (k + 1 < nT) copy(k + 1, tn, pn);
     if (active) {
-      g_phase1(k, nT, t, tp + PK_FRAGS * PFRAG, qf, s, pb, o, lane);
-      g_phase2(k, nT, nclean, ngt, band_j0, S, window, qi0, col, quad, p, s, sm, o, pb, c);
+      g_phase1<D>(k, nT, t, tp + PK_FRAGS * PFRAG, qf, s, pb, o, lane);
+      g_phase2<D>(k, nT, nclean, ngt, band_j0, S, window, qi0, col, quad, p, s, sm, o, pb, c);
     }
     ring_barrier();
   };
@@ -893,7 +925,7 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill_gathered(
     if (k + 1 < nT) copy(k + 1, tn, pn);
     if (active) {
       const floatx4 zero[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-      steady_step(t, tp + PK_FRAGS * PFRAG, zero, qf, s, pb, o, sm, c, lane);
+      steady_step<D>(t, tp + PK_FRAGS * PFRAG, zero, qf, s, pb, o, sm, c, lane);
     }
     ring_barrier();
   };
@@ -916,26 +948,47 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill_gathered(
 
   if (!active) return;
   // the ring buffers are free: every wave has passed the last barrier
-  float *stage = reinterpret_cast<float *>(wave < 2 ? sT0 : sT1) + (wave & 1) * (16 * 128);
-  store_rows(o, sm, stage, out, (size_t(b) * S * Hq + hq) * PD, size_t(Hq) * PD, qi0, S, lane);
+  float *stage = reinterpret_cast<float *>(wave < 2 ? sT0 : sT1) + (wave & 1) * (16 * PD);
+  store_rows<D>(o, sm, stage, out, (size_t(b) * S * Hq + hq) * PD, size_t(Hq) * PD, qi0, S, lane);
 }
 
-hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, const void *v,
-                          const float *logit, const float *noise, float temperature, int seq_len,
-                          float sm_scale, float *out, void *ws, hipStream_t st) {
+// The kernels of both head dimensions, instantiated here so that their host
+// launch stubs are emitted.
+#define DMS_PREFILL_KERNELS(D)                                                                    \
+  template __global__ void k_prefill_pack<D>(int, int, int, const uint16_t *, const uint16_t *,     \
+                                             const float *, const float *, float, float, int,       \
+                                             uint4 *, float *, uint4 *);                            \
+  template __global__ void k_prefill<D>(int, int, int, int, int, float, const uint16_t *,           \
+                                        const uint4 *, const floatx4 *, const uint4 *, float *);    \
+  template __global__ void k_sparse_pack<D>(int, int, int, const uint16_t *, const uint16_t *,      \
+                                            const int32_t *, const int32_t *, uint4 *, int32_t *);  \
+  template __global__ void k_prefill_gathered<D>(int, int, int, int, int, float, const uint16_t *,  \
+                                                 const uint4 *, const uint4 *, const int4 *,        \
+                                                 const int32_t *, const uint32_t *, float *);
+DMS_PREFILL_KERNELS(128)
+DMS_PREFILL_KERNELS(64)
+#undef DMS_PREFILL_KERNELS
+
+template <int D>
+static hipError_t launch_prefill_t(const dms_shape &s, const void *q, const void *k, const void *v,
+                                   const float *logit, const float *noise, float temperature,
+                                   int seq_len, float sm_scale, float *out, void *ws, hipStream_t st) {
+  PDIMS(D);
   const int ntiles = (seq_len + PBN - 1) / PBN;
   if (s.kv_heads > 65535 || s.batch > 65535) return hipErrorInvalidValue;  // pack grid y, z
   const size_t tiles = size_t(s.batch) * s.kv_heads * ntiles;
+  const size_t tile_bytes = size_t(PTILE_U4) * 16;
   uint4 *packed = static_cast<uint4 *>(ws);
-  float *mask = reinterpret_cast<float *>(static_cast<char *>(ws) + align256(tiles * 16384));
+  float *mask = reinterpret_cast<float *>(static_cast<char *>(ws) + align256(tiles * tile_bytes));
   // far-tile copy (masked keys zero); the relaxed mask hides no key, so its
   // far tiles read the plain copy
   const int relaxed = temperature > 0.f;
-  uint4 *packed_far = relaxed ? nullptr
-                              : reinterpret_cast<uint4 *>(static_cast<char *>(ws) + align256(tiles * 16384) +
-                                                          align256(tiles * PBN * sizeof(float)));
-  hipLaunchKernelGGL(k_prefill_pack, dim3(ntiles, s.kv_heads, s.batch), dim3(512), 0, st, seq_len,
-                     s.kv_heads, ntiles, static_cast<const uint16_t *>(k),
+  uint4 *packed_far =
+      relaxed ? nullptr
+              : reinterpret_cast<uint4 *>(static_cast<char *>(ws) + align256(tiles * tile_bytes) +
+                                          align256(tiles * PBN * sizeof(float)));
+  hipLaunchKernelGGL(k_prefill_pack<D>, dim3(ntiles, s.kv_heads, s.batch), dim3(4 * D), 0, st,
+                     seq_len, s.kv_heads, ntiles, static_cast<const uint16_t *>(k),
                      static_cast<const uint16_t *>(v), logit, noise,
                      relaxed ? 1.f / temperature : 0.f, 1.f / sm_scale, relaxed, packed, mask,
                      packed_far);
@@ -947,20 +1000,30 @@ hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, cons
   const int per_xcd_pairs = (nbh + 7) / 8;
   const long blocks = long(per_xcd_pairs) * nqb * 8;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_prefill, dim3(unsigned(blocks)), dim3(PNT), 0, st, s.batch, seq_len,
+  hipLaunchKernelGGL(k_prefill<D>, dim3(unsigned(blocks)), dim3(PNT), 0, st, s.batch, seq_len,
                      s.kv_heads, s.group, s.window, sm_scale * 1.4426950408889634f,
                      static_cast<const uint16_t *>(q), packed,
                      reinterpret_cast<const floatx4 *>(mask), packed_far ? packed_far : packed, out);
   return hipGetLastError();
 }
 
+hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, const void *v,
+                          const float *logit, const float *noise, float temperature, int seq_len,
+                          float sm_scale, float *out, void *ws, hipStream_t st) {
+  if (s.head_dim == 128)
+    return launch_prefill_t<128>(s, q, k, v, logit, noise, temperature, seq_len, sm_scale, out, ws, st);
+  if (s.head_dim == 64)
+    return launch_prefill_t<64>(s, q, k, v, logit, noise, temperature, seq_len, sm_scale, out, ws, st);
+  return hipErrorInvalidValue;
+}
 
-hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void *k, const void *v,
-                                   const float *logit, int seq_len, float sm_scale, float *out,
-                                   void *ws, hipStream_t st) {
+template <int D>
+static hipError_t launch_prefill_gathered_t(const dms_shape &s, const void *q, const void *k,
+                                            const void *v, const float *logit, int seq_len,
+                                            float sm_scale, float *out, void *ws, hipStream_t st) {
   const int ntiles = (seq_len + PBN - 1) / PBN;
   if (s.kv_heads > 65535 || s.batch > 65535) return hipErrorInvalidValue;
-  const PrefillGatheredLayout L = prefill_gathered_layout(s.batch, s.kv_heads, seq_len);
+  const PrefillGatheredLayout L = prefill_gathered_layout(s.batch, s.kv_heads, seq_len, D);
   char *base = static_cast<char *>(ws);
   uint4 *dense = reinterpret_cast<uint4 *>(base);
   float *mask = reinterpret_cast<float *>(base + L.dense_mask);
@@ -970,26 +1033,37 @@ hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void
   int32_t *tile_cnt = reinterpret_cast<int32_t *>(base + L.tile_cnt);
   uint32_t *keptw = reinterpret_cast<uint32_t *>(base + L.keptw);
   const uint16_t *k16 = static_cast<const uint16_t *>(k), *v16 = static_cast<const uint16_t *>(v);
-  hipLaunchKernelGGL(k_prefill_pack, dim3(ntiles, s.kv_heads, s.batch), dim3(512), 0, st, seq_len,
-                     s.kv_heads, ntiles, k16, v16, logit, nullptr, 0.f, 1.f, 0, dense, mask, nullptr);
+  hipLaunchKernelGGL(k_prefill_pack<D>, dim3(ntiles, s.kv_heads, s.batch), dim3(4 * D), 0, st,
+                     seq_len, s.kv_heads, ntiles, k16, v16, logit, nullptr, 0.f, 1.f, 0, dense, mask,
+                     nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_sparse_scan, dim3(s.batch * s.kv_heads), dim3(1024), 0, st, seq_len,
                      s.kv_heads, ntiles, logit, gpos, tile_cnt, keptw);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sparse_pack, dim3(ntiles, s.kv_heads, s.batch), dim3(512), 0, st, seq_len,
-                     s.kv_heads, ntiles, k16, v16, gpos, tile_cnt, gathered, gposp);
+  hipLaunchKernelGGL(k_sparse_pack<D>, dim3(ntiles, s.kv_heads, s.batch), dim3(4 * D), 0, st,
+                     seq_len, s.kv_heads, ntiles, k16, v16, gpos, tile_cnt, gathered, gposp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int ngh = (s.group + PHPW - 1) / PHPW;
   const int nbh = s.batch * s.kv_heads * ngh;
   const int nqb = (seq_len + PBN - 1) / PBN;
   const long blocks = long((nbh + 7) / 8) * nqb * 8;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_prefill_gathered, dim3(unsigned(blocks)), dim3(PNT), 0, st, s.batch,
+  hipLaunchKernelGGL(k_prefill_gathered<D>, dim3(unsigned(blocks)), dim3(PNT), 0, st, s.batch,
                      seq_len, s.kv_heads, s.group, s.window, sm_scale * 1.4426950408889634f,
                      static_cast<const uint16_t *>(q), dense, gathered,
                      reinterpret_cast<const int4 *>(gposp), tile_cnt, keptw, out);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void *k, const void *v,
+                                   const float *logit, int seq_len, float sm_scale, float *out,
+                                   void *ws, hipStream_t st) {
+  if (s.head_dim == 128)
+    return launch_prefill_gathered_t<128>(s, q, k, v, logit, seq_len, sm_scale, out, ws, st);
+  if (s.head_dim == 64)
+    return launch_prefill_gathered_t<64>(s, q, k, v, logit, seq_len, sm_scale, out, ws, st);
+  return hipErrorInvalidValue;
 }
 
 
@@ -1003,6 +1077,7 @@ hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void
 // than the chunk, or compacted after the chunk's first position (compact_pos,
 // kept with the plan), is flagged DMS_STATUS_CHUNK_INVALID in `status`.
 // ---------------------------------------------------------------------------
+template <int D>
 __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
     int hkv, int G, int window, int maxp, int C, float scale_log2, const uint16_t *__restrict__ q,
     const uint4 *__restrict__ k_pages, const uint4 *__restrict__ v_pages,
@@ -1011,6 +1086,7 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
     const int32_t *__restrict__ n_clean, const int32_t *__restrict__ seq_len,
     const int32_t *__restrict__ compact_pos, uint32_t *__restrict__ status,
     float *__restrict__ out) {
+  PDIMS(D);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
@@ -1087,9 +1163,9 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
                        uint4 *tn, int4 *pn, uint4 *an) {
     if (k + 1 < nt) copy(k + 1, tn, pn, an);
     if (active) {
-      if (k >= 1) pv_tile(tp + PK_FRAGS * PFRAG, pb, lane, o);
-      qk_tile(t, zero, qf, lane, s);
-      c_phase2(k, nt, nclean_t, ns, nc, window, t_first, col, quad, p,
+      if (k >= 1) pv_tile<D>(tp + PK_FRAGS * PFRAG, pb, lane, o);
+      qk_tile<D>(t, zero, qf, lane, s);
+      c_phase2<D>(k, nt, nclean_t, ns, nc, window, t_first, col, quad, p,
                reinterpret_cast<const uint2 *>(a), s, sm, o, pb, c);
     }
     ring_barrier();
@@ -1097,7 +1173,7 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
   auto clean_iteration = [&](int k, const uint4 *t, const uint4 *tp, uint4 *tn, int4 *pn,
                              uint4 *an) {
     if (k + 1 < nt) copy(k + 1, tn, pn, an);
-    if (active) steady_step(t, tp + PK_FRAGS * PFRAG, zero, qf, s, pb, o, sm, c, lane);
+    if (active) steady_step<D>(t, tp + PK_FRAGS * PFRAG, zero, qf, s, pb, o, sm, c, lane);
     ring_barrier();
   };
   // tile 0; the tiles 1 .. nclean_t - 1 wholly below n_clean in whole rounds
@@ -1121,28 +1197,42 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
   if (nt > 0 && active) {
     const int lt = (nt - 1) % 3;  // the last tile's buffer
     const uint4 *tl = lt == 0 ? sT0 : (lt == 1 ? sT1 : sT2);
-    pv_tile_tail(tl + PK_FRAGS * PFRAG, pb, lane, tail_valid, o);
+    pv_tile_tail<D>(tl + PK_FRAGS * PFRAG, pb, lane, tail_valid, o);
   }
   ring_barrier();  // every wave is done with the ring before it stages its output there
 
   if (!active) return;
   // the ring buffers are free: every wave has passed the last barrier
-  float *stage = reinterpret_cast<float *>(wave < 2 ? sT0 : sT1) + (wave & 1) * (16 * 128);
-  store_rows(o, sm, stage, out, (size_t(b) * C * Hq + hq) * PD, size_t(Hq) * PD, c0, C, lane);
+  float *stage = reinterpret_cast<float *>(wave < 2 ? sT0 : sT1) + (wave & 1) * (16 * PD);
+  store_rows<D>(o, sm, stage, out, (size_t(b) * C * Hq + hq) * PD, size_t(Hq) * PD, c0, C, lane);
 }
+
+template __global__ void k_chunk_attn<128>(int, int, int, int, int, float, const uint16_t *,
+                                           const uint4 *, const uint4 *, const int32_t *, const int4 *,
+                                           const uint4 *, const int32_t *, const int32_t *,
+                                           const int32_t *, const int32_t *, uint32_t *, float *);
+template __global__ void k_chunk_attn<64>(int, int, int, int, int, float, const uint16_t *,
+                                          const uint4 *, const uint4 *, const int32_t *, const int4 *,
+                                          const uint4 *, const int32_t *, const int32_t *,
+                                          const int32_t *, const int32_t *, uint32_t *, float *);
 
 hipError_t launch_chunk_attn(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
                              float *out, float sm_scale, hipStream_t st) {
   const int ngh = (s.group + PHPW - 1) / PHPW;
   const long gy = long(s.batch) * s.kv_heads * ngh;
   if (gy > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_chunk_attn, dim3((n_query + 31) / 32, unsigned(gy)), dim3(256), 0, st,
-                     s.kv_heads, s.group, s.window, s.max_pages_per_unit, n_query,
-                     sm_scale * 1.4426950408889634f, static_cast<const uint16_t *>(q),
-                     static_cast<const uint4 *>(c.k_pages), static_cast<const uint4 *>(c.v_pages),
-                     c.page_table, reinterpret_cast<const int4 *>(c.slot_pos),
-                     reinterpret_cast<const uint4 *>(c.slot_alpha), c.n_slots, c.n_clean, c.seq_len,
-                     c.plan + plan_layout(units_of(s)).compact_pos, c.status, out);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((n_query + 31) / 32, unsigned(gy)), dim3(256), 0, st,
+                       s.kv_heads, s.group, s.window, s.max_pages_per_unit, n_query,
+                       sm_scale * 1.4426950408889634f, static_cast<const uint16_t *>(q),
+                       static_cast<const uint4 *>(c.k_pages), static_cast<const uint4 *>(c.v_pages),
+                       c.page_table, reinterpret_cast<const int4 *>(c.slot_pos),
+                       reinterpret_cast<const uint4 *>(c.slot_alpha), c.n_slots, c.n_clean, c.seq_len,
+                       c.plan + plan_layout(units_of(s)).compact_pos, c.status, out);
+  };
+  if (s.head_dim == 128) go(k_chunk_attn<128>);
+  else if (s.head_dim == 64) go(k_chunk_attn<64>);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -325,9 +325,9 @@ size_t dms_decode_multi_workspace_bytes(const dms_shape *shape);
  * sets DMS_STATUS_CHUNK_INVALID in cache->status.
  *   q    [B][n_query][Hq][D] bf16,   out [B][n_query][Hq][D] float32
  * bf16 caches only (DMS_EUNSUPPORTED otherwise).  n_query >= 1.  Chunks of
- * 32 queries or more with head_dim 128
- * run a tiled kernel that reads the cache once per 32 queries; shorter ones
- * run the split-K decode kernel in launches of 16 / G queries.  Workspace:
+ * 32 queries or more run a tiled kernel that reads the cache once per 32
+ * queries; shorter ones run the split-K decode kernel in launches of 16 / G
+ * queries.  Workspace:
  * dms_decode_multi_workspace_bytes.  Errors as for dms_decode_attn.
  */
 int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const void *q,
@@ -356,7 +356,7 @@ size_t dms_prefill_workspace_bytes(const dms_shape *shape, int32_t seq_len);
  *   out    [B][S][Hq][D]  float32
  *   workspace  at least dms_prefill_workspace_bytes(shape, S) bytes, 16-byte
  *              aligned, no initialisation needed, nothing kept after the call
- * Only batch, kv_heads, group, head_dim (128), window and kv_dtype of
+ * Only batch, kv_heads, group, head_dim (64 or 128), window and kv_dtype of
  * `shape` are read.  The cache is filled separately with dms_append.
  */
 int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const void *v,

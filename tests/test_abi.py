@@ -193,6 +193,11 @@ def test_prefill_host_errors(L):
     assert G(ctypes.byref(bf), fake, fake, fake, fake, 16, -1.0, fake, fake, big, None) == lib.DMS_EINVAL
     assert G(ctypes.byref(bf), fake, fake, fake, fake, 16, 0.1, fake, fake, 10, None) == lib.DMS_EWORKSPACE
     assert lib.prefill_gathered_workspace_bytes(f32, 100) == 0
+    # head_dim 64 is built (tiles of 8 KB), other dims are not
+    d64 = _shape(kv_dtype=lib.DMS_KV_BF16, head_dim=64)
+    d128 = _shape(kv_dtype=lib.DMS_KV_BF16, head_dim=128)
+    assert 0 < lib.prefill_workspace_bytes(d64, 1000) < lib.prefill_workspace_bytes(d128, 1000)
+    assert 0 < lib.prefill_gathered_workspace_bytes(d64, 1000) < lib.prefill_gathered_workspace_bytes(d128, 1000)
 
 
 def test_product_package_does_not_import_oracle():

@@ -186,3 +186,10 @@ def test_chunk_longer_than_the_sequence_is_flagged(gpu, chunk):
     cache.decode_chunk(q.contiguous().to(gpu))
     torch.cuda.synchronize()
     assert cache.status_word() == lib.DMS_STATUS_CHUNK_INVALID
+
+
+@pytest.mark.parametrize("chunk", [32, 70])
+def test_long_chunks_tiled_kernel_head_dim_64(gpu, chunk):
+    """The tiled chunk kernel at head_dim 64 (Llama-3.2-1B heads)."""
+    worst = _run(gpu, 2, 2, 4, 64, 700, [chunk], 0.75, 7400 + chunk)
+    say(f"tiled chunk D=64 {chunk}: max err {worst:.2e}")

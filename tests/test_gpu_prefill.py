@@ -236,3 +236,69 @@ def test_prefill_constant_values(gpu, method):
                   temperature=0.5).cpu().double()
     ref = c.double().expand_as(out)
     assert torch.max(torch.abs(out - ref) / (1e-3 + ref.abs())).item() <= 1e-5
+
+
+# ---------------------------------------------------------------- head_dim 64 (Llama-3.2-1B heads)
+@pytest.mark.parametrize("method", METHODS + ["relaxed"])
+@pytest.mark.parametrize("b,s,hkv,g", [(2, 200, 2, 4), (1, 97, 1, 1), (1, 33, 3, 5), (1, 385, 1, 4),
+                                       (1, 1, 1, 4)])
+def test_prefill_head_dim_64_all_rows(gpu, b, s, hkv, g, method):
+    """head_dim 64: every row against the oracle (dense and gathered: the hard
+    rule; relaxed: the relaxed oracle at temperature 0.5 with logistic noise)."""
+    w, (q, k, v, logit) = _inputs(b, s, hkv, g, d=64, rate=0.7, seed=6100 + s + g)
+    if method == "relaxed":
+        noise = wl.logistic_noise(w)
+        out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16, method="relaxed",
+                      noise=noise.to(gpu), temperature=0.5).cpu()
+        worst = _check_relaxed(out, q, k, v, logit, noise, 0.5, np.arange(s), 16,
+                               what=f"relaxed D=64 B={b} S={s}")
+    else:
+        out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16, method=method).cpu()
+        worst = _check_rows(out, q, k, v, logit, np.arange(s), 16,
+                            what=f"{method} D=64 B={b} S={s} Hkv={hkv} G={g}")
+    say(f"prefill {method} D=64 B={b} S={s} Hkv={hkv} G={g}: max err {worst:.2e}")
+
+
+@pytest.mark.parametrize("method", METHODS)
+@pytest.mark.parametrize("rate", [0.0, 1.0])
+def test_prefill_head_dim_64_special_cases(gpu, method, rate):
+    """head_dim 64, nothing marked: causal SDPA; everything marked: band SDPA
+    of width 16 (torch on CPU, float64)."""
+    w, (q, k, v, logit) = _inputs(1, 150, 2, 4, d=64, rate=rate, seed=6201)
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16, method=method).cpu()
+    i = torch.arange(150)[:, None]
+    j = torch.arange(150)[None, :]
+    mask = (j <= i) if rate == 0.0 else ((i - j >= 0) & (i - j < 16))
+    qq = q[0].double().permute(1, 0, 2)
+    kk = k[0].double().permute(1, 0, 2).repeat_interleave(4, 0)
+    vv = v[0].double().permute(1, 0, 2).repeat_interleave(4, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask, scale=1 / 8.0)
+    assert torch.allclose(out[0].double(), ref.permute(1, 0, 2), rtol=2e-2, atol=2e-2)
+
+
+@pytest.mark.parametrize("method", METHODS + ["relaxed"])
+def test_prefill_head_dim_64_constant_values(gpu, method):
+    w, (q, k, v, logit) = _inputs(2, 333, 2, 4, d=64, rate=0.8, seed=6301)
+    c = torch.linspace(-3.0, 3.0, 64).to(torch.bfloat16)
+    v = c.expand_as(v).contiguous()
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16, method=method,
+                  temperature=0.5).cpu().double()
+    ref = c.double().expand_as(out)
+    assert torch.max(torch.abs(out - ref) / (1e-3 + ref.abs())).item() <= 1e-5
+
+
+@pytest.mark.parametrize("method", METHODS)
+def test_prefill_llama1b_shape_sampled_rows(gpu, method):
+    """A Llama-3.2-1B-shaped prompt (32 query / 8 KV heads, head_dim 64, CR 4):
+    B=4, S=4096; rows [0, 256) and [3840, 4096) of every head against the oracle."""
+    w = wl.Workload(name="prefill_llama", kind="prefill", batch=4, kv_heads=8, group=4, head_dim=64,
+                    dtype="bf16", context=4096, evict_rate=0.75, seed=6401)
+    q, k, v, logit = wl.prefill_inputs(w, device=gpu)
+    out = prefill(q, k, v, logit, window=16, method=method)
+    rows = np.concatenate([np.arange(0, 256), np.arange(3840, 4096)])
+    out_rows = out[:, torch.as_tensor(rows, device=gpu)].cpu()
+    full = torch.zeros((4, 4096, 32, 64), dtype=torch.float32)
+    full[:, torch.as_tensor(rows)] = out_rows
+    worst = _check_rows(full, q.cpu(), k.cpu(), v.cpu(), logit.cpu(), rows, 16,
+                        what=f"llama-shaped {method}")
+    say(f"prefill {method} Llama-1B shape, S=4096: max err {worst:.2e}")

@@ -188,7 +188,6 @@ int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const 
                           size_t workspace_bytes, hipStream_t stream) {
   int rc = dms_check_shape(shape);
   if (rc) return rc;
-  if (shape->kv_dtype != DMS_KV_BF16) return DMS_EUNSUPPORTED;
   if ((rc = check_cache(shape, cache))) return rc;
   if (n_query < 1) return DMS_EINVAL;
   if (!q || !out || !workspace) return DMS_EINVAL;

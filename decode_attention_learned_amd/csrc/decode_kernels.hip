@@ -29,7 +29,11 @@ namespace dms {
 //
 // One workgroup per chunk.  Tiles of 32 slots are staged in LDS as float32;
 // scores are formed per (head, slot), each head's online softmax is advanced
-// by one wave, and each thread accumulates its (head, d) outputs.
+// by one wave, and each thread accumulates its (head, d) outputs.  One query
+// per sequence: query cq of a chunk of C tokens just appended, at position
+// seq_len - C + cq (decode: C = 1, cq = 0); slots above n_clean are seen when
+// their position is at most the query's and they are alive there.
+// `chunk_status` (chunk queries only, else null): as in the matrix-core kernel.
 // ---------------------------------------------------------------------------
 constexpr int kGenTile = 32;
 
@@ -42,21 +46,28 @@ __device__ __forceinline__ float load_elem<uint32_t>(const uint32_t *p) { return
 
 template <typename E, int D, int G>
 __global__ __launch_bounds__(256) void k_decode_generic(
-    int units, int hkv, int window, int maxp, float scale_log2, const E *__restrict__ q,
-    const E *__restrict__ k_pages, const E *__restrict__ v_pages,
+    int units, int hkv, int window, int maxp, float scale_log2, int C, int cq,
+    const E *__restrict__ q, const E *__restrict__ k_pages, const E *__restrict__ v_pages,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ slot_pos,
     const uint8_t *__restrict__ slot_alpha, const int32_t *__restrict__ n_slots,
     const int32_t *__restrict__ n_clean_arr, const int32_t *__restrict__ seq_len,
-    int32_t *__restrict__ plan, float2 *__restrict__ part_ml, float *__restrict__ part_o,
-    float *__restrict__ out) {
+    int32_t *__restrict__ plan, uint32_t *__restrict__ chunk_status, float2 *__restrict__ part_ml,
+    float *__restrict__ part_o, float *__restrict__ out) {
   constexpr int OPT = (G * D + 255) / 256;  // outputs per thread
   const PlanLayout L = plan_layout(units);
   const int c = blockIdx.x;
   ChunkInfo ci;
   if (!locate_chunk(c, hkv, plan, n_slots, n_clean_arr, seq_len, L, ci)) return;
   const int u = ci.unit, b = ci.b, h = ci.h;
-  const int s_begin = ci.s_begin, s_end = ci.s_end, t = ci.t, nclean = ci.nclean;
+  const int s_begin = ci.s_begin, s_end = ci.s_end, nclean = ci.nclean;
+  const int t = ci.t - (C - 1) + cq;  // the query's position
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  if (chunk_status != nullptr && cq == 0 && c == ci.first && tid == 0) {
+    const int p0 = ci.t - (C - 1);  // the chunk's first position
+    if (p0 < 0 || plan[L.compact_pos + u] > p0) atomicOr(chunk_status, DMS_STATUS_CHUNK_INVALID);
+  }
+  // output of column x / D (query head h * G + x / D)
+  const OutMap om{((size_t(b) * C + cq) * hkv * G + size_t(h) * G) * D, size_t(hkv) * G * D, G, D};
 
   __shared__ float s_q[G][D];
   __shared__ float s_k[kGenTile][D + 1];
@@ -66,7 +77,7 @@ __global__ __launch_bounds__(256) void k_decode_generic(
 
   for (int x = tid; x < G * D; x += 256) {
     const int g = x / D, d = x % D;
-    s_q[g][d] = load_elem<E>(q + (size_t(b) * hkv * G + h * G + g) * D + d);
+    s_q[g][d] = load_elem<E>(q + ((size_t(b) * C + cq) * hkv * G + h * G + g) * D + d);
   }
   if (tid < G) {
     s_m[tid] = -INFINITY;
@@ -98,7 +109,8 @@ __global__ __launch_bounds__(256) void k_decode_generic(
         bool live = slot < nclean;
         if (!live) {
           const size_t m = size_t(page) * kPage + off0 + j;
-          live = slot_alpha[m] == 0 || (t - slot_pos[m]) < window;
+          const int pos = slot_pos[m];
+          live = pos <= t && (slot_alpha[m] == 0 || (t - pos) < window);
         }
         if (live) {
           float dot = 0.f;
@@ -149,7 +161,7 @@ __global__ __launch_bounds__(256) void k_decode_generic(
       if (x < G * D) {
         const int g = x / D;
         const float l = s_l[g];
-        out[size_t(u) * G * D + x] = l > 0.f ? acc[r] / l : 0.f;
+        out[om.at(x)] = l > 0.f ? acc[r] / l : 0.f;
       }
     }
     return;
@@ -164,7 +176,6 @@ __global__ __launch_bounds__(256) void k_decode_generic(
     publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + tid) + 1, s_l[tid]);
   }
   if (!fused_merge(units)) return;  // merged by k_merge_partials
-  const OutMap om{size_t(u) * G * D, size_t(G) * D, G, D};
   count_and_merge(ci, G, D, plan + L.merge_count, part_ml, part_o, out, om);
 }
 
@@ -203,23 +214,28 @@ hipError_t launch_merge(const dms_shape &s, const dms_cache &c, const DecodeWork
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
+// query cq of a chunk of C (decode: C = 1, cq = 0); chunk_status only for chunk queries
 template <typename E, int D, int G>
 static void launch_generic_t(const dms_shape &s, const dms_cache &c, const E *q, float *out,
-                             float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st) {
+                             float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
+                             int C, int cq, uint32_t *chunk_status) {
   hipLaunchKernelGGL((k_decode_generic<E, D, G>), dim3(w.max_chunks), dim3(256), 0, st,
-                     units_of(s), s.kv_heads,
-                     s.window, s.max_pages_per_unit, scale_log2, q, static_cast<const E *>(c.k_pages),
-                     static_cast<const E *>(c.v_pages), c.page_table, c.slot_pos, c.slot_alpha,
-                     c.n_slots, c.n_clean, c.seq_len, c.plan,
-                     reinterpret_cast<float2 *>(ws + w.part_ml), reinterpret_cast<float *>(ws + w.part_o),
-                     out);
+                     units_of(s), s.kv_heads, s.window, s.max_pages_per_unit, scale_log2, C, cq, q,
+                     static_cast<const E *>(c.k_pages), static_cast<const E *>(c.v_pages),
+                     c.page_table, c.slot_pos, c.slot_alpha, c.n_slots, c.n_clean, c.seq_len,
+                     c.plan, chunk_status, reinterpret_cast<float2 *>(ws + w.part_ml),
+                     reinterpret_cast<float *>(ws + w.part_o), out);
 }
 
 template <typename E, int D>
 static bool dispatch_group(const dms_shape &s, const dms_cache &c, const E *q, float *out,
-                           float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st) {
+                           float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
+                           int C = 1, int cq = 0, uint32_t *chunk_status = nullptr) {
   switch (s.group) {
-#define DMS_G(GG) case GG: launch_generic_t<E, D, GG>(s, c, q, out, scale_log2, w, ws, st); return true;
+#define DMS_G(GG)                                                                       \
+  case GG:                                                                              \
+    launch_generic_t<E, D, GG>(s, c, q, out, scale_log2, w, ws, st, C, cq, chunk_status); \
+    return true;
     DMS_G(1) DMS_G(2) DMS_G(3) DMS_G(4) DMS_G(5) DMS_G(6) DMS_G(7) DMS_G(8)
     DMS_G(9) DMS_G(10) DMS_G(11) DMS_G(12) DMS_G(13) DMS_G(14) DMS_G(15) DMS_G(16)
 #undef DMS_G
@@ -267,19 +283,34 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
   return launch_merge(s, c, w, ws, out, s.group, 0, 1, st);
 }
 
-// Queries of a chunk of n_query tokens just appended (bf16 caches).  Long
-// chunks (32 queries or more) run the tiled chunk kernel, one
-// pass over the cache per 32 queries; shorter ones run the split-K decode
-// kernel in launches of at most 16 / G queries.  The workspace holds partials
-// for 16 columns.
+// Queries of a chunk of n_query tokens just appended.  bf16 caches: long
+// chunks (32 queries or more) run the tiled chunk kernel, one pass over the
+// cache per 32 queries; shorter ones run the split-K decode kernel in
+// launches of at most 16 / G queries.  float32 caches: the vector kernel, one
+// launch per query position.  The workspace holds partials for 16 columns.
 constexpr int kChunkKernelMin = 32;
 
 hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
                                float *out, float sm_scale, void *wsv, hipStream_t st) {
-  if (n_query >= kChunkKernelMin && s.group <= 16)
-    return launch_chunk_attn(s, c, q, n_query, out, sm_scale, st);
   const DecodeWorkspace w = decode_workspace_layout(units_of(s), 16, s.head_dim);
   const float scale_log2 = sm_scale * 1.4426950408889634f;
+  if (s.kv_dtype == DMS_KV_F32) {
+    char *ws = static_cast<char *>(wsv);
+    const uint32_t *q32 = static_cast<const uint32_t *>(q);
+    for (int cq = 0; cq < n_query; ++cq) {
+      const bool ok = s.head_dim == 64
+                          ? dispatch_group<uint32_t, 64>(s, c, q32, out, scale_log2, w, ws, st, n_query, cq, c.status)
+                          : dispatch_group<uint32_t, 128>(s, c, q32, out, scale_log2, w, ws, st, n_query, cq, c.status);
+      if (!ok) return hipErrorInvalidValue;
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const hipError_t m = launch_merge(s, c, w, ws, out, s.group, cq, n_query, st);
+      if (m != hipSuccess) return m;
+    }
+    return hipSuccess;
+  }
+  if (n_query >= kChunkKernelMin && s.group <= 16)
+    return launch_chunk_attn(s, c, q, n_query, out, sm_scale, st);
   if (!launch_decode_mfma(s, c, q, out, scale_log2, w, static_cast<char *>(wsv), st, n_query,
                           nullptr, true))
     return hipErrorInvalidValue;

@@ -323,11 +323,11 @@ size_t dms_decode_multi_workspace_bytes(const dms_shape *shape);
  * per sequence: one that holds fewer than n_query tokens, or whose units were
  * compacted after the chunk's first position, gets unspecified outputs and
  * sets DMS_STATUS_CHUNK_INVALID in cache->status.
- *   q    [B][n_query][Hq][D] bf16,   out [B][n_query][Hq][D] float32
- * bf16 caches only (DMS_EUNSUPPORTED otherwise).  n_query >= 1.  Chunks of
- * 32 queries or more run a tiled kernel that reads the cache once per 32
- * queries; shorter ones run the split-K decode kernel in launches of 16 / G
- * queries.  Workspace:
+ *   q    [B][n_query][Hq][D] in kv_dtype,   out [B][n_query][Hq][D] float32
+ * n_query >= 1.  bf16 caches: chunks of 32 queries or more run a tiled kernel
+ * that reads the cache once per 32 queries; shorter ones run the split-K
+ * decode kernel in launches of 16 / G queries.  float32 caches run the vector
+ * decode kernel once per query position.  Workspace:
  * dms_decode_multi_workspace_bytes.  Errors as for dms_decode_attn.
  */
 int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const void *q,

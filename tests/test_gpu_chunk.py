@@ -193,3 +193,54 @@ def test_long_chunks_tiled_kernel_head_dim_64(gpu, chunk):
     """The tiled chunk kernel at head_dim 64 (Llama-3.2-1B heads)."""
     worst = _run(gpu, 2, 2, 4, 64, 700, [chunk], 0.75, 7400 + chunk)
     say(f"tiled chunk D=64 {chunk}: max err {worst:.2e}")
+
+
+@pytest.mark.parametrize("chunks,d", [([1, 3], 64), ([40], 64), ([5, 17], 128)])
+def test_chunk_queries_float32_cache(gpu, chunks, d):
+    """float32 caches: chunk queries through the vector kernel (one launch per
+    query position), against the oracle at the float32 tolerance (1e-5 max
+    abs), with compaction between chunks; G = 2 (the tiny float32 shape's)."""
+    from harness import F32_ATOL
+    b, hkv, g, prompt, window = 1, 2, 2, 300, 16
+    total = prompt + sum(chunks)
+    w = wl.Workload(name="chunk_f32", kind="prefill", batch=b, kv_heads=hkv, group=g, head_dim=d,
+                    dtype="f32", context=total, evict_rate=0.5, seed=7500 + d + len(chunks))
+    q, k, v, logit = wl.prefill_inputs(w)
+    cache = DmsCache(b, hkv, g, d, torch.float32, max_pages_per_unit=(total + 63) // 64 + 1,
+                     window=window, device=gpu)
+    cache.append(k[:, :prompt].contiguous().to(gpu), v[:, :prompt].contiguous().to(gpu),
+                 logit[:, :prompt].contiguous().to(gpu))
+    cache.compact()
+    alpha = orc.eviction_decisions(logit.numpy())
+    scale = 1.0 / math.sqrt(d)
+    t0, worst = prompt, 0.0
+    for n in chunks:
+        sl = slice(t0, t0 + n)
+        cache.append(k[:, sl].contiguous().to(gpu), v[:, sl].contiguous().to(gpu),
+                     logit[:, sl].contiguous().to(gpu))
+        out = cache.decode_chunk(q[:, sl].contiguous().to(gpu)).cpu().double().numpy()
+        assert cache.status_word() == 0
+        for h in range(hkv):
+            for c in range(n):
+                ref = orc.decode_output(q[0, t0 + c, h * g:(h + 1) * g].double().numpy(),
+                                        k[0, :, h].double().numpy(), v[0, :, h].double().numpy(),
+                                        alpha[0, :, h], t0 + c, window, scale)
+                err = np.abs(out[0, c, h * g:(h + 1) * g] - ref).max()
+                worst = max(worst, float(err))
+                assert err <= F32_ATOL, f"chunk at {t0}, query {c}, head {h}: {err:.3g}"
+        cache.compact()
+        t0 += n
+    say(f"float32 chunk queries {chunks} D={d}: max abs err {worst:.2e}")
+
+
+def test_float32_chunk_compacted_after_append_is_flagged(gpu):
+    from decode_attention_learned_amd import lib
+    w = wl.Workload(name="chunk_f32_flag", kind="prefill", batch=1, kv_heads=2, group=2, head_dim=64,
+                    dtype="f32", context=120, evict_rate=0.8, seed=7601)
+    q, k, v, logit = wl.prefill_inputs(w)
+    cache = DmsCache(1, 2, 2, 64, torch.float32, max_pages_per_unit=4, device=gpu)
+    cache.append(k.to(gpu), v.to(gpu), logit.to(gpu))
+    cache.compact()
+    cache.decode_chunk(q[:, 112:].contiguous().to(gpu))
+    torch.cuda.synchronize()
+    assert cache.status_word() == lib.DMS_STATUS_CHUNK_INVALID

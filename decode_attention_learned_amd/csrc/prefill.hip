@@ -755,9 +755,14 @@ __global__ __launch_bounds__(1024) void k_sparse_scan(int S, int hkv, int ntiles
 }
 
 // ---------------------------------------------------------------------------
-// gathered-key prefill, step 2: gathered tile gt of a unit holds kept keys
-// 32 gt .. 32 gt + 31 (in position order) in the packed fragment layout, and
-// their positions (INT_MAX past the last kept key).
+// gathered-key prefill, step 2, one workgroup (4 D threads) per (tile, h, b):
+//   * the values of dense tile `tile` (keys 32 tile .. +31) in the transposed
+//     fragment order, written to the value half of the dense tile (the band
+//     tiles' values; their keys are gathered by the attention kernel itself
+//     from K), zero past the end of the sequence;
+//   * gathered tile gt = tile of the unit, if it holds kept keys: kept keys
+//     32 gt .. 32 gt + 31 (in position order) in the packed fragment layout,
+//     and their positions (INT_MAX past the last kept key).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(512) void k_sparse_pack(int S, int hkv, int ntiles,
@@ -765,44 +770,57 @@ __global__ __launch_bounds__(512) void k_sparse_pack(int S, int hkv, int ntiles,
                                                      const uint16_t *__restrict__ v,
                                                      const int32_t *__restrict__ gpos,
                                                      const int32_t *__restrict__ tile_cnt,
+                                                     uint4 *__restrict__ dense,
                                                      uint4 *__restrict__ packed,
                                                      int32_t *__restrict__ gposp) {
   PDIMS(D);
   const int gt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int u = b * hkv + h;
   const int n = tile_cnt[size_t(u) * (ntiles + 1) + ntiles];
-  if (gt * PBN >= n) return;
   const int t = threadIdx.x;
   const size_t T = tile_index(b, h, gt, hkv, ntiles);
-  uint4 *kdst = packed + T * PTILE_U4;
-  uint4 *vdst = kdst + PK_FRAGS * PFRAG;
-  __shared__ __align__(16) uint16_t sv[PBN][PD + 8];
+  __shared__ __align__(16) uint16_t sv[PBN][PD + 8];   // dense tile values, row-major
+  __shared__ __align__(16) uint16_t sg[PBN][PD + 8];   // gathered tile values, row-major
+  const bool gathered = gt * PBN < n;
 
   const int jj = t / (PD / 8), dc = t % (PD / 8);
-  const int g = gt * PBN + jj;
-  uint4 kp = make_uint4(0, 0, 0, 0), vp = make_uint4(0, 0, 0, 0);
-  if (g < n) {
-    const int j = gpos[size_t(u) * S + g];
-    const size_t off = ((size_t(b) * S + j) * hkv + h) * PD + dc * 8;
-    kp = *reinterpret_cast<const uint4 *>(k + off);
-    vp = *reinterpret_cast<const uint4 *>(v + off);
-  }
-  const int tt = (jj & 7) >> 2, row = 4 * (jj >> 3) + (jj & 3);
-  const int ks = dc >> 2, qd = dc & 3;
-  kdst[(tt * PKS + ks) * PFRAG + qd * 16 + row] = kp;
-  *reinterpret_cast<uint4 *>(&sv[jj][dc * 8]) = vp;
-  if (t < PBN) {
-    const int gg = gt * PBN + t;
-    gposp[T * PBN + t] = gg < n ? gpos[size_t(u) * S + gg] : INT_MAX;
+  const int j = gt * PBN + jj;
+  *reinterpret_cast<uint4 *>(&sv[jj][dc * 8]) =
+      j < S ? *reinterpret_cast<const uint4 *>(v + ((size_t(b) * S + j) * hkv + h) * PD + dc * 8)
+            : make_uint4(0, 0, 0, 0);
+  if (gathered) {
+    const int g = gt * PBN + jj;
+    uint4 kp = make_uint4(0, 0, 0, 0), vp = make_uint4(0, 0, 0, 0);
+    if (g < n) {
+      const int jg = gpos[size_t(u) * S + g];
+      const size_t off = ((size_t(b) * S + jg) * hkv + h) * PD + dc * 8;
+      kp = *reinterpret_cast<const uint4 *>(k + off);
+      vp = *reinterpret_cast<const uint4 *>(v + off);
+    }
+    const int tt = (jj & 7) >> 2, row = 4 * (jj >> 3) + (jj & 3);
+    const int ks = dc >> 2, qd = dc & 3;
+    packed[T * PTILE_U4 + (tt * PKS + ks) * PFRAG + qd * 16 + row] = kp;
+    *reinterpret_cast<uint4 *>(&sg[jj][dc * 8]) = vp;
+    if (t < PBN) {
+      const int gg = gt * PBN + t;
+      gposp[T * PBN + t] = gg < n ? gpos[size_t(u) * S + gg] : INT_MAX;
+    }
   }
   __syncthreads();
+  // value fragment dt = t / 64, lane l = t % 64: dim dt*16 + l % 16, keys 8*(l/16) .. +8
   const int dt = t >> 6, l = t & 63;
   const int d = dt * 16 + (l & 15), k0 = 8 * (l >> 4);
   uint32_t w[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     w[e] = uint32_t(sv[k0 + 2 * e][d]) | (uint32_t(sv[k0 + 2 * e + 1][d]) << 16);
-  vdst[t] = make_uint4(w[0], w[1], w[2], w[3]);
+  dense[T * PTILE_U4 + PK_FRAGS * PFRAG + t] = make_uint4(w[0], w[1], w[2], w[3]);
+  if (gathered) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = uint32_t(sg[k0 + 2 * e][d]) | (uint32_t(sg[k0 + 2 * e + 1][d]) << 16);
+    packed[T * PTILE_U4 + PK_FRAGS * PFRAG + t] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
 // kept keys of unit u at positions <= x
@@ -822,7 +840,8 @@ __device__ __forceinline__ int kept_upto(int x, int S, int ntiles, const int32_t
 template <int D>
 __global__ __launch_bounds__(PNT, 3) void k_prefill_gathered(
     int batch, int S, int hkv, int G, int window, float scale_log2, const uint16_t *__restrict__ q,
-    const uint4 *__restrict__ dense, const uint4 *__restrict__ gathered,
+    const uint16_t *__restrict__ kmat, const uint4 *__restrict__ dense,
+    const uint4 *__restrict__ gathered,
     const int4 *__restrict__ gposp, const int32_t *__restrict__ tile_cnt,
     const uint32_t *__restrict__ keptw, float *__restrict__ out) {
   PDIMS(D);
@@ -895,7 +914,10 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill_gathered(
   const float c = scale_log2;
 
   // The tile ring of k_prefill; tile t comes from the gathered layout (t <
-  // ngt, with its key positions) or the dense one.
+  // ngt, with its key positions) or is a band tile: its key fragments are
+  // gathered by the load unit straight from K (each lane names the 16 bytes
+  // of the key row and dims its fragment lane holds, so the 1 KB a copy
+  // instruction writes is one fragment), its values come packed.
   const size_t ubase = size_t(u) * ntiles_all;
   __shared__ uint4 sT0[PTILE_U4], sT1[PTILE_U4], sT2[PTILE_U4];
   __shared__ int4 sP0[PBN / 4], sP1[PBN / 4], sP2[PBN / 4];
@@ -904,7 +926,18 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill_gathered(
       ring_copy<PTILE_U4>(gathered + (ubase + t) * PTILE_U4, dt, tid, wave);
       ring_copy_keys(gposp + (ubase + t) * (PBN / 4), dp, tid);
     } else {
-      ring_copy<PTILE_U4>(dense + (ubase + tb0 + t - ngt) * PTILE_U4, dt, tid, wave);
+      const int jt = tb0 + t - ngt;  // key tile
+      const int row = lane & 15, qd = lane >> 4;
+#pragma unroll
+      for (int f = wave; f < PK_FRAGS; f += PNT / kWave) {
+        const int tt = f / PKS, ks = f % PKS;
+        const int j = min(jt * PBN + 8 * (row >> 2) + 4 * tt + (row & 3), S - 1);
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const uint4 *>(kmat + ((size_t(b) * S + j) * hkv + h) * PD + ks * 32 + qd * 8),
+            dt + f * PFRAG, 16, 0, 0);
+      }
+      ring_copy<PV_FRAGS * PFRAG>(dense + (ubase + jt) * PTILE_U4 + PK_FRAGS * PFRAG,
+                                  dt + PK_FRAGS * PFRAG, tid, wave);
     }
   };
   copy(0, sT0, sP0);
@@ -961,10 +994,12 @@ __global__ __launch_bounds__(PNT, 3) void k_prefill_gathered(
   template __global__ void k_prefill<D>(int, int, int, int, int, float, const uint16_t *,           \
                                         const uint4 *, const floatx4 *, const uint4 *, float *);    \
   template __global__ void k_sparse_pack<D>(int, int, int, const uint16_t *, const uint16_t *,      \
-                                            const int32_t *, const int32_t *, uint4 *, int32_t *);  \
+                                            const int32_t *, const int32_t *, uint4 *, uint4 *,     \
+                                            int32_t *);                                             \
   template __global__ void k_prefill_gathered<D>(int, int, int, int, int, float, const uint16_t *,  \
-                                                 const uint4 *, const uint4 *, const int4 *,        \
-                                                 const int32_t *, const uint32_t *, float *);
+                                                 const uint16_t *, const uint4 *, const uint4 *,    \
+                                                 const int4 *, const int32_t *, const uint32_t *,   \
+                                                 float *);
 DMS_PREFILL_KERNELS(128)
 DMS_PREFILL_KERNELS(64)
 #undef DMS_PREFILL_KERNELS
@@ -1033,16 +1068,13 @@ static hipError_t launch_prefill_gathered_t(const dms_shape &s, const void *q, c
   int32_t *tile_cnt = reinterpret_cast<int32_t *>(base + L.tile_cnt);
   uint32_t *keptw = reinterpret_cast<uint32_t *>(base + L.keptw);
   const uint16_t *k16 = static_cast<const uint16_t *>(k), *v16 = static_cast<const uint16_t *>(v);
-  hipLaunchKernelGGL(k_prefill_pack<D>, dim3(ntiles, s.kv_heads, s.batch), dim3(4 * D), 0, st,
-                     seq_len, s.kv_heads, ntiles, k16, v16, logit, nullptr, 0.f, 1.f, 0, dense, mask,
-                     nullptr);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  (void)mask;
   hipLaunchKernelGGL(k_sparse_scan, dim3(s.batch * s.kv_heads), dim3(1024), 0, st, seq_len,
                      s.kv_heads, ntiles, logit, gpos, tile_cnt, keptw);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_sparse_pack<D>, dim3(ntiles, s.kv_heads, s.batch), dim3(4 * D), 0, st,
-                     seq_len, s.kv_heads, ntiles, k16, v16, gpos, tile_cnt, gathered, gposp);
+                     seq_len, s.kv_heads, ntiles, k16, v16, gpos, tile_cnt, dense, gathered, gposp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int ngh = (s.group + PHPW - 1) / PHPW;
   const int nbh = s.batch * s.kv_heads * ngh;
@@ -1051,7 +1083,7 @@ static hipError_t launch_prefill_gathered_t(const dms_shape &s, const void *q, c
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_prefill_gathered<D>, dim3(unsigned(blocks)), dim3(PNT), 0, st, s.batch,
                      seq_len, s.kv_heads, s.group, s.window, sm_scale * 1.4426950408889634f,
-                     static_cast<const uint16_t *>(q), dense, gathered,
+                     static_cast<const uint16_t *>(q), k16, dense, gathered,
                      reinterpret_cast<const int4 *>(gposp), tile_cnt, keptw, out);
   return hipGetLastError();
 }

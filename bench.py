@@ -241,8 +241,8 @@ def prefill_cpu_baseline(name: str = "prefill_8k", threads: int = 1) -> dict:
                       f"float64 NumPy, BLAS limited to {threads} thread(s)"}
 
 
-def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
-    """Masked prefill on the 8192-token workload, both kernels.
+def prefill_leg(name: str = "prefill_8k", iters: int = 10, relaxed: bool = True) -> dict:
+    """Masked prefill on one prefill workload (default: 8192 tokens, head_dim 128).
 
     Dense (dms_prefill_attn): causal FLOPs per second of one call (pack pass +
     attention kernel) against the dense bf16 MFMA peak.  Gathered
@@ -265,9 +265,10 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
     ms = _time_calls(lambda: prefill(q, k, v, logit, window=w.window, out=out, workspace=ws), iters)
     ms_g = _time_calls(lambda: prefill(q, k, v, logit, window=w.window, out=out, workspace=ws,
                                        method="gathered"), iters)
-    noise = wl.logistic_noise(w, device=dev)
-    ms_r = _time_calls(lambda: prefill(q, k, v, logit, window=w.window, out=out, workspace=ws,
-                                       method="relaxed", noise=noise, temperature=1.0), iters)
+    if relaxed:
+        noise = wl.logistic_noise(w, device=dev)
+        ms_r = _time_calls(lambda: prefill(q, k, v, logit, window=w.window, out=out, workspace=ws,
+                                           method="relaxed", noise=noise, temperature=1.0), iters)
     causal = 4.0 * d * s_len * (s_len + 1) / 2 * w.batch * w.q_heads
     # visible (query, key) pairs: |R(i)| = #{j <= i - w : unmarked} + min(w, i + 1), per (b, h)
     keep = (logit <= 0).to(torch.int64)                          # [B, S, Hkv]
@@ -284,7 +285,7 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
     # (32 query positions), QK and PV products over 32 keys x 32 queries x G heads x D
     executed = 4.0 * 32 * 32 * d * w.group * gathered_tiles(keep, s_len, w.window)
     g_tflops = executed / (ms_g * 1e-3) / 1e12
-    return {
+    rec = {
         "workload": name, "batch": w.batch, "seq_len": s_len, "q_heads": w.q_heads,
         "kv_heads": w.kv_heads, "head_dim": d, "evict_rate": w.evict_rate, "window": w.window,
         "ms": round(ms, 4), "causal_tflop": round(causal / 1e12, 4),
@@ -293,24 +294,27 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10) -> dict:
         "roofline": {"bound": "mfma", "kernel": "k_prefill_pack + k_prefill", "achieved": round(tflops, 1),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": prefill_traffic_from_profile(),
+                     "traffic": prefill_traffic_from_profile("dense") if name == "prefill_8k" else None,
                      "algorithmic_bytes_per_call": prefill_algorithmic_bytes(
                          w.batch, s_len, w.q_heads, w.kv_heads, d),
                      "workspace_bytes_per_call": prefill_workspace_traffic(
                          w.batch, s_len, w.kv_heads, d)},
-        "relaxed": {"ms": round(ms_r, 4), "temperature": 1.0, "noise": "logistic",
-                    "causal_tflops": round(causal / (ms_r * 1e-3) / 1e12, 1),
-                    "frac": round(causal / (ms_r * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
         "gathered": {
             "ms": round(ms_g, 4), "speedup_vs_dense": round(ms / ms_g, 2),
             "causal_equivalent_tflops": round(causal / (ms_g * 1e-3) / 1e12, 1),
             "executed_tflop": round(executed / 1e12, 4),
             "roofline": {"bound": "mfma",
-                         "kernel": "k_prefill_pack + k_sparse_scan + k_sparse_pack + k_prefill_gathered",
+                         "kernel": "k_sparse_scan + k_sparse_pack + k_prefill_gathered",
                          "achieved": round(g_tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(g_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None},
+                         "frac": round(g_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": prefill_traffic_from_profile("gathered") if name == "prefill_8k" else None},
         },
     }
+    if relaxed:
+        rec["relaxed"] = {"ms": round(ms_r, 4), "temperature": 1.0, "noise": "logistic",
+                          "causal_tflops": round(causal / (ms_r * 1e-3) / 1e12, 1),
+                          "frac": round(causal / (ms_r * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
+    return rec
 
 
 def chunk_leg(caches, w, dev, n_query: int = 4, rounds: int = 32) -> dict:
@@ -508,11 +512,11 @@ def traffic_from_profile(bytes_alg_per_launch: float):
     return rec.get("hbm_bytes_per_launch") if rec else None
 
 
-def prefill_traffic_from_profile():
-    """HBM bytes per dense prefill call (pack pass + attention kernel) from the
-    committed rocprofv3 counter summary."""
+def prefill_traffic_from_profile(method: str = "dense"):
+    """HBM bytes per prefill call of `method` ("dense", "gathered" or "relaxed":
+    every kernel of the call) from the committed rocprofv3 counter summary."""
     rec = _profile_record(PREFILL_PMC_FILE, PREFILL_SRC)
-    return rec.get("hbm_bytes_per_call") if rec else None
+    return rec.get(method, {}).get("hbm_bytes_per_call") if rec else None
 
 
 def prefill_algorithmic_bytes(batch: int, seq_len: int, q_heads: int, kv_heads: int, d: int) -> int:
@@ -811,6 +815,9 @@ def main():
         if not args.no_cpu_baseline:
             log("[bench] timing the oracle's masked prefill on a 1024-row sample")
             result["prefill"]["cpu_baseline"] = prefill_cpu_baseline(threads=1)
+        torch.cuda.empty_cache()
+        log("[bench] masked prefill, head_dim 64 (Llama-3.2-1B-shaped heads), 4096 tokens")
+        result["prefill_head_dim_64"] = prefill_leg("prefill_4k_d64", relaxed=False)
         torch.cuda.empty_cache()
         result["chunked_prefill"] = chunked_prefill_leg()
         log(f"[bench] chunked prefill: last {result['chunked_prefill']['chunk']} tokens in "

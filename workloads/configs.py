@@ -80,6 +80,12 @@ WORKLOADS = {
         name="prefill_8k", kind="prefill", batch=4, kv_heads=8, group=4, head_dim=128,
         dtype="bf16", context=8192, evict_rate=0.875, seed=5000,
     ),
+    # masked prefill of the Llama-3.2-1B-shaped layer (head_dim 64, 4x compression): the
+    # prompts of the llama1b_cr4 batch, 4096 tokens each
+    "prefill_4k_d64": Workload(
+        name="prefill_4k_d64", kind="prefill", batch=16, kv_heads=8, group=4, head_dim=64,
+        dtype="bf16", context=4096, evict_rate=0.75, seed=5100,
+    ),
 }
 
 

@@ -33,6 +33,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 METRIC = "DMS decode-attn tokens/s and KV GB/s (% HBM peak) at CR=8, Qwen3-8B shape"
+# the other decode workloads, each measured by a short step loop of its own:
+# Llama-3.2-1B-shaped heads at CR 4, the Qwen3-8B shape with nothing evicted,
+# ragged Qwen2.5-32B-shaped units
+DECODE_CONFIGS = ("llama1b_cr4", "qwen3_8b_cr1", "qwen32b_width")
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_qwen3_8b_cr8_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "decode_attention_learned_amd", "csrc", "decode_mfma.hip")
 PREFILL_PMC_FILE = os.path.join(ROOT, "profiles", "prefill_8k_traffic.json")
@@ -492,6 +496,76 @@ def chunked_prefill_leg(name: str = "prefill_8k", chunk: int = 512, iters: int =
             "tokens_per_s": round(w.batch * chunk / (ms * 1e-3), 1)}
 
 
+def decode_config_leg(name: str, steps: int = 64, warmup: int = 8, n_ev: int = 32) -> dict:
+    """The decode step on another decode workload (its own shape, eviction rates and
+    replica count), measured like the headline: `steps` steps between two events
+    (reserve + decode with the token, compaction every `compact_every` steps per
+    replica, round-robin over the replicas), then per-call events around the
+    decode launch on `n_ev` further steps for its time and KV rate."""
+    import torch
+
+    import workloads as wl
+
+    w = wl.get(name)
+    dev = torch.device("cuda:0")
+    replicas, every = w.replicas, w.compact_every
+    total = warmup + steps + n_ev
+    per_rep = (total + replicas - 1) // replicas
+    caches = [build_replica(w, r, dev, per_rep + every + 64) for r in range(replicas)]
+    inputs = [[wl.decode_step_inputs(w, j, device=dev, replica=r, rates=caches[r][1])
+               for j in range(per_rep)] for r in range(replicas)]
+    outs = [torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+            for _ in range(replicas)]
+    scale = 1.0 / math.sqrt(w.head_dim)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_ev)]
+
+    def step(i, ev=None):
+        r, j = i % replicas, i // replicas
+        cache = caches[r][0]
+        q, k, v, logit = inputs[r][j]
+        cache.reserve()
+        if ev is not None:
+            ev[0].record()
+        cache.fill_and_decode(k, v, logit, q, outs[r], scale)
+        if ev is not None:
+            ev[1].record()
+        if (i + 1) % every == 0:
+            caches[((i + 1) // every - 1) % replicas][0].compact()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    before = [retained_total(c) for c, _ in caches]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(warmup, warmup + steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / steps
+    for i in range(n_ev):
+        step(warmup + steps + i, evs[i])
+    torch.cuda.synchronize()
+    after = [retained_total(c) for c, _ in caches]
+    if any(c.status_word() for c, _ in caches):
+        raise RuntimeError(f"{name}: device status set")
+    dec_ms = sum(a.elapsed_time(b) for a, b in evs) / n_ev
+    retained = sum(a[0] + b[0] for a, b in zip(before, after)) / (2 * replicas)
+    bytes_alg = retained * w.head_dim * 2 * 2
+    kv_gbps = bytes_alg / (dec_ms * 1e-3) / 1e9
+    del caches, inputs, outs
+    torch.cuda.empty_cache()
+    return {"workload": name, "batch": w.batch, "kv_heads": w.kv_heads, "q_heads": w.q_heads,
+            "head_dim": w.head_dim, "context": w.context, "evict_rate": w.evict_rate,
+            "replicas": replicas, "steps": steps, "ms_per_step": round(ms_step, 4),
+            "tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
+            "decode_attn_us": round(dec_ms * 1e3, 2),
+            "retained_per_unit": round(retained / w.units, 1),
+            "kv_gbps": round(kv_gbps, 1), "hbm_frac": round(kv_gbps / HBM_PEAK_GBPS, 4)}
+
+
 def _profile_record(path: str, src: str):
     """A committed rocprofv3 counter summary, or None if there is none or the
     kernel source changed since it was taken."""
@@ -595,6 +669,10 @@ def main():
     ap.add_argument("--no-share", action="store_true", help="skip the shared-prefix leg")
     ap.add_argument("--chunked-prefill-only", action="store_true",
                     help="only run the chunked-prefill leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the decode step on the other decode workloads")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="only run the decode step on the other decode workloads")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -617,6 +695,9 @@ def main():
         return
     if args.chunked_prefill_only:
         print(json.dumps(chunked_prefill_leg()), flush=True)
+        return
+    if args.configs_only:
+        print(json.dumps({n: decode_config_leg(n) for n in DECODE_CONFIGS}), flush=True)
         return
     dev = torch.device("cuda:0")
     w = wl.get(args.workload)
@@ -806,6 +887,13 @@ def main():
         log(f"[bench] shared prompts: {sp['pages_shared']} pages vs {sp['pages_copied']}, decode "
             f"{sp['decode_us_shared']:.1f} us vs {sp['decode_us_copied']:.1f} us")
         torch.cuda.empty_cache()
+    if not args.no_configs:
+        result["decode_configs"] = {}
+        for n in DECODE_CONFIGS:
+            rec = decode_config_leg(n)
+            result["decode_configs"][n] = rec
+            log(f"[bench] {n}: {rec['ms_per_step'] * 1e3:.1f} us/step, decode {rec['decode_attn_us']:.1f} us "
+                f"= {rec['kv_gbps']:.0f} GB/s ({100 * rec['hbm_frac']:.1f}% of HBM peak)")
     if not args.no_prefill:
         log("[bench] masked prefill, 8192 tokens")
         result["prefill"] = prefill_leg()

@@ -138,10 +138,12 @@ inline size_t prefill_workspace_bytes(int batch, int kv_heads, int seq_len, int 
          align256(tiles * tile_bytes);
 }
 
-// Gathered-key prefill workspace: the dense prefill workspace (for the band
-// tiles), the same layout for the gathered kept keys plus their positions,
-// and per unit the kept positions in order, kept counts before each tile and
-// each tile's kept-key bits.  Byte offsets of each region.
+// Gathered-key prefill workspace: packed tiles as in the dense prefill
+// workspace, of which only the value half is written (band tiles read their
+// keys straight from K), the per-key masks, the same tile layout for the
+// gathered kept keys plus their positions, and per unit the kept positions in
+// order, kept counts before each tile and each tile's kept-key bits.  Byte
+// offsets of each region.
 struct PrefillGatheredLayout {
   size_t dense_mask, gathered, gathered_pos, gpos, tile_cnt, keptw, total;
 };

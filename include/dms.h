@@ -13,8 +13,10 @@
  *
  * Conventions shared by every call
  *   - All pointers are device pointers unless stated otherwise.  The library
- *     allocates no memory, keeps no pointer after a call returns and holds no
- *     global state: every buffer belongs to the caller.
+ *     allocates no memory and keeps no pointer after a call returns: every
+ *     buffer belongs to the caller.  Its one piece of global state is the
+ *     static device scratch array of dms_decode_attn_noalloc (one per GPU,
+ *     resident until the process ends); no other call touches it.
  *   - Calls enqueue kernels on `stream` (a hipStream_t; NULL = the default
  *     stream) and return without synchronising.  Calls on one cache must be
  *     ordered on one stream; calls on disjoint state may run on any streams.

@@ -125,7 +125,7 @@ int dms_decode_attn_noalloc(const dms_shape *shape, const dms_cache *cache, cons
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
   if (dms_decode_workspace_bytes(shape) > DMS_NOALLOC_SCRATCH_BYTES) return DMS_ESCRATCH;
   void *ws = nullptr;
-  if (dms::scratch_address(&ws) != hipSuccess) return DMS_EHIP;
+  if (dms::scratch_address(stream, &ws) != hipSuccess) return DMS_EHIP;
   return from_hip(dms::launch_decode(*shape, *cache, q, out, sm_scale, ws, stream));
 }
 

@@ -102,8 +102,8 @@ struct DecodeFill {
   const float *logit;         // [B][1][Hkv]
 };
 hipError_t launch_compact(const dms_shape &s, const dms_cache &c, hipStream_t st);
-// device address of the current GPU's static scratch array (decode_scratch.hip)
-hipError_t scratch_address(void **ptr);
+// device address of the static scratch array on the GPU of `stream` (decode_scratch.hip)
+hipError_t scratch_address(hipStream_t stream, void **ptr);
 hipError_t launch_export(const dms_shape &s, const dms_cache &c, int all_slots, int max_out,
                          int32_t *count_out, int32_t *pos_out, uint8_t *alpha_out, void *k_out,
                          void *v_out, hipStream_t st);

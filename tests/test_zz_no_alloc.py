@@ -35,12 +35,20 @@ def _case(dev, b, hkv, g, d, tokens, seed):
     return cache, q, k, v, lg
 
 
-def _noalloc(cache, q):
+def _noalloc(cache, q, stream=None):
+    """One call on `stream` (torch's current stream when None; the default
+    stream is the null stream, whose device is the current one; a stream of
+    its own makes the library take the device from the stream)."""
     out = torch.full((cache.batch, cache.kv_heads * cache.group, cache.head_dim), float("nan"),
                      device=q.device)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    if stream is not None:
+        s.wait_stream(torch.cuda.current_stream())
     rc = lib.dms_decode_attn_noalloc(cache.shape, cache.cache, q, out, 1.0 / math.sqrt(cache.head_dim),
-                                     torch.cuda.current_stream().cuda_stream)
+                                     s.cuda_stream)
     lib.check("dms_decode_attn_noalloc", rc)
+    if stream is not None:
+        torch.cuda.current_stream().wait_stream(s)
     return out
 
 
@@ -71,6 +79,19 @@ def test_noalloc_decode_equals_decode_twice_then_smaller(gpu):
         say(f"noalloc B={b} Hkv={hkv} G={g} D={d}: identical to dms_decode_attn, "
             f"max err vs oracle {worst:.2e}")
         assert cache.status_word() == 0
+
+
+@pytest.mark.gpu
+def test_noalloc_on_a_stream_of_its_own(gpu):
+    """The same call issued on a non-default stream gives the same outputs."""
+    cache, q, k, v, lg = _case(gpu, 4, 8, 4, 128, 2000, 9703)
+    qd = q.to(gpu)
+    ref_out = cache.decode(qd)
+    side = torch.cuda.Stream(device=gpu)
+    out = _noalloc(cache, qd, stream=side)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out), "dms_decode_attn_noalloc on a side stream differs"
+    assert cache.status_word() == 0
 
 
 def test_noalloc_rejects_shapes_beyond_the_scratch_size():

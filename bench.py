@@ -459,7 +459,8 @@ def shared_prefix_leg(w, dev, threads: int = 8, steps: int = 24) -> dict:
     }
 
 
-def chunked_prefill_leg(name: str = "prefill_8k", chunk: int = 512, iters: int = 5) -> dict:
+def chunked_prefill_leg(name: str = "prefill_8k", chunk: int = 512, iters: int = 5,
+                        batch: int | None = None) -> dict:
     """Chunked prefill into a cache: the prefill workload's first S - chunk
     tokens are appended and compacted, then the last `chunk` tokens are
     appended and attend at once (dms_decode_attn_multi, tiled kernel).  The
@@ -471,6 +472,9 @@ def chunked_prefill_leg(name: str = "prefill_8k", chunk: int = 512, iters: int =
     from decode_attention_learned_amd import DmsCache
 
     w = wl.get(name)
+    if batch is not None:
+        import dataclasses
+        w = dataclasses.replace(w, batch=batch)
     dev = torch.device("cuda:0")
     q, k, v, logit = wl.prefill_inputs(w, device=dev)
     s_len, d = w.context, w.head_dim
@@ -483,6 +487,17 @@ def chunked_prefill_leg(name: str = "prefill_8k", chunk: int = 512, iters: int =
     qc = q[:, head:].contiguous()
     out = torch.empty((w.batch, chunk, w.q_heads, d), dtype=torch.float32, device=dev)
     ms = _time_calls(lambda: cache.decode_chunk(qc, out=out), iters)
+    # the same call with the minimal workspace: no split of the tiles
+    from decode_attention_learned_amd import lib
+    small = torch.empty((max(lib.decode_multi_workspace_bytes(cache.shape), 1),), dtype=torch.uint8,
+                        device=dev)
+
+    def one_pass():
+        lib.check("dms_decode_attn_multi", lib.dms_decode_attn_multi(
+            cache.shape, cache.cache, qc, chunk, out, 1.0 / math.sqrt(d), small, small.numel(),
+            torch.cuda.current_stream().cuda_stream))
+
+    ms_one = _time_calls(one_pass, iters)
     if cache.status_word():
         raise RuntimeError("device status set in the chunked-prefill leg")
     keep = (logit <= 0).to(torch.int64)
@@ -491,7 +506,9 @@ def chunked_prefill_leg(name: str = "prefill_8k", chunk: int = 512, iters: int =
     kept_before = csum[:, i - w.window, :]
     pairs = (kept_before + w.window).sum().item() * w.group
     flops = 4.0 * d * pairs
-    return {"chunk": chunk, "context_before": head, "ms": round(ms, 4),
+    return {"batch": w.batch, "chunk": chunk, "context_before": head, "ms": round(ms, 4),
+            "ms_without_split": round(ms_one, 4),
+            "split_workspace_bytes": lib.decode_multi_split_workspace_bytes(cache.shape, chunk),
             "visible_pair_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
             "tokens_per_s": round(w.batch * chunk / (ms * 1e-3), 1)}
 
@@ -694,7 +711,8 @@ def main():
         print(json.dumps(prefill_leg()), flush=True)
         return
     if args.chunked_prefill_only:
-        print(json.dumps(chunked_prefill_leg()), flush=True)
+        print(json.dumps({"chunked_prefill": chunked_prefill_leg(),
+                          "chunked_prefill_one_sequence": chunked_prefill_leg(batch=1)}), flush=True)
         return
     if args.configs_only:
         print(json.dumps({n: decode_config_leg(n) for n in DECODE_CONFIGS}), flush=True)
@@ -910,6 +928,10 @@ def main():
         result["chunked_prefill"] = chunked_prefill_leg()
         log(f"[bench] chunked prefill: last {result['chunked_prefill']['chunk']} tokens in "
             f"{result['chunked_prefill']['ms']:.3f} ms")
+        result["chunked_prefill_one_sequence"] = chunked_prefill_leg(batch=1)
+        log(f"[bench] chunked prefill, one sequence: "
+            f"{result['chunked_prefill_one_sequence']['ms']:.3f} ms split, "
+            f"{result['chunked_prefill_one_sequence']['ms_without_split']:.3f} ms without")
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         # the oracle as it stands: BLAS on every core this process may use, then on one;

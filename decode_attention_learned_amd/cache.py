@@ -164,7 +164,8 @@ class DmsCache:
         if out is None:
             out = torch.empty(qshape, dtype=torch.float32, device=self.device)
         _need(out, "out", torch.float32, qshape, self.device)
-        need = lib.decode_multi_workspace_bytes(self.shape)
+        # the workspace that lets long chunks split their tiles over the chip
+        need = lib.decode_multi_split_workspace_bytes(self.shape, n_query)
         if getattr(self, "_multi_ws", None) is None or self._multi_ws.numel() < need:
             self._multi_ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=self.device)
         scale = 1.0 / math.sqrt(self.head_dim) if sm_scale is None else sm_scale

@@ -183,6 +183,14 @@ size_t dms_decode_multi_workspace_bytes(const dms_shape *shape) {
   return dms::decode_workspace_layout(dms::units_of(*shape), 16, shape->head_dim).bytes;
 }
 
+size_t dms_decode_multi_split_workspace_bytes(const dms_shape *shape, int32_t n_query) {
+  const size_t base = dms_decode_multi_workspace_bytes(shape);
+  if (base == 0 || n_query < 1) return 0;
+  if (shape->kv_dtype != DMS_KV_BF16 || n_query < 32) return base;
+  const size_t split = dms::chunk_split_bytes(*shape, n_query, dms::chunk_splits(*shape, n_query));
+  return split > base ? split : base;
+}
+
 int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const void *q,
                           int32_t n_query, float *out, float sm_scale, void *workspace,
                           size_t workspace_bytes, hipStream_t stream) {
@@ -194,7 +202,8 @@ int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const 
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return DMS_EINVAL;
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
   if (workspace_bytes < dms_decode_multi_workspace_bytes(shape)) return DMS_EWORKSPACE;
-  return from_hip(dms::launch_decode_multi(*shape, *cache, q, n_query, out, sm_scale, workspace, stream));
+  return from_hip(dms::launch_decode_multi(*shape, *cache, q, n_query, out, sm_scale, workspace,
+                                           workspace_bytes, stream));
 }
 
 static int check_prefill_shape(const dms_shape *shape, int32_t seq_len) {

@@ -291,7 +291,7 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
 constexpr int kChunkKernelMin = 32;
 
 hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
-                               float *out, float sm_scale, void *wsv, hipStream_t st) {
+                               float *out, float sm_scale, void *wsv, size_t ws_bytes, hipStream_t st) {
   const DecodeWorkspace w = decode_workspace_layout(units_of(s), 16, s.head_dim);
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   if (s.kv_dtype == DMS_KV_F32) {
@@ -310,7 +310,7 @@ hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const voi
     return hipSuccess;
   }
   if (n_query >= kChunkKernelMin && s.group <= 16)
-    return launch_chunk_attn(s, c, q, n_query, out, sm_scale, st);
+    return launch_chunk_attn(s, c, q, n_query, out, sm_scale, wsv, ws_bytes, st);
   if (!launch_decode_mfma(s, c, q, out, scale_log2, w, static_cast<char *>(wsv), st, n_query,
                           nullptr, true))
     return hipErrorInvalidValue;

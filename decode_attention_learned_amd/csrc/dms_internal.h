@@ -87,6 +87,38 @@ inline DecodeWorkspace decode_workspace_layout(int units, int group, int head_di
   return w;
 }
 
+// Split-K of the tiled chunk kernel (chunks of 32 queries or more).  Its
+// grid is one workgroup per 32 queries and (sequence, KV head, group of 4
+// query heads); three run per CU.  When that fills at most half of one
+// resident round (3 x 256), each workgroup's tiles are cut into `splits`
+// parts (at most 4, all still in one round) whose partials a merge launch
+// combines.  Measured: 512 queries of 4 sequences (512 workgroups, two
+// thirds of a round) took 0.132 ms split 3 ways against 0.069 ms unsplit,
+// the partials' traffic outweighing the extra third of the chip.
+constexpr int kChunkResident = 3 * 256;
+inline int chunk_splits(const dms_shape &s, int n_query) {
+  const long wgs = long((n_query + 31) / 32) * s.batch * s.kv_heads * ((s.group + 3) / 4);
+  if (wgs <= 0 || 2 * wgs > kChunkResident) return 1;
+  const long f = kChunkResident / wgs;
+  return f > 4 ? 4 : int(f);
+}
+// Partials of the splits: per split and output row (B * n_query * Hq rows),
+// (reference, row sum) and D floats of unnormalised output.
+struct ChunkSplitLayout {
+  size_t rows, part_ml, part_o, bytes;
+};
+inline ChunkSplitLayout chunk_split_layout(const dms_shape &s, int n_query, int splits) {
+  ChunkSplitLayout L;
+  L.rows = size_t(s.batch) * size_t(n_query) * size_t(s.kv_heads) * size_t(s.group);
+  L.part_ml = 0;
+  L.part_o = align256(size_t(splits) * L.rows * 2 * sizeof(float));
+  L.bytes = L.part_o + align256(size_t(splits) * L.rows * size_t(s.head_dim) * sizeof(float));
+  return L;
+}
+inline size_t chunk_split_bytes(const dms_shape &s, int n_query, int splits) {
+  return splits > 1 ? chunk_split_layout(s, n_query, splits).bytes : 0;
+}
+
 // ---- launchers (each defined in the translation unit holding its kernels) ----
 hipError_t launch_reset(const dms_shape &s, const dms_cache &c, hipStream_t st);
 hipError_t launch_append(const dms_shape &s, const dms_cache &c, const void *k_new,
@@ -114,9 +146,9 @@ hipError_t launch_share(const dms_shape &s, const dms_cache &c, int src, int dst
                         hipStream_t st);
 hipError_t launch_release(const dms_shape &s, const dms_cache &c, int first, int n, hipStream_t st);
 hipError_t launch_chunk_attn(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
-                             float *out, float sm_scale, hipStream_t st);
+                             float *out, float sm_scale, void *ws, size_t ws_bytes, hipStream_t st);
 hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
-                               float *out, float sm_scale, void *ws, hipStream_t st);
+                               float *out, float sm_scale, void *ws, size_t ws_bytes, hipStream_t st);
 // the deferred split-K merge after a decode launch (nothing for plans that merge in the launch)
 hipError_t launch_merge(const dms_shape &s, const dms_cache &c, const DecodeWorkspace &w, char *ws,
                         float *out, int ncol, int c0, int C, hipStream_t st);

@@ -256,7 +256,7 @@ __device__ __forceinline__ void pv_tile_tail(const uint4 *__restrict__ sv, const
 template <int D>
 __device__ __forceinline__ void store_rows(const floatx4 (&o)[D / 16][2], const Softmax &sm,
                                            float *stage, float *out, size_t row0, size_t rstride,
-                                           int i0, int S, int lane) {
+                                           int i0, int S, int lane, bool normalize = true) {
   PDIMS(D);
   constexpr int LPR = D / 4;      // lanes per row (four floats each)
   constexpr int RPI = 64 / LPR;   // rows per store instruction
@@ -266,7 +266,7 @@ __device__ __forceinline__ void store_rows(const floatx4 (&o)[D / 16][2], const 
     float l = sm.l[qt];
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = normalize ? (l > 0.f ? 1.f / l : 0.f) : 1.f;
 #pragma unroll
     for (int dt = 0; dt < PDT; ++dt)
       *reinterpret_cast<floatx4 *>(stage + col * D + ((dt * 16 + quad * 4 + 4 * col) & (D - 1))) =
@@ -1111,12 +1111,13 @@ hipError_t launch_prefill_gathered(const dms_shape &s, const void *q, const void
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
-    int hkv, int G, int window, int maxp, int C, float scale_log2, const uint16_t *__restrict__ q,
-    const uint4 *__restrict__ k_pages, const uint4 *__restrict__ v_pages,
-    const int32_t *__restrict__ page_table, const int4 *__restrict__ slot_pos,
-    const uint4 *__restrict__ slot_alpha, const int32_t *__restrict__ n_slots,
-    const int32_t *__restrict__ n_clean, const int32_t *__restrict__ seq_len,
-    const int32_t *__restrict__ compact_pos, uint32_t *__restrict__ status,
+    int hkv, int G, int window, int maxp, int C, float scale_log2, int nsplit,
+    const uint16_t *__restrict__ q, const uint4 *__restrict__ k_pages,
+    const uint4 *__restrict__ v_pages, const int32_t *__restrict__ page_table,
+    const int4 *__restrict__ slot_pos, const uint4 *__restrict__ slot_alpha,
+    const int32_t *__restrict__ n_slots, const int32_t *__restrict__ n_clean,
+    const int32_t *__restrict__ seq_len, const int32_t *__restrict__ compact_pos,
+    uint32_t *__restrict__ status, float2 *__restrict__ part_ml, float *__restrict__ part_o,
     float *__restrict__ out) {
   PDIMS(D);
   const int tid = threadIdx.x;
@@ -1130,17 +1131,27 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
   const int g = hg * PHPW + wave;
   const bool active = g < G;
   const int hq = h * G + (active ? g : 0);
-  const int c0 = blockIdx.x * 32;                 // first chunk query of the workgroup
+  const int qb = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;
+  const int c0 = qb * 32;                         // first chunk query of the workgroup
   const int t_first = seq_len[b] - C + c0;        // its position
   const int ns = n_slots[u], nc = n_clean[u];
   const int nt = (ns + PBN - 1) / PBN;
   const int nclean_t = nc / PBN;                  // tiles wholly below n_clean
   const int32_t *row = page_table + size_t(u) * maxp;
-  if (blockIdx.x == 0 && hg == 0 && tid == 0) {
+  // Tiles this workgroup reads.  The chunk's C tokens are the unit's last C
+  // slots (nothing compacted it since, else the status flag below), so
+  // query c0 + 31 sits in slot ns - C + c0 + 31 and later slots are hidden
+  // from every query of the workgroup.  Split sp of nsplit takes an equal
+  // share of the tiles up to there.
+  const int last_slot = ns - C + min(c0 + 31, C - 1);
+  const int nt_vis = last_slot < 0 ? 0 : min(nt, last_slot / PBN + 1);
+  const int kb = sp * nt_vis / nsplit, ke = (sp + 1) * nt_vis / nsplit;
+  if (qb == 0 && sp == 0 && hg == 0 && tid == 0) {
     const int p0 = seq_len[b] - C;  // the chunk's first position
     if (p0 < 0 || compact_pos[u] > p0) atomicOr(status, DMS_STATUS_CHUNK_INVALID);
   }
-  const int tail_valid = ns - (nt - 1) * PBN;     // slots in use in the last tile
+  // slots in use in the last tile read (all 32 unless it is the unit's last)
+  const int tail_valid = ke == nt ? ns - (nt - 1) * PBN : PBN;
 
   uint4 qf[2][PKS];
 #pragma unroll
@@ -1185,7 +1196,7 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
     if (wave == 1 && lane < PBN / 16)
       __builtin_amdgcn_global_load_lds(slot_alpha + grp * (PBN / 16) + lane, da, 16, 0, 0);
   };
-  if (nt > 0) copy(0, sT0, sP0, sA0);
+  if (ke > kb) copy(kb, sT0, sP0, sA0);
   ring_barrier();
 
   floatx4 s[2][2];
@@ -1193,9 +1204,9 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
   const floatx4 zero[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
   auto iteration = [&](int k, const uint4 *t, const int4 *p, const uint4 *a, const uint4 *tp,
                        uint4 *tn, int4 *pn, uint4 *an) {
-    if (k + 1 < nt) copy(k + 1, tn, pn, an);
+    if (k + 1 < ke) copy(k + 1, tn, pn, an);
     if (active) {
-      if (k >= 1) pv_tile<D>(tp + PK_FRAGS * PFRAG, pb, lane, o);
+      if (k > kb) pv_tile<D>(tp + PK_FRAGS * PFRAG, pb, lane, o);
       qk_tile<D>(t, zero, qf, lane, s);
       c_phase2<D>(k, nt, nclean_t, ns, nc, window, t_first, col, quad, p,
                reinterpret_cast<const uint2 *>(a), s, sm, o, pb, c);
@@ -1204,66 +1215,136 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
   };
   auto clean_iteration = [&](int k, const uint4 *t, const uint4 *tp, uint4 *tn, int4 *pn,
                              uint4 *an) {
-    if (k + 1 < nt) copy(k + 1, tn, pn, an);
+    if (k + 1 < ke) copy(k + 1, tn, pn, an);
     if (active) steady_step<D>(t, tp + PK_FRAGS * PFRAG, zero, qf, s, pb, o, sm, c, lane);
     ring_barrier();
   };
-  // tile 0; the tiles 1 .. nclean_t - 1 wholly below n_clean in whole rounds
-  // of three; the rest on the general path.  Tile k is in buffer k % 3.  The
-  // PV product of the last tile comes after the loop: its unused tail slots
-  // are cleared there, away from the loop body's registers.
-  if (nt > 0) iteration(0, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
-  int k = 1;
-  for (; k + 2 < nclean_t; k += 3) {
+  // tile kb; the tiles after it wholly below n_clean in whole rounds of
+  // three; the rest on the general path.  Tile k is in buffer (k - kb) % 3.
+  // The PV product of the last tile comes after the loop: its unused tail
+  // slots are cleared there, away from the loop body's registers.
+  if (ke > kb) iteration(kb, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
+  const int clean_end = min(nclean_t, ke);
+  int k = kb + 1;
+  for (; k + 2 < clean_end; k += 3) {
     clean_iteration(k, sT1, sT0, sT2, sP2, sA2);
     clean_iteration(k + 1, sT2, sT1, sT0, sP0, sA0);
     clean_iteration(k + 2, sT0, sT2, sT1, sP1, sA1);
   }
-  for (; k < nt; k += 3) {
+  for (; k < ke; k += 3) {
     iteration(k, sT1, sP1, sA1, sT0, sT2, sP2, sA2);
-    if (k + 1 >= nt) break;
+    if (k + 1 >= ke) break;
     iteration(k + 1, sT2, sP2, sA2, sT1, sT0, sP0, sA0);
-    if (k + 2 >= nt) break;
+    if (k + 2 >= ke) break;
     iteration(k + 2, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
   }
-  if (nt > 0 && active) {
-    const int lt = (nt - 1) % 3;  // the last tile's buffer
+  if (ke > kb && active) {
+    const int lt = (ke - 1 - kb) % 3;  // the last tile's buffer
     const uint4 *tl = lt == 0 ? sT0 : (lt == 1 ? sT1 : sT2);
     pv_tile_tail<D>(tl + PK_FRAGS * PFRAG, pb, lane, tail_valid, o);
   }
   ring_barrier();  // every wave is done with the ring before it stages its output there
 
   if (!active) return;
-  // the ring buffers are free: every wave has passed the last barrier
+  // The ring buffers are free: every wave has passed the last barrier.  One
+  // workgroup per 32 queries writes the output; a split writes its
+  // unnormalised output to its part of the workspace (same row order, row
+  // r = (b C + c) Hq + hq) and its reference and row sum per row, merged by
+  // k_chunk_merge.
+  const size_t R = size_t(gridDim.y / ngh) / hkv * size_t(C) * Hq;  // rows: B * C * Hq
+  float *dst = nsplit > 1 ? part_o + size_t(sp) * R * PD : out;
   float *stage = reinterpret_cast<float *>(wave < 2 ? sT0 : sT1) + (wave & 1) * (16 * PD);
-  store_rows<D>(o, sm, stage, out, (size_t(b) * C * Hq + hq) * PD, size_t(Hq) * PD, c0, C, lane);
+  store_rows<D>(o, sm, stage, dst, (size_t(b) * C * Hq + hq) * PD, size_t(Hq) * PD, c0, C, lane,
+                nsplit == 1);
+  if (nsplit > 1) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float l = sm.l[qt];
+      l += __shfl_xor(l, 16, kWave);
+      l += __shfl_xor(l, 32, kWave);
+      const int cq = c0 + 16 * qt + col;
+      if (quad == 0 && cq < C)
+        part_ml[size_t(sp) * R + (size_t(b) * C + cq) * Hq + hq] = make_float2(sm.m[qt], l);
+    }
+  }
 }
 
-template __global__ void k_chunk_attn<128>(int, int, int, int, int, float, const uint16_t *,
-                                           const uint4 *, const uint4 *, const int32_t *, const int4 *,
-                                           const uint4 *, const int32_t *, const int32_t *,
-                                           const int32_t *, const int32_t *, uint32_t *, float *);
-template __global__ void k_chunk_attn<64>(int, int, int, int, int, float, const uint16_t *,
-                                          const uint4 *, const uint4 *, const int32_t *, const int4 *,
-                                          const uint4 *, const int32_t *, const int32_t *,
-                                          const int32_t *, const int32_t *, uint32_t *, float *);
+// Merge of the splits of k_chunk_attn, one thread per four consecutive
+// output floats of a row: with each split's reference m_s (raw score units),
+// row sum l_s and unnormalised output o_s, out = sum_s w_s o_s / sum_s w_s l_s,
+// w_s = 2^((m_s - M) c), M = max_s m_s; rows no split saw a key of are zero.
+template <int D>
+__global__ __launch_bounds__(256) void k_chunk_merge(int rows, int nsplit, float scale_log2,
+                                                     const float2 *__restrict__ part_ml,
+                                                     const float *__restrict__ part_o,
+                                                     float *__restrict__ out) {
+  constexpr int Q = D / 4;  // threads per row
+  const size_t x = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (x >= size_t(rows) * Q) return;
+  const size_t r = x / Q;
+  float2 ml[4];
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    ml[s] = s < nsplit ? part_ml[size_t(s) * rows + r] : make_float2(-INFINITY, 0.f);
+    M = fmaxf(M, ml[s].x);
+  }
+  floatx4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s >= nsplit || ml[s].x == -INFINITY) continue;
+      const float w = exp2f((ml[s].x - M) * scale_log2);
+      den = fmaf(ml[s].y, w, den);
+      num += w * *reinterpret_cast<const floatx4 *>(part_o + (size_t(s) * rows * Q + x) * 4);
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  *reinterpret_cast<floatx4 *>(out + x * 4) = num * inv;
+}
+
+#define DMS_CHUNK_KERNELS(D)                                                                      \
+  template __global__ void k_chunk_attn<D>(int, int, int, int, int, float, int, const uint16_t *,   \
+                                           const uint4 *, const uint4 *, const int32_t *,           \
+                                           const int4 *, const uint4 *, const int32_t *,            \
+                                           const int32_t *, const int32_t *, const int32_t *,       \
+                                           uint32_t *, float2 *, float *, float *);                  \
+  template __global__ void k_chunk_merge<D>(int, int, float, const float2 *, const float *, float *);
+DMS_CHUNK_KERNELS(128)
+DMS_CHUNK_KERNELS(64)
+#undef DMS_CHUNK_KERNELS
 
 hipError_t launch_chunk_attn(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
-                             float *out, float sm_scale, hipStream_t st) {
+                             float *out, float sm_scale, void *ws, size_t ws_bytes, hipStream_t st) {
   const int ngh = (s.group + PHPW - 1) / PHPW;
   const long gy = long(s.batch) * s.kv_heads * ngh;
   if (gy > 65535) return hipErrorInvalidValue;
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((n_query + 31) / 32, unsigned(gy)), dim3(256), 0, st,
-                       s.kv_heads, s.group, s.window, s.max_pages_per_unit, n_query,
-                       sm_scale * 1.4426950408889634f, static_cast<const uint16_t *>(q),
+  const int nqb = (n_query + 31) / 32;
+  // split only when the workspace holds the partials
+  int nsplit = chunk_splits(s, n_query);
+  if (nsplit > 1 && (ws == nullptr || ws_bytes < chunk_split_bytes(s, n_query, nsplit))) nsplit = 1;
+  const ChunkSplitLayout L = chunk_split_layout(s, n_query, nsplit);
+  char *w = static_cast<char *>(ws);
+  float2 *part_ml = nsplit > 1 ? reinterpret_cast<float2 *>(w + L.part_ml) : nullptr;
+  float *part_o = nsplit > 1 ? reinterpret_cast<float *>(w + L.part_o) : nullptr;
+  const float scale_log2 = sm_scale * 1.4426950408889634f;
+  auto go = [&](auto kern, auto merge) {
+    hipLaunchKernelGGL(kern, dim3(unsigned(nqb * nsplit), unsigned(gy)), dim3(256), 0, st,
+                       s.kv_heads, s.group, s.window, s.max_pages_per_unit, n_query, scale_log2,
+                       nsplit, static_cast<const uint16_t *>(q),
                        static_cast<const uint4 *>(c.k_pages), static_cast<const uint4 *>(c.v_pages),
                        c.page_table, reinterpret_cast<const int4 *>(c.slot_pos),
                        reinterpret_cast<const uint4 *>(c.slot_alpha), c.n_slots, c.n_clean, c.seq_len,
-                       c.plan + plan_layout(units_of(s)).compact_pos, c.status, out);
+                       c.plan + plan_layout(units_of(s)).compact_pos, c.status, part_ml, part_o, out);
+    if (nsplit > 1) {
+      const size_t threads = size_t(L.rows) * (s.head_dim / 4);
+      hipLaunchKernelGGL(merge, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, st, int(L.rows),
+                         nsplit, scale_log2, part_ml, part_o, out);
+    }
   };
-  if (s.head_dim == 128) go(k_chunk_attn<128>);
-  else if (s.head_dim == 64) go(k_chunk_attn<64>);
+  if (s.head_dim == 128) go(k_chunk_attn<128>, k_chunk_merge<128>);
+  else if (s.head_dim == 64) go(k_chunk_attn<64>, k_chunk_merge<64>);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

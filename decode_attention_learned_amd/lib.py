@@ -53,6 +53,7 @@ EXPORTS = (
     "dms_append_reserve",
     "dms_decode_attn_fill",
     "dms_decode_multi_workspace_bytes",
+    "dms_decode_multi_split_workspace_bytes",
     "dms_decode_attn_multi",
     "dms_prefill_workspace_bytes",
     "dms_prefill_attn",
@@ -150,6 +151,7 @@ def load() -> ctypes.CDLL:
         "dms_decode_attn_fill": ([SP, CP, P, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t, P],
                                  ctypes.c_int),
         "dms_decode_multi_workspace_bytes": ([SP], ctypes.c_size_t),
+        "dms_decode_multi_split_workspace_bytes": ([SP, ctypes.c_int32], ctypes.c_size_t),
         "dms_decode_attn_multi": ([SP, CP, P, ctypes.c_int32, P, ctypes.c_float, P, ctypes.c_size_t, P],
                                   ctypes.c_int),
         "dms_prefill_workspace_bytes": ([SP, ctypes.c_int32], ctypes.c_size_t),
@@ -272,6 +274,10 @@ def dms_prefill_attn_relaxed(shape, q, k, v, logit, noise, temperature, seq_len,
 
 def decode_multi_workspace_bytes(shape: DmsShape) -> int:
     return load().dms_decode_multi_workspace_bytes(ctypes.byref(shape))
+
+
+def decode_multi_split_workspace_bytes(shape: DmsShape, n_query: int) -> int:
+    return load().dms_decode_multi_split_workspace_bytes(ctypes.byref(shape), int(n_query))
 
 
 def dms_decode_attn_multi(shape, cache, q, n_query, out, sm_scale, workspace, workspace_bytes,

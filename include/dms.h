@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define DMS_ABI_VERSION 4
+#define DMS_ABI_VERSION 5
 #define DMS_PAGE_SIZE 64
 
 /* host-side return codes */
@@ -313,6 +313,18 @@ int dms_release(const dms_shape *shape, const dms_cache *cache, int32_t first, i
 size_t dms_decode_multi_workspace_bytes(const dms_shape *shape);
 
 /*
+ * Bytes of workspace with which dms_decode_attn_multi splits a chunk of
+ * n_query >= 32 queries on a bf16 cache over the chip: when the tiled
+ * kernel's workgroups (one per 32 queries and sequence, KV head and group
+ * of 4 query heads) are fewer than one resident round (768), each takes a
+ * part of its keys and a merge launch combines the parts, which needs
+ * splits x B x n_query x Hq x (D + 2) floats.  At least
+ * dms_decode_multi_workspace_bytes(shape); equal to it where no split
+ * applies.  0 if the arguments are invalid.
+ */
+size_t dms_decode_multi_split_workspace_bytes(const dms_shape *shape, int32_t n_query);
+
+/*
  * Attention of the last n_query tokens of every sequence (a chunk appended
  * with dms_append(n_new = n_query)) over the cache: query c of sequence b
  * sits at position t_c = seq_len[b] - n_query + c and attends over the slots
@@ -327,10 +339,12 @@ size_t dms_decode_multi_workspace_bytes(const dms_shape *shape);
  * sets DMS_STATUS_CHUNK_INVALID in cache->status.
  *   q    [B][n_query][Hq][D] in kv_dtype,   out [B][n_query][Hq][D] float32
  * n_query >= 1.  bf16 caches: chunks of 32 queries or more run a tiled kernel
- * that reads the cache once per 32 queries; shorter ones run the split-K
- * decode kernel in launches of 16 / G queries.  float32 caches run the vector
- * decode kernel once per query position.  Workspace:
- * dms_decode_multi_workspace_bytes.  Errors as for dms_decode_attn.
+ * that reads the cache once per 32 queries, each group of 32 up to its last
+ * query's slot (split over the chip, then merged, when the workspace is at
+ * least dms_decode_multi_split_workspace_bytes(shape, n_query)); shorter
+ * ones run the split-K decode kernel in launches of 16 / G queries.  float32
+ * caches run the vector decode kernel once per query position.  Workspace:
+ * at least dms_decode_multi_workspace_bytes.  Errors as for dms_decode_attn.
  */
 int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const void *q,
                           int32_t n_query, float *out, float sm_scale, void *workspace,

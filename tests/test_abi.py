@@ -40,11 +40,11 @@ def test_test_build_exports_the_same_symbols(L):
         assert G is not L
         for name in _declared():
             assert hasattr(G, name), name
-        assert lib.version() == 4
+        assert lib.version() == 5
 
 
 def test_version_and_strerror(L):
-    assert lib.version() == 4
+    assert lib.version() == 5
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(lib.strerror(code), str)
 
@@ -86,6 +86,31 @@ def test_workspace_bytes(L):
     assert big >= 1536 * 4 * 128 * 4
     more = lib.decode_workspace_bytes(_shape(batch=256, kv_heads=8, group=4, head_dim=128))
     assert more >= 2048 * 4 * 128 * 4 > big
+
+
+def test_chunk_split_workspace_bytes(L):
+    """Workspace that lets a long bf16 chunk split its tiles: 512 queries of one
+    sequence with 32/8 heads make 16 x 8 = 128 tiled workgroups, at most half
+    a round of 768, so 4 splits of 512 x 32 rows of (m, l) and 128 floats."""
+    one = _shape(batch=1, kv_heads=8, group=4, head_dim=128, kv_dtype=lib.DMS_KV_BF16)
+    rows = 512 * 32
+    want = -(-4 * rows * 8 // 256) * 256 + -(-4 * rows * 128 * 4 // 256) * 256
+    assert lib.decode_multi_split_workspace_bytes(one, 512) == max(lib.decode_multi_workspace_bytes(one), want)
+    # 3 splits from 193 to 256 workgroups (768 // 256 = 3)
+    b3 = _shape(batch=4, kv_heads=4, group=4, head_dim=64, kv_dtype=lib.DMS_KV_BF16)   # 16 x 16 = 256
+    r3 = 4 * 512 * 16
+    want3 = -(-3 * r3 * 8 // 256) * 256 + -(-3 * r3 * 64 * 4 // 256) * 256
+    assert lib.decode_multi_split_workspace_bytes(b3, 512) == max(lib.decode_multi_workspace_bytes(b3), want3)
+    # no split: more than half a round (4 sequences: 512 workgroups), short
+    # chunks (the decode kernel serves them), float32 caches
+    sb = _shape(batch=4, kv_heads=8, group=4, head_dim=128, kv_dtype=lib.DMS_KV_BF16)
+    base = lib.decode_multi_workspace_bytes(sb)
+    assert lib.decode_multi_split_workspace_bytes(sb, 512) == base
+    assert lib.decode_multi_split_workspace_bytes(one, 31) == lib.decode_multi_workspace_bytes(one)
+    assert lib.decode_multi_split_workspace_bytes(_shape(kv_dtype=lib.DMS_KV_F32), 512) \
+        == lib.decode_multi_workspace_bytes(_shape(kv_dtype=lib.DMS_KV_F32))
+    assert lib.decode_multi_split_workspace_bytes(one, 0) == 0
+    assert lib.decode_multi_split_workspace_bytes(_shape(window=0), 64) == 0
 
 
 def test_host_side_errors_need_no_gpu(L):

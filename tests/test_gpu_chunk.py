@@ -244,3 +244,57 @@ def test_float32_chunk_compacted_after_append_is_flagged(gpu):
     cache.decode_chunk(q[:, 112:].contiguous().to(gpu))
     torch.cuda.synchronize()
     assert cache.status_word() == lib.DMS_STATUS_CHUNK_INVALID
+
+
+@pytest.mark.parametrize("zero_q", [True, False])
+def test_chunk_split_and_one_pass_agree(gpu, zero_q):
+    """Split-K of the tiled chunk kernel against its one-pass form and the
+    oracle: one sequence, 8 KV heads x G=4, D=128, a compacted 2000-token
+    prompt, then a 256-token chunk.  8 x 8 = 64 tiled workgroups, so the
+    library splits each four ways when the workspace allows (DmsCache sizes
+    it so) and runs one pass with the minimal workspace.
+    With zero queries every score is 0 and every weight exactly 1 in both
+    paths, so each output is the mean of the visible values to float32
+    rounding: both forms and the oracle agree to 1e-5, and a tile missed or
+    read twice by a split would show.  With random queries the weights enter
+    the PV product in bf16 (2^-9 relative), rounded against different
+    references in the two forms, so they agree to a few 1e-3 and each meets
+    the bf16 tolerance against the oracle."""
+    from decode_attention_learned_amd import lib
+    b, hkv, g, d, prompt, n = 1, 8, 4, 128, 2000, 256
+    q, k, v, logit = _tokens(b, hkv, g, d, prompt + n, 0.75, 6301)
+    if zero_q:
+        q = torch.zeros_like(q)
+    cache = DmsCache(b, hkv, g, d, torch.bfloat16, max_pages_per_unit=(prompt + n) // 64 + 2, device=gpu)
+    cache.append(k[:, :prompt].contiguous().to(gpu), v[:, :prompt].contiguous().to(gpu),
+                 logit[:, :prompt].contiguous().to(gpu))
+    cache.compact()
+    sl = slice(prompt, prompt + n)
+    cache.append(k[:, sl].contiguous().to(gpu), v[:, sl].contiguous().to(gpu), logit[:, sl].contiguous().to(gpu))
+    qc = q[:, sl].contiguous().to(gpu)
+    assert lib.decode_multi_split_workspace_bytes(cache.shape, n) > lib.decode_multi_workspace_bytes(cache.shape)
+    split = cache.decode_chunk(qc)
+    one = torch.empty_like(split)
+    small = torch.empty((lib.decode_multi_workspace_bytes(cache.shape),), dtype=torch.uint8, device=gpu)
+    lib.check("dms_decode_attn_multi", lib.dms_decode_attn_multi(
+        cache.shape, cache.cache, qc, n, one, 1.0 / math.sqrt(d), small, small.numel(),
+        torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert cache.status_word() == 0
+    gap = float((split - one).abs().max())
+    assert gap <= (1e-5 if zero_q else 4e-3), f"split and one-pass outputs differ by {gap:.3g}"
+    alpha = orc.eviction_decisions(logit.numpy())
+    worst = 0.0
+    for h in range(hkv):
+        kh, vh = k[0, :, h].float().numpy(), v[0, :, h].float().numpy()
+        for c in (0, 1, 31, 32, 100, 255):
+            t = prompt + c
+            ref = orc.decode_output(q[0, t, h * g:(h + 1) * g].float().numpy(), kh, vh, alpha[0, :, h], t,
+                                    16, 1.0 / math.sqrt(d))
+            for got_t in (split, one):
+                got = got_t[0, c, h * g:(h + 1) * g].cpu().double().numpy()
+                err = np.abs(got - ref)
+                worst = max(worst, float(err.max()))
+                bound = 1e-5 if zero_q else BF16_TOL["atol"] + BF16_TOL["rtol"] * np.abs(ref)
+                assert np.all(err <= bound), (h, c, float(err.max()))
+    say(f"chunk split vs one pass (zero q {zero_q}): max gap {gap:.2e}; vs oracle {worst:.2e}")

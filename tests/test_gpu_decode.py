@@ -478,3 +478,70 @@ def test_split_plan_ragged_800_units(gpu):
     p = cache.plan.cpu().numpy()
     merge = p[16 + cache.units + 1 + cap: 16 + cache.units + 1 + cap + cache.units]
     assert np.all(merge == 0), "merge counters not reset"
+
+
+def test_chunk_longer_than_the_staged_page_ids(gpu):
+    """One unit of 70,000 retained slots among 1536 units, all others evicting
+    every token: the lengths are ragged and the units as many as the ragged
+    budget (3 x 512 chunks), so every unit is one chunk and the long one spans
+    1095 pages, more than the 1024 page ids the matrix-core decode kernel stages
+    in LDS at a time: it walks that chunk in two segments.  The long unit's
+    queries are zero, so every weight is exactly 1 and its output is the mean
+    of its 70,001 values to float32 rounding (pinned to 1e-4 against the
+    oracle); other units are checked at the bf16 tolerance."""
+    b, hkv, g, d = 192, 8, 2, 64
+    n_long, chunk = 70000, 4096
+    maxp = n_long // 64 + 4
+    cache = DmsCache(b, hkv, g, d, torch.bfloat16, num_pages=b * hkv * 72 + maxp, max_pages_per_unit=maxp,
+                     device=gpu)
+    gen = torch.Generator(device=gpu).manual_seed(7301)
+    k0, v0 = [], []                 # unit 0 (sequence 0, KV head 0): every token
+    tail_k, tail_v = None, None     # the last chunk, for the other units
+    for start in range(0, n_long, chunk):
+        n = min(chunk, n_long - start)
+        k = torch.randn((b, n, hkv, d), generator=gen, device=gpu).to(torch.bfloat16)
+        v = torch.randn((b, n, hkv, d), generator=gen, device=gpu).to(torch.bfloat16)
+        logit = torch.ones((b, n, hkv), device=gpu)
+        logit[0, :, 0] = -1.0
+        cache.append(k, v, logit)
+        cache.compact()
+        k0.append(k[0, :, 0].float().cpu().numpy())
+        v0.append(v[0, :, 0].float().cpu().numpy())
+        tail_k, tail_v = k[:, -32:].float().cpu().numpy(), v[:, -32:].float().cpu().numpy()
+    q = torch.randn((b, hkv * g, d), generator=gen, device=gpu).to(torch.bfloat16)
+    q[0, :g] = 0
+    k = torch.randn((b, 1, hkv, d), generator=gen, device=gpu).to(torch.bfloat16)
+    v = torch.randn((b, 1, hkv, d), generator=gen, device=gpu).to(torch.bfloat16)
+    logit = torch.ones((b, 1, hkv), device=gpu)
+    logit[0, :, 0] = -1.0
+    cache.append(k, v, logit)
+    out = cache.decode(q).cpu()
+    torch.cuda.synchronize()
+    assert cache.status_word() == 0
+    n_slots = cache.n_slots.cpu().numpy()
+    assert n_slots[0] == n_long + 1 and n_slots[1:].max() <= 16 + chunk
+    plan = cache.plan.cpu().numpy()
+    assert plan[0] == b * hkv, "expected one chunk per unit"
+    assert plan[1] > 1024 * 64, "expected a chunk of more than 1024 pages"
+    scale = 1.0 / math.sqrt(d)
+    # unit 0: all 70,001 keys seen, zero queries -> the plain mean of the values
+    kk = np.concatenate(k0 + [k[0, :, 0].float().cpu().numpy()])
+    vv = np.concatenate(v0 + [v[0, :, 0].float().cpu().numpy()])
+    ref0 = orc.decode_output(np.zeros((g, d)), kk, vv, np.zeros(n_long + 1, dtype=np.int8), n_long, 16, scale)
+    err0 = float(np.abs(out[0, :g].double().numpy() - ref0).max())
+    assert err0 <= 1e-4, f"long unit: max err {err0:.3g}"
+    # other units: every token marked, so the last 16 (the window) are seen
+    ref = {}
+    t = n_long
+    for u in (1, 7, 8, 777, b * hkv - 1):
+        bi, h = divmod(u, hkv)
+        kk = np.zeros((t + 1, d))
+        vv = np.zeros((t + 1, d))
+        kk[t - 32:t] = tail_k[bi, :, h]
+        vv[t - 32:t] = tail_v[bi, :, h]
+        kk[t] = k[bi, 0, h].float().cpu().numpy()
+        vv[t] = v[bi, 0, h].float().cpu().numpy()
+        ref[u] = orc.decode_output(q[bi, h * g:(h + 1) * g].float().cpu().numpy(), kk, vv,
+                                   np.ones(t + 1, dtype=np.int8), t, 16, scale)
+    worst = compare_outputs(out, ref, hkv, g, torch.bfloat16, what="short units beside a long one")
+    say(f"1095-page chunk: long unit max err {err0:.2e}; short units {worst:.2e}")

@@ -1,6 +1,11 @@
 """DMS decode benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload qwen3_8b_cr8]
+                    [--batch B] [--context T] [--evict-rate R] [--window W]
+                    [--compact-every N] [--seed S] [--replicas N]
+
+(The page size is fixed at 64 slots by the library.)  A run with overrides
+reports them under config.overrides and no counter-based traffic figure.
 
 A step is one pass of the whole decode hot path for one attention layer over
 a batch: decide + append the new token of every (sequence, KV head) unit,
@@ -18,6 +23,8 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import contextlib
+import dataclasses
 import hashlib
 import json
 import re
@@ -37,6 +44,7 @@ METRIC = "DMS decode-attn tokens/s and KV GB/s (% HBM peak) at CR=8, Qwen3-8B sh
 # Llama-3.2-1B-shaped heads at CR 4, the Qwen3-8B shape with nothing evicted,
 # ragged Qwen2.5-32B-shaped units
 DECODE_CONFIGS = ("llama1b_cr4", "qwen3_8b_cr1", "qwen32b_width")
+DEFAULT_WORKLOAD = "qwen3_8b_cr8"
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_qwen3_8b_cr8_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "decode_attention_learned_amd", "csrc", "decode_mfma.hip")
 PREFILL_PMC_FILE = os.path.join(ROOT, "profiles", "prefill_8k_traffic.json")
@@ -45,6 +53,44 @@ PREFILL_SRC = os.path.join(ROOT, "decode_attention_learned_amd", "csrc", "prefil
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+@contextlib.contextmanager
+def marked(name: str):
+    """A roctx range named `name` around a part of the run (torch.cuda.nvtx emits
+    roctx ranges on ROCm builds): `rocprofv3 --marker-trace` then places every
+    kernel in its leg."""
+    import torch
+
+    torch.cuda.nvtx.range_push(name)
+    try:
+        yield
+    finally:
+        torch.cuda.nvtx.range_pop()
+
+
+# workload fields the command line may override, with their flags
+OVERRIDES = (("batch", "--batch", int, "sequences in the batch"),
+             ("context", "--context", int, "prompt tokens per sequence"),
+             ("evict_rate", "--evict-rate", float, "fraction of tokens marked for eviction"),
+             ("window", "--window", int, "delay window w (tokens)"),
+             ("compact_every", "--compact-every", int, "steps between compactions of a replica"),
+             ("seed", "--seed", int, "seed of the synthetic inputs"))
+
+
+def apply_overrides(w, args):
+    """The workload with the command line's overrides applied, and the overrides."""
+    over = {f: getattr(args, f) for f, *_ in OVERRIDES if getattr(args, f) is not None}
+    if not over:
+        return w, {}
+    if over.get("batch", 1) < 1 or over.get("context", 1) < 1 or over.get("window", 1) < 1 \
+            or over.get("compact_every", 1) < 1:
+        raise SystemExit(f"bench.py: overrides must be positive: {over}")
+    if not 0.0 <= over.get("evict_rate", 0.0) < 1.0:
+        raise SystemExit("bench.py: --evict-rate must lie in [0, 1)")
+    if "evict_rate" in over:
+        over["beta_rate"] = None          # a fixed rate replaces a per-unit draw
+    return dataclasses.replace(w, **over), over
 
 
 def src_hash(path: str) -> str:
@@ -218,7 +264,6 @@ def prefill_cpu_baseline(name: str = "prefill_8k", threads: int = 1) -> dict:
     distributions, query rows [0, 512) and [S - 512, S), every query head.  The
     oracle computes each row over all S keys (masked), so its cost per row is
     the same everywhere; the rate is query positions (all heads) per second."""
-    import dataclasses
 
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -391,7 +436,6 @@ def shared_prefix_leg(w, dev, threads: int = 8, steps: int = 24) -> dict:
     prompt once per thread (each thread appended it); the other holds it once
     per prompt and shares it (dms_share_prefix).  Same tokens, same outputs;
     reported: pages held and decode-attention time of both."""
-    import dataclasses
 
     import torch
 
@@ -473,7 +517,6 @@ def chunked_prefill_leg(name: str = "prefill_8k", chunk: int = 512, iters: int =
 
     w = wl.get(name)
     if batch is not None:
-        import dataclasses
         w = dataclasses.replace(w, batch=batch)
     dev = torch.device("cuda:0")
     q, k, v, logit = wl.prefill_inputs(w, device=dev)
@@ -671,8 +714,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen3_8b_cr8")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--replicas", type=int, default=None)
+    for field, flag, kind, what in OVERRIDES:
+        ap.add_argument(flag, dest=field, type=kind, default=None, help=f"override the workload's {what}")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate", type=float, default=None, metavar="GIB",
@@ -718,7 +763,7 @@ def main():
         print(json.dumps({n: decode_config_leg(n) for n in DECODE_CONFIGS}), flush=True)
         return
     dev = torch.device("cuda:0")
-    w = wl.get(args.workload)
+    w, over = apply_overrides(wl.get(args.workload), args)
     replicas = args.replicas or w.replicas
     every = w.compact_every
     # the breakdown pass: per-call events on every step, at least one compaction
@@ -731,7 +776,8 @@ def main():
     log(f"[bench] building {replicas} replica(s) of {w.name}: B={w.batch} Hkv={w.kv_heads} "
         f"G={w.group} D={w.head_dim} context={w.context}")
     t_build = time.perf_counter()
-    caches = [build_replica(w, r, dev, extra) for r in range(replicas)]
+    with marked("build"):
+        caches = [build_replica(w, r, dev, extra) for r in range(replicas)]
     log(f"[bench] built in {time.perf_counter() - t_build:.1f} s")
 
     inputs = [[wl.decode_step_inputs(w, j, device=dev, replica=r, rates=caches[r][1])
@@ -781,21 +827,23 @@ def main():
             ev[4].record()
         return compacted
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    with marked("warmup"):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
     before = [retained_total(c) for c, _ in caches]
 
     # the timed window: the steps alone between two events on the library's stream
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
     n_compact = 0
-    for i in range(args.warmup, args.warmup + args.steps):
-        n_compact += step(i)
-    end.record()
-    torch.cuda.synchronize()
+    with marked("timed steps"):
+        start.record()
+        for i in range(args.warmup, args.warmup + args.steps):
+            n_compact += step(i)
+        end.record()
+        torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     after = [retained_total(c) for c, _ in caches]
     status = [c.status_word() for c, _ in caches]
@@ -806,8 +854,9 @@ def main():
     i0 = args.warmup + args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_break)]
     peaks = []
-    flags = [step(i0 + i, evs[i], peaks) for i in range(n_break)]
-    torch.cuda.synchronize()
+    with marked("breakdown"):
+        flags = [step(i0 + i, evs[i], peaks) for i in range(n_break)]
+        torch.cuda.synchronize()
     if any(c.status_word() for c, _ in caches):
         raise RuntimeError("device status set in the breakdown pass")
     t_reserve = [e[0].elapsed_time(e[1]) for e in evs]
@@ -848,6 +897,7 @@ def main():
             "head_dim": w.head_dim, "context": w.context, "evict_rate": w.evict_rate,
             "window": w.window, "compact_every": every, "page_size": 64,
             "replicas": replicas, "kv_dtype": "bf16", "accumulate": "fp32",
+            "overrides": over or None,
         },
         "step_calls": ("dms_append + dms_decode_attn" if args.append_launch
                        else "dms_append_reserve + dms_decode_attn_fill") + " + dms_compact every "
@@ -873,12 +923,13 @@ def main():
         "dead_slot_overhead": round(bytes_read / bytes_alg - 1.0, 5),
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_decode_mfma<128>",
+            "kernel": f"k_decode_mfma<{w.head_dim}>",
             "achieved": round(kv_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(kv_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": traffic_from_profile(bytes_alg),
+            # the counters were taken on the default workload
+            "traffic": None if over or args.workload != DEFAULT_WORKLOAD else traffic_from_profile(bytes_alg),
             "algorithmic_bytes_per_launch": int(bytes_alg),
             "launch_time_from": "HIP events around each dms_decode_attn_fill call of the breakdown pass",
         },
@@ -889,18 +940,21 @@ def main():
     # context, not a ceiling: what two torch kernels reach on this GPU over 4 GiB (beyond
     # the MALL), a full read (sum) and a device copy (read + write); torch's reduction does
     # not stream at the HBM rate, so the decode kernel can exceed it
-    cal = calibrate(4.0)
+    with marked("calibration"):
+        cal = calibrate(4.0)
     result["torch_sum_read_gbps"] = cal["sum_read_gbps"]
     result["torch_copy_gbps"] = cal["copy_read_plus_write_gbps"]
     result["kv_frac_of_torch_copy"] = round(kv_gbps / cal["copy_read_plus_write_gbps"], 4)
     if not args.no_chunk:
-        result["chunk"] = chunk_leg(caches, w, dev)
+        with marked("chunk queries"):
+            result["chunk"] = chunk_leg(caches, w, dev)
         log(f"[bench] chunk of {result['chunk']['n_query']} queries: {result['chunk']['attn_us']:.1f} us, "
             f"{result['chunk']['tokens_per_s']:.0f} tok/s")
     del inputs, caches, outs
     torch.cuda.empty_cache()
     if not args.no_share:
-        result["shared_prefix"] = shared_prefix_leg(w, dev)
+        with marked("shared prefix"):
+            result["shared_prefix"] = shared_prefix_leg(w, dev)
         sp = result["shared_prefix"]
         log(f"[bench] shared prompts: {sp['pages_shared']} pages vs {sp['pages_copied']}, decode "
             f"{sp['decode_us_shared']:.1f} us vs {sp['decode_us_copied']:.1f} us")
@@ -908,13 +962,15 @@ def main():
     if not args.no_configs:
         result["decode_configs"] = {}
         for n in DECODE_CONFIGS:
-            rec = decode_config_leg(n)
+            with marked(f"decode {n}"):
+                rec = decode_config_leg(n)
             result["decode_configs"][n] = rec
             log(f"[bench] {n}: {rec['ms_per_step'] * 1e3:.1f} us/step, decode {rec['decode_attn_us']:.1f} us "
                 f"= {rec['kv_gbps']:.0f} GB/s ({100 * rec['hbm_frac']:.1f}% of HBM peak)")
     if not args.no_prefill:
         log("[bench] masked prefill, 8192 tokens")
-        result["prefill"] = prefill_leg()
+        with marked("prefill 8k"):
+            result["prefill"] = prefill_leg()
         log(f"[bench] prefill {result['prefill']['ms']:.3f} ms = "
             f"{result['prefill']['roofline']['achieved']:.0f} TFLOP/s causal; gathered "
             f"{result['prefill']['gathered']['ms']:.3f} ms")
@@ -923,12 +979,15 @@ def main():
             result["prefill"]["cpu_baseline"] = prefill_cpu_baseline(threads=1)
         torch.cuda.empty_cache()
         log("[bench] masked prefill, head_dim 64 (Llama-3.2-1B-shaped heads), 4096 tokens")
-        result["prefill_head_dim_64"] = prefill_leg("prefill_4k_d64", relaxed=False)
+        with marked("prefill 4k head_dim 64"):
+            result["prefill_head_dim_64"] = prefill_leg("prefill_4k_d64", relaxed=False)
         torch.cuda.empty_cache()
-        result["chunked_prefill"] = chunked_prefill_leg()
+        with marked("chunked prefill"):
+            result["chunked_prefill"] = chunked_prefill_leg()
         log(f"[bench] chunked prefill: last {result['chunked_prefill']['chunk']} tokens in "
             f"{result['chunked_prefill']['ms']:.3f} ms")
-        result["chunked_prefill_one_sequence"] = chunked_prefill_leg(batch=1)
+        with marked("chunked prefill one sequence"):
+            result["chunked_prefill_one_sequence"] = chunked_prefill_leg(batch=1)
         log(f"[bench] chunked prefill, one sequence: "
             f"{result['chunked_prefill_one_sequence']['ms']:.3f} ms split, "
             f"{result['chunked_prefill_one_sequence']['ms_without_split']:.3f} ms without")

@@ -71,13 +71,34 @@ class DmsCache:
         self.status = torch.empty((1,), **i32)
         self.plan = torch.empty((lib.plan_words(self.shape),), **i32)
         self.page_ref = torch.empty((self.num_pages,), **i32)
-        self.cache = lib.DmsCacheStruct(*[t.data_ptr() for t in (
-            self.k_pages, self.v_pages, self.page_table, self.slot_pos, self.slot_alpha,
-            self.n_slots, self.n_clean, self.append_base, self.seq_len, self.free_list,
-            self.free_top, self.status, self.plan, self.page_ref)])
+        self._bind()
         self.workspace_bytes = lib.decode_workspace_bytes(self.shape)
         self.workspace = torch.empty((self.workspace_bytes,), dtype=torch.uint8, device=dev)
         self.reset()
+
+    # The cache state: every buffer the library reads or writes, in the order of
+    # the dms_cache struct.  The library keeps nothing else, so these tensors
+    # are the whole state (a checkpoint is a copy of them).
+    STATE = ("k_pages", "v_pages", "page_table", "slot_pos", "slot_alpha", "n_slots", "n_clean",
+             "append_base", "seq_len", "free_list", "free_top", "status", "plan", "page_ref")
+
+    def _bind(self) -> None:
+        """(Re)build the dms_cache struct from the state tensors' addresses."""
+        self.cache = lib.DmsCacheStruct(*[getattr(self, n).data_ptr() for n in self.STATE])
+
+    def state_dict(self) -> dict:
+        """Copies of the state tensors (for torch.save)."""
+        return {n: getattr(self, n).clone() for n in self.STATE}
+
+    def load_state_dict(self, state: dict) -> None:
+        """Overwrite the state with a checkpoint of a cache of the same shape."""
+        for n in self.STATE:
+            dst = getattr(self, n)
+            src = state[n]
+            if src.shape != dst.shape or src.dtype != dst.dtype:
+                raise ValueError(f"checkpoint field {n}: {tuple(src.shape)} {src.dtype}, "
+                                 f"cache holds {tuple(dst.shape)} {dst.dtype}")
+            dst.copy_(src)
 
     # -- calls -------------------------------------------------------------
     def reset(self) -> None:

@@ -82,3 +82,26 @@ def test_oracle_baseline_record():
     rec = bench.cpu_baseline(w, seconds=0.3, threads=1)
     assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s" and rec["cores"] == 1
     assert rec["value"] > 0 and rec["seconds_per_step"] > 0 and "sample" in rec
+
+
+def test_workload_overrides():
+    """--batch/--context/--evict-rate/--window/--compact-every/--seed replace the
+    workload's fields; a fixed rate replaces a per-unit draw; bad values exit."""
+    import argparse
+
+    base = wl.get("qwen32b_width")
+    none = argparse.Namespace(**{f: None for f, *_ in bench.OVERRIDES})
+    w, over = bench.apply_overrides(base, none)
+    assert w is base and over == {}
+    args = argparse.Namespace(batch=2, context=1000, evict_rate=0.5, window=8, compact_every=4, seed=9)
+    w, over = bench.apply_overrides(base, args)
+    assert (w.batch, w.context, w.evict_rate, w.window, w.compact_every, w.seed) == (2, 1000, 0.5, 8, 4, 9)
+    assert w.beta_rate is None and over["beta_rate"] is None
+    assert (w.kv_heads, w.group, w.head_dim) == (base.kv_heads, base.group, base.head_dim)
+    for bad in (dict(batch=0), dict(evict_rate=1.0), dict(window=0)):
+        a = argparse.Namespace(**{**vars(none), **bad})
+        try:
+            bench.apply_overrides(base, a)
+        except SystemExit:
+            continue
+        raise AssertionError(f"{bad} accepted")

@@ -67,7 +67,7 @@ __global__ void k_reset(int units, int maxp, int num_pages, int batch, int32_t *
 // standalone planner (after reset and compaction)
 __global__ __launch_bounds__(kPlanThreads) void k_plan(int units, const int32_t *n_slots,
                                                        int32_t *plan) {
-  build_plan(units, n_slots, plan);
+  build_plan(units, [=](int u) { return n_slots[u]; }, plan);
 }
 
 hipError_t launch_plan(const dms_shape &s, const dms_cache &c, hipStream_t st) {
@@ -99,6 +99,9 @@ hipError_t launch_reset(const dms_shape &s, const dms_cache &c, hipStream_t st) 
 // handed out are distinct.  The result is deterministic.
 // ---------------------------------------------------------------------------
 constexpr int kAllocThreads = 1024;
+// up to this many units the planner reads the new counts from LDS, not back
+// from global memory
+constexpr int kAllocLdsUnits = 4096;
 
 __global__ __launch_bounds__(kAllocThreads) void k_append_alloc(
     int units, int batch, int maxp, int n_new, int32_t *page_table, int32_t *n_slots,
@@ -108,11 +111,16 @@ __global__ __launch_bounds__(kAllocThreads) void k_append_alloc(
   __shared__ int s_tmp[kAllocThreads / kWave];
   __shared__ int s_taken;
   __shared__ uint32_t s_flags;
+  __shared__ int32_t s_ns[kAllocLdsUnits];
   if (threadIdx.x == 0) {
     s_taken = 0;
     s_flags = 0u;
   }
+  // the free count, the first kAllocThreads counts and sequence lengths are
+  // requested together
   const int F = *free_top;
+  const int ns_first = int(threadIdx.x) < units ? n_slots[threadIdx.x] : 0;
+  const int len_first = int(threadIdx.x) < batch ? seq_len[threadIdx.x] : 0;
   __syncthreads();
   int carry = 0;
   for (int base = 0; base < units; base += kAllocThreads) {
@@ -120,7 +128,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_append_alloc(
     int ns = 0, have = 0, need = 0;
     bool row_ok = true;
     if (u < units) {
-      ns = n_slots[u];
+      ns = base == 0 ? ns_first : n_slots[u];
       have = (ns + kPage - 1) / kPage;
       const int want = (ns + n_new + kPage - 1) / kPage;
       row_ok = want <= maxp;
@@ -140,18 +148,23 @@ __global__ __launch_bounds__(kAllocThreads) void k_append_alloc(
         append_base[u] = -1;
         atomicOr(&s_flags, row_ok ? DMS_STATUS_POOL_EXHAUSTED : DMS_STATUS_ROW_OVERFLOW);
       }
+      if (u < kAllocLdsUnits) s_ns[u] = ok ? ns + n_new : ns;
     }
     carry += total;
   }
-  for (int b = threadIdx.x; b < batch; b += kAllocThreads) seq_len[b] += n_new;
+  for (int b = threadIdx.x; b < batch; b += kAllocThreads)
+    seq_len[b] = (b < kAllocThreads ? len_first : seq_len[b]) + n_new;
   __syncthreads();
   if (threadIdx.x == 0) {
     *free_top = F - s_taken;
     if (s_flags) atomicOr(status, s_flags);
   }
   // n_slots changed: rebuild the decode split plan (each thread re-reads only
-  // the entries it wrote above)
-  build_plan(units, n_slots, plan);
+  // the entries it wrote above; from LDS when they all fit there)
+  if (units <= kAllocLdsUnits)
+    build_plan(units, [&](int u) { return s_ns[u]; }, plan);
+  else
+    build_plan(units, [=](int u) { return n_slots[u]; }, plan);
 }
 
 // ---------------------------------------------------------------------------
@@ -571,7 +584,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_share_alloc(
   // every unit's n_slots is read back by the planner: make this workgroup's
   // writes visible to all of its threads first
   __threadfence_block();
-  build_plan(units, n_slots, plan);
+  build_plan(units, [=](int u) { return n_slots[u]; }, plan);
 }
 
 // prefix sharing, part 2: copy the source's page P + i into the receiver's
@@ -665,7 +678,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_release(int hkv, int maxp, in
   }
   for (int b = threadIdx.x; b < nseq; b += kAllocThreads) seq_len[first + b] = 0;
   __syncthreads();
-  build_plan(units, n_slots, plan);
+  build_plan(units, [=](int u) { return n_slots[u]; }, plan);
 }
 
 hipError_t launch_release(const dms_shape &s, const dms_cache &c, int first, int n, hipStream_t st) {

@@ -239,7 +239,9 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 // so that sum_u chunks(u) <= total / C + units <= budget.
 constexpr int kPlanThreads = 1024;
 
-__device__ inline void build_plan(int units, const int32_t *n_slots, int32_t *plan) {
+// `count(u)` returns n_slots of unit u.
+template <typename Count>
+__device__ inline void build_plan(int units, Count count, int32_t *plan) {
   const PlanLayout L = plan_layout(units);
   int32_t *hdr = plan + L.hdr;
   int32_t *first_chunk = plan + L.first_chunk;
@@ -256,7 +258,7 @@ __device__ inline void build_plan(int units, const int32_t *n_slots, int32_t *pl
   long long part = 0;
   int mx = 0;
   for (int u = threadIdx.x; u < units; u += kPlanThreads) {
-    const int n = n_slots[u];
+    const int n = count(u);
     part += n;
     mx = max(mx, n);
   }
@@ -285,7 +287,7 @@ __device__ inline void build_plan(int units, const int32_t *n_slots, int32_t *pl
     const int u = base + threadIdx.x;
     int nch = 0;
     if (u < units) {
-      const int n = n_slots[u];
+      const int n = count(u);
       nch = n > 0 ? (n + C - 1) / C : 1;
     }
     const int w = threadIdx.x / kWave, l = lane_id();

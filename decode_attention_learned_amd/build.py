@@ -26,7 +26,7 @@ LIB_GENERIC = os.path.join(HERE, "libdms_generic.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "cache_kernels.hip", "decode_kernels.hip", "decode_mfma.hip", "decode_scratch.hip",
-           "prefill.hip"]
+           "prefill.hip", "prefill_f32.hip"]
 
 # Packed fp32 instructions are switched off for all device code; hipcc's host
 # pass warns that it does not know the feature, which is harmless.

@@ -211,14 +211,19 @@ static int check_prefill_shape(const dms_shape *shape, int32_t seq_len) {
   if (shape->batch < 1 || shape->kv_heads < 1 || shape->group < 1 || shape->window < 1)
     return DMS_EINVAL;
   if (seq_len < 0) return DMS_EINVAL;
-  if ((shape->head_dim != 128 && shape->head_dim != 64) || shape->kv_dtype != DMS_KV_BF16 ||
-      shape->group > 16)
-    return DMS_EUNSUPPORTED;
+  if (shape->head_dim != 128 && shape->head_dim != 64) return DMS_EUNSUPPORTED;
+  if (shape->kv_dtype == DMS_KV_F32) return DMS_OK;  // the vector kernel: any group
+  if (shape->kv_dtype != DMS_KV_BF16 || shape->group > 16) return DMS_EUNSUPPORTED;
   return DMS_OK;
 }
 
+// float32 prefill uses no workspace; this many bytes are still asked for, so
+// that 0 keeps meaning invalid arguments
+constexpr size_t kPrefillF32Workspace = 256;
+
 size_t dms_prefill_workspace_bytes(const dms_shape *shape, int32_t seq_len) {
   if (check_prefill_shape(shape, seq_len) != DMS_OK) return 0;
+  if (shape->kv_dtype == DMS_KV_F32) return kPrefillF32Workspace;
   return dms::prefill_workspace_bytes(shape->batch, shape->kv_heads, seq_len, shape->head_dim);
 }
 
@@ -233,6 +238,9 @@ int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const
     return DMS_EINVAL;
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
   if (workspace_bytes < dms_prefill_workspace_bytes(shape, seq_len)) return DMS_EWORKSPACE;
+  if (shape->kv_dtype == DMS_KV_F32)
+    return from_hip(dms::launch_prefill_f32(*shape, q, k, v, logit, nullptr, 0.f, seq_len, sm_scale,
+                                            out, stream));
   return from_hip(dms::launch_prefill(*shape, q, k, v, logit, nullptr, 0.f, seq_len, sm_scale, out,
                                       workspace, stream));
 }
@@ -250,12 +258,16 @@ int dms_prefill_attn_relaxed(const dms_shape *shape, const void *q, const void *
     return DMS_EINVAL;
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
   if (workspace_bytes < dms_prefill_workspace_bytes(shape, seq_len)) return DMS_EWORKSPACE;
+  if (shape->kv_dtype == DMS_KV_F32)
+    return from_hip(dms::launch_prefill_f32(*shape, q, k, v, logit, noise, temperature, seq_len,
+                                            sm_scale, out, stream));
   return from_hip(dms::launch_prefill(*shape, q, k, v, logit, noise, temperature, seq_len, sm_scale,
                                       out, workspace, stream));
 }
 
 size_t dms_prefill_gathered_workspace_bytes(const dms_shape *shape, int32_t seq_len) {
   if (check_prefill_shape(shape, seq_len) != DMS_OK) return 0;
+  if (shape->kv_dtype == DMS_KV_F32) return kPrefillF32Workspace;
   return dms::prefill_gathered_layout(shape->batch, shape->kv_heads, seq_len, shape->head_dim).total;
 }
 
@@ -270,6 +282,10 @@ int dms_prefill_attn_gathered(const dms_shape *shape, const void *q, const void 
     return DMS_EINVAL;
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
   if (workspace_bytes < dms_prefill_gathered_workspace_bytes(shape, seq_len)) return DMS_EWORKSPACE;
+  // float32: the vector kernel, which skips the tiles no query of a block sees
+  if (shape->kv_dtype == DMS_KV_F32)
+    return from_hip(dms::launch_prefill_f32(*shape, q, k, v, logit, nullptr, 0.f, seq_len, sm_scale,
+                                            out, stream));
   return from_hip(
       dms::launch_prefill_gathered(*shape, q, k, v, logit, seq_len, sm_scale, out, workspace, stream));
 }

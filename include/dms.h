@@ -351,12 +351,12 @@ int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const 
                           size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Bytes of prefill workspace for `seq_len` tokens of this shape: keys and
- * values re-laid out per 32-key tile for the matrix cores, one float per key
- * (its decision as an additive mask), and the re-laid keys and values again
- * with every key masked out under the hard rule zeroed (read where all of a
- * tile's keys are at least w behind every query).  0 if the arguments are
- * invalid.
+ * Bytes of prefill workspace for `seq_len` tokens of this shape.  bf16:
+ * keys and values re-laid out per 32-key tile for the matrix cores, one float
+ * per key (its decision as an additive mask), and the re-laid keys and values
+ * again with every key masked out under the hard rule zeroed (read where all
+ * of a tile's keys are at least w behind every query).  float32: 256 (the
+ * vector kernel uses none).  0 if the arguments are invalid.
  */
 size_t dms_prefill_workspace_bytes(const dms_shape *shape, int32_t seq_len);
 
@@ -366,14 +366,17 @@ size_t dms_prefill_workspace_bytes(const dms_shape *shape, int32_t seq_len);
  * "Measured effects" for the 16-token window).  Row i of query head hq
  * attends to key j of KV head hq/G iff
  *   j <= i  and  not (alpha_j and i >= j + w),   alpha_j = logit_j > 0.
- *   q      [B][S][Hq][D]  kv_dtype (DMS_KV_BF16 only)
+ *   q      [B][S][Hq][D]  kv_dtype
  *   k, v   [B][S][Hkv][D] kv_dtype
  *   logit  [B][S][Hkv]    float32
  *   out    [B][S][Hq][D]  float32
  *   workspace  at least dms_prefill_workspace_bytes(shape, S) bytes, 16-byte
  *              aligned, no initialisation needed, nothing kept after the call
  * Only batch, kv_heads, group, head_dim (64 or 128), window and kv_dtype of
- * `shape` are read.  The cache is filled separately with dms_append.
+ * `shape` are read.  bf16 inputs run on the matrix cores (group <= 16);
+ * float32 inputs run a vector kernel with float32 products (any group), the
+ * same kernel for all three prefill calls, skipping tiles no query of a
+ * block sees.  The cache is filled separately with dms_append.
  */
 int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const void *v,
                      const float *logit, int32_t seq_len, float sm_scale, float *out,
@@ -402,8 +405,8 @@ int dms_prefill_attn_relaxed(const dms_shape *shape, const void *q, const void *
 /*
  * Bytes of workspace for dms_prefill_attn_gathered: the dense prefill
  * workspace, the same layout again for the gathered kept keys, and per
- * (sequence, KV head) the kept positions and per-tile counts.  0 if the
- * arguments are invalid.
+ * (sequence, KV head) the kept positions and per-tile counts (float32: 256,
+ * unused).  0 if the arguments are invalid.
  */
 size_t dms_prefill_gathered_workspace_bytes(const dms_shape *shape, int32_t seq_len);
 

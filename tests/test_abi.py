@@ -185,8 +185,15 @@ def test_prefill_host_errors(L):
     f32 = _shape()
     bf = _shape(kv_dtype=lib.DMS_KV_BF16, head_dim=128)
     big = 1 << 40
-    assert L.dms_prefill_attn(ctypes.byref(f32), fake, fake, fake, fake, 16, 0.1, fake, fake, big, None) \
-        == lib.DMS_EUNSUPPORTED
+    # float32 inputs are served (the vector kernel, no workspace used, 256 bytes asked
+    # for); a head dimension other than 64 or 128 is not
+    f32_d96 = _shape(head_dim=96)
+    assert L.dms_prefill_attn(ctypes.byref(f32_d96), fake, fake, fake, fake, 16, 0.1, fake, fake, big,
+                              None) == lib.DMS_EUNSUPPORTED
+    assert L.dms_prefill_attn(ctypes.byref(f32), fake, fake, fake, fake, 16, 0.1, fake, fake, 10, None) \
+        == lib.DMS_EWORKSPACE
+    assert L.dms_prefill_attn(ctypes.byref(f32), None, fake, fake, fake, 16, 0.1, fake, fake, big, None) \
+        == lib.DMS_EINVAL
     assert L.dms_prefill_attn(ctypes.byref(bf), fake, fake, fake, fake, -2, 0.1, fake, fake, big, None) \
         == lib.DMS_EINVAL
     assert L.dms_prefill_attn(ctypes.byref(bf), None, None, None, None, 0, 0.1, None, None, 0, None) \
@@ -198,7 +205,9 @@ def test_prefill_host_errors(L):
     # 2 sequences x 2 KV heads x ceil(100/32) tiles x 16 KB, plus 32 floats per tile,
     # plus the far-tile copy (16 KB per tile)
     assert lib.prefill_workspace_bytes(bf, 100) == 2 * (2 * 2 * 4 * 16384) + 2 * 2 * 4 * 32 * 4
-    assert lib.prefill_workspace_bytes(f32, 100) == 0
+    assert lib.prefill_workspace_bytes(f32, 100) == 256
+    assert lib.prefill_workspace_bytes(_shape(group=40), 100) == 256    # any group for float32
+    assert lib.prefill_workspace_bytes(_shape(kv_dtype=lib.DMS_KV_BF16, group=17), 100) == 0
     # gathered: dense part, gathered copy of it, kept positions (S per unit),
     # counts (ntiles + 1 per unit) and kept bits (ntiles per unit), each 256-aligned
     dense = 2 * 2 * 4 * 16384 + 2 * 2 * 4 * 32 * 4
@@ -209,16 +218,20 @@ def test_prefill_host_errors(L):
         == lib.DMS_EINVAL
     assert R(ctypes.byref(bf), fake, fake, fake, fake, None, 1.0, 16, 0.1, fake, fake, 10, None) \
         == lib.DMS_EWORKSPACE
-    assert R(ctypes.byref(f32), fake, fake, fake, fake, None, 1.0, 16, 0.1, fake, fake, big, None) \
+    assert R(ctypes.byref(f32_d96), fake, fake, fake, fake, None, 1.0, 16, 0.1, fake, fake, big, None) \
         == lib.DMS_EUNSUPPORTED
+    assert R(ctypes.byref(f32), fake, fake, fake, fake, None, 0.0, 16, 0.1, fake, fake, big, None) \
+        == lib.DMS_EINVAL
     G = L.dms_prefill_attn_gathered
-    assert G(ctypes.byref(f32), fake, fake, fake, fake, 16, 0.1, fake, fake, big, None) == lib.DMS_EUNSUPPORTED
+    assert G(ctypes.byref(f32_d96), fake, fake, fake, fake, 16, 0.1, fake, fake, big, None) \
+        == lib.DMS_EUNSUPPORTED
+    assert G(ctypes.byref(f32), fake, fake, fake, fake, 16, 0.1, fake, fake, 10, None) == lib.DMS_EWORKSPACE
     assert G(ctypes.byref(bf), fake, fake, fake, fake, -2, 0.1, fake, fake, big, None) == lib.DMS_EINVAL
     assert G(ctypes.byref(bf), None, None, None, None, 0, 0.1, None, None, 0, None) == lib.DMS_OK
     assert G(ctypes.byref(bf), None, fake, fake, fake, 16, 0.1, fake, fake, big, None) == lib.DMS_EINVAL
     assert G(ctypes.byref(bf), fake, fake, fake, fake, 16, -1.0, fake, fake, big, None) == lib.DMS_EINVAL
     assert G(ctypes.byref(bf), fake, fake, fake, fake, 16, 0.1, fake, fake, 10, None) == lib.DMS_EWORKSPACE
-    assert lib.prefill_gathered_workspace_bytes(f32, 100) == 0
+    assert lib.prefill_gathered_workspace_bytes(f32, 100) == 256
     # head_dim 64 is built (tiles of 8 KB), other dims are not
     d64 = _shape(kv_dtype=lib.DMS_KV_BF16, head_dim=64)
     d128 = _shape(kv_dtype=lib.DMS_KV_BF16, head_dim=128)

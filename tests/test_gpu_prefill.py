@@ -302,3 +302,95 @@ def test_prefill_llama1b_shape_sampled_rows(gpu, method):
     worst = _check_rows(full, q.cpu(), k.cpu(), v.cpu(), logit.cpu(), rows, 16,
                         what=f"llama-shaped {method}")
     say(f"prefill {method} Llama-1B shape, S=4096: max err {worst:.2e}")
+
+
+# ------------------------------------------------------------- float32 inputs
+# Float32 inputs run the vector kernel for all three methods; the tolerance is
+# the float32 one, max |o - o_ref| <= 1e-5 (inputs exact in float64).
+F32_ATOL = 1e-5
+
+
+def _inputs_f32(b, s, hkv, g, d, rate=0.5, seed=0):
+    w = wl.Workload(name="prefill_f32_case", kind="prefill", batch=b, kv_heads=hkv, group=g,
+                    head_dim=d, dtype="f32", context=s, evict_rate=rate, seed=seed)
+    return w, wl.prefill_inputs(w)
+
+
+def _check_rows_f32(out, q, k, v, logit, rows, window, what=""):
+    b_n, s, hq, d = q.shape
+    alpha = orc.eviction_decisions(logit.numpy())
+    worst = 0.0
+    for bi in range(b_n):
+        ref = orc.prefill_rows(q[bi].numpy(), k[bi].numpy(), v[bi].numpy(), alpha[bi], rows, window,
+                               1.0 / math.sqrt(d))
+        err = np.abs(out[bi, rows].double().numpy() - ref)
+        worst = max(worst, float(err.max()))
+        assert err.max() <= F32_ATOL, f"{what} seq {bi}: max err {err.max():.3g}"
+    return worst
+
+
+@pytest.mark.parametrize("method", METHODS)
+@pytest.mark.parametrize("b,s,hkv,g,d", [(2, 200, 2, 4, 128), (1, 97, 1, 1, 64), (1, 150, 1, 5, 128),
+                                         (1, 1, 1, 4, 64), (2, 385, 1, 3, 64), (1, 70, 2, 20, 64)])
+def test_prefill_f32_all_rows(gpu, b, s, hkv, g, d, method):
+    w, (q, k, v, logit) = _inputs_f32(b, s, hkv, g, d, rate=0.6, seed=6400 + s + g + d)
+    assert q.dtype == torch.float32
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16, method=method).cpu()
+    worst = _check_rows_f32(out, q, k, v, logit, np.arange(s), 16,
+                            what=f"f32 {method} B={b} S={s} Hkv={hkv} G={g} D={d}")
+    say(f"prefill f32 {method} B={b} S={s} Hkv={hkv} G={g} D={d}: max err {worst:.2e}")
+
+
+@pytest.mark.parametrize("window", [1, 40])
+@pytest.mark.parametrize("rate", [0.0, 0.9, 1.0])
+def test_prefill_f32_windows_and_rates(gpu, window, rate):
+    """Windows and eviction rates from nothing marked to everything marked, where
+    whole far tiles are skipped (rate 1: only the band is seen)."""
+    w, (q, k, v, logit) = _inputs_f32(1, 300, 2, 2, 128, rate=rate, seed=6500 + window)
+    qd, kd, vd, ld = q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu)
+    dense = prefill(qd, kd, vd, ld, window=window, method="dense").cpu()
+    _check_rows_f32(dense, q, k, v, logit, np.arange(300), window, what=f"f32 w={window} rate={rate}")
+    gath = prefill(qd, kd, vd, ld, window=window, method="gathered").cpu()
+    assert torch.equal(dense, gath), "float32 gathered and dense run the same kernel"
+
+
+def test_prefill_f32_all_keep_is_causal_sdpa(gpu):
+    w, (q, k, v, logit) = _inputs_f32(1, 129, 2, 2, 64, rate=0.0, seed=6601)
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16).cpu()
+    qq = q[0].double().permute(1, 0, 2)
+    kk = k[0].double().permute(1, 0, 2).repeat_interleave(2, 0)
+    vv = v[0].double().permute(1, 0, 2).repeat_interleave(2, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, is_causal=True, scale=1 / 8)
+    assert (out[0].double() - ref.permute(1, 0, 2)).abs().max() <= F32_ATOL
+
+
+@pytest.mark.parametrize("tau,with_noise", [(0.5, True), (2.0, False)])
+def test_prefill_f32_relaxed(gpu, tau, with_noise):
+    from oracle import soft_mask as smo
+
+    w, (q, k, v, logit) = _inputs_f32(2, 170, 2, 4, 128, rate=0.5, seed=6700)
+    noise = wl.logistic_noise(w) if with_noise else None
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16, method="relaxed",
+                  noise=noise.to(gpu) if noise is not None else None, temperature=tau).cpu()
+    for bi in range(2):
+        ref = smo.soft_prefill_rows(q[bi].numpy(), k[bi].numpy(), v[bi].numpy(), logit[bi].numpy(),
+                                    noise[bi].numpy() if noise is not None else 0.0, tau,
+                                    np.arange(170), 16, 1.0 / math.sqrt(128))
+        assert np.abs(out[bi].double().numpy() - ref).max() <= F32_ATOL
+
+
+def test_prefill_f32_matches_f32_decode(gpu):
+    """Prefill row t equals the float32 cache's decode at step t (both float32
+    paths, both exact-input), including after compactions."""
+    b, s, hkv, g, d = 1, 120, 2, 2, 64
+    w, (q, k, v, logit) = _inputs_f32(b, s, hkv, g, d, rate=0.7, seed=6801)
+    out = prefill(q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu), window=16).cpu()
+    cache = DmsCache(b, hkv, g, d, torch.float32, max_pages_per_unit=3, device=gpu)
+    for t in range(s):
+        cache.append(k[:, t:t + 1].contiguous().to(gpu), v[:, t:t + 1].contiguous().to(gpu),
+                     logit[:, t:t + 1].contiguous().to(gpu))
+        if t in (0, 15, 16, 63, 64, 119):
+            dec = cache.decode(q[:, t].contiguous().to(gpu)).cpu()
+            assert (dec - out[:, t]).abs().max() <= 2 * F32_ATOL, f"t={t}"
+        if t % 32 == 31:
+            cache.compact()

@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 (matrix and vector), published
 METRIC = "DMS decode-attn tokens/s and KV GB/s (% HBM peak) at CR=8, Qwen3-8B shape"
 # the other decode workloads, each measured by a short step loop of its own:
 # Llama-3.2-1B-shaped heads at CR 4, the Qwen3-8B shape with nothing evicted,
@@ -364,6 +365,34 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10, relaxed: bool = True)
                           "causal_tflops": round(causal / (ms_r * 1e-3) / 1e12, 1),
                           "frac": round(causal / (ms_r * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
     return rec
+
+
+def prefill_f32_leg(name: str = "prefill_8k", iters: int = 3) -> dict:
+    """Masked prefill of the same workload shape with float32 inputs
+    (k_prefill_f32 on v_mfma_f32_16x16x4_f32): causal FLOPs per second against
+    the fp32 peak, for the hard rule and the relaxed mask."""
+    import torch
+
+    import workloads as wl
+    from decode_attention_learned_amd import prefill
+
+    w = dataclasses.replace(wl.get(name), dtype="f32")
+    dev = torch.device("cuda:0")
+    q, k, v, logit = wl.prefill_inputs(w, device=dev)
+    s_len, d = w.context, w.head_dim
+    out = torch.empty((w.batch, s_len, w.q_heads, d), dtype=torch.float32, device=dev)
+    ws = torch.empty((256,), dtype=torch.uint8, device=dev)
+    ms = _time_calls(lambda: prefill(q, k, v, logit, window=w.window, out=out, workspace=ws), iters)
+    noise = wl.logistic_noise(w, device=dev)
+    ms_r = _time_calls(lambda: prefill(q, k, v, logit, window=w.window, out=out, workspace=ws,
+                                       method="relaxed", noise=noise, temperature=1.0), iters)
+    causal = 4.0 * d * s_len * (s_len + 1) / 2 * w.batch * w.q_heads
+    tf, tf_r = causal / (ms * 1e-3) / 1e12, causal / (ms_r * 1e-3) / 1e12
+    return {"workload": name, "dtype": "f32", "batch": w.batch, "seq_len": s_len, "head_dim": d,
+            "ms": round(ms, 3), "relaxed_ms": round(ms_r, 3),
+            "roofline": {"bound": "mfma", "kernel": f"k_prefill_f32<{d}>", "achieved": round(tf, 1),
+                         "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / FP32_PEAK_TFLOPS, 4),
+                         "relaxed_frac": round(tf_r / FP32_PEAK_TFLOPS, 4), "traffic": None}}
 
 
 def chunk_leg(caches, w, dev, n_query: int = 4, rounds: int = 32) -> dict:
@@ -724,6 +753,8 @@ def main():
                     help="only run the copy/read calibration on a buffer of GIB GiB")
     ap.add_argument("--no-prefill", action="store_true", help="skip the masked-prefill leg")
     ap.add_argument("--prefill-only", action="store_true", help="only run the masked-prefill leg")
+    ap.add_argument("--prefill-f32-only", action="store_true",
+                    help="only run the float32 masked-prefill leg")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunk-query leg")
     ap.add_argument("--append-launch", action="store_true",
                     help="time the step as dms_append + dms_decode_attn (the token written by its "
@@ -754,6 +785,9 @@ def main():
         return
     if args.prefill_only:
         print(json.dumps(prefill_leg()), flush=True)
+        return
+    if args.prefill_f32_only:
+        print(json.dumps(prefill_f32_leg()), flush=True)
         return
     if args.chunked_prefill_only:
         print(json.dumps({"chunked_prefill": chunked_prefill_leg(),
@@ -981,6 +1015,11 @@ def main():
         log("[bench] masked prefill, head_dim 64 (Llama-3.2-1B-shaped heads), 4096 tokens")
         with marked("prefill 4k head_dim 64"):
             result["prefill_head_dim_64"] = prefill_leg("prefill_4k_d64", relaxed=False)
+        torch.cuda.empty_cache()
+        with marked("prefill 8k float32"):
+            result["prefill_f32"] = prefill_f32_leg()
+        log(f"[bench] float32 prefill {result['prefill_f32']['ms']:.2f} ms = "
+            f"{result['prefill_f32']['roofline']['achieved']:.0f} TFLOP/s causal")
         torch.cuda.empty_cache()
         with marked("chunked prefill"):
             result["chunked_prefill"] = chunked_prefill_leg()

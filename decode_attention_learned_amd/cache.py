@@ -245,7 +245,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logit: torch.Tens
             method: str = "dense", noise: torch.Tensor | None = None,
             temperature: float = 1.0) -> torch.Tensor:
     """Masked DMS prefill: q [B, S, Hq, D], k, v [B, S, Hkv, D] (bf16, or float32 for the
-    vector kernel), logit [B, S, Hkv] f32.
+    float32 kernel), logit [B, S, Hkv] f32.
 
     method "dense" runs dms_prefill_attn (every causal tile, masked), "gathered"
     runs dms_prefill_attn_gathered (gathered kept keys plus the window band),

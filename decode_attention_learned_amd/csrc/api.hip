@@ -212,7 +212,7 @@ static int check_prefill_shape(const dms_shape *shape, int32_t seq_len) {
     return DMS_EINVAL;
   if (seq_len < 0) return DMS_EINVAL;
   if (shape->head_dim != 128 && shape->head_dim != 64) return DMS_EUNSUPPORTED;
-  if (shape->kv_dtype == DMS_KV_F32) return DMS_OK;  // the vector kernel: any group
+  if (shape->kv_dtype == DMS_KV_F32) return DMS_OK;  // the float32 kernel: any group
   if (shape->kv_dtype != DMS_KV_BF16 || shape->group > 16) return DMS_EUNSUPPORTED;
   return DMS_OK;
 }
@@ -282,7 +282,7 @@ int dms_prefill_attn_gathered(const dms_shape *shape, const void *q, const void 
     return DMS_EINVAL;
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return DMS_EINVAL;
   if (workspace_bytes < dms_prefill_gathered_workspace_bytes(shape, seq_len)) return DMS_EWORKSPACE;
-  // float32: the vector kernel, which skips the tiles no query of a block sees
+  // float32: the float32 kernel, which skips the tiles no query of a block sees
   if (shape->kv_dtype == DMS_KV_F32)
     return from_hip(dms::launch_prefill_f32(*shape, q, k, v, logit, nullptr, 0.f, seq_len, sm_scale,
                                             out, stream));

@@ -1,4 +1,4 @@
-// Masked prefill attention for float32 inputs, on the vector units.
+// Masked prefill attention for float32 inputs, on the gfx950 matrix cores.
 //
 // Method and visibility rule as in prefill.hip: atlas.scime.ai summary of
 // "Inference-Time Hyper-Scaling with KV Cache Compression", section
@@ -10,70 +10,127 @@
 // relaxed (training-form) rule replaces the exclusion by the additive term
 // log(1 - sigmoid((logit_j + noise_j) / tau)) for i - j >= w.
 //
-// The matrix cores of gfx950 take bf16 operands for this contraction at
-// full rate; float32 inputs are kept exact here and take the vector units:
-// products and sums in float32, the softmax in exp2 form with an exact
-// running maximum.
+// Float32 inputs keep float32 products: the contraction runs on
+// v_mfma_f32_16x16x4_f32 (float32 operands and accumulation) with the
+// softmax in float32 exp2 form and an exact running maximum.
 //
-// Work decomposition.  A workgroup of 256 threads takes 32 query rows of one
-// query head.  Key tiles of 32 keys (keys, values and each key's decision or
-// relaxed term) are staged in LDS with the query rows.  Eight consecutive
-// lanes serve one query row: for the scores each takes 4 keys of the tile,
-// for the output D / 8 consecutive dims.  Under the hard rule a tile whose
-// keys are all marked and all at least w behind every query of the block
-// adds nothing and is skipped, so the work follows the visible keys.
+// Work decomposition, as in the bf16 kernel: a workgroup of four waves
+// takes 32 query positions of one KV head, wave w serving query head
+// 4 hg + w of the group; key tiles of 32 are staged once per workgroup in
+// LDS and serve all four heads.  Per tile and wave
+//   S^T [32 keys x 16 queries] = K [32 x D] . Q^T [D x 16]   (x2 query tiles)
+//   O^T [D x 16 queries]      += V^T [D x 32 keys] . P^T [32 x 16]
+// Operand layouts of v_mfma_f32_16x16x4_f32 (lane l, q = l / 16): A holds
+// element (l % 16, q), B element (q, l % 16), the result rows 4q .. 4q + 3 of
+// column l % 16.  The reduction index of the QK product is permuted: k-step
+// ks of lane group q takes dim q * D/4 + ks, so that a lane's key and query
+// dims are consecutive (one 16-byte LDS read feeds four products).  In the
+// PV product k-step i of a 16-key half takes key 4q + i from lane group q:
+// the key whose score that lane already holds, so P needs no lane exchange;
+// values are staged transposed for it.  Under the hard rule a tile whose
+// keys are all marked and out of every query's window is skipped.  The next
+// tile's keys, values and logits are requested before the current one is
+// computed.
 #include "dms_internal.h"
 
 namespace dms {
 
 namespace {
 
-constexpr int FQB = 32;   // query rows per workgroup
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int FQB = 32;   // query positions per workgroup
 constexpr int FKT = 32;   // keys per tile
-constexpr int FNT = 256;  // threads per workgroup (8 per query row)
+constexpr int FHW = 4;    // query heads (waves) per workgroup
+constexpr int FNT = FHW * kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <int D>
-__global__ __launch_bounds__(FNT) void k_prefill_f32(int S, int hkv, int G, int window,
-                                                     float scale_log2, int relaxed, float inv_tau,
-                                                     const float *__restrict__ q,
-                                                     const float *__restrict__ k,
-                                                     const float *__restrict__ v,
-                                                     const float *__restrict__ logit,
-                                                     const float *__restrict__ noise,
-                                                     float *__restrict__ out) {
-  constexpr int D4 = D / 4;   // float4 per row
-  constexpr int RP = D4 + 1;  // padded row (float4), against bank conflicts between rows
-  constexpr int OD4 = D4 / 8; // output float4 per thread
-  const int qb = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
-  const int h = hq / G, Hq = hkv * G;
-  const int i0 = qb * FQB;
+__global__ __launch_bounds__(FNT, 2) void k_prefill_f32(int batch, int S, int hkv, int G, int window,
+                                                        float scale_log2, int relaxed, float inv_tau,
+                                                        const float *__restrict__ q,
+                                                        const float *__restrict__ k,
+                                                        const float *__restrict__ v,
+                                                        const float *__restrict__ logit,
+                                                        const float *__restrict__ noise,
+                                                        float *__restrict__ out) {
+  constexpr int DQ = D / 4;       // dims per lane group; k-steps of a QK product
+  constexpr int DT = D / 16;      // 16-dim blocks of the output
+  constexpr int KR = D + 4;       // sK row (floats): 16-byte rows, rotating banks
+  constexpr int VR = FKT + 4;     // sVt row (floats)
+  constexpr int NPT = FKT * D / 4 / FNT;  // float4 of keys (and of values) each thread stages
+  const int ngh = (G + FHW - 1) / FHW;
+  // Workgroup -> (b, h, hg, query block) as in the bf16 kernel: consecutive
+  // ids go to different XCDs, so all query blocks of one (b, h, hg) get ids of
+  // one residue modulo 8 and share an L2; the latest (longest) blocks first.
+  const int nqb = (S + FQB - 1) / FQB;
+  const int npairs = batch * hkv * ngh;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int pair = (slot / nqb) * 8 + xcd;
+  if (pair >= npairs) return;
+  const int qb = nqb - 1 - slot % nqb;
+  const int b = pair / (hkv * ngh), h = (pair / ngh) % hkv, hg = pair % ngh;
+  const int Hq = hkv * G;
   const int tid = threadIdx.x;
-  const int r = tid >> 3, sub = tid & 7;  // query row in the block, lane within the row
-  const int i = i0 + r;
+  const int wave = tid / kWave, lane = tid % kWave, col = lane & 15, quad = lane >> 4;
+  const int g = hg * FHW + wave;
+  const bool active = g < G;
+  const int hq = h * G + (active ? g : 0);
+  const int i0 = qb * FQB;
   const int i_last = min(S, i0 + FQB) - 1;
 
-  __shared__ float4 sQ[FQB][RP];
-  __shared__ float4 sK[FKT][RP];
-  __shared__ float4 sV[FKT][RP];
-  __shared__ float sP[FQB][FKT + 1];
-  __shared__ float sB[FKT];  // per key: additive term (log2 units) for i - j >= w
+  __shared__ __align__(16) float sK[FKT * KR];   // keys, row-major
+  __shared__ __align__(16) float sVt[D * VR];    // values, transposed: [dim][key]
+  // per key: additive term (log2 units) once i - j >= w; two buffers by tile
+  // parity, since a wave may write the next tile's while another still reads
+  // this one's
+  __shared__ float sB[2][FKT];
 
-  for (int x = tid; x < FQB * D4; x += FNT) {
-    const int rr = x / D4, c = x % D4;
-    const int ii = i0 + rr;
-    sQ[rr][c] = ii < S ? reinterpret_cast<const float4 *>(q + ((size_t(b) * S + ii) * Hq + hq) * D)[c]
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-
-  float4 o[OD4];
+  // Q^T operand of query tile qt: query i0 + 16 qt + col, dims quad * DQ .. + DQ
+  float4 qf[2][DQ / 4];
 #pragma unroll
-  for (int x = 0; x < OD4; ++x) o[x] = make_float4(0.f, 0.f, 0.f, 0.f);
-  float m_run = -INFINITY, l_run = 0.f;  // l_run: this lane's share of the row sum
+  for (int qt = 0; qt < 2; ++qt) {
+    const int i = i0 + 16 * qt + col;
+    const float4 *src = reinterpret_cast<const float4 *>(q + ((size_t(b) * S + i) * Hq + hq) * D + quad * DQ);
+#pragma unroll
+    for (int m = 0; m < DQ / 4; ++m)
+      qf[qt][m] = active && i < S ? src[m] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  floatx4 o[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+  // staging registers: float4 e = tid + x * FNT of the tile is key e / (D/4),
+  // dims 4 (e % (D/4)) .. + 3
+  float4 nk[NPT], nv[NPT];
+  float n_logit = 0.f, n_noise = 0.f;
+  auto fetch = [&](int j0) {
+#pragma unroll
+    for (int x = 0; x < NPT; ++x) {
+      const int e = tid + x * FNT;
+      const int jj = e / (D / 4), c4 = e % (D / 4);
+      const int j = j0 + jj;
+      const size_t row = ((size_t(b) * S + j) * hkv + h) * D;
+      nk[x] = j < S ? reinterpret_cast<const float4 *>(k + row)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      nv[x] = j < S ? reinterpret_cast<const float4 *>(v + row)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (tid < FKT && j0 + tid < S) {
+      const size_t at = (size_t(b) * S + j0 + tid) * hkv + h;
+      n_logit = logit[at];
+      n_noise = relaxed && noise ? noise[at] : 0.f;
+    }
+  };
+  fetch(0);
 
   for (int j0 = 0; j0 <= i_last; j0 += FKT) {
-    // sB is rewritten here: every thread is past the previous tile's scores
-    // (the barrier before its PV product)
+    float *sb = sB[(j0 / FKT) & 1];
     const bool far = j0 + FKT - 1 + window <= i0;  // every key >= w behind every query
     bool live = false;
     if (tid < FKT) {
@@ -81,112 +138,136 @@ __global__ __launch_bounds__(FNT) void k_prefill_f32(int S, int hkv, int G, int 
       float bias = 0.f;
       live = j < S;
       if (j < S) {
-        const size_t at = (size_t(b) * S + j) * hkv + h;
         if (relaxed) {
           // log(1 - sigmoid(x)) = -softplus(x), in log2 units
-          const float x = (logit[at] + (noise ? noise[at] : 0.f)) * inv_tau;
+          const float x = (n_logit + n_noise) * inv_tau;
           bias = -(fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))) * kLog2e;
-        } else if (evict_decision(logit[at])) {
+        } else if (evict_decision(n_logit)) {
           bias = -INFINITY;
           live = !far;
         }
       }
-      sB[tid] = bias;
+      sb[tid] = bias;
     }
-    // hard rule: a tile whose keys are all marked and out of every query's
-    // window is skipped (the barrier also publishes sB and, first time, sQ)
-    if (!__syncthreads_or(live)) continue;
-    for (int x = tid; x < FKT * D4; x += FNT) {
-      const int jj = x / D4, c = x % D4;
-      const int j = j0 + jj;
-      const size_t row = ((size_t(b) * S + j) * hkv + h) * D;
-      sK[jj][c] = j < S ? reinterpret_cast<const float4 *>(k + row)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-      sV[jj][c] = j < S ? reinterpret_cast<const float4 *>(v + row)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    __syncthreads();
-
-    // scores of row r for keys j0 + 4 sub .. + 3
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int c = 0; c < D4; ++c) {
-      const float4 qv = sQ[r][c];
+    // every wave is done with the previous tile; a tile no query sees is skipped
+    const bool any = __syncthreads_or(live);
+    if (any) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float4 kv = sK[4 * sub + e][c];
-        acc[e] = fmaf(qv.x, kv.x, acc[e]);
-        acc[e] = fmaf(qv.y, kv.y, acc[e]);
-        acc[e] = fmaf(qv.z, kv.z, acc[e]);
-        acc[e] = fmaf(qv.w, kv.w, acc[e]);
+      for (int x = 0; x < NPT; ++x) {
+        const int e = tid + x * FNT;
+        const int jj = e / (D / 4), c4 = e % (D / 4);
+        *reinterpret_cast<float4 *>(&sK[jj * KR + 4 * c4]) = nk[x];
+        sVt[(4 * c4 + 0) * VR + jj] = nv[x].x;
+        sVt[(4 * c4 + 1) * VR + jj] = nv[x].y;
+        sVt[(4 * c4 + 2) * VR + jj] = nv[x].z;
+        sVt[(4 * c4 + 3) * VR + jj] = nv[x].w;
       }
     }
-    float s[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int jj = 4 * sub + e, j = j0 + jj;
-      const float add = i - j >= window ? sB[jj] : 0.f;
-      s[e] = (j <= i && i < S) ? fmaf(acc[e], scale_log2, add) : -INFINITY;
-      mx = fmaxf(mx, s[e]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 1, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 2, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 4, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    // corr rescales what was accumulated against m_run; nothing visible yet: 0
-    const float corr = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
-    const float m_sub = m_new == -INFINITY ? 0.f : m_new;
-    float lsum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p = exp2f(s[e] - m_sub);
-      sP[r][4 * sub + e] = p;
-      lsum += p;
-    }
-    l_run = fmaf(l_run, corr, lsum);
-    m_run = m_new;
-    __syncthreads();  // the row's weights are in LDS
+    if (j0 + FKT <= i_last) fetch(j0 + FKT);
+    if (!any) continue;
+    __syncthreads();
+    if (!active) continue;
 
-    // output dims 4 (sub * OD4 + x) .. + 3 of row r
+    // scores: s[qt][t] rows = keys 16 t + 4 quad + r, column = query 16 qt + col
+    floatx4 s[2][2];
 #pragma unroll
-    for (int x = 0; x < OD4; ++x) {
-      o[x].x *= corr;
-      o[x].y *= corr;
-      o[x].z *= corr;
-      o[x].w *= corr;
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s[qt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < DQ / 4; ++m) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float4 ka = *reinterpret_cast<const float4 *>(&sK[(16 * t + col) * KR + quad * DQ + 4 * m]);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          s[qt][t] = mfma4(ka.x, qf[qt][m].x, s[qt][t]);
+          s[qt][t] = mfma4(ka.y, qf[qt][m].y, s[qt][t]);
+          s[qt][t] = mfma4(ka.z, qf[qt][m].z, s[qt][t]);
+          s[qt][t] = mfma4(ka.w, qf[qt][m].w, s[qt][t]);
+        }
+      }
     }
-    for (int jj = 0; jj < FKT; ++jj) {
-      const float p = sP[r][jj];
+    // the rule, then the online softmax per query (exact running maximum)
 #pragma unroll
-      for (int x = 0; x < OD4; ++x) {
-        const float4 vv = sV[jj][sub * OD4 + x];
-        o[x].x = fmaf(p, vv.x, o[x].x);
-        o[x].y = fmaf(p, vv.y, o[x].y);
-        o[x].z = fmaf(p, vv.z, o[x].z);
-        o[x].w = fmaf(p, vv.w, o[x].w);
+    for (int qt = 0; qt < 2; ++qt) {
+      const int i = i0 + 16 * qt + col;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jj = 16 * t + 4 * quad + r, j = j0 + jj;
+          const float add = i - j >= window ? sb[jj] : 0.f;
+          const float x = (j <= i && i < S) ? fmaf(s[qt][t][r], scale_log2, add) : -INFINITY;
+          s[qt][t][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_run[qt], mx);
+      const float corr = m_run[qt] == -INFINITY ? 0.f : exp2f(m_run[qt] - m_new);
+      const float m_sub = m_new == -INFINITY ? 0.f : m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = exp2f(s[qt][t][r] - m_sub);
+          s[qt][t][r] = p;
+          lsum += p;
+        }
+      l_run[qt] = fmaf(l_run[qt], corr, lsum);
+      m_run[qt] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= corr;
+    }
+    // PV: k-step i of half t takes key 16 t + 4 quad + i (this lane's weight s[qt][t][i])
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float4 va = *reinterpret_cast<const float4 *>(&sVt[(16 * dt + col) * VR + 16 * t + 4 * quad]);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          o[dt][qt] = mfma4(va.x, s[qt][t][0], o[dt][qt]);
+          o[dt][qt] = mfma4(va.y, s[qt][t][1], o[dt][qt]);
+          o[dt][qt] = mfma4(va.z, s[qt][t][2], o[dt][qt]);
+          o[dt][qt] = mfma4(va.w, s[qt][t][3], o[dt][qt]);
+        }
       }
     }
   }
-  float l = l_run;
-  l += __shfl_xor(l, 1, kWave);
-  l += __shfl_xor(l, 2, kWave);
-  l += __shfl_xor(l, 4, kWave);
-  if (i >= S) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  float4 *dst = reinterpret_cast<float4 *>(out + ((size_t(b) * S + i) * Hq + hq) * D) + sub * OD4;
+  if (!active) return;
+  // o[dt][qt][r]: query 16 qt + col, dim 16 dt + 4 quad + r
 #pragma unroll
-  for (int x = 0; x < OD4; ++x)
-    dst[x] = make_float4(o[x].x * inv, o[x].y * inv, o[x].z * inv, o[x].w * inv);
+  for (int qt = 0; qt < 2; ++qt) {
+    float l = l_run[qt];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const int i = i0 + 16 * qt + col;
+    if (i >= S) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float *dst = out + ((size_t(b) * S + i) * Hq + hq) * D + 4 * quad;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const floatx4 x = o[dt][qt] * inv;
+      *reinterpret_cast<float4 *>(dst + 16 * dt) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+  }
 }
 
 template <int D>
 hipError_t launch_t(const dms_shape &s, const float *q, const float *k, const float *v,
                     const float *logit, const float *noise, float temperature, int seq_len,
                     float sm_scale, float *out, hipStream_t st) {
-  const int hq = s.kv_heads * s.group;
-  if (hq > 65535 || s.batch > 65535) return hipErrorInvalidValue;  // grid y, z
-  const dim3 grid((seq_len + FQB - 1) / FQB, hq, s.batch);
+  const long pairs = long(s.batch) * s.kv_heads * ((s.group + FHW - 1) / FHW);
+  const long nqb = (seq_len + FQB - 1) / FQB;
+  const long blocks = (pairs + 7) / 8 * nqb * 8;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
   const int relaxed = temperature > 0.f;
-  hipLaunchKernelGGL(k_prefill_f32<D>, grid, dim3(FNT), 0, st, seq_len, s.kv_heads, s.group,
+  hipLaunchKernelGGL(k_prefill_f32<D>, dim3(unsigned(blocks)), dim3(FNT), 0, st, s.batch, seq_len,
+                     s.kv_heads, s.group,
                      s.window, sm_scale * kLog2e, relaxed, relaxed ? 1.f / temperature : 0.f, q, k, v,
                      logit, noise, out);
   return hipGetLastError();

@@ -355,8 +355,8 @@ int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const 
  * keys and values re-laid out per 32-key tile for the matrix cores, one float
  * per key (its decision as an additive mask), and the re-laid keys and values
  * again with every key masked out under the hard rule zeroed (read where all
- * of a tile's keys are at least w behind every query).  float32: 256 (the
- * vector kernel uses none).  0 if the arguments are invalid.
+ * of a tile's keys are at least w behind every query).  float32: 256 (its
+ * kernel uses none).  0 if the arguments are invalid.
  */
 size_t dms_prefill_workspace_bytes(const dms_shape *shape, int32_t seq_len);
 
@@ -374,9 +374,10 @@ size_t dms_prefill_workspace_bytes(const dms_shape *shape, int32_t seq_len);
  *              aligned, no initialisation needed, nothing kept after the call
  * Only batch, kv_heads, group, head_dim (64 or 128), window and kv_dtype of
  * `shape` are read.  bf16 inputs run on the matrix cores (group <= 16);
- * float32 inputs run a vector kernel with float32 products (any group), the
- * same kernel for all three prefill calls, skipping tiles no query of a
- * block sees.  The cache is filled separately with dms_append.
+ * float32 inputs run a kernel of their own on the float32 matrix
+ * instruction (float32 operands, any group), the same kernel for all three
+ * prefill calls, skipping tiles no query of a block sees.  The cache is
+ * filled separately with dms_append.
  */
 int dms_prefill_attn(const dms_shape *shape, const void *q, const void *k, const void *v,
                      const float *logit, int32_t seq_len, float sm_scale, float *out,

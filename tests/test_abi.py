@@ -185,7 +185,7 @@ def test_prefill_host_errors(L):
     f32 = _shape()
     bf = _shape(kv_dtype=lib.DMS_KV_BF16, head_dim=128)
     big = 1 << 40
-    # float32 inputs are served (the vector kernel, no workspace used, 256 bytes asked
+    # float32 inputs are served (their own kernel, no workspace used, 256 bytes asked
     # for); a head dimension other than 64 or 128 is not
     f32_d96 = _shape(head_dim=96)
     assert L.dms_prefill_attn(ctypes.byref(f32_d96), fake, fake, fake, fake, 16, 0.1, fake, fake, big,

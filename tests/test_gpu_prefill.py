@@ -305,8 +305,8 @@ def test_prefill_llama1b_shape_sampled_rows(gpu, method):
 
 
 # ------------------------------------------------------------- float32 inputs
-# Float32 inputs run the vector kernel for all three methods; the tolerance is
-# the float32 one, max |o - o_ref| <= 1e-5 (inputs exact in float64).
+# Float32 inputs run the float32 matrix-core kernel for all three methods; the
+# tolerance is the float32 one, max |o - o_ref| <= 1e-5 (inputs exact in float64).
 F32_ATOL = 1e-5
 
 

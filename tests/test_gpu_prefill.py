@@ -394,3 +394,21 @@ def test_prefill_f32_matches_f32_decode(gpu):
             assert (dec - out[:, t]).abs().max() <= 2 * F32_ATOL, f"t={t}"
         if t % 32 == 31:
             cache.compact()
+
+
+def test_prefill_f32_8k_sampled_rows(gpu):
+    """The 8K prefill shape (B=4, S=8192, 32/8 heads, D=128, CR 8) with float32
+    inputs, in the launch configuration the bench times: rows [0, 256) and
+    [7936, 8192) of every sequence and head against the oracle at 1e-5."""
+    import dataclasses
+
+    w = dataclasses.replace(wl.get("prefill_8k"), dtype="f32")
+    q, k, v, logit = wl.prefill_inputs(w, device=gpu)
+    assert q.dtype == torch.float32
+    out = prefill(q, k, v, logit, window=16)
+    rows = np.concatenate([np.arange(0, 256), np.arange(7936, 8192)])
+    out_rows = out[:, torch.as_tensor(rows, device=gpu)].cpu()
+    full = torch.zeros((w.batch, w.context, w.q_heads, 128), dtype=torch.float32)
+    full[:, torch.as_tensor(rows)] = out_rows
+    worst = _check_rows_f32(full, q.cpu(), k.cpu(), v.cpu(), logit.cpu(), rows, 16, what="f32 8k")
+    say(f"prefill f32 8k: max err {worst:.2e}")

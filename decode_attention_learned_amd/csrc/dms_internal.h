@@ -26,6 +26,11 @@ constexpr int kWave = 64;              // CDNA wavefront width
 #endif
 constexpr int kTargetChunks = DMS_TARGET_CHUNKS;
 constexpr int kRaggedRounds = 3;
+// Even lengths are not split into chunks shorter than this many slots: below
+// it the split's extra workgroups and merge cost more than the parallelism
+// gains (Llama-3.2-1B-shaped heads, 128 units of ~1100 slots: 25.2 -> 23.3 us
+// per decode step unsplit).  A multiple of the page size.
+constexpr int kMinEvenChunk = 2048;
 
 // The largest chunk count of a plan for `units` units.  build_plan gives one
 // chunk per unit when units >= its budget (kTargetChunks, or kRaggedRounds *
@@ -240,7 +245,8 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 // unit holds more than twice the mean (max_u n_u > 2 * total / units), else 1:
 //   units >= budget:  C = 64 * ceil(max_u n_u / 64)   (one chunk per unit)
 //   otherwise:        C = 64 * max(1, ceil(total / (64 * (budget - units))))
-// so that sum_u chunks(u) <= total / C + units <= budget.
+// so that sum_u chunks(u) <= total / C + units <= budget; for even lengths C
+// is at least kMinEvenChunk (fewer chunks still).
 constexpr int kPlanThreads = 1024;
 
 // `count(u)` returns n_slots of unit u.
@@ -285,7 +291,7 @@ __device__ inline void build_plan(int units, Count count, int32_t *plan) {
     const long long room = (long long)kPage * (budget - units);
     per = (total + room - 1) / room;
   }
-  const int C = kPage * int(per < 1 ? 1 : per);
+  const int C = max(ragged ? kPage : kMinEvenChunk, kPage * int(per < 1 ? 1 : per));
   int carry = 0;
   for (int base = 0; base < units; base += kPlanThreads) {
     const int u = base + threadIdx.x;

@@ -438,13 +438,13 @@ def _check_units(out, q, k, v, lg, units, hkv):
 
 def test_split_plan_even_units_fill_one_round(gpu):
     """512 units of equal length: one chunk per unit (no merge); 128 units of equal
-    length: split to at most one round of 512 workgroups.  Outputs against the oracle
-    on sampled units."""
+    length (6000 slots): split to at most one round of 512 workgroups, chunks of at
+    least 2048 slots.  Outputs against the oracle on sampled units."""
     cache, q, k, v, lg = _plan_case(64, 8, 300, lambda u: -1.0, gpu, 91)
     count, _, _ = _check_plan(cache, 512)
     assert count == 512
     _check_units(cache.decode(q.to(gpu)).cpu(), q, k, v, lg, range(0, 512, 37), 8)
-    cache, q, k, v, lg = _plan_case(16, 8, 2000, lambda u: -1.0, gpu, 92)
+    cache, q, k, v, lg = _plan_case(16, 8, 6000, lambda u: -1.0, gpu, 92)
     count, _, _ = _check_plan(cache, 512)
     assert 128 < count <= 512
     _check_units(cache.decode(q.to(gpu)).cpu(), q, k, v, lg, range(0, 128, 11), 8)

@@ -2,8 +2,9 @@
 decode grid are sized for (CPU only).
 
 The chunk-size rule is restated here from its description in the library
-(units of even length: one round of 512 chunks; ragged lengths, the longest
-above twice the mean: up to three rounds; at least one chunk per unit), and
+(units of even length: one round of 512 chunks, none shorter than 2048 slots;
+ragged lengths, the longest above twice the mean: up to three rounds; at least
+one chunk per unit), and
 the capacity is read from the library itself: dms_plan_words(shape) =
 16 + (units + 1) + max_chunks + 2 * units.  Ragged length mixes between 513
 and 1535 units are the case the capacity once missed."""
@@ -20,13 +21,14 @@ def plan_chunks(n):
     """Chunks of a plan for per-unit slot counts n (the rule stated above)."""
     n = np.asarray(n, dtype=np.int64)
     units, total, mx = n.size, int(n.sum()), int(n.max())
-    budget = (ROUNDS if mx * units > 2 * total else 1) * TARGET
+    ragged = mx * units > 2 * total
+    budget = (ROUNDS if ragged else 1) * TARGET
     if units >= budget:
         per = -(-mx // PAGE)
     else:
         room = PAGE * (budget - units)
         per = -(-total // room)
-    C = PAGE * max(1, per)
+    C = max(PAGE if ragged else 2048, PAGE * max(1, per))
     return int(np.where(n > 0, -(-n // C), 1).sum())
 
 

@@ -65,7 +65,9 @@ def _oracle(q, k, v, lg, hkv, g, d):
 
 @pytest.mark.gpu
 def test_noalloc_decode_equals_decode_twice_then_smaller(gpu):
-    cases = [(8, 8, 4, 128, 3000, 9701), (2, 4, 5, 64, 1000, 9702)]   # 64 units, then 8
+    # 64 units, then 8, each long enough (about 4800 and 2400 retained slots) that the
+    # plan splits even lengths (chunks of at least 2048 slots)
+    cases = [(8, 8, 4, 128, 12000, 9701), (2, 4, 5, 64, 6000, 9702)]
     built = [_case(gpu, *c) for c in cases]
     for (cache, q, k, v, lg), (b, hkv, g, d, _, _) in zip(built + built[:1], cases + cases[:1]):
         assert int(cache.plan[0].item()) > cache.units, "expected split units (merge path)"

@@ -283,10 +283,11 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
   return launch_merge(s, c, w, ws, out, s.group, 0, 1, st);
 }
 
-// Queries of a chunk of n_query tokens just appended.  bf16 caches: long
-// chunks (32 queries or more) run the tiled chunk kernel, one pass over the
-// cache per 32 queries; shorter ones run the split-K decode kernel in
-// launches of at most 16 / G queries.  float32 caches: the vector kernel, one
+// Queries of a chunk of n_query tokens just appended.  Long chunks (32
+// queries or more) run a tiled chunk kernel, one pass over the cache per 32
+// queries (bf16: matrix cores in bf16; float32: the float32 matrix
+// instruction).  Shorter ones: bf16 caches run the split-K decode kernel in
+// launches of at most 16 / G queries, float32 caches the vector kernel, one
 // launch per query position.  The workspace holds partials for 16 columns.
 constexpr int kChunkKernelMin = 32;
 
@@ -294,6 +295,8 @@ hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const voi
                                float *out, float sm_scale, void *wsv, size_t ws_bytes, hipStream_t st) {
   const DecodeWorkspace w = decode_workspace_layout(units_of(s), 16, s.head_dim);
   const float scale_log2 = sm_scale * 1.4426950408889634f;
+  if (s.kv_dtype == DMS_KV_F32 && n_query >= kChunkKernelMin)
+    return launch_chunk_f32(s, c, q, n_query, out, sm_scale, st);
   if (s.kv_dtype == DMS_KV_F32) {
     char *ws = static_cast<char *>(wsv);
     const uint32_t *q32 = static_cast<const uint32_t *>(q);

@@ -161,6 +161,9 @@ hipError_t launch_merge(const dms_shape &s, const dms_cache &c, const DecodeWork
 hipError_t launch_prefill(const dms_shape &s, const void *q, const void *k, const void *v,
                           const float *logit, const float *noise, float temperature, int seq_len,
                           float sm_scale, float *out, void *ws, hipStream_t st);
+// float32 caches, chunks of 32 queries or more (prefill_f32.hip); no workspace
+hipError_t launch_chunk_f32(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
+                            float *out, float sm_scale, hipStream_t st);
 // float32 inputs, every prefill method (prefill_f32.hip); no workspace
 hipError_t launch_prefill_f32(const dms_shape &s, const void *q, const void *k, const void *v,
                               const float *logit, const float *noise, float temperature,

@@ -273,6 +273,221 @@ hipError_t launch_t(const dms_shape &s, const float *q, const float *k, const fl
   return hipGetLastError();
 }
 
+// Chunk queries over a float32 cache (the last C appended tokens of every
+// sequence, each at its own position; the rule of dms_decode_attn_multi):
+// the products above, with key tiles of 32 slots (half a page) staged from
+// the page layout, whose runs of 8 consecutive dims of a key and of 8
+// consecutive slots of a value dim land as they are in the row-major keys
+// and the transposed values in LDS.  Slots below n_clean are seen by every
+// query; above it slot j is seen by position t iff it is in use, pos_j <= t,
+// and it is unmarked or t - pos_j < w.  Slots past n_slots in the last tile
+// (a recycled page may hold anything there) are staged as zeros.  Grid
+// (ceil(C / 32), units * ceil(G / 4)); a sequence shorter than the chunk, or
+// compacted after the chunk's first position, is flagged
+// DMS_STATUS_CHUNK_INVALID.
+template <int D>
+__global__ __launch_bounds__(FNT, 2) void k_chunk_f32(
+    int hkv, int G, int window, int maxp, int C, float scale_log2, const float *__restrict__ q,
+    const float *__restrict__ k_pages, const float *__restrict__ v_pages,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ slot_pos,
+    const uint8_t *__restrict__ slot_alpha, const int32_t *__restrict__ n_slots,
+    const int32_t *__restrict__ n_clean, const int32_t *__restrict__ seq_len,
+    const int32_t *__restrict__ compact_pos, uint32_t *__restrict__ status,
+    float *__restrict__ out) {
+  constexpr int DQ = D / 4, DT = D / 16, KR = D + 4, VR = FKT + 4;
+  constexpr int NRUN = FKT * D / 8 / FNT;  // 8-element runs of keys (and of values) per thread
+  const int ngh = (G + FHW - 1) / FHW;
+  const int u = blockIdx.y / ngh, hg = blockIdx.y % ngh;
+  const int b = u / hkv, h = u % hkv;
+  const int Hq = hkv * G;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave, col = lane & 15, quad = lane >> 4;
+  const int g = hg * FHW + wave;
+  const bool active = g < G;
+  const int hq = h * G + (active ? g : 0);
+  const int c0 = blockIdx.x * FQB;             // first chunk query of the workgroup
+  const int t_first = seq_len[b] - C + c0;     // its position
+  const int ns = n_slots[u], nc = n_clean[u];
+  const int32_t *row = page_table + size_t(u) * maxp;
+  // the chunk's tokens are the unit's last C slots, so query c0 + 31 sits in
+  // slot ns - C + c0 + 31 and later slots are hidden from the workgroup
+  const int last_slot = ns - C + min(c0 + FQB - 1, C - 1);
+  const int nt = last_slot < 0 ? 0 : min((ns + FKT - 1) / FKT, last_slot / FKT + 1);
+  if (blockIdx.x == 0 && hg == 0 && tid == 0) {
+    const int p0 = seq_len[b] - C;  // the chunk's first position
+    if (p0 < 0 || compact_pos[u] > p0) atomicOr(status, DMS_STATUS_CHUNK_INVALID);
+  }
+
+  __shared__ __align__(16) float sK[FKT * KR];
+  __shared__ __align__(16) float sVt[D * VR];
+  __shared__ int sPos[FKT];
+  __shared__ int sMark[FKT];
+
+  float4 qf[2][DQ / 4];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int cq = c0 + 16 * qt + col;
+    const float4 *src =
+        reinterpret_cast<const float4 *>(q + ((size_t(b) * C + cq) * Hq + hq) * D + quad * DQ);
+#pragma unroll
+    for (int m = 0; m < DQ / 4; ++m)
+      qf[qt][m] = active && cq < C ? src[m] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  floatx4 o[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+  // staging registers: run e = tid + x * FNT of the tile is, for keys, slot
+  // e / (D/8) dims 8 (e % (D/8)) .. + 7, and for values, dim e / 4 slots
+  // 8 (e % 4) .. + 7
+  float4 nk[NRUN][2], nv[NRUN][2];
+  int n_pos = 0, n_mark = 0;
+  auto fetch = [&](int t) {
+    const int page = row[t >> 1];
+    const int j0 = (t & 1) * FKT;           // first slot of the tile within its page
+    const size_t pbase = size_t(page) * kPage * D;
+    const int valid = ns - t * FKT;          // slots in use in this tile (>= 1)
+#pragma unroll
+    for (int x = 0; x < NRUN; ++x) {
+      const int e = tid + x * FNT;
+      const int js = e / (D / 8), c8 = e % (D / 8);
+      const float4 *kp = reinterpret_cast<const float4 *>(k_pages + pbase + key_index(j0 + js, 8 * c8, D));
+      const bool used = js < valid;
+      nk[x][0] = used ? kp[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+      nk[x][1] = used ? kp[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int d = e / 4, r8 = e % 4;
+      const float4 *vp = reinterpret_cast<const float4 *>(v_pages + pbase + value_index(j0 + 8 * r8, d, D));
+      float4 a = vp[0], bb = vp[1];
+      const int s0 = 8 * r8;                 // slots s0 .. s0 + 7 of the tile
+      a.x = s0 + 0 < valid ? a.x : 0.f;
+      a.y = s0 + 1 < valid ? a.y : 0.f;
+      a.z = s0 + 2 < valid ? a.z : 0.f;
+      a.w = s0 + 3 < valid ? a.w : 0.f;
+      bb.x = s0 + 4 < valid ? bb.x : 0.f;
+      bb.y = s0 + 5 < valid ? bb.y : 0.f;
+      bb.z = s0 + 6 < valid ? bb.z : 0.f;
+      bb.w = s0 + 7 < valid ? bb.w : 0.f;
+      nv[x][0] = a;
+      nv[x][1] = bb;
+    }
+    if (tid < FKT) {
+      n_pos = slot_pos[size_t(page) * kPage + j0 + tid];
+      n_mark = slot_alpha[size_t(page) * kPage + j0 + tid];
+    }
+  };
+  if (nt > 0) fetch(0);
+
+  for (int t = 0; t < nt; ++t) {
+    __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+    for (int x = 0; x < NRUN; ++x) {
+      const int e = tid + x * FNT;
+      const int js = e / (D / 8), c8 = e % (D / 8);
+      *reinterpret_cast<float4 *>(&sK[js * KR + 8 * c8]) = nk[x][0];
+      *reinterpret_cast<float4 *>(&sK[js * KR + 8 * c8 + 4]) = nk[x][1];
+      const int d = e / 4, r8 = e % 4;
+      *reinterpret_cast<float4 *>(&sVt[d * VR + 8 * r8]) = nv[x][0];
+      *reinterpret_cast<float4 *>(&sVt[d * VR + 8 * r8 + 4]) = nv[x][1];
+    }
+    if (tid < FKT) {
+      sPos[tid] = n_pos;
+      sMark[tid] = n_mark;
+    }
+    if (t + 1 < nt) fetch(t + 1);
+    __syncthreads();
+    if (!active) continue;
+
+    floatx4 s[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) s[qt][t2] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < DQ / 4; ++m) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const float4 ka = *reinterpret_cast<const float4 *>(&sK[(16 * t2 + col) * KR + quad * DQ + 4 * m]);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          s[qt][t2] = mfma4(ka.x, qf[qt][m].x, s[qt][t2]);
+          s[qt][t2] = mfma4(ka.y, qf[qt][m].y, s[qt][t2]);
+          s[qt][t2] = mfma4(ka.z, qf[qt][m].z, s[qt][t2]);
+          s[qt][t2] = mfma4(ka.w, qf[qt][m].w, s[qt][t2]);
+        }
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int cq = c0 + 16 * qt + col;
+      const int tq = t_first + 16 * qt + col;  // this column's position
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int js = 16 * t2 + 4 * quad + r, slot = t * FKT + js;
+          const int pos = sPos[js];
+          const bool live = (cq < C) & (slot < ns) &
+                            ((slot < nc) | ((pos <= tq) & ((sMark[js] == 0) | (tq - pos < window))));
+          const float x = live ? s[qt][t2][r] * scale_log2 : -INFINITY;
+          s[qt][t2][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_run[qt], mx);
+      const float corr = m_run[qt] == -INFINITY ? 0.f : exp2f(m_run[qt] - m_new);
+      const float m_sub = m_new == -INFINITY ? 0.f : m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = exp2f(s[qt][t2][r] - m_sub);
+          s[qt][t2][r] = p;
+          lsum += p;
+        }
+      l_run[qt] = fmaf(l_run[qt], corr, lsum);
+      m_run[qt] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= corr;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const float4 va = *reinterpret_cast<const float4 *>(&sVt[(16 * dt + col) * VR + 16 * t2 + 4 * quad]);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          o[dt][qt] = mfma4(va.x, s[qt][t2][0], o[dt][qt]);
+          o[dt][qt] = mfma4(va.y, s[qt][t2][1], o[dt][qt]);
+          o[dt][qt] = mfma4(va.z, s[qt][t2][2], o[dt][qt]);
+          o[dt][qt] = mfma4(va.w, s[qt][t2][3], o[dt][qt]);
+        }
+      }
+    }
+  }
+  if (!active) return;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float l = l_run[qt];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const int cq = c0 + 16 * qt + col;
+    if (cq >= C) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float *dst = out + ((size_t(b) * C + cq) * Hq + hq) * D + 4 * quad;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const floatx4 x = o[dt][qt] * inv;
+      *reinterpret_cast<float4 *>(dst + 16 * dt) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill_f32(const dms_shape &s, const void *q, const void *k, const void *v,
@@ -285,6 +500,24 @@ hipError_t launch_prefill_f32(const dms_shape &s, const void *q, const void *k, 
   if (s.head_dim == 64)
     return launch_t<64>(s, qf, kf, vf, logit, noise, temperature, seq_len, sm_scale, out, st);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_f32(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
+                            float *out, float sm_scale, hipStream_t st) {
+  const long gy = long(s.batch) * s.kv_heads * ((s.group + FHW - 1) / FHW);
+  if (gy > 65535) return hipErrorInvalidValue;  // grid y
+  const dim3 grid(unsigned((n_query + FQB - 1) / FQB), unsigned(gy));
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(FNT), 0, st, s.kv_heads, s.group, s.window,
+                       s.max_pages_per_unit, n_query, sm_scale * kLog2e, static_cast<const float *>(q),
+                       static_cast<const float *>(c.k_pages), static_cast<const float *>(c.v_pages),
+                       c.page_table, c.slot_pos, c.slot_alpha, c.n_slots, c.n_clean, c.seq_len,
+                       c.plan + plan_layout(units_of(s)).compact_pos, c.status, out);
+  };
+  if (s.head_dim == 128) go(k_chunk_f32<128>);
+  else if (s.head_dim == 64) go(k_chunk_f32<64>);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace dms

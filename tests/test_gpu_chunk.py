@@ -298,3 +298,62 @@ def test_chunk_split_and_one_pass_agree(gpu, zero_q):
                 bound = 1e-5 if zero_q else BF16_TOL["atol"] + BF16_TOL["rtol"] * np.abs(ref)
                 assert np.all(err <= bound), (h, c, float(err.max()))
     say(f"chunk split vs one pass (zero q {zero_q}): max gap {gap:.2e}; vs oracle {worst:.2e}")
+
+
+@pytest.mark.parametrize("chunks,d,g", [([32, 70], 128, 5), ([100], 64, 16), ([40, 33], 64, 2)])
+def test_chunk_queries_float32_tiled(gpu, chunks, d, g):
+    """float32 caches, chunks of 32 queries or more: the tiled kernel on the
+    float32 matrix instruction, every query against the oracle at the float32
+    tolerance (1e-5 max abs), with compaction between chunks.  Every page
+    starts as NaN, so the slots past n_slots of a unit's last page are NaN
+    and must not reach any output."""
+    from harness import F32_ATOL
+    b, hkv, prompt, window = 2, 2, 500, 16
+    total = prompt + sum(chunks)
+    w = wl.Workload(name="chunk_f32_tiled", kind="prefill", batch=b, kv_heads=hkv, group=g, head_dim=d,
+                    dtype="f32", context=total, evict_rate=0.6, seed=7700 + d + g)
+    q, k, v, logit = wl.prefill_inputs(w)
+    cache = DmsCache(b, hkv, g, d, torch.float32, max_pages_per_unit=(total + 63) // 64 + 1,
+                     window=window, device=gpu)
+    cache.k_pages.fill_(float("nan"))
+    cache.v_pages.fill_(float("nan"))
+    cache.append(k[:, :prompt].contiguous().to(gpu), v[:, :prompt].contiguous().to(gpu),
+                 logit[:, :prompt].contiguous().to(gpu))
+    cache.compact()
+    alpha = orc.eviction_decisions(logit.numpy())
+    scale = 1.0 / math.sqrt(d)
+    t0, worst = prompt, 0.0
+    for n in chunks:
+        sl = slice(t0, t0 + n)
+        cache.append(k[:, sl].contiguous().to(gpu), v[:, sl].contiguous().to(gpu),
+                     logit[:, sl].contiguous().to(gpu))
+        out = cache.decode_chunk(q[:, sl].contiguous().to(gpu)).cpu().double().numpy()
+        assert cache.status_word() == 0
+        assert np.isfinite(out).all()
+        for bi in range(b):
+            for h in range(hkv):
+                kh, vh = k[bi, :, h].double().numpy(), v[bi, :, h].double().numpy()
+                for c in range(n):
+                    ref = orc.decode_output(q[bi, t0 + c, h * g:(h + 1) * g].double().numpy(), kh, vh,
+                                            alpha[bi, :, h], t0 + c, window, scale)
+                    err = np.abs(out[bi, c, h * g:(h + 1) * g] - ref).max()
+                    worst = max(worst, float(err))
+                    assert err <= F32_ATOL, f"chunk at {t0}, seq {bi}, query {c}, head {h}: {err:.3g}"
+        cache.compact()
+        t0 += n
+    say(f"float32 tiled chunk queries {chunks} D={d} G={g}: max abs err {worst:.2e}")
+
+
+def test_float32_long_chunk_compacted_after_append_is_flagged(gpu):
+    """The tiled float32 kernel flags a chunk compacted after its append, as the
+    vector path does."""
+    from decode_attention_learned_amd import lib
+    w = wl.Workload(name="chunk_f32_flag_long", kind="prefill", batch=1, kv_heads=2, group=2, head_dim=64,
+                    dtype="f32", context=200, evict_rate=0.8, seed=7602)
+    q, k, v, logit = wl.prefill_inputs(w)
+    cache = DmsCache(1, 2, 2, 64, torch.float32, max_pages_per_unit=5, device=gpu)
+    cache.append(k.to(gpu), v.to(gpu), logit.to(gpu))
+    cache.compact()
+    cache.decode_chunk(q[:, 150:].contiguous().to(gpu))
+    torch.cuda.synchronize()
+    assert cache.status_word() == lib.DMS_STATUS_CHUNK_INVALID

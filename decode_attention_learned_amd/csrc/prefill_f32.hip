@@ -49,6 +49,111 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// QK product of one staged tile for both query tiles: s[qt][t][r] is the
+// score of key 16 t + 4 quad + r for query 16 qt + col (raw units).  sK holds
+// the tile's keys row-major, rows of D + 4 floats; qf the Q^T operand.
+template <int D>
+__device__ __forceinline__ void f32_scores(const float *sK, const float4 (&qf)[2][D / 16], int col,
+                                           int quad, floatx4 (&s)[2][2]) {
+  constexpr int DQ = D / 4, KR = D + 4;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) s[qt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < DQ / 4; ++m) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float4 ka = *reinterpret_cast<const float4 *>(&sK[(16 * t + col) * KR + quad * DQ + 4 * m]);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        s[qt][t] = mfma4(ka.x, qf[qt][m].x, s[qt][t]);
+        s[qt][t] = mfma4(ka.y, qf[qt][m].y, s[qt][t]);
+        s[qt][t] = mfma4(ka.z, qf[qt][m].z, s[qt][t]);
+        s[qt][t] = mfma4(ka.w, qf[qt][m].w, s[qt][t]);
+      }
+    }
+  }
+}
+
+// Online softmax over one tile: s holds each pair's score in log2 units (or
+// -inf where the key is hidden from the query) and becomes the weights p;
+// the running maximum is exact, and the accumulators are rescaled when it
+// moves.  l_run is this lane's share of the row sum.
+template <int D>
+__device__ __forceinline__ void f32_softmax(floatx4 (&s)[2][2], float (&m_run)[2], float (&l_run)[2],
+                                            floatx4 (&o)[D / 16][2]) {
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[qt][t][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run[qt], mx);
+    const float corr = m_run[qt] == -INFINITY ? 0.f : exp2f(m_run[qt] - m_new);
+    const float m_sub = m_new == -INFINITY ? 0.f : m_new;
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp2f(s[qt][t][r] - m_sub);
+        s[qt][t][r] = p;
+        lsum += p;
+      }
+    l_run[qt] = fmaf(l_run[qt], corr, lsum);
+    m_run[qt] = m_new;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[dt][qt] *= corr;
+  }
+}
+
+// PV product of one staged tile: k-step i of half t takes key 16 t + 4 quad
+// + i, whose weight this lane holds in p[qt][t][i].  sVt holds the tile's
+// values transposed, rows of 32 + 4 floats.
+template <int D>
+__device__ __forceinline__ void f32_pv(const float *sVt, const floatx4 (&p)[2][2], int col, int quad,
+                                       floatx4 (&o)[D / 16][2]) {
+  constexpr int VR = 32 + 4;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float4 va = *reinterpret_cast<const float4 *>(&sVt[(16 * dt + col) * VR + 16 * t + 4 * quad]);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        o[dt][qt] = mfma4(va.x, p[qt][t][0], o[dt][qt]);
+        o[dt][qt] = mfma4(va.y, p[qt][t][1], o[dt][qt]);
+        o[dt][qt] = mfma4(va.z, p[qt][t][2], o[dt][qt]);
+        o[dt][qt] = mfma4(va.w, p[qt][t][3], o[dt][qt]);
+      }
+    }
+  }
+}
+
+// Normalised output of query tile qt to row dst[qt] (null: not a query):
+// o[dt][qt][r] is dim 16 dt + 4 quad + r of query 16 qt + col.
+template <int D>
+__device__ __forceinline__ void f32_store(const floatx4 (&o)[D / 16][2], const float (&l_run)[2],
+                                          float *const (&dst)[2], int quad) {
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float l = l_run[qt];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (dst[qt] == nullptr) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const floatx4 x = o[dt][qt] * inv;
+      *reinterpret_cast<float4 *>(dst[qt] + 16 * dt + 4 * quad) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(FNT, 2) void k_prefill_f32(int batch, int S, int hkv, int G, int window,
                                                         float scale_log2, int relaxed, float inv_tau,
@@ -168,93 +273,29 @@ __global__ __launch_bounds__(FNT, 2) void k_prefill_f32(int batch, int S, int hk
     __syncthreads();
     if (!active) continue;
 
-    // scores: s[qt][t] rows = keys 16 t + 4 quad + r, column = query 16 qt + col
     floatx4 s[2][2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) s[qt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < DQ / 4; ++m) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const float4 ka = *reinterpret_cast<const float4 *>(&sK[(16 * t + col) * KR + quad * DQ + 4 * m]);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          s[qt][t] = mfma4(ka.x, qf[qt][m].x, s[qt][t]);
-          s[qt][t] = mfma4(ka.y, qf[qt][m].y, s[qt][t]);
-          s[qt][t] = mfma4(ka.z, qf[qt][m].z, s[qt][t]);
-          s[qt][t] = mfma4(ka.w, qf[qt][m].w, s[qt][t]);
-        }
-      }
-    }
-    // the rule, then the online softmax per query (exact running maximum)
+    f32_scores<D>(sK, qf, col, quad, s);
+    // the rule: causal, and the key's term once it is w or more behind the query
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const int i = i0 + 16 * qt + col;
-      float mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int jj = 16 * t + 4 * quad + r, j = j0 + jj;
           const float add = i - j >= window ? sb[jj] : 0.f;
-          const float x = (j <= i && i < S) ? fmaf(s[qt][t][r], scale_log2, add) : -INFINITY;
-          s[qt][t][r] = x;
-          mx = fmaxf(mx, x);
+          s[qt][t][r] = (j <= i && i < S) ? fmaf(s[qt][t][r], scale_log2, add) : -INFINITY;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run[qt], mx);
-      const float corr = m_run[qt] == -INFINITY ? 0.f : exp2f(m_run[qt] - m_new);
-      const float m_sub = m_new == -INFINITY ? 0.f : m_new;
-      float lsum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(s[qt][t][r] - m_sub);
-          s[qt][t][r] = p;
-          lsum += p;
-        }
-      l_run[qt] = fmaf(l_run[qt], corr, lsum);
-      m_run[qt] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= corr;
     }
-    // PV: k-step i of half t takes key 16 t + 4 quad + i (this lane's weight s[qt][t][i])
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const float4 va = *reinterpret_cast<const float4 *>(&sVt[(16 * dt + col) * VR + 16 * t + 4 * quad]);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          o[dt][qt] = mfma4(va.x, s[qt][t][0], o[dt][qt]);
-          o[dt][qt] = mfma4(va.y, s[qt][t][1], o[dt][qt]);
-          o[dt][qt] = mfma4(va.z, s[qt][t][2], o[dt][qt]);
-          o[dt][qt] = mfma4(va.w, s[qt][t][3], o[dt][qt]);
-        }
-      }
-    }
+    f32_softmax<D>(s, m_run, l_run, o);
+    f32_pv<D>(sVt, s, col, quad, o);
   }
   if (!active) return;
-  // o[dt][qt][r]: query 16 qt + col, dim 16 dt + 4 quad + r
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    float l = l_run[qt];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
-    const int i = i0 + 16 * qt + col;
-    if (i >= S) continue;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    float *dst = out + ((size_t(b) * S + i) * Hq + hq) * D + 4 * quad;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const floatx4 x = o[dt][qt] * inv;
-      *reinterpret_cast<float4 *>(dst + 16 * dt) = make_float4(x[0], x[1], x[2], x[3]);
-    }
-  }
+  float *const dst[2] = {
+      i0 + col < S ? out + ((size_t(b) * S + i0 + col) * Hq + hq) * D : nullptr,
+      i0 + 16 + col < S ? out + ((size_t(b) * S + i0 + 16 + col) * Hq + hq) * D : nullptr};
+  f32_store<D>(o, l_run, dst, quad);
 }
 
 template <int D>
@@ -401,29 +442,12 @@ __global__ __launch_bounds__(FNT, 2) void k_chunk_f32(
     if (!active) continue;
 
     floatx4 s[2][2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) s[qt][t2] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < DQ / 4; ++m) {
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const float4 ka = *reinterpret_cast<const float4 *>(&sK[(16 * t2 + col) * KR + quad * DQ + 4 * m]);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          s[qt][t2] = mfma4(ka.x, qf[qt][m].x, s[qt][t2]);
-          s[qt][t2] = mfma4(ka.y, qf[qt][m].y, s[qt][t2]);
-          s[qt][t2] = mfma4(ka.z, qf[qt][m].z, s[qt][t2]);
-          s[qt][t2] = mfma4(ka.w, qf[qt][m].w, s[qt][t2]);
-        }
-      }
-    }
+    f32_scores<D>(sK, qf, col, quad, s);
+    // liveness of each slot for this column's query position
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const int cq = c0 + 16 * qt + col;
-      const int tq = t_first + 16 * qt + col;  // this column's position
-      float mx = -INFINITY;
+      const int tq = t_first + 16 * qt + col;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -432,60 +456,17 @@ __global__ __launch_bounds__(FNT, 2) void k_chunk_f32(
           const int pos = sPos[js];
           const bool live = (cq < C) & (slot < ns) &
                             ((slot < nc) | ((pos <= tq) & ((sMark[js] == 0) | (tq - pos < window))));
-          const float x = live ? s[qt][t2][r] * scale_log2 : -INFINITY;
-          s[qt][t2][r] = x;
-          mx = fmaxf(mx, x);
+          s[qt][t2][r] = live ? s[qt][t2][r] * scale_log2 : -INFINITY;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run[qt], mx);
-      const float corr = m_run[qt] == -INFINITY ? 0.f : exp2f(m_run[qt] - m_new);
-      const float m_sub = m_new == -INFINITY ? 0.f : m_new;
-      float lsum = 0.f;
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(s[qt][t2][r] - m_sub);
-          s[qt][t2][r] = p;
-          lsum += p;
-        }
-      l_run[qt] = fmaf(l_run[qt], corr, lsum);
-      m_run[qt] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= corr;
     }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const float4 va = *reinterpret_cast<const float4 *>(&sVt[(16 * dt + col) * VR + 16 * t2 + 4 * quad]);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          o[dt][qt] = mfma4(va.x, s[qt][t2][0], o[dt][qt]);
-          o[dt][qt] = mfma4(va.y, s[qt][t2][1], o[dt][qt]);
-          o[dt][qt] = mfma4(va.z, s[qt][t2][2], o[dt][qt]);
-          o[dt][qt] = mfma4(va.w, s[qt][t2][3], o[dt][qt]);
-        }
-      }
-    }
+    f32_softmax<D>(s, m_run, l_run, o);
+    f32_pv<D>(sVt, s, col, quad, o);
   }
   if (!active) return;
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    float l = l_run[qt];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
-    const int cq = c0 + 16 * qt + col;
-    if (cq >= C) continue;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    float *dst = out + ((size_t(b) * C + cq) * Hq + hq) * D + 4 * quad;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const floatx4 x = o[dt][qt] * inv;
-      *reinterpret_cast<float4 *>(dst + 16 * dt) = make_float4(x[0], x[1], x[2], x[3]);
-    }
-  }
+  float *const dst[2] = {
+      c0 + col < C ? out + ((size_t(b) * C + c0 + col) * Hq + hq) * D : nullptr,
+      c0 + 16 + col < C ? out + ((size_t(b) * C + c0 + 16 + col) * Hq + hq) * D : nullptr};
+  f32_store<D>(o, l_run, dst, quad);
 }
 
 }  // namespace

@@ -15,7 +15,7 @@ import torch
 
 import workloads as wl
 from decode_attention_learned_amd import DmsCache, lib
-from harness import BF16_TOL, say
+from harness import BF16_TOL, check_accounting, say
 from oracle import dms_oracle as orc
 
 pytestmark = pytest.mark.gpu
@@ -30,28 +30,6 @@ def _prompt_and_steps(b, hkv, g, d, prompt, steps, rate, seed):
                      dtype="bf16", context=steps, evict_rate=rate, seed=seed + 1)
     sq, sk, sv, sl = wl.prefill_inputs(w2)
     return (pk, pv, pl), (sq, sk, sv, sl)
-
-
-def check_accounting(cache):
-    """Every page is on the free stack or in some unit's row; page_ref = holders - 1."""
-    torch.cuda.synchronize()
-    n = cache.n_slots.cpu().long()
-    rows = cache.page_table.cpu()
-    holders = torch.zeros(cache.num_pages, dtype=torch.long)
-    for u in range(cache.units):
-        np_ = (int(n[u]) + 63) // 64
-        for pg in rows[u, :np_].tolist():
-            assert pg >= 0
-            holders[pg] += 1
-    top = int(cache.free_top.item())
-    free = cache.free_list[:top].cpu().long()
-    assert len(set(free.tolist())) == top, "a page is on the free stack twice"
-    assert torch.all(holders[free] == 0), "a held page is on the free stack"
-    assert top + int((holders > 0).sum()) == cache.num_pages, "pages lost"
-    ref = cache.page_ref.cpu().long()
-    held = holders > 0
-    assert torch.equal(ref[held], holders[held] - 1)
-    assert torch.all(ref[~held] == 0)
 
 
 def _run_pair(gpu, b, hkv, g, d, prompt, steps, rate, seed, n_share=None, release=None):

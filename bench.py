@@ -48,8 +48,8 @@ DECODE_CONFIGS = ("llama1b_cr4", "qwen3_8b_cr1", "qwen32b_width")
 DEFAULT_WORKLOAD = "qwen3_8b_cr8"
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_qwen3_8b_cr8_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "decode_attention_learned_amd", "csrc", "decode_mfma.hip")
-PREFILL_PMC_FILE = os.path.join(ROOT, "profiles", "prefill_8k_traffic.json")
 PREFILL_SRC = os.path.join(ROOT, "decode_attention_learned_amd", "csrc", "prefill.hip")
+PREFILL_F32_SRC = os.path.join(ROOT, "decode_attention_learned_amd", "csrc", "prefill_f32.hip")
 
 
 def log(*a):
@@ -344,7 +344,7 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10, relaxed: bool = True)
         "roofline": {"bound": "mfma", "kernel": "k_prefill_pack + k_prefill", "achieved": round(tflops, 1),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": prefill_traffic_from_profile("dense") if name == "prefill_8k" else None,
+                     "traffic": prefill_traffic_from_profile("dense", name),
                      "algorithmic_bytes_per_call": prefill_algorithmic_bytes(
                          w.batch, s_len, w.q_heads, w.kv_heads, d),
                      "workspace_bytes_per_call": prefill_workspace_traffic(
@@ -357,7 +357,7 @@ def prefill_leg(name: str = "prefill_8k", iters: int = 10, relaxed: bool = True)
                          "kernel": "k_sparse_scan + k_sparse_pack + k_prefill_gathered",
                          "achieved": round(g_tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(g_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                         "traffic": prefill_traffic_from_profile("gathered") if name == "prefill_8k" else None},
+                         "traffic": prefill_traffic_from_profile("gathered", name)},
         },
     }
     if relaxed:
@@ -392,7 +392,11 @@ def prefill_f32_leg(name: str = "prefill_8k", iters: int = 3) -> dict:
             "ms": round(ms, 3), "relaxed_ms": round(ms_r, 3),
             "roofline": {"bound": "mfma", "kernel": f"k_prefill_f32<{d}>", "achieved": round(tf, 1),
                          "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / FP32_PEAK_TFLOPS, 4),
-                         "relaxed_frac": round(tf_r / FP32_PEAK_TFLOPS, 4), "traffic": None}}
+                         "relaxed_frac": round(tf_r / FP32_PEAK_TFLOPS, 4),
+                         "traffic": prefill_traffic_from_profile("dense", name, f32=True),
+                         "relaxed_traffic": prefill_traffic_from_profile("relaxed", name, f32=True),
+                         "algorithmic_bytes_per_call": prefill_algorithmic_bytes(
+                             w.batch, s_len, w.q_heads, w.kv_heads, d, in_bytes=4)}}
 
 
 def chunk_leg(caches, w, dev, n_query: int = 4, rounds: int = 32) -> dict:
@@ -675,19 +679,24 @@ def traffic_from_profile(bytes_alg_per_launch: float):
     return rec.get("hbm_bytes_per_launch") if rec else None
 
 
-def prefill_traffic_from_profile(method: str = "dense"):
+def prefill_traffic_from_profile(method: str = "dense", workload: str = "prefill_8k", f32: bool = False):
     """HBM bytes per prefill call of `method` ("dense", "gathered" or "relaxed":
-    every kernel of the call) from the committed rocprofv3 counter summary."""
-    rec = _profile_record(PREFILL_PMC_FILE, PREFILL_SRC)
+    every kernel of the call) on `workload` from the committed rocprofv3 counter
+    summary (bf16 inputs, or float32 with `f32`), or None if there is none."""
+    name = f"prefill_f32_{workload.removeprefix('prefill_')}" if f32 else workload
+    rec = _profile_record(os.path.join(ROOT, "profiles", f"{name}_traffic.json"),
+                          PREFILL_F32_SRC if f32 else PREFILL_SRC)
     return rec.get(method, {}).get("hbm_bytes_per_call") if rec else None
 
 
-def prefill_algorithmic_bytes(batch: int, seq_len: int, q_heads: int, kv_heads: int, d: int) -> int:
+def prefill_algorithmic_bytes(batch: int, seq_len: int, q_heads: int, kv_heads: int, d: int,
+                              in_bytes: int = 2) -> int:
     """Bytes a masked prefill call must move through HBM whatever its design
-    (bf16 inputs, fp32 output): Q, K, V and the logits in once, O out once."""
-    kv = batch * seq_len * kv_heads * d * 2 * 2          # K and V, bf16
+    (inputs of `in_bytes` per element, fp32 output): Q, K, V and the logits in
+    once, O out once."""
+    kv = batch * seq_len * kv_heads * d * in_bytes * 2   # K and V
     logits = batch * seq_len * kv_heads * 4
-    q = batch * seq_len * q_heads * d * 2
+    q = batch * seq_len * q_heads * d * in_bytes
     o = batch * seq_len * q_heads * d * 4
     return kv + logits + q + o
 
@@ -753,6 +762,8 @@ def main():
                     help="only run the copy/read calibration on a buffer of GIB GiB")
     ap.add_argument("--no-prefill", action="store_true", help="skip the masked-prefill leg")
     ap.add_argument("--prefill-only", action="store_true", help="only run the masked-prefill leg")
+    ap.add_argument("--prefill-d64-only", action="store_true",
+                    help="only run the head_dim 64 masked-prefill leg (4096 tokens)")
     ap.add_argument("--prefill-f32-only", action="store_true",
                     help="only run the float32 masked-prefill leg")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunk-query leg")
@@ -785,6 +796,9 @@ def main():
         return
     if args.prefill_only:
         print(json.dumps(prefill_leg()), flush=True)
+        return
+    if args.prefill_d64_only:
+        print(json.dumps(prefill_leg("prefill_4k_d64", relaxed=False)), flush=True)
         return
     if args.prefill_f32_only:
         print(json.dumps(prefill_f32_leg()), flush=True)

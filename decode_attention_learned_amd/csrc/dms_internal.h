@@ -95,9 +95,9 @@ inline DecodeWorkspace decode_workspace_layout(int units, int group, int head_di
 // Split-K of the tiled chunk kernel (chunks of 32 queries or more).  Its
 // grid is one workgroup per 32 queries and (sequence, KV head, group of 4
 // query heads); three run per CU.  When that fills at most half of one
-// resident round (3 x 256), each workgroup's tiles are cut into `splits`
-// parts (at most 4, all still in one round) whose partials a merge launch
-// combines.  Measured: 512 queries of 4 sequences (512 workgroups, two
+// resident round (3 x 256), each workgroup's tiles are dealt round-robin
+// into `splits` parts (at most 4, all still in one round) whose partials a
+// merge launch combines.  Measured: 512 queries of 4 sequences (512 workgroups, two
 // thirds of a round) took 0.132 ms split 3 ways against 0.069 ms unsplit,
 // the partials' traffic outweighing the extra third of the chip.
 constexpr int kChunkResident = 3 * 256;

@@ -1141,17 +1141,24 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
   // Tiles this workgroup reads.  The chunk's C tokens are the unit's last C
   // slots (nothing compacted it since, else the status flag below), so
   // query c0 + 31 sits in slot ns - C + c0 + 31 and later slots are hidden
-  // from every query of the workgroup.  Split sp of nsplit takes an equal
-  // share of the tiles up to there.
+  // from every query of the workgroup.  Split sp of nsplit takes every
+  // nsplit-th tile up to there, tiles sp, sp + nsplit, ...: each split gets
+  // its share of the clean tiles and of the costlier ones above n_clean,
+  // which hold the chunk itself (equal ranges left the last split with the
+  // chunk's tiles, the others idle at the end).  Tile i of the split is
+  // tile_of(i); its first ni_clean tiles lie wholly below n_clean.
   const int last_slot = ns - C + min(c0 + 31, C - 1);
   const int nt_vis = last_slot < 0 ? 0 : min(nt, last_slot / PBN + 1);
-  const int kb = sp * nt_vis / nsplit, ke = (sp + 1) * nt_vis / nsplit;
+  const int nt_clean = min(nclean_t, nt_vis);
+  const int ni = nt_vis > sp ? (nt_vis - sp + nsplit - 1) / nsplit : 0;
+  const int ni_clean = nt_clean > sp ? (nt_clean - sp + nsplit - 1) / nsplit : 0;
+  auto tile_of = [&](int i) { return sp + i * nsplit; };
   if (qb == 0 && sp == 0 && hg == 0 && tid == 0) {
     const int p0 = seq_len[b] - C;  // the chunk's first position
     if (p0 < 0 || compact_pos[u] > p0) atomicOr(status, DMS_STATUS_CHUNK_INVALID);
   }
   // slots in use in the last tile read (all 32 unless it is the unit's last)
-  const int tail_valid = ke == nt ? ns - (nt - 1) * PBN : PBN;
+  const int tail_valid = ni > 0 && tile_of(ni - 1) == nt - 1 ? ns - (nt - 1) * PBN : PBN;
 
   uint4 qf[2][PKS];
 #pragma unroll
@@ -1196,50 +1203,49 @@ __global__ __launch_bounds__(PNT, 3) void k_chunk_attn(
     if (wave == 1 && lane < PBN / 16)
       __builtin_amdgcn_global_load_lds(slot_alpha + grp * (PBN / 16) + lane, da, 16, 0, 0);
   };
-  if (ke > kb) copy(kb, sT0, sP0, sA0);
+  if (ni > 0) copy(tile_of(0), sT0, sP0, sA0);
   ring_barrier();
 
   floatx4 s[2][2];
   uint4 pb[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
   const floatx4 zero[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-  auto iteration = [&](int k, const uint4 *t, const int4 *p, const uint4 *a, const uint4 *tp,
+  auto iteration = [&](int i, const uint4 *t, const int4 *p, const uint4 *a, const uint4 *tp,
                        uint4 *tn, int4 *pn, uint4 *an) {
-    if (k + 1 < ke) copy(k + 1, tn, pn, an);
+    if (i + 1 < ni) copy(tile_of(i + 1), tn, pn, an);
     if (active) {
-      if (k > kb) pv_tile<D>(tp + PK_FRAGS * PFRAG, pb, lane, o);
+      if (i > 0) pv_tile<D>(tp + PK_FRAGS * PFRAG, pb, lane, o);
       qk_tile<D>(t, zero, qf, lane, s);
-      c_phase2<D>(k, nt, nclean_t, ns, nc, window, t_first, col, quad, p,
+      c_phase2<D>(tile_of(i), nt, nclean_t, ns, nc, window, t_first, col, quad, p,
                reinterpret_cast<const uint2 *>(a), s, sm, o, pb, c);
     }
     ring_barrier();
   };
-  auto clean_iteration = [&](int k, const uint4 *t, const uint4 *tp, uint4 *tn, int4 *pn,
+  auto clean_iteration = [&](int i, const uint4 *t, const uint4 *tp, uint4 *tn, int4 *pn,
                              uint4 *an) {
-    if (k + 1 < ke) copy(k + 1, tn, pn, an);
+    if (i + 1 < ni) copy(tile_of(i + 1), tn, pn, an);
     if (active) steady_step<D>(t, tp + PK_FRAGS * PFRAG, zero, qf, s, pb, o, sm, c, lane);
     ring_barrier();
   };
-  // tile kb; the tiles after it wholly below n_clean in whole rounds of
-  // three; the rest on the general path.  Tile k is in buffer (k - kb) % 3.
+  // the split's tile 0; its tiles after it wholly below n_clean in whole
+  // rounds of three; the rest on the general path.  Tile i is in buffer i % 3.
   // The PV product of the last tile comes after the loop: its unused tail
   // slots are cleared there, away from the loop body's registers.
-  if (ke > kb) iteration(kb, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
-  const int clean_end = min(nclean_t, ke);
-  int k = kb + 1;
-  for (; k + 2 < clean_end; k += 3) {
-    clean_iteration(k, sT1, sT0, sT2, sP2, sA2);
-    clean_iteration(k + 1, sT2, sT1, sT0, sP0, sA0);
-    clean_iteration(k + 2, sT0, sT2, sT1, sP1, sA1);
+  if (ni > 0) iteration(0, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
+  int i = 1;
+  for (; i + 2 < ni_clean; i += 3) {
+    clean_iteration(i, sT1, sT0, sT2, sP2, sA2);
+    clean_iteration(i + 1, sT2, sT1, sT0, sP0, sA0);
+    clean_iteration(i + 2, sT0, sT2, sT1, sP1, sA1);
   }
-  for (; k < ke; k += 3) {
-    iteration(k, sT1, sP1, sA1, sT0, sT2, sP2, sA2);
-    if (k + 1 >= ke) break;
-    iteration(k + 1, sT2, sP2, sA2, sT1, sT0, sP0, sA0);
-    if (k + 2 >= ke) break;
-    iteration(k + 2, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
+  for (; i < ni; i += 3) {
+    iteration(i, sT1, sP1, sA1, sT0, sT2, sP2, sA2);
+    if (i + 1 >= ni) break;
+    iteration(i + 1, sT2, sP2, sA2, sT1, sT0, sP0, sA0);
+    if (i + 2 >= ni) break;
+    iteration(i + 2, sT0, sP0, sA0, sT2, sT1, sP1, sA1);
   }
-  if (ke > kb && active) {
-    const int lt = (ke - 1 - kb) % 3;  // the last tile's buffer
+  if (ni > 0 && active) {
+    const int lt = (ni - 1) % 3;  // the last tile's buffer
     const uint4 *tl = lt == 0 ? sT0 : (lt == 1 ? sT1 : sT2);
     pv_tile_tail<D>(tl + PK_FRAGS * PFRAG, pb, lane, tail_valid, o);
   }

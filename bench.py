@@ -44,7 +44,7 @@ METRIC = "DMS decode-attn tokens/s and KV GB/s (% HBM peak) at CR=8, Qwen3-8B sh
 # the other decode workloads, each measured by a short step loop of its own:
 # Llama-3.2-1B-shaped heads at CR 4, the Qwen3-8B shape with nothing evicted,
 # ragged Qwen2.5-32B-shaped units
-DECODE_CONFIGS = ("llama1b_cr4", "qwen3_8b_cr1", "qwen32b_width")
+DECODE_CONFIGS = ("llama1b_cr4", "qwen3_8b_cr1", "qwen32b_width", "qwen3_8b_cr8_f32")
 DEFAULT_WORKLOAD = "qwen3_8b_cr8"
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_qwen3_8b_cr8_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "decode_attention_learned_amd", "csrc", "decode_mfma.hip")
@@ -144,7 +144,8 @@ def build_replica(w, r, dev, extra_tokens):
 
     rates = wl.unit_eviction_rates(w, r)
     max_pages, num_pages = pool_size(w, rates, extra_tokens)
-    cache = DmsCache(w.batch, w.kv_heads, w.group, w.head_dim, torch.bfloat16,
+    cache = DmsCache(w.batch, w.kv_heads, w.group, w.head_dim,
+                     torch.float32 if w.dtype == "f32" else torch.bfloat16,
                      num_pages=num_pages, max_pages_per_unit=max_pages,
                      window=w.window, device=dev)
     for ci, start in enumerate(range(0, w.context, w.prompt_chunk)):
@@ -590,11 +591,13 @@ def chunked_prefill_leg(name: str = "prefill_8k", chunk: int = 512, iters: int =
 
 
 def decode_config_leg(name: str, steps: int = 64, warmup: int = 8, n_ev: int = 32) -> dict:
-    """The decode step on another decode workload (its own shape, eviction rates and
-    replica count), measured like the headline: `steps` steps between two events
-    (reserve + decode with the token, compaction every `compact_every` steps per
-    replica, round-robin over the replicas), then per-call events around the
-    decode launch on `n_ev` further steps for its time and KV rate."""
+    """The decode step on another decode workload (its own shape, key/value dtype,
+    eviction rates and replica count), measured like the headline: `steps` steps
+    between two events (reserve + decode with the token, compaction every
+    `compact_every` steps per replica, round-robin over the replicas), then
+    per-call events around the decode call on `n_ev` further steps for its time
+    and KV rate (on float32 caches the call also holds the launch that writes
+    the token)."""
     import torch
 
     import workloads as wl
@@ -646,12 +649,12 @@ def decode_config_leg(name: str, steps: int = 64, warmup: int = 8, n_ev: int = 3
         raise RuntimeError(f"{name}: device status set")
     dec_ms = sum(a.elapsed_time(b) for a, b in evs) / n_ev
     retained = sum(a[0] + b[0] for a, b in zip(before, after)) / (2 * replicas)
-    bytes_alg = retained * w.head_dim * 2 * 2
+    bytes_alg = retained * w.head_dim * 2 * (4 if w.dtype == "f32" else 2)
     kv_gbps = bytes_alg / (dec_ms * 1e-3) / 1e9
     del caches, inputs, outs
     torch.cuda.empty_cache()
     return {"workload": name, "batch": w.batch, "kv_heads": w.kv_heads, "q_heads": w.q_heads,
-            "head_dim": w.head_dim, "context": w.context, "evict_rate": w.evict_rate,
+            "head_dim": w.head_dim, "kv_dtype": w.dtype, "context": w.context, "evict_rate": w.evict_rate,
             "replicas": replicas, "steps": steps, "ms_per_step": round(ms_step, 4),
             "tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
             "decode_attn_us": round(dec_ms * 1e3, 2),

@@ -25,8 +25,8 @@ LIB = os.path.join(HERE, "libdms.so")
 LIB_GENERIC = os.path.join(HERE, "libdms_generic.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "cache_kernels.hip", "decode_kernels.hip", "decode_mfma.hip", "decode_scratch.hip",
-           "prefill.hip", "prefill_f32.hip"]
+SOURCES = ["api.hip", "cache_kernels.hip", "decode_f32.hip", "decode_kernels.hip", "decode_mfma.hip",
+           "decode_scratch.hip", "prefill.hip", "prefill_f32.hip"]
 
 # Packed fp32 instructions are switched off for all device code; hipcc's host
 # pass warns that it does not know the feature, which is harmless.
@@ -40,6 +40,7 @@ FLAGS = [
 # The attention kernels mask with -inf and never rely on NaN semantics; without
 # NaN honouring the compiler drops the NaN-quieting copies before every max.
 PER_FILE_FLAGS = {
+    "decode_f32.hip": ["-fno-honor-nans"],
     "decode_mfma.hip": ["-fno-honor-nans"],
     "prefill.hip": ["-fno-honor-nans"],
 }

@@ -1,0 +1,298 @@
+// Split-K decode attention for float32 caches on the gfx950 matrix cores.
+//
+// Same result as the generic kernel (decode_kernels.hip holds the method and
+// its sources); this file carries out the two contractions of a chunk on
+// v_mfma_f32_16x16x4_f32, float32 operands and accumulation.  Per 32-slot
+// group of a page, for the G query heads of the unit (zero-padded to 16
+// columns):
+//   S^T [32 slots x 16] = K [32 x D] . Q^T [D x 16]
+//   O^T [D x 16]       += V^T [D x 32] . P^T [32 x 16]
+// Every K/V byte is loaded from HBM once, straight into operand registers,
+// and serves all G heads of the group.
+//
+// Operand layouts of v_mfma_f32_16x16x4_f32 (lane l, quad = l / 16): A holds
+// element (l % 16, quad), B element (quad, l % 16), the result rows
+// 4 quad .. 4 quad + 3 of column l % 16.
+//   QK: the reduction index is permuted.  K-step kb of lane group quad takes
+//       dim quad * D/4 + kb, so lane (quad, r) needs D/4 consecutive dims of
+//       the slot at tile row r: whole 8-float runs of the page layout
+//       (key_index).  The two 16-slot tiles of a group take their rows from
+//       the slot permutation (tile t, row 4a + j -> slot 8a + 4t + j), so
+//       lane (quad, col) ends with the scores of head col for the eight
+//       consecutive slots 8 quad .. 8 quad + 7.
+//   PV: k-step e of lane group quad takes slot 8 quad + e.  The B operand is
+//       then the lane's own weight, and the A operand, dim dt * 16 + l % 16
+//       of those eight slots, is one 8-float run of the page layout
+//       (value_index).  No data moves between lanes except the two shuffles
+//       of the row maximum.
+// The softmax is the bf16 kernel's: float32 exp2 form with a lazy reference,
+// and the row sums add the same weights that enter the PV product.
+#include "decode_common.h"
+
+namespace dms {
+
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kF32Waves = 4;  // waves per workgroup: two workgroups per CU
+constexpr int kF32Threads = kF32Waves * kWave;
+constexpr int kF32Group = 32;             // slots per group (half a page)
+constexpr int kF32ChunkPages = 1024;      // page ids staged in LDS per segment
+constexpr float kF32Lazy = 8.0f;          // reference slack, log2 units
+
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// K/V bytes are read once per call.  A lane takes 16 bytes of a 32-byte run
+// per load, so each load instruction touches every line of its 2 KB half and
+// the next instruction reads the other halves of the same lines.  Keys are
+// read with plain loads, whose lines the second instruction still finds in
+// the cache; values with nontemporal loads, which keep the stream from
+// displacing other lines.  Measured at B = 64, 8 KV heads, 4112 slots per
+// unit: 351 us per call, against 387 us with nontemporal loads for both and
+// 363 us with plain loads for both.
+__device__ __forceinline__ floatx4 ld4(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
+__device__ __forceinline__ floatx4 ld4_stream(const float *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p));
+}
+
+}  // namespace
+
+// One query per sequence: query cq of a chunk of C tokens just appended, at
+// position seq_len - C + cq (decode: C = 1, cq = 0).  `chunk_status` (chunk
+// queries only, else null): as in the bf16 kernel.
+template <int D>
+__global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
+    int units, int hkv, int G, int window, int maxp, float scale_log2, int C, int cq,
+    const float *__restrict__ q, const float *__restrict__ k_pages,
+    const float *__restrict__ v_pages, const int32_t *__restrict__ page_table,
+    const int32_t *__restrict__ slot_pos, const uint8_t *__restrict__ slot_alpha,
+    const int32_t *__restrict__ n_slots, const int32_t *__restrict__ n_clean_arr,
+    const int32_t *__restrict__ seq_len, int32_t *__restrict__ plan,
+    uint32_t *__restrict__ chunk_status, float2 *__restrict__ part_ml,
+    float *__restrict__ part_o, float *__restrict__ out) {
+  constexpr int DQ = D / 4;     // QK k-steps: dims per lane group
+  constexpr int RUNS = DQ / 8;  // 8-float key runs per lane and tile
+  constexpr int KS = D / 32;    // key fragments per tile in the page layout
+  constexpr int DT = D / 16;    // PV products per k-step
+  const PlanLayout L = plan_layout(units);
+  const int c = blockIdx.x;
+  ChunkInfo ci;
+  if (!locate_chunk(c, hkv, plan, n_slots, n_clean_arr, seq_len, L, ci)) return;
+  const int u = ci.unit, b = ci.b, h = ci.h;
+  const int s_begin = ci.s_begin, s_end = ci.s_end, nclean = ci.nclean;
+  const int t = ci.t - (C - 1) + cq;  // the query's position
+  const int tid = threadIdx.x;
+  if (chunk_status != nullptr && cq == 0 && c == ci.first && tid == 0) {
+    const int p0 = ci.t - (C - 1);  // the chunk's first position
+    if (p0 < 0 || plan[L.compact_pos + u] > p0) atomicOr(chunk_status, DMS_STATUS_CHUNK_INVALID);
+  }
+  const int32_t *row = page_table + size_t(u) * maxp;
+  const int lim = min(nclean, s_end);  // slots below lim need no liveness test
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = lane_id();
+  const int col = lane & 15;  // head column in B and results, slot row or dim in A
+  const int quad = lane >> 4;
+
+  __shared__ int s_pages[kF32ChunkPages];
+  const int p_first = s_begin / kPage;
+  const int npages = (s_end - s_begin + kPage - 1) / kPage;
+
+  // Q^T operand: head col, dims quad * DQ .. + DQ; zero for columns >= G
+  floatx4 qv[DQ / 4];
+#pragma unroll
+  for (int m = 0; m < DQ / 4; ++m) qv[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (col < G) {
+    const float *qp = q + ((size_t(b) * C + cq) * hkv * G + size_t(h) * G + col) * D + quad * DQ;
+#pragma unroll
+    for (int m = 0; m < DQ / 4; ++m) qv[m] = *reinterpret_cast<const floatx4 *>(qp + 4 * m);
+  }
+
+  floatx4 o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // m_run: the column's reference (-inf until a live slot is seen); m_thr =
+  // m_run + kF32Lazy; m_sub: what the exponent subtracts (0 while m_run = -inf)
+  float m_run = -INFINITY, l_run = 0.f, m_thr = -INFINITY, m_sub = 0.f;
+  const int ngroups = (s_end - s_begin + kF32Group - 1) / kF32Group;
+
+  // operand registers of one group
+  struct Regs {
+    floatx4 k[2][2 * RUNS];  // tile, dims quad * DQ + 4 i .. + 4 of slot row col
+    floatx4 v[DT][2];        // dim dt * 16 + col, slots 8 quad + 4 i .. + 4
+    int page;
+  };
+  auto load_group = [&](Regs &r, int gi, int seg0) {
+    const int pi = (gi * kF32Group) / kPage - seg0;
+    r.page = __builtin_amdgcn_readfirstlane(s_pages[pi]);
+    const size_t base = size_t(r.page) * kPage * D + size_t((gi * kF32Group) % kPage) * D;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < RUNS; ++i) {
+        const int d0 = quad * DQ + 8 * i;  // key_index of (row col of tile tt, d0 .. d0 + 7)
+        const float *kp = k_pages + base + (((tt * KS + (d0 >> 5)) * 4 + ((d0 >> 3) & 3)) * 16 + col) * 8;
+        r.k[tt][2 * i] = ld4(kp);
+        r.k[tt][2 * i + 1] = ld4(kp + 4);
+      }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {  // value_index of (slots 8 quad .. + 8, dim dt * 16 + col)
+      const float *vp = v_pages + base + ((dt * 4 + quad) * 16 + col) * 8;
+      r.v[dt][0] = ld4_stream(vp);
+      r.v[dt][1] = ld4_stream(vp + 4);
+    }
+  };
+
+  auto process = [&](Regs &r, int gi) {
+    const int gs = s_begin + gi * kF32Group;
+    const int poff = gs % kPage;
+    floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < DQ / 4; ++m) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        s0 = mfma4(r.k[0][m][x], qv[m][x], s0);
+        s1 = mfma4(r.k[1][m][x], qv[m][x], s1);
+      }
+    }
+    // scores of head col for slots gs + 8 quad + e, in log2 units
+    float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[e] *= scale_log2;
+
+    if (gs + kF32Group > lim) {  // wave-uniform: tail of the chunk or not yet compacted
+      // the lane's eight slots: decisions (8 bytes) and positions (2 x 16
+      // bytes), always inside the page, then a branch-free liveness test
+      const size_t mb = size_t(r.page) * kPage + poff + quad * 8;
+      const uint2 a8 = *reinterpret_cast<const uint2 *>(slot_alpha + mb);
+      const int4 p0 = *reinterpret_cast<const int4 *>(slot_pos + mb);
+      const int4 p1 = *reinterpret_cast<const int4 *>(slot_pos + mb + 4);
+      const int pos[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int slot = gs + quad * 8 + e;
+        const uint32_t marked = ((e < 4 ? a8.x : a8.y) >> (8 * (e & 3))) & 0xffu;
+        const bool live = (slot < s_end) & ((slot < nclean) | ((pos[e] <= t) &
+                                            ((marked == 0u) | ((t - pos[e]) < window))));
+        sv[e] = live ? sv[e] : -INFINITY;
+        // a slot hidden from the query, or unused, must not reach the PV
+        // product even as 0 * NaN (a recycled page may hold NaN there)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) r.v[dt][e >> 2][e & 3] = live ? r.v[dt][e >> 2][e & 3] : 0.f;
+      }
+    }
+
+    // Lazy reference: a column's reference m_run moves only when one of its
+    // scores exceeds it by more than kF32Lazy (log2 units), so every p <=
+    // 2^kF32Lazy; the result is independent of the reference.
+    float mx = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+    if (__ballot(mx > m_thr)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const bool move = mx > m_thr;  // uniform over the four lanes of a column
+      const float corr = move ? (m_run == -INFINITY ? 0.f : exp2f(m_run - mx)) : 1.f;
+      l_run *= corr;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
+      m_run = move ? mx : m_run;
+      m_thr = move ? mx + kF32Lazy : m_thr;
+      m_sub = m_run == -INFINITY ? 0.f : m_run;
+    }
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = exp2f(sv[e] - m_sub);
+      l_run += p[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] = mfma4(r.v[dt][e >> 2][e & 3], p[e], o[dt]);
+  };
+
+  for (int seg0 = 0; seg0 < npages; seg0 += kF32ChunkPages) {
+    const int segp = min(kF32ChunkPages, npages - seg0);
+    __syncthreads();  // every wave is done with the previous segment
+    for (int i = tid; i < segp; i += kF32Threads) s_pages[i] = row[p_first + seg0 + i];
+    __syncthreads();
+    const int g_end = min(ngroups, (seg0 + segp) * (kPage / kF32Group));
+    for (int gi = seg0 * (kPage / kF32Group) + wave; gi < g_end; gi += kF32Waves) {
+      Regs r;
+      load_group(r, gi, seg0);
+      process(r, gi);
+    }
+  }
+
+  // combine the waves: per column the row sum over the lane's quads, then
+  // the log-sum-exp rule over the waves in LDS
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  constexpr int OS = D + 4;  // row stride of the staged outputs
+  __shared__ float s_m[kF32Waves][16], s_l[kF32Waves][16];
+  __shared__ __align__(16) float s_o[kF32Waves * 16 * OS];
+  if (quad == 0) {
+    s_m[wave][col] = m_run;
+    s_l[wave][col] = l_run;
+  }
+  if (col < G) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<floatx4 *>(&s_o[(wave * 16 + col) * OS + dt * 16 + quad * 4]) = o[dt];
+  }
+  __syncthreads();
+  // output of column x / D (query head h * G + x / D)
+  const OutMap om{((size_t(b) * C + cq) * hkv * G + size_t(h) * G) * D, size_t(hkv) * G * D, G, D};
+  for (int x = tid; x < G * D; x += kF32Threads) {
+    const int g = x / D, d = x % D;
+    float M = s_m[0][g];
+#pragma unroll
+    for (int w = 1; w < kF32Waves; ++w) M = fmaxf(M, s_m[w][g]);
+    float Ls = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kF32Waves; ++w) {
+        const float mw = s_m[w][g];
+        if (mw == -INFINITY) continue;
+        const float f = exp2f(mw - M);
+        Ls = fmaf(s_l[w][g], f, Ls);
+        O = fmaf(s_o[(w * 16 + g) * OS + d], f, O);
+      }
+    }
+    if (ci.nch == 1) {
+      out[om.at(x)] = Ls > 0.f ? O / Ls : 0.f;
+    } else {
+      publish(part_o + size_t(c) * G * D + x, O);
+      if (d == 0) {
+        publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + g), M);
+        publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + g) + 1, Ls);
+      }
+    }
+  }
+  if (ci.nch > 1 && fused_merge(units))  // else merged by k_merge_partials
+    count_and_merge(ci, G, D, plan + L.merge_count, part_ml, part_o, out, om);
+}
+
+bool launch_decode_f32(const dms_shape &s, const dms_cache &c, const void *q, float *out,
+                       float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st, int C,
+                       int cq, uint32_t *chunk_status) {
+  if (s.kv_dtype != DMS_KV_F32 || s.group > 16) return false;
+  auto run = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(w.max_chunks), dim3(kF32Threads), 0, st, units_of(s), s.kv_heads,
+                       s.group, s.window, s.max_pages_per_unit, scale_log2, C, cq,
+                       static_cast<const float *>(q), static_cast<const float *>(c.k_pages),
+                       static_cast<const float *>(c.v_pages), c.page_table, c.slot_pos, c.slot_alpha,
+                       c.n_slots, c.n_clean, c.seq_len, c.plan, chunk_status,
+                       reinterpret_cast<float2 *>(ws + w.part_ml),
+                       reinterpret_cast<float *>(ws + w.part_o), out);
+  };
+  if (s.head_dim == 128) run(k_decode_f32<128>);
+  else if (s.head_dim == 64) run(k_decode_f32<64>);
+  else return false;
+  return true;
+}
+
+}  // namespace dms

@@ -246,12 +246,17 @@ static bool dispatch_group(const dms_shape &s, const dms_cache &c, const E *q, f
 bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                         float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
                         int n_query, const DecodeFill *fill, bool chunk);
+bool launch_decode_f32(const dms_shape &s, const dms_cache &c, const void *q, float *out,
+                       float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st, int C,
+                       int cq, uint32_t *chunk_status);
 
 // The decode grid has one workgroup per possible chunk (max_chunks_of(units));
 // workgroups past the plan's chunk count exit at once.  Plans of fewer than
-// kTargetChunks units are merged by a second launch (launch_merge).  With `fill`, the
-// matrix-core kernel writes the reserved token itself; the vector kernels
-// take it from a write launch ahead of them.
+// kTargetChunks units are merged by a second launch (launch_merge).  bf16
+// caches run the bf16 matrix-core kernel, float32 caches the float32 one
+// (decode_f32.hip); the vector kernel serves the test build that routes bf16
+// decode to it.  With `fill`, the bf16 matrix-core kernel writes the reserved
+// token itself; the other kernels take it from a write launch ahead of them.
 hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, float *out,
                          float sm_scale, void *wsv, hipStream_t st, const DecodeFill *fill) {
   const DecodeWorkspace w = decode_workspace_layout(units_of(s), s.group, s.head_dim);
@@ -271,9 +276,7 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
                  ? dispatch_group<uint16_t, 64>(s, c, static_cast<const uint16_t *>(q), out, scale_log2, w, ws, st)
                  : dispatch_group<uint16_t, 128>(s, c, static_cast<const uint16_t *>(q), out, scale_log2, w, ws, st);
   } else {
-    done = s.head_dim == 64
-               ? dispatch_group<uint32_t, 64>(s, c, static_cast<const uint32_t *>(q), out, scale_log2, w, ws, st)
-               : dispatch_group<uint32_t, 128>(s, c, static_cast<const uint32_t *>(q), out, scale_log2, w, ws, st);
+    done = launch_decode_f32(s, c, q, out, scale_log2, w, ws, st, 1, 0, nullptr);
   }
   if (!done) return hipErrorInvalidValue;
   const hipError_t e = hipGetLastError();
@@ -287,8 +290,9 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
 // queries or more) run a tiled chunk kernel, one pass over the cache per 32
 // queries (bf16: matrix cores in bf16; float32: the float32 matrix
 // instruction).  Shorter ones: bf16 caches run the split-K decode kernel in
-// launches of at most 16 / G queries, float32 caches the vector kernel, one
-// launch per query position.  The workspace holds partials for 16 columns.
+// launches of at most 16 / G queries, float32 caches the float32 split-K
+// decode kernel, one launch per query position.  The workspace holds
+// partials for 16 columns.
 constexpr int kChunkKernelMin = 32;
 
 hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
@@ -299,12 +303,9 @@ hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const voi
     return launch_chunk_f32(s, c, q, n_query, out, sm_scale, st);
   if (s.kv_dtype == DMS_KV_F32) {
     char *ws = static_cast<char *>(wsv);
-    const uint32_t *q32 = static_cast<const uint32_t *>(q);
     for (int cq = 0; cq < n_query; ++cq) {
-      const bool ok = s.head_dim == 64
-                          ? dispatch_group<uint32_t, 64>(s, c, q32, out, scale_log2, w, ws, st, n_query, cq, c.status)
-                          : dispatch_group<uint32_t, 128>(s, c, q32, out, scale_log2, w, ws, st, n_query, cq, c.status);
-      if (!ok) return hipErrorInvalidValue;
+      if (!launch_decode_f32(s, c, q, out, scale_log2, w, ws, st, n_query, cq, c.status))
+        return hipErrorInvalidValue;
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       const hipError_t m = launch_merge(s, c, w, ws, out, s.group, cq, n_query, st);

@@ -219,7 +219,9 @@ size_t dms_decode_workspace_bytes(const dms_shape *shape);
  *   q    [B][Hq][D] in kv_dtype, Hq = Hkv*G
  *   out  [B][Hq][D] float32
  * The caller appends token t before this call, so each query sees its own
- * token.  A unit with no slots gives zeros.  The work of each unit is split
+ * token.  A unit with no slots gives zeros.  Both products run on the matrix
+ * cores: bf16 caches in bf16 with float32 accumulation, float32 caches in
+ * float32 throughout.  The work of each unit is split
  * into chunks of whole pages following cache->plan (sized on the device from
  * the live lengths: one chunk per unit when the units are many and of even
  * length), and the chunk partials of a split unit are merged with the
@@ -345,7 +347,7 @@ size_t dms_decode_multi_split_workspace_bytes(const dms_shape *shape, int32_t n_
  * ones run the split-K decode kernel in launches of 16 / G queries.  float32
  * caches: chunks of 32 queries or more run a tiled kernel on the float32
  * matrix instruction (one pass over the cache per 32 queries), shorter ones
- * the vector decode kernel once per query position.  Workspace:
+ * the float32 split-K decode kernel once per query position.  Workspace:
  * at least dms_decode_multi_workspace_bytes.  Errors as for dms_decode_attn.
  */
 int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const void *q,

@@ -261,6 +261,16 @@ def test_qwen3_8b_cr8_full_sampled(gpu):
     assert 7.0 < cr < 9.0
 
 
+def test_qwen3_8b_cr8_f32_full_sampled(gpu):
+    """The same shape with float32 keys and values (the float32 matrix-core decode
+    kernel at the size the bench times): every unit at sampled steps."""
+    w = wl.get("qwen3_8b_cr8_f32")
+    say("qwen3_8b_cr8_f32 full size: building 32768-token context")
+    cache, _, _ = run_decode(w, gpu, steps=17, check_steps={0, 16}, gen_device=gpu,
+                             max_pages=140, kv_units=range(0, w.units, 97))
+    assert cache.k_pages.dtype == torch.float32
+
+
 def test_qwen32b_width_ragged_full_sampled(gpu):
     """Qwen2.5-32B heads (G=5), per-unit Beta(7,1) rates: ragged lengths, every unit."""
     w = wl.get("qwen32b_width")

@@ -63,6 +63,12 @@ WORKLOADS = {
         dtype="bf16", context=32768, steps=200, evict_rate=0.875, prompt_chunk=4096,
         replicas=4, warmup=20, seed=3000,
     ),
+    # the headline shape with float32 keys and values (twice the bytes per retained entry)
+    "qwen3_8b_cr8_f32": Workload(
+        name="qwen3_8b_cr8_f32", kind="decode", batch=64, kv_heads=8, group=4, head_dim=128,
+        dtype="f32", context=32768, steps=32, evict_rate=0.875, prompt_chunk=4096,
+        replicas=2, warmup=5, seed=3200,
+    ),
     # same shape, nothing evicted (compression ratio 1): the dense control
     "qwen3_8b_cr1": Workload(
         name="qwen3_8b_cr1", kind="decode", batch=64, kv_heads=8, group=4, head_dim=128,

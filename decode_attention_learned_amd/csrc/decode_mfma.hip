@@ -171,8 +171,9 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
 
   const int ngroups = (s_end - s_begin + kGroup - 1) / kGroup;
 
-  // operand registers of one group.  Latency is hidden by occupancy (4 waves
-  // per SIMD at this register count) rather than by a second register set.
+  // operand registers of one group.  At D = 128 latency is hidden by
+  // occupancy (4 waves per SIMD at this register count) rather than by a
+  // second register set; D = 64 keeps two groups in flight (below).
   struct Regs {
     uint4 k0[KSTEPS], k1[KSTEPS], v[DTILES];
     int page;
@@ -282,10 +283,26 @@ __global__ __launch_bounds__(kMfmaThreads, 4) void k_decode_mfma(
     for (int i = tid; i < segp; i += kMfmaThreads) s_pages[i] = row[p_first + seg0 + i];
     __syncthreads();
     const int g_end = min(ngroups, (seg0 + segp) * (kPage / kGroup));
-    for (int gi = seg0 * (kPage / kGroup) + wave; gi < g_end; gi += kMfmaWaves) {
-      Regs r;
-      load_group(r, gi, seg0);
-      process(r, gi);
+    if constexpr (D == 64) {
+      // At D = 64 a group is 8 KB per wave and two fit the register budget:
+      // a wave requests its next group before it computes the current one,
+      // halving the dependent round trips of a chunk (short chunks of small
+      // heads are latency bound: Llama-1B-shaped step 22.2-23.4 -> 21.4-22.5
+      // us, identical outputs).  At D = 128 a second set would cost occupancy.
+      for (int gi = seg0 * (kPage / kGroup) + wave; gi < g_end; gi += 2 * kMfmaWaves) {
+        Regs r0, r1;
+        const bool two = gi + kMfmaWaves < g_end;  // wave-uniform
+        load_group(r0, gi, seg0);
+        if (two) load_group(r1, gi + kMfmaWaves, seg0);
+        process(r0, gi);
+        if (two) process(r1, gi + kMfmaWaves);
+      }
+    } else {
+      for (int gi = seg0 * (kPage / kGroup) + wave; gi < g_end; gi += kMfmaWaves) {
+        Regs r;
+        load_group(r, gi, seg0);
+        process(r, gi);
+      }
     }
   }
   // The token, by the last wave after its stream (the staging copies issued

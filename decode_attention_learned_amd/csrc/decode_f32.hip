@@ -3,12 +3,12 @@
 // Same result as the generic kernel (decode_kernels.hip holds the method and
 // its sources); this file carries out the two contractions of a chunk on
 // v_mfma_f32_16x16x4_f32, float32 operands and accumulation.  Per 32-slot
-// group of a page, for the G query heads of the unit (zero-padded to 16
-// columns):
+// group of a page, for the G query heads of the unit (or the heads of up to
+// 16 / G queries of a chunk; zero-padded to 16 columns):
 //   S^T [32 slots x 16] = K [32 x D] . Q^T [D x 16]
 //   O^T [D x 16]       += V^T [D x 32] . P^T [32 x 16]
 // Every K/V byte is loaded from HBM once, straight into operand registers,
-// and serves all G heads of the group.
+// and serves every column.
 //
 // Operand layouts of v_mfma_f32_16x16x4_f32 (lane l, quad = l / 16): A holds
 // element (l % 16, quad), B element (quad, l % 16), the result rows
@@ -60,12 +60,16 @@ __device__ __forceinline__ floatx4 ld4_stream(const float *p) {
 
 }  // namespace
 
-// One query per sequence: query cq of a chunk of C tokens just appended, at
-// position seq_len - C + cq (decode: C = 1, cq = 0).  `chunk_status` (chunk
-// queries only, else null): as in the bf16 kernel.
+// Several queries per sequence, as in the bf16 kernel: a chunk of C tokens
+// just appended, at positions seq_len - C .. seq_len - 1; one launch serves
+// queries c0 .. c0 + nq - 1 of the chunk, and the 16 operand columns hold
+// (query, head) pairs col = (c - c0) * G + g, nq * G <= 16.  Decode is
+// nq = C = 1.  `chunk_status` (chunk queries only, else null): the first
+// launch of a chunk flags DMS_STATUS_CHUNK_INVALID for a sequence shorter
+// than the chunk or compacted after the chunk's first position.
 template <int D>
 __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
-    int units, int hkv, int G, int window, int maxp, float scale_log2, int C, int cq,
+    int units, int hkv, int G, int window, int maxp, float scale_log2, int nq, int c0, int C,
     const float *__restrict__ q, const float *__restrict__ k_pages,
     const float *__restrict__ v_pages, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ slot_pos, const uint8_t *__restrict__ slot_alpha,
@@ -83,9 +87,8 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
   if (!locate_chunk(c, hkv, plan, n_slots, n_clean_arr, seq_len, L, ci)) return;
   const int u = ci.unit, b = ci.b, h = ci.h;
   const int s_begin = ci.s_begin, s_end = ci.s_end, nclean = ci.nclean;
-  const int t = ci.t - (C - 1) + cq;  // the query's position
   const int tid = threadIdx.x;
-  if (chunk_status != nullptr && cq == 0 && c == ci.first && tid == 0) {
+  if (chunk_status != nullptr && c0 == 0 && c == ci.first && tid == 0) {
     const int p0 = ci.t - (C - 1);  // the chunk's first position
     if (p0 < 0 || plan[L.compact_pos + u] > p0) atomicOr(chunk_status, DMS_STATUS_CHUNK_INVALID);
   }
@@ -93,19 +96,26 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
   const int lim = min(nclean, s_end);  // slots below lim need no liveness test
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
-  const int col = lane & 15;  // head column in B and results, slot row or dim in A
+  const int col = lane & 15;  // (query, head) column in B and results, slot row or dim in A
   const int quad = lane >> 4;
+  const int ncol = nq * G;
+  const int cq = col < ncol ? col / G : 0;
+  // query positions: this column's, and the first and last of the launch
+  const int t_first = ci.t - (C - 1) + c0;
+  const int t_last = t_first + nq - 1;
+  const int t_col = t_first + cq;
 
   __shared__ int s_pages[kF32ChunkPages];
   const int p_first = s_begin / kPage;
   const int npages = (s_end - s_begin + kPage - 1) / kPage;
 
-  // Q^T operand: head col, dims quad * DQ .. + DQ; zero for columns >= G
+  // Q^T operand: column col, dims quad * DQ .. + DQ; zero for columns >= nq * G
   floatx4 qv[DQ / 4];
 #pragma unroll
   for (int m = 0; m < DQ / 4; ++m) qv[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-  if (col < G) {
-    const float *qp = q + ((size_t(b) * C + cq) * hkv * G + size_t(h) * G + col) * D + quad * DQ;
+  if (col < ncol) {
+    const int g = col - cq * G;
+    const float *qp = q + ((size_t(b) * C + c0 + cq) * hkv * G + size_t(h) * G + g) * D + quad * DQ;
 #pragma unroll
     for (int m = 0; m < DQ / 4; ++m) qv[m] = *reinterpret_cast<const floatx4 *>(qp + 4 * m);
   }
@@ -157,7 +167,7 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
         s1 = mfma4(r.k[1][m][x], qv[m][x], s1);
       }
     }
-    // scores of head col for slots gs + 8 quad + e, in log2 units
+    // scores of column col for slots gs + 8 quad + e, in log2 units
     float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
 #pragma unroll
     for (int e = 0; e < 8; ++e) sv[e] *= scale_log2;
@@ -174,13 +184,17 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
       for (int e = 0; e < 8; ++e) {
         const int slot = gs + quad * 8 + e;
         const uint32_t marked = ((e < 4 ? a8.x : a8.y) >> (8 * (e & 3))) & 0xffu;
-        const bool live = (slot < s_end) & ((slot < nclean) | ((pos[e] <= t) &
-                                            ((marked == 0u) | ((t - pos[e]) < window))));
+        // live for this column's query; live for at least one query of the launch
+        const bool live = (slot < s_end) & ((slot < nclean) | ((pos[e] <= t_col) &
+                                            ((marked == 0u) | ((t_col - pos[e]) < window))));
+        const bool any = (slot < s_end) & ((slot < nclean) | ((pos[e] <= t_last) &
+                                           ((marked == 0u) | ((t_first - pos[e]) < window))));
         sv[e] = live ? sv[e] : -INFINITY;
-        // a slot hidden from the query, or unused, must not reach the PV
-        // product even as 0 * NaN (a recycled page may hold NaN there)
+        // a slot hidden from every query of the launch, or unused, must not
+        // reach the PV product even as 0 * NaN (a recycled page may hold NaN
+        // there; the value row serves every column)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) r.v[dt][e >> 2][e & 3] = live ? r.v[dt][e >> 2][e & 3] : 0.f;
+        for (int dt = 0; dt < DT; ++dt) r.v[dt][e >> 2][e & 3] = any ? r.v[dt][e >> 2][e & 3] : 0.f;
       }
     }
 
@@ -238,15 +252,15 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
     s_m[wave][col] = m_run;
     s_l[wave][col] = l_run;
   }
-  if (col < G) {
+  if (col < ncol) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       *reinterpret_cast<floatx4 *>(&s_o[(wave * 16 + col) * OS + dt * 16 + quad * 4]) = o[dt];
   }
   __syncthreads();
-  // output of column x / D (query head h * G + x / D)
-  const OutMap om{((size_t(b) * C + cq) * hkv * G + size_t(h) * G) * D, size_t(hkv) * G * D, G, D};
-  for (int x = tid; x < G * D; x += kF32Threads) {
+  // output of column x / D: query c0 + col / G, head h * G + col % G
+  const OutMap om{((size_t(b) * C + c0) * hkv * G + size_t(h) * G) * D, size_t(hkv) * G * D, G, D};
+  for (int x = tid; x < ncol * D; x += kF32Threads) {
     const int g = x / D, d = x % D;
     float M = s_m[0][g];
 #pragma unroll
@@ -265,24 +279,24 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
     if (ci.nch == 1) {
       out[om.at(x)] = Ls > 0.f ? O / Ls : 0.f;
     } else {
-      publish(part_o + size_t(c) * G * D + x, O);
+      publish(part_o + size_t(c) * ncol * D + x, O);
       if (d == 0) {
-        publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + g), M);
-        publish(reinterpret_cast<float *>(part_ml + size_t(c) * G + g) + 1, Ls);
+        publish(reinterpret_cast<float *>(part_ml + size_t(c) * ncol + g), M);
+        publish(reinterpret_cast<float *>(part_ml + size_t(c) * ncol + g) + 1, Ls);
       }
     }
   }
   if (ci.nch > 1 && fused_merge(units))  // else merged by k_merge_partials
-    count_and_merge(ci, G, D, plan + L.merge_count, part_ml, part_o, out, om);
+    count_and_merge(ci, ncol, D, plan + L.merge_count, part_ml, part_o, out, om);
 }
 
 bool launch_decode_f32(const dms_shape &s, const dms_cache &c, const void *q, float *out,
-                       float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st, int C,
-                       int cq, uint32_t *chunk_status) {
-  if (s.kv_dtype != DMS_KV_F32 || s.group > 16) return false;
+                       float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st, int nq,
+                       int c0, int C, uint32_t *chunk_status) {
+  if (s.kv_dtype != DMS_KV_F32 || nq < 1 || nq * s.group > 16) return false;
   auto run = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(w.max_chunks), dim3(kF32Threads), 0, st, units_of(s), s.kv_heads,
-                       s.group, s.window, s.max_pages_per_unit, scale_log2, C, cq,
+                       s.group, s.window, s.max_pages_per_unit, scale_log2, nq, c0, C,
                        static_cast<const float *>(q), static_cast<const float *>(c.k_pages),
                        static_cast<const float *>(c.v_pages), c.page_table, c.slot_pos, c.slot_alpha,
                        c.n_slots, c.n_clean, c.seq_len, c.plan, chunk_status,

@@ -247,8 +247,8 @@ bool launch_decode_mfma(const dms_shape &s, const dms_cache &c, const void *q, f
                         float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st,
                         int n_query, const DecodeFill *fill, bool chunk);
 bool launch_decode_f32(const dms_shape &s, const dms_cache &c, const void *q, float *out,
-                       float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st, int C,
-                       int cq, uint32_t *chunk_status);
+                       float scale_log2, const DecodeWorkspace &w, char *ws, hipStream_t st, int nq,
+                       int c0, int C, uint32_t *chunk_status);
 
 // The decode grid has one workgroup per possible chunk (max_chunks_of(units));
 // workgroups past the plan's chunk count exit at once.  Plans of fewer than
@@ -276,7 +276,7 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
                  ? dispatch_group<uint16_t, 64>(s, c, static_cast<const uint16_t *>(q), out, scale_log2, w, ws, st)
                  : dispatch_group<uint16_t, 128>(s, c, static_cast<const uint16_t *>(q), out, scale_log2, w, ws, st);
   } else {
-    done = launch_decode_f32(s, c, q, out, scale_log2, w, ws, st, 1, 0, nullptr);
+    done = launch_decode_f32(s, c, q, out, scale_log2, w, ws, st, 1, 0, 1, nullptr);
   }
   if (!done) return hipErrorInvalidValue;
   const hipError_t e = hipGetLastError();
@@ -289,10 +289,10 @@ hipError_t launch_decode(const dms_shape &s, const dms_cache &c, const void *q, 
 // Queries of a chunk of n_query tokens just appended.  Long chunks (32
 // queries or more) run a tiled chunk kernel, one pass over the cache per 32
 // queries (bf16: matrix cores in bf16; float32: the float32 matrix
-// instruction).  Shorter ones: bf16 caches run the split-K decode kernel in
-// launches of at most 16 / G queries, float32 caches the float32 split-K
-// decode kernel, one launch per query position.  The workspace holds
-// partials for 16 columns.
+// instruction).  Shorter ones run the split-K decode kernel of the cache's
+// dtype in launches of at most 16 / G queries (the matrix products' 16
+// columns), each merged after it.  The workspace holds partials for 16
+// columns.
 constexpr int kChunkKernelMin = 32;
 
 hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const void *q, int n_query,
@@ -303,12 +303,14 @@ hipError_t launch_decode_multi(const dms_shape &s, const dms_cache &c, const voi
     return launch_chunk_f32(s, c, q, n_query, out, sm_scale, st);
   if (s.kv_dtype == DMS_KV_F32) {
     char *ws = static_cast<char *>(wsv);
-    for (int cq = 0; cq < n_query; ++cq) {
-      if (!launch_decode_f32(s, c, q, out, scale_log2, w, ws, st, n_query, cq, c.status))
+    const int per = 16 / s.group;  // queries per launch
+    for (int c0 = 0; c0 < n_query; c0 += per) {
+      const int nq = n_query - c0 < per ? n_query - c0 : per;
+      if (!launch_decode_f32(s, c, q, out, scale_log2, w, ws, st, nq, c0, n_query, c.status))
         return hipErrorInvalidValue;
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      const hipError_t m = launch_merge(s, c, w, ws, out, s.group, cq, n_query, st);
+      const hipError_t m = launch_merge(s, c, w, ws, out, nq * s.group, c0, n_query, st);
       if (m != hipSuccess) return m;
     }
     return hipSuccess;

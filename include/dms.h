@@ -347,7 +347,7 @@ size_t dms_decode_multi_split_workspace_bytes(const dms_shape *shape, int32_t n_
  * ones run the split-K decode kernel in launches of 16 / G queries.  float32
  * caches: chunks of 32 queries or more run a tiled kernel on the float32
  * matrix instruction (one pass over the cache per 32 queries), shorter ones
- * the float32 split-K decode kernel once per query position.  Workspace:
+ * the float32 split-K decode kernel in launches of 16 / G queries.  Workspace:
  * at least dms_decode_multi_workspace_bytes.  Errors as for dms_decode_attn.
  */
 int dms_decode_attn_multi(const dms_shape *shape, const dms_cache *cache, const void *q,

@@ -195,13 +195,15 @@ def test_long_chunks_tiled_kernel_head_dim_64(gpu, chunk):
     say(f"tiled chunk D=64 {chunk}: max err {worst:.2e}")
 
 
-@pytest.mark.parametrize("chunks,d", [([1, 3], 64), ([40], 64), ([5, 17], 128)])
-def test_chunk_queries_float32_cache(gpu, chunks, d):
-    """float32 caches: chunk queries through the vector kernel (one launch per
-    query position), against the oracle at the float32 tolerance (1e-5 max
-    abs), with compaction between chunks; G = 2 (the tiny float32 shape's)."""
+@pytest.mark.parametrize("chunks,d,g", [([1, 3], 64, 2), ([40], 64, 2), ([5, 17], 128, 2),
+                                         ([7, 13], 128, 5), ([4, 9], 64, 16), ([31], 128, 4)])
+def test_chunk_queries_float32_cache(gpu, chunks, d, g):
+    """float32 caches: chunks shorter than 32 queries through the float32 split-K
+    decode kernel, in launches of 16 / G queries (G = 5 leaves a partial last
+    launch, G = 16 one query per launch), against the oracle at the float32
+    tolerance (1e-5 max abs), with compaction between chunks."""
     from harness import F32_ATOL
-    b, hkv, g, prompt, window = 1, 2, 2, 300, 16
+    b, hkv, prompt, window = 1, 2, 300, 16
     total = prompt + sum(chunks)
     w = wl.Workload(name="chunk_f32", kind="prefill", batch=b, kv_heads=hkv, group=g, head_dim=d,
                     dtype="f32", context=total, evict_rate=0.5, seed=7500 + d + len(chunks))
@@ -230,7 +232,7 @@ def test_chunk_queries_float32_cache(gpu, chunks, d):
                 assert err <= F32_ATOL, f"chunk at {t0}, query {c}, head {h}: {err:.3g}"
         cache.compact()
         t0 += n
-    say(f"float32 chunk queries {chunks} D={d}: max abs err {worst:.2e}")
+    say(f"float32 chunk queries {chunks} D={d} G={g}: max abs err {worst:.2e}")
 
 
 def test_float32_chunk_compacted_after_append_is_flagged(gpu):

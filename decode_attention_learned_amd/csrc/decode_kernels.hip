@@ -27,7 +27,10 @@ namespace dms {
 // ---------------------------------------------------------------------------
 // generic split-K decode (VALU, float32 arithmetic, either element type)
 //
-// One workgroup per chunk.  Tiles of 32 slots are staged in LDS as float32;
+// The reference path of the test build (libdms_generic.so routes one-query
+// decode of bf16 caches here), against which tests check the matrix-core
+// kernels; the product library reaches it only for shapes those kernels
+// refuse.  One workgroup per chunk.  Tiles of 32 slots are staged in LDS as float32;
 // scores are formed per (head, slot), each head's online softmax is advanced
 // by one wave, and each thread accumulates its (head, d) outputs.  One query
 // per sequence: query cq of a chunk of C tokens just appended, at position

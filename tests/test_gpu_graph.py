@@ -29,13 +29,14 @@ def _content(cache):
             cache.n_slots.cpu(), cache.n_clean.cpu()]
 
 
-@pytest.mark.parametrize("name,batch", [("llama1b_cr4", 4), ("qwen3_8b_cr8", 2)])
+@pytest.mark.parametrize("name,batch", [("llama1b_cr4", 4), ("qwen3_8b_cr8", 2), ("qwen3_8b_cr8_f32", 2)])
 def test_decode_step_graph_replays_match_eager(gpu, name, batch):
     w = dataclasses.replace(wl.get(name), batch=batch, context=1500, prompt_chunk=1500, replicas=1)
     say(f"graph case: {name} B={batch} context {w.context}")
     steps, every = 24, 4
     maxp = (w.context + steps) // 64 + 3
-    caches = [DmsCache(w.batch, w.kv_heads, w.group, w.head_dim, torch.bfloat16,
+    dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    caches = [DmsCache(w.batch, w.kv_heads, w.group, w.head_dim, dtype,
                        max_pages_per_unit=maxp, window=w.window, device=gpu) for _ in range(2)]
     k, v, logit = (t.to(gpu) for t in wl.prompt_chunk_inputs(w, 0, w.context))
     for c in caches:

@@ -13,10 +13,15 @@
 // Operand layouts of v_mfma_f32_16x16x4_f32 (lane l, quad = l / 16): A holds
 // element (l % 16, quad), B element (quad, l % 16), the result rows
 // 4 quad .. 4 quad + 3 of column l % 16.
-//   QK: the reduction index is permuted.  K-step kb of lane group quad takes
-//       dim quad * D/4 + kb, so lane (quad, r) needs D/4 consecutive dims of
-//       the slot at tile row r: whole 8-float runs of the page layout
-//       (key_index).  The two 16-slot tiles of a group take their rows from
+//   QK: the reduction index is permuted so that key loads are whole lines.
+//       The page layout (key_index) keeps 8 consecutive dims of a slot as a
+//       32-byte run, and the runs of the 16 rows of a tile for one dim range
+//       are one 512-byte block.  Lane groups 0 and 1 take the two 16-byte
+//       halves of the same runs, groups 2 and 3 those of the other half of
+//       the dims: lane (quad, r) holds, for m = 0 .. D/16 - 1, dims
+//       8 f + 4 (quad & 1) .. + 4 of row r with f = (quad >> 1) D/16 + m, and
+//       k-step (m, i) takes its dim i.  Each load instruction then reads two
+//       whole 512-byte blocks.  The two 16-slot tiles of a group take their rows from
 //       the slot permutation (tile t, row 4a + j -> slot 8a + 4t + j), so
 //       lane (quad, col) ends with the scores of head col for the eight
 //       consecutive slots 8 quad .. 8 quad + 7.
@@ -45,15 +50,12 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// K/V bytes are read once per call.  A lane takes 16 bytes of a 32-byte run
-// per load, so each load instruction touches every line of its 2 KB half and
-// the next instruction reads the other halves of the same lines.  Keys are
-// read with plain loads, whose lines the second instruction still finds in
-// the cache; values with nontemporal loads, which keep the stream from
-// displacing other lines.  Measured at B = 64, 8 KV heads, 4112 slots per
-// unit: 351 us per call, against 387 us with nontemporal loads for both and
-// 363 us with plain loads for both.
-__device__ __forceinline__ floatx4 ld4(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
+// K/V bytes are read once per call: nontemporal loads keep them from
+// displacing reusable lines in the caches.  Key loads read whole 512-byte
+// blocks (the k-step order below); a value load reads 16 bytes of each
+// 32-byte run, the next instruction the other halves.  Measured at B = 64,
+// 8 KV heads, 4112 slots per unit: 334 us per call; with plain key loads 346
+// us.  Key loads of half runs took 387 us nontemporal and 351 us plain.
 __device__ __forceinline__ floatx4 ld4_stream(const float *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p));
 }
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
     uint32_t *__restrict__ chunk_status, float2 *__restrict__ part_ml,
     float *__restrict__ part_o, float *__restrict__ out) {
   constexpr int DQ = D / 4;     // QK k-steps: dims per lane group
-  constexpr int RUNS = DQ / 8;  // 8-float key runs per lane and tile
+  constexpr int NH = D / 16;    // 4-float half runs per lane and tile
   constexpr int KS = D / 32;    // key fragments per tile in the page layout
   constexpr int DT = D / 16;    // PV products per k-step
   const PlanLayout L = plan_layout(units);
@@ -109,15 +111,17 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
   const int p_first = s_begin / kPage;
   const int npages = (s_end - s_begin + kPage - 1) / kPage;
 
-  // Q^T operand: column col, dims quad * DQ .. + DQ; zero for columns >= nq * G
-  floatx4 qv[DQ / 4];
+  // Q^T operand: column col, the lane's dims (as for its keys); zero for
+  // columns >= nq * G
+  floatx4 qv[NH];
 #pragma unroll
-  for (int m = 0; m < DQ / 4; ++m) qv[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < NH; ++m) qv[m] = floatx4{0.f, 0.f, 0.f, 0.f};
   if (col < ncol) {
     const int g = col - cq * G;
-    const float *qp = q + ((size_t(b) * C + c0 + cq) * hkv * G + size_t(h) * G + g) * D + quad * DQ;
+    const float *qp = q + ((size_t(b) * C + c0 + cq) * hkv * G + size_t(h) * G + g) * D + 4 * (quad & 1);
 #pragma unroll
-    for (int m = 0; m < DQ / 4; ++m) qv[m] = *reinterpret_cast<const floatx4 *>(qp + 4 * m);
+    for (int m = 0; m < NH; ++m)
+      qv[m] = *reinterpret_cast<const floatx4 *>(qp + 8 * ((quad >> 1) * NH + m));
   }
 
   floatx4 o[DT];
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
 
   // operand registers of one group
   struct Regs {
-    floatx4 k[2][2 * RUNS];  // tile, dims quad * DQ + 4 i .. + 4 of slot row col
+    floatx4 k[2][NH];        // tile, the lane's m-th 4 dims of slot row col
     floatx4 v[DT][2];        // dim dt * 16 + col, slots 8 quad + 4 i .. + 4
     int page;
   };
@@ -141,11 +145,11 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int i = 0; i < RUNS; ++i) {
-        const int d0 = quad * DQ + 8 * i;  // key_index of (row col of tile tt, d0 .. d0 + 7)
-        const float *kp = k_pages + base + (((tt * KS + (d0 >> 5)) * 4 + ((d0 >> 3) & 3)) * 16 + col) * 8;
-        r.k[tt][2 * i] = ld4(kp);
-        r.k[tt][2 * i + 1] = ld4(kp + 4);
+      for (int m = 0; m < NH; ++m) {
+        // key_index of (row col of tile tt, dims 8 f + 4 (quad & 1) .. + 4)
+        const int f = (quad >> 1) * NH + m;
+        r.k[tt][m] = ld4_stream(k_pages + base + (((tt * KS + (f >> 2)) * 4 + (f & 3)) * 16 + col) * 8 +
+                         4 * (quad & 1));
       }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {  // value_index of (slots 8 quad .. + 8, dim dt * 16 + col)
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
     const int poff = gs % kPage;
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < DQ / 4; ++m) {
+    for (int m = 0; m < NH; ++m) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         s0 = mfma4(r.k[0][m][x], qv[m][x], s0);

@@ -3,11 +3,12 @@ decode launch takes the step's token as one more softmax term and writes it
 to its page) against dms_append + dms_decode_attn on a twin cache, and against
 the oracle: the same cache state (slot positions and decisions, K/V bytes,
 counts, status; page ids may differ, as compaction returns pages from
-concurrent workgroups); outputs bit-identical on the vector kernels (float32
-caches, bf16 with the generic kernel forced, which write the token with the
-append's kernel) and within 2e-3 on the matrix-core kernel (the token's weight
-is not rounded to bf16 there), with one chunk per unit and with split chunks,
-across page crossings, compactions and refused units."""
+concurrent workgroups); outputs bit-identical where the token is written by
+the append's kernel ahead of the decode (float32 caches, and bf16 with the
+generic kernel forced) and within 2e-3 on the bf16 matrix-core kernel, which
+takes the token itself (its weight is not rounded to bf16 there), with one
+chunk per unit and with split chunks, across page crossings, compactions and
+refused units."""
 
 import numpy as np
 import pytest

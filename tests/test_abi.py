@@ -162,7 +162,7 @@ def test_host_side_errors_need_no_gpu(L):
     assert M(ctypes.byref(sb), ctypes.byref(full), fake, 0, fake, 0.125, fake, 1 << 30, None) == lib.DMS_EINVAL
     assert M(ctypes.byref(sb), ctypes.byref(full), fake, 4, fake, 0.125, fake, 10, None) == lib.DMS_EWORKSPACE
     assert M(ctypes.byref(sb), ctypes.byref(full), fake, 4, fake, 0.0, fake, 1 << 30, None) == lib.DMS_EINVAL
-    # float32 caches are served (by the vector kernel); a short workspace is refused on the host
+    # float32 caches are served (by the float32 kernels); a short workspace is refused on the host
     assert M(ctypes.byref(_shape(kv_dtype=lib.DMS_KV_F32)), ctypes.byref(full), fake, 4, fake, 0.125, fake,
              10, None) == lib.DMS_EWORKSPACE
     # partials for 16 columns, whatever the group

@@ -323,8 +323,8 @@ def test_dead_uncompacted_slot_with_dominant_score_is_excluded(gpu, kernel, dtyp
     """A marked token whose key dominates every query must stop counting once it is
     `window` positions old, even while its slot is still in the cache (no compaction).
     If it leaked in, the output would be pulled to its value vector."""
-    if dtype == torch.float32 and kernel == "mfma":
-        pytest.skip("float32 caches always use the generic kernel")
+    if dtype == torch.float32 and kernel == "generic":
+        pytest.skip("float32 caches run the float32 matrix-core kernel in both builds")
     with decode_build(kernel):
         _dominant_dead_slot(gpu, dtype)
 
@@ -365,8 +365,8 @@ def test_constant_values_give_the_constant(gpu, kernel, dtype):
     add into the row sums exactly the weights that multiply the values (the
     matrix-core kernel: the bf16-rounded ones), so the ratio is c up to float32
     rounding: 1e-5 relative."""
-    if dtype == torch.float32 and kernel == "mfma":
-        pytest.skip("float32 caches always use the generic kernel")
+    if dtype == torch.float32 and kernel == "generic":
+        pytest.skip("float32 caches run the float32 matrix-core kernel in both builds")
     with decode_build(kernel):
         _constant_values(gpu, dtype)
 

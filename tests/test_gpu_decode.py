@@ -496,27 +496,28 @@ def test_split_plan_ragged_800_units(gpu, dtype):
     assert np.all(merge == 0), "merge counters not reset"
 
 
-def test_chunk_longer_than_the_staged_page_ids(gpu):
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_chunk_longer_than_the_staged_page_ids(gpu, dtype):
     """One unit of 70,000 retained slots among 1536 units, all others evicting
     every token: the lengths are ragged and the units as many as the ragged
     budget (3 x 512 chunks), so every unit is one chunk and the long one spans
-    1095 pages, more than the 1024 page ids the matrix-core decode kernel stages
-    in LDS at a time: it walks that chunk in two segments.  The long unit's
+    1095 pages, more than the 1024 page ids each matrix-core decode kernel (bf16
+    and float32) stages in LDS at a time: it walks that chunk in two segments.  The long unit's
     queries are zero, so every weight is exactly 1 and its output is the mean
     of its 70,001 values to float32 rounding (pinned to 1e-4 against the
-    oracle); other units are checked at the bf16 tolerance."""
+    oracle); other units are checked at the bf16 tolerance (either dtype)."""
     b, hkv, g, d = 192, 8, 2, 64
     n_long, chunk = 70000, 4096
     maxp = n_long // 64 + 4
-    cache = DmsCache(b, hkv, g, d, torch.bfloat16, num_pages=b * hkv * 72 + maxp, max_pages_per_unit=maxp,
+    cache = DmsCache(b, hkv, g, d, dtype, num_pages=b * hkv * 72 + maxp, max_pages_per_unit=maxp,
                      device=gpu)
     gen = torch.Generator(device=gpu).manual_seed(7301)
     k0, v0 = [], []                 # unit 0 (sequence 0, KV head 0): every token
     tail_k, tail_v = None, None     # the last chunk, for the other units
     for start in range(0, n_long, chunk):
         n = min(chunk, n_long - start)
-        k = torch.randn((b, n, hkv, d), generator=gen, device=gpu).to(torch.bfloat16)
-        v = torch.randn((b, n, hkv, d), generator=gen, device=gpu).to(torch.bfloat16)
+        k = torch.randn((b, n, hkv, d), generator=gen, device=gpu).to(dtype)
+        v = torch.randn((b, n, hkv, d), generator=gen, device=gpu).to(dtype)
         logit = torch.ones((b, n, hkv), device=gpu)
         logit[0, :, 0] = -1.0
         cache.append(k, v, logit)
@@ -524,10 +525,10 @@ def test_chunk_longer_than_the_staged_page_ids(gpu):
         k0.append(k[0, :, 0].float().cpu().numpy())
         v0.append(v[0, :, 0].float().cpu().numpy())
         tail_k, tail_v = k[:, -32:].float().cpu().numpy(), v[:, -32:].float().cpu().numpy()
-    q = torch.randn((b, hkv * g, d), generator=gen, device=gpu).to(torch.bfloat16)
+    q = torch.randn((b, hkv * g, d), generator=gen, device=gpu).to(dtype)
     q[0, :g] = 0
-    k = torch.randn((b, 1, hkv, d), generator=gen, device=gpu).to(torch.bfloat16)
-    v = torch.randn((b, 1, hkv, d), generator=gen, device=gpu).to(torch.bfloat16)
+    k = torch.randn((b, 1, hkv, d), generator=gen, device=gpu).to(dtype)
+    v = torch.randn((b, 1, hkv, d), generator=gen, device=gpu).to(dtype)
     logit = torch.ones((b, 1, hkv), device=gpu)
     logit[0, :, 0] = -1.0
     cache.append(k, v, logit)
@@ -559,5 +560,5 @@ def test_chunk_longer_than_the_staged_page_ids(gpu):
         vv[t] = v[bi, 0, h].float().cpu().numpy()
         ref[u] = orc.decode_output(q[bi, h * g:(h + 1) * g].float().cpu().numpy(), kk, vv,
                                    np.ones(t + 1, dtype=np.int8), t, 16, scale)
-    worst = compare_outputs(out, ref, hkv, g, torch.bfloat16, what="short units beside a long one")
+    worst = compare_outputs(out, ref, hkv, g, dtype, what="short units beside a long one")
     say(f"1095-page chunk: long unit max err {err0:.2e}; short units {worst:.2e}")

@@ -13,23 +13,24 @@
 // Operand layouts of v_mfma_f32_16x16x4_f32 (lane l, quad = l / 16): A holds
 // element (l % 16, quad), B element (quad, l % 16), the result rows
 // 4 quad .. 4 quad + 3 of column l % 16.
-//   QK: the reduction index is permuted so that key loads are whole lines.
-//       The page layout (key_index) keeps 8 consecutive dims of a slot as a
-//       32-byte run, and the runs of the 16 rows of a tile for one dim range
-//       are one 512-byte block.  Lane groups 0 and 1 take the two 16-byte
-//       halves of the same runs, groups 2 and 3 those of the other half of
-//       the dims: lane (quad, r) holds, for m = 0 .. D/16 - 1, dims
-//       8 f + 4 (quad & 1) .. + 4 of row r with f = (quad >> 1) D/16 + m, and
-//       k-step (m, i) takes its dim i.  Each load instruction then reads two
-//       whole 512-byte blocks.  The two 16-slot tiles of a group take their rows from
-//       the slot permutation (tile t, row 4a + j -> slot 8a + 4t + j), so
-//       lane (quad, col) ends with the scores of head col for the eight
-//       consecutive slots 8 quad .. 8 quad + 7.
-//   PV: k-step e of lane group quad takes slot 8 quad + e.  The B operand is
-//       then the lane's own weight, and the A operand, dim dt * 16 + l % 16
-//       of those eight slots, is one 8-float run of the page layout
-//       (value_index).  No data moves between lanes except the two shuffles
-//       of the row maximum.
+//   Product tile T of a group is its slots 16 T .. 16 T + 15 in order, so
+//       lane (quad, col) ends the QK product with the scores of column col
+//       for slots 16 T + 4 quad .. + 3 of both tiles, and PV k-step e of lane
+//       group quad takes slot 16 (e >> 2) + 4 quad + (e & 3): the B operand is
+//       the lane's own weight.  No data moves between lanes except the two
+//       shuffles of the row maximum.
+//   Loads are whole lines.  The page layout keeps 8 consecutive dims of a
+//       key, and 8 consecutive slots of a value dim, as 32-byte runs; lane
+//       groups 0 and 1 take the two 16-byte halves of the same runs, groups 2
+//       and 3 those of the next ones.  Keys: the QK reduction index is
+//       permuted, lane (quad, r) holding for m = 0 .. D/16 - 1 dims
+//       8 f + 4 (quad & 1) .. + 4 with f = (quad >> 1) D/16 + m, k-step (m, i)
+//       taking its dim i; a load instruction reads the runs of 8 layout rows
+//       of both layout tiles (key_index: slot 8a + 4t + j sits in tile t, row
+//       4a + j).  Values: the A operand of k-steps 4T .. 4T + 3 is half
+//       (quad & 1) of the run of slots 8 (2T + (quad >> 1)) .. + 8 for dim
+//       dt * 16 + l % 16 (value_index); a load instruction reads 1 KB in one
+//       block.
 // The softmax is the bf16 kernel's: float32 exp2 form with a lazy reference,
 // and the row sums add the same weights that enter the PV product.
 #include "decode_common.h"
@@ -51,11 +52,11 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
 }
 
 // K/V bytes are read once per call: nontemporal loads keep them from
-// displacing reusable lines in the caches.  Key loads read whole 512-byte
-// blocks (the k-step order below); a value load reads 16 bytes of each
-// 32-byte run, the next instruction the other halves.  Measured at B = 64,
-// 8 KV heads, 4112 slots per unit: 334 us per call; with plain key loads 346
-// us.  Key loads of half runs took 387 us nontemporal and 351 us plain.
+// displacing reusable lines in the caches.  Every load instruction reads
+// whole lines (the operand orders described above).  Measured at B = 64, 8 KV
+// heads, 4112 slots per unit, per call: 319-333 us; with value loads of half
+// runs 334-336 us; with key loads of half runs too 387 us (351 us with plain
+// key loads).
 __device__ __forceinline__ floatx4 ld4_stream(const float *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p));
 }
@@ -134,29 +135,37 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
 
   // operand registers of one group
   struct Regs {
-    floatx4 k[2][NH];        // tile, the lane's m-th 4 dims of slot row col
-    floatx4 v[DT][2];        // dim dt * 16 + col, slots 8 quad + 4 i .. + 4
+    floatx4 k[2][NH];        // product tile, the lane's m-th 4 dims of its row col
+    floatx4 v[DT][2];        // dim dt * 16 + col, slots 16 T + 4 quad .. + 4
     int page;
   };
   auto load_group = [&](Regs &r, int gi, int seg0) {
     const int pi = (gi * kF32Group) / kPage - seg0;
     r.page = __builtin_amdgcn_readfirstlane(s_pages[pi]);
     const size_t base = size_t(r.page) * kPage * D + size_t((gi * kF32Group) % kPage) * D;
+    // keys: row col of product tile T is slot 16 T + col of the group, which
+    // the page layout keeps in tile (col >> 2) & 1 at row 4 (2 T + (col >> 3))
+    // + (col & 3); the 16 rows of a product tile are two runs of 8 layout rows
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int T = 0; T < 2; ++T) {
+      const int lt = (col >> 2) & 1, lrow = 4 * (2 * T + (col >> 3)) + (col & 3);
 #pragma unroll
       for (int m = 0; m < NH; ++m) {
-        // key_index of (row col of tile tt, dims 8 f + 4 (quad & 1) .. + 4)
+        // key_index of (that slot, dims 8 f + 4 (quad & 1) .. + 4)
         const int f = (quad >> 1) * NH + m;
-        r.k[tt][m] = ld4_stream(k_pages + base + (((tt * KS + (f >> 2)) * 4 + (f & 3)) * 16 + col) * 8 +
-                         4 * (quad & 1));
+        r.k[T][m] = ld4_stream(k_pages + base + (((lt * KS + (f >> 2)) * 4 + (f & 3)) * 16 + lrow) * 8 +
+                               4 * (quad & 1));
       }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {  // value_index of (slots 8 quad .. + 8, dim dt * 16 + col)
-      const float *vp = v_pages + base + ((dt * 4 + quad) * 16 + col) * 8;
-      r.v[dt][0] = ld4_stream(vp);
-      r.v[dt][1] = ld4_stream(vp + 4);
     }
+    // values: slots 16 T + 4 quad .. + 4 of dim dt * 16 + col, half (quad & 1)
+    // of the run of slots 8 (2 T + (quad >> 1)) .. + 8 (value_index); lane
+    // groups 0 and 1 read the two halves of the same runs
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+        r.v[dt][T] = ld4_stream(v_pages + base + ((dt * 4 + 2 * T + (quad >> 1)) * 16 + col) * 8 +
+                                4 * (quad & 1));
   };
 
   auto process = [&](Regs &r, int gi) {
@@ -171,23 +180,25 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
         s1 = mfma4(r.k[1][m][x], qv[m][x], s1);
       }
     }
-    // scores of column col for slots gs + 8 quad + e, in log2 units
+    // scores of column col for slots gs + 16 (e >> 2) + 4 quad + (e & 3), in log2 units
     float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
 #pragma unroll
     for (int e = 0; e < 8; ++e) sv[e] *= scale_log2;
 
     if (gs + kF32Group > lim) {  // wave-uniform: tail of the chunk or not yet compacted
-      // the lane's eight slots: decisions (8 bytes) and positions (2 x 16
-      // bytes), always inside the page, then a branch-free liveness test
-      const size_t mb = size_t(r.page) * kPage + poff + quad * 8;
-      const uint2 a8 = *reinterpret_cast<const uint2 *>(slot_alpha + mb);
+      // the lane's eight slots (4 quad .. + 4 and 16 + 4 quad .. + 4 of the
+      // group): decisions (2 x 4 bytes) and positions (2 x 16 bytes), always
+      // inside the page, then a branch-free liveness test
+      const size_t mb = size_t(r.page) * kPage + poff + quad * 4;
+      const uint32_t a4[2] = {*reinterpret_cast<const uint32_t *>(slot_alpha + mb),
+                              *reinterpret_cast<const uint32_t *>(slot_alpha + mb + 16)};
       const int4 p0 = *reinterpret_cast<const int4 *>(slot_pos + mb);
-      const int4 p1 = *reinterpret_cast<const int4 *>(slot_pos + mb + 4);
+      const int4 p1 = *reinterpret_cast<const int4 *>(slot_pos + mb + 16);
       const int pos[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int slot = gs + quad * 8 + e;
-        const uint32_t marked = ((e < 4 ? a8.x : a8.y) >> (8 * (e & 3))) & 0xffu;
+        const int slot = gs + 16 * (e >> 2) + quad * 4 + (e & 3);
+        const uint32_t marked = (a4[e >> 2] >> (8 * (e & 3))) & 0xffu;
         // live for this column's query; live for at least one query of the launch
         const bool live = (slot < s_end) & ((slot < nclean) | ((pos[e] <= t_col) &
                                             ((marked == 0u) | ((t_col - pos[e]) < window))));

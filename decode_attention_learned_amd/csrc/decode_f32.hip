@@ -80,7 +80,6 @@ __global__ __launch_bounds__(kF32Threads, 2) void k_decode_f32(
     const int32_t *__restrict__ seq_len, int32_t *__restrict__ plan,
     uint32_t *__restrict__ chunk_status, float2 *__restrict__ part_ml,
     float *__restrict__ part_o, float *__restrict__ out) {
-  constexpr int DQ = D / 4;     // QK k-steps: dims per lane group
   constexpr int NH = D / 16;    // 4-float half runs per lane and tile
   constexpr int KS = D / 32;    // key fragments per tile in the page layout
   constexpr int DT = D / 16;    // PV products per k-step

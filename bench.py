@@ -220,6 +220,44 @@ def cpu_baseline(w, seconds: float = 12.0, threads: int = 1) -> dict:
                       f"same for the full batch (each of its steps is {w.batch} such sequences)"}
 
 
+def fill_launch_ms(caches, inputs, outs, scale: float, n_launch: int) -> float:
+    """Mean duration of the decode launch (dms_decode_attn_fill) with no event
+    between launches.  Every replica first takes one more step (reserve, then
+    the fill) with its last prepared inputs; then `n_launch` further fill
+    launches, rotating over the replicas, run back to back between two events
+    on the library's stream (one untimed launch first, so that the stream is
+    busy when the start event is recorded).  A repeated fill serves the
+    replica's reserved token again with the same inputs: it streams the same
+    slots and rewrites the token's slot with the same bytes, so every cache
+    ends as after its one step.  An event recorded between launches costs a
+    few microseconds of queue time, which per-call events would add to every
+    launch."""
+    import torch
+
+    replicas = len(caches)
+    for r in range(replicas):
+        q, k, v, logit = inputs[r][-1]
+        caches[r][0].reserve()
+        caches[r][0].fill_and_decode(k, v, logit, q, outs[r], scale)
+
+    def launch(n):
+        r = n % replicas
+        q, k, v, logit = inputs[r][-1]
+        caches[r][0].fill_and_decode(k, v, logit, q, outs[r], scale)
+
+    launch(0)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for n in range(1, n_launch + 1):
+        launch(n)
+    end.record()
+    torch.cuda.synchronize()
+    if any(c.status_word() for c, _ in caches):
+        raise RuntimeError("device status set in the launch pass")
+    return start.elapsed_time(end) / n_launch
+
+
 def _time_calls(fn, iters: int) -> float:
     """Mean milliseconds of fn() over `iters` calls, HIP events on the current stream.
 
@@ -595,9 +633,9 @@ def decode_config_leg(name: str, steps: int = 64, warmup: int = 8, n_ev: int = 3
     eviction rates and replica count), measured like the headline: `steps` steps
     between two events (reserve + decode with the token, compaction every
     `compact_every` steps per replica, round-robin over the replicas), then
-    per-call events around the decode call on `n_ev` further steps for its time
-    and KV rate (on float32 caches the call also holds the launch that writes
-    the token)."""
+    `n_ev` back-to-back decode launches (fill_launch_ms) for its time and KV
+    rate (on float32 caches the call also holds the launch that writes the
+    token)."""
     import torch
 
     import workloads as wl
@@ -605,27 +643,21 @@ def decode_config_leg(name: str, steps: int = 64, warmup: int = 8, n_ev: int = 3
     w = wl.get(name)
     dev = torch.device("cuda:0")
     replicas, every = w.replicas, w.compact_every
-    total = warmup + steps + n_ev
-    per_rep = (total + replicas - 1) // replicas
+    # one more input per replica for the launch pass
+    per_rep = (warmup + steps + replicas - 1) // replicas + 1
     caches = [build_replica(w, r, dev, per_rep + every + 64) for r in range(replicas)]
     inputs = [[wl.decode_step_inputs(w, j, device=dev, replica=r, rates=caches[r][1])
                for j in range(per_rep)] for r in range(replicas)]
     outs = [torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
             for _ in range(replicas)]
     scale = 1.0 / math.sqrt(w.head_dim)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_ev)]
 
-    def step(i, ev=None):
+    def step(i):
         r, j = i % replicas, i // replicas
         cache = caches[r][0]
         q, k, v, logit = inputs[r][j]
         cache.reserve()
-        if ev is not None:
-            ev[0].record()
         cache.fill_and_decode(k, v, logit, q, outs[r], scale)
-        if ev is not None:
-            ev[1].record()
         if (i + 1) % every == 0:
             caches[((i + 1) // every - 1) % replicas][0].compact()
 
@@ -641,13 +673,10 @@ def decode_config_leg(name: str, steps: int = 64, warmup: int = 8, n_ev: int = 3
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / steps
-    for i in range(n_ev):
-        step(warmup + steps + i, evs[i])
-    torch.cuda.synchronize()
-    after = [retained_total(c) for c, _ in caches]
     if any(c.status_word() for c, _ in caches):
         raise RuntimeError(f"{name}: device status set")
-    dec_ms = sum(a.elapsed_time(b) for a, b in evs) / n_ev
+    dec_ms = fill_launch_ms(caches, inputs, outs, scale, n_ev)
+    after = [retained_total(c) for c, _ in caches]
     retained = sum(a[0] + b[0] for a, b in zip(before, after)) / (2 * replicas)
     bytes_alg = retained * w.head_dim * 2 * (4 if w.dtype == "f32" else 2)
     kv_gbps = bytes_alg / (dec_ms * 1e-3) / 1e9
@@ -821,7 +850,9 @@ def main():
     # of every replica, after the timed window
     n_break = max(64, every * replicas)
     total = args.warmup + args.steps + n_break
-    per_rep = (total + replicas - 1) // replicas
+    # one more input per replica for the launch pass (fill_launch_ms)
+    per_rep = (total + replicas - 1) // replicas + 1
+    n_launch = 64
     extra = per_rep + every + 64
 
     log(f"[bench] building {replicas} replica(s) of {w.name}: B={w.batch} Hkv={w.kv_heads} "
@@ -915,9 +946,14 @@ def main():
     t_compact = [e[3].elapsed_time(e[4]) for e, f in zip(evs, flags) if f]
     peak_pages = max(int(p) for p, _ in peaks)
     peak_slots = max(int(n) for _, n in peaks)
+    # the decode launch's duration for the roofline: back-to-back launches
+    with marked("launch pass"):
+        launch_ms = (fill_launch_ms(caches, inputs, outs, scale, n_launch)
+                     if not args.append_launch else None)
 
     ms_step = total_ms / args.steps
-    dec_ms = sum(t_decode) / len(t_decode)
+    dec_ev_ms = sum(t_decode) / len(t_decode)   # with an event before and after every call
+    dec_ms = launch_ms if launch_ms is not None else dec_ev_ms
     res_ms = sum(t_reserve) / len(t_reserve)
     cmp_ms = sum(t_compact) / len(t_compact)
     retained = sum(a[0] + b[0] for a, b in zip(before, after)) / (2 * replicas)
@@ -960,9 +996,10 @@ def main():
         "retained_per_unit": round(retained / w.units, 1),
         "breakdown": {
             "steps": n_break, "reserve_us": round(res_ms * 1e3, 2),
-            "decode_attn_us": round(dec_ms * 1e3, 2), "compact_us": round(cmp_ms * 1e3, 2),
+            "decode_attn_us": round(dec_ev_ms * 1e3, 2), "compact_us": round(cmp_ms * 1e3, 2),
             "compactions": len(t_compact),
-            "step_us": round((res_ms + dec_ms + cmp_ms / every) * 1e3, 2),
+            "step_us": round((res_ms + dec_ev_ms + cmp_ms / every) * 1e3, 2),
+            "events": "one before and after every call (each adds a few microseconds)",
         },
         "memory": {
             "peak_pages_in_use": peak_pages, "page_bytes": 64 * w.head_dim * 2 * elem,
@@ -982,7 +1019,12 @@ def main():
             # the counters were taken on the default workload
             "traffic": None if over or args.workload != DEFAULT_WORKLOAD else traffic_from_profile(bytes_alg),
             "algorithmic_bytes_per_launch": int(bytes_alg),
-            "launch_time_from": "HIP events around each dms_decode_attn_fill call of the breakdown pass",
+            "launch_us": round(dec_ms * 1e3, 2),
+            "launch_time_from": (
+                f"two HIP events around {n_launch} back-to-back dms_decode_attn_fill launches "
+                "rotating over the replicas (each serving its reserved token again)"
+                if launch_ms is not None else
+                "HIP events around each dms_decode_attn call of the breakdown pass"),
         },
     }
     log(f"[bench] {tokens_s:.0f} tok/s, {ms_step * 1e3:.1f} us/step ({n_compact} compactions in the "

@@ -209,3 +209,24 @@ def test_step_full_size_qwen3_8b_cr8(gpu):
     say(f"full-size fill path vs oracle: max abs err {worst:.2e} over {len(sample)} units")
     assert b.status_word() == 0
     _same_state(a, b, range(0, w.units, 61))
+
+
+def test_repeated_fill_leaves_the_step_state(gpu):
+    """bench.py times the decode launch by repeating dms_decode_attn_fill after
+    one reserve: a repeated fill serves the same reserved token again (the same
+    slots streamed, the token's slot rewritten with the same bytes), so the
+    cache ends as after the one step and every repeat gives the same output."""
+    w = _workload(4, 8, 4, 128, "bf16", 300, 0.875, 8601)
+    a, b, rates = _twins(w, gpu)
+    scale = scale_of(w.head_dim)
+    for step in range(3):
+        q, k, v, logit = wl.decode_step_inputs(w, step, rates=rates)
+        q, k, v, logit = q.to(gpu), k.to(gpu), v.to(gpu), logit.to(gpu)
+        oa = a.step(k, v, logit, q)
+        b.reserve()
+        outs = [b.fill_and_decode(k, v, logit, q, torch.empty_like(oa), scale) for _ in range(4)]
+        for i, ob in enumerate(outs):
+            assert torch.equal(oa, ob), f"step {step}, fill {i}: outputs differ"
+        _same_state(a, b, range(w.units))
+        assert torch.equal(a.append_base.cpu(), b.append_base.cpu())
+    assert b.status_word() == 0

@@ -280,7 +280,10 @@ __device__ __forceinline__ void store_rows(const floatx4 (&o)[D / 16][2], const 
       const int row = r + sub;
       const int i = i0 + 16 * qt + row;
       const floatx4 v = *reinterpret_cast<const floatx4 *>(stage + row * D + ((c4 + 4 * row) & (D - 1)));
-      if (i < S) *reinterpret_cast<floatx4 *>(out + row0 + size_t(i) * rstride + c4) = v;
+      // nontemporal: the output is not read again by this launch (gathered
+      // call 0.407 -> 0.397 ms, the dense and relaxed calls unchanged)
+      if (i < S)
+        __builtin_nontemporal_store(v, reinterpret_cast<floatx4 *>(out + row0 + size_t(i) * rstride + c4));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
